@@ -1,0 +1,147 @@
+"""fp64 CPU oracle of the verification step (tree attention, acceptance, commit).
+
+TEST INFRASTRUCTURE ONLY.  The tests, the smoke check and the benchmark's
+CPU-baseline leg use it; the product path (the HIP library and its binding)
+never imports it.  The arithmetic lives in ``oracle.c`` (plain C, double
+precision); this module only builds it and marshals NumPy arrays through ctypes.
+
+Every function here is pinned by the CPU test-suite against facts the pages and
+the mathematics fix (brute-force per-path causal attention, library attention,
+closed forms, the chi-square test of the output distribution, worked examples).
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force=True):
+    """Compile oracle.c into liboracle.so with gcc (OpenMP, no fast-math)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", _LIB + ".tmp", "-lm"]
+    if force or not os.path.exists(_LIB):
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        D = ctypes.c_double
+        lib.oracle_tree_attn.argtypes = [I, I, I, I, I, I, I, D, P, P, P, P, P, I, P, P]
+        lib.oracle_tree_attn.restype = I
+        lib.oracle_accept.argtypes = [I, I, I, I, P, P, P, P, P, P, D, D, D, P, P, P, P, P]
+        lib.oracle_accept.restype = I
+        lib.oracle_commit.argtypes = [I, I, I, I, I, P, P, P, P, P]
+        lib.oracle_commit.restype = I
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def tree_attn(q, k_cache, v_cache, prefix_len, parent, dtype, scale=None, rows=None):
+    """Tree attention in fp64.
+
+    q [B][N][Hq][D], k_cache/v_cache [B][Hkv][cap][D] (float32, or uint16
+    bf16 bits when dtype == "bf16"), prefix_len [B], parent [B][N] or None for
+    a chain.  rows: optional (n, 3) int array of (b, node, q-head); the result
+    is then [n][D], else [B][N][Hq][D] (float64).
+    """
+    B, N, Hq, D = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    dt = 1 if dtype == "bf16" else 0
+    store = np.uint16 if dt else np.float32
+    q, k, v = _c(q, store), _c(k_cache, store), _c(v_cache, store)
+    pl = _c(prefix_len, np.int32)
+    par = _c(parent, np.int32)
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    if rows is None:
+        out = np.empty((B, N, Hq, D), dtype=np.float64)
+        sel, nsel = None, 0
+    else:
+        sel = _c(rows, np.int32).reshape(-1, 3)
+        nsel = sel.shape[0]
+        out = np.empty((nsel, D), dtype=np.float64)
+    rc = _load().oracle_tree_attn(B, N, Hq, Hkv, D, cap, dt, float(scale), _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(pl), _ptr(par), nsel, _ptr(sel), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_tree_attn rejected its arguments")
+    return out
+
+
+def accept(rule, target_logits, tokens, parent, temperature, draft_probs=None, u_accept=None,
+           u_sample=None, epsilon=0.0, delta=0.0):
+    """Acceptance in fp64 ("reject" or "typical").
+
+    Returns dict(accept_len [B], path [B][N], out_tokens [B][N], margin [B],
+    stop [B]).
+    """
+    B, N, V = target_logits.shape
+    r = {"reject": 0, "typical": 1}[rule]
+    lg = _c(target_logits, np.float32)
+    dp = _c(draft_probs, np.float32)
+    tk = _c(tokens, np.int32)
+    par = _c(parent, np.int32)
+    ua = _c(u_accept, np.float32) if u_accept is not None else np.zeros((B, N), np.float32)
+    us = _c(u_sample, np.float32) if u_sample is not None else np.zeros((B, N), np.float32)
+    acc = np.empty(B, np.int32)
+    path = np.empty((B, N), np.int32)
+    out = np.empty((B, N), np.int32)
+    margin = np.empty(B, np.float64)
+    stop = np.empty(B, np.int32)
+    rc = _load().oracle_accept(B, N, V, r, _ptr(lg), _ptr(dp), _ptr(tk), _ptr(par), _ptr(ua), _ptr(us),
+                               float(temperature), float(epsilon), float(delta), _ptr(acc), _ptr(path),
+                               _ptr(out), _ptr(margin), _ptr(stop))
+    if rc != 0:
+        raise ValueError("oracle_accept rejected its arguments")
+    return dict(accept_len=acc, path=path, out_tokens=out, margin=margin, stop=stop)
+
+
+def commit(k_cache, v_cache, prefix_len, path, accept_len):
+    """In-place commit of the accepted path's KV rows (NumPy arrays, modified).
+
+    Returns the updated prefix_len (also written in place when it is an int32
+    contiguous array).
+    """
+    B, Hkv, cap, D = k_cache.shape
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    N = path.shape[1]
+    pl = prefix_len if (prefix_len.dtype == np.int32 and prefix_len.flags.c_contiguous) else _c(prefix_len, np.int32)
+    pa = _c(path, np.int32)
+    al = _c(accept_len, np.int32)
+    rc = _load().oracle_commit(B, N, Hkv, cap, D * k_cache.itemsize, _ptr(k_cache), _ptr(v_cache), _ptr(pl),
+                               _ptr(pa), _ptr(al))
+    if rc != 0:
+        raise ValueError("oracle_commit rejected its arguments")
+    return pl
+
+
+def run_workload(w, rows=None, attention=True, accept_=True):
+    """Oracle outputs for a workloads.Workload (attention and/or acceptance)."""
+    res = {}
+    par = None if w.is_chain else w.parent
+    if attention:
+        res["attn"] = tree_attn(w.q, w.k_cache, w.v_cache, w.prefix_len, par, w.dtype, rows=rows)
+    if accept_:
+        res["accept"] = accept(w.rule, w.target_logits, w.tokens, par, w.temperature, w.draft_probs,
+                               w.u_accept, w.u_sample, w.epsilon, w.delta)
+    return res

@@ -1,0 +1,361 @@
+/*
+ * oracle.c -- plain, slow fp64 CPU reference of the speculative-decoding
+ * verification step.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and
+ * the benchmark's CPU-baseline leg call it; the product path never does.  It
+ * shares no code with the HIP library.
+ *
+ * Every floating-point step is done in double precision on the exact input
+ * values (bf16 and fp32 widen to double without rounding).  The loops follow
+ * the definitions directly: no blocking, no fusion, no reordering.
+ *
+ * Sources (the pages this reference is written from):
+ *  - "MEDUSA" section of "Fast Inference from Transformers via Speculative
+ *    Decoding" blog post (taking-lying-flat.github.io, spec-decoding-i),
+ *    tree attention paragraph: a node attends to itself, its ancestors and the
+ *    verified prefix; positions follow tree depth; candidates are the
+ *    Cartesian product of per-head top predictions.
+ *  - Same page, "Speculative Decoding" / "Speculative Sampling" sections: the
+ *    draft token x is kept when a uniform u satisfies u < p(x)/q(x); on the
+ *    first rejection one token is drawn from norm(max(0, p - q)) and the rest
+ *    are dropped; if every draft is kept one extra token is drawn from the
+ *    target's distribution at the last position; sampling transforms such as
+ *    temperature are applied to the probabilities first.
+ *  - Same page, MEDUSA "typical acceptance" paragraph: a candidate token is
+ *    accepted when p(x) > min(eps, delta * exp(-H(p))); the first token is
+ *    greedy and always accepted; the output is the longest accepted prefix
+ *    over all candidates; temperature 0 reduces to greedy.
+ *
+ * Readings where the pages are silent (their formulas were lost in
+ * extraction):
+ *  - node 0 is the root (the pending token from the previous step); its
+ *    logits give the distribution of the depth-1 nodes; N rows = K + 1;
+ *  - the rejection test is the strict u * q(x) < p(x);
+ *  - every node is tested once with its own uniform u_accept[node]; the
+ *    longest accepted root path wins, ties to the smallest stop-node index;
+ *    the residual uses the smallest-index child of the stop node;
+ *  - a draw from weights r with uniform u is the smallest token id x whose
+ *    ascending cumulative sum exceeds u * sum(r) (fallback: the largest x with
+ *    r_x > 0); a residual of zero total mass falls back to p itself;
+ *  - typical rule: the entropy uses the natural log and the temperature-
+ *    scaled p; the root is accepted unconditionally and the step's last token
+ *    is argmax p at the stop node;
+ *  - temperature 0 makes p one-hot at the lowest-index argmax.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+static double load_elem(const void* base, int dtype, size_t idx) {
+    if (dtype == ORACLE_F32) return (double)((const float*)base)[idx];
+    uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+static int parent_of(const int32_t* parent, int N, int b, int i) {
+    if (i == 0) return -1;
+    return parent ? parent[(size_t)b * N + i] : i - 1;
+}
+
+/* ---------------------------------------------------------------------------
+ * Tree attention.  For query row (b, node i, q-head h), with kv-head
+ * g = h / (Hq / Hkv):
+ *   keys  = prefix rows [0, L_b)  plus tree rows L_b + n for every n on the
+ *           root path of i (i itself included);
+ *   s_j   = scale * <q, k_j>;  out = sum_j exp(s_j - max s) v_j / sum_j exp(s_j - max s).
+ * sel == NULL computes every row into out[B][N][Hq][D]; otherwise sel holds
+ * nsel (b, i, h) triples and out is [nsel][D].
+ * ------------------------------------------------------------------------- */
+int oracle_tree_attn(int B, int N, int Hq, int Hkv, int D, int cap, int dtype, double scale,
+                     const void* q, const void* k, const void* v, const int32_t* prefix_len,
+                     const int32_t* parent, int nsel, const int32_t* sel, double* out) {
+    if (B < 0 || N < 1 || N > 64 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1) return -1;
+    const int G = Hq / Hkv;
+    const long total = sel ? (long)nsel : (long)B * N * Hq;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long r = 0; r < total; ++r) {
+        int b, i, h;
+        if (sel) {
+            b = sel[3 * r + 0];
+            i = sel[3 * r + 1];
+            h = sel[3 * r + 2];
+        } else {
+            b = (int)(r / ((long)N * Hq));
+            i = (int)((r / Hq) % N);
+            h = (int)(r % Hq);
+        }
+        const int g = h / G;
+        const int L = prefix_len[b];
+        int path[64], np = 0;
+        for (int n = i; n >= 0; n = parent_of(parent, N, b, n)) path[np++] = n;
+        const long nkeys = (long)L + np;
+        if ((long)L + N > cap) {
+#pragma omp atomic write
+            err = 1;
+            continue;
+        }
+        double* s = (double*)malloc(sizeof(double) * (size_t)nkeys);
+        const size_t qoff = (((size_t)b * N + i) * Hq + h) * (size_t)D;
+        const size_t kvbase = ((size_t)b * Hkv + g) * (size_t)cap;
+        double m = -INFINITY;
+        for (long j = 0; j < nkeys; ++j) {
+            const long row = j < L ? j : (long)L + path[j - L];
+            double dot = 0.0;
+            for (int d = 0; d < D; ++d)
+                dot += load_elem(q, dtype, qoff + d) * load_elem(k, dtype, (kvbase + row) * D + d);
+            s[j] = scale * dot;
+            if (s[j] > m) m = s[j];
+        }
+        double den = 0.0;
+        for (long j = 0; j < nkeys; ++j) {
+            s[j] = exp(s[j] - m);
+            den += s[j];
+        }
+        double* o = out + (size_t)r * D;
+        for (int d = 0; d < D; ++d) o[d] = 0.0;
+        for (long j = 0; j < nkeys; ++j) {
+            const long row = j < L ? j : (long)L + path[j - L];
+            for (int d = 0; d < D; ++d) o[d] += s[j] * load_elem(v, dtype, (kvbase + row) * D + d);
+        }
+        for (int d = 0; d < D; ++d) o[d] /= den;
+        free(s);
+    }
+    return err ? -1 : 0;
+}
+
+/* Lowest index of the largest value of a float row. */
+static int row_argmax(const float* row, int V) {
+    int best = 0;
+    for (int x = 1; x < V; ++x)
+        if (row[x] > row[best]) best = x;
+    return best;
+}
+
+/* p = softmax(l / T) in fp64; T == 0 gives the one-hot at the argmax.
+ * Also returns the entropy -sum p ln p (0 ln 0 = 0). */
+static double target_probs(const float* row, int V, double T, double* p) {
+    if (T == 0.0) {
+        for (int x = 0; x < V; ++x) p[x] = 0.0;
+        p[row_argmax(row, V)] = 1.0;
+        return 0.0;
+    }
+    double m = -INFINITY;
+    for (int x = 0; x < V; ++x) {
+        const double z = (double)row[x] / T;
+        if (z > m) m = z;
+    }
+    double S = 0.0;
+    for (int x = 0; x < V; ++x) {
+        p[x] = exp((double)row[x] / T - m);
+        S += p[x];
+    }
+    double H = 0.0;
+    for (int x = 0; x < V; ++x) {
+        p[x] /= S;
+        if (p[x] > 0.0) H -= p[x] * log(p[x]);
+    }
+    return H;
+}
+
+/* Inverse-CDF draw from non-negative weights r (total S > 0) with uniform u.
+ * *margin receives the distance, in the units of r, from u*S to the nearest
+ * boundary of the chosen token's interval that borders another token of
+ * non-zero weight (INFINITY when no such boundary exists). */
+static int draw(const double* r, int V, double S, double u, double* margin) {
+    const double t = u * S;
+    double cum = 0.0;
+    int x = -1;
+    double lo = 0.0;
+    for (int y = 0; y < V; ++y) {
+        if (r[y] <= 0.0) continue;
+        lo = cum;
+        cum += r[y];
+        if (cum > t) {
+            x = y;
+            break;
+        }
+    }
+    if (x < 0) { /* rounding left u*S at or above the total */
+        for (int y = V - 1; y >= 0; --y)
+            if (r[y] > 0.0) {
+                x = y;
+                break;
+            }
+        *margin = 0.0;
+        return x;
+    }
+    int any_below = 0, any_above = 0;
+    for (int y = 0; y < x; ++y)
+        if (r[y] > 0.0) {
+            any_below = 1;
+            break;
+        }
+    for (int y = x + 1; y < V; ++y)
+        if (r[y] > 0.0) {
+            any_above = 1;
+            break;
+        }
+    double mg = INFINITY;
+    if (any_below && t - lo < mg) mg = t - lo;
+    if (any_above && cum - t < mg) mg = cum - t;
+    *margin = mg;
+    return x;
+}
+
+/* ---------------------------------------------------------------------------
+ * Acceptance.  rule 0 = rejection rule, rule 1 = typical acceptance.
+ * Per request b:
+ *   p_u = softmax(l_u / T) for each node row u that has children (and the stop
+ *   row); node i >= 1 with parent u, token x = tokens[i]:
+ *     rejection: ok_i <=> u_accept[i] * q_i(x) < p_u(x)
+ *     typical:   ok_i <=> p_u(x) > min(eps, delta * exp(-H(p_u)))
+ *   acc_0 = 1, acc_i = ok_i && acc_parent(i); v = deepest accepted node
+ *   (smallest index on ties); a = depth(v); path = root .. v.
+ *   final token:
+ *     typical: argmax p_v
+ *     rejection, v has children: c = smallest child, r = max(0, p_v - q_c),
+ *       r = p_v if sum r == 0, final = draw(r, u_sample[v]);
+ *     rejection, v a leaf: final = draw(p_v, u_sample[v]).
+ * Outputs accept_len[b] = a, path[b][0..a] then -1, out_tokens[b][0..a-1] =
+ * tokens of path[1..a], out_tokens[b][a] = final, then -1.  margin[b] is the
+ * smallest distance of any decision that can change the output from its
+ * threshold (|min(1, p/q) - u|, |p - thr|, the draw margin in probability
+ * units); stop[b] = v.
+ * ------------------------------------------------------------------------- */
+int oracle_accept(int B, int N, int V, int rule, const float* logits, const float* draft,
+                  const int32_t* tokens, const int32_t* parent, const float* u_accept,
+                  const float* u_sample, double T, double eps, double delta, int32_t* accept_len,
+                  int32_t* path, int32_t* out_tokens, double* margin, int32_t* stop) {
+    if (B < 0 || N < 1 || N > 64 || V < 1 || (rule != 0 && rule != 1) || !(T >= 0.0)) return -1;
+    if (rule == 0 && N > 1 && !draft) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+        int par[64], depth[64], has_child[64], acc[64];
+        for (int i = 0; i < N; ++i) has_child[i] = 0;
+        for (int i = 0; i < N; ++i) {
+            par[i] = parent_of(parent, N, b, i);
+            depth[i] = i == 0 ? 0 : depth[par[i]] + 1;
+            if (i > 0) has_child[par[i]] = 1;
+        }
+        double* P = (double*)calloc((size_t)N * V, sizeof(double));
+        double H[64];
+        int have[64];
+        for (int u = 0; u < N; ++u) {
+            have[u] = 0;
+            if (has_child[u]) {
+                H[u] = target_probs(logits + ((size_t)b * N + u) * V, V, T, P + (size_t)u * V);
+                have[u] = 1;
+            }
+        }
+        double mg = INFINITY;
+        acc[0] = 1;
+        for (int i = 1; i < N; ++i) {
+            const int u = par[i];
+            const int x = tokens[(size_t)b * N + i];
+            const double pu = P[(size_t)u * V + x];
+            int ok;
+            if (rule == 0) {
+                const double qx = draft[((size_t)b * N + i) * V + x];
+                const double ua = u_accept[(size_t)b * N + i];
+                ok = ua * qx < pu;
+                if (acc[u]) {
+                    const double ratio = qx > 0.0 ? pu / qx : (pu > 0.0 ? INFINITY : 0.0);
+                    const double d = fabs(fmin(1.0, ratio) - ua);
+                    if (d < mg) mg = d;
+                }
+            } else {
+                const double thr = fmin(eps, delta * exp(-H[u]));
+                ok = pu > thr;
+                if (acc[u]) {
+                    const double d = fabs(pu - thr);
+                    if (d < mg) mg = d;
+                }
+            }
+            acc[i] = ok && acc[u];
+        }
+        int v = 0;
+        for (int i = 1; i < N; ++i)
+            if (acc[i] && depth[i] > depth[v]) v = i;
+        const int a = depth[v];
+        int32_t* pth = path + (size_t)b * N;
+        int32_t* ot = out_tokens + (size_t)b * N;
+        for (int i = 0; i < N; ++i) pth[i] = ot[i] = -1;
+        for (int n = v, d = a; n >= 0; n = par[n], --d) pth[d] = n;
+        for (int d = 1; d <= a; ++d) ot[d - 1] = tokens[(size_t)b * N + pth[d]];
+
+        const float* lv = logits + ((size_t)b * N + v) * V;
+        int final;
+        if (rule == 1) {
+            final = row_argmax(lv, V);
+        } else {
+            if (!have[v]) target_probs(lv, V, T, P + (size_t)v * V);
+            const double* pv = P + (size_t)v * V;
+            double* r = (double*)malloc(sizeof(double) * (size_t)V);
+            double S = 0.0;
+            if (has_child[v]) {
+                int c = -1;
+                for (int i = 1; i < N && c < 0; ++i)
+                    if (par[i] == v) c = i;
+                const float* qc = draft + ((size_t)b * N + c) * V;
+                for (int x = 0; x < V; ++x) {
+                    const double d = pv[x] - (double)qc[x];
+                    r[x] = d > 0.0 ? d : 0.0;
+                    S += r[x];
+                }
+            }
+            if (S == 0.0) {
+                S = 0.0;
+                for (int x = 0; x < V; ++x) {
+                    r[x] = pv[x];
+                    S += r[x];
+                }
+            }
+            double dm;
+            final = draw(r, V, S, (double)u_sample[(size_t)b * N + v], &dm);
+            if (dm < mg) mg = dm;
+            free(r);
+        }
+        ot[a] = final;
+        accept_len[b] = a;
+        if (margin) margin[b] = mg;
+        if (stop) stop[b] = v;
+        free(P);
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Commit: for every request b and kv-head, the accepted path's rows
+ * L_b + path[d] (d = 0..a) move to L_b + d; every source row is read before
+ * any row is written.  prefix_len[b] becomes L_b + a + 1.  row_bytes = D *
+ * element size; the caches are [B][Hkv][cap][row_bytes].
+ * ------------------------------------------------------------------------- */
+int oracle_commit(int B, int N, int Hkv, int cap, int row_bytes, uint8_t* k, uint8_t* v,
+                  int32_t* prefix_len, const int32_t* path, const int32_t* accept_len) {
+    for (int b = 0; b < B; ++b) {
+        const int L = prefix_len[b];
+        const int a = accept_len[b];
+        if (a < 0 || a >= N || L + N > cap) return -1;
+        uint8_t* tmp = (uint8_t*)malloc((size_t)(a + 1) * row_bytes);
+        for (int which = 0; which < 2; ++which) {
+            uint8_t* base = which ? v : k;
+            for (int g = 0; g < Hkv; ++g) {
+                uint8_t* head = base + ((size_t)b * Hkv + g) * (size_t)cap * row_bytes;
+                for (int d = 0; d <= a; ++d)
+                    memcpy(tmp + (size_t)d * row_bytes,
+                           head + (size_t)(L + path[(size_t)b * N + d]) * row_bytes, row_bytes);
+                for (int d = 0; d <= a; ++d)
+                    memcpy(head + (size_t)(L + d) * row_bytes, tmp + (size_t)d * row_bytes, row_bytes);
+            }
+        }
+        free(tmp);
+        prefix_len[b] = L + a + 1;
+    }
+    return 0;
+}
