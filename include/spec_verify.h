@@ -1,0 +1,156 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X (gfx950) speculative-decoding
+ * verification step: tree-verify attention, rejection / typical acceptance
+ * over the vocabulary, and the in-place KV commit of the accepted path.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE memory owned by the caller.  The library
+ *    never allocates, frees or synchronises; every call only enqueues kernels
+ *    on `stream` (a hipStream_t; NULL = the null stream) and returns.
+ *  - Calls are stateless and re-entrant.  Two calls that share a workspace or
+ *    an output must not overlap in time (same rule as any stream work).
+ *  - Row-major layouts; int32 indices; `B` = batch, `N` = tree nodes per
+ *    request INCLUDING the root (a chain of K drafts has N = K + 1), `V` =
+ *    vocabulary size.
+ *  - Host-detectable argument errors return SPEC_EINVAL / SPEC_EUNSUPPORTED /
+ *    SPEC_EWORKSPACE before anything is launched; a failed launch returns
+ *    SPEC_EHIP.  Device-side contract violations (a malformed parent array, a
+ *    token >= V, a uniform outside [0,1)) give undefined results but never an
+ *    out-of-bounds access: the kernels clamp every index they read.
+ *  - B == 0 is a no-op returning SPEC_OK.
+ *
+ * Tree model (MEDUSA section of the blog page "Fast Inference from
+ * Transformers via Speculative Decoding", tree-attention paragraph): node 0 is
+ * the root, the pending token whose logits give the depth-1 candidates; every
+ * other node i has parent[i] < i.  A node attends to the verified prefix, its
+ * ancestors and itself; its position is L_b + depth(i).  parent == NULL means
+ * a chain (parent[i] = i - 1).
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum spec_status {
+    SPEC_OK = 0,
+    SPEC_EINVAL = -1,       /* bad pointer, size or parameter value */
+    SPEC_EUNSUPPORTED = -2, /* valid in principle but not built (dtype, head_dim) */
+    SPEC_EWORKSPACE = -3,   /* workspace smaller than the matching *_workspace_bytes */
+    SPEC_EHIP = -4          /* a kernel launch failed */
+} spec_status;
+
+typedef enum spec_dtype { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
+
+/* Shape of the attention problem.  q/out are [B][N][Hq][D]; the caches are
+ * [B][Hkv][kv_capacity][D].  Hq % Hkv == 0; query head h reads kv head
+ * h / (Hq / Hkv).  head_dim is 64 or 128.  1 <= num_nodes <= 64.
+ * softmax_scale <= 0 selects 1/sqrt(head_dim). */
+typedef struct spec_attn_desc {
+    int32_t batch;
+    int32_t num_nodes;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t kv_capacity; /* rows per (b, kv head); must be >= max_prefix_len + num_nodes */
+    int32_t dtype;       /* spec_dtype of q, the caches and out */
+    float softmax_scale;
+} spec_attn_desc;
+
+/* Workspace bytes spec_verify_attn needs for this shape and prefix bound
+ * (split-KV partial results).  Returns 0 for an invalid descriptor. */
+size_t spec_verify_attn_workspace_bytes(const spec_attn_desc* desc, int32_t max_prefix_len);
+
+/* Tree-verify attention (the parallel scoring pass of the verification step:
+ * "Speculative Sampling" section -- all draft positions are scored in one
+ * target pass -- with the MEDUSA tree mask).  For every (b, node i, q-head h):
+ *   keys  = cache rows [0, L_b) and L_b + n for n on the root path of i;
+ *   out   = softmax(scale * q k^T) v over those keys, fp32 accumulation.
+ * Arguments
+ *   max_prefix_len  host int >= every prefix_len[b] (sizes the KV split)
+ *   q               [B][N][Hq][D] (dtype)
+ *   k_cache,v_cache [B][Hkv][cap][D] (dtype); rows [0, L_b) are the verified
+ *                   prefix, rows [L_b, L_b + N) the tree nodes' K/V (written
+ *                   by the caller, node order); rows beyond are never read
+ *   prefix_len      [B] int32, device
+ *   parent          [B][N] int32 or NULL (chain)
+ *   out             [B][N][Hq][D] (dtype), written
+ *   workspace       >= spec_verify_attn_workspace_bytes(desc, max_prefix_len) */
+int spec_verify_attn(const spec_attn_desc* desc, int32_t max_prefix_len, const void* q,
+                     const void* k_cache, const void* v_cache, const int32_t* prefix_len,
+                     const int32_t* parent, void* out, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Workspace bytes for either acceptance entry point.  0 for invalid sizes. */
+size_t spec_accept_workspace_bytes(int32_t batch, int32_t num_nodes, int32_t vocab);
+
+/* Rejection-rule acceptance ("Speculative Decoding" and "Speculative
+ * Sampling" sections of the blog page "Fast Inference from Transformers via
+ * Speculative Decoding").  p_u = softmax(target_logits[b][u] / T) (T == 0: the
+ * one-hot lowest-index argmax).  Node i >= 1 with parent u and token x =
+ * tokens[b][i] passes when u_accept[b][i] * draft_probs[b][i][x] < p_u(x); a
+ * node is accepted when it and all its ancestors pass.  The stop node v is the
+ * deepest accepted node (smallest index on ties), a = depth(v).  The last
+ * token is drawn by inverse CDF (ascending token ids, uniform u_sample[b][v])
+ * from norm(max(0, p_v - q_c)) when v has children (c = its smallest-index
+ * child; p_v itself if that residual is all zero), else from p_v (the bonus
+ * token).
+ *   target_logits [B][N][V] fp32, row i = target logits at node i
+ *   draft_probs   [B][N][V] fp32, row i = the distribution node i's token was
+ *                 drawn from (already temperature-transformed); row 0 unused
+ *   tokens        [B][N] int32 (entry 0 unused); parent [B][N] or NULL
+ *   u_accept, u_sample [B][N] fp32 in [0, 1)
+ *   temperature   >= 0, finite; batch <= 65535
+ * Outputs: accept_len [B] = a; path [B][N] = root .. v then -1;
+ *   out_tokens [B][N] = tokens of path[1..a], the drawn token, then -1. */
+int spec_accept_reject(int32_t batch, int32_t num_nodes, int32_t vocab, const float* target_logits,
+                       const float* draft_probs, const int32_t* tokens, const int32_t* parent,
+                       const float* u_accept, const float* u_sample, float temperature,
+                       int32_t* accept_len, int32_t* path, int32_t* out_tokens, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Typical acceptance (MEDUSA section, typical-acceptance paragraph of the
+ * same page).  Node i >= 1 with parent u and token x passes when
+ * p_u(x) > min(epsilon, delta * exp(-H(p_u))), H in nats with p_u =
+ * softmax(target_logits[b][u] / T).  The root is the previous step's greedy
+ * token and is accepted unconditionally; acceptance, the stop node and the
+ * outputs are as for spec_accept_reject except that the last token is
+ * argmax p_v (lowest index on ties).  epsilon, delta >= 0, finite. */
+int spec_accept_typical(int32_t batch, int32_t num_nodes, int32_t vocab, const float* target_logits,
+                        const int32_t* tokens, const int32_t* parent, float temperature,
+                        float epsilon, float delta, int32_t* accept_len, int32_t* path,
+                        int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Commit of the accepted path (the rejected candidates are discarded, as the
+ * speculative-decoding loop prescribes): for every request b and kv head the
+ * cache rows L_b + path[b][d], d = 0..accept_len[b], move to L_b + d, in
+ * place (all sources are read before they can be overwritten), then
+ * prefix_len[b] += accept_len[b] + 1.  For a chain nothing moves.  Uses the
+ * desc fields batch, num_nodes, num_kv_heads, head_dim, kv_capacity, dtype. */
+int spec_commit_kv(const spec_attn_desc* desc, void* k_cache, void* v_cache, int32_t* prefix_len,
+                   const int32_t* path, const int32_t* accept_len, void* stream);
+
+/* Depth-based positions of the tree nodes (MEDUSA tree-attention paragraph):
+ * positions[b][i] = prefix_len[b] + depth(i).  For callers that rotate q/k
+ * before spec_verify_attn. */
+int spec_tree_positions(int32_t batch, int32_t num_nodes, const int32_t* prefix_len,
+                        const int32_t* parent, int32_t* positions, void* stream);
+
+/* Debug check of a parent array: status[b] = 0 when parent[b][0] == -1 and
+ * 0 <= parent[b][i] < i for all i >= 1, else 1 + the first offending node index. */
+int spec_validate_tree(int32_t batch, int32_t num_nodes, const int32_t* parent, int32_t* status,
+                       void* stream);
+
+/* Static string naming a spec_status value. */
+const char* spec_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -45,6 +45,8 @@ def _load():
         lib.oracle_accept.restype = I
         lib.oracle_commit.argtypes = [I, I, I, I, I, P, P, P, P, P]
         lib.oracle_commit.restype = I
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = I
         _lib = lib
     return _lib
 
@@ -133,6 +135,11 @@ def commit(k_cache, v_cache, prefix_len, path, accept_len):
     if rc != 0:
         raise ValueError("oracle_commit rejected its arguments")
     return pl
+
+
+def num_threads():
+    """OpenMP threads the oracle runs with."""
+    return int(_load().oracle_num_threads())
 
 
 def run_workload(w, rows=None, attention=True, accept_=True):

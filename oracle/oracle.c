@@ -42,6 +42,9 @@
  *  - temperature 0 makes p one-hot at the lowest-index argmax.
  */
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -225,8 +228,8 @@ static int draw(const double* r, int V, double S, double u, double* margin) {
  * Outputs accept_len[b] = a, path[b][0..a] then -1, out_tokens[b][0..a-1] =
  * tokens of path[1..a], out_tokens[b][a] = final, then -1.  margin[b] is the
  * smallest distance of any decision that can change the output from its
- * threshold (|min(1, p/q) - u|, |p - thr|, the draw margin in probability
- * units); stop[b] = v.
+ * threshold (|min(1, p/q) - u|; |p - thr| / max(p, thr) for the typical
+ * test; the draw margin in probability units); stop[b] = v.
  * ------------------------------------------------------------------------- */
 int oracle_accept(int B, int N, int V, int rule, const float* logits, const float* draft,
                   const int32_t* tokens, const int32_t* parent, const float* u_accept,
@@ -272,8 +275,9 @@ int oracle_accept(int B, int N, int V, int rule, const float* logits, const floa
             } else {
                 const double thr = fmin(eps, delta * exp(-H[u]));
                 ok = pu > thr;
-                if (acc[u]) {
-                    const double d = fabs(pu - thr);
+                if (acc[u]) { /* relative: p and thr both carry relative rounding */
+                    const double den = fmax(pu, thr);
+                    const double d = den > 0.0 ? fabs(pu - thr) / den : INFINITY;
                     if (d < mg) mg = d;
                 }
             }
@@ -358,4 +362,13 @@ int oracle_commit(int B, int N, int Hkv, int cap, int row_bytes, uint8_t* k, uin
         prefix_len[b] = L + a + 1;
     }
     return 0;
+}
+
+/* Threads the OpenMP loops above use (1 without OpenMP). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }

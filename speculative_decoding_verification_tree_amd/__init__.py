@@ -1,0 +1,25 @@
+"""MI355X (gfx950) speculative-decoding verification step.
+
+Tree-verify attention, rejection / typical acceptance over the vocabulary and
+the in-place KV commit, as hand-written HIP kernels behind the C ABI of
+include/spec_verify.h.  This package is the thin PyTorch binding of that ABI.
+"""
+from .api import (
+    SpecError,
+    attn_desc,
+    spec_accept_reject,
+    spec_accept_typical,
+    spec_accept_workspace_bytes,
+    spec_commit_kv,
+    spec_tree_positions,
+    spec_validate_tree,
+    spec_verify_attn,
+    spec_verify_attn_workspace_bytes,
+)
+from ._native import LIB_PATH, SIGNATURES, lib, status_string
+
+__all__ = [
+    "SpecError", "attn_desc", "spec_accept_reject", "spec_accept_typical", "spec_accept_workspace_bytes",
+    "spec_commit_kv", "spec_tree_positions", "spec_validate_tree", "spec_verify_attn",
+    "spec_verify_attn_workspace_bytes", "LIB_PATH", "SIGNATURES", "lib", "status_string",
+]

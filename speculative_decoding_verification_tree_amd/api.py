@@ -1,0 +1,185 @@
+"""Thin PyTorch binding of the C ABI in include/spec_verify.h.
+
+Each function has the name of the C entry point it calls and only marshals
+arguments: it checks that the tensors are contiguous device tensors of the
+right dtype, passes their data pointers and the current HIP stream, and raises
+on a non-zero status.  All arithmetic runs in the HIP kernels.  Output and
+workspace tensors may be passed in (no allocation) or are created with
+``torch.empty`` when omitted.
+"""
+import ctypes
+
+import torch
+
+from . import _native
+from ._native import AttnDesc, SPEC_BF16, SPEC_F32
+
+
+class SpecError(RuntimeError):
+    def __init__(self, fn, rc):
+        super().__init__(f"{fn}: {_native.status_string(rc)} ({rc})")
+        self.status = rc
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise SpecError(fn, rc)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(dt):
+    if dt == torch.bfloat16:
+        return SPEC_BF16
+    if dt == torch.float32:
+        return SPEC_F32
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def attn_desc(batch, num_nodes, num_q_heads, num_kv_heads, head_dim, kv_capacity, dtype, softmax_scale=0.0):
+    return AttnDesc(batch, num_nodes, num_q_heads, num_kv_heads, head_dim, kv_capacity,
+                    _dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype), float(softmax_scale))
+
+
+def spec_verify_attn_workspace_bytes(desc, max_prefix_len):
+    return int(_native.lib().spec_verify_attn_workspace_bytes(ctypes.byref(desc), int(max_prefix_len)))
+
+
+def spec_verify_attn(q, k_cache, v_cache, prefix_len, parent, max_prefix_len, out=None, workspace=None,
+                     softmax_scale=0.0, stream=None):
+    """Tree-verify attention.  q [B][N][Hq][D]; caches [B][Hkv][cap][D] (same
+    dtype, bf16 or fp32); prefix_len [B] int32; parent [B][N] int32 or None
+    (chain); max_prefix_len: host int >= every prefix length."""
+    B, N, Hq, D = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, n, q.dtype)
+    _dev(prefix_len, "prefix_len", torch.int32)
+    _dev(parent, "parent", torch.int32)
+    desc = attn_desc(B, N, Hq, Hkv, D, cap, q.dtype, softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    need = spec_verify_attn_workspace_bytes(desc, max_prefix_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = _native.lib().spec_verify_attn(ctypes.byref(desc), int(max_prefix_len), _ptr(q), _ptr(k_cache),
+                                        _ptr(v_cache), _ptr(prefix_len), _ptr(parent), _ptr(out),
+                                        _ptr(workspace), nbytes, _stream(stream))
+    _check("spec_verify_attn", rc)
+    return out
+
+
+def spec_accept_workspace_bytes(batch, num_nodes, vocab):
+    return int(_native.lib().spec_accept_workspace_bytes(int(batch), int(num_nodes), int(vocab)))
+
+
+def _accept_outputs(B, N, dev, accept_len, path, out_tokens):
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if path is None:
+        path = torch.empty(B, N, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty(B, N, dtype=torch.int32, device=dev)
+    for t, n in ((accept_len, "accept_len"), (path, "path"), (out_tokens, "out_tokens")):
+        _dev(t, n, torch.int32)
+    return accept_len, path, out_tokens
+
+
+def spec_accept_reject(target_logits, draft_probs, tokens, parent, u_accept, u_sample, temperature,
+                       accept_len=None, path=None, out_tokens=None, workspace=None, stream=None):
+    """Rejection-rule acceptance; returns (accept_len, path, out_tokens)."""
+    B, N, V = target_logits.shape
+    _dev(target_logits, "target_logits", torch.float32)
+    _dev(draft_probs, "draft_probs", torch.float32)
+    _dev(tokens, "tokens", torch.int32)
+    _dev(parent, "parent", torch.int32)
+    _dev(u_accept, "u_accept", torch.float32)
+    _dev(u_sample, "u_sample", torch.float32)
+    accept_len, path, out_tokens = _accept_outputs(B, N, target_logits.device, accept_len, path, out_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(spec_accept_workspace_bytes(B, N, V), 1), dtype=torch.uint8,
+                                device=target_logits.device)
+    rc = _native.lib().spec_accept_reject(B, N, V, _ptr(target_logits), _ptr(draft_probs), _ptr(tokens),
+                                          _ptr(parent), _ptr(u_accept), _ptr(u_sample), float(temperature),
+                                          _ptr(accept_len), _ptr(path), _ptr(out_tokens), _ptr(workspace),
+                                          workspace.numel(), _stream(stream))
+    _check("spec_accept_reject", rc)
+    return accept_len, path, out_tokens
+
+
+def spec_accept_typical(target_logits, tokens, parent, temperature, epsilon, delta, accept_len=None,
+                        path=None, out_tokens=None, workspace=None, stream=None):
+    """Typical acceptance; returns (accept_len, path, out_tokens)."""
+    B, N, V = target_logits.shape
+    _dev(target_logits, "target_logits", torch.float32)
+    _dev(tokens, "tokens", torch.int32)
+    _dev(parent, "parent", torch.int32)
+    accept_len, path, out_tokens = _accept_outputs(B, N, target_logits.device, accept_len, path, out_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(spec_accept_workspace_bytes(B, N, V), 1), dtype=torch.uint8,
+                                device=target_logits.device)
+    rc = _native.lib().spec_accept_typical(B, N, V, _ptr(target_logits), _ptr(tokens), _ptr(parent),
+                                           float(temperature), float(epsilon), float(delta), _ptr(accept_len),
+                                           _ptr(path), _ptr(out_tokens), _ptr(workspace), workspace.numel(),
+                                           _stream(stream))
+    _check("spec_accept_typical", rc)
+    return accept_len, path, out_tokens
+
+
+def spec_commit_kv(k_cache, v_cache, prefix_len, path, accept_len, stream=None):
+    """In-place commit of the accepted path's KV rows; advances prefix_len."""
+    B, Hkv, cap, D = k_cache.shape
+    N = path.shape[1]
+    _dev(k_cache, "k_cache")
+    _dev(v_cache, "v_cache", k_cache.dtype)
+    _dev(prefix_len, "prefix_len", torch.int32)
+    _dev(path, "path", torch.int32)
+    _dev(accept_len, "accept_len", torch.int32)
+    desc = attn_desc(B, N, Hkv, Hkv, D, cap, k_cache.dtype)
+    rc = _native.lib().spec_commit_kv(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(prefix_len),
+                                      _ptr(path), _ptr(accept_len), _stream(stream))
+    _check("spec_commit_kv", rc)
+
+
+def spec_tree_positions(prefix_len, parent, num_nodes, positions=None, stream=None):
+    B = prefix_len.shape[0]
+    _dev(prefix_len, "prefix_len", torch.int32)
+    _dev(parent, "parent", torch.int32)
+    if positions is None:
+        positions = torch.empty(B, num_nodes, dtype=torch.int32, device=prefix_len.device)
+    _dev(positions, "positions", torch.int32)
+    rc = _native.lib().spec_tree_positions(B, int(num_nodes), _ptr(prefix_len), _ptr(parent), _ptr(positions),
+                                           _stream(stream))
+    _check("spec_tree_positions", rc)
+    return positions
+
+
+def spec_validate_tree(parent, status=None, stream=None):
+    B, N = parent.shape
+    _dev(parent, "parent", torch.int32)
+    if status is None:
+        status = torch.empty(B, dtype=torch.int32, device=parent.device)
+    _dev(status, "status", torch.int32)
+    rc = _native.lib().spec_validate_tree(B, N, _ptr(parent), _ptr(status), _stream(stream))
+    _check("spec_validate_tree", rc)
+    return status

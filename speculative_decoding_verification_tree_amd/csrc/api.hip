@@ -1,0 +1,139 @@
+// extern "C" entry points: argument validation, then kernel launches.
+// Nothing here allocates, frees or synchronises.
+#include <math.h>
+
+#include "spec_common.h"
+#include "spec_internal.h"
+
+using namespace specv;
+
+static bool desc_ok(const spec_attn_desc* d, int* err) {
+    if (!d) {
+        *err = SPEC_EINVAL;
+        return false;
+    }
+    if (d->batch < 0 || d->num_nodes < 1 || d->num_nodes > kMaxNodes || d->num_q_heads < 1 ||
+        d->num_kv_heads < 1 || d->num_q_heads % d->num_kv_heads != 0 || d->kv_capacity < 1 ||
+        !(d->softmax_scale == d->softmax_scale) || isinf(d->softmax_scale)) {
+        *err = SPEC_EINVAL;
+        return false;
+    }
+    if (d->head_dim != 64 && d->head_dim != 128) {
+        *err = d->head_dim > 0 ? SPEC_EUNSUPPORTED : SPEC_EINVAL;
+        return false;
+    }
+    if (d->dtype != SPEC_F32 && d->dtype != SPEC_BF16) {
+        *err = SPEC_EUNSUPPORTED;
+        return false;
+    }
+    return true;
+}
+
+extern "C" {
+
+size_t spec_verify_attn_workspace_bytes(const spec_attn_desc* desc, int32_t max_prefix_len) {
+    int err;
+    if (!desc_ok(desc, &err) || max_prefix_len < 0) return 0;
+    if (desc->batch == 0) return 0;
+    return plan_attn(*desc, max_prefix_len).ws_bytes;
+}
+
+int spec_verify_attn(const spec_attn_desc* desc, int32_t max_prefix_len, const void* q, const void* k_cache,
+                     const void* v_cache, const int32_t* prefix_len, const int32_t* parent, void* out,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    int err;
+    if (!desc_ok(desc, &err)) return err;
+    if (desc->batch == 0) return SPEC_OK;
+    if (max_prefix_len < 0 || static_cast<long>(max_prefix_len) + desc->num_nodes > desc->kv_capacity)
+        return SPEC_EINVAL;
+    if (!q || !k_cache || !v_cache || !prefix_len || !out) return SPEC_EINVAL;
+    const AttnPlan plan = plan_attn(*desc, max_prefix_len);
+    if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes)) return SPEC_EWORKSPACE;
+    return launch_verify_attn(*desc, plan, q, k_cache, v_cache, prefix_len, parent, out, workspace,
+                              static_cast<hipStream_t>(stream));
+}
+
+size_t spec_accept_workspace_bytes(int32_t batch, int32_t num_nodes, int32_t vocab) {
+    if (batch < 1 || num_nodes < 1 || num_nodes > kMaxNodes || vocab < 1) return 0;
+    return plan_accept(batch, num_nodes, vocab).ws_bytes;
+}
+
+static int accept_common_checks(int32_t B, int32_t N, int32_t V, const float* logits, const int32_t* tokens,
+                                int32_t* accept_len, int32_t* path, int32_t* out_tokens, float T) {
+    if (B > 65535 || N < 1 || N > kMaxNodes || V < 1) return SPEC_EINVAL;
+    if (!(T >= 0.f) || isinf(T)) return SPEC_EINVAL;
+    if (!logits || !tokens || !accept_len || !path || !out_tokens) return SPEC_EINVAL;
+    return SPEC_OK;
+}
+
+int spec_accept_reject(int32_t batch, int32_t num_nodes, int32_t vocab, const float* target_logits,
+                       const float* draft_probs, const int32_t* tokens, const int32_t* parent,
+                       const float* u_accept, const float* u_sample, float temperature, int32_t* accept_len,
+                       int32_t* path, int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    if (batch < 0) return SPEC_EINVAL;
+    if (batch == 0) return SPEC_OK;
+    int rc = accept_common_checks(batch, num_nodes, vocab, target_logits, tokens, accept_len, path, out_tokens,
+                                  temperature);
+    if (rc != SPEC_OK) return rc;
+    if ((num_nodes > 1 && (!draft_probs || !u_accept)) || !u_sample) return SPEC_EINVAL;
+    const AcceptPlan plan = plan_accept(batch, num_nodes, vocab);
+    if (!workspace || workspace_bytes < plan.ws_bytes) return SPEC_EWORKSPACE;
+    return launch_accept(0, batch, num_nodes, vocab, target_logits, draft_probs, tokens, parent, u_accept,
+                         u_sample, temperature, 0.f, 0.f, accept_len, path, out_tokens, workspace, plan,
+                         static_cast<hipStream_t>(stream));
+}
+
+int spec_accept_typical(int32_t batch, int32_t num_nodes, int32_t vocab, const float* target_logits,
+                        const int32_t* tokens, const int32_t* parent, float temperature, float epsilon,
+                        float delta, int32_t* accept_len, int32_t* path, int32_t* out_tokens, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    if (batch < 0) return SPEC_EINVAL;
+    if (batch == 0) return SPEC_OK;
+    int rc = accept_common_checks(batch, num_nodes, vocab, target_logits, tokens, accept_len, path, out_tokens,
+                                  temperature);
+    if (rc != SPEC_OK) return rc;
+    if (!(epsilon >= 0.f) || !(delta >= 0.f) || isinf(epsilon) || isinf(delta)) return SPEC_EINVAL;
+    const AcceptPlan plan = plan_accept(batch, num_nodes, vocab);
+    if (!workspace || workspace_bytes < plan.ws_bytes) return SPEC_EWORKSPACE;
+    return launch_accept(1, batch, num_nodes, vocab, target_logits, nullptr, tokens, parent, nullptr, nullptr,
+                         temperature, epsilon, delta, accept_len, path, out_tokens, workspace, plan,
+                         static_cast<hipStream_t>(stream));
+}
+
+int spec_commit_kv(const spec_attn_desc* desc, void* k_cache, void* v_cache, int32_t* prefix_len,
+                   const int32_t* path, const int32_t* accept_len, void* stream) {
+    int err;
+    if (!desc_ok(desc, &err)) return err;
+    if (desc->batch == 0) return SPEC_OK;
+    if (!k_cache || !v_cache || !prefix_len || !path || !accept_len) return SPEC_EINVAL;
+    return launch_commit(*desc, k_cache, v_cache, prefix_len, path, accept_len, static_cast<hipStream_t>(stream));
+}
+
+int spec_tree_positions(int32_t batch, int32_t num_nodes, const int32_t* prefix_len, const int32_t* parent,
+                        int32_t* positions, void* stream) {
+    if (batch < 0 || num_nodes < 1 || num_nodes > kMaxNodes) return SPEC_EINVAL;
+    if (batch == 0) return SPEC_OK;
+    if (!prefix_len || !positions) return SPEC_EINVAL;
+    return launch_positions(batch, num_nodes, prefix_len, parent, positions, static_cast<hipStream_t>(stream));
+}
+
+int spec_validate_tree(int32_t batch, int32_t num_nodes, const int32_t* parent, int32_t* status, void* stream) {
+    if (batch < 0 || num_nodes < 1 || num_nodes > kMaxNodes) return SPEC_EINVAL;
+    if (batch == 0) return SPEC_OK;
+    if (!parent || !status) return SPEC_EINVAL;
+    return launch_validate(batch, num_nodes, parent, status, static_cast<hipStream_t>(stream));
+}
+
+const char* spec_status_string(int status) {
+    switch (status) {
+        case SPEC_OK: return "SPEC_OK";
+        case SPEC_EINVAL: return "SPEC_EINVAL: invalid argument";
+        case SPEC_EUNSUPPORTED: return "SPEC_EUNSUPPORTED: unsupported dtype or head_dim";
+        case SPEC_EWORKSPACE: return "SPEC_EWORKSPACE: workspace too small";
+        case SPEC_EHIP: return "SPEC_EHIP: kernel launch failed";
+        default: return "unknown spec_status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,625 @@
+// Tree-verify attention for gfx950.
+//
+// Computes, for every request b, kv head g and query row r = node * G + j
+// (q head g*G + j), softmax(scale * q k^T) v over the verified prefix rows
+// [0, L_b) plus the tree rows L_b + n for every n on the root path of the
+// row's node (MEDUSA section of the blog page "Fast Inference from
+// Transformers via Speculative Decoding", tree-attention paragraph; the
+// parallel scoring of all draft positions is the "Speculative Sampling"
+// section of the same page).
+//
+// Work decomposition: the key axis of one (b, g) is cut into fixed-size
+// chunks (split-KV); a workgroup owns one chunk and every query row of its
+// row group, so each KV element is read from HBM once and shared by all
+// N * G rows.  Within a workgroup the waves take interleaved 32-key blocks and
+// merge their (max, sum, O) at the end through LDS; chunks merge in
+// attn_combine with an exact log-sum-exp rescale.
+//
+// bf16 MFMA path (v_mfma_f32_16x16x32_bf16):
+//   S^T = K * Q^T : A = 16 keys x 32 dims of K straight from HBM (16-byte
+//                   loads), B = Q^T held in registers for the whole chunk.
+//   The two 16-key halves of a block use the key order
+//     row m of half h  <->  key 8*(m/4) + 4*h + m%4
+//   so that lane (n, q) ends up holding row n's scores for keys 8q..8q+7:
+//   exactly the A operand of the PV product, with no register shuffle.
+//   O += P * V    : B = V^T slice read from a per-wave transposed LDS copy
+//                   (16-byte reads, XOR-swizzled 16-byte columns).
+// fp32 (and any dtype) VALU path: 32 rows x 32 keys tiles through LDS.
+#include <stdlib.h>
+
+#include "spec_common.h"
+#include "spec_internal.h"
+
+namespace specv {
+
+struct AttnArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    float* ws_o;    // [B][Hkv][S][R][D]  unnormalised partial O per split
+    float2* ws_ml;  // [B][Hkv][S][R]     (max in log2 units, sum)
+    const int32_t* prefix_len;
+    const int32_t* parent;
+    int B, N, Hq, Hkv, G, cap, R, nrg, chunk, nsplit_max;
+    int max_keys;      // host bound on L_b + N (sizes the split workspace)
+    float scale_log2;  // softmax scale * log2(e)
+};
+
+// Ancestor-or-self bit masks of every node, built from the parent array.
+__device__ __forceinline__ void build_anc(const AttnArgs& a, int b, uint64_t* s_anc) {
+    const int tid = threadIdx.x;
+    if (tid < a.N) {
+        uint64_t m = 0;
+        int n = tid;
+        for (int s = 0; s < kMaxNodes && n >= 0; ++s) {
+            m |= 1ull << n;
+            n = tree_parent(a.parent, a.N, b, n);
+        }
+        s_anc[tid] = m;
+    }
+}
+
+// Workgroup -> (request, kv head, split, row group).  The row groups of one
+// chunk get consecutive dispatch slots on one XCD (block i runs on XCD i % 8),
+// so they share the chunk through that XCD's L2.
+struct Work {
+    int b, g, s, rg;
+    bool live;
+};
+
+__device__ __forceinline__ Work decode_block(const AttnArgs& a) {
+    const int i = blockIdx.x;
+    const int xcd = i & 7, j = i >> 3;
+    const int unit = (j / a.nrg) * 8 + xcd;
+    Work w;
+    w.rg = j % a.nrg;
+    w.s = unit % a.nsplit_max;
+    const int bg = unit / a.nsplit_max;
+    w.live = bg < a.B * a.Hkv;
+    w.b = w.live ? bg / a.Hkv : 0;
+    w.g = w.live ? bg % a.Hkv : 0;
+    return w;
+}
+
+__device__ __forceinline__ void store_out(void* out, bool bf16, size_t idx, float val) {
+    if (bf16)
+        static_cast<uint16_t*>(out)[idx] = static_cast<uint16_t>(f32_to_bf16_bits(val));
+    else
+        static_cast<float*>(out)[idx] = val;
+}
+
+// XOR swizzle of the four 16-byte key columns of a transposed-V row.
+__device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 3)) & 3; }
+
+// ----------------------------------------------------------------------------
+// MFMA path (bf16).  D in {64, 128}; RT 16-row tiles per wave; WK waves.
+// ----------------------------------------------------------------------------
+template <int D, int RT, int WK>
+__global__ __launch_bounds__(64 * WK) void attn_mfma(AttnArgs a) {
+    constexpr int NC32 = D / 32;  // k-steps of the QK product
+    constexpr int NC16 = D / 16;  // n-tiles of the PV product
+    constexpr int CPR = D / 8;    // 16-byte chunks per cache row
+    constexpr int KG = 64 / CPR;  // key groups of the V load
+    constexpr int KPL = 32 / KG;  // keys per lane in the V load (8 or 4)
+    constexpr int VT_BYTES = D * 64;
+    constexpr int MERGE_BYTES = WK * 16 * RT * D * 4;
+    constexpr int LDS_BYTES = (WK * VT_BYTES > MERGE_BYTES) ? WK * VT_BYTES : MERGE_BYTES;
+    __shared__ __attribute__((aligned(16))) unsigned char s_buf[LDS_BYTES];
+    __shared__ uint64_t s_anc[kMaxNodes];
+    __shared__ float s_m[WK][16 * RT];
+    __shared__ float s_l[WK][16 * RT];
+
+    const Work w = decode_block(a);
+    if (!w.live) return;
+    const int b = w.b, g = w.g;
+    const int L = a.prefix_len[b];
+    const int Tk = L + a.N;
+    if (L < 0 || Tk > a.cap || Tk > a.max_keys) return;  // outside the contract: leave out unwritten
+    const int k0 = w.s * a.chunk;
+    if (k0 >= Tk) return;
+    const int k1 = min(k0 + a.chunk, Tk);
+    const int nsplit = (Tk + a.chunk - 1) / a.chunk;
+
+    build_anc(a, b, s_anc);
+    __syncthreads();
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n16 = lane & 15, q4 = lane >> 4;
+
+    // Query rows owned by this lane (row n16 of each tile) and their masks.
+    uint64_t anc[RT];
+    bf16x8 qf[RT][NC32];
+    const uint16_t* qb = static_cast<const uint16_t*>(a.q);
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        const int r = (w.rg * RT + t) * 16 + n16;
+        const bool valid = r < a.R;
+        const int node = valid ? r / a.G : 0;
+        const int hq = g * a.G + (valid ? r % a.G : 0);
+        anc[t] = valid ? s_anc[node] : ~0ull;
+        const uint16_t* qrow = qb + ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D;
+#pragma unroll
+        for (int c = 0; c < NC32; ++c) {
+            u32x4 u = {0u, 0u, 0u, 0u};
+            if (valid) u = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * q4);
+            qf[t][c] = __builtin_bit_cast(bf16x8, u);
+        }
+    }
+
+    float m_run[RT], l_run[RT];
+    f32x4 o[RT][NC16];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        m_run[t] = -INFINITY;
+        l_run[t] = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC16; ++c) o[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const size_t head = (static_cast<size_t>(b) * a.Hkv + g) * a.cap;
+    const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + head * D;
+    const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + head * D;
+    unsigned char* vt = s_buf + wave * VT_BYTES;
+    const int vch = lane % CPR, vkg = lane / CPR;
+
+    for (int kb = k0 + wave * 32; kb < k1; kb += 32 * WK) {
+        // K: A operand rows in the paired-half key order.
+        u32x4 kf[2][NC32];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int key = kb + 8 * (n16 >> 2) + 4 * h + (n16 & 3);
+            const int row = min(key, Tk - 1);
+#pragma unroll
+            for (int c = 0; c < NC32; ++c)
+                kf[h][c] = *reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(row) * D + 32 * c + 8 * q4);
+        }
+        // V: KPL consecutive keys of one 8-dim chunk per lane.
+        u32x4 vr[KPL];
+#pragma unroll
+        for (int jj = 0; jj < KPL; ++jj) {
+            const int row = min(kb + vkg * KPL + jj, Tk - 1);
+            vr[jj] = *reinterpret_cast<const u32x4*>(vbase + static_cast<size_t>(row) * D + 8 * vch);
+        }
+        // Transpose into LDS: row d holds keys 0..31 of the block.
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int d = 8 * vch + t;
+            const int key0 = vkg * KPL;
+            const int pch = (key0 >> 3) ^ vt_swz(d);
+            unsigned char* dst = vt + d * 64 + pch * 16 + (key0 & 7) * 2;
+            const int sh = 16 * (t & 1);
+            if constexpr (KPL == 8) {
+                u32x4 wv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t lo = (vr[2 * e][t >> 1] >> sh) & 0xFFFFu;
+                    const uint32_t hi = (vr[2 * e + 1][t >> 1] >> sh) & 0xFFFFu;
+                    wv[e] = lo | (hi << 16);
+                }
+                *reinterpret_cast<u32x4*>(dst) = wv;
+            } else {
+                uint2 wv;
+                wv.x = ((vr[0][t >> 1] >> sh) & 0xFFFFu) | (((vr[1][t >> 1] >> sh) & 0xFFFFu) << 16);
+                wv.y = ((vr[2][t >> 1] >> sh) & 0xFFFFu) | (((vr[3][t >> 1] >> sh) & 0xFFFFu) << 16);
+                *reinterpret_cast<uint2*>(dst) = wv;
+            }
+        }
+        wave_lds_sync();
+        // B operand of PV: V[keys 8q..8q+7][d = 16c + n].
+        u32x4 vf[NC16];
+#pragma unroll
+        for (int c = 0; c < NC16; ++c) {
+            const int d = 16 * c + n16;
+            vf[c] = *reinterpret_cast<const u32x4*>(vt + d * 64 + ((q4 ^ vt_swz(d)) * 16));
+        }
+
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            f32x4 st[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < NC32; ++c)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[h][c]), qf[t][c], acc,
+                                                                  0, 0, 0);
+                st[h] = acc;
+            }
+            float s[8];
+            float bm = -INFINITY;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int key = kb + 8 * q4 + 4 * h + ii;
+                    const bool ok = key < k1 && (key < L || ((anc[t] >> (key - L)) & 1ull));
+                    const float x = ok ? st[h][ii] * a.scale_log2 : -INFINITY;
+                    s[4 * h + ii] = x;
+                    bm = fmaxf(bm, x);
+                }
+            bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
+            bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+            const float mn = fmaxf(m_run[t], bm);
+            const float mu = mn == -INFINITY ? 0.f : mn;
+            const float alpha = exp2f(m_run[t] - mu);
+            float rs = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                s[e] = exp2f(s[e] - mu);
+                rs += s[e];
+            }
+            rs += __shfl_xor(rs, 16, kWave);
+            rs += __shfl_xor(rs, 32, kWave);
+            l_run[t] = l_run[t] * alpha + rs;
+            m_run[t] = mn;
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const float ao = __shfl(alpha, 4 * q4 + ii, kWave);
+#pragma unroll
+                for (int c = 0; c < NC16; ++c) o[t][c][ii] *= ao;
+            }
+            u32x4 pp;
+            pp[0] = pack_bf16x2(s[0], s[1]);
+            pp[1] = pack_bf16x2(s[2], s[3]);
+            pp[2] = pack_bf16x2(s[4], s[5]);
+            pp[3] = pack_bf16x2(s[6], s[7]);
+            const bf16x8 pa = __builtin_bit_cast(bf16x8, pp);
+#pragma unroll
+            for (int c = 0; c < NC16; ++c)
+                o[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, vf[c]), o[t][c], 0, 0, 0);
+        }
+        wave_lds_sync();
+    }
+
+    // ---- merge the waves of this workgroup --------------------------------
+    __syncthreads();
+    if (q4 == 0) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            s_m[wave][t * 16 + n16] = m_run[t];
+            s_l[wave][t * 16 + n16] = l_run[t];
+        }
+    }
+    __syncthreads();
+    float* reg = reinterpret_cast<float*>(s_buf);
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int row = t * 16 + 4 * q4 + ii;
+            float M = -INFINITY;
+#pragma unroll
+            for (int x = 0; x < WK; ++x) M = fmaxf(M, s_m[x][row]);
+            const float sc = exp2f(s_m[wave][row] - (M == -INFINITY ? 0.f : M));
+#pragma unroll
+            for (int c = 0; c < NC16; ++c) reg[(wave * 16 * RT + row) * D + 16 * c + n16] = o[t][c][ii] * sc;
+        }
+    __syncthreads();
+
+    const bool bf16_out = true;
+    for (int e = tid; e < 16 * RT * D; e += 64 * WK) {
+        const int row = e / D, d = e % D;
+        const int r = w.rg * RT * 16 + row;
+        if (r >= a.R) continue;
+        float M = -INFINITY;
+#pragma unroll
+        for (int x = 0; x < WK; ++x) M = fmaxf(M, s_m[x][row]);
+        const float Mu = M == -INFINITY ? 0.f : M;
+        float lsum = 0.f, osum = 0.f;
+#pragma unroll
+        for (int x = 0; x < WK; ++x) {
+            lsum += s_l[x][row] * exp2f(s_m[x][row] - Mu);
+            osum += reg[(x * 16 * RT + row) * D + d];
+        }
+        const int node = r / a.G, hq = g * a.G + r % a.G;
+        if (nsplit == 1) {
+            const size_t oi = ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D + d;
+            store_out(a.out, bf16_out, oi, lsum > 0.f ? osum / lsum : 0.f);
+        } else {
+            const size_t pi = (static_cast<size_t>(b) * a.Hkv + g) * a.nsplit_max + w.s;
+            a.ws_o[(pi * a.R + r) * D + d] = osum;
+            if (d == 0) a.ws_ml[pi * a.R + r] = make_float2(M, lsum);
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// VALU path: 32 query rows x 32-key tiles staged in LDS, fp32 arithmetic.
+// ----------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ float load_elem(const T* p, size_t i);
+template <>
+__device__ __forceinline__ float load_elem<float>(const float* p, size_t i) {
+    return p[i];
+}
+template <>
+__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, size_t i) {
+    return bf16_bits_to_f32(p[i]);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_valu(AttnArgs a) {
+    constexpr int DP = D + 1;
+    __shared__ float s_q[32][DP];
+    __shared__ float s_k[32][DP];
+    __shared__ float s_v[32][DP];
+    __shared__ float s_p[32][33];
+    __shared__ uint64_t s_anc[kMaxNodes];
+
+    const Work w = decode_block(a);
+    if (!w.live) return;
+    const int b = w.b, g = w.g;
+    const int L = a.prefix_len[b];
+    const int Tk = L + a.N;
+    if (L < 0 || Tk > a.cap || Tk > a.max_keys) return;  // outside the contract: leave out unwritten
+    const int k0 = w.s * a.chunk;
+    if (k0 >= Tk) return;
+    const int k1 = min(k0 + a.chunk, Tk);
+    const int nsplit = (Tk + a.chunk - 1) / a.chunk;
+
+    build_anc(a, b, s_anc);
+    const int tid = threadIdx.x;
+    const T* qp = static_cast<const T*>(a.q);
+    for (int e = tid; e < 32 * D; e += 256) {
+        const int lr = e / D, d = e % D;
+        const int r = w.rg * 32 + lr;
+        float x = 0.f;
+        if (r < a.R) {
+            const int node = r / a.G, hq = g * a.G + r % a.G;
+            x = load_elem(qp, ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D + d);
+        }
+        s_q[lr][d] = x;
+    }
+    __syncthreads();
+
+    const int sr = tid >> 3, sk = tid & 7;
+    const int r = w.rg * 32 + sr;
+    const bool rvalid = r < a.R;
+    const uint64_t anc = rvalid ? s_anc[r / a.G] : ~0ull;
+    float m_run = -INFINITY, l_run = 0.f;
+    float o[D / 8];
+#pragma unroll
+    for (int j = 0; j < D / 8; ++j) o[j] = 0.f;
+
+    const size_t head = (static_cast<size_t>(b) * a.Hkv + g) * a.cap;
+    const T* kp = static_cast<const T*>(a.k) + head * D;
+    const T* vp = static_cast<const T*>(a.v) + head * D;
+
+    for (int kb = k0; kb < k1; kb += 32) {
+        __syncthreads();
+        for (int e = tid; e < 32 * D; e += 256) {
+            const int kk = e / D, d = e % D;
+            const size_t row = static_cast<size_t>(min(kb + kk, Tk - 1));
+            s_k[kk][d] = load_elem(kp, row * D + d);
+            s_v[kk][d] = load_elem(vp, row * D + d);
+        }
+        __syncthreads();
+        float s[4];
+        float bm = -INFINITY;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int kk = sk + 8 * jj;
+            const int key = kb + kk;
+            float dot = 0.f;
+#pragma unroll 8
+            for (int d = 0; d < D; ++d) dot = fmaf(s_q[sr][d], s_k[kk][d], dot);
+            const bool ok = key < k1 && (key < L || ((anc >> (key - L)) & 1ull));
+            s[jj] = ok ? dot * a.scale_log2 : -INFINITY;
+            bm = fmaxf(bm, s[jj]);
+        }
+        bm = fmaxf(bm, __shfl_xor(bm, 1, kWave));
+        bm = fmaxf(bm, __shfl_xor(bm, 2, kWave));
+        bm = fmaxf(bm, __shfl_xor(bm, 4, kWave));
+        const float mn = fmaxf(m_run, bm);
+        const float mu = mn == -INFINITY ? 0.f : mn;
+        const float alpha = exp2f(m_run - mu);
+        float rs = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const float p = exp2f(s[jj] - mu);
+            s_p[sr][sk + 8 * jj] = p;
+            rs += p;
+        }
+        rs += __shfl_xor(rs, 1, kWave);
+        rs += __shfl_xor(rs, 2, kWave);
+        rs += __shfl_xor(rs, 4, kWave);
+        l_run = l_run * alpha + rs;
+        m_run = mn;
+#pragma unroll
+        for (int j = 0; j < D / 8; ++j) o[j] *= alpha;
+        __syncthreads();
+        for (int kk = 0; kk < 32; ++kk) {
+            const float p = s_p[sr][kk];
+#pragma unroll
+            for (int j = 0; j < D / 8; ++j) o[j] = fmaf(p, s_v[kk][sk + 8 * j], o[j]);
+        }
+    }
+    if (!rvalid) return;
+    const int node = r / a.G, hq = g * a.G + r % a.G;
+    const bool bf16_out = sizeof(T) == 2;
+    if (nsplit == 1) {
+        const size_t ob = ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D;
+#pragma unroll
+        for (int j = 0; j < D / 8; ++j) store_out(a.out, bf16_out, ob + sk + 8 * j, l_run > 0.f ? o[j] / l_run : 0.f);
+    } else {
+        const size_t pi = (static_cast<size_t>(b) * a.Hkv + g) * a.nsplit_max + w.s;
+#pragma unroll
+        for (int j = 0; j < D / 8; ++j) a.ws_o[(pi * a.R + r) * D + sk + 8 * j] = o[j];
+        if (sk == 0) a.ws_ml[pi * a.R + r] = make_float2(m_run, l_run);
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Split combine: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// One wavefront per (request, kv head, query row).
+// ----------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int bf16_out) {
+    const int lane = threadIdx.x & 63;
+    const long id = static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (id >= static_cast<long>(a.B) * a.Hkv * a.R) return;
+    const int r = static_cast<int>(id % a.R);
+    const int bg = static_cast<int>(id / a.R);
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
+    const int L = a.prefix_len[b];
+    const int Tk = L + a.N;
+    if (L < 0 || Tk > a.cap || Tk > a.max_keys) return;  // outside the contract: leave out unwritten
+    const int nsplit = (Tk + a.chunk - 1) / a.chunk;
+    if (nsplit <= 1) return;
+    const size_t base = static_cast<size_t>(bg) * a.nsplit_max;
+    float M = -INFINITY;
+    for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, a.ws_ml[(base + s) * a.R + r].x);
+    M = wave_max(M);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    float lsum = 0.f;
+    for (int s = lane; s < nsplit; s += 64) {
+        const float2 ml = a.ws_ml[(base + s) * a.R + r];
+        lsum += ml.y * exp2f(ml.x - Mu);
+    }
+    lsum = wave_sum(lsum);
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const int node = r / a.G, hq = g * a.G + r % a.G;
+    const size_t ob = ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D;
+    for (int d = lane; d < D; d += 64) {
+        float acc = 0.f;
+        for (int s = 0; s < nsplit; ++s) {
+            const float wgt = exp2f(a.ws_ml[(base + s) * a.R + r].x - Mu);
+            acc += wgt * a.ws_o[((base + s) * a.R + r) * D + d];
+        }
+        store_out(a.out, bf16_out != 0, ob + d, acc * inv);
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Host side
+// ----------------------------------------------------------------------------
+static int env_chunk_override() {
+    static int v = -1;
+    if (v < 0) {
+        const char* s = getenv("SPEC_VERIFY_KV_CHUNK");
+        v = s ? atoi(s) : 0;
+        if (v < 0) v = 0;
+    }
+    return v;
+}
+
+AttnPlan plan_attn(const spec_attn_desc& d, int max_prefix_len) {
+    AttnPlan p{};
+    const int G = d.num_q_heads / d.num_kv_heads;
+    p.rows = d.num_nodes * G;
+    int unit_keys;
+    if (d.dtype == SPEC_BF16) {
+        p.mfma = true;
+        if (p.rows <= 64) {
+            p.row_tiles = (p.rows + 15) / 16;
+            p.row_groups = 1;
+        } else {
+            p.row_tiles = 4;
+            p.row_groups = (p.rows + 63) / 64;
+        }
+        p.waves = p.row_tiles <= 2 ? 4 : 2;
+        unit_keys = 32 * p.waves;
+    } else {
+        p.mfma = false;
+        p.row_tiles = 0;
+        p.row_groups = (p.rows + 31) / 32;
+        p.waves = 4;
+        unit_keys = 32;
+    }
+    const long keys_max = static_cast<long>(max_prefix_len) + d.num_nodes;
+    const long units = static_cast<long>(d.batch) * d.num_kv_heads * p.row_groups;
+    const long want = units >= 1024 ? 1 : (1024 + units - 1) / units;
+    long chunk = (keys_max + want - 1) / want;
+    const long min_chunk = env_chunk_override() > 0 ? env_chunk_override() : 256;
+    if (chunk < min_chunk) chunk = min_chunk;
+    chunk = (chunk + unit_keys - 1) / unit_keys * unit_keys;
+    p.chunk = static_cast<int>(chunk);
+    p.nsplit_max = static_cast<int>((keys_max + chunk - 1) / chunk);
+    p.max_keys = static_cast<int>(keys_max);
+    if (p.nsplit_max < 1) p.nsplit_max = 1;
+    if (p.nsplit_max > 1) {
+        const size_t parts = static_cast<size_t>(d.batch) * d.num_kv_heads * p.nsplit_max * p.rows;
+        p.ws_bytes = align_up(parts * d.head_dim * sizeof(float), 256) + align_up(parts * sizeof(float2), 256);
+    } else {
+        p.ws_bytes = 0;
+    }
+    return p;
+}
+
+template <int D>
+static void launch_mfma_rt(const AttnPlan& p, const AttnArgs& a, dim3 grid, hipStream_t st) {
+    switch (p.row_tiles) {
+        case 1: hipLaunchKernelGGL((attn_mfma<D, 1, 4>), grid, dim3(256), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((attn_mfma<D, 2, 4>), grid, dim3(256), 0, st, a); break;
+        case 3: hipLaunchKernelGGL((attn_mfma<D, 3, 2>), grid, dim3(128), 0, st, a); break;
+        default: hipLaunchKernelGGL((attn_mfma<D, 4, 2>), grid, dim3(128), 0, st, a); break;
+    }
+}
+
+int launch_verify_attn(const spec_attn_desc& d, const AttnPlan& p, const void* q, const void* k,
+                       const void* v, const int32_t* prefix_len, const int32_t* parent, void* out,
+                       void* workspace, hipStream_t stream) {
+    AttnArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.prefix_len = prefix_len;
+    a.parent = parent;
+    a.B = d.batch;
+    a.N = d.num_nodes;
+    a.Hq = d.num_q_heads;
+    a.Hkv = d.num_kv_heads;
+    a.G = d.num_q_heads / d.num_kv_heads;
+    a.cap = d.kv_capacity;
+    a.R = p.rows;
+    a.nrg = p.row_groups;
+    a.chunk = p.chunk;
+    a.nsplit_max = p.nsplit_max;
+    a.max_keys = p.max_keys;
+    const float scale = d.softmax_scale > 0.f ? d.softmax_scale : 1.0f / sqrtf(static_cast<float>(d.head_dim));
+    a.scale_log2 = scale * 1.4426950408889634f;
+    if (p.nsplit_max > 1) {
+        const size_t parts = static_cast<size_t>(d.batch) * d.num_kv_heads * p.nsplit_max * p.rows;
+        a.ws_o = static_cast<float*>(workspace);
+        a.ws_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) +
+                                            align_up(parts * d.head_dim * sizeof(float), 256));
+    } else {
+        a.ws_o = nullptr;
+        a.ws_ml = nullptr;
+    }
+    const long units = static_cast<long>(d.batch) * d.num_kv_heads * p.nsplit_max;
+    const long units_pad = (units + 7) / 8 * 8;
+    const dim3 grid(static_cast<unsigned>(units_pad * p.row_groups));
+    if (p.mfma) {
+        if (d.head_dim == 128)
+            launch_mfma_rt<128>(p, a, grid, stream);
+        else
+            launch_mfma_rt<64>(p, a, grid, stream);
+    } else if (d.dtype == SPEC_F32) {
+        if (d.head_dim == 128)
+            hipLaunchKernelGGL((attn_valu<float, 128>), grid, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((attn_valu<float, 64>), grid, dim3(256), 0, stream, a);
+    } else {
+        if (d.head_dim == 128)
+            hipLaunchKernelGGL((attn_valu<uint16_t, 128>), grid, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((attn_valu<uint16_t, 64>), grid, dim3(256), 0, stream, a);
+    }
+    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+    if (p.nsplit_max > 1) {
+        const long rows = static_cast<long>(d.batch) * d.num_kv_heads * p.rows;
+        const dim3 cgrid(static_cast<unsigned>((rows + 3) / 4));
+        const int bf16_out = d.dtype == SPEC_BF16;
+        if (d.head_dim == 128)
+            hipLaunchKernelGGL((attn_combine<128>), cgrid, dim3(256), 0, stream, a, bf16_out);
+        else
+            hipLaunchKernelGGL((attn_combine<64>), cgrid, dim3(256), 0, stream, a, bf16_out);
+        if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+    }
+    return SPEC_OK;
+}
+
+}  // namespace specv

@@ -1,0 +1,55 @@
+// Host-side plumbing shared by the entry points and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/spec_verify.h"
+
+namespace specv {
+
+// Execution plan of spec_verify_attn for one descriptor and prefix bound.
+struct AttnPlan {
+    bool mfma;       // bf16 MFMA path (else the VALU path)
+    int rows;        // R = N * (Hq / Hkv): query rows per (request, kv head)
+    int row_tiles;   // MFMA: 16-row tiles per wave
+    int waves;       // wavefronts per workgroup
+    int row_groups;  // workgroups sharing one KV chunk (different query rows)
+    int chunk;       // keys per split
+    int nsplit_max;  // splits of the longest request
+    int max_keys;    // max_prefix_len + N
+    size_t ws_bytes; // split partials (0 when one split covers every request)
+};
+
+AttnPlan plan_attn(const spec_attn_desc& d, int max_prefix_len);
+
+int launch_verify_attn(const spec_attn_desc& d, const AttnPlan& plan, const void* q, const void* k,
+                       const void* v, const int32_t* prefix_len, const int32_t* parent, void* out,
+                       void* workspace, hipStream_t stream);
+
+struct AcceptPlan {
+    int chunk;   // vocabulary entries per chunk
+    int nchunk;
+    size_t off_rowstat, off_dec, off_cstat, ws_bytes;
+};
+
+AcceptPlan plan_accept(int B, int N, int V);
+
+int launch_accept(int rule, int B, int N, int V, const float* logits, const float* draft,
+                  const int32_t* tokens, const int32_t* parent, const float* u_accept,
+                  const float* u_sample, float temperature, float epsilon, float delta,
+                  int32_t* accept_len, int32_t* path, int32_t* out_tokens, void* workspace,
+                  const AcceptPlan& plan, hipStream_t stream);
+
+int launch_commit(const spec_attn_desc& d, void* k, void* v, int32_t* prefix_len, const int32_t* path,
+                  const int32_t* accept_len, hipStream_t stream);
+
+int launch_positions(int B, int N, const int32_t* prefix_len, const int32_t* parent, int32_t* pos,
+                     hipStream_t stream);
+
+int launch_validate(int B, int N, const int32_t* parent, int32_t* status, hipStream_t stream);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace specv

@@ -1,0 +1,126 @@
+"""The C ABI on the CPU: the library loads, exports every entry point that
+include/spec_verify.h declares (with a binding signature for each), and
+rejects invalid arguments with the documented status before launching
+anything (no GPU is touched by these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import speculative_decoding_verification_tree_amd as sv
+from speculative_decoding_verification_tree_amd._native import AttnDesc, SIGNATURES
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE = 0, -1, -2, -3
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == 9, names
+    lib = sv.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in SIGNATURES, n
+    assert set(SIGNATURES) == set(names)
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(AttnDesc) == 32
+
+
+def _desc(**kw):
+    d = dict(batch=1, num_nodes=6, num_q_heads=32, num_kv_heads=8, head_dim=128, kv_capacity=2054, dtype=1,
+             softmax_scale=0.0)
+    d.update(kw)
+    return AttnDesc(**d)
+
+
+def _attn(desc, mpl=2048, ws_bytes=1 << 30, ws=FAKE):
+    return sv.lib().spec_verify_attn(ctypes.byref(desc) if desc is not None else None, mpl, FAKE, FAKE, FAKE,
+                                     FAKE, None, FAKE, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(num_nodes=0), EINVAL),
+    (dict(num_nodes=65), EINVAL),
+    (dict(num_q_heads=30), EINVAL),
+    (dict(num_kv_heads=0), EINVAL),
+    (dict(head_dim=96), EUNSUPPORTED),
+    (dict(head_dim=0), EINVAL),
+    (dict(dtype=7), EUNSUPPORTED),
+    (dict(kv_capacity=2053), EINVAL),
+    (dict(batch=-1), EINVAL),
+    (dict(softmax_scale=float("nan")), EINVAL),
+])
+def test_attention_argument_errors(kw, want):
+    assert _attn(_desc(**kw)) == want
+
+
+def test_attention_null_and_workspace_errors():
+    lib = sv.lib()
+    assert _attn(None) == EINVAL
+    d = _desc()
+    need = lib.spec_verify_attn_workspace_bytes(ctypes.byref(d), 2048)
+    assert need > 0
+    assert _attn(d, ws_bytes=need - 1) == EWORKSPACE
+    assert _attn(d, ws=None) == EWORKSPACE
+    assert lib.spec_verify_attn(ctypes.byref(d), 2048, None, FAKE, FAKE, FAKE, None, FAKE, FAKE, need, None) == EINVAL
+    assert _attn(d, mpl=-1) == EINVAL
+    # empty batch: nothing to do, nothing launched
+    assert _attn(_desc(batch=0)) == OK
+    assert lib.spec_verify_attn_workspace_bytes(ctypes.byref(_desc(head_dim=96)), 10) == 0
+
+
+def _rej(B=2, N=6, V=1000, T=1.0, ws_bytes=1 << 30, ws=FAKE, draft=FAKE, us=FAKE):
+    return sv.lib().spec_accept_reject(B, N, V, FAKE, draft, FAKE, None, FAKE, us, T, FAKE, FAKE, FAKE, ws,
+                                       ws_bytes, None)
+
+
+def _typ(B=2, N=6, V=1000, T=1.0, eps=0.1, delta=0.2, ws_bytes=1 << 30):
+    return sv.lib().spec_accept_typical(B, N, V, FAKE, FAKE, None, T, eps, delta, FAKE, FAKE, FAKE, FAKE, ws_bytes,
+                                        None)
+
+
+def test_accept_argument_errors():
+    lib = sv.lib()
+    assert _rej(V=0) == EINVAL
+    assert _rej(N=0) == EINVAL
+    assert _rej(N=65) == EINVAL
+    assert _rej(B=-1) == EINVAL
+    assert _rej(T=-0.5) == EINVAL
+    assert _rej(T=float("nan")) == EINVAL
+    assert _rej(T=float("inf")) == EINVAL
+    assert _rej(draft=None) == EINVAL
+    assert _rej(us=None) == EINVAL
+    need = lib.spec_accept_workspace_bytes(2, 6, 1000)
+    assert need > 0
+    assert _rej(ws_bytes=need - 1) == EWORKSPACE
+    assert _rej(ws=None) == EWORKSPACE
+    assert _typ(eps=-1.0) == EINVAL
+    assert _typ(delta=float("nan")) == EINVAL
+    assert _typ(T=-1.0) == EINVAL
+    assert _typ(ws_bytes=lib.spec_accept_workspace_bytes(2, 6, 1000) - 8) == EWORKSPACE
+    assert _rej(B=0) == OK and _typ(B=0) == OK
+    assert lib.spec_accept_workspace_bytes(0, 6, 10) == 0
+
+
+def test_commit_and_helper_errors():
+    lib = sv.lib()
+    assert lib.spec_commit_kv(ctypes.byref(_desc(head_dim=80)), FAKE, FAKE, FAKE, FAKE, FAKE, None) == EUNSUPPORTED
+    assert lib.spec_commit_kv(ctypes.byref(_desc()), None, FAKE, FAKE, FAKE, FAKE, None) == EINVAL
+    assert lib.spec_commit_kv(ctypes.byref(_desc(batch=0)), None, None, None, None, None, None) == OK
+    assert lib.spec_tree_positions(2, 0, FAKE, None, FAKE, None) == EINVAL
+    assert lib.spec_tree_positions(2, 4, None, None, FAKE, None) == EINVAL
+    assert lib.spec_validate_tree(2, 65, FAKE, FAKE, None) == EINVAL
+    assert lib.spec_validate_tree(2, 4, None, FAKE, None) == EINVAL
+    for rc in (0, -1, -2, -3, -4, 5):
+        assert sv.status_string(rc)

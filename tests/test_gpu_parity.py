@@ -1,0 +1,185 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs, for the five workloads (reduced sizes with every output
+row, and full sizes with sampled rows) and their edge cases."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import speculative_decoding_verification_tree_amd as sv
+from workloads import generate, scaled
+from tests.gpu_helpers import (announce, check_accept, check_attention, oracle_accept, run_accept, run_attention)
+
+pytestmark = pytest.mark.gpu
+
+
+def _attn_all_rows(w, what):
+    announce(f"attention all rows: {what} B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} D={w.D} "
+             f"L={w.prefix_len.min()}..{w.prefix_len.max()} {w.dtype}")
+    gpu = run_attention(w)
+    ref = oracle.tree_attn(w.q, w.k_cache, w.v_cache, w.prefix_len, None if w.is_chain else w.parent, w.dtype)
+    return check_attention(gpu, ref, what)
+
+
+def _attn_sampled(w, what, nrows=160, seed=0):
+    announce(f"attention sampled rows: {what} B={w.B} N={w.N} Hq={w.Hq} L<={w.max_prefix_len}")
+    rng = np.random.default_rng(seed)
+    rows = np.stack([rng.integers(w.B, size=nrows), rng.integers(w.N, size=nrows), rng.integers(w.Hq, size=nrows)], 1)
+    rows[0] = [0, 0, 0]
+    rows[1] = [w.B - 1, w.N - 1, w.Hq - 1]
+    rows = rows.astype(np.int32)
+    gpu = run_attention(w)
+    ref = oracle.tree_attn(w.q, w.k_cache, w.v_cache, w.prefix_len, None if w.is_chain else w.parent, w.dtype,
+                           rows=rows)
+    return check_attention(gpu[rows[:, 0], rows[:, 1], rows[:, 2]], ref, what)
+
+
+# --------------------------------------------------------------- attention
+@pytest.mark.parametrize("cid,over", [
+    (1, {}),
+    (2, {}),
+    (3, dict(batch=2, prefix_len=700)),
+    (4, dict(batch=6, prefix_len=(100, 1500))),
+    (5, dict(batch=2, prefix_len=1000)),
+])
+def test_attention_all_rows(cid, over):
+    w = generate(scaled(cid, **over), with_accept=False)
+    _attn_all_rows(w, f"cfg{cid} {over}")
+
+
+@pytest.mark.parametrize("cid", [3, 4, 5])
+def test_attention_full_size_sampled(cid):
+    w = generate(scaled(cid), with_accept=False, poison=False)
+    _attn_sampled(w, f"cfg{cid} full size", seed=cid)
+
+
+@pytest.mark.parametrize("over", [
+    dict(drafts=0),                                   # N = 1: plain decode
+    dict(prefix_len=0),                               # empty prefix
+    dict(prefix_len=250),                             # keys = 256 - 0: chunk edge
+    dict(prefix_len=251),
+    dict(prefix_len=505),
+    dict(head_dim=64),                                # D = 64 MFMA
+    dict(num_q_heads=8, num_kv_heads=8),              # MHA chain, R = 6
+    dict(num_q_heads=64, num_kv_heads=8, drafts=7),   # R = 64
+    dict(num_q_heads=8, num_kv_heads=1, drafts=9),    # R = 80: two row groups
+    dict(dtype="f32", head_dim=128),                  # fp32 VALU, D = 128
+])
+def test_attention_edge_cases(over):
+    base = dict(batch=2, prefix_len=300)
+    base.update(over)
+    w = generate(scaled(2, **base), with_accept=False)
+    _attn_all_rows(w, f"edge {over}")
+
+
+@pytest.mark.parametrize("over", [
+    dict(nodes=64, max_depth=63, prefix_len=37),      # max nodes, deep tree
+    dict(nodes=2, prefix_len=5),
+    dict(dtype="f32", head_dim=64, nodes=20),         # fp32 tree
+    dict(num_q_heads=8, num_kv_heads=8, nodes=33, head_dim=64),
+])
+def test_attention_tree_edge_cases(over):
+    base = dict(batch=3, prefix_len=(0, 600), num_q_heads=16, num_kv_heads=4)
+    base.update(over)
+    w = generate(scaled(5, **base), with_accept=False)
+    _attn_all_rows(w, f"tree edge {over}")
+
+
+def test_attention_empty_batch():
+    announce("attention B=0")
+    q = torch.empty(0, 6, 32, 128, dtype=torch.bfloat16, device="cuda")
+    k = torch.empty(0, 8, 16, 128, dtype=torch.bfloat16, device="cuda")
+    pl = torch.empty(0, dtype=torch.int32, device="cuda")
+    out = sv.spec_verify_attn(q, k, k, pl, None, 0)
+    assert out.shape == q.shape
+
+
+# --------------------------------------------------------------- acceptance
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_accept_full_size(cid):
+    w = generate(scaled(cid), with_attention=False)
+    announce(f"accept cfg{cid} full: B={w.B} N={w.N} V={w.V} rule={w.rule} T={w.temperature}")
+    gpu = run_accept(w)
+    ref = oracle_accept(w)
+    excl = check_accept(w, gpu, ref)
+    announce(f"  near-tie requests excluded from the bit-exact check: {excl} of {w.B}")
+    # draws over V ~ 1e5 tokens land within 1e-6 of a CDF boundary a few % of the time
+    assert excl <= max(2, w.B // 10), excl
+
+
+@pytest.mark.parametrize("cid,over", [
+    (2, dict(batch=40, temperature=0.0)),                         # greedy rejection rule
+    (3, dict(batch=8, temperature=0.0)),                          # greedy typical rule
+    (3, dict(batch=8, epsilon=0.0, delta=0.0)),                   # everything passes: stop at a leaf
+    (3, dict(batch=8, epsilon=1.0, delta=1.0, temperature=3.0)),  # nearly nothing passes
+    (1, dict(batch=64, vocab=1001, drafts=6)),                    # V % 4 != 0
+    (1, dict(batch=16, vocab=1, drafts=3)),                       # V = 1
+    (1, dict(batch=32, drafts=0)),                                # N = 1: bonus only
+    (5, dict(batch=6, vocab=5000, nodes=64, max_depth=63)),       # deep tree, max N
+    (4, dict(batch=32, vocab=20000, draft_noise=[0.0])),          # q == p: all accepted
+])
+def test_accept_edge_cases(cid, over):
+    w = generate(scaled(cid, **over), with_attention=False)
+    announce(f"accept edge cfg{cid} {over}")
+    gpu = run_accept(w)
+    ref = oracle_accept(w)
+    excl = check_accept(w, gpu, ref)
+    announce(f"  near-tie requests excluded from the bit-exact check: {excl} of {w.B}")
+    assert excl <= max(2, w.B // 10), excl
+    if over.get("draft_noise") == [0.0]:
+        # draft == target: every draft passes (p_draft = p_target => ratio 1)
+        assert (gpu["accept_len"] == w.N - 1).sum() >= w.B - 1
+
+
+def test_accept_empty_batch():
+    announce("accept B=0")
+    lg = torch.empty(0, 4, 100, device="cuda")
+    tk = torch.empty(0, 4, dtype=torch.int32, device="cuda")
+    al, _, _ = sv.spec_accept_typical(lg, tk, None, 1.0, 0.1, 0.1, workspace=torch.empty(1, dtype=torch.uint8,
+                                                                                              device="cuda"))
+    assert al.numel() == 0
+
+
+# --------------------------------------------------------------- commit & helpers
+@pytest.mark.parametrize("cid,over", [
+    (5, dict(batch=4, prefix_len=(0, 300), vocab=3000)),
+    (4, dict(batch=8, prefix_len=(10, 200), vocab=3000)),
+    (1, dict(batch=1)),
+])
+def test_commit_matches_oracle(cid, over):
+    w = generate(scaled(cid, **over))
+    announce(f"commit cfg{cid} {over}")
+    gpu_acc = run_accept(w)
+    k = w.k_cache.copy()
+    v = w.v_cache.copy()
+    from tests.gpu_helpers import dev_kv
+    kd, vd = dev_kv(k, w.dtype), dev_kv(v, w.dtype)
+    pl = torch.from_numpy(w.prefix_len.copy()).cuda()
+    path = torch.from_numpy(gpu_acc["path"]).cuda()
+    al = torch.from_numpy(gpu_acc["accept_len"]).cuda()
+    sv.spec_commit_kv(kd, vd, pl, path, al)
+    torch.cuda.synchronize()
+    pl_ref = oracle.commit(k, v, w.prefix_len.copy(), gpu_acc["path"], gpu_acc["accept_len"])
+    np.testing.assert_array_equal(pl.cpu().numpy(), pl_ref)
+    view = np.int16 if w.dtype == "bf16" else np.float32
+    kk = kd.view(torch.int16).cpu().numpy() if w.dtype == "bf16" else kd.cpu().numpy()
+    vv = vd.view(torch.int16).cpu().numpy() if w.dtype == "bf16" else vd.cpu().numpy()
+    np.testing.assert_array_equal(kk.view(np.uint8), k.view(view).view(np.uint8))
+    np.testing.assert_array_equal(vv.view(np.uint8), v.view(view).view(np.uint8))
+
+
+def test_positions_and_validate():
+    announce("positions / validate")
+    w = generate(scaled(5, batch=5, prefix_len=(0, 100), vocab=10), with_attention=False, with_accept=False)
+    par = torch.from_numpy(w.parent).cuda()
+    pl = torch.from_numpy(w.prefix_len).cuda()
+    pos = sv.spec_tree_positions(pl, par, w.N).cpu().numpy()
+    depth = np.zeros((w.B, w.N), int)
+    for i in range(1, w.N):
+        depth[:, i] = depth[np.arange(w.B), w.parent[:, i]] + 1
+    np.testing.assert_array_equal(pos, w.prefix_len[:, None] + depth)
+    bad = w.parent.copy()
+    bad[1, 7] = 9
+    bad[3, 0] = 0
+    st = sv.spec_validate_tree(torch.from_numpy(bad).cuda()).cpu().numpy()
+    np.testing.assert_array_equal(st, [0, 8, 0, 1, 0])
