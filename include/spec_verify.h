@@ -62,7 +62,9 @@ typedef struct spec_attn_desc {
 } spec_attn_desc;
 
 /* Workspace bytes spec_verify_attn needs for this shape and prefix bound
- * (split-KV partial results).  Returns 0 for an invalid descriptor. */
+ * (split-KV partial results).  Returns 0 for an invalid descriptor or when no
+ * workspace is needed (one KV split covers every request).  Contents need no
+ * initialisation. */
 size_t spec_verify_attn_workspace_bytes(const spec_attn_desc* desc, int32_t max_prefix_len);
 
 /* Tree-verify attention (the parallel scoring pass of the verification step:
@@ -85,7 +87,9 @@ int spec_verify_attn(const spec_attn_desc* desc, int32_t max_prefix_len, const v
                      const int32_t* parent, void* out, void* workspace, size_t workspace_bytes,
                      void* stream);
 
-/* Workspace bytes for either acceptance entry point.  0 for invalid sizes. */
+/* Workspace bytes for either acceptance entry point (per-chunk statistics;
+ * contents need no initialisation).  0 for invalid sizes.  vocab <= 8388608,
+ * batch <= 65535. */
 size_t spec_accept_workspace_bytes(int32_t batch, int32_t num_nodes, int32_t vocab);
 
 /* Rejection-rule acceptance ("Speculative Decoding" and "Speculative

@@ -5,7 +5,8 @@ arguments: it checks that the tensors are contiguous device tensors of the
 right dtype, passes their data pointers and the current HIP stream, and raises
 on a non-zero status.  All arithmetic runs in the HIP kernels.  Output and
 workspace tensors may be passed in (no allocation) or are created with
-``torch.empty`` when omitted.
+``torch.empty`` (outputs) / ``torch.zeros`` (workspaces, whose completion
+counters must start at zero) when omitted.
 """
 import ctypes
 
@@ -80,7 +81,7 @@ def spec_verify_attn(q, k_cache, v_cache, prefix_len, parent, max_prefix_len, ou
     _dev(out, "out", q.dtype)
     need = spec_verify_attn_workspace_bytes(desc, max_prefix_len)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)  # counters start at zero
     nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = _native.lib().spec_verify_attn(ctypes.byref(desc), int(max_prefix_len), _ptr(q), _ptr(k_cache),
                                         _ptr(v_cache), _ptr(prefix_len), _ptr(parent), _ptr(out),
@@ -117,8 +118,8 @@ def spec_accept_reject(target_logits, draft_probs, tokens, parent, u_accept, u_s
     _dev(u_sample, "u_sample", torch.float32)
     accept_len, path, out_tokens = _accept_outputs(B, N, target_logits.device, accept_len, path, out_tokens)
     if workspace is None:
-        workspace = torch.empty(max(spec_accept_workspace_bytes(B, N, V), 1), dtype=torch.uint8,
-                                device=target_logits.device)
+        workspace = torch.zeros(max(spec_accept_workspace_bytes(B, N, V), 1), dtype=torch.uint8,
+                                device=target_logits.device)  # counters start at zero
     rc = _native.lib().spec_accept_reject(B, N, V, _ptr(target_logits), _ptr(draft_probs), _ptr(tokens),
                                           _ptr(parent), _ptr(u_accept), _ptr(u_sample), float(temperature),
                                           _ptr(accept_len), _ptr(path), _ptr(out_tokens), _ptr(workspace),
@@ -136,8 +137,8 @@ def spec_accept_typical(target_logits, tokens, parent, temperature, epsilon, del
     _dev(parent, "parent", torch.int32)
     accept_len, path, out_tokens = _accept_outputs(B, N, target_logits.device, accept_len, path, out_tokens)
     if workspace is None:
-        workspace = torch.empty(max(spec_accept_workspace_bytes(B, N, V), 1), dtype=torch.uint8,
-                                device=target_logits.device)
+        workspace = torch.zeros(max(spec_accept_workspace_bytes(B, N, V), 1), dtype=torch.uint8,
+                                device=target_logits.device)  # counters start at zero
     rc = _native.lib().spec_accept_typical(B, N, V, _ptr(target_logits), _ptr(tokens), _ptr(parent),
                                            float(temperature), float(epsilon), float(delta), _ptr(accept_len),
                                            _ptr(path), _ptr(out_tokens), _ptr(workspace), workspace.numel(),

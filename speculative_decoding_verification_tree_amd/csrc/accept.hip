@@ -11,19 +11,22 @@
 // token is the greedy one.  Over a tree the output is the longest accepted
 // root path.
 //
-// Kernels, in stream order:
-//   accept_rowstats  grid (chunks, N, B): for every node row that has
-//                    children, per vocabulary chunk: max logit (+ lowest
-//                    argmax), sum exp((l - max)/T) and sum t*exp(t) (entropy)
-//   accept_decide    grid B, one wavefront: combine the chunk statistics,
-//                    run every node's test in fp64 from the gathered logit and
-//                    draft probability, pick the stop node and write path /
-//                    accepted tokens; decide what the last token needs
-//   accept_chunks    grid (chunks, B): per chunk of the stop row, the residual
-//                    mass, the bonus mass or the argmax
-//   accept_select    grid B: pick the chunk holding u * total by an ordered
-//                    scan of the chunk masses, then the token by a block scan
-//                    inside that chunk (ascending token ids)
+// Three launches per call; kernel boundaries are the only cross-workgroup
+// synchronisation (a device-scope fence inside a kernel costs an L2 write-back
+// and invalidate on this chip):
+//   accept_rowstats grid (chunks, N, B): every node row with children, per
+//                   vocabulary chunk: max logit (+ lowest argmax),
+//                   sum exp((l - max)/T) and sum t*exp(t) (entropy).
+//   accept_sample   grid (chunks, B): every workgroup combines the chunk
+//                   statistics of its request and runs the node tests (fp64,
+//                   from the gathered logit and draft probability) -- cheap
+//                   and identical in every workgroup, so no workgroup waits
+//                   for another; chunk 0 writes the path, the accepted tokens
+//                   and the decision.  Then each workgroup reduces its chunk
+//                   of the stop row: residual mass, bonus mass or argmax.
+//   accept_select   grid B: scan the chunk masses in token order, find the
+//                   chunk that holds u * total and the token inside it (block
+//                   scan, ascending token ids).
 #include "spec_common.h"
 #include "spec_internal.h"
 
@@ -46,7 +49,7 @@ struct Decision {  // per request
 };
 
 struct ChunkStat {  // per (request, chunk) of the stop row
-    double m1;      // residual mass | bonus mass relative to M
+    double m1;      // residual mass | bonus mass relative to the chunk max
     double m2;      // plain target mass (residual fallback)
     float M;        // chunk max logit (bonus / argmax)
     int arg;
@@ -70,8 +73,9 @@ struct AcceptArgs {
 };
 
 constexpr int kThreads = 256;
+constexpr int kRowsPerWave = kMaxNodes / 4;
+constexpr int kMaxChunks = 1024;
 
-// Block-wide reductions (256 threads = 4 waves).
 __device__ double block_sum_d(double v, double* s_red) {
     v = wave_sum(v);
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -79,6 +83,20 @@ __device__ double block_sum_d(double v, double* s_red) {
     if (lane == 0) s_red[wv] = v;
     __syncthreads();
     return s_red[0] + s_red[1] + s_red[2] + s_red[3];
+}
+
+__device__ void block_sum2_d(double& a, double& b, double* s_red) {
+    a = wave_sum(a);
+    b = wave_sum(b);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) {
+        s_red[wv] = a;
+        s_red[4 + wv] = b;
+    }
+    __syncthreads();
+    a = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+    b = s_red[4] + s_red[5] + s_red[6] + s_red[7];
 }
 
 __device__ void block_argmax(float& v, int& i, float* s_v, int* s_i) {
@@ -99,31 +117,19 @@ __device__ void block_argmax(float& v, int& i, float* s_v, int* s_i) {
         }
 }
 
-// p_v(x) as the stop-row residual and sampling kernels evaluate it (fp32).
+// p_v(x) as the residual and sampling passes evaluate it (fp32).
 __device__ __forceinline__ float target_prob(float l, float M, float T, float invS) {
     return expf((l - M) / T) * invS;
 }
 
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void accept_rowstats(AcceptArgs a) {
-    const int c = blockIdx.x, u = blockIdx.y, b = blockIdx.z;
-    __shared__ int s_has;
-    __shared__ double s_red[4];
-    __shared__ float s_v[4];
-    __shared__ int s_i[4];
-    if (threadIdx.x == 0) s_has = 0;
-    __syncthreads();
-    for (int i = 1 + threadIdx.x; i < a.N; i += kThreads)
-        if (tree_parent(a.parent, a.N, b, i) == u) s_has = 1;
-    __syncthreads();
-    if (!s_has) return;
-
-    const float* row = a.logits + (static_cast<size_t>(b) * a.N + u) * a.V;
-    const int x0 = c * a.chunk, x1 = min(x0 + a.chunk, a.V);
-    constexpr int EPT = 8;  // chunk == 8 * kThreads
+// Chunk statistics of one target row: lowest-index argmax, then (T > 0) the
+// exp sums relative to the chunk max.
+template <int EPT>
+__device__ void row_chunk_stats(const float* row, int x0, int x1, float T, float& best, int& bi, double& S,
+                                double& A, float* s_v, int* s_i, double* s_red) {
     float val[EPT];
-    float best = -INFINITY;
-    int bi = 0x7fffffff;
+    best = -INFINITY;
+    bi = 0x7fffffff;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
         const int x = x0 + threadIdx.x + e * kThreads;
@@ -134,21 +140,219 @@ __global__ __launch_bounds__(kThreads) void accept_rowstats(AcceptArgs a) {
         }
     }
     block_argmax(best, bi, s_v, s_i);
-    double S = 0.0, A = 0.0;
-    if (a.T > 0.f) {
+    S = 0.0;
+    A = 0.0;
+    if (T > 0.f) {
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
             const int x = x0 + threadIdx.x + e * kThreads;
             if (x < x1) {
-                const float t = (val[e] - best) / a.T;
+                const float t = (val[e] - best) / T;
                 const float ex = expf(t);
                 S += static_cast<double>(ex);
                 A += static_cast<double>(t) * static_cast<double>(ex);
             }
         }
-        S = block_sum_d(S, s_red);
-        A = block_sum_d(A, s_red);
+        block_sum2_d(S, A, s_red);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Parent array of request b in LDS, and which nodes have children.
+__device__ void load_tree(const AcceptArgs& a, int b, int* s_par, int* s_has) {
+    const int tid = threadIdx.x;
+    if (tid < kMaxNodes) s_has[tid] = 0;
+    if (tid < a.N) s_par[tid] = tree_parent(a.parent, a.N, b, tid);
+    __syncthreads();
+    if (tid > 0 && tid < a.N && s_par[tid] >= 0) s_has[s_par[tid]] = 1;
+    __syncthreads();
+}
+
+// Decision of request b from the chunk statistics.  Every accept_sample
+// workgroup of the request computes it (same inputs, same code, same result);
+// only the writer stores path, accepted tokens, accept_len and the record.
+__device__ void decide_request(const AcceptArgs& a, int b, bool writer, const int* s_par, const int* s_has,
+                               Decision* s_dec) {
+    const int N = a.N, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ float s_M[kMaxNodes];
+    __shared__ int s_arg[kMaxNodes];
+    __shared__ double s_S[kMaxNodes], s_H[kMaxNodes];
+    __shared__ int s_path[kMaxNodes], s_depth[kMaxNodes];
+
+    // Whole-row statistics: wave w owns rows w, w+4, ...  Lane c first loads
+    // chunk c of every row it serves in one round of independent loads; only
+    // vocabularies of more than 64 chunks take the extra loops.
+    const double T = a.T;
+    float mc[kRowsPerWave], m[kRowsPerWave];
+    int ac[kRowsPerWave], ar[kRowsPerWave];
+    double sc[kRowsPerWave], scA[kRowsPerWave];
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave; ++k) {
+        const int u = wave + 4 * k;
+        mc[k] = -INFINITY;
+        ac[k] = 0x7fffffff;
+        sc[k] = 0.0;
+        scA[k] = 0.0;
+        if (u < N && s_has[u] && lane < a.nchunk) {
+            const RowStat r = a.rowstat[(static_cast<size_t>(b) * N + u) * a.nchunk + lane];
+            mc[k] = r.M;
+            ac[k] = r.arg;
+            sc[k] = r.S;
+            scA[k] = r.A;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave; ++k) {
+        m[k] = mc[k];
+        ar[k] = ac[k];
+        const int u = wave + 4 * k;
+        if (u < N && s_has[u]) {  // wave-uniform
+            for (int c = lane + 64; c < a.nchunk; c += 64) {
+                const RowStat& r = a.rowstat[(static_cast<size_t>(b) * N + u) * a.nchunk + c];
+                if (r.M > m[k] || (r.M == m[k] && r.arg < ar[k])) {
+                    m[k] = r.M;
+                    ar[k] = r.arg;
+                }
+            }
+            wave_argmax(m[k], ar[k]);
+        }
+    }
+    if (T > 0.0) {
+#pragma unroll
+        for (int k = 0; k < kRowsPerWave; ++k) {
+            const int u = wave + 4 * k;
+            double S = 0.0, A = 0.0;
+            if (u < N && s_has[u]) {
+                if (lane < a.nchunk) {
+                    const double dl = (static_cast<double>(mc[k]) - m[k]) / T;
+                    const double wgt = exp(dl);
+                    S = wgt * sc[k];
+                    A = wgt * (scA[k] + dl * sc[k]);
+                }
+                for (int c = lane + 64; c < a.nchunk; c += 64) {
+                    const RowStat r = a.rowstat[(static_cast<size_t>(b) * N + u) * a.nchunk + c];
+                    const double dl = (static_cast<double>(r.M) - m[k]) / T;
+                    const double wgt = exp(dl);
+                    S += wgt * r.S;
+                    A += wgt * (r.A + dl * r.S);
+                }
+            }
+            if (u < N && s_has[u]) {  // wave-uniform
+                S = wave_sum(S);
+                A = wave_sum(A);
+                if (lane == 0) {
+                    s_S[u] = S;
+                    s_H[u] = log(S) - A / S;
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave; ++k) {
+        const int u = wave + 4 * k;
+        if (lane == 0 && u < N && s_has[u]) {
+            s_M[u] = m[k];
+            s_arg[u] = ar[k];
+            if (!(T > 0.0)) {
+                s_S[u] = 0.0;
+                s_H[u] = 0.0;
+            }
+        }
+    }
+    __syncthreads();
+
+    if (wave == 0) {
+        // Per-node tests in fp64 from the gathered values (nodes live in wave 0).
+        bool ok = false;
+        if (lane >= 1 && lane < N) {
+            const int u = s_par[lane];
+            if (u >= 0) {
+                int x = a.tokens[static_cast<size_t>(b) * N + lane];
+                x = min(max(x, 0), a.V - 1);
+                double pu;
+                if (T > 0.0) {
+                    const double l = a.logits[(static_cast<size_t>(b) * N + u) * a.V + x];
+                    pu = exp((l - static_cast<double>(s_M[u])) / T) / s_S[u];
+                } else {
+                    pu = x == s_arg[u] ? 1.0 : 0.0;
+                }
+                if (a.rule == 0) {
+                    const double qx = a.draft[(static_cast<size_t>(b) * N + lane) * a.V + x];
+                    ok = static_cast<double>(a.u_acc[static_cast<size_t>(b) * N + lane]) * qx < pu;
+                } else {
+                    const double thr =
+                        fmin(static_cast<double>(a.eps), static_cast<double>(a.delta) * exp(-s_H[u]));
+                    ok = pu > thr;
+                }
+            }
+        }
+        const unsigned long long okm = __ballot(ok);
+        if (lane == 0) {
+            uint64_t acc = 1ull;  // the root is always accepted
+            s_depth[0] = 0;
+            int v = 0, dv = 0;
+            for (int i = 1; i < N; ++i) {
+                const int u = s_par[i];
+                const int di = u >= 0 ? s_depth[u] + 1 : 0;
+                s_depth[i] = di;
+                if (u >= 0 && ((okm >> i) & 1ull) && ((acc >> u) & 1ull)) {
+                    acc |= 1ull << i;
+                    if (di > dv) {
+                        v = i;
+                        dv = di;
+                    }
+                }
+            }
+            for (int n = v, d = dv; d >= 0; n = s_par[n], --d) s_path[d] = n;
+            int c = -1;
+            for (int i = v + 1; i < N && c < 0; ++i)
+                if (s_par[i] == v) c = i;
+            Decision d;
+            d.v = v;
+            d.c = c;
+            d.a = dv;
+            d.u = a.u_smp ? a.u_smp[static_cast<size_t>(b) * N + v] : 0.f;
+            d.M = s_has[v] ? s_M[v] : 0.f;
+            d.S = s_has[v] ? s_S[v] : 0.0;
+            if (a.rule == 1 || !(T > 0.0))
+                d.mode = s_has[v] ? MODE_DONE : MODE_ARGMAX;
+            else
+                d.mode = s_has[v] ? MODE_RESID : MODE_BONUS;
+            *s_dec = d;
+        }
+    }
+    __syncthreads();
+    if (writer) {
+        const Decision d = *s_dec;
+        if (tid < N) {
+            const size_t o = static_cast<size_t>(b) * N + tid;
+            a.path[o] = tid <= d.a ? s_path[tid] : -1;
+            int tok = tid < d.a ? a.tokens[static_cast<size_t>(b) * N + s_path[tid + 1]] : -1;
+            if (tid == d.a && d.mode == MODE_DONE) tok = s_arg[d.v];
+            a.out_tokens[o] = tok;
+        }
+        if (tid == 0) {
+            a.accept_len[b] = d.a;
+            a.dec[b] = d;
+        }
+    }
+}
+
+template <int EPT>
+__global__ __launch_bounds__(kThreads) void accept_rowstats(AcceptArgs a) {
+    const int c = blockIdx.x, u = blockIdx.y, b = blockIdx.z;
+    __shared__ int s_par[kMaxNodes], s_has[kMaxNodes];
+    __shared__ double s_red[8];
+    __shared__ float s_v[4];
+    __shared__ int s_i[4];
+    load_tree(a, b, s_par, s_has);
+    if (!s_has[u]) return;  // leaves need no statistics
+    const float* row = a.logits + (static_cast<size_t>(b) * a.N + u) * a.V;
+    const int x0 = c * a.chunk, x1 = min(x0 + a.chunk, a.V);
+    float best;
+    int bi;
+    double S, A;
+    row_chunk_stats<EPT>(row, x0, x1, a.T, best, bi, S, A, s_v, s_i, s_red);
     if (threadIdx.x == 0) {
         RowStat rs;
         rs.S = S;
@@ -159,146 +363,20 @@ __global__ __launch_bounds__(kThreads) void accept_rowstats(AcceptArgs a) {
     }
 }
 
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void accept_decide(AcceptArgs a) {
-    const int b = blockIdx.x, lane = threadIdx.x;
-    const int N = a.N;
-    __shared__ int s_par[kMaxNodes], s_has[kMaxNodes], s_arg[kMaxNodes], s_path[kMaxNodes];
-    __shared__ float s_M[kMaxNodes];
-    __shared__ double s_S[kMaxNodes], s_H[kMaxNodes];
-    __shared__ int s_v, s_a, s_c;
-    if (lane < N) {
-        s_par[lane] = tree_parent(a.parent, N, b, lane);
-        s_has[lane] = 0;
-    }
-    __syncthreads();
-    if (lane > 0 && lane < N && s_par[lane] >= 0) s_has[s_par[lane]] = 1;
-    __syncthreads();
-
-    // Whole-row statistics of every node row with children.
-    for (int u = 0; u < N; ++u) {
-        if (!s_has[u]) continue;
-        const RowStat* rs = a.rowstat + (static_cast<size_t>(b) * N + u) * a.nchunk;
-        float M = -INFINITY;
-        int arg = 0x7fffffff;
-        for (int c = lane; c < a.nchunk; c += 64) {
-            const float m = rs[c].M;
-            const int i = rs[c].arg;
-            if (m > M || (m == M && i < arg)) {
-                M = m;
-                arg = i;
-            }
-        }
-        wave_argmax(M, arg);
-        double S = 0.0, A = 0.0;
-        if (a.T > 0.f) {
-            const double T = a.T;
-            for (int c = lane; c < a.nchunk; c += 64) {
-                const double dl = (static_cast<double>(rs[c].M) - M) / T;
-                const double wgt = exp(dl);
-                S += wgt * rs[c].S;
-                A += wgt * (rs[c].A + dl * rs[c].S);
-            }
-            S = wave_sum(S);
-            A = wave_sum(A);
-        }
-        if (lane == 0) {
-            s_M[u] = M;
-            s_arg[u] = arg;
-            s_S[u] = S;
-            s_H[u] = a.T > 0.f ? log(S) - A / S : 0.0;
-        }
-    }
-    __syncthreads();
-
-    // Per-node tests, evaluated in fp64 from the gathered values.
-    bool ok = false;
-    if (lane >= 1 && lane < N) {
-        const int u = s_par[lane];
-        if (u >= 0) {
-            int x = a.tokens[static_cast<size_t>(b) * N + lane];
-            x = min(max(x, 0), a.V - 1);
-            double pu;
-            if (a.T > 0.f) {
-                const double l = a.logits[(static_cast<size_t>(b) * N + u) * a.V + x];
-                pu = exp((l - static_cast<double>(s_M[u])) / static_cast<double>(a.T)) / s_S[u];
-            } else {
-                pu = x == s_arg[u] ? 1.0 : 0.0;
-            }
-            if (a.rule == 0) {
-                const double qx = a.draft[(static_cast<size_t>(b) * N + lane) * a.V + x];
-                ok = static_cast<double>(a.u_acc[static_cast<size_t>(b) * N + lane]) * qx < pu;
-            } else {
-                const double thr = fmin(static_cast<double>(a.eps), static_cast<double>(a.delta) * exp(-s_H[u]));
-                ok = pu > thr;
-            }
-        }
-    }
-    const unsigned long long okm = __ballot(ok);
-
-    if (lane == 0) {
-        uint64_t acc = 1ull;  // root
-        int depth[kMaxNodes];
-        depth[0] = 0;
-        int v = 0;
-        for (int i = 1; i < N; ++i) {
-            const int u = s_par[i];
-            depth[i] = u >= 0 ? depth[u] + 1 : 0;
-            if (u >= 0 && ((okm >> i) & 1ull) && ((acc >> u) & 1ull)) {
-                acc |= 1ull << i;
-                if (depth[i] > depth[v]) v = i;
-            }
-        }
-        const int av = depth[v];
-        for (int n = v, d = av; d >= 0; n = s_par[n], --d) s_path[d] = n;
-        int c = -1;
-        for (int i = v + 1; i < N && c < 0; ++i)
-            if (s_par[i] == v) c = i;
-        s_v = v;
-        s_a = av;
-        s_c = c;
-    }
-    __syncthreads();
-    const int v = s_v, av = s_a, c = s_c;
-    if (lane < N) {
-        const size_t o = static_cast<size_t>(b) * N + lane;
-        a.path[o] = lane <= av ? s_path[lane] : -1;
-        a.out_tokens[o] = lane < av ? a.tokens[static_cast<size_t>(b) * N + s_path[lane + 1]] : -1;
-    }
-    if (lane == 0) {
-        a.accept_len[b] = av;
-        Decision d;
-        d.v = v;
-        d.c = c;
-        d.a = av;
-        d.u = a.u_smp ? a.u_smp[static_cast<size_t>(b) * N + v] : 0.f;
-        d.M = s_has[v] ? s_M[v] : 0.f;
-        d.S = s_has[v] ? s_S[v] : 0.0;
-        if (a.rule == 1 || a.T == 0.f) {
-            if (s_has[v]) {
-                d.mode = MODE_DONE;
-                a.out_tokens[static_cast<size_t>(b) * N + av] = s_arg[v];
-            } else {
-                d.mode = MODE_ARGMAX;
-            }
-        } else {
-            d.mode = s_has[v] ? MODE_RESID : MODE_BONUS;
-        }
-        a.dec[b] = d;
-    }
-}
-
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void accept_chunks(AcceptArgs a) {
+template <int EPT>
+__global__ __launch_bounds__(kThreads) void accept_sample(AcceptArgs a) {
     const int c = blockIdx.x, b = blockIdx.y;
-    const Decision d = a.dec[b];
-    if (d.mode == MODE_DONE) return;
-    __shared__ double s_red[4];
+    __shared__ int s_par[kMaxNodes], s_has[kMaxNodes];
+    __shared__ Decision s_dec;
+    __shared__ double s_red[8];
     __shared__ float s_v[4];
     __shared__ int s_i[4];
+    load_tree(a, b, s_par, s_has);
+    decide_request(a, b, c == 0, s_par, s_has, &s_dec);
+    const Decision d = s_dec;
+    if (d.mode == MODE_DONE) return;
     const float* row = a.logits + (static_cast<size_t>(b) * a.N + d.v) * a.V;
     const int x0 = c * a.chunk, x1 = min(x0 + a.chunk, a.V);
-    constexpr int EPT = 8;
     ChunkStat cs;
     cs.m1 = cs.m2 = 0.0;
     cs.M = 0.f;
@@ -316,51 +394,40 @@ __global__ __launch_bounds__(kThreads) void accept_chunks(AcceptArgs a) {
                 p += static_cast<double>(pv);
             }
         }
-        cs.m1 = block_sum_d(r, s_red);
-        cs.m2 = block_sum_d(p, s_red);
+        block_sum2_d(r, p, s_red);
+        cs.m1 = r;
+        cs.m2 = p;
     } else {
-        float val[EPT];
-        float best = -INFINITY;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            const int x = x0 + threadIdx.x + e * kThreads;
-            val[e] = x < x1 ? row[x] : -INFINITY;
-            if (x < x1 && (val[e] > best || (val[e] == best && x < bi))) {
-                best = val[e];
-                bi = x;
-            }
-        }
-        block_argmax(best, bi, s_v, s_i);
+        float best;
+        int bi;
+        double S, A;
+        row_chunk_stats<EPT>(row, x0, x1, d.mode == MODE_BONUS ? a.T : 0.f, best, bi, S, A, s_v, s_i, s_red);
         cs.M = best;
         cs.arg = bi;
-        if (d.mode == MODE_BONUS) {
-            double S = 0.0;
-#pragma unroll
-            for (int e = 0; e < EPT; ++e) {
-                const int x = x0 + threadIdx.x + e * kThreads;
-                if (x < x1) S += static_cast<double>(expf((val[e] - best) / a.T));
-            }
-            cs.m1 = block_sum_d(S, s_red);
-        }
+        cs.m1 = S;
     }
     if (threadIdx.x == 0) a.cstat[static_cast<size_t>(b) * a.nchunk + c] = cs;
 }
 
 // ---------------------------------------------------------------------------
+template <int EPT>
 __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
     const int b = blockIdx.x;
-    const Decision d = a.dec[b];
-    if (d.mode == MODE_DONE) return;
     const int tid = threadIdx.x;
-    const ChunkStat* cs = a.cstat + static_cast<size_t>(b) * a.nchunk;
-    int32_t* out = a.out_tokens + static_cast<size_t>(b) * a.N + d.a;
+    __shared__ Decision s_d;
     __shared__ float s_v[4];
     __shared__ int s_i[4];
+    __shared__ double s_red[8];
+    __shared__ double s_w[kMaxChunks];
     __shared__ double s_scan[kThreads];
-    __shared__ int s_chunk, s_usep;
-    __shared__ double s_base, s_t, s_scale;
-    __shared__ float s_Mc;
+    __shared__ int s_pick;
+    __shared__ double s_base;
+    if (tid == 0) s_d = a.dec[b];
+    __syncthreads();
+    const Decision d = s_d;
+    if (d.mode == MODE_DONE) return;
+    const ChunkStat* cs = a.cstat + static_cast<size_t>(b) * a.nchunk;
+    int32_t* out = a.out_tokens + static_cast<size_t>(b) * a.N + d.a;
 
     if (d.mode == MODE_ARGMAX) {
         float best = -INFINITY;
@@ -375,69 +442,30 @@ __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
         return;
     }
 
-    // Ordered scan of the chunk masses (one thread, at most a few hundred chunks).
-    if (tid == 0) {
-        const double T = a.T;
-        double Mg = -INFINITY;
-        if (d.mode == MODE_BONUS)
-            for (int c = 0; c < a.nchunk; ++c) Mg = fmax(Mg, static_cast<double>(cs[c].M));
-        int usep = 0;
-        double total = 0.0;
-        for (int c = 0; c < a.nchunk; ++c) total += d.mode == MODE_RESID ? cs[c].m1 : cs[c].m1 * exp((cs[c].M - Mg) / T);
-        if (d.mode == MODE_RESID && !(total > 0.0)) {
-            usep = 1;
-            total = 0.0;
-            for (int c = 0; c < a.nchunk; ++c) total += cs[c].m2;
-        }
-        const double t = static_cast<double>(d.u) * total;
-        double cum = 0.0, base = 0.0;
-        int pick = -1, last = -1;
-        for (int c = 0; c < a.nchunk; ++c) {
-            const double wgt = d.mode == MODE_RESID ? (usep ? cs[c].m2 : cs[c].m1) : cs[c].m1 * exp((cs[c].M - Mg) / T);
-            if (wgt > 0.0) last = c;
-            if (pick < 0 && wgt > 0.0 && cum + wgt > t) {
-                pick = c;
-                base = cum;
-            }
-            cum += wgt;
-        }
-        if (pick < 0) {  // rounding: fall back to the last chunk with mass
-            pick = last < 0 ? 0 : last;
-            base = -INFINITY;
-        }
-        s_chunk = pick;
-        s_usep = usep;
-        s_base = base;
-        s_t = t;
-        s_Mc = cs[pick].M;
-        s_scale = d.mode == MODE_BONUS ? exp((cs[pick].M - Mg) / T) : 1.0;
+    // Chunk weights in token order.
+    const double T = a.T;
+    double Mg = -INFINITY, tot1 = 0.0;
+    if (d.mode == MODE_BONUS) {
+        float mloc = -INFINITY;
+        int dummy = 0;
+        for (int c = tid; c < a.nchunk; c += kThreads) mloc = fmaxf(mloc, cs[c].M);
+        block_argmax(mloc, dummy, s_v, s_i);
+        Mg = mloc;
+    } else {
+        double t1 = 0.0;
+        for (int c = tid; c < a.nchunk; c += kThreads) t1 += cs[c].m1;
+        tot1 = block_sum_d(t1, s_red);
     }
+    const bool usep = d.mode == MODE_RESID && !(tot1 > 0.0);  // all-zero residual: fall back to p_v
+    for (int c = tid; c < a.nchunk; c += kThreads)
+        s_w[c] = d.mode == MODE_BONUS ? cs[c].m1 * exp((static_cast<double>(cs[c].M) - Mg) / T)
+                                      : (usep ? cs[c].m2 : cs[c].m1);
     __syncthreads();
-    const int c = s_chunk;
-    const int x0 = c * a.chunk, x1 = min(x0 + a.chunk, a.V);
-    constexpr int EPT = 8;
-    const int xs = x0 + tid * EPT;  // contiguous run per thread: ascending order
-    const float* row = a.logits + (static_cast<size_t>(b) * a.N + d.v) * a.V;
-    const float* qrow = d.mode == MODE_RESID ? a.draft + (static_cast<size_t>(b) * a.N + d.c) * a.V : nullptr;
-    const float invS = d.mode == MODE_RESID ? static_cast<float>(1.0 / d.S) : 0.f;
-    double wv[EPT];
+    // Inclusive scan of the chunk weights: each thread owns a run of chunks.
+    const int per = (a.nchunk + kThreads - 1) / kThreads;
+    const int c0 = tid * per, c1 = min(c0 + per, a.nchunk);
     double run = 0.0;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-        const int x = xs + e;
-        double wgt = 0.0;
-        if (x < x1) {
-            if (d.mode == MODE_RESID) {
-                const float pv = target_prob(row[x], d.M, a.T, invS);
-                wgt = s_usep ? static_cast<double>(pv) : static_cast<double>(fmaxf(pv - qrow[x], 0.f));
-            } else {
-                wgt = static_cast<double>(expf((row[x] - s_Mc) / a.T)) * s_scale;
-            }
-        }
-        wv[e] = wgt;
-        run += wgt;
-    }
-    // exclusive scan of the per-thread totals (ascending thread order)
+    for (int c = c0; c < c1; ++c) run += s_w[c];
     s_scan[tid] = run;
     __syncthreads();
     for (int off = 1; off < kThreads; off <<= 1) {
@@ -446,35 +474,108 @@ __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
         s_scan[tid] += add;
         __syncthreads();
     }
-    double cum = s_base + (s_scan[tid] - run);
-    int hit = 0x7fffffff, lastnz = -1;
+    const double total = s_scan[kThreads - 1];
+    const double t = static_cast<double>(d.u) * total;
+    double cum = s_scan[tid] - run;
+    int hit = 0x7fffffff, lastc = -1;
+    double hit_base = 0.0;
+    for (int c = c0; c < c1; ++c) {
+        if (s_w[c] > 0.0) {
+            lastc = c;
+            if (hit == 0x7fffffff && cum + s_w[c] > t) {
+                hit = c;
+                hit_base = cum;
+            }
+        }
+        cum += s_w[c];
+    }
+    // smallest chunk with a hit, else the last chunk with weight
+    float fh = hit == 0x7fffffff ? -INFINITY : -static_cast<float>(hit);
+    int ih = hit;
+    block_argmax(fh, ih, s_v, s_i);
+    float fl = static_cast<float>(lastc);
+    int il = -lastc;
+    block_argmax(fl, il, s_v, s_i);
+    if (tid == 0) {
+        s_pick = ih != 0x7fffffff ? ih : max(-il, 0);
+        s_base = ih != 0x7fffffff ? 0.0 : -INFINITY;  // -inf: take the last token with weight
+    }
+    __syncthreads();
+    if (ih != 0x7fffffff && hit == ih) s_base = hit_base;
+    __syncthreads();
+
+    // Token inside the chosen chunk: contiguous runs per thread, ascending.
+    const int pc = s_pick;
+    const int x0 = pc * a.chunk, x1 = min(x0 + a.chunk, a.V);
+    const int xs = x0 + tid * EPT;
+    const float* row = a.logits + (static_cast<size_t>(b) * a.N + d.v) * a.V;
+    const float* qrow = d.mode == MODE_RESID ? a.draft + (static_cast<size_t>(b) * a.N + d.c) * a.V : nullptr;
+    const float invS = d.mode == MODE_RESID ? static_cast<float>(1.0 / d.S) : 0.f;
+    const float Mc = cs[pc].M;
+    const double scale = d.mode == MODE_BONUS ? exp((static_cast<double>(Mc) - Mg) / T) : 1.0;
+    double wv[EPT];
+    run = 0.0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int x = xs + e;
+        double wgt = 0.0;
+        if (x < x1) {
+            if (d.mode == MODE_RESID) {
+                const float pv = target_prob(row[x], d.M, a.T, invS);
+                wgt = usep ? static_cast<double>(pv) : static_cast<double>(fmaxf(pv - qrow[x], 0.f));
+            } else {
+                wgt = static_cast<double>(expf((row[x] - Mc) / a.T)) * scale;
+            }
+        }
+        wv[e] = wgt;
+        run += wgt;
+    }
+    __syncthreads();
+    s_scan[tid] = run;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+        const double add = tid >= off ? s_scan[tid - off] : 0.0;
+        __syncthreads();
+        s_scan[tid] += add;
+        __syncthreads();
+    }
+    cum = s_base + (s_scan[tid] - run);
+    int xhit = 0x7fffffff, lastnz = -1;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
         const int x = xs + e;
         if (wv[e] > 0.0) {
             lastnz = x;
             cum += wv[e];
-            if (hit == 0x7fffffff && cum > s_t) hit = x;
+            if (xhit == 0x7fffffff && cum > t) xhit = x;
         }
     }
-    // first hit (smallest token id), else the last token with weight
-    float fh = hit == 0x7fffffff ? -INFINITY : -static_cast<float>(hit);
-    int ih = hit;
-    block_argmax(fh, ih, s_v, s_i);
-    float fl = static_cast<float>(lastnz);
-    int il = -lastnz;
-    block_argmax(fl, il, s_v, s_i);
+    float fx = xhit == 0x7fffffff ? -INFINITY : -static_cast<float>(xhit);
+    int ix = xhit;
+    block_argmax(fx, ix, s_v, s_i);
+    float fz = static_cast<float>(lastnz);
+    int iz = -lastnz;
+    block_argmax(fz, iz, s_v, s_i);
     if (tid == 0) {
-        int final = ih != 0x7fffffff && fh != -INFINITY ? ih : -il;
+        int final = ix != 0x7fffffff ? ix : -iz;
         if (final < 0) final = x0;
         *out = final;
     }
 }
 
 // ---------------------------------------------------------------------------
+// Entries per thread and chunk: 8, raised to 16 or 32 for large batches so
+// the statistics kernel launches at most ~8k workgroups of useful size.
+static int accept_ept(int B, int N, int V) {
+    int ept = 8;
+    auto nchunk = [&](int e) { return (V + e * kThreads - 1) / (e * kThreads); };
+    while (ept < 32 && (static_cast<long>(B) * N * nchunk(ept) > 8192 || nchunk(ept) > kMaxChunks)) ept *= 2;
+    return ept;
+}
+
 AcceptPlan plan_accept(int B, int N, int V) {
     AcceptPlan p{};
-    p.chunk = 8 * kThreads;
+    p.chunk = accept_ept(B, N, V) * kThreads;
     p.nchunk = (V + p.chunk - 1) / p.chunk;
     size_t off = 0;
     p.off_rowstat = off;
@@ -485,6 +586,21 @@ AcceptPlan plan_accept(int B, int N, int V) {
     off = align_up(off + static_cast<size_t>(B) * p.nchunk * sizeof(ChunkStat), 256);
     p.ws_bytes = off;
     return p;
+}
+
+int max_accept_vocab() { return kMaxChunks * 32 * kThreads; }
+
+template <int EPT>
+static int launch_accept_ept(const AcceptArgs& a, const AcceptPlan& p, hipStream_t stream) {
+    if (a.N > 1) {
+        hipLaunchKernelGGL((accept_rowstats<EPT>), dim3(p.nchunk, a.N, a.B), dim3(kThreads), 0, stream, a);
+        if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+    }
+    hipLaunchKernelGGL((accept_sample<EPT>), dim3(p.nchunk, a.B), dim3(kThreads), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+    hipLaunchKernelGGL((accept_select<EPT>), dim3(a.B), dim3(kThreads), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+    return SPEC_OK;
 }
 
 int launch_accept(int rule, int B, int N, int V, const float* logits, const float* draft,
@@ -515,17 +631,11 @@ int launch_accept(int rule, int B, int N, int V, const float* logits, const floa
     a.T = temperature;
     a.eps = epsilon;
     a.delta = delta;
-    if (N > 1) {
-        hipLaunchKernelGGL(accept_rowstats, dim3(p.nchunk, N, B), dim3(kThreads), 0, stream, a);
-        if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+    switch (p.chunk / kThreads) {
+        case 8: return launch_accept_ept<8>(a, p, stream);
+        case 16: return launch_accept_ept<16>(a, p, stream);
+        default: return launch_accept_ept<32>(a, p, stream);
     }
-    hipLaunchKernelGGL(accept_decide, dim3(B), dim3(64), 0, stream, a);
-    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-    hipLaunchKernelGGL(accept_chunks, dim3(p.nchunk, B), dim3(kThreads), 0, stream, a);
-    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-    hipLaunchKernelGGL(accept_select, dim3(B), dim3(kThreads), 0, stream, a);
-    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-    return SPEC_OK;
 }
 
 }  // namespace specv

@@ -54,13 +54,15 @@ int spec_verify_attn(const spec_attn_desc* desc, int32_t max_prefix_len, const v
 }
 
 size_t spec_accept_workspace_bytes(int32_t batch, int32_t num_nodes, int32_t vocab) {
-    if (batch < 1 || num_nodes < 1 || num_nodes > kMaxNodes || vocab < 1) return 0;
+    if (batch < 1 || batch > 65535 || num_nodes < 1 || num_nodes > kMaxNodes || vocab < 1 ||
+        vocab > max_accept_vocab())
+        return 0;
     return plan_accept(batch, num_nodes, vocab).ws_bytes;
 }
 
 static int accept_common_checks(int32_t B, int32_t N, int32_t V, const float* logits, const int32_t* tokens,
                                 int32_t* accept_len, int32_t* path, int32_t* out_tokens, float T) {
-    if (B > 65535 || N < 1 || N > kMaxNodes || V < 1) return SPEC_EINVAL;
+    if (B > 65535 || N < 1 || N > kMaxNodes || V < 1 || V > max_accept_vocab()) return SPEC_EINVAL;
     if (!(T >= 0.f) || isinf(T)) return SPEC_EINVAL;
     if (!logits || !tokens || !accept_len || !path || !out_tokens) return SPEC_EINVAL;
     return SPEC_OK;

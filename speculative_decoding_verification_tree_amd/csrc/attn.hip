@@ -95,13 +95,41 @@ __device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 3)) & 3;
 // ----------------------------------------------------------------------------
 // MFMA path (bf16).  D in {64, 128}; RT 16-row tiles per wave; WK waves.
 // ----------------------------------------------------------------------------
+// K fragments (A operand, paired-half key order) and V rows of one 32-key
+// block, held in registers between the load and its use.
+template <int D>
+struct KVBlock {
+    static constexpr int NC32 = D / 32;
+    static constexpr int KPL = 32 / (64 / (D / 8));
+    u32x4 kf[2][NC32];
+    u32x4 vr[KPL];
+};
+
+// Issue the loads of the block starting at key kb; rows are clamped to
+// row_max so every address is inside the cache.
+template <int D>
+__device__ __forceinline__ void load_kv_block(KVBlock<D>& blk, const uint16_t* kbase, const uint16_t* vbase, int kb,
+                                              int row_max, int n16, int q4, int vch, int vkg) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int row = min(kb + 8 * (n16 >> 2) + 4 * h + (n16 & 3), row_max);
+#pragma unroll
+        for (int c = 0; c < KVBlock<D>::NC32; ++c)
+            blk.kf[h][c] = *reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(row) * D + 32 * c + 8 * q4);
+    }
+#pragma unroll
+    for (int jj = 0; jj < KVBlock<D>::KPL; ++jj) {
+        const int row = min(kb + vkg * KVBlock<D>::KPL + jj, row_max);
+        blk.vr[jj] = *reinterpret_cast<const u32x4*>(vbase + static_cast<size_t>(row) * D + 8 * vch);
+    }
+}
+
 template <int D, int RT, int WK>
 __global__ __launch_bounds__(64 * WK) void attn_mfma(AttnArgs a) {
     constexpr int NC32 = D / 32;  // k-steps of the QK product
     constexpr int NC16 = D / 16;  // n-tiles of the PV product
     constexpr int CPR = D / 8;    // 16-byte chunks per cache row
-    constexpr int KG = 64 / CPR;  // key groups of the V load
-    constexpr int KPL = 32 / KG;  // keys per lane in the V load (8 or 4)
+    constexpr int KPL = KVBlock<D>::KPL;  // keys per lane in the V load (8 or 4)
     constexpr int VT_BYTES = D * 64;
     constexpr int MERGE_BYTES = WK * 16 * RT * D * 4;
     constexpr int LDS_BYTES = (WK * VT_BYTES > MERGE_BYTES) ? WK * VT_BYTES : MERGE_BYTES;
@@ -109,36 +137,38 @@ __global__ __launch_bounds__(64 * WK) void attn_mfma(AttnArgs a) {
     __shared__ uint64_t s_anc[kMaxNodes];
     __shared__ float s_m[WK][16 * RT];
     __shared__ float s_l[WK][16 * RT];
+    __shared__ float2 s_row[16 * RT];
 
     const Work w = decode_block(a);
     if (!w.live) return;
     const int b = w.b, g = w.g;
-    const int L = a.prefix_len[b];
-    const int Tk = L + a.N;
-    if (L < 0 || Tk > a.cap || Tk > a.max_keys) return;  // outside the contract: leave out unwritten
     const int k0 = w.s * a.chunk;
-    if (k0 >= Tk) return;
-    const int k1 = min(k0 + a.chunk, Tk);
-    const int nsplit = (Tk + a.chunk - 1) / a.chunk;
-
-    build_anc(a, b, s_anc);
-    __syncthreads();
-
+    if (k0 >= a.max_keys) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n16 = lane & 15, q4 = lane >> 4;
+    const int vch = lane % CPR, vkg = lane / CPR;
+    const size_t head = (static_cast<size_t>(b) * a.Hkv + g) * a.cap;
+    const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + head * D;
+    const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + head * D;
 
-    // Query rows owned by this lane (row n16 of each tile) and their masks.
-    uint64_t anc[RT];
+    // Everything that does not depend on the prefix length goes out first:
+    // the prefix length itself, the first KV block (rows clamped to the cache,
+    // out-of-range values masked once L is known), the tree and the queries.
+    const int L = a.prefix_len[b];
+    int kb = k0 + wave * 32;
+    KVBlock<D> cur;
+    load_kv_block<D>(cur, kbase, vbase, kb, a.cap - 1, n16, q4, vch, vkg);
+    build_anc(a, b, s_anc);
     bf16x8 qf[RT][NC32];
+    int rnode[RT];
     const uint16_t* qb = static_cast<const uint16_t*>(a.q);
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
         const int r = (w.rg * RT + t) * 16 + n16;
         const bool valid = r < a.R;
-        const int node = valid ? r / a.G : 0;
+        rnode[t] = valid ? r / a.G : -1;
         const int hq = g * a.G + (valid ? r % a.G : 0);
-        anc[t] = valid ? s_anc[node] : ~0ull;
-        const uint16_t* qrow = qb + ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D;
+        const uint16_t* qrow = qb + ((static_cast<size_t>(b) * a.N + (valid ? rnode[t] : 0)) * a.Hq + hq) * D;
 #pragma unroll
         for (int c = 0; c < NC32; ++c) {
             u32x4 u = {0u, 0u, 0u, 0u};
@@ -146,6 +176,16 @@ __global__ __launch_bounds__(64 * WK) void attn_mfma(AttnArgs a) {
             qf[t][c] = __builtin_bit_cast(bf16x8, u);
         }
     }
+    __syncthreads();
+
+    const int Tk = L + a.N;
+    if (L < 0 || Tk > a.cap || Tk > a.max_keys) return;  // outside the contract: leave out unwritten
+    if (k0 >= Tk) return;
+    const int k1 = min(k0 + a.chunk, Tk);
+    const int nsplit = (Tk + a.chunk - 1) / a.chunk;
+    uint64_t anc[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) anc[t] = rnode[t] >= 0 ? s_anc[rnode[t]] : ~0ull;
 
     float m_run[RT], l_run[RT];
     f32x4 o[RT][NC16];
@@ -156,32 +196,19 @@ __global__ __launch_bounds__(64 * WK) void attn_mfma(AttnArgs a) {
 #pragma unroll
         for (int c = 0; c < NC16; ++c) o[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-
-    const size_t head = (static_cast<size_t>(b) * a.Hkv + g) * a.cap;
-    const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + head * D;
-    const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + head * D;
     unsigned char* vt = s_buf + wave * VT_BYTES;
-    const int vch = lane % CPR, vkg = lane / CPR;
 
-    for (int kb = k0 + wave * 32; kb < k1; kb += 32 * WK) {
-        // K: A operand rows in the paired-half key order.
-        u32x4 kf[2][NC32];
+    for (; kb < k1; kb += 32 * WK) {
+        // Prefetch the wave's next block while this one is processed.
+        KVBlock<D> nxt;
+        const int kn = kb + 32 * WK;
+        if (kn < k1) load_kv_block<D>(nxt, kbase, vbase, kn, Tk - 1, n16, q4, vch, vkg);
+
+        // Transpose V into LDS (row d holds the block's 32 keys); keys at or
+        // past the split end are zeroed so no stale value reaches P*V.
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int key = kb + 8 * (n16 >> 2) + 4 * h + (n16 & 3);
-            const int row = min(key, Tk - 1);
-#pragma unroll
-            for (int c = 0; c < NC32; ++c)
-                kf[h][c] = *reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(row) * D + 32 * c + 8 * q4);
-        }
-        // V: KPL consecutive keys of one 8-dim chunk per lane.
-        u32x4 vr[KPL];
-#pragma unroll
-        for (int jj = 0; jj < KPL; ++jj) {
-            const int row = min(kb + vkg * KPL + jj, Tk - 1);
-            vr[jj] = *reinterpret_cast<const u32x4*>(vbase + static_cast<size_t>(row) * D + 8 * vch);
-        }
-        // Transpose into LDS: row d holds keys 0..31 of the block.
+        for (int jj = 0; jj < KPL; ++jj)
+            if (kb + vkg * KPL + jj >= k1) cur.vr[jj] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const int d = 8 * vch + t;
@@ -193,26 +220,19 @@ __global__ __launch_bounds__(64 * WK) void attn_mfma(AttnArgs a) {
                 u32x4 wv;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const uint32_t lo = (vr[2 * e][t >> 1] >> sh) & 0xFFFFu;
-                    const uint32_t hi = (vr[2 * e + 1][t >> 1] >> sh) & 0xFFFFu;
+                    const uint32_t lo = (cur.vr[2 * e][t >> 1] >> sh) & 0xFFFFu;
+                    const uint32_t hi = (cur.vr[2 * e + 1][t >> 1] >> sh) & 0xFFFFu;
                     wv[e] = lo | (hi << 16);
                 }
                 *reinterpret_cast<u32x4*>(dst) = wv;
             } else {
                 uint2 wv;
-                wv.x = ((vr[0][t >> 1] >> sh) & 0xFFFFu) | (((vr[1][t >> 1] >> sh) & 0xFFFFu) << 16);
-                wv.y = ((vr[2][t >> 1] >> sh) & 0xFFFFu) | (((vr[3][t >> 1] >> sh) & 0xFFFFu) << 16);
+                wv.x = ((cur.vr[0][t >> 1] >> sh) & 0xFFFFu) | (((cur.vr[1][t >> 1] >> sh) & 0xFFFFu) << 16);
+                wv.y = ((cur.vr[2][t >> 1] >> sh) & 0xFFFFu) | (((cur.vr[3][t >> 1] >> sh) & 0xFFFFu) << 16);
                 *reinterpret_cast<uint2*>(dst) = wv;
             }
         }
         wave_lds_sync();
-        // B operand of PV: V[keys 8q..8q+7][d = 16c + n].
-        u32x4 vf[NC16];
-#pragma unroll
-        for (int c = 0; c < NC16; ++c) {
-            const int d = 16 * c + n16;
-            vf[c] = *reinterpret_cast<const u32x4*>(vt + d * 64 + ((q4 ^ vt_swz(d)) * 16));
-        }
 
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
@@ -222,8 +242,8 @@ __global__ __launch_bounds__(64 * WK) void attn_mfma(AttnArgs a) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int c = 0; c < NC32; ++c)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[h][c]), qf[t][c], acc,
-                                                                  0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.kf[h][c]), qf[t][c],
+                                                                  acc, 0, 0, 0);
                 st[h] = acc;
             }
             float s[8];
@@ -238,8 +258,7 @@ __global__ __launch_bounds__(64 * WK) void attn_mfma(AttnArgs a) {
                     s[4 * h + ii] = x;
                     bm = fmaxf(bm, x);
                 }
-            bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
-            bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+            bm = max_across_rows(bm);
             const float mn = fmaxf(m_run[t], bm);
             const float mu = mn == -INFINITY ? 0.f : mn;
             const float alpha = exp2f(m_run[t] - mu);
@@ -249,16 +268,11 @@ __global__ __launch_bounds__(64 * WK) void attn_mfma(AttnArgs a) {
                 s[e] = exp2f(s[e] - mu);
                 rs += s[e];
             }
-            rs += __shfl_xor(rs, 16, kWave);
-            rs += __shfl_xor(rs, 32, kWave);
+            rs = sum_across_rows(rs);
             l_run[t] = l_run[t] * alpha + rs;
             m_run[t] = mn;
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const float ao = __shfl(alpha, 4 * q4 + ii, kWave);
-#pragma unroll
-                for (int c = 0; c < NC16; ++c) o[t][c][ii] *= ao;
-            }
+            for (int c = 0; c < NC16; ++c) o[t][c] *= alpha;  // o holds row n16 of this lane
             u32x4 pp;
             pp[0] = pack_bf16x2(s[0], s[1]);
             pp[1] = pack_bf16x2(s[2], s[3]);
@@ -266,10 +280,17 @@ __global__ __launch_bounds__(64 * WK) void attn_mfma(AttnArgs a) {
             pp[3] = pack_bf16x2(s[6], s[7]);
             const bf16x8 pa = __builtin_bit_cast(bf16x8, pp);
 #pragma unroll
-            for (int c = 0; c < NC16; ++c)
-                o[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, vf[c]), o[t][c], 0, 0, 0);
+            for (int c = 0; c < NC16; ++c) {
+                // O^T = V^T P^T: A = V^T (lane: keys 8q..8q+7 of dim 16c + n,
+                // straight from LDS), B = P^T; the result lands as
+                // O[row n][dims 16c + 4q .. 16c + 4q + 3] in this lane.
+                const int d = 16 * c + n16;
+                const u32x4 vf = *reinterpret_cast<const u32x4*>(vt + d * 64 + ((q4 ^ vt_swz(d)) * 16));
+                o[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf), pa, o[t][c], 0, 0, 0);
+            }
         }
         wave_lds_sync();
+        cur = nxt;
     }
 
     // ---- merge the waves of this workgroup --------------------------------
@@ -282,44 +303,47 @@ __global__ __launch_bounds__(64 * WK) void attn_mfma(AttnArgs a) {
         }
     }
     __syncthreads();
+    if (tid < 16 * RT) {  // per-row (max, sum) of the workgroup
+        float M = -INFINITY;
+#pragma unroll
+        for (int x = 0; x < WK; ++x) M = fmaxf(M, s_m[x][tid]);
+        const float Mu = M == -INFINITY ? 0.f : M;
+        float lsum = 0.f;
+#pragma unroll
+        for (int x = 0; x < WK; ++x) lsum += s_l[x][tid] * exp2f(s_m[x][tid] - Mu);
+        s_row[tid] = make_float2(M, lsum);
+    }
     float* reg = reinterpret_cast<float*>(s_buf);
 #pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int row = t * 16 + 4 * q4 + ii;
-            float M = -INFINITY;
-#pragma unroll
-            for (int x = 0; x < WK; ++x) M = fmaxf(M, s_m[x][row]);
-            const float sc = exp2f(s_m[wave][row] - (M == -INFINITY ? 0.f : M));
-#pragma unroll
-            for (int c = 0; c < NC16; ++c) reg[(wave * 16 * RT + row) * D + 16 * c + n16] = o[t][c][ii] * sc;
-        }
-    __syncthreads();
-
-    const bool bf16_out = true;
-    for (int e = tid; e < 16 * RT * D; e += 64 * WK) {
-        const int row = e / D, d = e % D;
-        const int r = w.rg * RT * 16 + row;
-        if (r >= a.R) continue;
+    for (int t = 0; t < RT; ++t) {
+        const int row = t * 16 + n16;
         float M = -INFINITY;
 #pragma unroll
         for (int x = 0; x < WK; ++x) M = fmaxf(M, s_m[x][row]);
-        const float Mu = M == -INFINITY ? 0.f : M;
-        float lsum = 0.f, osum = 0.f;
+        const float sc = exp2f(m_run[t] - (M == -INFINITY ? 0.f : M));
 #pragma unroll
-        for (int x = 0; x < WK; ++x) {
-            lsum += s_l[x][row] * exp2f(s_m[x][row] - Mu);
-            osum += reg[(x * 16 * RT + row) * D + d];
-        }
-        const int node = r / a.G, hq = g * a.G + r % a.G;
+        for (int c = 0; c < NC16; ++c)
+            *reinterpret_cast<f32x4*>(reg + (wave * 16 * RT + row) * D + 16 * c + 4 * q4) = o[t][c] * sc;
+    }
+    __syncthreads();
+
+    const int rbase = w.rg * RT * 16;
+    const int rows = min(16 * RT, a.R - rbase);
+    const size_t pbase = (static_cast<size_t>(b) * a.Hkv + g) * a.nsplit_max;
+    for (int e = tid; e < rows * D; e += 64 * WK) {
+        const int row = e / D, d = e % D;
+        float osum = 0.f;
+#pragma unroll
+        for (int x = 0; x < WK; ++x) osum += reg[(x * 16 * RT + row) * D + d];
+        const int r = rbase + row;
         if (nsplit == 1) {
+            const int node = r / a.G, hq = g * a.G + r % a.G;
+            const float lsum = s_row[row].y;
             const size_t oi = ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D + d;
-            store_out(a.out, bf16_out, oi, lsum > 0.f ? osum / lsum : 0.f);
+            store_out(a.out, true, oi, lsum > 0.f ? osum / lsum : 0.f);
         } else {
-            const size_t pi = (static_cast<size_t>(b) * a.Hkv + g) * a.nsplit_max + w.s;
-            a.ws_o[(pi * a.R + r) * D + d] = osum;
-            if (d == 0) a.ws_ml[pi * a.R + r] = make_float2(M, lsum);
+            a.ws_o[((pbase + w.s) * a.R + r) * D + d] = osum;
+            if (d == 0) a.ws_ml[(pbase + w.s) * a.R + r] = s_row[row];
         }
     }
 }
@@ -408,9 +432,10 @@ __global__ __launch_bounds__(256) void attn_valu(AttnArgs a) {
             s[jj] = ok ? dot * a.scale_log2 : -INFINITY;
             bm = fmaxf(bm, s[jj]);
         }
-        bm = fmaxf(bm, __shfl_xor(bm, 1, kWave));
-        bm = fmaxf(bm, __shfl_xor(bm, 2, kWave));
-        bm = fmaxf(bm, __shfl_xor(bm, 4, kWave));
+        // reductions over the 8 lanes of a row (xor 1, xor 2, mirror within 8)
+        bm = fmaxf(bm, __uint_as_float(dpp_xor1(__float_as_uint(bm))));
+        bm = fmaxf(bm, __uint_as_float(dpp_xor2(__float_as_uint(bm))));
+        bm = fmaxf(bm, __uint_as_float(dpp_mirror8(__float_as_uint(bm))));
         const float mn = fmaxf(m_run, bm);
         const float mu = mn == -INFINITY ? 0.f : mn;
         const float alpha = exp2f(m_run - mu);
@@ -421,9 +446,9 @@ __global__ __launch_bounds__(256) void attn_valu(AttnArgs a) {
             s_p[sr][sk + 8 * jj] = p;
             rs += p;
         }
-        rs += __shfl_xor(rs, 1, kWave);
-        rs += __shfl_xor(rs, 2, kWave);
-        rs += __shfl_xor(rs, 4, kWave);
+        rs += __uint_as_float(dpp_xor1(__float_as_uint(rs)));
+        rs += __uint_as_float(dpp_xor2(__float_as_uint(rs)));
+        rs += __uint_as_float(dpp_mirror8(__float_as_uint(rs)));
         l_run = l_run * alpha + rs;
         m_run = mn;
 #pragma unroll
@@ -456,6 +481,8 @@ __global__ __launch_bounds__(256) void attn_valu(AttnArgs a) {
 // ----------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int bf16_out) {
+    constexpr int DPL = D / 64;  // output elements per lane
+    constexpr int SB = 16;       // splits whose loads are in flight together
     const int lane = threadIdx.x & 63;
     const long id = static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (id >= static_cast<long>(a.B) * a.Hkv * a.R) return;
@@ -468,27 +495,48 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int bf16_out) {
     const int nsplit = (Tk + a.chunk - 1) / a.chunk;
     if (nsplit <= 1) return;
     const size_t base = static_cast<size_t>(bg) * a.nsplit_max;
-    float M = -INFINITY;
-    for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, a.ws_ml[(base + s) * a.R + r].x);
-    M = wave_max(M);
-    const float Mu = M == -INFINITY ? 0.f : M;
-    float lsum = 0.f;
-    for (int s = lane; s < nsplit; s += 64) {
-        const float2 ml = a.ws_ml[(base + s) * a.R + r];
-        lsum += ml.y * exp2f(ml.x - Mu);
+    // Running (max, sum, O) over batches of SB splits, each batch one round of loads.
+    float M = -INFINITY, lsum = 0.f;
+    float acc[DPL];
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) acc[j] = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += SB) {
+        float2 ml[SB];
+        float ov[SB][DPL];
+#pragma unroll
+        for (int k = 0; k < SB; ++k) {
+            const int s = s0 + k;
+            ml[k] = make_float2(-INFINITY, 0.f);
+#pragma unroll
+            for (int j = 0; j < DPL; ++j) ov[k][j] = 0.f;
+            if (s < nsplit) {
+                ml[k] = a.ws_ml[(base + s) * a.R + r];
+#pragma unroll
+                for (int j = 0; j < DPL; ++j) ov[k][j] = a.ws_o[((base + s) * a.R + r) * D + lane + 64 * j];
+            }
+        }
+        float Mn = M;
+#pragma unroll
+        for (int k = 0; k < SB; ++k) Mn = fmaxf(Mn, ml[k].x);
+        const float Mu = Mn == -INFINITY ? 0.f : Mn;
+        const float sc = exp2f(M - Mu);
+        lsum *= sc;
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) acc[j] *= sc;
+#pragma unroll
+        for (int k = 0; k < SB; ++k) {
+            const float wgt = exp2f(ml[k].x - Mu);
+            lsum += wgt * ml[k].y;
+#pragma unroll
+            for (int j = 0; j < DPL; ++j) acc[j] += wgt * ov[k][j];
+        }
+        M = Mn;
     }
-    lsum = wave_sum(lsum);
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     const int node = r / a.G, hq = g * a.G + r % a.G;
     const size_t ob = ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D;
-    for (int d = lane; d < D; d += 64) {
-        float acc = 0.f;
-        for (int s = 0; s < nsplit; ++s) {
-            const float wgt = exp2f(a.ws_ml[(base + s) * a.R + r].x - Mu);
-            acc += wgt * a.ws_o[((base + s) * a.R + r) * D + d];
-        }
-        store_out(a.out, bf16_out != 0, ob + d, acc * inv);
-    }
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) store_out(a.out, bf16_out != 0, ob + lane + 64 * j, acc[j] * inv);
 }
 
 // ----------------------------------------------------------------------------
@@ -582,9 +630,10 @@ int launch_verify_attn(const spec_attn_desc& d, const AttnPlan& p, const void* q
     a.scale_log2 = scale * 1.4426950408889634f;
     if (p.nsplit_max > 1) {
         const size_t parts = static_cast<size_t>(d.batch) * d.num_kv_heads * p.nsplit_max * p.rows;
-        a.ws_o = static_cast<float*>(workspace);
-        a.ws_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) +
-                                            align_up(parts * d.head_dim * sizeof(float), 256));
+        char* ws = static_cast<char*>(workspace);
+        a.ws_o = reinterpret_cast<float*>(ws);
+        ws += align_up(parts * d.head_dim * sizeof(float), 256);
+        a.ws_ml = reinterpret_cast<float2*>(ws);
     } else {
         a.ws_o = nullptr;
         a.ws_ml = nullptr;

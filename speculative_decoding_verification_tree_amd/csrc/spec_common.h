@@ -30,33 +30,108 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        T w = __shfl_xor(v, o, kWave);
-        v = w > v ? w : v;
-    }
-    return v;
+// ---- cross-lane exchange without the LDS crossbar -------------------------
+// DPP moves within a 16-lane row, v_permlane16/32_swap across rows.  Each
+// helper returns the value held by the partner lane (xor 1, xor 2, mirror in
+// 8, mirror in 16) or, for the swaps, the pair whose combination pairs every
+// lane with its xor-16 / xor-32 partner.
+__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) { return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false); }
+__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) { return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); }
+__device__ __forceinline__ uint32_t dpp_mirror8(uint32_t v) { return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false); }
+__device__ __forceinline__ uint32_t dpp_mirror16(uint32_t v) { return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false); }
+
+template <class F>
+__device__ __forceinline__ float xrow_combine16(float v, F op) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <class F>
+__device__ __forceinline__ float xrow_combine32(float v, F op) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+// Reduction over the four lanes n, n+16, n+32, n+48 (one per 16-lane row).
+__device__ __forceinline__ float max_across_rows(float v) {
+    auto mx = [](float x, float y) { return fmaxf(x, y); };
+    return xrow_combine32(xrow_combine16(v, mx), mx);
+}
+__device__ __forceinline__ float sum_across_rows(float v) {
+    auto ad = [](float x, float y) { return x + y; };
+    return xrow_combine32(xrow_combine16(v, ad), ad);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, __uint_as_float(dpp_xor1(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_xor2(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_mirror8(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_mirror16(__float_as_uint(v))));
+    return max_across_rows(v);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v += __uint_as_float(dpp_xor1(__float_as_uint(v)));
+    v += __uint_as_float(dpp_xor2(__float_as_uint(v)));
+    v += __uint_as_float(dpp_mirror8(__float_as_uint(v)));
+    v += __uint_as_float(dpp_mirror16(__float_as_uint(v)));
+    return sum_across_rows(v);
+}
+
+// 64-bit lane exchange: both halves through the same permutation.
+template <uint32_t (*MOVE)(uint32_t)>
+__device__ __forceinline__ double move_d(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint64_t lo = MOVE(static_cast<uint32_t>(u)), hi = MOVE(static_cast<uint32_t>(u >> 32));
+    return __builtin_bit_cast(double, lo | (hi << 32));
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+    v += move_d<dpp_xor1>(v);
+    v += move_d<dpp_xor2>(v);
+    v += move_d<dpp_mirror8>(v);
+    v += move_d<dpp_mirror16>(v);
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    auto a = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(u), static_cast<uint32_t>(u), false, false);
+    auto b = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(u >> 32), static_cast<uint32_t>(u >> 32), false, false);
+    v = __builtin_bit_cast(double, static_cast<uint64_t>(a[0]) | (static_cast<uint64_t>(b[0]) << 32)) +
+        __builtin_bit_cast(double, static_cast<uint64_t>(a[1]) | (static_cast<uint64_t>(b[1]) << 32));
+    const uint64_t w = __builtin_bit_cast(uint64_t, v);
+    a = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(w), static_cast<uint32_t>(w), false, false);
+    b = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(w >> 32), static_cast<uint32_t>(w >> 32), false, false);
+    return __builtin_bit_cast(double, static_cast<uint64_t>(a[0]) | (static_cast<uint64_t>(b[0]) << 32)) +
+           __builtin_bit_cast(double, static_cast<uint64_t>(a[1]) | (static_cast<uint64_t>(b[1]) << 32));
+}
+
+__device__ __forceinline__ void argmax_step(float& v, int& i, float w, int j) {
+    if (w > v || (w == v && j < i)) {
+        v = w;
+        i = j;
+    }
 }
 
 // (value, index) argmax across a wavefront: largest value, lowest index on ties.
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        float w = __shfl_xor(v, o, kWave);
-        int j = __shfl_xor(i, o, kWave);
-        if (w > v || (w == v && j < i)) {
-            v = w;
-            i = j;
-        }
+    argmax_step(v, i, __uint_as_float(dpp_xor1(__float_as_uint(v))), static_cast<int>(dpp_xor1(i)));
+    argmax_step(v, i, __uint_as_float(dpp_xor2(__float_as_uint(v))), static_cast<int>(dpp_xor2(i)));
+    argmax_step(v, i, __uint_as_float(dpp_mirror8(__float_as_uint(v))), static_cast<int>(dpp_mirror8(i)));
+    argmax_step(v, i, __uint_as_float(dpp_mirror16(__float_as_uint(v))), static_cast<int>(dpp_mirror16(i)));
+    {
+        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        const auto b = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(i), static_cast<uint32_t>(i), false, false);
+        float v0 = __uint_as_float(a[0]);
+        int i0 = static_cast<int>(b[0]);
+        argmax_step(v0, i0, __uint_as_float(a[1]), static_cast<int>(b[1]));
+        v = v0;
+        i = i0;
+    }
+    {
+        const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        const auto b = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(i), static_cast<uint32_t>(i), false, false);
+        float v0 = __uint_as_float(a[0]);
+        int i0 = static_cast<int>(b[0]);
+        argmax_step(v0, i0, __uint_as_float(a[1]), static_cast<int>(b[1]));
+        v = v0;
+        i = i0;
     }
 }
 

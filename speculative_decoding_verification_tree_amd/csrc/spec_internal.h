@@ -35,6 +35,7 @@ struct AcceptPlan {
 };
 
 AcceptPlan plan_accept(int B, int N, int V);
+int max_accept_vocab();
 
 int launch_accept(int rule, int B, int N, int V, const float* logits, const float* draft,
                   const int32_t* tokens, const int32_t* parent, const float* u_accept,

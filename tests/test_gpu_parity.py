@@ -117,6 +117,8 @@ def test_accept_full_size(cid):
     (1, dict(batch=32, drafts=0)),                                # N = 1: bonus only
     (5, dict(batch=6, vocab=5000, nodes=64, max_depth=63)),       # deep tree, max N
     (4, dict(batch=32, vocab=20000, draft_noise=[0.0])),          # q == p: all accepted
+    (2, dict(batch=3, vocab=300000)),                             # > 64 vocabulary chunks
+    (3, dict(batch=2, vocab=300001, temperature=0.0)),            # > 64 chunks, argmax path
 ])
 def test_accept_edge_cases(cid, over):
     w = generate(scaled(cid, **over), with_attention=False)

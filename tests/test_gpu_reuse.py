@@ -1,0 +1,80 @@
+"""GPU: workspaces reused across calls (the completion counters must come back
+to zero after every call) and the step replayed from a HIP graph (each replay,
+with eager work in between, must reproduce the eager result)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import speculative_decoding_verification_tree_amd as sv
+from workloads import generate, scaled
+from tests.gpu_helpers import (announce, check_accept, check_attention, dev_kv, host_f64, oracle_accept)
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev_inputs(w):
+    return dict(
+        q=dev_kv(w.q, w.dtype), k=dev_kv(w.k_cache, w.dtype), v=dev_kv(w.v_cache, w.dtype),
+        pl=torch.from_numpy(w.prefix_len).cuda(),
+        par=None if w.is_chain else torch.from_numpy(w.parent).cuda(),
+        lg=torch.from_numpy(w.target_logits).cuda(), tk=torch.from_numpy(w.tokens).cuda(),
+        dp=torch.from_numpy(w.draft_probs).cuda() if w.draft_probs is not None else None,
+        ua=torch.from_numpy(w.u_accept).cuda(), us=torch.from_numpy(w.u_sample).cuda())
+
+
+def test_shared_workspaces_across_calls():
+    ws_attn = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    ws_acc = torch.zeros(16 << 20, dtype=torch.uint8, device="cuda")
+    cases = [scaled(2, prefix_len=900), scaled(5, batch=2, prefix_len=700, vocab=9000),
+             scaled(4, batch=5, prefix_len=(50, 1300), vocab=7000), scaled(2, prefix_len=900)]
+    for i, cfg in enumerate(cases):
+        w = generate(cfg, variant=i)
+        announce(f"workspace reuse call {i}: cfg{cfg['id']} B={w.B} N={w.N} L<={w.max_prefix_len}")
+        d = _dev_inputs(w)
+        out = sv.spec_verify_attn(d["q"], d["k"], d["v"], d["pl"], d["par"], w.max_prefix_len, workspace=ws_attn)
+        al, path, otok = sv.spec_accept_reject(d["lg"], d["dp"], d["tk"], d["par"], d["ua"], d["us"],
+                                               w.temperature, workspace=ws_acc)
+        torch.cuda.synchronize()
+        ref = oracle.tree_attn(w.q, w.k_cache, w.v_cache, w.prefix_len, None if w.is_chain else w.parent, w.dtype)
+        check_attention(host_f64(out), ref, f"reuse {i}")
+        gpu = dict(accept_len=al.cpu().numpy(), path=path.cpu().numpy(), out_tokens=otok.cpu().numpy())
+        check_accept(w, gpu, oracle_accept(w))
+
+
+def test_graph_replay_matches_eager():
+    w = generate(scaled(4, batch=6, prefix_len=(100, 2500), vocab=12000))
+    announce("graph replay: cfg4 B=6")
+    d = _dev_inputs(w)
+    ws_attn = torch.zeros(max(sv.spec_verify_attn_workspace_bytes(
+        sv.attn_desc(w.B, w.N, w.Hq, w.Hkv, w.D, w.cap, torch.bfloat16), w.max_prefix_len), 1),
+        dtype=torch.uint8, device="cuda")
+    ws_acc = torch.zeros(sv.spec_accept_workspace_bytes(w.B, w.N, w.V), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d["q"])
+    al = torch.empty(w.B, dtype=torch.int32, device="cuda")
+    path = torch.empty(w.B, w.N, dtype=torch.int32, device="cuda")
+    otok = torch.empty(w.B, w.N, dtype=torch.int32, device="cuda")
+
+    def step():
+        sv.spec_verify_attn(d["q"], d["k"], d["v"], d["pl"], d["par"], w.max_prefix_len, out=out, workspace=ws_attn)
+        sv.spec_accept_reject(d["lg"], d["dp"], d["tk"], d["par"], d["ua"], d["us"], w.temperature, al, path, otok,
+                              workspace=ws_acc)
+
+    step()
+    torch.cuda.synchronize()
+    eager = (out.clone(), al.clone(), path.clone(), otok.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        out.zero_()
+        otok.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[0]), rep
+        assert torch.equal(al, eager[1]) and torch.equal(path, eager[2]) and torch.equal(otok, eager[3]), rep
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+    ref = oracle.tree_attn(w.q, w.k_cache, w.v_cache, w.prefix_len, None, w.dtype)
+    check_attention(host_f64(eager[0]), ref, "graph")
