@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (default: the Llama-3-8B chain)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline sample budget")
+    ap.add_argument("--rotate-mb", type=int, default=ROTATE_BYTES >> 20,
+                    help="input bytes cycled between reuses of one copy (default beats the 256 MB Infinity Cache; "
+                         "0 keeps two copies, i.e. cache-warm)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration)")
     return ap.parse_args()
@@ -94,7 +97,7 @@ def main():
     w = generate(cfg, poison=False)
     B, N, V = w.B, w.N, w.V
     touched = attn_bytes(w) + (N * V * 4) * (2 if w.draft_probs is not None else 1)
-    ncopies = max(2, math.ceil(ROTATE_BYTES / max(touched, 1)))
+    ncopies = max(2, math.ceil((args.rotate_mb << 20) / max(touched, 1)))
     reps = max(1, math.ceil(args.steps / ncopies))
     # Every commit advances a copy's prefix by at most N rows (a real decode
     # loop does the same); size the capacity and the prefix bound for all uses:
@@ -244,8 +247,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if bf16 else "f32",
-        "data": "synthetic (seeded; inputs resident in HBM, rotated over "
-                f"{ncopies} copies to defeat the 256 MB Infinity Cache)",
+        "data": f"synthetic (seeded; inputs resident in HBM, rotated over {ncopies} copies, "
+                f"{ncopies * touched / 2**20:.0f} MB between reuses of one copy)",
         "config": {
             "workload": f"{name}: B={B}, Hq={w.Hq}/Hkv={w.Hkv}, D={w.D}, {w.dtype} KV prefix "
                         f"{int(w.prefix_len.min())}..{int(w.prefix_len.max())}, N={N} nodes "

@@ -199,10 +199,13 @@ __global__ __launch_bounds__(64 * WK) void attn_mfma(AttnArgs a) {
     unsigned char* vt = s_buf + wave * VT_BYTES;
 
     for (; kb < k1; kb += 32 * WK) {
-        // Prefetch the wave's next block while this one is processed.
+        // Prefetch the wave's next block while this one is processed.  The
+        // loads are unconditional (past the split end they re-read this
+        // block: cache hits) so the wait before using this block counts only
+        // the older loads and never drains the prefetch.
         KVBlock<D> nxt;
         const int kn = kb + 32 * WK;
-        if (kn < k1) load_kv_block<D>(nxt, kbase, vbase, kn, Tk - 1, n16, q4, vch, vkg);
+        load_kv_block<D>(nxt, kbase, vbase, kn < k1 ? kn : kb, Tk - 1, n16, q4, vch, vkg);
 
         // Transpose V into LDS (row d holds the block's 32 keys); keys at or
         // past the split end are zeroed so no stale value reaches P*V.
@@ -215,25 +218,25 @@ __global__ __launch_bounds__(64 * WK) void attn_mfma(AttnArgs a) {
             const int key0 = vkg * KPL;
             const int pch = (key0 >> 3) ^ vt_swz(d);
             unsigned char* dst = vt + d * 64 + pch * 16 + (key0 & 7) * 2;
-            const int sh = 16 * (t & 1);
+            // element t of two keys' rows -> one dword (byte select: low or high half)
+            const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
             if constexpr (KPL == 8) {
                 u32x4 wv;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t lo = (cur.vr[2 * e][t >> 1] >> sh) & 0xFFFFu;
-                    const uint32_t hi = (cur.vr[2 * e + 1][t >> 1] >> sh) & 0xFFFFu;
-                    wv[e] = lo | (hi << 16);
-                }
+                for (int e = 0; e < 4; ++e)
+                    wv[e] = __builtin_amdgcn_perm(cur.vr[2 * e + 1][t >> 1], cur.vr[2 * e][t >> 1], sel);
                 *reinterpret_cast<u32x4*>(dst) = wv;
             } else {
                 uint2 wv;
-                wv.x = ((cur.vr[0][t >> 1] >> sh) & 0xFFFFu) | (((cur.vr[1][t >> 1] >> sh) & 0xFFFFu) << 16);
-                wv.y = ((cur.vr[2][t >> 1] >> sh) & 0xFFFFu) | (((cur.vr[3][t >> 1] >> sh) & 0xFFFFu) << 16);
+                wv.x = __builtin_amdgcn_perm(cur.vr[1][t >> 1], cur.vr[0][t >> 1], sel);
+                wv.y = __builtin_amdgcn_perm(cur.vr[3][t >> 1], cur.vr[2][t >> 1], sel);
                 *reinterpret_cast<uint2*>(dst) = wv;
             }
         }
         wave_lds_sync();
 
+        // Blocks wholly inside the prefix and the split need no key mask.
+        const bool interior = kb + 32 <= L && kb + 32 <= k1;
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
             f32x4 st[2];
@@ -246,33 +249,51 @@ __global__ __launch_bounds__(64 * WK) void attn_mfma(AttnArgs a) {
                                                                   acc, 0, 0, 0);
                 st[h] = acc;
             }
+            // This lane's keys are kb + 8*q4 + e, e = 0..7 (e = 4h + ii).
+            // Bit e of the mask: key below the split end and either a prefix
+            // key or a tree key on the row's root path.
+            uint32_t kmask = 0xFFu;
+            if (!interior) {
+                const int base = kb + 8 * q4;
+                const int nend = min(max(k1 - base, 0), 8);
+                const int npre = min(max(L - base, 0), 8);
+                const int sh = base - L;  // tree offset of key e is sh + e
+                const uint32_t tree = sh >= 0 ? static_cast<uint32_t>(anc[t] >> min(sh, 63))
+                                              : static_cast<uint32_t>(anc[t] << min(-sh, 63));
+                const uint32_t pre = (1u << npre) - 1u;
+                kmask = ((tree & 0xFFu) | pre) & ((1u << nend) - 1u);
+            }
             float s[8];
             float bm = -INFINITY;
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
-                    const int key = kb + 8 * q4 + 4 * h + ii;
-                    const bool ok = key < k1 && (key < L || ((anc[t] >> (key - L)) & 1ull));
-                    const float x = ok ? st[h][ii] * a.scale_log2 : -INFINITY;
-                    s[4 * h + ii] = x;
+                    const int e = 4 * h + ii;
+                    const float x = ((kmask >> e) & 1u) ? st[h][ii] * a.scale_log2 : -INFINITY;
+                    s[e] = x;
                     bm = fmaxf(bm, x);
                 }
             bm = max_across_rows(bm);
-            const float mn = fmaxf(m_run[t], bm);
-            const float mu = mn == -INFINITY ? 0.f : mn;
-            const float alpha = exp2f(m_run[t] - mu);
+            // Lazy rescale: keep the running max unless a row's block max
+            // exceeds it by more than 8 (probabilities stay <= 2^8, exact in
+            // fp32 and as precise in bf16); the decision is wave-uniform.
+            if (__builtin_amdgcn_ballot_w64(bm > m_run[t] + 8.f) != 0ull) {
+                const float mn = fmaxf(m_run[t], bm);
+                const float alpha = m_run[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[t] - mn);
+                l_run[t] *= alpha;
+#pragma unroll
+                for (int c = 0; c < NC16; ++c) o[t][c] *= alpha;  // o holds row n16 of this lane
+                m_run[t] = mn;
+            }
+            const float mu = m_run[t] == -INFINITY ? 0.f : m_run[t];
             float rs = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                s[e] = exp2f(s[e] - mu);
+                s[e] = __builtin_amdgcn_exp2f(s[e] - mu);
                 rs += s[e];
             }
-            rs = sum_across_rows(rs);
-            l_run[t] = l_run[t] * alpha + rs;
-            m_run[t] = mn;
-#pragma unroll
-            for (int c = 0; c < NC16; ++c) o[t][c] *= alpha;  // o holds row n16 of this lane
+            l_run[t] += sum_across_rows(rs);
             u32x4 pp;
             pp[0] = pack_bf16x2(s[0], s[1]);
             pp[1] = pack_bf16x2(s[2], s[3]);
