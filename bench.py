@@ -2,7 +2,10 @@
 
 A step is the whole hot path over one batch: tree-verify attention
 (spec_verify_attn), acceptance (spec_accept_reject / spec_accept_typical) and
-the KV commit (spec_commit_kv).  The default workload is the Llama-3-8B-shaped
+the KV commit (spec_commit_kv).  Every step runs all three on the same fixed
+workload: the commit moves the accepted rows and advances its own copy of the
+prefix lengths inside spare cache capacity, while attention keeps reading the
+workload's prefix lengths.  The default workload is the Llama-3-8B-shaped
 chain (batch 1, 32 query / 8 KV heads, head dim 128, bf16 KV prefix 2048,
 K = 5 drafts, vocabulary 128256, T = 1, rejection rule).
 
@@ -98,13 +101,17 @@ def main():
     B, N, V = w.B, w.N, w.V
     touched = attn_bytes(w) + (N * V * 4) * (2 if w.draft_probs is not None else 1)
     ncopies = max(2, math.ceil((args.rotate_mb << 20) / max(touched, 1)))
-    reps = max(1, math.ceil(args.steps / ncopies))
-    # Every commit advances a copy's prefix by at most N rows (a real decode
-    # loop does the same); size the capacity and the prefix bound for all uses:
-    # eager warm-up, then (1 + reps) replays each of the step and commit graphs.
-    uses = math.ceil(max(args.warmup, ncopies) / ncopies) + 2 * (reps + 1) + 1
-    mpl = int(w.prefix_len.max()) + uses * N
-    cap = mpl + N
+    # One graph replay runs `spg` steps over the copies in rotation; at least
+    # 32 steps per replay so the per-replay launch cost is amortised.
+    spg = ncopies * math.ceil(32 / ncopies)
+    reps = max(1, math.ceil(args.steps / spg))
+    # The commit advances its own copy of the prefix lengths by at most N rows
+    # per use (attention keeps reading the fixed workload's lengths), so the
+    # cache gets headroom for every use: eager warm-up, then (1 + reps)
+    # replays each of the step and commit graphs.
+    uses = math.ceil(max(args.warmup, ncopies) / ncopies) + 2 * (reps + 1) * (spg // ncopies) + 1
+    mpl = int(w.prefix_len.max())
+    cap = mpl + (uses + 1) * N
 
     def to_dev(arr, bf16):
         t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16) if bf16 else np.ascontiguousarray(arr))
@@ -128,7 +135,8 @@ def main():
     copies = []
     for _ in range(ncopies):
         c = {k: (t.clone() if t is not None else None) for k, t in base.items()}
-        c["pl"] = torch.from_numpy(w.prefix_len.copy()).to(dev)
+        c["pl"] = torch.from_numpy(w.prefix_len.copy()).to(dev)        # read by attention
+        c["pl_commit"] = torch.from_numpy(w.prefix_len.copy()).to(dev)  # advanced by the commit
         c["out"] = torch.empty_like(c["q"])
         c["al"] = torch.empty(B, dtype=torch.int32, device=dev)
         c["path"] = torch.empty(B, N, dtype=torch.int32, device=dev)
@@ -150,7 +158,7 @@ def main():
                                    c["al"], c["path"], c["otok"], workspace=acc_ws)
 
     def commit(c):
-        sv.spec_commit_kv(c["k"], c["v"], c["pl"], c["path"], c["al"])
+        sv.spec_commit_kv(c["k"], c["v"], c["pl_commit"], c["path"], c["al"])
 
     def step(c):
         attn(c)
@@ -167,9 +175,9 @@ def main():
     def capture(fns):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for c in copies:
+            for i in range(spg):
                 for fn in fns:
-                    fn(c)
+                    fn(copies[i % ncopies])
         return g
 
     g_step = capture([attn, accept, commit])
@@ -189,9 +197,9 @@ def main():
             g.replay()
         t1.record()
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / (reps * ncopies)
+        return t0.elapsed_time(t1) / (reps * spg)
 
-    K = reps * ncopies
+    K = reps * spg
     ms_step = timed(g_step, reps)
     attn_ms = timed(g_attn, reps)
     accept_ms = timed(g_acc, reps)

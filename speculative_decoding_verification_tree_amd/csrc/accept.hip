@@ -69,14 +69,19 @@ struct AcceptArgs {
     Decision* dec;
     ChunkStat* cstat;
     int B, N, V, chunk, nchunk, rule;  // rule 0 = rejection, 1 = typical
+    int vec4;                          // rows are 16-byte aligned: 16-byte loads
     float T, eps, delta;
 };
 
 constexpr int kThreads = 256;
+
+// Helpers that take LDS arrays by pointer are force-inlined: called out of
+// line they receive generic pointers, whose LDS-aperture test this compiler
+// fails to select.
 constexpr int kRowsPerWave = kMaxNodes / 4;
 constexpr int kMaxChunks = 1024;
 
-__device__ double block_sum_d(double v, double* s_red) {
+__device__ __forceinline__ double block_sum_d(double v, double* s_red) {
     v = wave_sum(v);
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     __syncthreads();
@@ -85,7 +90,7 @@ __device__ double block_sum_d(double v, double* s_red) {
     return s_red[0] + s_red[1] + s_red[2] + s_red[3];
 }
 
-__device__ void block_sum2_d(double& a, double& b, double* s_red) {
+__device__ __forceinline__ void block_sum2_d(double& a, double& b, double* s_red) {
     a = wave_sum(a);
     b = wave_sum(b);
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -99,7 +104,7 @@ __device__ void block_sum2_d(double& a, double& b, double* s_red) {
     b = s_red[4] + s_red[5] + s_red[6] + s_red[7];
 }
 
-__device__ void block_argmax(float& v, int& i, float* s_v, int* s_i) {
+__device__ __forceinline__ void block_argmax(float& v, int& i, float* s_v, int* s_i) {
     wave_argmax(v, i);
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     __syncthreads();
@@ -122,18 +127,58 @@ __device__ __forceinline__ float target_prob(float l, float M, float T, float in
     return expf((l - M) / T) * invS;
 }
 
+// Element e of this thread's share of a chunk starting at x0: strided by
+// the block (coalesced), in runs of four with 16-byte loads.
+__device__ __forceinline__ int elem_index(int x0, int e, bool vec4) {
+    return vec4 ? x0 + 4 * (static_cast<int>(threadIdx.x) + kThreads * (e >> 2)) + (e & 3)
+                : x0 + static_cast<int>(threadIdx.x) + kThreads * e;
+}
+
+template <int EPT>
+struct Vals {
+    float v[EPT];
+};
+
+template <int EPT>
+__device__ __forceinline__ Vals<EPT> load_chunk(const float* row, int x0, int x1, bool vec4, float fill) {
+    Vals<EPT> r;
+    if (vec4) {
+#pragma unroll
+        for (int j = 0; j < EPT / 4; ++j) {
+            const int x = x0 + 4 * (static_cast<int>(threadIdx.x) + kThreads * j);
+            if (x + 3 < x1) {
+                const float4 v = *reinterpret_cast<const float4*>(row + x);
+                r.v[4 * j] = v.x;
+                r.v[4 * j + 1] = v.y;
+                r.v[4 * j + 2] = v.z;
+                r.v[4 * j + 3] = v.w;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) r.v[4 * j + k] = x + k < x1 ? row[x + k] : fill;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int x = x0 + static_cast<int>(threadIdx.x) + kThreads * e;
+            r.v[e] = x < x1 ? row[x] : fill;
+        }
+    }
+    return r;
+}
+
 // Chunk statistics of one target row: lowest-index argmax, then (T > 0) the
 // exp sums relative to the chunk max.
 template <int EPT>
-__device__ void row_chunk_stats(const float* row, int x0, int x1, float T, float& best, int& bi, double& S,
-                                double& A, float* s_v, int* s_i, double* s_red) {
-    float val[EPT];
+__device__ __forceinline__ void row_chunk_stats(const float* row, int x0, int x1, bool vec4, float T, float& best, int& bi,
+                                double& S, double& A, float* s_v, int* s_i, double* s_red) {
+    const Vals<EPT> vals = load_chunk<EPT>(row, x0, x1, vec4, -INFINITY);
+    const float* val = vals.v;
     best = -INFINITY;
     bi = 0x7fffffff;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-        const int x = x0 + threadIdx.x + e * kThreads;
-        val[e] = x < x1 ? row[x] : -INFINITY;
+        const int x = elem_index(x0, e, vec4);
         if (x < x1 && (val[e] > best || (val[e] == best && x < bi))) {
             best = val[e];
             bi = x;
@@ -145,8 +190,7 @@ __device__ void row_chunk_stats(const float* row, int x0, int x1, float T, float
     if (T > 0.f) {
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
-            const int x = x0 + threadIdx.x + e * kThreads;
-            if (x < x1) {
+            if (elem_index(x0, e, vec4) < x1) {
                 const float t = (val[e] - best) / T;
                 const float ex = expf(t);
                 S += static_cast<double>(ex);
@@ -159,7 +203,7 @@ __device__ void row_chunk_stats(const float* row, int x0, int x1, float T, float
 
 // ---------------------------------------------------------------------------
 // Parent array of request b in LDS, and which nodes have children.
-__device__ void load_tree(const AcceptArgs& a, int b, int* s_par, int* s_has) {
+__device__ __forceinline__ void load_tree(const AcceptArgs& a, int b, int* s_par, int* s_has) {
     const int tid = threadIdx.x;
     if (tid < kMaxNodes) s_has[tid] = 0;
     if (tid < a.N) s_par[tid] = tree_parent(a.parent, a.N, b, tid);
@@ -171,7 +215,10 @@ __device__ void load_tree(const AcceptArgs& a, int b, int* s_par, int* s_has) {
 // Decision of request b from the chunk statistics.  Every accept_sample
 // workgroup of the request computes it (same inputs, same code, same result);
 // only the writer stores path, accepted tokens, accept_len and the record.
-__device__ void decide_request(const AcceptArgs& a, int b, bool writer, const int* s_par, const int* s_has,
+// (Templated on the caller's chunk width only so that each kernel owns its
+// copy of the LDS arrays below.)
+template <int EPT>
+__device__ __forceinline__ void decide_request(const AcceptArgs& a, int b, bool writer, const int* s_par, const int* s_has,
                                Decision* s_dec) {
     const int N = a.N, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __shared__ float s_M[kMaxNodes];
@@ -352,7 +399,7 @@ __global__ __launch_bounds__(kThreads) void accept_rowstats(AcceptArgs a) {
     float best;
     int bi;
     double S, A;
-    row_chunk_stats<EPT>(row, x0, x1, a.T, best, bi, S, A, s_v, s_i, s_red);
+    row_chunk_stats<EPT>(row, x0, x1, a.vec4 != 0, a.T, best, bi, S, A, s_v, s_i, s_red);
     if (threadIdx.x == 0) {
         RowStat rs;
         rs.S = S;
@@ -372,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void accept_sample(AcceptArgs a) {
     __shared__ float s_v[4];
     __shared__ int s_i[4];
     load_tree(a, b, s_par, s_has);
-    decide_request(a, b, c == 0, s_par, s_has, &s_dec);
+    decide_request<EPT>(a, b, c == 0, s_par, s_has, &s_dec);
     const Decision d = s_dec;
     if (d.mode == MODE_DONE) return;
     const float* row = a.logits + (static_cast<size_t>(b) * a.N + d.v) * a.V;
@@ -381,16 +428,20 @@ __global__ __launch_bounds__(kThreads) void accept_sample(AcceptArgs a) {
     cs.m1 = cs.m2 = 0.0;
     cs.M = 0.f;
     cs.arg = 0;
+    const bool vec4 = a.vec4 != 0;
     if (d.mode == MODE_RESID) {
         const float* qrow = a.draft + (static_cast<size_t>(b) * a.N + d.c) * a.V;
         const float invS = static_cast<float>(1.0 / d.S);
+        const Vals<EPT> lvals = load_chunk<EPT>(row, x0, x1, vec4, -INFINITY);
+        const Vals<EPT> qvals = load_chunk<EPT>(qrow, x0, x1, vec4, 0.f);
+        const float* lv = lvals.v;
+        const float* qv = qvals.v;
         double r = 0.0, p = 0.0;
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
-            const int x = x0 + threadIdx.x + e * kThreads;
-            if (x < x1) {
-                const float pv = target_prob(row[x], d.M, a.T, invS);
-                r += static_cast<double>(fmaxf(pv - qrow[x], 0.f));
+            if (elem_index(x0, e, vec4) < x1) {
+                const float pv = target_prob(lv[e], d.M, a.T, invS);
+                r += static_cast<double>(fmaxf(pv - qv[e], 0.f));
                 p += static_cast<double>(pv);
             }
         }
@@ -401,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void accept_sample(AcceptArgs a) {
         float best;
         int bi;
         double S, A;
-        row_chunk_stats<EPT>(row, x0, x1, d.mode == MODE_BONUS ? a.T : 0.f, best, bi, S, A, s_v, s_i, s_red);
+        row_chunk_stats<EPT>(row, x0, x1, vec4, d.mode == MODE_BONUS ? a.T : 0.f, best, bi, S, A, s_v, s_i, s_red);
         cs.M = best;
         cs.arg = bi;
         cs.m1 = S;
@@ -420,6 +471,7 @@ __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
     __shared__ double s_red[8];
     __shared__ double s_w[kMaxChunks];
     __shared__ double s_scan[kThreads];
+    __shared__ float s_wt[EPT * kThreads];
     __shared__ int s_pick;
     __shared__ double s_base;
     if (tid == 0) s_d = a.dec[b];
@@ -504,31 +556,45 @@ __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
     if (ih != 0x7fffffff && hit == ih) s_base = hit_base;
     __syncthreads();
 
-    // Token inside the chosen chunk: contiguous runs per thread, ascending.
+    // Token inside the chosen chunk.  Weights are computed from coalesced
+    // loads and staged in LDS (fp32, the same values accept_sample summed);
+    // each thread then scans a contiguous run in ascending token order.
     const int pc = s_pick;
     const int x0 = pc * a.chunk, x1 = min(x0 + a.chunk, a.V);
-    const int xs = x0 + tid * EPT;
+    const bool vec4 = a.vec4 != 0;
     const float* row = a.logits + (static_cast<size_t>(b) * a.N + d.v) * a.V;
     const float* qrow = d.mode == MODE_RESID ? a.draft + (static_cast<size_t>(b) * a.N + d.c) * a.V : nullptr;
     const float invS = d.mode == MODE_RESID ? static_cast<float>(1.0 / d.S) : 0.f;
     const float Mc = cs[pc].M;
     const double scale = d.mode == MODE_BONUS ? exp((static_cast<double>(Mc) - Mg) / T) : 1.0;
+    {
+        const Vals<EPT> lvals = load_chunk<EPT>(row, x0, x1, vec4, -INFINITY);
+        const Vals<EPT> qvals = d.mode == MODE_RESID ? load_chunk<EPT>(qrow, x0, x1, vec4, 0.f) : Vals<EPT>{};
+        const float* lv = lvals.v;
+        const float* qv = qvals.v;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int x = elem_index(x0, e, vec4);
+            float wgt = 0.f;
+            if (x < x1) {
+                if (d.mode == MODE_RESID) {
+                    const float pv = target_prob(lv[e], d.M, a.T, invS);
+                    wgt = usep ? pv : fmaxf(pv - qv[e], 0.f);
+                } else {
+                    wgt = expf((lv[e] - Mc) / a.T);
+                }
+            }
+            if (x - x0 < EPT * kThreads) s_wt[x - x0] = wgt;
+        }
+    }
+    __syncthreads();
+    const int xs = x0 + tid * EPT;
     double wv[EPT];
     run = 0.0;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-        const int x = xs + e;
-        double wgt = 0.0;
-        if (x < x1) {
-            if (d.mode == MODE_RESID) {
-                const float pv = target_prob(row[x], d.M, a.T, invS);
-                wgt = usep ? static_cast<double>(pv) : static_cast<double>(fmaxf(pv - qrow[x], 0.f));
-            } else {
-                wgt = static_cast<double>(expf((row[x] - Mc) / a.T)) * scale;
-            }
-        }
-        wv[e] = wgt;
-        run += wgt;
+        wv[e] = static_cast<double>(s_wt[tid * EPT + e]) * scale;
+        run += wv[e];
     }
     __syncthreads();
     s_scan[tid] = run;
@@ -628,6 +694,8 @@ int launch_accept(int rule, int B, int N, int V, const float* logits, const floa
     a.chunk = p.chunk;
     a.nchunk = p.nchunk;
     a.rule = rule;
+    a.vec4 = (V % 4 == 0) && (reinterpret_cast<uintptr_t>(logits) % 16 == 0) &&
+             (draft == nullptr || reinterpret_cast<uintptr_t>(draft) % 16 == 0);
     a.T = temperature;
     a.eps = epsilon;
     a.delta = delta;
