@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 ROTATE_BYTES = 640 << 20
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_llama3_8b_chain_traffic.json")
 
 
 def parse():
