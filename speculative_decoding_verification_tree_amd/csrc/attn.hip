@@ -8,12 +8,13 @@
 // parallel scoring of all draft positions is the "Speculative Sampling"
 // section of the same page).
 //
-// Work decomposition: the key axis of one (b, g) is cut into fixed-size
-// chunks (split-KV); a workgroup owns one chunk and every query row of its
-// row group, so each KV element is read from HBM once and shared by all
-// N * G rows.  Within a workgroup the waves take interleaved 32-key blocks and
-// merge their (max, sum, O) at the end through LDS; chunks merge in
-// attn_combine with an exact log-sum-exp rescale.
+// Work decomposition: the key axis of one (b, g) is shared by S splits
+// (split-KV, S = ceil(keys / chunk)); split s and its waves take the 32-key
+// blocks s*WK + wave + t*S*WK, so the splits of a slab sweep it front to back
+// together.  A workgroup holds every query row of its row group, so each KV
+// element is read from HBM once and shared by all N * G rows.  The waves merge
+// their (max, sum, O) at the end through LDS; splits merge in attn_combine
+// with an exact log-sum-exp rescale.
 //
 // bf16 MFMA path (v_mfma_f32_16x16x32_bf16):
 //   S^T = K * Q^T : A = 16 keys x 32 dims of K straight from HBM (16-byte
@@ -155,7 +156,11 @@ __global__ __launch_bounds__(64 * WK) void attn_mfma(AttnArgs a) {
     // the prefix length itself, the first KV block (rows clamped to the cache,
     // out-of-range values masked once L is known), the tree and the queries.
     const int L = a.prefix_len[b];
-    int kb = k0 + wave * 32;
+    // Split s of a (request, kv head) takes the interleaved 32-key blocks
+    // s*WK + wave + t*S*WK, S = the request's split count: the splits of one
+    // slab sweep it together, front to back, like one streaming read.
+    const int first_blk = w.s * WK + wave;
+    int kb = first_blk * 32;
     KVBlock<D> cur;
     load_kv_block<D>(cur, kbase, vbase, kb, a.cap - 1, n16, q4, vch, vkg);
     build_anc(a, b, s_anc);
@@ -181,8 +186,9 @@ __global__ __launch_bounds__(64 * WK) void attn_mfma(AttnArgs a) {
     const int Tk = L + a.N;
     if (L < 0 || Tk > a.cap || Tk > a.max_keys) return;  // outside the contract: leave out unwritten
     if (k0 >= Tk) return;
-    const int k1 = min(k0 + a.chunk, Tk);
     const int nsplit = (Tk + a.chunk - 1) / a.chunk;
+    const int k1 = Tk;                  // keys past the request's end are masked
+    const int kstep = 32 * WK * nsplit;  // interleave stride of this request
     uint64_t anc[RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t) anc[t] = rnode[t] >= 0 ? s_anc[rnode[t]] : ~0ull;
@@ -198,13 +204,13 @@ __global__ __launch_bounds__(64 * WK) void attn_mfma(AttnArgs a) {
     }
     unsigned char* vt = s_buf + wave * VT_BYTES;
 
-    for (; kb < k1; kb += 32 * WK) {
+    for (; kb < k1; kb += kstep) {
         // Prefetch the wave's next block while this one is processed.  The
-        // loads are unconditional (past the split end they re-read this
-        // block: cache hits) so the wait before using this block counts only
-        // the older loads and never drains the prefetch.
+        // loads are unconditional (past the end they re-read this block:
+        // cache hits) so the wait before using this block counts only the
+        // older loads and never drains the prefetch.
         KVBlock<D> nxt;
-        const int kn = kb + 32 * WK;
+        const int kn = kb + kstep;
         load_kv_block<D>(nxt, kbase, vbase, kn < k1 ? kn : kb, Tk - 1, n16, q4, vch, vkg);
 
         // Transpose V into LDS (row d holds the block's 32 keys); keys at or
