@@ -8,23 +8,40 @@
 // parallel scoring of all draft positions is the "Speculative Sampling"
 // section of the same page).
 //
-// Work decomposition: the key axis of one (b, g) is shared by S splits
-// (split-KV, S = ceil(keys / chunk)); split s and its waves take the 32-key
-// blocks s*WK + wave + t*S*WK, so the splits of a slab sweep it front to back
-// together.  A workgroup holds every query row of its row group, so each KV
-// element is read from HBM once and shared by all N * G rows.  The waves merge
-// their (max, sum, O) at the end through LDS; splits merge in attn_combine
-// with an exact log-sum-exp rescale.
+// Work decomposition.  The keys of one (b, g) -- a slab -- are cut into
+// 32-key blocks.  A workgroup holds every query row of its row group, so each
+// KV element is read from HBM once per row group and shared by all its rows;
+// it walks one or more segments (a run of consecutive blocks of one slab).
+// Two ways to hand out segments:
+//   balanced : the blocks of all slabs, concatenated slab after slab, are cut
+//              into P equal ranges, one per workgroup, with P about the number
+//              of workgroups the chip holds at once.  Ragged prefix lengths
+//              then cost nothing in balance, and no second wave of workgroups
+//              runs at partial occupancy.  Segment (workgroup p, slab q) has
+//              partial index p + q: both grow along the concatenation.
+//   fixed    : split s of slab q takes blocks [s*C, (s+1)*C) (large batches,
+//              where slabs far outnumber resident workgroups; VALU path).
+// A slab covered by one segment is written straight to out; otherwise each
+// segment writes its unnormalised partial (O, max, sum) and attn_combine
+// merges a slab's partials with an exact log-sum-exp rescale, from the
+// (first partial, count) table the segments leave in the workspace.
+//
+// The MFMA path runs one wavefront per workgroup: the wave streams its range
+// with nothing to wait for but its own loads (no workgroup barrier, no
+// cross-wave merge), prefetching one block ahead, across segment ends too.
 //
 // bf16 MFMA path (v_mfma_f32_16x16x32_bf16):
-//   S^T = K * Q^T : A = 16 keys x 32 dims of K straight from HBM (16-byte
-//                   loads), B = Q^T held in registers for the whole chunk.
+//   S^T = K * Q^T : A = 16 keys x 32 dims of K, B = Q^T held in registers.
 //   The two 16-key halves of a block use the key order
 //     row m of half h  <->  key 8*(m/4) + 4*h + m%4
 //   so that lane (n, q) ends up holding row n's scores for keys 8q..8q+7:
 //   exactly the A operand of the PV product, with no register shuffle.
 //   O += P * V    : B = V^T slice read from a per-wave transposed LDS copy
 //                   (16-byte reads, XOR-swizzled 16-byte columns).
+//   A block is loaded into registers one iteration ahead; at the top of its
+//   iteration it is moved to the wave's LDS stage (K as loaded, V
+//   transposed) and the same registers take the next block's loads, so only
+//   one block per wave occupies registers.
 // fp32 (and any dtype) VALU path: 32 rows x 32 keys tiles through LDS.
 #include <stdlib.h>
 
@@ -38,49 +55,190 @@ struct AttnArgs {
     const void* k;
     const void* v;
     void* out;
-    float* ws_o;    // [B][Hkv][S][R][D]  unnormalised partial O per split
-    float2* ws_ml;  // [B][Hkv][S][R]     (max in log2 units, sum)
+    float* ws_o;    // [parts][R][D]  unnormalised partial O
+    float2* ws_ml;  // [parts][R]     (max in log2 units, sum)
+    int2* seg;      // [B*Hkv]        (first partial, partial count) of each slab
     const int32_t* prefix_len;
     const int32_t* parent;
-    int B, N, Hq, Hkv, G, cap, R, nrg, chunk, nsplit_max;
-    int max_keys;      // host bound on L_b + N (sizes the split workspace)
+    int B, N, Hq, Hkv, G, cap, R, nrg;
+    int balanced;      // 1: balanced ranges; 0: fixed splits
+    int nparts;        // balanced: P; fixed: splits per slab
+    int split_blocks;  // fixed: 32-key blocks per split
+    int max_keys;      // host bound on L_b + N
     float scale_log2;  // softmax scale * log2(e)
 };
 
-// Ancestor-or-self bit masks of every node, built from the parent array.
-__device__ __forceinline__ void build_anc(const AttnArgs& a, int b, uint64_t* s_anc) {
-    const int tid = threadIdx.x;
-    if (tid < a.N) {
-        uint64_t m = 0;
-        int n = tid;
-        for (int s = 0; s < kMaxNodes && n >= 0; ++s) {
-            m |= 1ull << n;
-            n = tree_parent(a.parent, a.N, b, n);
-        }
-        s_anc[tid] = m;
-    }
+// Largest batch the balanced mode serves (its block-count scan lives in LDS).
+constexpr int kMaxBalancedBatch = 480;
+
+// Number of 32-key blocks of request b's slabs; 0 outside the contract
+// (L < 0 or L + N beyond the cache or the host bound): such requests are
+// skipped and their output is left unwritten.
+__device__ __forceinline__ int request_blocks(const AttnArgs& a, int L) {
+    const int Tk = L + a.N;
+    return (L < 0 || Tk > a.cap || Tk > a.max_keys) ? 0 : (Tk + 31) >> 5;
 }
 
-// Workgroup -> (request, kv head, split, row group).  The row groups of one
-// chunk get consecutive dispatch slots on one XCD (block i runs on XCD i % 8),
-// so they share the chunk through that XCD's L2.
-struct Work {
-    int b, g, s, rg;
-    bool live;
-};
-
-__device__ __forceinline__ Work decode_block(const AttnArgs& a) {
+// Workgroup -> (unit, row group).  The row groups of one unit get
+// consecutive dispatch slots on one XCD (block i runs on XCD i % 8), so they
+// share the unit's KV blocks through that XCD's L2.
+__device__ __forceinline__ void decode_unit(const AttnArgs& a, int& unit, int& rg) {
     const int i = blockIdx.x;
     const int xcd = i & 7, j = i >> 3;
-    const int unit = (j / a.nrg) * 8 + xcd;
-    Work w;
-    w.rg = j % a.nrg;
-    w.s = unit % a.nsplit_max;
-    const int bg = unit / a.nsplit_max;
-    w.live = bg < a.B * a.Hkv;
-    w.b = w.live ? bg / a.Hkv : 0;
-    w.g = w.live ? bg % a.Hkv : 0;
-    return w;
+    rg = j % a.nrg;
+    unit = (j / a.nrg) * 8 + xcd;
+}
+
+// s_cum[b] = blocks of requests 0..b-1 (per kv head), b = 0..B, and
+// s_len[b] = prefix length of request b, computed by one wavefront.
+// Balanced mode only (B <= kMaxBalancedBatch).
+__device__ __forceinline__ void scan_request_blocks(const AttnArgs& a, int* s_cum, int* s_len) {
+    const int lane = threadIdx.x & 63;
+    const int per = (a.B + 63) / 64;
+    const int lo = lane * per, hi = min(lo + per, a.B);
+    int sum = 0;
+    for (int i = lo; i < hi; ++i) {
+        const int L = a.prefix_len[i];
+        const int nb = request_blocks(a, L);
+        s_len[i] = L;
+        s_cum[i + 1] = nb;
+        sum += nb;
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    wave_lds_sync();
+    int run = incl - sum;
+    for (int i = lo; i < hi; ++i) {
+        run += s_cum[i + 1];
+        s_cum[i + 1] = run;
+    }
+    if (lane == 0) s_cum[0] = 0;
+    wave_lds_sync();
+}
+
+// One segment: blocks [blk0, blk1) of slab (b, g); L = prefix length of b.
+struct Seg {
+    int b, g, blk0, blk1, L;
+    int part;    // partial index (unused when direct)
+    int direct;  // the segment covers its whole slab: write out
+    int table;   // this workgroup records the slab's (first, count)
+    int first, count;
+};
+
+struct SegIter {
+    long x, hi, nb_total;  // balanced: next block, end of range, all blocks
+    int unit;
+    bool done;
+};
+
+// Workgroup of global block x in balanced mode: p with floor(p*NB/P) <= x.
+__device__ __forceinline__ int part_of(long x, long nb_total, int P) {
+    return static_cast<int>(((x + 1) * P - 1) / nb_total);
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Start the segment walk of this workgroup (one wavefront; balanced mode
+// scans the request block counts into s_cum).
+__device__ __forceinline__ SegIter begin_segments(const AttnArgs& a, int unit, int* s_cum, int* s_len) {
+    SegIter it;
+    it.unit = unit;
+    it.done = false;
+    it.x = it.hi = it.nb_total = 0;
+    if (a.balanced) {
+        scan_request_blocks(a, s_cum, s_len);
+        it.nb_total = static_cast<long>(a.Hkv) * s_cum[a.B];
+        if (unit < a.nparts) {
+            it.x = static_cast<long>(unit) * it.nb_total / a.nparts;
+            it.hi = static_cast<long>(unit + 1) * it.nb_total / a.nparts;
+        }
+    }
+    return it;
+}
+
+__device__ __forceinline__ bool next_segment(const AttnArgs& a, SegIter& it, const int* s_cum, const int* s_len,
+                                             Seg& sg) {
+    if (a.balanced) {
+        if (it.x >= it.hi) return false;
+        // request b: s_cum[b] <= x / Hkv < s_cum[b + 1]
+        const int y = static_cast<int>(it.x / a.Hkv);
+        int lo = 0, hi = a.B;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_cum[mid] <= y) lo = mid; else hi = mid - 1;
+        }
+        const int b = uniform(lo);
+        const int nb = s_cum[b + 1] - s_cum[b];
+        const long local = it.x - static_cast<long>(a.Hkv) * s_cum[b];
+        const int g = static_cast<int>(local / nb), off = static_cast<int>(local % nb);
+        const long begin = it.x - off, end = begin + nb;
+        const long x1 = end < it.hi ? end : it.hi;
+        const int q = b * a.Hkv + g;
+        const int pf = part_of(begin, it.nb_total, a.nparts), pl = part_of(end - 1, it.nb_total, a.nparts);
+        sg.b = b;
+        sg.L = uniform(s_len[b]);
+        sg.g = uniform(g);
+        sg.blk0 = uniform(off);
+        sg.blk1 = uniform(off + static_cast<int>(x1 - it.x));
+        sg.part = it.unit + q;
+        sg.direct = pf == pl;
+        sg.table = off == 0;
+        sg.first = pf + q;
+        sg.count = pl - pf + 1;
+        it.x = x1;
+        return true;
+    }
+    if (it.done) return false;
+    it.done = true;
+    const int q = it.unit / a.nparts, s = it.unit % a.nparts;
+    if (q >= a.B * a.Hkv) return false;
+    const int b = q / a.Hkv;
+    const int L = a.prefix_len[b];
+    const int nb = request_blocks(a, L);
+    const int x0 = s * a.split_blocks;
+    if (x0 >= nb) return false;
+    sg.b = b;
+    sg.L = L;
+    sg.g = q % a.Hkv;
+    sg.blk0 = x0;
+    sg.blk1 = min(nb, x0 + a.split_blocks);
+    sg.part = q * a.nparts + s;
+    sg.count = (nb + a.split_blocks - 1) / a.split_blocks;
+    sg.direct = sg.count == 1;
+    sg.table = s == 0;
+    sg.first = q * a.nparts;
+    return true;
+}
+
+// Ancestor-or-self bit mask of node `lane` of request b (lanes >= N give
+// node 0's), by pointer doubling over the parent array in one wavefront:
+// after round k a lane holds its first 2^k path nodes and its 2^k-th
+// ancestor.
+__device__ __forceinline__ uint64_t anc_mask(const AttnArgs& a, int b) {
+    const int lane = threadIdx.x & 63;
+    const int i = lane < a.N ? lane : 0;
+    int up = tree_parent(a.parent, a.N, b, i);
+    uint64_t m = 1ull << i;
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+        const int src = up >= 0 ? up : 0;
+        const uint32_t lo = __shfl(static_cast<uint32_t>(m), src), hi = __shfl(static_cast<uint32_t>(m >> 32), src);
+        const int upup = __shfl(up, src);
+        if (up >= 0) {
+            m |= static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
+            up = upup;
+        }
+    }
+    return m;
+}
+
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+    const uint32_t lo = __shfl(static_cast<uint32_t>(v), src), hi = __shfl(static_cast<uint32_t>(v >> 32), src);
+    return static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
 }
 
 __device__ __forceinline__ void store_out(void* out, bool bf16, size_t idx, float val) {
@@ -94,10 +252,10 @@ __device__ __forceinline__ void store_out(void* out, bool bf16, size_t idx, floa
 __device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 3)) & 3; }
 
 // ----------------------------------------------------------------------------
-// MFMA path (bf16).  D in {64, 128}; RT 16-row tiles per wave; WK waves.
+// MFMA path (bf16).  D in {64, 128}; RT 16-row tiles; one wavefront.
 // ----------------------------------------------------------------------------
 // K fragments (A operand, paired-half key order) and V rows of one 32-key
-// block, held in registers between the load and its use.
+// block, held in registers between the load and the LDS stage.
 template <int D>
 struct KVBlock {
     static constexpr int NC32 = D / 32;
@@ -107,7 +265,7 @@ struct KVBlock {
 };
 
 // Issue the loads of the block starting at key kb; rows are clamped to
-// row_max so every address is inside the cache.
+// row_max (the slab's last key) so no row past the tree is read.
 template <int D>
 __device__ __forceinline__ void load_kv_block(KVBlock<D>& blk, const uint16_t* kbase, const uint16_t* vbase, int kb,
                                               int row_max, int n16, int q4, int vch, int vkg) {
@@ -125,253 +283,241 @@ __device__ __forceinline__ void load_kv_block(KVBlock<D>& blk, const uint16_t* k
     }
 }
 
-template <int D, int RT, int WK>
-__global__ __launch_bounds__(64 * WK) void attn_mfma(AttnArgs a) {
+template <int D, int RT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(RT <= 2 ? 2 : 1))) void attn_mfma(AttnArgs a) {
     constexpr int NC32 = D / 32;  // k-steps of the QK product
     constexpr int NC16 = D / 16;  // n-tiles of the PV product
     constexpr int CPR = D / 8;    // 16-byte chunks per cache row
     constexpr int KPL = KVBlock<D>::KPL;  // keys per lane in the V load (8 or 4)
-    constexpr int VT_BYTES = D * 64;
-    constexpr int MERGE_BYTES = WK * 16 * RT * D * 4;
-    constexpr int LDS_BYTES = (WK * VT_BYTES > MERGE_BYTES) ? WK * VT_BYTES : MERGE_BYTES;
-    __shared__ __attribute__((aligned(16))) unsigned char s_buf[LDS_BYTES];
-    __shared__ uint64_t s_anc[kMaxNodes];
-    __shared__ float s_m[WK][16 * RT];
-    __shared__ float s_l[WK][16 * RT];
-    __shared__ float2 s_row[16 * RT];
+    constexpr int KS_BYTES = 2 * NC32 * 64 * 16;  // K fragments of one block, lane-major
+    constexpr int VT_BYTES = D * 64;              // V^T of one block
+    __shared__ __attribute__((aligned(16))) unsigned char s_stage[KS_BYTES + VT_BYTES];
+    __shared__ int s_cum[kMaxBalancedBatch + 1];
+    __shared__ int s_len[kMaxBalancedBatch];
 
-    const Work w = decode_block(a);
-    if (!w.live) return;
-    const int b = w.b, g = w.g;
-    const int k0 = w.s * a.chunk;
-    if (k0 >= a.max_keys) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int unit, rg;
+    decode_unit(a, unit, rg);
+    const int lane = threadIdx.x;
     const int n16 = lane & 15, q4 = lane >> 4;
     const int vch = lane % CPR, vkg = lane / CPR;
-    const size_t head = (static_cast<size_t>(b) * a.Hkv + g) * a.cap;
-    const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + head * D;
-    const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + head * D;
-
-    // Everything that does not depend on the prefix length goes out first:
-    // the prefix length itself, the first KV block (rows clamped to the cache,
-    // out-of-range values masked once L is known), the tree and the queries.
-    const int L = a.prefix_len[b];
-    // Split s of a (request, kv head) takes the interleaved 32-key blocks
-    // s*WK + wave + t*S*WK, S = the request's split count: the splits of one
-    // slab sweep it together, front to back, like one streaming read.
-    const int first_blk = w.s * WK + wave;
-    int kb = first_blk * 32;
-    KVBlock<D> cur;
-    load_kv_block<D>(cur, kbase, vbase, kb, a.cap - 1, n16, q4, vch, vkg);
-    build_anc(a, b, s_anc);
-    bf16x8 qf[RT][NC32];
-    int rnode[RT];
+    unsigned char* ks = s_stage;
+    unsigned char* vt = s_stage + KS_BYTES;
     const uint16_t* qb = static_cast<const uint16_t*>(a.q);
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
-        const int r = (w.rg * RT + t) * 16 + n16;
-        const bool valid = r < a.R;
-        rnode[t] = valid ? r / a.G : -1;
-        const int hq = g * a.G + (valid ? r % a.G : 0);
-        const uint16_t* qrow = qb + ((static_cast<size_t>(b) * a.N + (valid ? rnode[t] : 0)) * a.Hq + hq) * D;
-#pragma unroll
-        for (int c = 0; c < NC32; ++c) {
-            u32x4 u = {0u, 0u, 0u, 0u};
-            if (valid) u = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * q4);
-            qf[t][c] = __builtin_bit_cast(bf16x8, u);
-        }
+    const uint16_t* kc = static_cast<const uint16_t*>(a.k);
+    const uint16_t* vc = static_cast<const uint16_t*>(a.v);
+
+    SegIter it = begin_segments(a, unit, s_cum, s_len);
+    Seg cur;
+    if (!next_segment(a, it, s_cum, s_len, cur)) return;
+    int L = cur.L;
+    KVBlock<D> R;
+    {
+        const size_t head = (static_cast<size_t>(cur.b) * a.Hkv + cur.g) * a.cap * D;
+        load_kv_block<D>(R, kc + head, vc + head, cur.blk0 * 32, L + a.N - 1, n16, q4, vch, vkg);
     }
-    __syncthreads();
+    for (;;) {
+        const int b = cur.b, g = cur.g;
+        const int Tk = L + a.N;
+        const size_t head = (static_cast<size_t>(b) * a.Hkv + g) * a.cap * D;
+        const uint16_t* kbase = kc + head;
+        const uint16_t* vbase = vc + head;
+        // The next segment, whose first block is loaded during this one's last.
+        Seg nxt;
+        const bool more = next_segment(a, it, s_cum, s_len, nxt);
+        const int Ln = more ? nxt.L : 0;
+        const size_t nhead = more ? (static_cast<size_t>(nxt.b) * a.Hkv + nxt.g) * a.cap * D : head;
 
-    const int Tk = L + a.N;
-    if (L < 0 || Tk > a.cap || Tk > a.max_keys) return;  // outside the contract: leave out unwritten
-    if (k0 >= Tk) return;
-    const int nsplit = (Tk + a.chunk - 1) / a.chunk;
-    const int k1 = Tk;                  // keys past the request's end are masked
-    const int kstep = 32 * WK * nsplit;  // interleave stride of this request
-    uint64_t anc[RT];
-#pragma unroll
-    for (int t = 0; t < RT; ++t) anc[t] = rnode[t] >= 0 ? s_anc[rnode[t]] : ~0ull;
-
-    float m_run[RT], l_run[RT];
-    f32x4 o[RT][NC16];
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
-        m_run[t] = -INFINITY;
-        l_run[t] = 0.f;
-#pragma unroll
-        for (int c = 0; c < NC16; ++c) o[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    unsigned char* vt = s_buf + wave * VT_BYTES;
-
-    for (; kb < k1; kb += kstep) {
-        // Prefetch the wave's next block while this one is processed.  The
-        // loads are unconditional (past the end they re-read this block:
-        // cache hits) so the wait before using this block counts only the
-        // older loads and never drains the prefetch.
-        KVBlock<D> nxt;
-        const int kn = kb + kstep;
-        load_kv_block<D>(nxt, kbase, vbase, kn < k1 ? kn : kb, Tk - 1, n16, q4, vch, vkg);
-
-        // Transpose V into LDS (row d holds the block's 32 keys); keys at or
-        // past the split end are zeroed so no stale value reaches P*V.
-#pragma unroll
-        for (int jj = 0; jj < KPL; ++jj)
-            if (kb + vkg * KPL + jj >= k1) cur.vr[jj] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int d = 8 * vch + t;
-            const int key0 = vkg * KPL;
-            const int pch = (key0 >> 3) ^ vt_swz(d);
-            unsigned char* dst = vt + d * 64 + pch * 16 + (key0 & 7) * 2;
-            // element t of two keys' rows -> one dword (byte select: low or high half)
-            const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
-            if constexpr (KPL == 8) {
-                u32x4 wv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    wv[e] = __builtin_amdgcn_perm(cur.vr[2 * e + 1][t >> 1], cur.vr[2 * e][t >> 1], sel);
-                *reinterpret_cast<u32x4*>(dst) = wv;
-            } else {
-                uint2 wv;
-                wv.x = __builtin_amdgcn_perm(cur.vr[1][t >> 1], cur.vr[0][t >> 1], sel);
-                wv.y = __builtin_amdgcn_perm(cur.vr[3][t >> 1], cur.vr[2][t >> 1], sel);
-                *reinterpret_cast<uint2*>(dst) = wv;
-            }
-        }
-        wave_lds_sync();
-
-        // Blocks wholly inside the prefix and the split need no key mask.
-        const bool interior = kb + 32 <= L && kb + 32 <= k1;
+        // Queries and ancestor masks of this workgroup's rows.
+        const uint64_t node_anc = anc_mask(a, b);
+        bf16x8 qf[RT][NC32];
+        uint64_t anc[RT];
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
-            f32x4 st[2];
+            const int r = (rg * RT + t) * 16 + n16;
+            const bool valid = r < a.R;
+            const int node = valid ? r / a.G : 0;
+            const uint64_t m = shfl_u64(node_anc, node);
+            anc[t] = valid ? m : ~0ull;
+            const int hq = g * a.G + (valid ? r % a.G : 0);
+            const uint16_t* qrow = qb + ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int c = 0; c < NC32; ++c) {
+                u32x4 u = {0u, 0u, 0u, 0u};
+                if (valid) u = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * q4);
+                qf[t][c] = __builtin_bit_cast(bf16x8, u);
+            }
+        }
+
+        float m_run[RT], l_run[RT];
+        f32x4 o[RT][NC16];
 #pragma unroll
-                for (int c = 0; c < NC32; ++c)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.kf[h][c]), qf[t][c],
-                                                                  acc, 0, 0, 0);
-                st[h] = acc;
-            }
-            // This lane's keys are kb + 8*q4 + e, e = 0..7 (e = 4h + ii).
-            // Bit e of the mask: key below the split end and either a prefix
-            // key or a tree key on the row's root path.
-            uint32_t kmask = 0xFFu;
-            if (!interior) {
-                const int base = kb + 8 * q4;
-                const int nend = min(max(k1 - base, 0), 8);
-                const int npre = min(max(L - base, 0), 8);
-                const int sh = base - L;  // tree offset of key e is sh + e
-                const uint32_t tree = sh >= 0 ? static_cast<uint32_t>(anc[t] >> min(sh, 63))
-                                              : static_cast<uint32_t>(anc[t] << min(-sh, 63));
-                const uint32_t pre = (1u << npre) - 1u;
-                kmask = ((tree & 0xFFu) | pre) & ((1u << nend) - 1u);
-            }
-            float s[8];
-            float bm = -INFINITY;
+        for (int t = 0; t < RT; ++t) {
+            m_run[t] = -INFINITY;
+            l_run[t] = 0.f;
+#pragma unroll
+            for (int c = 0; c < NC16; ++c) o[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+
+        for (int xb = cur.blk0; xb < cur.blk1; ++xb) {
+            const int kb = xb * 32;
+            // Stage the block: K fragments as loaded (each lane reads back its
+            // own), V transposed (row d holds the block's 32 keys); keys at
+            // or past the slab end are zeroed so no stale value reaches P*V.
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const int e = 4 * h + ii;
-                    const float x = ((kmask >> e) & 1u) ? st[h][ii] * a.scale_log2 : -INFINITY;
-                    s[e] = x;
-                    bm = fmaxf(bm, x);
+                for (int c = 0; c < NC32; ++c)
+                    *reinterpret_cast<u32x4*>(ks + ((h * NC32 + c) * 64 + lane) * 16) = R.kf[h][c];
+#pragma unroll
+            for (int jj = 0; jj < KPL; ++jj)
+                if (kb + vkg * KPL + jj >= Tk) R.vr[jj] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int d = 8 * vch + t;
+                const int key0 = vkg * KPL;
+                const int pch = (key0 >> 3) ^ vt_swz(d);
+                unsigned char* dst = vt + d * 64 + pch * 16 + (key0 & 7) * 2;
+                // element t of two keys' rows -> one dword (byte select: low or high half)
+                const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+                if constexpr (KPL == 8) {
+                    u32x4 wv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        wv[e] = __builtin_amdgcn_perm(R.vr[2 * e + 1][t >> 1], R.vr[2 * e][t >> 1], sel);
+                    *reinterpret_cast<u32x4*>(dst) = wv;
+                } else {
+                    uint2 wv;
+                    wv.x = __builtin_amdgcn_perm(R.vr[1][t >> 1], R.vr[0][t >> 1], sel);
+                    wv.y = __builtin_amdgcn_perm(R.vr[3][t >> 1], R.vr[2][t >> 1], sel);
+                    *reinterpret_cast<uint2*>(dst) = wv;
                 }
-            bm = max_across_rows(bm);
-            // Lazy rescale: keep the running max unless a row's block max
-            // exceeds it by more than 8 (probabilities stay <= 2^8, exact in
-            // fp32 and as precise in bf16); the decision is wave-uniform.
-            if (__builtin_amdgcn_ballot_w64(bm > m_run[t] + 8.f) != 0ull) {
-                const float mn = fmaxf(m_run[t], bm);
-                const float alpha = m_run[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[t] - mn);
-                l_run[t] *= alpha;
-#pragma unroll
-                for (int c = 0; c < NC16; ++c) o[t][c] *= alpha;  // o holds row n16 of this lane
-                m_run[t] = mn;
             }
-            const float mu = m_run[t] == -INFINITY ? 0.f : m_run[t];
-            float rs = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                s[e] = __builtin_amdgcn_exp2f(s[e] - mu);
-                rs += s[e];
+            // The registers are free: load the next block -- this segment's,
+            // else the next segment's first, else this one again (a cache
+            // hit).  The load is unconditional so the wait at the top of an
+            // iteration never drains a prefetch early.
+            asm volatile("" ::: "memory");
+            {
+                const bool here = xb + 1 < cur.blk1;
+                const uint16_t* nk = here || !more ? kbase : kc + nhead;
+                const uint16_t* nv = here || !more ? vbase : vc + nhead;
+                const int nkb = here ? kb + 32 : (more ? nxt.blk0 * 32 : kb);
+                const int nmax = here || !more ? Tk - 1 : Ln + a.N - 1;
+                load_kv_block<D>(R, nk, nv, nkb, nmax, n16, q4, vch, vkg);
             }
-            l_run[t] += sum_across_rows(rs);
-            u32x4 pp;
-            pp[0] = pack_bf16x2(s[0], s[1]);
-            pp[1] = pack_bf16x2(s[2], s[3]);
-            pp[2] = pack_bf16x2(s[4], s[5]);
-            pp[3] = pack_bf16x2(s[6], s[7]);
-            const bf16x8 pa = __builtin_bit_cast(bf16x8, pp);
-#pragma unroll
-            for (int c = 0; c < NC16; ++c) {
-                // O^T = V^T P^T: A = V^T (lane: keys 8q..8q+7 of dim 16c + n,
-                // straight from LDS), B = P^T; the result lands as
-                // O[row n][dims 16c + 4q .. 16c + 4q + 3] in this lane.
-                const int d = 16 * c + n16;
-                const u32x4 vf = *reinterpret_cast<const u32x4*>(vt + d * 64 + ((q4 ^ vt_swz(d)) * 16));
-                o[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf), pa, o[t][c], 0, 0, 0);
-            }
-        }
-        wave_lds_sync();
-        cur = nxt;
-    }
+            wave_lds_sync();
 
-    // ---- merge the waves of this workgroup --------------------------------
-    __syncthreads();
-    if (q4 == 0) {
+            // Blocks wholly inside the prefix need no key mask.
+            const bool interior = kb + 32 <= L;
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                f32x4 st[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int c = 0; c < NC32; ++c) {
+                        const u32x4 kf = *reinterpret_cast<const u32x4*>(ks + ((h * NC32 + c) * 64 + lane) * 16);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf), qf[t][c], acc,
+                                                                      0, 0, 0);
+                    }
+                    st[h] = acc;
+                }
+                // This lane's keys are kb + 8*q4 + e, e = 0..7 (e = 4h + ii).
+                // Bit e of the mask: key below the slab end and either a
+                // prefix key or a tree key on the row's root path.
+                uint32_t kmask = 0xFFu;
+                if (!interior) {
+                    const int base = kb + 8 * q4;
+                    const int nend = min(max(Tk - base, 0), 8);
+                    const int npre = min(max(L - base, 0), 8);
+                    const int sh = base - L;  // tree offset of key e is sh + e
+                    const uint32_t tree = sh >= 0 ? static_cast<uint32_t>(anc[t] >> min(sh, 63))
+                                                  : static_cast<uint32_t>(anc[t] << min(-sh, 63));
+                    const uint32_t pre = (1u << npre) - 1u;
+                    kmask = ((tree & 0xFFu) | pre) & ((1u << nend) - 1u);
+                }
+                float s[8];
+                float bm = -INFINITY;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) {
+                        const int e = 4 * h + ii;
+                        const float x = ((kmask >> e) & 1u) ? st[h][ii] * a.scale_log2 : -INFINITY;
+                        s[e] = x;
+                        bm = fmaxf(bm, x);
+                    }
+                bm = max_across_rows(bm);
+                // Lazy rescale: keep the running max unless a row's block max
+                // exceeds it by more than 8 (probabilities stay <= 2^8, exact
+                // in fp32 and as precise in bf16); the decision is
+                // wave-uniform.
+                if (__builtin_amdgcn_ballot_w64(bm > m_run[t] + 8.f) != 0ull) {
+                    const float mn = fmaxf(m_run[t], bm);
+                    const float alpha = m_run[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[t] - mn);
+                    l_run[t] *= alpha;
+#pragma unroll
+                    for (int c = 0; c < NC16; ++c) o[t][c] *= alpha;  // o holds row n16 of this lane
+                    m_run[t] = mn;
+                }
+                const float mu = m_run[t] == -INFINITY ? 0.f : m_run[t];
+                float rs = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    s[e] = __builtin_amdgcn_exp2f(s[e] - mu);
+                    rs += s[e];
+                }
+                l_run[t] += sum_across_rows(rs);
+                u32x4 pp;
+                pp[0] = pack_bf16x2(s[0], s[1]);
+                pp[1] = pack_bf16x2(s[2], s[3]);
+                pp[2] = pack_bf16x2(s[4], s[5]);
+                pp[3] = pack_bf16x2(s[6], s[7]);
+                const bf16x8 pa = __builtin_bit_cast(bf16x8, pp);
+#pragma unroll
+                for (int c = 0; c < NC16; ++c) {
+                    // O^T = V^T P^T: A = V^T (lane: keys 8q..8q+7 of dim
+                    // 16c + n, straight from LDS), B = P^T; the result lands
+                    // as O[row n][dims 16c + 4q .. 16c + 4q + 3] in this lane.
+                    const int d = 16 * c + n16;
+                    const u32x4 vf = *reinterpret_cast<const u32x4*>(vt + d * 64 + ((q4 ^ vt_swz(d)) * 16));
+                    o[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf), pa, o[t][c], 0,
+                                                                      0, 0);
+                }
+            }
+            wave_lds_sync();
+        }
+
+        // ---- this segment's result, straight from registers ---------------
+        // Lane (n, q) holds row n of each tile: dims 16c + 4q .. +3 of O and
+        // the row's running (max, sum).
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
-            s_m[wave][t * 16 + n16] = m_run[t];
-            s_l[wave][t * 16 + n16] = l_run[t];
+            const int r = (rg * RT + t) * 16 + n16;
+            if (r >= a.R) continue;
+            if (cur.direct) {
+                const int node = r / a.G, hq = g * a.G + r % a.G;
+                const float inv = l_run[t] > 0.f ? 1.f / l_run[t] : 0.f;
+                uint16_t* orow = static_cast<uint16_t*>(a.out) + ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D;
+#pragma unroll
+                for (int c = 0; c < NC16; ++c) {
+                    uint2 pk;
+                    pk.x = pack_bf16x2(o[t][c][0] * inv, o[t][c][1] * inv);
+                    pk.y = pack_bf16x2(o[t][c][2] * inv, o[t][c][3] * inv);
+                    *reinterpret_cast<uint2*>(orow + 16 * c + 4 * q4) = pk;
+                }
+            } else {
+                float* prow = a.ws_o + (static_cast<size_t>(cur.part) * a.R + r) * D;
+#pragma unroll
+                for (int c = 0; c < NC16; ++c) *reinterpret_cast<f32x4*>(prow + 16 * c + 4 * q4) = o[t][c];
+                if (q4 == 0) a.ws_ml[static_cast<size_t>(cur.part) * a.R + r] = make_float2(m_run[t], l_run[t]);
+            }
         }
-    }
-    __syncthreads();
-    if (tid < 16 * RT) {  // per-row (max, sum) of the workgroup
-        float M = -INFINITY;
-#pragma unroll
-        for (int x = 0; x < WK; ++x) M = fmaxf(M, s_m[x][tid]);
-        const float Mu = M == -INFINITY ? 0.f : M;
-        float lsum = 0.f;
-#pragma unroll
-        for (int x = 0; x < WK; ++x) lsum += s_l[x][tid] * exp2f(s_m[x][tid] - Mu);
-        s_row[tid] = make_float2(M, lsum);
-    }
-    float* reg = reinterpret_cast<float*>(s_buf);
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
-        const int row = t * 16 + n16;
-        float M = -INFINITY;
-#pragma unroll
-        for (int x = 0; x < WK; ++x) M = fmaxf(M, s_m[x][row]);
-        const float sc = exp2f(m_run[t] - (M == -INFINITY ? 0.f : M));
-#pragma unroll
-        for (int c = 0; c < NC16; ++c)
-            *reinterpret_cast<f32x4*>(reg + (wave * 16 * RT + row) * D + 16 * c + 4 * q4) = o[t][c] * sc;
-    }
-    __syncthreads();
-
-    const int rbase = w.rg * RT * 16;
-    const int rows = min(16 * RT, a.R - rbase);
-    const size_t pbase = (static_cast<size_t>(b) * a.Hkv + g) * a.nsplit_max;
-    for (int e = tid; e < rows * D; e += 64 * WK) {
-        const int row = e / D, d = e % D;
-        float osum = 0.f;
-#pragma unroll
-        for (int x = 0; x < WK; ++x) osum += reg[(x * 16 * RT + row) * D + d];
-        const int r = rbase + row;
-        if (nsplit == 1) {
-            const int node = r / a.G, hq = g * a.G + r % a.G;
-            const float lsum = s_row[row].y;
-            const size_t oi = ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D + d;
-            store_out(a.out, true, oi, lsum > 0.f ? osum / lsum : 0.f);
-        } else {
-            a.ws_o[((pbase + w.s) * a.R + r) * D + d] = osum;
-            if (d == 0) a.ws_ml[(pbase + w.s) * a.R + r] = s_row[row];
-        }
+        if (cur.table && rg == 0 && lane == 0 && a.seg) a.seg[b * a.Hkv + g] = make_int2(cur.first, cur.count);
+        if (!more) break;
+        cur = nxt;
+        L = Ln;
     }
 }
 
@@ -398,23 +544,29 @@ __global__ __launch_bounds__(256) void attn_valu(AttnArgs a) {
     __shared__ float s_p[32][33];
     __shared__ uint64_t s_anc[kMaxNodes];
 
-    const Work w = decode_block(a);
-    if (!w.live) return;
-    const int b = w.b, g = w.g;
-    const int L = a.prefix_len[b];
+    int unit, rg;
+    decode_unit(a, unit, rg);
+    SegIter it;  // fixed splits only
+    it.unit = unit;
+    it.done = false;
+    it.x = it.hi = it.nb_total = 0;
+    Seg sg;
+    if (!next_segment(a, it, nullptr, nullptr, sg)) return;
+    const int b = sg.b, g = sg.g;
+    const int L = sg.L;
     const int Tk = L + a.N;
-    if (L < 0 || Tk > a.cap || Tk > a.max_keys) return;  // outside the contract: leave out unwritten
-    const int k0 = w.s * a.chunk;
-    if (k0 >= Tk) return;
-    const int k1 = min(k0 + a.chunk, Tk);
-    const int nsplit = (Tk + a.chunk - 1) / a.chunk;
+    const int k0 = sg.blk0 * 32;
+    const int k1 = min(sg.blk1 * 32, Tk);
 
-    build_anc(a, b, s_anc);
     const int tid = threadIdx.x;
+    if (tid < 64) {
+        const uint64_t m = anc_mask(a, b);
+        if (tid < a.N) s_anc[tid] = m;
+    }
     const T* qp = static_cast<const T*>(a.q);
     for (int e = tid; e < 32 * D; e += 256) {
         const int lr = e / D, d = e % D;
-        const int r = w.rg * 32 + lr;
+        const int r = rg * 32 + lr;
         float x = 0.f;
         if (r < a.R) {
             const int node = r / a.G, hq = g * a.G + r % a.G;
@@ -425,7 +577,7 @@ __global__ __launch_bounds__(256) void attn_valu(AttnArgs a) {
     __syncthreads();
 
     const int sr = tid >> 3, sk = tid & 7;
-    const int r = w.rg * 32 + sr;
+    const int r = rg * 32 + sr;
     const bool rvalid = r < a.R;
     const uint64_t anc = rvalid ? s_anc[r / a.G] : ~0ull;
     float m_run = -INFINITY, l_run = 0.f;
@@ -487,15 +639,16 @@ __global__ __launch_bounds__(256) void attn_valu(AttnArgs a) {
             for (int j = 0; j < D / 8; ++j) o[j] = fmaf(p, s_v[kk][sk + 8 * j], o[j]);
         }
     }
+    if (sg.table && rg == 0 && tid == 0 && a.seg) a.seg[b * a.Hkv + g] = make_int2(sg.first, sg.count);
     if (!rvalid) return;
     const int node = r / a.G, hq = g * a.G + r % a.G;
     const bool bf16_out = sizeof(T) == 2;
-    if (nsplit == 1) {
+    if (sg.direct) {
         const size_t ob = ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D;
 #pragma unroll
         for (int j = 0; j < D / 8; ++j) store_out(a.out, bf16_out, ob + sk + 8 * j, l_run > 0.f ? o[j] / l_run : 0.f);
     } else {
-        const size_t pi = (static_cast<size_t>(b) * a.Hkv + g) * a.nsplit_max + w.s;
+        const size_t pi = static_cast<size_t>(sg.part);
 #pragma unroll
         for (int j = 0; j < D / 8; ++j) a.ws_o[(pi * a.R + r) * D + sk + 8 * j] = o[j];
         if (sk == 0) a.ws_ml[pi * a.R + r] = make_float2(m_run, l_run);
@@ -503,43 +656,41 @@ __global__ __launch_bounds__(256) void attn_valu(AttnArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// Split combine: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// One wavefront per (request, kv head, query row).
+// Split combine: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the
+// partials of one slab.  One wavefront per (request, kv head, query row).
 // ----------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int bf16_out) {
     constexpr int DPL = D / 64;  // output elements per lane
-    constexpr int SB = 16;       // splits whose loads are in flight together
+    constexpr int SB = 16;       // partials whose loads are in flight together
     const int lane = threadIdx.x & 63;
     const long id = static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (id >= static_cast<long>(a.B) * a.Hkv * a.R) return;
     const int r = static_cast<int>(id % a.R);
     const int bg = static_cast<int>(id / a.R);
     const int b = bg / a.Hkv, g = bg % a.Hkv;
-    const int L = a.prefix_len[b];
-    const int Tk = L + a.N;
-    if (L < 0 || Tk > a.cap || Tk > a.max_keys) return;  // outside the contract: leave out unwritten
-    const int nsplit = (Tk + a.chunk - 1) / a.chunk;
-    if (nsplit <= 1) return;
-    const size_t base = static_cast<size_t>(bg) * a.nsplit_max;
-    // Running (max, sum, O) over batches of SB splits, each batch one round of loads.
+    if (request_blocks(a, a.prefix_len[b]) == 0) return;  // outside the contract: out left unwritten
+    const int2 sp = a.seg[bg];
+    const int first = sp.x, count = sp.y;
+    if (count <= 1) return;  // written by its only segment
+    // Running (max, sum, O) over batches of SB partials, each batch one round of loads.
     float M = -INFINITY, lsum = 0.f;
     float acc[DPL];
 #pragma unroll
     for (int j = 0; j < DPL; ++j) acc[j] = 0.f;
-    for (int s0 = 0; s0 < nsplit; s0 += SB) {
+    for (int s0 = 0; s0 < count; s0 += SB) {
         float2 ml[SB];
         float ov[SB][DPL];
 #pragma unroll
         for (int k = 0; k < SB; ++k) {
-            const int s = s0 + k;
+            const size_t pi = static_cast<size_t>(first + s0 + k);
             ml[k] = make_float2(-INFINITY, 0.f);
 #pragma unroll
             for (int j = 0; j < DPL; ++j) ov[k][j] = 0.f;
-            if (s < nsplit) {
-                ml[k] = a.ws_ml[(base + s) * a.R + r];
+            if (s0 + k < count) {
+                ml[k] = a.ws_ml[pi * a.R + r];
 #pragma unroll
-                for (int j = 0; j < DPL; ++j) ov[k][j] = a.ws_o[((base + s) * a.R + r) * D + lane + 64 * j];
+                for (int j = 0; j < DPL; ++j) ov[k][j] = a.ws_o[(pi * a.R + r) * D + lane + 64 * j];
             }
         }
         float Mn = M;
@@ -569,21 +720,20 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int bf16_out) {
 // ----------------------------------------------------------------------------
 // Host side
 // ----------------------------------------------------------------------------
-static int env_chunk_override() {
-    static int v = -1;
-    if (v < 0) {
-        const char* s = getenv("SPEC_VERIFY_KV_CHUNK");
-        v = s ? atoi(s) : 0;
-        if (v < 0) v = 0;
-    }
-    return v;
+static int env_int(const char* name) {
+    const char* s = getenv(name);
+    const int v = s ? atoi(s) : 0;
+    return v > 0 ? v : 0;
 }
+
+// Upper bound on resident workgroups of one launch (4 per CU on 256 CUs);
+// sizes the balanced-mode partials independently of the device.
+constexpr int kMaxResident = 2048;
 
 AttnPlan plan_attn(const spec_attn_desc& d, int max_prefix_len) {
     AttnPlan p{};
     const int G = d.num_q_heads / d.num_kv_heads;
     p.rows = d.num_nodes * G;
-    int unit_keys;
     if (d.dtype == SPEC_BF16) {
         p.mfma = true;
         if (p.rows <= 64) {
@@ -593,42 +743,97 @@ AttnPlan plan_attn(const spec_attn_desc& d, int max_prefix_len) {
             p.row_tiles = 4;
             p.row_groups = (p.rows + 63) / 64;
         }
-        p.waves = p.row_tiles <= 2 ? 4 : 2;
-        unit_keys = 32 * p.waves;
+        p.waves = 1;
     } else {
         p.mfma = false;
         p.row_tiles = 0;
         p.row_groups = (p.rows + 31) / 32;
         p.waves = 4;
-        unit_keys = 32;
     }
+    const long slabs = static_cast<long>(d.batch) * d.num_kv_heads;
     const long keys_max = static_cast<long>(max_prefix_len) + d.num_nodes;
-    const long units = static_cast<long>(d.batch) * d.num_kv_heads * p.row_groups;
-    const long want = units >= 1024 ? 1 : (1024 + units - 1) / units;
-    long chunk = (keys_max + want - 1) / want;
-    const long min_chunk = env_chunk_override() > 0 ? env_chunk_override() : 256;
-    if (chunk < min_chunk) chunk = min_chunk;
-    chunk = (chunk + unit_keys - 1) / unit_keys * unit_keys;
-    p.chunk = static_cast<int>(chunk);
-    p.nsplit_max = static_cast<int>((keys_max + chunk - 1) / chunk);
+    const long blocks_max = (keys_max + 31) / 32;
     p.max_keys = static_cast<int>(keys_max);
-    if (p.nsplit_max < 1) p.nsplit_max = 1;
-    if (p.nsplit_max > 1) {
-        const size_t parts = static_cast<size_t>(d.batch) * d.num_kv_heads * p.nsplit_max * p.rows;
-        p.ws_bytes = align_up(parts * d.head_dim * sizeof(float), 256) + align_up(parts * sizeof(float2), 256);
+    long parts;
+    p.balanced = p.mfma && d.batch <= kMaxBalancedBatch;
+    if (p.balanced) {
+        // P is picked per launch from the device (resident workgroups); the
+        // workspace holds the most partials any device can ask for.
+        const long min_blocks = env_int("SPEC_VERIFY_MIN_BLOCKS") ? env_int("SPEC_VERIFY_MIN_BLOCKS") : 2;
+        long pcap = kMaxResident / p.row_groups;
+        if (pcap < 8) pcap = 8;
+        const long by_work = (slabs * blocks_max + min_blocks - 1) / min_blocks;
+        p.parts_max = static_cast<int>(by_work < pcap ? by_work : pcap);
+        if (p.parts_max < 1) p.parts_max = 1;
+        p.split_blocks = static_cast<int>(min_blocks);
+        parts = p.parts_max > 1 ? p.parts_max + slabs : 0;
+        p.nsplit_max = 0;
+    } else {
+        // Fixed splits: about 4096 units of work, at least 8 blocks each.
+        const long units = slabs * p.row_groups;
+        const long want = units >= 4096 ? 1 : (4096 + units - 1) / units;
+        long chunk_blocks = (blocks_max + want - 1) / want;
+        const long min_blocks = env_int("SPEC_VERIFY_KV_CHUNK") ? (env_int("SPEC_VERIFY_KV_CHUNK") + 31) / 32 : 8;
+        if (chunk_blocks < min_blocks) chunk_blocks = min_blocks;
+        p.split_blocks = static_cast<int>(chunk_blocks);
+        p.nsplit_max = static_cast<int>((blocks_max + chunk_blocks - 1) / chunk_blocks);
+        if (p.nsplit_max < 1) p.nsplit_max = 1;
+        p.parts_max = 0;
+        parts = p.nsplit_max > 1 ? slabs * p.nsplit_max : 0;
+    }
+    if (parts > 0) {
+        p.ws_bytes = align_up(static_cast<size_t>(parts) * p.rows * d.head_dim * sizeof(float), 256) +
+                     align_up(static_cast<size_t>(parts) * p.rows * sizeof(float2), 256) +
+                     align_up(static_cast<size_t>(slabs) * sizeof(int2), 256);
     } else {
         p.ws_bytes = 0;
     }
     return p;
 }
 
+template <typename K>
+static int resident_per_cu(K kernel, int threads) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1) n = 1;
+    return n;
+}
+
+static int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+template <int D, int RT>
+static int mfma_resident() {
+    static int n = 0;
+    if (n == 0) n = resident_per_cu(attn_mfma<D, RT>, 64);
+    return n;
+}
+
+template <int D>
+static int mfma_resident_rt(int rt) {
+    switch (rt) {
+        case 1: return mfma_resident<D, 1>();
+        case 2: return mfma_resident<D, 2>();
+        case 3: return mfma_resident<D, 3>();
+        default: return mfma_resident<D, 4>();
+    }
+}
+
 template <int D>
 static void launch_mfma_rt(const AttnPlan& p, const AttnArgs& a, dim3 grid, hipStream_t st) {
     switch (p.row_tiles) {
-        case 1: hipLaunchKernelGGL((attn_mfma<D, 1, 4>), grid, dim3(256), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((attn_mfma<D, 2, 4>), grid, dim3(256), 0, st, a); break;
-        case 3: hipLaunchKernelGGL((attn_mfma<D, 3, 2>), grid, dim3(128), 0, st, a); break;
-        default: hipLaunchKernelGGL((attn_mfma<D, 4, 2>), grid, dim3(128), 0, st, a); break;
+        case 1: hipLaunchKernelGGL((attn_mfma<D, 1>), grid, dim3(64), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((attn_mfma<D, 2>), grid, dim3(64), 0, st, a); break;
+        case 3: hipLaunchKernelGGL((attn_mfma<D, 3>), grid, dim3(64), 0, st, a); break;
+        default: hipLaunchKernelGGL((attn_mfma<D, 4>), grid, dim3(64), 0, st, a); break;
     }
 }
 
@@ -650,22 +855,41 @@ int launch_verify_attn(const spec_attn_desc& d, const AttnPlan& p, const void* q
     a.cap = d.kv_capacity;
     a.R = p.rows;
     a.nrg = p.row_groups;
-    a.chunk = p.chunk;
-    a.nsplit_max = p.nsplit_max;
+    a.balanced = p.balanced ? 1 : 0;
+    a.split_blocks = p.split_blocks;
     a.max_keys = p.max_keys;
     const float scale = d.softmax_scale > 0.f ? d.softmax_scale : 1.0f / sqrtf(static_cast<float>(d.head_dim));
     a.scale_log2 = scale * 1.4426950408889634f;
-    if (p.nsplit_max > 1) {
-        const size_t parts = static_cast<size_t>(d.batch) * d.num_kv_heads * p.nsplit_max * p.rows;
+    const long slabs = static_cast<long>(d.batch) * d.num_kv_heads;
+    long units;
+    bool combine;
+    if (p.balanced) {
+        const int per_cu = d.head_dim == 128 ? mfma_resident_rt<128>(p.row_tiles) : mfma_resident_rt<64>(p.row_tiles);
+        long P = static_cast<long>(per_cu) * device_cus() / p.row_groups;
+        if (P > p.parts_max) P = p.parts_max;
+        if (P >= 8) P = P / 8 * 8;
+        if (P < 1) P = 1;
+        a.nparts = static_cast<int>(P);
+        units = P;
+        combine = P > 1;
+    } else {
+        a.nparts = p.nsplit_max;
+        units = slabs * p.nsplit_max;
+        combine = p.nsplit_max > 1;
+    }
+    if (combine) {
+        const long parts = p.balanced ? p.parts_max + slabs : slabs * p.nsplit_max;
         char* ws = static_cast<char*>(workspace);
         a.ws_o = reinterpret_cast<float*>(ws);
-        ws += align_up(parts * d.head_dim * sizeof(float), 256);
+        ws += align_up(static_cast<size_t>(parts) * p.rows * d.head_dim * sizeof(float), 256);
         a.ws_ml = reinterpret_cast<float2*>(ws);
+        ws += align_up(static_cast<size_t>(parts) * p.rows * sizeof(float2), 256);
+        a.seg = reinterpret_cast<int2*>(ws);
     } else {
         a.ws_o = nullptr;
         a.ws_ml = nullptr;
+        a.seg = nullptr;
     }
-    const long units = static_cast<long>(d.batch) * d.num_kv_heads * p.nsplit_max;
     const long units_pad = (units + 7) / 8 * 8;
     const dim3 grid(static_cast<unsigned>(units_pad * p.row_groups));
     if (p.mfma) {
@@ -685,8 +909,8 @@ int launch_verify_attn(const spec_attn_desc& d, const AttnPlan& p, const void* q
             hipLaunchKernelGGL((attn_valu<uint16_t, 64>), grid, dim3(256), 0, stream, a);
     }
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-    if (p.nsplit_max > 1) {
-        const long rows = static_cast<long>(d.batch) * d.num_kv_heads * p.rows;
+    if (combine) {
+        const long rows = slabs * p.rows;
         const dim3 cgrid(static_cast<unsigned>((rows + 3) / 4));
         const int bf16_out = d.dtype == SPEC_BF16;
         if (d.head_dim == 128)

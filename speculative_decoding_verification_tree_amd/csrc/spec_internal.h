@@ -11,15 +11,17 @@ namespace specv {
 
 // Execution plan of spec_verify_attn for one descriptor and prefix bound.
 struct AttnPlan {
-    bool mfma;       // bf16 MFMA path (else the VALU path)
-    int rows;        // R = N * (Hq / Hkv): query rows per (request, kv head)
-    int row_tiles;   // MFMA: 16-row tiles per wave
-    int waves;       // wavefronts per workgroup
-    int row_groups;  // workgroups sharing one KV chunk (different query rows)
-    int chunk;       // keys per split
-    int nsplit_max;  // splits of the longest request
-    int max_keys;    // max_prefix_len + N
-    size_t ws_bytes; // split partials (0 when one split covers every request)
+    bool mfma;        // bf16 MFMA path (else the VALU path)
+    bool balanced;    // balanced block ranges (else fixed splits per slab)
+    int rows;         // R = N * (Hq / Hkv): query rows per (request, kv head)
+    int row_tiles;    // MFMA: 16-row tiles per wave
+    int waves;        // wavefronts per workgroup
+    int row_groups;   // workgroups sharing one KV range (different query rows)
+    int split_blocks; // fixed: 32-key blocks per split; balanced: least blocks per range
+    int nsplit_max;   // fixed: splits of the longest request
+    int parts_max;    // balanced: most ranges P a launch may use
+    int max_keys;     // max_prefix_len + N
+    size_t ws_bytes;  // partials + per-slab table (0 when no slab is ever split)
 };
 
 AttnPlan plan_attn(const spec_attn_desc& d, int max_prefix_len);

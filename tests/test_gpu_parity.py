@@ -85,6 +85,33 @@ def test_attention_tree_edge_cases(over):
     _attn_all_rows(w, f"tree edge {over}")
 
 
+@pytest.mark.parametrize("batch", [480, 481, 520])
+def test_attention_batch_mode_edge(batch):
+    # 480 is the largest batch of the balanced ranges; larger batches take
+    # fixed splits per slab.
+    w = generate(scaled(4, batch=batch, num_q_heads=8, num_kv_heads=2, prefix_len=(0, 300)), with_accept=False)
+    _attn_all_rows(w, f"batch-mode edge B={batch}")
+
+
+def test_attention_many_short_segments(monkeypatch):
+    # One block per range: ranges cross slab ends everywhere and slabs merge
+    # many partials.
+    monkeypatch.setenv("SPEC_VERIFY_MIN_BLOCKS", "1")
+    w = generate(scaled(4, batch=6, prefix_len=(0, 1500)), with_accept=False)
+    _attn_all_rows(w, "min blocks 1, ragged")
+    w = generate(scaled(5, batch=3, prefix_len=(0, 900), nodes=40), with_accept=False)
+    _attn_all_rows(w, "min blocks 1, tree")
+
+
+def test_attention_loose_prefix_bound():
+    # The host bound far above every actual prefix: most ranges are empty.
+    w = generate(scaled(4, batch=5, prefix_len=(0, 200)), with_accept=False, capacity=6000)
+    announce("attention loose prefix bound 5000")
+    gpu = run_attention(w, max_prefix_len=5000)
+    ref = oracle.tree_attn(w.q, w.k_cache, w.v_cache, w.prefix_len, None, w.dtype)
+    check_attention(gpu, ref, "loose bound")
+
+
 def test_attention_empty_batch():
     announce("attention B=0")
     q = torch.empty(0, 6, 32, 128, dtype=torch.bfloat16, device="cuda")
