@@ -25,16 +25,16 @@
 //                   and the decision.  Then each workgroup reduces its chunk
 //                   of the stop row: residual mass, bonus mass or argmax.
 //   accept_select   grid B: scan the chunk masses in token order, find the
-//                   chunk that holds u * total and the token inside it (block
-//                   scan, ascending token ids).
+//                   chunk that holds u * total and the token inside it
+//                   (wavefront scans, ascending token ids).
 #include "spec_common.h"
 #include "spec_internal.h"
 
 namespace specv {
 
 struct RowStat {  // per (request, node row, chunk)
-    double S;     // sum exp((l - M)/T) over the chunk
-    double A;     // sum t * exp(t), t = (l - M)/T
+    double S;     // sum 2^t2 over the chunk, t2 = (l - M) * log2(e) / T
+    double A;     // sum t2 * 2^t2 (so sum t * exp(t) = ln2 * A for t = (l - M) / T)
     float M;      // chunk max logit
     int arg;      // lowest index of the chunk max
 };
@@ -122,9 +122,10 @@ __device__ __forceinline__ void block_argmax(float& v, int& i, float* s_v, int* 
         }
 }
 
-// p_v(x) as the residual and sampling passes evaluate it (fp32).
-__device__ __forceinline__ float target_prob(float l, float M, float T, float invS) {
-    return expf((l - M) / T) * invS;
+// p_v(x) as the residual and sampling passes evaluate it (fp32): the
+// weight 2^((l - M) * c2) / S, c2 = log2(e) / T.
+__device__ __forceinline__ float target_prob(float l, float M, float c2, float invS) {
+    return __builtin_amdgcn_exp2f((l - M) * c2) * invS;
 }
 
 // Element e of this thread's share of a chunk starting at x0: strided by
@@ -167,71 +168,136 @@ __device__ __forceinline__ Vals<EPT> load_chunk(const float* row, int x0, int x1
     return r;
 }
 
-// Chunk statistics of one target row: lowest-index argmax, then (T > 0) the
-// exp sums relative to the chunk max.
+// Per-wave partial results of a chunk reduction.
+struct WaveRed {
+    float m[4];
+    int i[4];
+    double s[4], a[4];
+};
+
+// Chunk statistics of one target row: max logit with its lowest index and,
+// for T > 0, S = sum 2^t2 and A2 = sum t2 * 2^t2 with t2 = (l - max) * c2
+// (so sum exp(t) = S and sum t * exp(t) = ln2 * A2 for t = (l - max) / T).
+// Each wave reduces relative to its own max; one barrier, then every thread
+// merges the four waves in the same order.
 template <int EPT>
-__device__ __forceinline__ void row_chunk_stats(const float* row, int x0, int x1, bool vec4, float T, float& best, int& bi,
-                                double& S, double& A, float* s_v, int* s_i, double* s_red) {
+__device__ __forceinline__ void chunk_stats(const float* row, int x0, int x1, bool vec4, float T, float& M, int& arg,
+                                            double& S, double& A2, WaveRed* s) {
     const Vals<EPT> vals = load_chunk<EPT>(row, x0, x1, vec4, -INFINITY);
-    const float* val = vals.v;
-    best = -INFINITY;
-    bi = 0x7fffffff;
+    float best = -INFINITY;
+    int bi = 0x7fffffff;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
         const int x = elem_index(x0, e, vec4);
-        if (x < x1 && (val[e] > best || (val[e] == best && x < bi))) {
-            best = val[e];
+        if (x < x1 && (vals.v[e] > best || (vals.v[e] == best && x < bi))) {
+            best = vals.v[e];
             bi = x;
         }
     }
-    block_argmax(best, bi, s_v, s_i);
-    S = 0.0;
-    A = 0.0;
-    if (T > 0.f) {
+    wave_argmax(best, bi);
+    double sw = 0.0, aw = 0.0;
+    if (T > 0.f && best > -INFINITY) {
+        const float c2 = 1.4426950408889634f / T;
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
             if (elem_index(x0, e, vec4) < x1) {
-                const float t = (val[e] - best) / T;
-                const float ex = expf(t);
-                S += static_cast<double>(ex);
-                A += static_cast<double>(t) * static_cast<double>(ex);
+                const float t2 = (vals.v[e] - best) * c2;
+                const float ex = __builtin_amdgcn_exp2f(t2);
+                sw += static_cast<double>(ex);
+                aw += static_cast<double>(t2) * static_cast<double>(ex);
             }
         }
-        block_sum2_d(S, A, s_red);
+        sw = wave_sum(sw);
+        aw = wave_sum(aw);
+    }
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    if (lane == 0) {
+        s->m[wv] = best;
+        s->i[wv] = bi;
+        s->s[wv] = sw;
+        s->a[wv] = aw;
+    }
+    __syncthreads();
+    M = s->m[0];
+    arg = s->i[0];
+#pragma unroll
+    for (int k = 1; k < 4; ++k)
+        if (s->m[k] > M || (s->m[k] == M && s->i[k] < arg)) {
+            M = s->m[k];
+            arg = s->i[k];
+        }
+    S = 0.0;
+    A2 = 0.0;
+    if (T > 0.f) {
+        const double c2 = 1.4426950408889634 / static_cast<double>(T);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (s->m[k] > -INFINITY) {
+                const double dl = (static_cast<double>(s->m[k]) - M) * c2;
+                const double w = exp2(dl);
+                S += w * s->s[k];
+                A2 += w * (s->a[k] + dl * s->s[k]);
+            }
     }
 }
 
-// ---------------------------------------------------------------------------
-// Parent array of request b in LDS, and which nodes have children.
-__device__ __forceinline__ void load_tree(const AcceptArgs& a, int b, int* s_par, int* s_has) {
-    const int tid = threadIdx.x;
-    if (tid < kMaxNodes) s_has[tid] = 0;
-    if (tid < a.N) s_par[tid] = tree_parent(a.parent, a.N, b, tid);
-    __syncthreads();
-    if (tid > 0 && tid < a.N && s_par[tid] >= 0) s_has[s_par[tid]] = 1;
-    __syncthreads();
+// Does node u of request b have a child?  (Wave-uniform; chains need no load.)
+__device__ __forceinline__ bool row_has_children(const AcceptArgs& a, int b, int u) {
+    if (!a.parent) return u < a.N - 1;
+    const int i = (threadIdx.x & 63) + 1;
+    const int p = i < a.N ? tree_parent(a.parent, a.N, b, i) : -1;
+    return __ballot(p == u) != 0ull;
+}
+
+template <int EPT>
+__global__ __launch_bounds__(kThreads) void accept_rowstats(AcceptArgs a) {
+    const int c = blockIdx.x, u = blockIdx.y, b = blockIdx.z;
+    __shared__ WaveRed s_red;
+    if (!row_has_children(a, b, u)) return;  // leaves need no statistics
+    const float* row = a.logits + (static_cast<size_t>(b) * a.N + u) * a.V;
+    const int x0 = c * a.chunk, x1 = min(x0 + a.chunk, a.V);
+    float M;
+    int arg;
+    double S, A2;
+    chunk_stats<EPT>(row, x0, x1, a.vec4 != 0, a.T, M, arg, S, A2, &s_red);
+    if (threadIdx.x == 0) {
+        RowStat rs;
+        rs.S = S;
+        rs.A = A2;
+        rs.M = M;
+        rs.arg = arg;
+        a.rowstat[(static_cast<size_t>(b) * a.N + u) * a.nchunk + c] = rs;
+    }
 }
 
 // Decision of request b from the chunk statistics.  Every accept_sample
 // workgroup of the request computes it (same inputs, same code, same result);
 // only the writer stores path, accepted tokens, accept_len and the record.
-// (Templated on the caller's chunk width only so that each kernel owns its
-// copy of the LDS arrays below.)
-template <int EPT>
-__device__ __forceinline__ void decide_request(const AcceptArgs& a, int b, bool writer, const int* s_par, const int* s_has,
-                               Decision* s_dec) {
+// Every load that depends on nothing else is issued first: the tree, the
+// drafted tokens and uniforms, and the chunk records of every row (a leaf's
+// records are stale and never used).
+__device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, bool writer) {
     const int N = a.N, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __shared__ float s_M[kMaxNodes];
     __shared__ int s_arg[kMaxNodes];
     __shared__ double s_S[kMaxNodes], s_H[kMaxNodes];
-    __shared__ int s_path[kMaxNodes], s_depth[kMaxNodes];
+    __shared__ int s_path[kMaxNodes];
+    __shared__ Decision s_dec;
 
-    // Whole-row statistics: wave w owns rows w, w+4, ...  Lane c first loads
-    // chunk c of every row it serves in one round of independent loads; only
-    // vocabularies of more than 64 chunks take the extra loops.
+    int pi = -1, xi = 0;
+    float ui = 0.f;
+    if (wave == 0 && lane < N) {
+        pi = tree_parent(a.parent, N, b, lane);
+        const int x = a.tokens[static_cast<size_t>(b) * N + lane];
+        xi = min(max(x, 0), a.V - 1);
+        if (a.rule == 0 && a.u_acc) ui = a.u_acc[static_cast<size_t>(b) * N + lane];
+    }
+    // Whole-row statistics: wave w owns rows w, w+4, ...; lane c loads chunk
+    // c of each in one round (vocabularies of more than 64 chunks loop).
     const double T = a.T;
-    float mc[kRowsPerWave], m[kRowsPerWave];
-    int ac[kRowsPerWave], ar[kRowsPerWave];
+    const double c2 = T > 0.0 ? 1.4426950408889634 / T : 0.0;
+    float mc[kRowsPerWave];
+    int ac[kRowsPerWave];
     double sc[kRowsPerWave], scA[kRowsPerWave];
 #pragma unroll
     for (int k = 0; k < kRowsPerWave; ++k) {
@@ -240,7 +306,7 @@ __device__ __forceinline__ void decide_request(const AcceptArgs& a, int b, bool 
         ac[k] = 0x7fffffff;
         sc[k] = 0.0;
         scA[k] = 0.0;
-        if (u < N && s_has[u] && lane < a.nchunk) {
+        if (u < N - 1 + (a.parent != nullptr) && lane < a.nchunk) {
             const RowStat r = a.rowstat[(static_cast<size_t>(b) * N + u) * a.nchunk + lane];
             mc[k] = r.M;
             ac[k] = r.arg;
@@ -248,129 +314,116 @@ __device__ __forceinline__ void decide_request(const AcceptArgs& a, int b, bool 
             scA[k] = r.A;
         }
     }
+    // The tested values, gathered at the drafted tokens as soon as they land.
+    double gl = 0.0, gq = 0.0;
+    if (wave == 0 && lane >= 1 && lane < N && pi >= 0) {
+        gl = a.logits[(static_cast<size_t>(b) * N + pi) * a.V + xi];
+        if (a.rule == 0) gq = a.draft[(static_cast<size_t>(b) * N + lane) * a.V + xi];
+    }
 #pragma unroll
     for (int k = 0; k < kRowsPerWave; ++k) {
-        m[k] = mc[k];
-        ar[k] = ac[k];
         const int u = wave + 4 * k;
-        if (u < N && s_has[u]) {  // wave-uniform
+        if (!(u < N - 1 + (a.parent != nullptr))) continue;  // wave-uniform
+        float m = mc[k];
+        int ar = ac[k];
+        for (int c = lane + 64; c < a.nchunk; c += 64) {
+            const RowStat& r = a.rowstat[(static_cast<size_t>(b) * N + u) * a.nchunk + c];
+            if (r.M > m || (r.M == m && r.arg < ar)) {
+                m = r.M;
+                ar = r.arg;
+            }
+        }
+        wave_argmax(m, ar);
+        double S = 0.0, A2 = 0.0;
+        if (T > 0.0) {
+            if (lane < a.nchunk) {
+                const double dl = (static_cast<double>(mc[k]) - m) * c2;
+                const double w = exp2(dl);
+                S = w * sc[k];
+                A2 = w * (scA[k] + dl * sc[k]);
+            }
             for (int c = lane + 64; c < a.nchunk; c += 64) {
-                const RowStat& r = a.rowstat[(static_cast<size_t>(b) * N + u) * a.nchunk + c];
-                if (r.M > m[k] || (r.M == m[k] && r.arg < ar[k])) {
-                    m[k] = r.M;
-                    ar[k] = r.arg;
-                }
+                const RowStat r = a.rowstat[(static_cast<size_t>(b) * N + u) * a.nchunk + c];
+                const double dl = (static_cast<double>(r.M) - m) * c2;
+                const double w = exp2(dl);
+                S += w * r.S;
+                A2 += w * (r.A + dl * r.S);
             }
-            wave_argmax(m[k], ar[k]);
+            S = wave_sum(S);
+            A2 = wave_sum(A2);
         }
-    }
-    if (T > 0.0) {
-#pragma unroll
-        for (int k = 0; k < kRowsPerWave; ++k) {
-            const int u = wave + 4 * k;
-            double S = 0.0, A = 0.0;
-            if (u < N && s_has[u]) {
-                if (lane < a.nchunk) {
-                    const double dl = (static_cast<double>(mc[k]) - m[k]) / T;
-                    const double wgt = exp(dl);
-                    S = wgt * sc[k];
-                    A = wgt * (scA[k] + dl * sc[k]);
-                }
-                for (int c = lane + 64; c < a.nchunk; c += 64) {
-                    const RowStat r = a.rowstat[(static_cast<size_t>(b) * N + u) * a.nchunk + c];
-                    const double dl = (static_cast<double>(r.M) - m[k]) / T;
-                    const double wgt = exp(dl);
-                    S += wgt * r.S;
-                    A += wgt * (r.A + dl * r.S);
-                }
-            }
-            if (u < N && s_has[u]) {  // wave-uniform
-                S = wave_sum(S);
-                A = wave_sum(A);
-                if (lane == 0) {
-                    s_S[u] = S;
-                    s_H[u] = log(S) - A / S;
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < kRowsPerWave; ++k) {
-        const int u = wave + 4 * k;
-        if (lane == 0 && u < N && s_has[u]) {
-            s_M[u] = m[k];
-            s_arg[u] = ar[k];
-            if (!(T > 0.0)) {
-                s_S[u] = 0.0;
-                s_H[u] = 0.0;
-            }
+        if (lane == 0) {
+            s_M[u] = m;
+            s_arg[u] = ar;
+            s_S[u] = S;
+            s_H[u] = T > 0.0 ? log(S) - 0.6931471805599453 * A2 / S : 0.0;
         }
     }
     __syncthreads();
 
     if (wave == 0) {
-        // Per-node tests in fp64 from the gathered values (nodes live in wave 0).
+        // Node tests in fp64 from the gathered values.
         bool ok = false;
-        if (lane >= 1 && lane < N) {
-            const int u = s_par[lane];
-            if (u >= 0) {
-                int x = a.tokens[static_cast<size_t>(b) * N + lane];
-                x = min(max(x, 0), a.V - 1);
-                double pu;
-                if (T > 0.0) {
-                    const double l = a.logits[(static_cast<size_t>(b) * N + u) * a.V + x];
-                    pu = exp((l - static_cast<double>(s_M[u])) / T) / s_S[u];
-                } else {
-                    pu = x == s_arg[u] ? 1.0 : 0.0;
-                }
-                if (a.rule == 0) {
-                    const double qx = a.draft[(static_cast<size_t>(b) * N + lane) * a.V + x];
-                    ok = static_cast<double>(a.u_acc[static_cast<size_t>(b) * N + lane]) * qx < pu;
-                } else {
-                    const double thr =
-                        fmin(static_cast<double>(a.eps), static_cast<double>(a.delta) * exp(-s_H[u]));
-                    ok = pu > thr;
-                }
+        if (lane >= 1 && lane < N && pi >= 0) {
+            double pu;
+            if (T > 0.0)
+                pu = exp((gl - static_cast<double>(s_M[pi])) / T) / s_S[pi];
+            else
+                pu = xi == s_arg[pi] ? 1.0 : 0.0;
+            if (a.rule == 0) {
+                ok = static_cast<double>(ui) * gq < pu;
+            } else {
+                const double thr = fmin(static_cast<double>(a.eps), static_cast<double>(a.delta) * exp(-s_H[pi]));
+                ok = pu > thr;
             }
         }
-        const unsigned long long okm = __ballot(ok);
-        if (lane == 0) {
-            uint64_t acc = 1ull;  // the root is always accepted
-            s_depth[0] = 0;
-            int v = 0, dv = 0;
-            for (int i = 1; i < N; ++i) {
-                const int u = s_par[i];
-                const int di = u >= 0 ? s_depth[u] + 1 : 0;
-                s_depth[i] = di;
-                if (u >= 0 && ((okm >> i) & 1ull) && ((acc >> u) & 1ull)) {
-                    acc |= 1ull << i;
-                    if (di > dv) {
-                        v = i;
-                        dv = di;
-                    }
-                }
+        const uint64_t okm = __ballot(ok) | 1ull;  // the root is always accepted
+        // Root paths by pointer doubling: after round k a lane holds its
+        // first 2^k path nodes and its 2^k-th ancestor.
+        const int me = lane < N ? lane : 0;
+        int up = lane < N ? pi : -1;
+        uint64_t anc = 1ull << me;
+#pragma unroll
+        for (int r = 0; r < 6; ++r) {
+            const int src = up >= 0 ? up : 0;
+            const uint32_t lo = __shfl(static_cast<uint32_t>(anc), src), hi = __shfl(static_cast<uint32_t>(anc >> 32), src);
+            const int upup = __shfl(up, src);
+            if (up >= 0) {
+                anc |= static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
+                up = upup;
             }
-            for (int n = v, d = dv; d >= 0; n = s_par[n], --d) s_path[d] = n;
-            int c = -1;
-            for (int i = v + 1; i < N && c < 0; ++i)
-                if (s_par[i] == v) c = i;
+        }
+        // Accepted: every node on the root path passed.  The stop node is the
+        // deepest accepted node, the lowest index among equals.
+        const bool accepted = lane < N && (anc & ~okm) == 0ull;
+        const int depth = __popcll(anc) - 1;
+        float key = accepted ? static_cast<float>(depth) : -1.f;
+        int v = lane;
+        wave_argmax(key, v);
+        const int dv = static_cast<int>(key);
+        const uint32_t vlo = __shfl(static_cast<uint32_t>(anc), v), vhi = __shfl(static_cast<uint32_t>(anc >> 32), v);
+        const uint64_t anc_v = static_cast<uint64_t>(vlo) | (static_cast<uint64_t>(vhi) << 32);
+        if (lane < N && ((anc_v >> lane) & 1ull)) s_path[depth] = lane;
+        const uint64_t kids = __ballot(lane >= 1 && lane < N && pi == v);
+        const bool v_has = kids != 0ull;
+        if (lane == 0) {
             Decision d;
             d.v = v;
-            d.c = c;
+            d.c = v_has ? __ffsll(static_cast<long long>(kids)) - 1 : -1;
             d.a = dv;
             d.u = a.u_smp ? a.u_smp[static_cast<size_t>(b) * N + v] : 0.f;
-            d.M = s_has[v] ? s_M[v] : 0.f;
-            d.S = s_has[v] ? s_S[v] : 0.0;
+            d.M = v_has ? s_M[v] : 0.f;
+            d.S = v_has ? s_S[v] : 0.0;
             if (a.rule == 1 || !(T > 0.0))
-                d.mode = s_has[v] ? MODE_DONE : MODE_ARGMAX;
+                d.mode = v_has ? MODE_DONE : MODE_ARGMAX;
             else
-                d.mode = s_has[v] ? MODE_RESID : MODE_BONUS;
-            *s_dec = d;
+                d.mode = v_has ? MODE_RESID : MODE_BONUS;
+            s_dec = d;
         }
     }
     __syncthreads();
+    const Decision d = s_dec;
     if (writer) {
-        const Decision d = *s_dec;
         if (tid < N) {
             const size_t o = static_cast<size_t>(b) * N + tid;
             a.path[o] = tid <= d.a ? s_path[tid] : -1;
@@ -383,44 +436,15 @@ __device__ __forceinline__ void decide_request(const AcceptArgs& a, int b, bool 
             a.dec[b] = d;
         }
     }
-}
-
-template <int EPT>
-__global__ __launch_bounds__(kThreads) void accept_rowstats(AcceptArgs a) {
-    const int c = blockIdx.x, u = blockIdx.y, b = blockIdx.z;
-    __shared__ int s_par[kMaxNodes], s_has[kMaxNodes];
-    __shared__ double s_red[8];
-    __shared__ float s_v[4];
-    __shared__ int s_i[4];
-    load_tree(a, b, s_par, s_has);
-    if (!s_has[u]) return;  // leaves need no statistics
-    const float* row = a.logits + (static_cast<size_t>(b) * a.N + u) * a.V;
-    const int x0 = c * a.chunk, x1 = min(x0 + a.chunk, a.V);
-    float best;
-    int bi;
-    double S, A;
-    row_chunk_stats<EPT>(row, x0, x1, a.vec4 != 0, a.T, best, bi, S, A, s_v, s_i, s_red);
-    if (threadIdx.x == 0) {
-        RowStat rs;
-        rs.S = S;
-        rs.A = A;
-        rs.M = best;
-        rs.arg = bi;
-        a.rowstat[(static_cast<size_t>(b) * a.N + u) * a.nchunk + c] = rs;
-    }
+    return d;
 }
 
 template <int EPT>
 __global__ __launch_bounds__(kThreads) void accept_sample(AcceptArgs a) {
     const int c = blockIdx.x, b = blockIdx.y;
-    __shared__ int s_par[kMaxNodes], s_has[kMaxNodes];
-    __shared__ Decision s_dec;
-    __shared__ double s_red[8];
-    __shared__ float s_v[4];
-    __shared__ int s_i[4];
-    load_tree(a, b, s_par, s_has);
-    decide_request<EPT>(a, b, c == 0, s_par, s_has, &s_dec);
-    const Decision d = s_dec;
+    __shared__ WaveRed s_red;
+    __shared__ double s_r2[8];
+    const Decision d = decide_request(a, b, c == 0);
     if (d.mode == MODE_DONE) return;
     const float* row = a.logits + (static_cast<size_t>(b) * a.N + d.v) * a.V;
     const int x0 = c * a.chunk, x1 = min(x0 + a.chunk, a.V);
@@ -432,114 +456,181 @@ __global__ __launch_bounds__(kThreads) void accept_sample(AcceptArgs a) {
     if (d.mode == MODE_RESID) {
         const float* qrow = a.draft + (static_cast<size_t>(b) * a.N + d.c) * a.V;
         const float invS = static_cast<float>(1.0 / d.S);
+        const float c2 = 1.4426950408889634f / a.T;
         const Vals<EPT> lvals = load_chunk<EPT>(row, x0, x1, vec4, -INFINITY);
         const Vals<EPT> qvals = load_chunk<EPT>(qrow, x0, x1, vec4, 0.f);
-        const float* lv = lvals.v;
-        const float* qv = qvals.v;
         double r = 0.0, p = 0.0;
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
             if (elem_index(x0, e, vec4) < x1) {
-                const float pv = target_prob(lv[e], d.M, a.T, invS);
-                r += static_cast<double>(fmaxf(pv - qv[e], 0.f));
+                const float pv = target_prob(lvals.v[e], d.M, c2, invS);
+                r += static_cast<double>(fmaxf(pv - qvals.v[e], 0.f));
                 p += static_cast<double>(pv);
             }
         }
-        block_sum2_d(r, p, s_red);
+        block_sum2_d(r, p, s_r2);
         cs.m1 = r;
         cs.m2 = p;
     } else {
-        float best;
-        int bi;
-        double S, A;
-        row_chunk_stats<EPT>(row, x0, x1, vec4, d.mode == MODE_BONUS ? a.T : 0.f, best, bi, S, A, s_v, s_i, s_red);
-        cs.M = best;
-        cs.arg = bi;
+        float M;
+        int arg;
+        double S, A2;
+        chunk_stats<EPT>(row, x0, x1, vec4, d.mode == MODE_BONUS ? a.T : 0.f, M, arg, S, A2, &s_red);
+        cs.M = M;
+        cs.arg = arg;
         cs.m1 = S;
     }
     if (threadIdx.x == 0) a.cstat[static_cast<size_t>(b) * a.nchunk + c] = cs;
 }
 
 // ---------------------------------------------------------------------------
+// Inclusive prefix sum over the lanes of a wavefront.
+__device__ __forceinline__ double wave_incl_scan(double v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double t = __shfl_up(v, o);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// First token of a chunk whose cumulative weight (from `base`, ascending
+// token order) exceeds t, and the last token with weight.  The chunk is held
+// in its coalesced layout: row j is W*kThreads consecutive tokens, W per
+// thread (W = 4 with 16-byte loads, else 1).  Per row: wave scans of the
+// threads' sums, then one barrier for the wave totals.
+template <int EPT, int W>
+__device__ __forceinline__ void locate_token(const double* wv, int x0, double base, double t, double* s_wtot, int& xhit,
+                                             int& lastnz) {
+    constexpr int ROWS = EPT / W;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    double rbefore[ROWS];
+#pragma unroll
+    for (int j = 0; j < ROWS; ++j) {
+        double sj = 0.0;
+#pragma unroll
+        for (int k = 0; k < W; ++k) sj += wv[j * W + k];
+        const double inc = wave_incl_scan(sj);
+        rbefore[j] = inc - sj;
+        if (lane == 63) s_wtot[j * 4 + wave] = inc;
+    }
+    __syncthreads();
+    double rowbase = base;
+#pragma unroll
+    for (int j = 0; j < ROWS; ++j) {
+        double c = rowbase + rbefore[j];
+        for (int k = 0; k < wave; ++k) c += s_wtot[j * 4 + k];
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+            const double wk = wv[j * W + k];
+            if (wk > 0.0) {
+                const int x = x0 + W * (tid + kThreads * j) + k;
+                lastnz = x;
+                c += wk;
+                if (xhit == 0x7fffffff && c > t) xhit = x;
+            }
+        }
+        rowbase += s_wtot[j * 4] + s_wtot[j * 4 + 1] + s_wtot[j * 4 + 2] + s_wtot[j * 4 + 3];
+    }
+}
+
+// Sampling by inverse CDF over the stop row in ascending token order: the
+// chunk totals locate the chunk that holds u * total, then the chunk's
+// weights (recomputed from the same fp32 terms accept_sample summed) locate
+// the token.  Zero-weight tokens are never drawn; if rounding leaves u*total
+// past the end, the last token with weight is taken.
 template <int EPT>
 __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
+    constexpr int CPT = kMaxChunks / kThreads;  // chunk records per thread
     const int b = blockIdx.x;
-    const int tid = threadIdx.x;
-    __shared__ Decision s_d;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __shared__ float s_v[4];
     __shared__ int s_i[4];
     __shared__ double s_red[8];
-    __shared__ double s_w[kMaxChunks];
-    __shared__ double s_scan[kThreads];
-    __shared__ float s_wt[EPT * kThreads];
+    __shared__ double s_wtot[4 * (EPT > CPT ? EPT : CPT)];
     __shared__ int s_pick;
     __shared__ double s_base;
-    if (tid == 0) s_d = a.dec[b];
-    __syncthreads();
-    const Decision d = s_d;
+
+    // The decision and this thread's run of chunk records, loaded together.
+    const Decision d = a.dec[b];
+    const ChunkStat* csb = a.cstat + static_cast<size_t>(b) * a.nchunk;
+    ChunkStat cs[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const int c = tid * CPT + k;
+        if (c < a.nchunk) cs[k] = csb[c];
+        else {
+            cs[k].m1 = cs[k].m2 = 0.0;
+            cs[k].M = -INFINITY;
+            cs[k].arg = 0x7fffffff;
+        }
+    }
     if (d.mode == MODE_DONE) return;
-    const ChunkStat* cs = a.cstat + static_cast<size_t>(b) * a.nchunk;
     int32_t* out = a.out_tokens + static_cast<size_t>(b) * a.N + d.a;
 
     if (d.mode == MODE_ARGMAX) {
         float best = -INFINITY;
         int bi = 0x7fffffff;
-        for (int c = tid; c < a.nchunk; c += kThreads)
-            if (cs[c].M > best || (cs[c].M == best && cs[c].arg < bi)) {
-                best = cs[c].M;
-                bi = cs[c].arg;
+#pragma unroll
+        for (int k = 0; k < CPT; ++k)
+            if (cs[k].M > best || (cs[k].M == best && cs[k].arg < bi)) {
+                best = cs[k].M;
+                bi = cs[k].arg;
             }
         block_argmax(best, bi, s_v, s_i);
         if (tid == 0) *out = bi;
         return;
     }
 
-    // Chunk weights in token order.
+    // Chunk weights in token order (thread t owns chunks t*CPT .. t*CPT+CPT-1).
     const double T = a.T;
+    const double c2d = 1.4426950408889634 / T;
     double Mg = -INFINITY, tot1 = 0.0;
     if (d.mode == MODE_BONUS) {
         float mloc = -INFINITY;
         int dummy = 0;
-        for (int c = tid; c < a.nchunk; c += kThreads) mloc = fmaxf(mloc, cs[c].M);
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) mloc = fmaxf(mloc, cs[k].M);
         block_argmax(mloc, dummy, s_v, s_i);
         Mg = mloc;
     } else {
         double t1 = 0.0;
-        for (int c = tid; c < a.nchunk; c += kThreads) t1 += cs[c].m1;
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) t1 += cs[k].m1;
         tot1 = block_sum_d(t1, s_red);
     }
     const bool usep = d.mode == MODE_RESID && !(tot1 > 0.0);  // all-zero residual: fall back to p_v
-    for (int c = tid; c < a.nchunk; c += kThreads)
-        s_w[c] = d.mode == MODE_BONUS ? cs[c].m1 * exp((static_cast<double>(cs[c].M) - Mg) / T)
-                                      : (usep ? cs[c].m2 : cs[c].m1);
-    __syncthreads();
-    // Inclusive scan of the chunk weights: each thread owns a run of chunks.
-    const int per = (a.nchunk + kThreads - 1) / kThreads;
-    const int c0 = tid * per, c1 = min(c0 + per, a.nchunk);
+    double w[CPT];
     double run = 0.0;
-    for (int c = c0; c < c1; ++c) run += s_w[c];
-    s_scan[tid] = run;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-        const double add = tid >= off ? s_scan[tid - off] : 0.0;
-        __syncthreads();
-        s_scan[tid] += add;
-        __syncthreads();
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        w[k] = tid * CPT + k >= a.nchunk ? 0.0
+               : d.mode == MODE_BONUS    ? cs[k].m1 * exp2((static_cast<double>(cs[k].M) - Mg) * c2d)
+               : usep                    ? cs[k].m2
+                                         : cs[k].m1;
+        run += w[k];
     }
-    const double total = s_scan[kThreads - 1];
+    // Exclusive prefix of this thread's run: wave scan + wave totals.
+    const double incl = wave_incl_scan(run);
+    if (lane == 63) s_wtot[wave] = incl;
+    __syncthreads();
+    double before = incl - run;
+    for (int k = 0; k < wave; ++k) before += s_wtot[k];
+    const double total = s_wtot[0] + s_wtot[1] + s_wtot[2] + s_wtot[3];
     const double t = static_cast<double>(d.u) * total;
-    double cum = s_scan[tid] - run;
     int hit = 0x7fffffff, lastc = -1;
-    double hit_base = 0.0;
-    for (int c = c0; c < c1; ++c) {
-        if (s_w[c] > 0.0) {
-            lastc = c;
-            if (hit == 0x7fffffff && cum + s_w[c] > t) {
-                hit = c;
+    double hit_base = 0.0, cum = before;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        if (w[k] > 0.0) {
+            lastc = tid * CPT + k;
+            if (hit == 0x7fffffff && cum + w[k] > t) {
+                hit = tid * CPT + k;
                 hit_base = cum;
             }
         }
-        cum += s_w[c];
+        cum += w[k];
     }
     // smallest chunk with a hit, else the last chunk with weight
     float fh = hit == 0x7fffffff ? -INFINITY : -static_cast<float>(hit);
@@ -556,66 +647,44 @@ __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
     if (ih != 0x7fffffff && hit == ih) s_base = hit_base;
     __syncthreads();
 
-    // Token inside the chosen chunk.  Weights are computed from coalesced
-    // loads and staged in LDS (fp32, the same values accept_sample summed);
-    // each thread then scans a contiguous run in ascending token order.
+    // Token inside the chosen chunk, from its coalesced layout: row j of the
+    // layout is W*kThreads consecutive tokens, W per thread (W = 4 with
+    // 16-byte loads, else 1).
     const int pc = s_pick;
+    const double base = s_base;
     const int x0 = pc * a.chunk, x1 = min(x0 + a.chunk, a.V);
     const bool vec4 = a.vec4 != 0;
     const float* row = a.logits + (static_cast<size_t>(b) * a.N + d.v) * a.V;
     const float* qrow = d.mode == MODE_RESID ? a.draft + (static_cast<size_t>(b) * a.N + d.c) * a.V : nullptr;
     const float invS = d.mode == MODE_RESID ? static_cast<float>(1.0 / d.S) : 0.f;
-    const float Mc = cs[pc].M;
-    const double scale = d.mode == MODE_BONUS ? exp((static_cast<double>(Mc) - Mg) / T) : 1.0;
-    {
-        const Vals<EPT> lvals = load_chunk<EPT>(row, x0, x1, vec4, -INFINITY);
-        const Vals<EPT> qvals = d.mode == MODE_RESID ? load_chunk<EPT>(qrow, x0, x1, vec4, 0.f) : Vals<EPT>{};
-        const float* lv = lvals.v;
-        const float* qv = qvals.v;
+    const float c2 = 1.4426950408889634f / a.T;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            const int x = elem_index(x0, e, vec4);
-            float wgt = 0.f;
-            if (x < x1) {
-                if (d.mode == MODE_RESID) {
-                    const float pv = target_prob(lv[e], d.M, a.T, invS);
-                    wgt = usep ? pv : fmaxf(pv - qv[e], 0.f);
-                } else {
-                    wgt = expf((lv[e] - Mc) / a.T);
-                }
-            }
-            if (x - x0 < EPT * kThreads) s_wt[x - x0] = wgt;
-        }
-    }
+    for (int k = 0; k < CPT; ++k)
+        if (tid * CPT + k == pc) s_v[0] = cs[k].M;
     __syncthreads();
-    const int xs = x0 + tid * EPT;
+    const float Mc = s_v[0];
+    const double scale = d.mode == MODE_BONUS ? exp2((static_cast<double>(Mc) - Mg) * c2d) : 1.0;
+    const Vals<EPT> lvals = load_chunk<EPT>(row, x0, x1, vec4, -INFINITY);
+    const Vals<EPT> qvals = d.mode == MODE_RESID ? load_chunk<EPT>(qrow, x0, x1, vec4, 0.f) : Vals<EPT>{};
     double wv[EPT];
-    run = 0.0;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-        wv[e] = static_cast<double>(s_wt[tid * EPT + e]) * scale;
-        run += wv[e];
-    }
-    __syncthreads();
-    s_scan[tid] = run;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-        const double add = tid >= off ? s_scan[tid - off] : 0.0;
-        __syncthreads();
-        s_scan[tid] += add;
-        __syncthreads();
-    }
-    cum = s_base + (s_scan[tid] - run);
-    int xhit = 0x7fffffff, lastnz = -1;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-        const int x = xs + e;
-        if (wv[e] > 0.0) {
-            lastnz = x;
-            cum += wv[e];
-            if (xhit == 0x7fffffff && cum > t) xhit = x;
+        float wgt = 0.f;
+        if (elem_index(x0, e, vec4) < x1) {
+            if (d.mode == MODE_RESID) {
+                const float pv = target_prob(lvals.v[e], d.M, c2, invS);
+                wgt = usep ? pv : fmaxf(pv - qvals.v[e], 0.f);
+            } else {
+                wgt = __builtin_amdgcn_exp2f((lvals.v[e] - Mc) * c2);
+            }
         }
+        wv[e] = static_cast<double>(wgt) * scale;
     }
+    int xhit = 0x7fffffff, lastnz = -1;
+    if (vec4)
+        locate_token<EPT, 4>(wv, x0, base, t, s_wtot, xhit, lastnz);
+    else
+        locate_token<EPT, 1>(wv, x0, base, t, s_wtot, xhit, lastnz);
     float fx = xhit == 0x7fffffff ? -INFINITY : -static_cast<float>(xhit);
     int ix = xhit;
     block_argmax(fx, ix, s_v, s_i);
