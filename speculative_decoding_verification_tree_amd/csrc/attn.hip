@@ -130,14 +130,24 @@ struct Seg {
 };
 
 struct SegIter {
-    long x, hi, nb_total;  // balanced: next block, end of range, all blocks
+    int x, hi, nb_total;  // balanced: next block, end of range, all blocks
     int unit;
     bool done;
 };
 
+// floor(num / den) for 0 <= num < 2^52, 0 < den < 2^31: a correctly rounded
+// double quotient is off by at most one, fixed with exact integer products
+// (a 64-bit integer division is a long software sequence here).
+__device__ __forceinline__ int floor_div(long num, int den) {
+    int q = static_cast<int>(static_cast<double>(num) / static_cast<double>(den));
+    if (static_cast<long>(q) * den > num) --q;
+    else if (static_cast<long>(q + 1) * den <= num) ++q;
+    return q;
+}
+
 // Workgroup of global block x in balanced mode: p with floor(p*NB/P) <= x.
-__device__ __forceinline__ int part_of(long x, long nb_total, int P) {
-    return static_cast<int>(((x + 1) * P - 1) / nb_total);
+__device__ __forceinline__ int part_of(int x, int nb_total, int P) {
+    return floor_div(static_cast<long>(x + 1) * P - 1, nb_total);
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -151,10 +161,10 @@ __device__ __forceinline__ SegIter begin_segments(const AttnArgs& a, int unit, i
     it.x = it.hi = it.nb_total = 0;
     if (a.balanced) {
         scan_request_blocks(a, s_cum, s_len);
-        it.nb_total = static_cast<long>(a.Hkv) * s_cum[a.B];
+        it.nb_total = a.Hkv * s_cum[a.B];
         if (unit < a.nparts) {
-            it.x = static_cast<long>(unit) * it.nb_total / a.nparts;
-            it.hi = static_cast<long>(unit + 1) * it.nb_total / a.nparts;
+            it.x = floor_div(static_cast<long>(unit) * it.nb_total, a.nparts);
+            it.hi = floor_div(static_cast<long>(unit + 1) * it.nb_total, a.nparts);
         }
     }
     return it;
@@ -165,7 +175,7 @@ __device__ __forceinline__ bool next_segment(const AttnArgs& a, SegIter& it, con
     if (a.balanced) {
         if (it.x >= it.hi) return false;
         // request b: s_cum[b] <= x / Hkv < s_cum[b + 1]
-        const int y = static_cast<int>(it.x / a.Hkv);
+        const int y = it.x / a.Hkv;
         int lo = 0, hi = a.B;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -173,17 +183,17 @@ __device__ __forceinline__ bool next_segment(const AttnArgs& a, SegIter& it, con
         }
         const int b = uniform(lo);
         const int nb = s_cum[b + 1] - s_cum[b];
-        const long local = it.x - static_cast<long>(a.Hkv) * s_cum[b];
-        const int g = static_cast<int>(local / nb), off = static_cast<int>(local % nb);
-        const long begin = it.x - off, end = begin + nb;
-        const long x1 = end < it.hi ? end : it.hi;
+        const int local = it.x - a.Hkv * s_cum[b];
+        const int g = local / nb, off = local - g * nb;
+        const int begin = it.x - off, end = begin + nb;
+        const int x1 = end < it.hi ? end : it.hi;
         const int q = b * a.Hkv + g;
         const int pf = part_of(begin, it.nb_total, a.nparts), pl = part_of(end - 1, it.nb_total, a.nparts);
         sg.b = b;
         sg.L = uniform(s_len[b]);
         sg.g = uniform(g);
         sg.blk0 = uniform(off);
-        sg.blk1 = uniform(off + static_cast<int>(x1 - it.x));
+        sg.blk1 = uniform(off + (x1 - it.x));
         sg.part = it.unit + q;
         sg.direct = pf == pl;
         sg.table = off == 0;
@@ -221,6 +231,7 @@ __device__ __forceinline__ bool next_segment(const AttnArgs& a, SegIter& it, con
 __device__ __forceinline__ uint64_t anc_mask(const AttnArgs& a, int b) {
     const int lane = threadIdx.x & 63;
     const int i = lane < a.N ? lane : 0;
+    if (!a.parent) return i == 63 ? ~0ull : (2ull << i) - 1ull;  // chain: nodes 0..i
     int up = tree_parent(a.parent, a.N, b, i);
     uint64_t m = 1ull << i;
 #pragma unroll
@@ -659,10 +670,9 @@ __global__ __launch_bounds__(256) void attn_valu(AttnArgs a) {
 // Split combine: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the
 // partials of one slab.  One wavefront per (request, kv head, query row).
 // ----------------------------------------------------------------------------
-template <int D>
+template <int D, int SB>  // SB: partials whose loads are in flight together
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int bf16_out) {
     constexpr int DPL = D / 64;  // output elements per lane
-    constexpr int SB = 16;       // partials whose loads are in flight together
     const int lane = threadIdx.x & 63;
     const long id = static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (id >= static_cast<long>(a.B) * a.Hkv * a.R) return;
@@ -734,6 +744,10 @@ AttnPlan plan_attn(const spec_attn_desc& d, int max_prefix_len) {
     AttnPlan p{};
     const int G = d.num_q_heads / d.num_kv_heads;
     p.rows = d.num_nodes * G;
+    const long slabs = static_cast<long>(d.batch) * d.num_kv_heads;
+    const long keys_max = static_cast<long>(max_prefix_len) + d.num_nodes;
+    const long blocks_max = (keys_max + 31) / 32;
+    long min_blocks = 2;  // balanced mode: least blocks per range
     if (d.dtype == SPEC_BF16) {
         p.mfma = true;
         if (p.rows <= 64) {
@@ -750,16 +764,15 @@ AttnPlan plan_attn(const spec_attn_desc& d, int max_prefix_len) {
         p.row_groups = (p.rows + 31) / 32;
         p.waves = 4;
     }
-    const long slabs = static_cast<long>(d.batch) * d.num_kv_heads;
-    const long keys_max = static_cast<long>(max_prefix_len) + d.num_nodes;
-    const long blocks_max = (keys_max + 31) / 32;
     p.max_keys = static_cast<int>(keys_max);
     long parts;
-    p.balanced = p.mfma && d.batch <= kMaxBalancedBatch;
+    // Balanced ranges index blocks in 32 bits.
+    p.balanced = p.mfma && d.batch <= kMaxBalancedBatch &&
+                 static_cast<long>(d.batch) * d.num_kv_heads * blocks_max < (1L << 30);
     if (p.balanced) {
         // P is picked per launch from the device (resident workgroups); the
         // workspace holds the most partials any device can ask for.
-        const long min_blocks = env_int("SPEC_VERIFY_MIN_BLOCKS") ? env_int("SPEC_VERIFY_MIN_BLOCKS") : 2;
+        if (env_int("SPEC_VERIFY_MIN_BLOCKS")) min_blocks = env_int("SPEC_VERIFY_MIN_BLOCKS");
         long pcap = kMaxResident / p.row_groups;
         if (pcap < 8) pcap = 8;
         const long by_work = (slabs * blocks_max + min_blocks - 1) / min_blocks;
@@ -773,8 +786,8 @@ AttnPlan plan_attn(const spec_attn_desc& d, int max_prefix_len) {
         const long units = slabs * p.row_groups;
         const long want = units >= 4096 ? 1 : (4096 + units - 1) / units;
         long chunk_blocks = (blocks_max + want - 1) / want;
-        const long min_blocks = env_int("SPEC_VERIFY_KV_CHUNK") ? (env_int("SPEC_VERIFY_KV_CHUNK") + 31) / 32 : 8;
-        if (chunk_blocks < min_blocks) chunk_blocks = min_blocks;
+        const long min_split = env_int("SPEC_VERIFY_KV_CHUNK") ? (env_int("SPEC_VERIFY_KV_CHUNK") + 31) / 32 : 8;
+        if (chunk_blocks < min_split) chunk_blocks = min_split;
         p.split_blocks = static_cast<int>(chunk_blocks);
         p.nsplit_max = static_cast<int>((blocks_max + chunk_blocks - 1) / chunk_blocks);
         if (p.nsplit_max < 1) p.nsplit_max = 1;
@@ -913,10 +926,23 @@ int launch_verify_attn(const spec_attn_desc& d, const AttnPlan& p, const void* q
         const long rows = slabs * p.rows;
         const dim3 cgrid(static_cast<unsigned>((rows + 3) / 4));
         const int bf16_out = d.dtype == SPEC_BF16;
-        if (d.head_dim == 128)
-            hipLaunchKernelGGL((attn_combine<128>), cgrid, dim3(256), 0, stream, a, bf16_out);
-        else
-            hipLaunchKernelGGL((attn_combine<64>), cgrid, dim3(256), 0, stream, a, bf16_out);
+        // Partials of the longest slab: its blocks over the blocks per range
+        // (plus one for a range that starts inside it), or its splits.
+        long most;
+        if (p.balanced) {
+            const long per = (slabs * ((static_cast<long>(p.max_keys) + 31) / 32)) / a.nparts;
+            most = per > 0 ? ((p.max_keys + 31) / 32 + per - 1) / per + 1 : a.nparts;
+        } else {
+            most = p.nsplit_max;
+        }
+        const bool wide = most > 16;  // 32 partials per round (more registers)
+        if (d.head_dim == 128) {
+            if (wide) hipLaunchKernelGGL((attn_combine<128, 32>), cgrid, dim3(256), 0, stream, a, bf16_out);
+            else hipLaunchKernelGGL((attn_combine<128, 16>), cgrid, dim3(256), 0, stream, a, bf16_out);
+        } else {
+            if (wide) hipLaunchKernelGGL((attn_combine<64, 32>), cgrid, dim3(256), 0, stream, a, bf16_out);
+            else hipLaunchKernelGGL((attn_combine<64, 16>), cgrid, dim3(256), 0, stream, a, bf16_out);
+        }
         if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     }
     return SPEC_OK;
