@@ -152,15 +152,17 @@ __device__ __forceinline__ int part_of(int x, int nb_total, int P) {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Start the segment walk of this workgroup (one wavefront; balanced mode
-// scans the request block counts into s_cum).
-__device__ __forceinline__ SegIter begin_segments(const AttnArgs& a, int unit, int* s_cum, int* s_len) {
+// Start the segment walk of this workgroup.  In balanced mode `scan` has one
+// wavefront scan the request block counts into s_cum / s_len first;
+// without it they must already be there.
+__device__ __forceinline__ SegIter begin_segments(const AttnArgs& a, int unit, int* s_cum, int* s_len,
+                                                  bool scan = true) {
     SegIter it;
     it.unit = unit;
     it.done = false;
     it.x = it.hi = it.nb_total = 0;
     if (a.balanced) {
-        scan_request_blocks(a, s_cum, s_len);
+        if (scan) scan_request_blocks(a, s_cum, s_len);
         it.nb_total = a.Hkv * s_cum[a.B];
         if (unit < a.nparts) {
             it.x = floor_div(static_cast<long>(unit) * it.nb_total, a.nparts);
@@ -294,6 +296,153 @@ __device__ __forceinline__ void load_kv_block(KVBlock<D>& blk, const uint16_t* k
     }
 }
 
+// Query fragments (B operand of S^T = K Q^T) and ancestor masks of the 16-row
+// tiles starting at row0; rows past R get zero queries and no key mask.
+template <int D, int RT>
+__device__ __forceinline__ void load_q(const AttnArgs& a, int b, int g, int row0, uint64_t node_anc,
+                                       bf16x8 (&qf)[RT][D / 32], uint64_t (&anc)[RT]) {
+    const int lane = threadIdx.x & 63, n16 = lane & 15, q4 = lane >> 4;
+    const uint16_t* qb = static_cast<const uint16_t*>(a.q);
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        const int r = row0 + t * 16 + n16;
+        const bool valid = r < a.R;
+        const int node = valid ? r / a.G : 0;
+        const uint64_t m = shfl_u64(node_anc, node);
+        anc[t] = valid ? m : ~0ull;
+        const int hq = g * a.G + (valid ? r % a.G : 0);
+        const uint16_t* qrow = qb + ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D;
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) {
+            u32x4 u = {0u, 0u, 0u, 0u};
+            if (valid) u = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * q4);
+            qf[t][c] = __builtin_bit_cast(bf16x8, u);
+        }
+    }
+}
+
+// One 32-key block for RT row tiles: S^T = K Q^T (kread(h, c) gives the K
+// fragment of half h, k-step c), the key mask, the online softmax, and
+// O^T += V^T P^T from the transposed V in vt.
+template <int D, int RT, class KRead>
+__device__ __forceinline__ void block_update(const KRead& kread, const unsigned char* vt, const bf16x8 (&qf)[RT][D / 32],
+                                             const uint64_t (&anc)[RT], int kb, int L, int Tk, float scale_log2,
+                                             float (&m_run)[RT], float (&l_run)[RT], f32x4 (&o)[RT][D / 16]) {
+    constexpr int NC32 = D / 32, NC16 = D / 16;
+    const int lane = threadIdx.x & 63, n16 = lane & 15, q4 = lane >> 4;
+    // Blocks wholly inside the prefix need no key mask.
+    const bool interior = kb + 32 <= L;
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        f32x4 st[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NC32; ++c)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kread(h, c)), qf[t][c], acc, 0, 0,
+                                                              0);
+            st[h] = acc;
+        }
+        // This lane's keys are kb + 8*q4 + e, e = 0..7 (e = 4h + ii).  Bit e
+        // of the mask: key below the slab end and either a prefix key or a
+        // tree key on the row's root path.
+        uint32_t kmask = 0xFFu;
+        if (!interior) {
+            const int base = kb + 8 * q4;
+            const int nend = min(max(Tk - base, 0), 8);
+            const int npre = min(max(L - base, 0), 8);
+            const int sh = base - L;  // tree offset of key e is sh + e
+            const uint32_t tree = sh >= 0 ? static_cast<uint32_t>(anc[t] >> min(sh, 63))
+                                          : static_cast<uint32_t>(anc[t] << min(-sh, 63));
+            const uint32_t pre = (1u << npre) - 1u;
+            kmask = ((tree & 0xFFu) | pre) & ((1u << nend) - 1u);
+        }
+        float s[8];
+        float bm = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int e = 4 * h + ii;
+                const float x = ((kmask >> e) & 1u) ? st[h][ii] * scale_log2 : -INFINITY;
+                s[e] = x;
+                bm = fmaxf(bm, x);
+            }
+        bm = max_across_rows(bm);
+        // Lazy rescale: keep the running max unless a row's block max exceeds
+        // it by more than 8 (probabilities stay <= 2^8, exact in fp32 and as
+        // precise in bf16); the decision is wave-uniform.
+        if (__builtin_amdgcn_ballot_w64(bm > m_run[t] + 8.f) != 0ull) {
+            const float mn = fmaxf(m_run[t], bm);
+            const float alpha = m_run[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[t] - mn);
+            l_run[t] *= alpha;
+#pragma unroll
+            for (int c = 0; c < NC16; ++c) o[t][c] *= alpha;  // o holds row n16 of this lane
+            m_run[t] = mn;
+        }
+        const float mu = m_run[t] == -INFINITY ? 0.f : m_run[t];
+        float rs = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            s[e] = __builtin_amdgcn_exp2f(s[e] - mu);
+            rs += s[e];
+        }
+        l_run[t] += sum_across_rows(rs);
+        u32x4 pp;
+        pp[0] = pack_bf16x2(s[0], s[1]);
+        pp[1] = pack_bf16x2(s[2], s[3]);
+        pp[2] = pack_bf16x2(s[4], s[5]);
+        pp[3] = pack_bf16x2(s[6], s[7]);
+        const bf16x8 pa = __builtin_bit_cast(bf16x8, pp);
+#pragma unroll
+        for (int c = 0; c < NC16; ++c) {
+            // O^T = V^T P^T: A = V^T (lane: keys 8q..8q+7 of dim 16c + n,
+            // straight from LDS), B = P^T; the result lands as
+            // O[row n][dims 16c + 4q .. 16c + 4q + 3] in this lane.
+            const int d = 16 * c + n16;
+            const u32x4 vf = *reinterpret_cast<const u32x4*>(vt + d * 64 + ((q4 ^ vt_swz(d)) * 16));
+            o[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf), pa, o[t][c], 0, 0, 0);
+        }
+        // Re-read the K fragments for the next tile rather than keep them
+        // live (registers are what bound the waves per SIMD here).
+        asm volatile("" ::: "memory");
+    }
+}
+
+// A segment's result for the 16-row tiles starting at row0, straight from
+// registers: lane (n, q) holds row n of each tile (dims 16c + 4q .. +3 of O
+// and the row's running max and sum).  The normalised output when the
+// segment covers its slab, else the partial.
+template <int D, int RT>
+__device__ __forceinline__ void write_rows(const AttnArgs& a, const Seg& cur, int row0, const float (&m_run)[RT],
+                                           const float (&l_run)[RT], const f32x4 (&o)[RT][D / 16]) {
+    const int lane = threadIdx.x & 63, n16 = lane & 15, q4 = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        const int r = row0 + t * 16 + n16;
+        if (r >= a.R) continue;
+        if (cur.direct) {
+            const int node = r / a.G, hq = cur.g * a.G + r % a.G;
+            const float inv = l_run[t] > 0.f ? 1.f / l_run[t] : 0.f;
+            uint16_t* orow =
+                static_cast<uint16_t*>(a.out) + ((static_cast<size_t>(cur.b) * a.N + node) * a.Hq + hq) * D;
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) {
+                uint2 pk;
+                pk.x = pack_bf16x2(o[t][c][0] * inv, o[t][c][1] * inv);
+                pk.y = pack_bf16x2(o[t][c][2] * inv, o[t][c][3] * inv);
+                *reinterpret_cast<uint2*>(orow + 16 * c + 4 * q4) = pk;
+            }
+        } else {
+            float* prow = a.ws_o + (static_cast<size_t>(cur.part) * a.R + r) * D;
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) *reinterpret_cast<f32x4*>(prow + 16 * c + 4 * q4) = o[t][c];
+            if (q4 == 0) a.ws_ml[static_cast<size_t>(cur.part) * a.R + r] = make_float2(m_run[t], l_run[t]);
+        }
+    }
+}
+
 template <int D, int RT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(RT <= 2 ? 2 : 1))) void attn_mfma(AttnArgs a) {
     constexpr int NC32 = D / 32;  // k-steps of the QK product
@@ -313,7 +462,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(RT <= 2 ? 2 
     const int vch = lane % CPR, vkg = lane / CPR;
     unsigned char* ks = s_stage;
     unsigned char* vt = s_stage + KS_BYTES;
-    const uint16_t* qb = static_cast<const uint16_t*>(a.q);
     const uint16_t* kc = static_cast<const uint16_t*>(a.k);
     const uint16_t* vc = static_cast<const uint16_t*>(a.v);
 
@@ -326,6 +474,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(RT <= 2 ? 2 
         const size_t head = (static_cast<size_t>(cur.b) * a.Hkv + cur.g) * a.cap * D;
         load_kv_block<D>(R, kc + head, vc + head, cur.blk0 * 32, L + a.N - 1, n16, q4, vch, vkg);
     }
+    auto kread = [&](int h, int c) { return *reinterpret_cast<const u32x4*>(ks + ((h * NC32 + c) * 64 + lane) * 16); };
     for (;;) {
         const int b = cur.b, g = cur.g;
         const int Tk = L + a.N;
@@ -338,27 +487,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(RT <= 2 ? 2 
         const int Ln = more ? nxt.L : 0;
         const size_t nhead = more ? (static_cast<size_t>(nxt.b) * a.Hkv + nxt.g) * a.cap * D : head;
 
-        // Queries and ancestor masks of this workgroup's rows.
-        const uint64_t node_anc = anc_mask(a, b);
         bf16x8 qf[RT][NC32];
         uint64_t anc[RT];
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-            const int r = (rg * RT + t) * 16 + n16;
-            const bool valid = r < a.R;
-            const int node = valid ? r / a.G : 0;
-            const uint64_t m = shfl_u64(node_anc, node);
-            anc[t] = valid ? m : ~0ull;
-            const int hq = g * a.G + (valid ? r % a.G : 0);
-            const uint16_t* qrow = qb + ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D;
-#pragma unroll
-            for (int c = 0; c < NC32; ++c) {
-                u32x4 u = {0u, 0u, 0u, 0u};
-                if (valid) u = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * q4);
-                qf[t][c] = __builtin_bit_cast(bf16x8, u);
-            }
-        }
-
+        load_q<D, RT>(a, b, g, rg * RT * 16, anc_mask(a, b), qf, anc);
         float m_run[RT], l_run[RT];
         f32x4 o[RT][NC16];
 #pragma unroll
@@ -417,118 +548,183 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(RT <= 2 ? 2 
                 load_kv_block<D>(R, nk, nv, nkb, nmax, n16, q4, vch, vkg);
             }
             wave_lds_sync();
-
-            // Blocks wholly inside the prefix need no key mask.
-            const bool interior = kb + 32 <= L;
-#pragma unroll
-            for (int t = 0; t < RT; ++t) {
-                f32x4 st[2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int c = 0; c < NC32; ++c) {
-                        const u32x4 kf = *reinterpret_cast<const u32x4*>(ks + ((h * NC32 + c) * 64 + lane) * 16);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf), qf[t][c], acc,
-                                                                      0, 0, 0);
-                    }
-                    st[h] = acc;
-                }
-                // This lane's keys are kb + 8*q4 + e, e = 0..7 (e = 4h + ii).
-                // Bit e of the mask: key below the slab end and either a
-                // prefix key or a tree key on the row's root path.
-                uint32_t kmask = 0xFFu;
-                if (!interior) {
-                    const int base = kb + 8 * q4;
-                    const int nend = min(max(Tk - base, 0), 8);
-                    const int npre = min(max(L - base, 0), 8);
-                    const int sh = base - L;  // tree offset of key e is sh + e
-                    const uint32_t tree = sh >= 0 ? static_cast<uint32_t>(anc[t] >> min(sh, 63))
-                                                  : static_cast<uint32_t>(anc[t] << min(-sh, 63));
-                    const uint32_t pre = (1u << npre) - 1u;
-                    kmask = ((tree & 0xFFu) | pre) & ((1u << nend) - 1u);
-                }
-                float s[8];
-                float bm = -INFINITY;
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) {
-                        const int e = 4 * h + ii;
-                        const float x = ((kmask >> e) & 1u) ? st[h][ii] * a.scale_log2 : -INFINITY;
-                        s[e] = x;
-                        bm = fmaxf(bm, x);
-                    }
-                bm = max_across_rows(bm);
-                // Lazy rescale: keep the running max unless a row's block max
-                // exceeds it by more than 8 (probabilities stay <= 2^8, exact
-                // in fp32 and as precise in bf16); the decision is
-                // wave-uniform.
-                if (__builtin_amdgcn_ballot_w64(bm > m_run[t] + 8.f) != 0ull) {
-                    const float mn = fmaxf(m_run[t], bm);
-                    const float alpha = m_run[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[t] - mn);
-                    l_run[t] *= alpha;
-#pragma unroll
-                    for (int c = 0; c < NC16; ++c) o[t][c] *= alpha;  // o holds row n16 of this lane
-                    m_run[t] = mn;
-                }
-                const float mu = m_run[t] == -INFINITY ? 0.f : m_run[t];
-                float rs = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    s[e] = __builtin_amdgcn_exp2f(s[e] - mu);
-                    rs += s[e];
-                }
-                l_run[t] += sum_across_rows(rs);
-                u32x4 pp;
-                pp[0] = pack_bf16x2(s[0], s[1]);
-                pp[1] = pack_bf16x2(s[2], s[3]);
-                pp[2] = pack_bf16x2(s[4], s[5]);
-                pp[3] = pack_bf16x2(s[6], s[7]);
-                const bf16x8 pa = __builtin_bit_cast(bf16x8, pp);
-#pragma unroll
-                for (int c = 0; c < NC16; ++c) {
-                    // O^T = V^T P^T: A = V^T (lane: keys 8q..8q+7 of dim
-                    // 16c + n, straight from LDS), B = P^T; the result lands
-                    // as O[row n][dims 16c + 4q .. 16c + 4q + 3] in this lane.
-                    const int d = 16 * c + n16;
-                    const u32x4 vf = *reinterpret_cast<const u32x4*>(vt + d * 64 + ((q4 ^ vt_swz(d)) * 16));
-                    o[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf), pa, o[t][c], 0,
-                                                                      0, 0);
-                }
-            }
+            block_update<D, RT>(kread, vt, qf, anc, kb, L, Tk, a.scale_log2, m_run, l_run, o);
             wave_lds_sync();
         }
 
-        // ---- this segment's result, straight from registers ---------------
-        // Lane (n, q) holds row n of each tile: dims 16c + 4q .. +3 of O and
-        // the row's running (max, sum).
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-            const int r = (rg * RT + t) * 16 + n16;
-            if (r >= a.R) continue;
-            if (cur.direct) {
-                const int node = r / a.G, hq = g * a.G + r % a.G;
-                const float inv = l_run[t] > 0.f ? 1.f / l_run[t] : 0.f;
-                uint16_t* orow = static_cast<uint16_t*>(a.out) + ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D;
-#pragma unroll
-                for (int c = 0; c < NC16; ++c) {
-                    uint2 pk;
-                    pk.x = pack_bf16x2(o[t][c][0] * inv, o[t][c][1] * inv);
-                    pk.y = pack_bf16x2(o[t][c][2] * inv, o[t][c][3] * inv);
-                    *reinterpret_cast<uint2*>(orow + 16 * c + 4 * q4) = pk;
-                }
-            } else {
-                float* prow = a.ws_o + (static_cast<size_t>(cur.part) * a.R + r) * D;
-#pragma unroll
-                for (int c = 0; c < NC16; ++c) *reinterpret_cast<f32x4*>(prow + 16 * c + 4 * q4) = o[t][c];
-                if (q4 == 0) a.ws_ml[static_cast<size_t>(cur.part) * a.R + r] = make_float2(m_run[t], l_run[t]);
-            }
-        }
+        write_rows<D, RT>(a, cur, rg * RT * 16, m_run, l_run, o);
         if (cur.table && rg == 0 && lane == 0 && a.seg) a.seg[b * a.Hkv + g] = make_int2(cur.first, cur.count);
         if (!more) break;
         cur = nxt;
         L = Ln;
+    }
+}
+
+// ----------------------------------------------------------------------------
+// MFMA path for many query rows (bf16): WK waves share each KV block through
+// LDS and wave w owns row tiles [w*RT, (w+1)*RT) of the workgroup's rows, so
+// a block is read once per WK*RT*16 rows and no cross-wave merge is needed.
+// The workgroup loads each 32-key block cooperatively (coalesced 16-byte
+// chunks), two blocks ahead in registers, into a double-buffered LDS stage;
+// one barrier per block.
+// ----------------------------------------------------------------------------
+// K of one block in LDS: row-major 32 keys x D, 16-byte chunks XOR-swizzled
+// so that the 16 rows one A-operand read touches (paired-half key order)
+// fall on distinct banks (D = 128; two-way for D = 64).
+__device__ __forceinline__ int k_swz(int row) { return (row & 3) | ((row >> 1) & 12); }
+
+template <int D, int WK>
+struct SharedKV {
+    static constexpr int CPR = D / 8;
+    static constexpr int NT = 64 * WK;
+    static constexpr int KPT = 32 * CPR / NT;         // K chunks per thread
+    static constexpr int VTASK = 16 * CPR;             // (key pair, chunk) tasks of V
+    static constexpr int VPT = (VTASK + NT - 1) / NT;  // V tasks per thread
+    u32x4 k[KPT];
+    u32x4 v[VPT][2];
+    int kb, Tk;  // the block's first key and its slab's key count
+};
+
+template <int D, int WK>
+__device__ __forceinline__ void load_shared_kv(SharedKV<D, WK>& s, const uint16_t* kbase, const uint16_t* vbase, int kb,
+                                               int Tk) {
+    using S = SharedKV<D, WK>;
+    const int tid = threadIdx.x;
+    s.kb = kb;
+    s.Tk = Tk;
+#pragma unroll
+    for (int j = 0; j < S::KPT; ++j) {
+        const int ci = tid + S::NT * j;
+        const int row = min(kb + ci / S::CPR, Tk - 1);
+        s.k[j] = *reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(row) * D + (ci % S::CPR) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < S::VPT; ++j) {
+        const int vt = tid + S::NT * j;
+        const int task = vt < S::VTASK ? vt : 0;  // spare lanes re-read task 0 and never stage it
+        const int kp = task / S::CPR, ch = task % S::CPR;
+        const int r0 = min(kb + 2 * kp, Tk - 1), r1 = min(kb + 2 * kp + 1, Tk - 1);
+        s.v[j][0] = *reinterpret_cast<const u32x4*>(vbase + static_cast<size_t>(r0) * D + ch * 8);
+        s.v[j][1] = *reinterpret_cast<const u32x4*>(vbase + static_cast<size_t>(r1) * D + ch * 8);
+    }
+}
+
+// K row-major (swizzled chunks), V transposed; V keys at or past the slab
+// end are zeroed so no stale value reaches P*V.
+template <int D, int WK>
+__device__ __forceinline__ void stage_shared_kv(const SharedKV<D, WK>& s, unsigned char* ks, unsigned char* vt) {
+    using S = SharedKV<D, WK>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < S::KPT; ++j) {
+        const int ci = tid + S::NT * j;
+        const int row = ci / S::CPR, col = ci % S::CPR;
+        *reinterpret_cast<u32x4*>(ks + row * (2 * D) + ((col ^ k_swz(row)) & (S::CPR - 1)) * 16) = s.k[j];
+    }
+#pragma unroll
+    for (int j = 0; j < S::VPT; ++j) {
+        const int vtask = tid + S::NT * j;
+        if (vtask >= S::VTASK) continue;
+        const int kp = vtask / S::CPR, ch = vtask % S::CPR;
+        const int key0 = 2 * kp;
+        const u32x4 v0 = s.kb + key0 < s.Tk ? s.v[j][0] : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 v1 = s.kb + key0 + 1 < s.Tk ? s.v[j][1] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int d = 8 * ch + t;
+            const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+            const uint32_t w = __builtin_amdgcn_perm(v1[t >> 1], v0[t >> 1], sel);
+            *reinterpret_cast<uint32_t*>(vt + d * 64 + (((key0 >> 3) ^ vt_swz(d)) * 16) + (key0 & 7) * 2) = w;
+        }
+    }
+}
+
+template <int D, int RT, int WK>
+__global__ __launch_bounds__(64 * WK) __attribute__((amdgpu_waves_per_eu(2))) void attn_mfma_wg(AttnArgs a) {
+    constexpr int NC32 = D / 32, NC16 = D / 16, CPR = D / 8;
+    constexpr int KS_BYTES = 32 * D * 2;  // K of one block, row-major
+    constexpr int VT_BYTES = D * 64;      // V^T of one block
+    constexpr int STAGE = KS_BYTES + VT_BYTES;
+    __shared__ __attribute__((aligned(16))) unsigned char s_stage[2 * STAGE];
+    __shared__ int s_cum[kMaxBalancedBatch + 1];
+    __shared__ int s_len[kMaxBalancedBatch];
+
+    int unit, rg;
+    decode_unit(a, unit, rg);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n16 = lane & 15, q4 = lane >> 4;
+    const uint16_t* kc = static_cast<const uint16_t*>(a.k);
+    const uint16_t* vc = static_cast<const uint16_t*>(a.v);
+    const int row0 = (rg * WK + wave) * RT * 16;
+
+    if (wave == 0) (void)begin_segments(a, unit, s_cum, s_len, true);
+    __syncthreads();
+    // Two cursors over the same segment walk: one computes, one loads two
+    // blocks ahead (through segment ends too).
+    SegIter it = begin_segments(a, unit, s_cum, s_len, false);
+    SegIter lit = it;
+    Seg cur, lseg;
+    if (!next_segment(a, it, s_cum, s_len, cur)) return;
+    (void)next_segment(a, lit, s_cum, s_len, lseg);
+    int lb = lseg.blk0;
+    bool lmore = true;
+    auto load_next = [&](SharedKV<D, WK>& S) {
+        const size_t head = (static_cast<size_t>(lseg.b) * a.Hkv + lseg.g) * a.cap * D;
+        load_shared_kv<D, WK>(S, kc + head, vc + head, lb * 32, lseg.L + a.N);
+        if (lb + 1 < lseg.blk1) {
+            ++lb;
+        } else if (lmore) {
+            Seg t;
+            lmore = next_segment(a, lit, s_cum, s_len, t);
+            if (lmore) {
+                lseg = t;
+                lb = t.blk0;
+            }
+        }
+    };
+    SharedKV<D, WK> R0, R1;
+    load_next(R0);
+    load_next(R1);
+    int bi = 0;
+    stage_shared_kv<D, WK>(R0, s_stage, s_stage + KS_BYTES);
+    R0 = R1;
+    load_next(R1);
+    __syncthreads();
+
+    for (;;) {
+        const int b = cur.b, g = cur.g;
+        const int L = cur.L, Tk = L + a.N;
+        bf16x8 qf[RT][NC32];
+        uint64_t anc[RT];
+        load_q<D, RT>(a, b, g, row0, anc_mask(a, b), qf, anc);
+        float m_run[RT], l_run[RT];
+        f32x4 o[RT][NC16];
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            m_run[t] = -INFINITY;
+            l_run[t] = 0.f;
+#pragma unroll
+            for (int c = 0; c < NC16; ++c) o[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        for (int xb = cur.blk0; xb < cur.blk1; ++xb) {
+            const unsigned char* ks = s_stage + bi * STAGE;
+            const unsigned char* vt = ks + KS_BYTES;
+            auto kread = [&](int h, int c) {
+                const int row = 8 * (n16 >> 2) + 4 * h + (n16 & 3);
+                return *reinterpret_cast<const u32x4*>(ks + row * (2 * D) + (((4 * c + q4) ^ k_swz(row)) & (CPR - 1)) * 16);
+            };
+            block_update<D, RT>(kread, vt, qf, anc, xb * 32, L, Tk, a.scale_log2, m_run, l_run, o);
+            // The next block into the other buffer (its previous block was
+            // finished by every wave before the last barrier), then refill.
+            stage_shared_kv<D, WK>(R0, s_stage + (bi ^ 1) * STAGE, s_stage + (bi ^ 1) * STAGE + KS_BYTES);
+            R0 = R1;
+            load_next(R1);
+            __syncthreads();
+            bi ^= 1;
+        }
+        write_rows<D, RT>(a, cur, row0, m_run, l_run, o);
+        if (cur.table && rg == 0 && tid == 0 && a.seg) a.seg[b * a.Hkv + g] = make_int2(cur.first, cur.count);
+        if (!next_segment(a, it, s_cum, s_len, cur)) break;
     }
 }
 
@@ -750,14 +946,15 @@ AttnPlan plan_attn(const spec_attn_desc& d, int max_prefix_len) {
     long min_blocks = 2;  // balanced mode: least blocks per range
     if (d.dtype == SPEC_BF16) {
         p.mfma = true;
-        if (p.rows <= 64) {
+        if (p.rows <= 64) {  // one wave holds every row
             p.row_tiles = (p.rows + 15) / 16;
             p.row_groups = 1;
-        } else {
-            p.row_tiles = 4;
-            p.row_groups = (p.rows + 63) / 64;
+            p.waves = 1;
+        } else {  // four waves of 32 rows share each KV block
+            p.row_tiles = 2;
+            p.waves = 4;
+            p.row_groups = (p.rows + 127) / 128;
         }
-        p.waves = 1;
     } else {
         p.mfma = false;
         p.row_tiles = 0;
@@ -831,7 +1028,15 @@ static int mfma_resident() {
 }
 
 template <int D>
-static int mfma_resident_rt(int rt) {
+static int mfma_wg_resident() {
+    static int n = 0;
+    if (n == 0) n = resident_per_cu(attn_mfma_wg<D, 2, 4>, 256);
+    return n;
+}
+
+template <int D>
+static int mfma_resident_rt(int rt, int waves) {
+    if (waves > 1) return mfma_wg_resident<D>();
     switch (rt) {
         case 1: return mfma_resident<D, 1>();
         case 2: return mfma_resident<D, 2>();
@@ -842,6 +1047,10 @@ static int mfma_resident_rt(int rt) {
 
 template <int D>
 static void launch_mfma_rt(const AttnPlan& p, const AttnArgs& a, dim3 grid, hipStream_t st) {
+    if (p.waves > 1) {
+        hipLaunchKernelGGL((attn_mfma_wg<D, 2, 4>), grid, dim3(256), 0, st, a);
+        return;
+    }
     switch (p.row_tiles) {
         case 1: hipLaunchKernelGGL((attn_mfma<D, 1>), grid, dim3(64), 0, st, a); break;
         case 2: hipLaunchKernelGGL((attn_mfma<D, 2>), grid, dim3(64), 0, st, a); break;
@@ -877,7 +1086,8 @@ int launch_verify_attn(const spec_attn_desc& d, const AttnPlan& p, const void* q
     long units;
     bool combine;
     if (p.balanced) {
-        const int per_cu = d.head_dim == 128 ? mfma_resident_rt<128>(p.row_tiles) : mfma_resident_rt<64>(p.row_tiles);
+        const int per_cu = d.head_dim == 128 ? mfma_resident_rt<128>(p.row_tiles, p.waves)
+                                             : mfma_resident_rt<64>(p.row_tiles, p.waves);
         long P = static_cast<long>(per_cu) * device_cus() / p.row_groups;
         if (P > p.parts_max) P = p.parts_max;
         if (P >= 8) P = P / 8 * 8;
