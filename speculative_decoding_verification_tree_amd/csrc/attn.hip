@@ -324,7 +324,7 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int b, int g, int row0
 // One 32-key block for RT row tiles: S^T = K Q^T (kread(h, c) gives the K
 // fragment of half h, k-step c), the key mask, the online softmax, and
 // O^T += V^T P^T from the transposed V in vt.
-template <int D, int RT, class KRead>
+template <int D, int RT, bool PHASED, class KRead>
 __device__ __forceinline__ void block_update(const KRead& kread, const unsigned char* vt, const bf16x8 (&qf)[RT][D / 32],
                                              const uint64_t (&anc)[RT], int kb, int L, int Tk, float scale_log2,
                                              float (&m_run)[RT], float (&l_run)[RT], f32x4 (&o)[RT][D / 16]) {
@@ -332,18 +332,37 @@ __device__ __forceinline__ void block_update(const KRead& kread, const unsigned 
     const int lane = threadIdx.x & 63, n16 = lane & 15, q4 = lane >> 4;
     // Blocks wholly inside the prefix need no key mask.
     const bool interior = kb + 32 <= L;
+    // PHASED: the scores of every tile first, each K fragment read once
+    // and feeding 2*RT independent accumulator chains (more registers);
+    // otherwise tile by tile, re-reading the K fragments.
+    f32x4 sc[PHASED ? RT : 1][2];
+    if constexpr (PHASED) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t) sc[t][0] = sc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC32; ++c)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bf16x8 kf = __builtin_bit_cast(bf16x8, kread(h, c));
+#pragma unroll
+                for (int t = 0; t < RT; ++t)
+                    sc[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[t][c], sc[t][h], 0, 0, 0);
+            }
+    }
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-        f32x4 st[2];
+        if constexpr (!PHASED) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int h = 0; h < 2; ++h) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int c = 0; c < NC32; ++c)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kread(h, c)), qf[t][c], acc, 0, 0,
-                                                              0);
-            st[h] = acc;
+                for (int c = 0; c < NC32; ++c)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kread(h, c)), qf[t][c], acc,
+                                                                  0, 0, 0);
+                sc[0][h] = acc;
+            }
         }
+        const f32x4* st = sc[PHASED ? t : 0];
         // This lane's keys are kb + 8*q4 + e, e = 0..7 (e = 4h + ii).  Bit e
         // of the mask: key below the slab end and either a prefix key or a
         // tree key on the row's root path.
@@ -358,6 +377,8 @@ __device__ __forceinline__ void block_update(const KRead& kread, const unsigned 
             const uint32_t pre = (1u << npre) - 1u;
             kmask = ((tree & 0xFFu) | pre) & ((1u << nend) - 1u);
         }
+        // Raw scores (masked to -inf); the max is scaled once, and each
+        // probability is exp2(score * scale - max) with one fma.
         float s[8];
         float bm = -INFINITY;
 #pragma unroll
@@ -365,11 +386,11 @@ __device__ __forceinline__ void block_update(const KRead& kread, const unsigned 
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int e = 4 * h + ii;
-                const float x = ((kmask >> e) & 1u) ? st[h][ii] * scale_log2 : -INFINITY;
+                const float x = ((kmask >> e) & 1u) ? st[h][ii] : -INFINITY;
                 s[e] = x;
                 bm = fmaxf(bm, x);
             }
-        bm = max_across_rows(bm);
+        bm = max_across_rows(bm) * scale_log2;
         // Lazy rescale: keep the running max unless a row's block max exceeds
         // it by more than 8 (probabilities stay <= 2^8, exact in fp32 and as
         // precise in bf16); the decision is wave-uniform.
@@ -385,7 +406,7 @@ __device__ __forceinline__ void block_update(const KRead& kread, const unsigned 
         float rs = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            s[e] = __builtin_amdgcn_exp2f(s[e] - mu);
+            s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, -mu));
             rs += s[e];
         }
         l_run[t] += sum_across_rows(rs);
@@ -404,9 +425,9 @@ __device__ __forceinline__ void block_update(const KRead& kread, const unsigned 
             const u32x4 vf = *reinterpret_cast<const u32x4*>(vt + d * 64 + ((q4 ^ vt_swz(d)) * 16));
             o[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf), pa, o[t][c], 0, 0, 0);
         }
-        // Re-read the K fragments for the next tile rather than keep them
-        // live (registers are what bound the waves per SIMD here).
-        asm volatile("" ::: "memory");
+        // Tile by tile: re-read the K fragments for the next tile rather than
+        // keep them live (registers bound the waves per SIMD).
+        if constexpr (!PHASED) asm volatile("" ::: "memory");
     }
 }
 
@@ -548,7 +569,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(RT <= 2 ? 2 
                 load_kv_block<D>(R, nk, nv, nkb, nmax, n16, q4, vch, vkg);
             }
             wave_lds_sync();
-            block_update<D, RT>(kread, vt, qf, anc, kb, L, Tk, a.scale_log2, m_run, l_run, o);
+            block_update<D, RT, false>(kread, vt, qf, anc, kb, L, Tk, a.scale_log2, m_run, l_run, o);
             wave_lds_sync();
         }
 
@@ -682,13 +703,14 @@ __global__ __launch_bounds__(64 * WK) __attribute__((amdgpu_waves_per_eu(2))) vo
             }
         }
     };
+    // Two register sets take turns: at block i the set holding block i+1 is
+    // staged and then refilled with block i+3.
     SharedKV<D, WK> R0, R1;
     load_next(R0);
     load_next(R1);
-    int bi = 0;
+    int bi = 0, sel = 1;
     stage_shared_kv<D, WK>(R0, s_stage, s_stage + KS_BYTES);
-    R0 = R1;
-    load_next(R1);
+    load_next(R0);
     __syncthreads();
 
     for (;;) {
@@ -713,14 +735,20 @@ __global__ __launch_bounds__(64 * WK) __attribute__((amdgpu_waves_per_eu(2))) vo
                 const int row = 8 * (n16 >> 2) + 4 * h + (n16 & 3);
                 return *reinterpret_cast<const u32x4*>(ks + row * (2 * D) + (((4 * c + q4) ^ k_swz(row)) & (CPR - 1)) * 16);
             };
-            block_update<D, RT>(kread, vt, qf, anc, xb * 32, L, Tk, a.scale_log2, m_run, l_run, o);
+            block_update<D, RT, true>(kread, vt, qf, anc, xb * 32, L, Tk, a.scale_log2, m_run, l_run, o);
             // The next block into the other buffer (its previous block was
             // finished by every wave before the last barrier), then refill.
-            stage_shared_kv<D, WK>(R0, s_stage + (bi ^ 1) * STAGE, s_stage + (bi ^ 1) * STAGE + KS_BYTES);
-            R0 = R1;
-            load_next(R1);
+            unsigned char* nks = s_stage + (bi ^ 1) * STAGE;
+            if (sel) {
+                stage_shared_kv<D, WK>(R1, nks, nks + KS_BYTES);
+                load_next(R1);
+            } else {
+                stage_shared_kv<D, WK>(R0, nks, nks + KS_BYTES);
+                load_next(R0);
+            }
             __syncthreads();
             bi ^= 1;
+            sel ^= 1;
         }
         write_rows<D, RT>(a, cur, row0, m_run, l_run, o);
         if (cur.table && rg == 0 && tid == 0 && a.seg) a.seg[b * a.Hkv + g] = make_int2(cur.first, cur.count);
