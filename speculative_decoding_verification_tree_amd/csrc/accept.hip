@@ -381,16 +381,22 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
         // Root paths by pointer doubling: after round k a lane holds its
         // first 2^k path nodes and its 2^k-th ancestor.
         const int me = lane < N ? lane : 0;
-        int up = lane < N ? pi : -1;
-        uint64_t anc = 1ull << me;
+        uint64_t anc;
+        if (!a.parent) {  // chain: nodes 0..me
+            anc = me == 63 ? ~0ull : (2ull << me) - 1ull;
+        } else {
+            int up = lane < N ? pi : -1;
+            anc = 1ull << me;
 #pragma unroll
-        for (int r = 0; r < 6; ++r) {
-            const int src = up >= 0 ? up : 0;
-            const uint32_t lo = __shfl(static_cast<uint32_t>(anc), src), hi = __shfl(static_cast<uint32_t>(anc >> 32), src);
-            const int upup = __shfl(up, src);
-            if (up >= 0) {
-                anc |= static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
-                up = upup;
+            for (int r = 0; r < 6; ++r) {
+                const int src = up >= 0 ? up : 0;
+                const uint32_t lo = __shfl(static_cast<uint32_t>(anc), src),
+                               hi = __shfl(static_cast<uint32_t>(anc >> 32), src);
+                const int upup = __shfl(up, src);
+                if (up >= 0) {
+                    anc |= static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
+                    up = upup;
+                }
             }
         }
         // Accepted: every node on the root path passed.  The stop node is the
@@ -484,14 +490,26 @@ __global__ __launch_bounds__(kThreads) void accept_sample(AcceptArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Inclusive prefix sum over the lanes of a wavefront.
+// 64-bit DPP move of a double (both halves with the same control); lanes
+// without a source read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_d(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(u), CTRL, ROW_MASK, 0xF, true);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(u >> 32), CTRL, ROW_MASK, 0xF, true);
+    return __builtin_bit_cast(double, static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32));
+}
+
+// Inclusive prefix sum over the lanes of a wavefront: shifts by 1, 2, 4, 8
+// inside each 16-lane row, then the last lane of row 0 (row 2) is added to
+// row 1 (row 3), and lane 31 to rows 2 and 3.
 __device__ __forceinline__ double wave_incl_scan(double v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const double t = __shfl_up(v, o);
-        if (lane >= o) v += t;
-    }
+    v += dpp_d<0x111, 0xF>(v);  // row_shr:1
+    v += dpp_d<0x112, 0xF>(v);  // row_shr:2
+    v += dpp_d<0x114, 0xF>(v);  // row_shr:4
+    v += dpp_d<0x118, 0xF>(v);  // row_shr:8
+    v += dpp_d<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_d<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
     return v;
 }
 
