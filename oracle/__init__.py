@@ -45,6 +45,10 @@ def _load():
         lib.oracle_accept.restype = I
         lib.oracle_commit.argtypes = [I, I, I, I, I, P, P, P, P, P]
         lib.oracle_commit.restype = I
+        lib.oracle_medusa_tree.argtypes = [I, I, P, I, I, P, P, P, P]
+        lib.oracle_medusa_tree.restype = I
+        lib.oracle_tree_rope.argtypes = [I, I, I, I, I, I, I, P, P, P, P, D, P, P]
+        lib.oracle_tree_rope.restype = I
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = I
         _lib = lib
@@ -135,6 +139,51 @@ def commit(k_cache, v_cache, prefix_len, path, accept_len):
     if rc != 0:
         raise ValueError("oracle_commit rejected its arguments")
     return pl
+
+
+def medusa_tree(widths, root_tokens, head_tokens, max_nodes=64):
+    """Cartesian-product candidate tree of the Medusa heads.
+
+    widths: s_1..s_K; root_tokens [B]; head_tokens [B][K][max_width].
+    Returns (parent [B][N], tokens [B][N]) int32.
+    """
+    w = _c(widths, np.int32)
+    root = _c(root_tokens, np.int32)
+    head = _c(head_tokens, np.int32)
+    B, K, W = head.shape
+    n = 1
+    level = 1
+    for s in w:
+        level *= int(s)
+        n += level
+    parent = np.empty((B, max(n, 1)), np.int32)
+    tokens = np.empty((B, max(n, 1)), np.int32)
+    N = _load().oracle_medusa_tree(B, K, _ptr(w), W, int(max_nodes), _ptr(root), _ptr(head), _ptr(parent),
+                                   _ptr(tokens))
+    if N < 0:
+        raise ValueError("oracle_medusa_tree rejected its arguments")
+    return parent, tokens
+
+
+def tree_rope(q, k_cache, prefix_len, parent, dtype, base):
+    """Depth-position rotary embedding of q and the tree's K rows (fp64, unrounded).
+
+    Returns (q_out [B][N][Hq][D], k_out [B][Hkv][N][D]) float64.
+    """
+    B, N, Hq, D = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    dt = 1 if dtype == "bf16" else 0
+    q_ = np.ascontiguousarray(q)
+    k_ = np.ascontiguousarray(k_cache)
+    pl = _c(prefix_len, np.int32)
+    par = _c(parent, np.int32)
+    q_out = np.empty((B, N, Hq, D), np.float64)
+    k_out = np.empty((B, Hkv, N, D), np.float64)
+    rc = _load().oracle_tree_rope(B, N, Hq, Hkv, D, cap, dt, _ptr(q_), _ptr(k_), _ptr(pl), _ptr(par), float(base),
+                                  _ptr(q_out), _ptr(k_out))
+    if rc != 0:
+        raise ValueError("oracle_tree_rope rejected its arguments")
+    return q_out, k_out
 
 
 def num_threads():

@@ -364,6 +364,101 @@ int oracle_commit(int B, int N, int Hkv, int cap, int row_bytes, uint8_t* k, uin
     return 0;
 }
 
+/* ---------------------------------------------------------------------------
+ * Medusa candidate tree (MEDUSA section, candidate construction and tree
+ * attention paragraphs): head k (k = 1..K) proposes its top-s_k tokens;
+ * the candidates are the Cartesian product of the heads' proposals, arranged
+ * as a tree.  Node 0 is the root (root_tokens[b]).  Reading: the tree is
+ * built level by level (breadth first); the children of a depth-(d-1) node
+ * are its extensions by head d's candidates in rank order, and the parents
+ * of one level are visited in the order the previous level was built.  So
+ * node (i_1, ..., i_d) has parent (i_1, ..., i_{d-1}) and token
+ * head_tokens[b][d-1][i_d].  head_tokens is [B][K][max_width].
+ * Returns the node count N (1 + sum over d of prod_{k<=d} s_k), or -1 if a
+ * width is outside [1, max_width] or N exceeds max_nodes; parent and tokens
+ * are [B][N].
+ * ------------------------------------------------------------------------- */
+int oracle_medusa_tree(int B, int K, const int32_t* widths, int max_width, int max_nodes,
+                       const int32_t* root_tokens, const int32_t* head_tokens, int32_t* parent,
+                       int32_t* tokens) {
+    long n = 1, level = 1;
+    for (int k = 0; k < K; ++k) {
+        if (widths[k] < 1 || widths[k] > max_width) return -1;
+        level *= widths[k];
+        n += level;
+        if (n > max_nodes) return -1;
+    }
+    const int N = (int)n;
+    int* frontier = (int*)malloc(sizeof(int) * (size_t)N);
+    int* next = (int*)malloc(sizeof(int) * (size_t)N);
+    for (int b = 0; b < B; ++b) {
+        int32_t* par = parent + (size_t)b * N;
+        int32_t* tok = tokens + (size_t)b * N;
+        par[0] = -1;
+        tok[0] = root_tokens[b];
+        int nf = 1, built = 1;
+        frontier[0] = 0;
+        for (int k = 0; k < K; ++k) {
+            int nn = 0;
+            for (int f = 0; f < nf; ++f)
+                for (int c = 0; c < widths[k]; ++c) {
+                    par[built] = frontier[f];
+                    tok[built] = head_tokens[((size_t)b * K + k) * max_width + c];
+                    next[nn++] = built++;
+                }
+            memcpy(frontier, next, sizeof(int) * (size_t)nn);
+            nf = nn;
+        }
+    }
+    free(frontier);
+    free(next);
+    return N;
+}
+
+/* ---------------------------------------------------------------------------
+ * Depth-position rotary embedding of the tree (MEDUSA tree-attention
+ * paragraph: position indices follow tree depth).  Node i of request b sits
+ * at position pos = L_b + depth(i).  Reading: the rotary embedding of the
+ * Llama family, in its rotate-half layout: for j < D/2 the pair
+ * (x_j, x_{j+D/2}) is turned by the angle pos * base^(-2j/D):
+ *   x_j'       = x_j cos - x_{j+D/2} sin
+ *   x_{j+D/2}' = x_j sin + x_{j+D/2} cos.
+ * Applied to q[b][i][h] (every q head) and to the tree's K rows
+ * k_cache[b][g][L_b + i] (every kv head).  Outputs are fp64, unrounded:
+ * q_out [B][N][Hq][D], k_out [B][Hkv][N][D].
+ * ------------------------------------------------------------------------- */
+static void rope_row(const void* src, int dtype, size_t off, int D, double pos, double base, double* out) {
+    for (int j = 0; j < D / 2; ++j) {
+        const double theta = pos * pow(base, -2.0 * j / D);
+        const double c = cos(theta), sn = sin(theta);
+        const double x = load_elem(src, dtype, off + j), y = load_elem(src, dtype, off + j + D / 2);
+        out[j] = x * c - y * sn;
+        out[j + D / 2] = x * sn + y * c;
+    }
+}
+
+int oracle_tree_rope(int B, int N, int Hq, int Hkv, int D, int cap, int dtype, const void* q,
+                     const void* k_cache, const int32_t* prefix_len, const int32_t* parent, double base,
+                     double* q_out, double* k_out) {
+    if (D % 2 != 0) return -1;
+    for (int b = 0; b < B; ++b) {
+        const int L = prefix_len[b];
+        if (L < 0 || L + N > cap) return -1;
+        for (int i = 0; i < N; ++i) {
+            int depth = 0;
+            for (int n = parent_of(parent, N, b, i); n >= 0; n = parent_of(parent, N, b, n)) ++depth;
+            const double pos = (double)L + depth;
+            for (int h = 0; h < Hq; ++h)
+                rope_row(q, dtype, (((size_t)b * N + i) * Hq + h) * D, D, pos, base,
+                         q_out + (((size_t)b * N + i) * Hq + h) * D);
+            for (int g = 0; g < Hkv; ++g)
+                rope_row(k_cache, dtype, (((size_t)b * Hkv + g) * cap + L + i) * D, D, pos, base,
+                         k_out + (((size_t)b * Hkv + g) * N + i) * D);
+        }
+    }
+    return 0;
+}
+
 /* Threads the OpenMP loops above use (1 without OpenMP). */
 int oracle_num_threads(void) {
 #ifdef _OPENMP
