@@ -150,6 +150,44 @@ int spec_tree_positions(int32_t batch, int32_t num_nodes, const int32_t* prefix_
 int spec_validate_tree(int32_t batch, int32_t num_nodes, const int32_t* parent, int32_t* status,
                        void* stream);
 
+/* Candidate tree of Medusa heads (MEDUSA section, candidate-construction and
+ * tree-attention paragraphs: head k proposes its top-s_k tokens, and the
+ * candidates are the Cartesian product of the heads' proposals arranged as a
+ * tree).  Node 0 is the root with token root_tokens[b].  The tree is built
+ * breadth first: the children of a depth-(d-1) node are its extensions by
+ * head d's candidates in rank order, parents visited in the order their level
+ * was built.  Node (i_1..i_d) thus has parent (i_1..i_{d-1}) and token
+ * head_tokens[b][d-1][i_d].
+ * spec_medusa_tree_nodes returns N = 1 + sum_d prod_{k<=d} s_k, or 0 when
+ * num_heads is outside [1, 63], a width is outside [1, max_width] or N > 64.
+ * Arguments
+ *   widths       host array of num_heads widths s_1..s_K
+ *   max_width    row stride of head_tokens (>= every width)
+ *   root_tokens  [B] int32, device
+ *   head_tokens  [B][K][max_width] int32, device (entries past a width unread)
+ *   parent, tokens [B][N] int32, device, written (parent[b][0] = -1)
+ * Errors: SPEC_EINVAL for an invalid shape (as above) or a NULL pointer. */
+int32_t spec_medusa_tree_nodes(int32_t num_heads, const int32_t* widths, int32_t max_width);
+int spec_medusa_tree(int32_t batch, int32_t num_heads, const int32_t* widths, int32_t max_width,
+                     const int32_t* root_tokens, const int32_t* head_tokens, int32_t* parent,
+                     int32_t* tokens, void* stream);
+
+/* Depth-position rotary embedding of the tree, in place (MEDUSA section,
+ * tree-attention paragraph: position indices follow tree depth).  Node i of
+ * request b sits at position pos = L_b + depth(i).  The rotation is the
+ * Llama family's rotary embedding in its rotate-half layout: for j < D/2 the
+ * pair (x_j, x_{j+D/2}) turns by pos * rope_base^(-2j/D)
+ *   x_j' = x_j cos - x_{j+D/2} sin,   x_{j+D/2}' = x_j sin + x_{j+D/2} cos,
+ * angles and products in fp64, rounded to fp32 (then to bf16).  Applied
+ * to q[b][i][h] for every q head and to the tree's K rows
+ * k_cache[b][g][L_b + i] for every kv head; the prefix rows and V are not
+ * touched.  desc as for spec_verify_attn (softmax_scale unused); parent NULL
+ * means a chain.  A request with L_b < 0 or L_b + N > cap is skipped.
+ * Errors: SPEC_EINVAL for a bad descriptor, rope_base <= 0 or not finite, or
+ * a NULL q / k_cache / prefix_len. */
+int spec_tree_rope(const spec_attn_desc* desc, void* q, void* k_cache, const int32_t* prefix_len,
+                   const int32_t* parent, float rope_base, void* stream);
+
 /* Static string naming a spec_status value. */
 const char* spec_status_string(int status);
 

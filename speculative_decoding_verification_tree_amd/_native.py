@@ -23,6 +23,9 @@ SIGNATURES = {
     "spec_commit_kv": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
     "spec_tree_positions": (ctypes.c_int, [_I, _I, _P, _P, _P, _P]),
     "spec_validate_tree": (ctypes.c_int, [_I, _I, _P, _P, _P]),
+    "spec_medusa_tree_nodes": (_I, [_I, _P, _I]),
+    "spec_medusa_tree": (ctypes.c_int, [_I, _I, _P, _I, _P, _P, _P, _P, _P]),
+    "spec_tree_rope": (ctypes.c_int, [_P, _P, _P, _P, _P, _F, _P]),
     "spec_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 

@@ -184,3 +184,49 @@ def spec_validate_tree(parent, status=None, stream=None):
     rc = _native.lib().spec_validate_tree(B, N, _ptr(parent), _ptr(status), _stream(stream))
     _check("spec_validate_tree", rc)
     return status
+
+
+def spec_medusa_tree_nodes(widths, max_width=None):
+    """Node count N of the Medusa candidate tree for head widths s_1..s_K (0 if invalid)."""
+    w = (ctypes.c_int32 * len(widths))(*[int(x) for x in widths])
+    mw = max(int(x) for x in widths) if max_width is None else int(max_width)
+    return int(_native.lib().spec_medusa_tree_nodes(len(widths), w, mw))
+
+
+def spec_medusa_tree(widths, root_tokens, head_tokens, parent=None, tokens=None, stream=None):
+    """Cartesian-product candidate tree: head_tokens [B][K][max_width] int32 (top-s_k
+    candidates of head k in rank order), root_tokens [B]; returns (parent, tokens) [B][N]."""
+    B, K, W = head_tokens.shape
+    if len(widths) != K:
+        raise ValueError("one width per head")
+    _dev(root_tokens, "root_tokens", torch.int32)
+    _dev(head_tokens, "head_tokens", torch.int32)
+    N = spec_medusa_tree_nodes(widths, W)
+    if N == 0:
+        raise SpecError("spec_medusa_tree", _native.SPEC_EINVAL)
+    if parent is None:
+        parent = torch.empty(B, N, dtype=torch.int32, device=head_tokens.device)
+    if tokens is None:
+        tokens = torch.empty(B, N, dtype=torch.int32, device=head_tokens.device)
+    _dev(parent, "parent", torch.int32)
+    _dev(tokens, "tokens", torch.int32)
+    w = (ctypes.c_int32 * K)(*[int(x) for x in widths])
+    rc = _native.lib().spec_medusa_tree(B, K, w, W, _ptr(root_tokens), _ptr(head_tokens), _ptr(parent),
+                                        _ptr(tokens), _stream(stream))
+    _check("spec_medusa_tree", rc)
+    return parent, tokens
+
+
+def spec_tree_rope(q, k_cache, prefix_len, parent, rope_base, stream=None):
+    """In-place depth-position rotary embedding of q [B][N][Hq][D] and the tree rows of
+    k_cache [B][Hkv][cap][D] (positions L_b + depth)."""
+    B, N, Hq, D = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    _dev(q, "q")
+    _dev(k_cache, "k_cache", q.dtype)
+    _dev(prefix_len, "prefix_len", torch.int32)
+    _dev(parent, "parent", torch.int32)
+    desc = attn_desc(B, N, Hq, Hkv, D, cap, q.dtype)
+    rc = _native.lib().spec_tree_rope(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(prefix_len), _ptr(parent),
+                                      float(rope_base), _stream(stream))
+    _check("spec_tree_rope", rc)

@@ -127,6 +127,65 @@ int spec_validate_tree(int32_t batch, int32_t num_nodes, const int32_t* parent, 
     return launch_validate(batch, num_nodes, parent, status, static_cast<hipStream_t>(stream));
 }
 
+int32_t spec_medusa_tree_nodes(int32_t num_heads, const int32_t* widths, int32_t max_width) {
+    if (num_heads < 1 || num_heads > kMaxNodes - 1 || !widths || max_width < 1) return 0;
+    long n = 1, level = 1;
+    for (int k = 0; k < num_heads; ++k) {
+        if (widths[k] < 1 || widths[k] > max_width) return 0;
+        level *= widths[k];
+        n += level;
+        if (n > kMaxNodes) return 0;
+    }
+    return static_cast<int32_t>(n);
+}
+
+int spec_medusa_tree(int32_t batch, int32_t num_heads, const int32_t* widths, int32_t max_width,
+                     const int32_t* root_tokens, const int32_t* head_tokens, int32_t* parent, int32_t* tokens,
+                     void* stream) {
+    const int32_t N = spec_medusa_tree_nodes(num_heads, widths, max_width);
+    if (batch < 0 || N == 0) return SPEC_EINVAL;
+    if (batch == 0) return SPEC_OK;
+    if (!root_tokens || !head_tokens || !parent || !tokens) return SPEC_EINVAL;
+    MedusaTreeArgs a{};
+    a.K = num_heads;
+    a.W = max_width;
+    a.N = N;
+    a.off[0] = 0;
+    a.off[1] = 1;
+    long level = 1;
+    for (int k = 0; k < num_heads; ++k) {
+        a.widths[k] = widths[k];
+        level *= widths[k];
+        a.off[k + 2] = static_cast<int>(a.off[k + 1] + level);
+    }
+    a.root = root_tokens;
+    a.head = head_tokens;
+    a.parent = parent;
+    a.tokens = tokens;
+    return launch_medusa_tree(a, batch, static_cast<hipStream_t>(stream));
+}
+
+int spec_tree_rope(const spec_attn_desc* desc, void* q, void* k_cache, const int32_t* prefix_len,
+                   const int32_t* parent, float rope_base, void* stream) {
+    int err;
+    if (!desc_ok(desc, &err)) return err;
+    if (!(rope_base > 0.f) || isinf(rope_base)) return SPEC_EINVAL;
+    if (desc->batch == 0) return SPEC_OK;
+    if (!q || !k_cache || !prefix_len) return SPEC_EINVAL;
+    TreeRopeArgs a;
+    a.q = q;
+    a.k = k_cache;
+    a.prefix_len = prefix_len;
+    a.parent = parent;
+    a.N = desc->num_nodes;
+    a.Hq = desc->num_q_heads;
+    a.Hkv = desc->num_kv_heads;
+    a.D = desc->head_dim;
+    a.cap = desc->kv_capacity;
+    a.log2_base = log2(static_cast<double>(rope_base));
+    return launch_tree_rope(a, desc->batch, desc->dtype == SPEC_BF16, static_cast<hipStream_t>(stream));
+}
+
 const char* spec_status_string(int status) {
     switch (status) {
         case SPEC_OK: return "SPEC_OK";

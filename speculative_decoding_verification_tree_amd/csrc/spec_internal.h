@@ -9,6 +9,8 @@
 
 namespace specv {
 
+constexpr int kTreeMaxNodes = 64;
+
 // Execution plan of spec_verify_attn for one descriptor and prefix bound.
 struct AttnPlan {
     bool mfma;        // bf16 MFMA path (else the VALU path)
@@ -52,6 +54,29 @@ int launch_positions(int B, int N, const int32_t* prefix_len, const int32_t* par
                      hipStream_t stream);
 
 int launch_validate(int B, int N, const int32_t* parent, int32_t* status, hipStream_t stream);
+
+struct MedusaTreeArgs {
+    int K, W, N;
+    int widths[kTreeMaxNodes];
+    int off[kTreeMaxNodes + 1];  // first node of each level (off[1] = 1)
+    const int32_t* root;
+    const int32_t* head;
+    int32_t* parent;
+    int32_t* tokens;
+};
+
+int launch_medusa_tree(const MedusaTreeArgs& a, int B, hipStream_t stream);
+
+struct TreeRopeArgs {
+    void* q;
+    void* k;
+    const int32_t* prefix_len;
+    const int32_t* parent;
+    int N, Hq, Hkv, D, cap;
+    double log2_base;
+};
+
+int launch_tree_rope(const TreeRopeArgs& a, int B, bool bf16, hipStream_t stream);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

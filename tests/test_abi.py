@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 12, names
     lib = sv.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -124,3 +124,25 @@ def test_commit_and_helper_errors():
     assert lib.spec_validate_tree(2, 4, None, FAKE, None) == EINVAL
     for rc in (0, -1, -2, -3, -4, 5):
         assert sv.status_string(rc)
+
+
+def test_medusa_tree_and_rope_errors():
+    lib = sv.lib()
+    W = ctypes.c_int32 * 8
+    assert lib.spec_medusa_tree_nodes(4, W(3, 2, 2, 2), 3) == 46
+    assert lib.spec_medusa_tree_nodes(1, W(1), 1) == 2
+    assert lib.spec_medusa_tree_nodes(3, W(4, 4, 4), 4) == 0   # 85 nodes
+    assert lib.spec_medusa_tree_nodes(2, W(2, 3), 2) == 0      # width above max_width
+    assert lib.spec_medusa_tree_nodes(2, W(0, 3), 3) == 0
+    assert lib.spec_medusa_tree_nodes(0, W(1), 1) == 0
+    assert lib.spec_medusa_tree_nodes(2, None, 3) == 0
+    assert lib.spec_medusa_tree(2, 3, W(4, 4, 4), 4, FAKE, FAKE, FAKE, FAKE, None) == EINVAL
+    assert lib.spec_medusa_tree(-1, 1, W(2), 2, FAKE, FAKE, FAKE, FAKE, None) == EINVAL
+    assert lib.spec_medusa_tree(2, 1, W(2), 2, None, FAKE, FAKE, FAKE, None) == EINVAL
+    assert lib.spec_medusa_tree(0, 1, W(2), 2, None, None, None, None, None) == OK
+    d = _desc()
+    assert lib.spec_tree_rope(ctypes.byref(d), FAKE, FAKE, FAKE, None, 0.0, None) == EINVAL
+    assert lib.spec_tree_rope(ctypes.byref(d), FAKE, FAKE, FAKE, None, float("inf"), None) == EINVAL
+    assert lib.spec_tree_rope(ctypes.byref(d), FAKE, FAKE, None, None, 10000.0, None) == EINVAL
+    assert lib.spec_tree_rope(ctypes.byref(_desc(head_dim=96)), FAKE, FAKE, FAKE, None, 1e4, None) == EUNSUPPORTED
+    assert lib.spec_tree_rope(ctypes.byref(_desc(batch=0)), None, None, None, None, 1e4, None) == OK
