@@ -165,6 +165,25 @@ def main():
         accept(c)
         commit(c)
 
+    # The step before the path, timed on its own: the Medusa candidate tree
+    # (tree workloads built as a Cartesian product) and the depth-position
+    # rotary embedding of q and the tree's K rows, in place.
+    rope_base = 500000.0
+    cartesian = cfg["tree"] == "cartesian"
+    if cartesian:
+        widths = list(cfg["topk"])
+        head_tok = torch.randint(0, V, (B, len(widths), max(widths)), dtype=torch.int32, device=dev)
+        root_tok = torch.randint(0, V, (B,), dtype=torch.int32, device=dev)
+        tree_par = torch.empty(B, N, dtype=torch.int32, device=dev)
+        tree_tok = torch.empty(B, N, dtype=torch.int32, device=dev)
+
+    def tree_rope(c):
+        if cartesian:
+            sv.spec_medusa_tree(widths, root_tok, head_tok, tree_par, tree_tok)
+            sv.spec_tree_rope(c["q"], c["k"], c["pl"], tree_par, rope_base)
+        else:
+            sv.spec_tree_rope(c["q"], c["k"], c["pl"], c["parent"], rope_base)
+
     # eager warm-up (also checks every call returns SPEC_OK)
     for i in range(max(args.warmup, ncopies)):
         step(copies[i % ncopies])
@@ -184,7 +203,8 @@ def main():
     g_attn = capture([attn])
     g_acc = capture([accept])
     g_commit = capture([commit])
-    for g in (g_step, g_attn, g_acc, g_commit):
+    g_rope = capture([tree_rope])
+    for g in (g_step, g_attn, g_acc, g_commit, g_rope):
         g.replay()
     torch.cuda.synchronize()
 
@@ -204,6 +224,9 @@ def main():
     attn_ms = timed(g_attn, reps)
     accept_ms = timed(g_acc, reps)
     commit_ms = timed(g_commit, reps)
+    rope_ms = timed(g_rope, reps)
+    esz = 2 if bf16 else 4
+    rope_bytes = 2 * (B * N * w.Hq * w.D + B * w.Hkv * N * w.D) * esz  # read + write, q and tree K rows
 
     a_bytes = attn_bytes(w)
     achieved = a_bytes / (attn_ms * 1e-3) / 1e9
@@ -264,7 +287,12 @@ def main():
             "global_batch": B,
             "parallelism": "single GPU",
         },
-        "breakdown_us": {"attention": attn_ms * 1e3, "accept": accept_ms * 1e3, "commit": commit_ms * 1e3},
+        "breakdown_us": {"attention": attn_ms * 1e3, "accept": accept_ms * 1e3, "commit": commit_ms * 1e3,
+                         "tree_rope": rope_ms * 1e3},
+        "tree_rope": {"us": rope_ms * 1e3, "bytes": rope_bytes,
+                      "achieved_GBs": rope_bytes / (rope_ms * 1e-3) / 1e9,
+                      "calls": ("spec_medusa_tree + " if cartesian else "") + "spec_tree_rope",
+                      "note": "before the path; not part of ms_per_step"},
         "roofline": {
             "bound": "hbm",
             "kernel": "spec_verify_attn",
