@@ -168,6 +168,15 @@ __device__ __forceinline__ Vals<EPT> load_chunk(const float* row, int x0, int x1
     return r;
 }
 
+// In-place pairwise (tree) sum of n floats; the total lands in v[0].
+template <int n>
+__device__ __forceinline__ void pairwise_sum(float (&v)[n]) {
+#pragma unroll
+    for (int w = n / 2; w >= 1; w /= 2)
+#pragma unroll
+        for (int e = 0; e < w; ++e) v[e] += v[e + w];
+}
+
 // Per-wave partial results of a chunk reduction.
 struct WaveRed {
     float m[4];
@@ -197,18 +206,21 @@ __device__ __forceinline__ void chunk_stats(const float* row, int x0, int x1, bo
     wave_argmax(best, bi);
     double sw = 0.0, aw = 0.0;
     if (T > 0.f && best > -INFINITY) {
+        // The thread's terms are summed pairwise in fp32 (same-sign terms:
+        // relative error below log2(EPT) * 2^-24), the threads' sums in fp64.
         const float c2 = 1.4426950408889634f / T;
+        float ex[EPT], ax[EPT];
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
-            if (elem_index(x0, e, vec4) < x1) {
-                const float t2 = (vals.v[e] - best) * c2;
-                const float ex = __builtin_amdgcn_exp2f(t2);
-                sw += static_cast<double>(ex);
-                aw += static_cast<double>(t2) * static_cast<double>(ex);
-            }
+            const float t2 = (vals.v[e] - best) * c2;
+            const bool in = elem_index(x0, e, vec4) < x1;
+            ex[e] = in ? __builtin_amdgcn_exp2f(t2) : 0.f;
+            ax[e] = in ? t2 * ex[e] : 0.f;
         }
-        sw = wave_sum(sw);
-        aw = wave_sum(aw);
+        pairwise_sum<EPT>(ex);
+        pairwise_sum<EPT>(ax);
+        sw = wave_sum(static_cast<double>(ex[0]));
+        aw = wave_sum(static_cast<double>(ax[0]));
     }
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     if (lane == 0) {
@@ -465,15 +477,18 @@ __global__ __launch_bounds__(kThreads) void accept_sample(AcceptArgs a) {
         const float c2 = 1.4426950408889634f / a.T;
         const Vals<EPT> lvals = load_chunk<EPT>(row, x0, x1, vec4, -INFINITY);
         const Vals<EPT> qvals = load_chunk<EPT>(qrow, x0, x1, vec4, 0.f);
-        double r = 0.0, p = 0.0;
+        // Non-negative terms: pairwise in fp32 per thread, fp64 across threads.
+        float rv[EPT], pvv[EPT];
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
-            if (elem_index(x0, e, vec4) < x1) {
-                const float pv = target_prob(lvals.v[e], d.M, c2, invS);
-                r += static_cast<double>(fmaxf(pv - qvals.v[e], 0.f));
-                p += static_cast<double>(pv);
-            }
+            const bool in = elem_index(x0, e, vec4) < x1;
+            const float pv = in ? target_prob(lvals.v[e], d.M, c2, invS) : 0.f;
+            pvv[e] = pv;
+            rv[e] = in ? fmaxf(pv - qvals.v[e], 0.f) : 0.f;
         }
+        pairwise_sum<EPT>(rv);
+        pairwise_sum<EPT>(pvv);
+        double r = rv[0], p = pvv[0];
         block_sum2_d(r, p, s_r2);
         cs.m1 = r;
         cs.m2 = p;
