@@ -288,6 +288,7 @@ __global__ __launch_bounds__(kThreads) void accept_rowstats(AcceptArgs a) {
 // Every load that depends on nothing else is issued first: the tree, the
 // drafted tokens and uniforms, and the chunk records of every row (a leaf's
 // records are stale and never used).
+template <int RPW>  // node rows per wave (N <= 4 * RPW)
 __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, bool writer) {
     const int N = a.N, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __shared__ float s_M[kMaxNodes];
@@ -308,11 +309,11 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
     // c of each in one round (vocabularies of more than 64 chunks loop).
     const double T = a.T;
     const double c2 = T > 0.0 ? 1.4426950408889634 / T : 0.0;
-    float mc[kRowsPerWave];
-    int ac[kRowsPerWave];
-    double sc[kRowsPerWave], scA[kRowsPerWave];
+    float mc[RPW];
+    int ac[RPW];
+    double sc[RPW], scA[RPW];
 #pragma unroll
-    for (int k = 0; k < kRowsPerWave; ++k) {
+    for (int k = 0; k < RPW; ++k) {
         const int u = wave + 4 * k;
         mc[k] = -INFINITY;
         ac[k] = 0x7fffffff;
@@ -333,7 +334,7 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
         if (a.rule == 0) gq = a.draft[(static_cast<size_t>(b) * N + lane) * a.V + xi];
     }
 #pragma unroll
-    for (int k = 0; k < kRowsPerWave; ++k) {
+    for (int k = 0; k < RPW; ++k) {
         const int u = wave + 4 * k;
         if (!(u < N - 1 + (a.parent != nullptr))) continue;  // wave-uniform
         float m = mc[k];
@@ -457,12 +458,12 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
     return d;
 }
 
-template <int EPT>
+template <int EPT, int RPW>
 __global__ __launch_bounds__(kThreads) void accept_sample(AcceptArgs a) {
     const int c = blockIdx.x, b = blockIdx.y;
     __shared__ WaveRed s_red;
     __shared__ double s_r2[8];
-    const Decision d = decide_request(a, b, c == 0);
+    const Decision d = decide_request<RPW>(a, b, c == 0);
     if (d.mode == MODE_DONE) return;
     const float* row = a.logits + (static_cast<size_t>(b) * a.N + d.v) * a.V;
     const int x0 = c * a.chunk, x1 = min(x0 + a.chunk, a.V);
@@ -764,7 +765,11 @@ static int launch_accept_ept(const AcceptArgs& a, const AcceptPlan& p, hipStream
         hipLaunchKernelGGL((accept_rowstats<EPT>), dim3(p.nchunk, a.N, a.B), dim3(kThreads), 0, stream, a);
         if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     }
-    hipLaunchKernelGGL((accept_sample<EPT>), dim3(p.nchunk, a.B), dim3(kThreads), 0, stream, a);
+    // Few rows need fewer registers for the decision: more workgroups per CU.
+    if (a.N <= 16)
+        hipLaunchKernelGGL((accept_sample<EPT, 4>), dim3(p.nchunk, a.B), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((accept_sample<EPT, kRowsPerWave>), dim3(p.nchunk, a.B), dim3(kThreads), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     hipLaunchKernelGGL((accept_select<EPT>), dim3(a.B), dim3(kThreads), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
