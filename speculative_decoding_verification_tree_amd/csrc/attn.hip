@@ -1011,7 +1011,10 @@ AttnPlan plan_attn(const spec_attn_desc& d, int max_prefix_len) {
         const long units = slabs * p.row_groups;
         const long want = units >= 4096 ? 1 : (4096 + units - 1) / units;
         long chunk_blocks = (blocks_max + want - 1) / want;
-        const long min_split = env_int("SPEC_VERIFY_KV_CHUNK") ? (env_int("SPEC_VERIFY_KV_CHUNK") + 31) / 32 : 8;
+        // At least 8 blocks per MFMA split; the VALU path (one tile per
+        // barrier round) spreads small problems down to one block per split.
+        const long min_split = env_int("SPEC_VERIFY_KV_CHUNK") ? (env_int("SPEC_VERIFY_KV_CHUNK") + 31) / 32
+                                                               : (p.mfma ? 8 : 1);
         if (chunk_blocks < min_split) chunk_blocks = min_split;
         p.split_blocks = static_cast<int>(chunk_blocks);
         p.nsplit_max = static_cast<int>((blocks_max + chunk_blocks - 1) / chunk_blocks);
