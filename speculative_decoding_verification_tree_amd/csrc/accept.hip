@@ -122,6 +122,41 @@ __device__ __forceinline__ void block_argmax(float& v, int& i, float* s_v, int* 
         }
 }
 
+// Minimum of mn and maximum of mx over a wavefront, the two reductions
+// interleaved (DPP within rows, permlane swaps across rows).
+__device__ __forceinline__ void wave_min_max_i(int& mn, int& mx) {
+    mn = min(mn, static_cast<int>(dpp_xor1(static_cast<uint32_t>(mn))));
+    mx = max(mx, static_cast<int>(dpp_xor1(static_cast<uint32_t>(mx))));
+    mn = min(mn, static_cast<int>(dpp_xor2(static_cast<uint32_t>(mn))));
+    mx = max(mx, static_cast<int>(dpp_xor2(static_cast<uint32_t>(mx))));
+    mn = min(mn, static_cast<int>(dpp_mirror8(static_cast<uint32_t>(mn))));
+    mx = max(mx, static_cast<int>(dpp_mirror8(static_cast<uint32_t>(mx))));
+    mn = min(mn, static_cast<int>(dpp_mirror16(static_cast<uint32_t>(mn))));
+    mx = max(mx, static_cast<int>(dpp_mirror16(static_cast<uint32_t>(mx))));
+    auto a = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(mn), static_cast<uint32_t>(mn), false, false);
+    auto c = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(mx), static_cast<uint32_t>(mx), false, false);
+    mn = min(static_cast<int>(a[0]), static_cast<int>(a[1]));
+    mx = max(static_cast<int>(c[0]), static_cast<int>(c[1]));
+    a = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(mn), static_cast<uint32_t>(mn), false, false);
+    c = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(mx), static_cast<uint32_t>(mx), false, false);
+    mn = min(static_cast<int>(a[0]), static_cast<int>(a[1]));
+    mx = max(static_cast<int>(c[0]), static_cast<int>(c[1]));
+}
+
+// The same over the workgroup: one LDS exchange.
+__device__ __forceinline__ void block_min_max_i(int& mn, int& mx, int* s_mn, int* s_mx) {
+    wave_min_max_i(mn, mx);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) {
+        s_mn[wv] = mn;
+        s_mx[wv] = mx;
+    }
+    __syncthreads();
+    mn = min(min(s_mn[0], s_mn[1]), min(s_mn[2], s_mn[3]));
+    mx = max(max(s_mx[0], s_mx[1]), max(s_mx[2], s_mx[3]));
+}
+
 // p_v(x) as the residual and sampling passes evaluate it (fp32): the
 // weight 2^((l - M) * c2) / S, c2 = log2(e) / T.
 __device__ __forceinline__ float target_prob(float l, float M, float c2, float invS) {
@@ -585,6 +620,7 @@ __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
     __shared__ double s_wtot[4 * (EPT > CPT ? EPT : CPT)];
     __shared__ int s_pick;
     __shared__ double s_base;
+    __shared__ int s_mn[4], s_mx[4];
 
     // The decision and this thread's run of chunk records, loaded together.
     const Decision d = a.dec[b];
@@ -667,14 +703,10 @@ __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
         cum += w[k];
     }
     // smallest chunk with a hit, else the last chunk with weight
-    float fh = hit == 0x7fffffff ? -INFINITY : -static_cast<float>(hit);
-    int ih = hit;
-    block_argmax(fh, ih, s_v, s_i);
-    float fl = static_cast<float>(lastc);
-    int il = -lastc;
-    block_argmax(fl, il, s_v, s_i);
+    int ih = hit, il = lastc;
+    block_min_max_i(ih, il, s_mn, s_mx);
     if (tid == 0) {
-        s_pick = ih != 0x7fffffff ? ih : max(-il, 0);
+        s_pick = ih != 0x7fffffff ? ih : max(il, 0);
         s_base = ih != 0x7fffffff ? 0.0 : -INFINITY;  // -inf: take the last token with weight
     }
     __syncthreads();
@@ -719,14 +751,10 @@ __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
         locate_token<EPT, 4>(wv, x0, base, t, s_wtot, xhit, lastnz);
     else
         locate_token<EPT, 1>(wv, x0, base, t, s_wtot, xhit, lastnz);
-    float fx = xhit == 0x7fffffff ? -INFINITY : -static_cast<float>(xhit);
-    int ix = xhit;
-    block_argmax(fx, ix, s_v, s_i);
-    float fz = static_cast<float>(lastnz);
-    int iz = -lastnz;
-    block_argmax(fz, iz, s_v, s_i);
+    int ix = xhit, iz = lastnz;
+    block_min_max_i(ix, iz, s_mn, s_mx);
     if (tid == 0) {
-        int final = ix != 0x7fffffff ? ix : -iz;
+        int final = ix != 0x7fffffff ? ix : iz;
         if (final < 0) final = x0;
         *out = final;
     }
