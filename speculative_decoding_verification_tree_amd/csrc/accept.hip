@@ -451,10 +451,11 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
         // deepest accepted node, the lowest index among equals.
         const bool accepted = lane < N && (anc & ~okm) == 0ull;
         const int depth = __popcll(anc) - 1;
-        float key = accepted ? static_cast<float>(depth) : -1.f;
-        int v = lane;
-        wave_argmax(key, v);
-        const int dv = static_cast<int>(key);
+        // deepest accepted node, lowest index among equals: one integer max
+        int key = accepted ? (depth << 6) | (63 - lane) : -1, unused = 0;
+        wave_min_max_i(unused, key);
+        const int v = 63 - (key & 63);
+        const int dv = key >> 6;
         const uint32_t vlo = __shfl(static_cast<uint32_t>(anc), v), vhi = __shfl(static_cast<uint32_t>(anc >> 32), v);
         const uint64_t anc_v = static_cast<uint64_t>(vlo) | (static_cast<uint64_t>(vhi) << 32);
         if (lane < N && ((anc_v >> lane) & 1ull)) s_path[depth] = lane;
@@ -656,7 +657,7 @@ __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
     // Chunk weights in token order (thread t owns chunks t*CPT .. t*CPT+CPT-1).
     const double T = a.T;
     const double c2d = 1.4426950408889634 / T;
-    double Mg = -INFINITY, tot1 = 0.0;
+    double Mg = -INFINITY;
     if (d.mode == MODE_BONUS) {
         float mloc = -INFINITY;
         int dummy = 0;
@@ -664,30 +665,32 @@ __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
         for (int k = 0; k < CPT; ++k) mloc = fmaxf(mloc, cs[k].M);
         block_argmax(mloc, dummy, s_v, s_i);
         Mg = mloc;
-    } else {
-        double t1 = 0.0;
-#pragma unroll
-        for (int k = 0; k < CPT; ++k) t1 += cs[k].m1;
-        tot1 = block_sum_d(t1, s_red);
     }
-    const bool usep = d.mode == MODE_RESID && !(tot1 > 0.0);  // all-zero residual: fall back to p_v
-    double w[CPT];
-    double run = 0.0;
+    // Chunk weights, then the exclusive prefix of this thread's run (wave
+    // scan + wave totals).  A residual of zero total mass falls back to p_v:
+    // its masses are scanned instead (rare).
+    bool usep = false;
+    double w[CPT], run, incl, total;
+    for (int pass = 0; pass < 2; ++pass) {
+        run = 0.0;
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-        w[k] = tid * CPT + k >= a.nchunk ? 0.0
-               : d.mode == MODE_BONUS    ? cs[k].m1 * exp2((static_cast<double>(cs[k].M) - Mg) * c2d)
-               : usep                    ? cs[k].m2
-                                         : cs[k].m1;
-        run += w[k];
+        for (int k = 0; k < CPT; ++k) {
+            w[k] = tid * CPT + k >= a.nchunk ? 0.0
+                   : d.mode == MODE_BONUS    ? cs[k].m1 * exp2((static_cast<double>(cs[k].M) - Mg) * c2d)
+                   : usep                    ? cs[k].m2
+                                             : cs[k].m1;
+            run += w[k];
+        }
+        incl = wave_incl_scan(run);
+        if (pass) __syncthreads();  // the first pass's totals are read before they are replaced
+        if (lane == 63) s_wtot[wave] = incl;
+        __syncthreads();
+        total = s_wtot[0] + s_wtot[1] + s_wtot[2] + s_wtot[3];
+        if (d.mode != MODE_RESID || total > 0.0 || usep) break;
+        usep = true;
     }
-    // Exclusive prefix of this thread's run: wave scan + wave totals.
-    const double incl = wave_incl_scan(run);
-    if (lane == 63) s_wtot[wave] = incl;
-    __syncthreads();
     double before = incl - run;
     for (int k = 0; k < wave; ++k) before += s_wtot[k];
-    const double total = s_wtot[0] + s_wtot[1] + s_wtot[2] + s_wtot[3];
     const double t = static_cast<double>(d.u) * total;
     int hit = 0x7fffffff, lastc = -1;
     double hit_base = 0.0, cum = before;
