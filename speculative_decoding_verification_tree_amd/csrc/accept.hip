@@ -69,6 +69,7 @@ struct AcceptArgs {
     Decision* dec;
     ChunkStat* cstat;
     int B, N, V, chunk, nchunk, rule;  // rule 0 = rejection, 1 = typical
+    int lg_seg;                        // log2 of the lanes per row in the decision: 2^lg_seg >= min(nchunk, 64)
     int vec4;                          // rows are 16-byte aligned: 16-byte loads
     float T, eps, delta;
 };
@@ -157,6 +158,55 @@ __device__ __forceinline__ void block_min_max_i(int& mn, int& mx, int* s_mn, int
     mx = max(max(s_mx[0], s_mx[1]), max(s_mx[2], s_mx[3]));
 }
 
+// Reductions over aligned segments of 2^lg lanes (lg wave-uniform, 0..6):
+// the butterfly of the wave reductions cut after lg levels.
+__device__ __forceinline__ double seg_sum(double v, int lg) {
+    if (lg >= 1) v += move_d<dpp_xor1>(v);
+    if (lg >= 2) v += move_d<dpp_xor2>(v);
+    if (lg >= 3) v += move_d<dpp_mirror8>(v);
+    if (lg >= 4) v += move_d<dpp_mirror16>(v);
+    if (lg >= 5) {
+        const uint64_t u = __builtin_bit_cast(uint64_t, v);
+        const auto x = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(u), static_cast<uint32_t>(u), false, false);
+        const auto y =
+            __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(u >> 32), static_cast<uint32_t>(u >> 32), false, false);
+        v = __builtin_bit_cast(double, static_cast<uint64_t>(x[0]) | (static_cast<uint64_t>(y[0]) << 32)) +
+            __builtin_bit_cast(double, static_cast<uint64_t>(x[1]) | (static_cast<uint64_t>(y[1]) << 32));
+    }
+    if (lg >= 6) {
+        const uint64_t u = __builtin_bit_cast(uint64_t, v);
+        const auto x = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(u), static_cast<uint32_t>(u), false, false);
+        const auto y =
+            __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(u >> 32), static_cast<uint32_t>(u >> 32), false, false);
+        v = __builtin_bit_cast(double, static_cast<uint64_t>(x[0]) | (static_cast<uint64_t>(y[0]) << 32)) +
+            __builtin_bit_cast(double, static_cast<uint64_t>(x[1]) | (static_cast<uint64_t>(y[1]) << 32));
+    }
+    return v;
+}
+
+// (value, index) argmax over aligned segments of 2^lg lanes: largest value,
+// lowest index on ties.
+__device__ __forceinline__ void seg_argmax(float& v, int& i, int lg) {
+    if (lg >= 1) argmax_step(v, i, __uint_as_float(dpp_xor1(__float_as_uint(v))), static_cast<int>(dpp_xor1(i)));
+    if (lg >= 2) argmax_step(v, i, __uint_as_float(dpp_xor2(__float_as_uint(v))), static_cast<int>(dpp_xor2(i)));
+    if (lg >= 3) argmax_step(v, i, __uint_as_float(dpp_mirror8(__float_as_uint(v))), static_cast<int>(dpp_mirror8(i)));
+    if (lg >= 4) argmax_step(v, i, __uint_as_float(dpp_mirror16(__float_as_uint(v))), static_cast<int>(dpp_mirror16(i)));
+    if (lg >= 5) {
+        const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        const auto y = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(i), static_cast<uint32_t>(i), false, false);
+        v = __uint_as_float(x[0]);
+        i = static_cast<int>(y[0]);
+        argmax_step(v, i, __uint_as_float(x[1]), static_cast<int>(y[1]));
+    }
+    if (lg >= 6) {
+        const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        const auto y = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(i), static_cast<uint32_t>(i), false, false);
+        v = __uint_as_float(x[0]);
+        i = static_cast<int>(y[0]);
+        argmax_step(v, i, __uint_as_float(x[1]), static_cast<int>(y[1]));
+    }
+}
+
 // p_v(x) as the residual and sampling passes evaluate it (fp32): the
 // weight 2^((l - M) * c2) / S, c2 = log2(e) / T.
 __device__ __forceinline__ float target_prob(float l, float M, float c2, float invS) {
@@ -175,6 +225,11 @@ struct Vals {
     float v[EPT];
 };
 
+// The loads are unconditional (from a clamped address inside the chunk) and
+// the fill is selected afterwards, so every load of the thread is in flight
+// at once; a load under a branch would make the compiler wait for it before
+// the next.  With 16-byte rows x1 is a multiple of 4, like every x here, so
+// a run of four is either wholly inside the chunk or wholly outside.
 template <int EPT>
 __device__ __forceinline__ Vals<EPT> load_chunk(const float* row, int x0, int x1, bool vec4, float fill) {
     Vals<EPT> r;
@@ -182,25 +237,72 @@ __device__ __forceinline__ Vals<EPT> load_chunk(const float* row, int x0, int x1
 #pragma unroll
         for (int j = 0; j < EPT / 4; ++j) {
             const int x = x0 + 4 * (static_cast<int>(threadIdx.x) + kThreads * j);
-            if (x + 3 < x1) {
-                const float4 v = *reinterpret_cast<const float4*>(row + x);
-                r.v[4 * j] = v.x;
-                r.v[4 * j + 1] = v.y;
-                r.v[4 * j + 2] = v.z;
-                r.v[4 * j + 3] = v.w;
-            } else {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) r.v[4 * j + k] = x + k < x1 ? row[x + k] : fill;
-            }
+            const float4 v = *reinterpret_cast<const float4*>(row + static_cast<unsigned>(min(x, x1 - 4)));
+            const bool in = x < x1;
+            r.v[4 * j] = in ? v.x : fill;
+            r.v[4 * j + 1] = in ? v.y : fill;
+            r.v[4 * j + 2] = in ? v.z : fill;
+            r.v[4 * j + 3] = in ? v.w : fill;
         }
     } else {
+        // Element e sits kThreads * e past this thread's first element; lim
+        // is the last in-range offset (negative: the thread has none), and
+        // out-of-range loads read the chunk's first element instead.
+        const int tid = static_cast<int>(threadIdx.x);
+        const float* p = row + x0 + tid;
+        const int lim = x1 - x0 - tid - 1;
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
-            const int x = x0 + static_cast<int>(threadIdx.x) + kThreads * e;
-            r.v[e] = x < x1 ? row[x] : fill;
+            const bool in = kThreads * e <= lim;
+            const float v = p[in ? kThreads * e : -tid];
+            r.v[e] = in ? v : fill;
         }
     }
     return r;
+}
+
+// The same chunk of two rows, every load of both issued before the first
+// select (one branch on the layout for the pair).
+template <int EPT>
+__device__ __forceinline__ void load_chunk2(const float* row, const float* qrow, int x0, int x1, bool vec4, Vals<EPT>& l,
+                                            Vals<EPT>& q) {
+    if (vec4) {
+        float4 lv[EPT / 4], qv[EPT / 4];
+#pragma unroll
+        for (int j = 0; j < EPT / 4; ++j) {
+            const unsigned x = static_cast<unsigned>(min(x0 + 4 * (static_cast<int>(threadIdx.x) + kThreads * j), x1 - 4));
+            lv[j] = *reinterpret_cast<const float4*>(row + x);
+            qv[j] = *reinterpret_cast<const float4*>(qrow + x);
+        }
+#pragma unroll
+        for (int j = 0; j < EPT / 4; ++j) {
+            const bool in = x0 + 4 * (static_cast<int>(threadIdx.x) + kThreads * j) < x1;
+            l.v[4 * j] = in ? lv[j].x : -INFINITY;
+            l.v[4 * j + 1] = in ? lv[j].y : -INFINITY;
+            l.v[4 * j + 2] = in ? lv[j].z : -INFINITY;
+            l.v[4 * j + 3] = in ? lv[j].w : -INFINITY;
+            q.v[4 * j] = in ? qv[j].x : 0.f;
+            q.v[4 * j + 1] = in ? qv[j].y : 0.f;
+            q.v[4 * j + 2] = in ? qv[j].z : 0.f;
+            q.v[4 * j + 3] = in ? qv[j].w : 0.f;
+        }
+    } else {
+        const int tid = static_cast<int>(threadIdx.x);
+        const int lim = x1 - x0 - tid - 1;
+        float lv[EPT], qv[EPT];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int off = x0 + tid + (kThreads * e <= lim ? kThreads * e : -tid);
+            lv[e] = row[off];
+            qv[e] = qrow[off];
+        }
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const bool in = kThreads * e <= lim;
+            l.v[e] = in ? lv[e] : -INFINITY;
+            q.v[e] = in ? qv[e] : 0.f;
+        }
+    }
 }
 
 // In-place pairwise (tree) sum of n floats; the total lands in v[0].
@@ -340,27 +442,26 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
         xi = min(max(x, 0), a.V - 1);
         if (a.rule == 0 && a.u_acc) ui = a.u_acc[static_cast<size_t>(b) * N + lane];
     }
-    // Whole-row statistics: wave w owns rows w, w+4, ...; lane c loads chunk
-    // c of each in one round (vocabularies of more than 64 chunks loop).
+    // Whole-row statistics, several rows per pass: the chunks of a row sit
+    // on an aligned segment of L = 2^lg_seg lanes (L >= chunks, at most 64),
+    // so a wave combines 64 / L rows at once.  Wave w owns rows w, w + 4, ...,
+    // taken 64 / L to a pass; vocabularies of more than 64 chunks loop over
+    // the extra chunks on all 64 lanes (one row per pass).
     const double T = a.T;
     const double c2 = T > 0.0 ? 1.4426950408889634 / T : 0.0;
-    float mc[RPW];
-    int ac[RPW];
-    double sc[RPW], scA[RPW];
+    const int nrows = N - 1 + (a.parent != nullptr);
+    const int lg = a.lg_seg, R = 64 >> lg, sr = lane >> lg, cc = lane & ((1 << lg) - 1);
+    const int mine = nrows > wave ? (nrows - wave + 3) / 4 : 0;
+    const int passes = (mine + R - 1) / R;
+    // Loads from clamped (always valid) indexes, selected afterwards: no
+    // load under a branch, so all of them are in flight at once.  Entries
+    // of rows that are not combined are read and dropped.
+    RowStat rr[RPW];
+    {
+        const int cl = min(cc, a.nchunk - 1);
 #pragma unroll
-    for (int k = 0; k < RPW; ++k) {
-        const int u = wave + 4 * k;
-        mc[k] = -INFINITY;
-        ac[k] = 0x7fffffff;
-        sc[k] = 0.0;
-        scA[k] = 0.0;
-        if (u < N - 1 + (a.parent != nullptr) && lane < a.nchunk) {
-            const RowStat r = a.rowstat[(static_cast<size_t>(b) * N + u) * a.nchunk + lane];
-            mc[k] = r.M;
-            ac[k] = r.arg;
-            sc[k] = r.S;
-            scA[k] = r.A;
-        }
+        for (int t = 0; t < RPW; ++t)
+            rr[t] = a.rowstat[(static_cast<size_t>(b) * N + min(wave + 4 * (t * R + sr), N - 1)) * a.nchunk + cl];
     }
     // The tested values, gathered at the drafted tokens as soon as they land.
     double gl = 0.0, gq = 0.0;
@@ -369,42 +470,47 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
         if (a.rule == 0) gq = a.draft[(static_cast<size_t>(b) * N + lane) * a.V + xi];
     }
 #pragma unroll
-    for (int k = 0; k < RPW; ++k) {
-        const int u = wave + 4 * k;
-        if (!(u < N - 1 + (a.parent != nullptr))) continue;  // wave-uniform
-        float m = mc[k];
-        int ar = ac[k];
-        for (int c = lane + 64; c < a.nchunk; c += 64) {
-            const RowStat& r = a.rowstat[(static_cast<size_t>(b) * N + u) * a.nchunk + c];
-            if (r.M > m || (r.M == m && r.arg < ar)) {
-                m = r.M;
-                ar = r.arg;
+    for (int t = 0; t < RPW; ++t) {
+        if (t < passes) {  // wave-uniform
+            const int u = wave + 4 * (t * R + sr);
+            const bool row_in = u < nrows, in = row_in && cc < a.nchunk;
+            float m = in ? rr[t].M : -INFINITY;
+            int ar = in ? rr[t].arg : 0x7fffffff;
+            const size_t rbase = (static_cast<size_t>(b) * N + min(u, N - 1)) * a.nchunk;
+            if (row_in)
+                for (int c = lane + 64; c < a.nchunk; c += 64) {
+                    const RowStat& r = a.rowstat[rbase + c];
+                    if (r.M > m || (r.M == m && r.arg < ar)) {
+                        m = r.M;
+                        ar = r.arg;
+                    }
+                }
+            seg_argmax(m, ar, lg);
+            double S = 0.0, A2 = 0.0;
+            if (T > 0.0) {
+                if (in) {
+                    const double dl = (static_cast<double>(rr[t].M) - m) * c2;
+                    const double w = exp2(dl);
+                    S = w * rr[t].S;
+                    A2 = w * (rr[t].A + dl * rr[t].S);
+                }
+                if (row_in)
+                    for (int c = lane + 64; c < a.nchunk; c += 64) {
+                        const RowStat r = a.rowstat[rbase + c];
+                        const double dl = (static_cast<double>(r.M) - m) * c2;
+                        const double w = exp2(dl);
+                        S += w * r.S;
+                        A2 += w * (r.A + dl * r.S);
+                    }
+                S = seg_sum(S, lg);
+                A2 = seg_sum(A2, lg);
             }
-        }
-        wave_argmax(m, ar);
-        double S = 0.0, A2 = 0.0;
-        if (T > 0.0) {
-            if (lane < a.nchunk) {
-                const double dl = (static_cast<double>(mc[k]) - m) * c2;
-                const double w = exp2(dl);
-                S = w * sc[k];
-                A2 = w * (scA[k] + dl * sc[k]);
+            if (cc == 0 && row_in) {
+                s_M[u] = m;
+                s_arg[u] = ar;
+                s_S[u] = S;
+                s_H[u] = T > 0.0 ? log(S) - 0.6931471805599453 * A2 / S : 0.0;
             }
-            for (int c = lane + 64; c < a.nchunk; c += 64) {
-                const RowStat r = a.rowstat[(static_cast<size_t>(b) * N + u) * a.nchunk + c];
-                const double dl = (static_cast<double>(r.M) - m) * c2;
-                const double w = exp2(dl);
-                S += w * r.S;
-                A2 += w * (r.A + dl * r.S);
-            }
-            S = wave_sum(S);
-            A2 = wave_sum(A2);
-        }
-        if (lane == 0) {
-            s_M[u] = m;
-            s_arg[u] = ar;
-            s_S[u] = S;
-            s_H[u] = T > 0.0 ? log(S) - 0.6931471805599453 * A2 / S : 0.0;
         }
     }
     __syncthreads();
@@ -512,8 +618,8 @@ __global__ __launch_bounds__(kThreads) void accept_sample(AcceptArgs a) {
         const float* qrow = a.draft + (static_cast<size_t>(b) * a.N + d.c) * a.V;
         const float invS = static_cast<float>(1.0 / d.S);
         const float c2 = 1.4426950408889634f / a.T;
-        const Vals<EPT> lvals = load_chunk<EPT>(row, x0, x1, vec4, -INFINITY);
-        const Vals<EPT> qvals = load_chunk<EPT>(qrow, x0, x1, vec4, 0.f);
+        Vals<EPT> lvals, qvals;
+        load_chunk2<EPT>(row, qrow, x0, x1, vec4, lvals, qvals);
         // Non-negative terms: pairwise in fp32 per thread, fp64 across threads.
         float rv[EPT], pvv[EPT];
 #pragma unroll
@@ -724,7 +830,9 @@ __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
     const int x0 = pc * a.chunk, x1 = min(x0 + a.chunk, a.V);
     const bool vec4 = a.vec4 != 0;
     const float* row = a.logits + (static_cast<size_t>(b) * a.N + d.v) * a.V;
-    const float* qrow = d.mode == MODE_RESID ? a.draft + (static_cast<size_t>(b) * a.N + d.c) * a.V : nullptr;
+    // Outside the residual mode the second row is the stop row again (read,
+    // never used), so the pair's loads need no branch.
+    const float* qrow = d.mode == MODE_RESID ? a.draft + (static_cast<size_t>(b) * a.N + d.c) * a.V : row;
     const float invS = d.mode == MODE_RESID ? static_cast<float>(1.0 / d.S) : 0.f;
     const float c2 = 1.4426950408889634f / a.T;
 #pragma unroll
@@ -733,8 +841,8 @@ __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
     __syncthreads();
     const float Mc = s_v[0];
     const double scale = d.mode == MODE_BONUS ? exp2((static_cast<double>(Mc) - Mg) * c2d) : 1.0;
-    const Vals<EPT> lvals = load_chunk<EPT>(row, x0, x1, vec4, -INFINITY);
-    const Vals<EPT> qvals = d.mode == MODE_RESID ? load_chunk<EPT>(qrow, x0, x1, vec4, 0.f) : Vals<EPT>{};
+    Vals<EPT> lvals, qvals;
+    load_chunk2<EPT>(row, qrow, x0, x1, vec4, lvals, qvals);
     double wv[EPT];
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
@@ -832,6 +940,8 @@ int launch_accept(int rule, int B, int N, int V, const float* logits, const floa
     a.chunk = p.chunk;
     a.nchunk = p.nchunk;
     a.rule = rule;
+    a.lg_seg = 0;
+    while ((1 << a.lg_seg) < std::min(p.nchunk, 64)) ++a.lg_seg;
     a.vec4 = (V % 4 == 0) && (reinterpret_cast<uintptr_t>(logits) % 16 == 0) &&
              (draft == nullptr || reinterpret_cast<uintptr_t>(draft) % 16 == 0);
     a.T = temperature;

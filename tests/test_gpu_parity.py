@@ -146,6 +146,9 @@ def test_accept_full_size(cid):
     (4, dict(batch=32, vocab=20000, draft_noise=[0.0])),          # q == p: all accepted
     (2, dict(batch=3, vocab=300000)),                             # > 64 vocabulary chunks
     (3, dict(batch=2, vocab=300001, temperature=0.0)),            # > 64 chunks, argmax path
+    (5, dict(batch=5, vocab=4000, nodes=40, max_depth=8)),        # 2 chunks: 32 rows per decision pass
+    (5, dict(batch=7, vocab=15000, nodes=64, max_depth=5)),       # 8 chunks: 8 rows per decision pass
+    (3, dict(batch=3, vocab=7000, epsilon=0.02, delta=0.05)),     # 4 chunks, typical rule
 ])
 def test_accept_edge_cases(cid, over):
     w = generate(scaled(cid, **over), with_attention=False)
