@@ -214,10 +214,11 @@ __device__ __forceinline__ float target_prob(float l, float M, float c2, float i
 }
 
 // Element e of this thread's share of a chunk starting at x0: strided by
-// the block (coalesced), in runs of four with 16-byte loads.
-__device__ __forceinline__ int elem_index(int x0, int e, bool vec4) {
-    return vec4 ? x0 + 4 * (static_cast<int>(threadIdx.x) + kThreads * (e >> 2)) + (e & 3)
-                : x0 + static_cast<int>(threadIdx.x) + kThreads * e;
+// the block (coalesced), in runs of four with 16-byte loads.  Its token id is
+// x0 + 4 * threadIdx.x + elem_off(e) with 16-byte loads, else
+// x0 + threadIdx.x + elem_off(e); offsets ascend with e.
+__device__ __forceinline__ int elem_off(int e, bool vec4) {
+    return vec4 ? 4 * kThreads * (e >> 2) + (e & 3) : kThreads * e;
 }
 
 template <int EPT>
@@ -324,22 +325,25 @@ struct WaveRed {
 // Chunk statistics of one target row: max logit with its lowest index and,
 // for T > 0, S = sum 2^t2 and A2 = sum t2 * 2^t2 with t2 = (l - max) * c2
 // (so sum exp(t) = S and sum t * exp(t) = ln2 * A2 for t = (l - max) / T).
-// Each wave reduces relative to its own max; one barrier, then every thread
-// merges the four waves in the same order.
+// Branch-free per element: the thread's elements ascend in token id, so the
+// lowest index of the max is the first element equal to it.  Each wave
+// reduces relative to its own max; one barrier, then wave 0 merges the four
+// waves (the results are valid in wave 0 only).
 template <int EPT>
 __device__ __forceinline__ void chunk_stats(const float* row, int x0, int x1, bool vec4, float T, float& M, int& arg,
                                             double& S, double& A2, WaveRed* s) {
     const Vals<EPT> vals = load_chunk<EPT>(row, x0, x1, vec4, -INFINITY);
+    const int tid = static_cast<int>(threadIdx.x);
+    // Element e has token id first + off(e); it is in range iff off(e) < lim
+    // (with 16-byte rows a run of four is wholly in or out).
+    const int first = x0 + (vec4 ? 4 * tid : tid), lim = x1 - first;
+    auto off = [vec4](int e) { return elem_off(e, vec4); };
     float best = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) best = fmaxf(best, vals.v[e]);
     int bi = 0x7fffffff;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-        const int x = elem_index(x0, e, vec4);
-        if (x < x1 && (vals.v[e] > best || (vals.v[e] == best && x < bi))) {
-            best = vals.v[e];
-            bi = x;
-        }
-    }
+    for (int e = EPT - 1; e >= 0; --e) bi = vals.v[e] == best && off(e) < lim ? first + off(e) : bi;
     wave_argmax(best, bi);
     double sw = 0.0, aw = 0.0;
     if (T > 0.f && best > -INFINITY) {
@@ -350,7 +354,7 @@ __device__ __forceinline__ void chunk_stats(const float* row, int x0, int x1, bo
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
             const float t2 = (vals.v[e] - best) * c2;
-            const bool in = elem_index(x0, e, vec4) < x1;
+            const bool in = off(e) < lim;
             ex[e] = in ? __builtin_amdgcn_exp2f(t2) : 0.f;
             ax[e] = in ? t2 * ex[e] : 0.f;
         }
@@ -359,7 +363,7 @@ __device__ __forceinline__ void chunk_stats(const float* row, int x0, int x1, bo
         sw = wave_sum(static_cast<double>(ex[0]));
         aw = wave_sum(static_cast<double>(ax[0]));
     }
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = tid & 63, wv = tid >> 6;
     if (lane == 0) {
         s->m[wv] = best;
         s->i[wv] = bi;
@@ -367,6 +371,11 @@ __device__ __forceinline__ void chunk_stats(const float* row, int x0, int x1, bo
         s->a[wv] = aw;
     }
     __syncthreads();
+    M = -INFINITY;
+    arg = 0x7fffffff;
+    S = 0.0;
+    A2 = 0.0;
+    if (wv != 0) return;
     M = s->m[0];
     arg = s->i[0];
 #pragma unroll
@@ -375,8 +384,6 @@ __device__ __forceinline__ void chunk_stats(const float* row, int x0, int x1, bo
             M = s->m[k];
             arg = s->i[k];
         }
-    S = 0.0;
-    A2 = 0.0;
     if (T > 0.f) {
         const double c2 = 1.4426950408889634 / static_cast<double>(T);
 #pragma unroll
@@ -620,11 +627,12 @@ __global__ __launch_bounds__(kThreads) void accept_sample(AcceptArgs a) {
         const float c2 = 1.4426950408889634f / a.T;
         Vals<EPT> lvals, qvals;
         load_chunk2<EPT>(row, qrow, x0, x1, vec4, lvals, qvals);
+        const int lim = x1 - (x0 + (vec4 ? 4 * static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x)));
         // Non-negative terms: pairwise in fp32 per thread, fp64 across threads.
         float rv[EPT], pvv[EPT];
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
-            const bool in = elem_index(x0, e, vec4) < x1;
+            const bool in = elem_off(e, vec4) < lim;
             const float pv = in ? target_prob(lvals.v[e], d.M, c2, invS) : 0.f;
             pvv[e] = pv;
             rv[e] = in ? fmaxf(pv - qvals.v[e], 0.f) : 0.f;
@@ -676,38 +684,47 @@ __device__ __forceinline__ double wave_incl_scan(double v) {
 // in its coalesced layout: row j is W*kThreads consecutive tokens, W per
 // thread (W = 4 with 16-byte loads, else 1).  Per row: wave scans of the
 // threads' sums, then one barrier for the wave totals.
-template <int EPT, int W>
-__device__ __forceinline__ void locate_token(const double* wv, int x0, double base, double t, double* s_wtot, int& xhit,
-                                             int& lastnz) {
-    constexpr int ROWS = EPT / W;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    double rbefore[ROWS];
+// This thread's run of EPT consecutive tokens first .. first + EPT - 1 of a
+// chunk ending at x1, from two rows (16-byte loads when the rows allow):
+// the layout of the token search, which walks each run in token order.
+// Loads from clamped addresses, selected afterwards (all in flight at once).
+template <int EPT>
+__device__ __forceinline__ void load_run2(const float* row, const float* qrow, int first, int x1, bool vec4,
+                                          Vals<EPT>& l, Vals<EPT>& q) {
+    if (vec4) {
+        float4 lv[EPT / 4], qv[EPT / 4];
 #pragma unroll
-    for (int j = 0; j < ROWS; ++j) {
-        double sj = 0.0;
-#pragma unroll
-        for (int k = 0; k < W; ++k) sj += wv[j * W + k];
-        const double inc = wave_incl_scan(sj);
-        rbefore[j] = inc - sj;
-        if (lane == 63) s_wtot[j * 4 + wave] = inc;
-    }
-    __syncthreads();
-    double rowbase = base;
-#pragma unroll
-    for (int j = 0; j < ROWS; ++j) {
-        double c = rowbase + rbefore[j];
-        for (int k = 0; k < wave; ++k) c += s_wtot[j * 4 + k];
-#pragma unroll
-        for (int k = 0; k < W; ++k) {
-            const double wk = wv[j * W + k];
-            if (wk > 0.0) {
-                const int x = x0 + W * (tid + kThreads * j) + k;
-                lastnz = x;
-                c += wk;
-                if (xhit == 0x7fffffff && c > t) xhit = x;
-            }
+        for (int j = 0; j < EPT / 4; ++j) {
+            const unsigned x = static_cast<unsigned>(min(first + 4 * j, x1 - 4));
+            lv[j] = *reinterpret_cast<const float4*>(row + x);
+            qv[j] = *reinterpret_cast<const float4*>(qrow + x);
         }
-        rowbase += s_wtot[j * 4] + s_wtot[j * 4 + 1] + s_wtot[j * 4 + 2] + s_wtot[j * 4 + 3];
+#pragma unroll
+        for (int j = 0; j < EPT / 4; ++j) {
+            const bool in = first + 4 * j < x1;
+            l.v[4 * j] = in ? lv[j].x : -INFINITY;
+            l.v[4 * j + 1] = in ? lv[j].y : -INFINITY;
+            l.v[4 * j + 2] = in ? lv[j].z : -INFINITY;
+            l.v[4 * j + 3] = in ? lv[j].w : -INFINITY;
+            q.v[4 * j] = in ? qv[j].x : 0.f;
+            q.v[4 * j + 1] = in ? qv[j].y : 0.f;
+            q.v[4 * j + 2] = in ? qv[j].z : 0.f;
+            q.v[4 * j + 3] = in ? qv[j].w : 0.f;
+        }
+    } else {
+        float lv[EPT], qv[EPT];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const unsigned x = static_cast<unsigned>(min(first + e, x1 - 1));
+            lv[e] = row[x];
+            qv[e] = qrow[x];
+        }
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const bool in = first + e < x1;
+            l.v[e] = in ? lv[e] : -INFINITY;
+            q.v[e] = in ? qv[e] : 0.f;
+        }
     }
 }
 
@@ -724,7 +741,7 @@ __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
     __shared__ float s_v[4];
     __shared__ int s_i[4];
     __shared__ double s_red[8];
-    __shared__ double s_wtot[4 * (EPT > CPT ? EPT : CPT)];
+    __shared__ double s_wtot[8];
     __shared__ int s_pick;
     __shared__ double s_base;
     __shared__ int s_mn[4], s_mx[4];
@@ -734,15 +751,14 @@ __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
     const ChunkStat* csb = a.cstat + static_cast<size_t>(b) * a.nchunk;
     ChunkStat cs[CPT];
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-        const int c = tid * CPT + k;
-        if (c < a.nchunk) cs[k] = csb[c];
-        else {
+    for (int k = 0; k < CPT; ++k) cs[k] = csb[min(tid * CPT + k, a.nchunk - 1)];  // clamped: no load under a branch
+#pragma unroll
+    for (int k = 0; k < CPT; ++k)
+        if (tid * CPT + k >= a.nchunk) {
             cs[k].m1 = cs[k].m2 = 0.0;
             cs[k].M = -INFINITY;
             cs[k].arg = 0x7fffffff;
         }
-    }
     if (d.mode == MODE_DONE) return;
     int32_t* out = a.out_tokens + static_cast<size_t>(b) * a.N + d.a;
 
@@ -841,27 +857,46 @@ __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
     __syncthreads();
     const float Mc = s_v[0];
     const double scale = d.mode == MODE_BONUS ? exp2((static_cast<double>(Mc) - Mg) * c2d) : 1.0;
+    // Thread tid owns tokens first .. first + EPT - 1 of the chunk; weights
+    // of tokens past the chunk end are 0.
+    const int first = x0 + tid * EPT;
     Vals<EPT> lvals, qvals;
-    load_chunk2<EPT>(row, qrow, x0, x1, vec4, lvals, qvals);
+    load_run2<EPT>(row, qrow, first, x1, vec4, lvals, qvals);
     double wv[EPT];
+    if (d.mode == MODE_RESID) {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const float pv = target_prob(lvals.v[e], d.M, c2, invS);
+            const float wgt = usep ? pv : fmaxf(pv - qvals.v[e], 0.f);
+            wv[e] = first + e < x1 ? static_cast<double>(wgt) : 0.0;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const float wgt = __builtin_amdgcn_exp2f((lvals.v[e] - Mc) * c2);
+            wv[e] = first + e < x1 ? static_cast<double>(wgt) * scale : 0.0;
+        }
+    }
+    // Mass before this thread's run: block exclusive scan of the run totals.
+    double mine = 0.0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) mine += wv[e];
+    const double incl_r = wave_incl_scan(mine);
+    if (lane == 63) s_wtot[4 + wave] = incl_r;  // slots 4..7: the chunk scan's 0..3 may still be read
+    __syncthreads();
+    double c = base + (incl_r - mine);
+    for (int k = 0; k < wave; ++k) c += s_wtot[4 + k];
+    // Walk the run in token order: the first token whose cumulative mass
+    // exceeds t, and the last token with weight (the fallback when rounding
+    // leaves the chunk's recomputed mass short of t).
+    int xhit = 0x7fffffff, lastnz = -1;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-        float wgt = 0.f;
-        if (elem_index(x0, e, vec4) < x1) {
-            if (d.mode == MODE_RESID) {
-                const float pv = target_prob(lvals.v[e], d.M, c2, invS);
-                wgt = usep ? pv : fmaxf(pv - qvals.v[e], 0.f);
-            } else {
-                wgt = __builtin_amdgcn_exp2f((lvals.v[e] - Mc) * c2);
-            }
-        }
-        wv[e] = static_cast<double>(wgt) * scale;
+        const bool nz = wv[e] > 0.0;
+        c += wv[e];
+        lastnz = nz ? first + e : lastnz;
+        xhit = nz && xhit == 0x7fffffff && c > t ? first + e : xhit;
     }
-    int xhit = 0x7fffffff, lastnz = -1;
-    if (vec4)
-        locate_token<EPT, 4>(wv, x0, base, t, s_wtot, xhit, lastnz);
-    else
-        locate_token<EPT, 1>(wv, x0, base, t, s_wtot, xhit, lastnz);
     int ix = xhit, iz = lastnz;
     block_min_max_i(ix, iz, s_mn, s_mx);
     if (tid == 0) {
