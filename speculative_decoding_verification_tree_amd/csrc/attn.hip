@@ -377,19 +377,19 @@ __device__ __forceinline__ void block_update(const KRead& kread, const unsigned 
             const uint32_t pre = (1u << npre) - 1u;
             kmask = ((tree & 0xFFu) | pre) & ((1u << nend) - 1u);
         }
-        // Raw scores (masked to -inf); the max is scaled once, and each
+        // Raw scores (masked to -inf only in blocks that reach past the
+        // prefix: a wave-uniform branch); the max is scaled once, and each
         // probability is exp2(score * scale - max) with one fma.
         float s[8];
-        float bm = -INFINITY;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int e = 4 * h + ii;
-                const float x = ((kmask >> e) & 1u) ? st[h][ii] : -INFINITY;
-                s[e] = x;
-                bm = fmaxf(bm, x);
-            }
+            for (int ii = 0; ii < 4; ++ii) s[4 * h + ii] = st[h][ii];
+        if (!interior) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s[e] = ((kmask >> e) & 1u) ? s[e] : -INFINITY;
+        }
+        float bm = vmax(vmax3(vmax3(s[0], s[1], s[2]), vmax3(s[3], s[4], s[5]), s[6]), s[7]);
         bm = max_across_rows(bm) * scale_log2;
         // Lazy rescale: keep the running max unless a row's block max exceeds
         // it by more than 8 (probabilities stay <= 2^8, exact in fp32 and as
