@@ -377,24 +377,25 @@ __device__ __forceinline__ void block_update(const KRead& kread, const unsigned 
             const uint32_t pre = (1u << npre) - 1u;
             kmask = ((tree & 0xFFu) | pre) & ((1u << nend) - 1u);
         }
-        // Raw scores (masked to -inf only in blocks that reach past the
-        // prefix: a wave-uniform branch); the max is scaled once, and each
-        // probability is exp2(score * scale - max) with one fma.
+        // Scores scaled to log2 units (masked to -inf only in blocks that
+        // reach past the prefix: a wave-uniform branch).
         float s[8];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) s[4 * h + ii] = st[h][ii];
+            for (int ii = 0; ii < 4; ++ii) s[4 * h + ii] = st[h][ii] * scale_log2;
         if (!interior) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) s[e] = ((kmask >> e) & 1u) ? s[e] : -INFINITY;
         }
-        float bm = vmax(vmax3(vmax3(s[0], s[1], s[2]), vmax3(s[3], s[4], s[5]), s[6]), s[7]);
-        bm = max_across_rows(bm) * scale_log2;
         // Lazy rescale: keep the running max unless a row's block max exceeds
         // it by more than 8 (probabilities stay <= 2^8, exact in fp32 and as
-        // precise in bf16); the decision is wave-uniform.
+        // precise in bf16).  A row's max exceeds it iff one of its four lanes'
+        // does, so the wave-uniform test takes each lane's own max; the row
+        // maxima are formed only when some row rescales.
+        float bm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
         if (__builtin_amdgcn_ballot_w64(bm > m_run[t] + 8.f) != 0ull) {
+            bm = max_across_rows(bm);
             const float mn = fmaxf(m_run[t], bm);
             const float alpha = m_run[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[t] - mn);
             l_run[t] *= alpha;
@@ -403,18 +404,18 @@ __device__ __forceinline__ void block_update(const KRead& kread, const unsigned 
             m_run[t] = mn;
         }
         const float mu = m_run[t] == -INFINITY ? 0.f : m_run[t];
-        float rs = 0.f;
+        float p[8], rs = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, -mu));
-            rs += s[e];
+            p[e] = __builtin_amdgcn_exp2f(s[e] - mu);
+            rs += p[e];
         }
-        l_run[t] += sum_across_rows(rs);
+        l_run[t] += rs;  // this lane's share of the row sum; the four shares are added at the end
         u32x4 pp;
-        pp[0] = pack_bf16x2(s[0], s[1]);
-        pp[1] = pack_bf16x2(s[2], s[3]);
-        pp[2] = pack_bf16x2(s[4], s[5]);
-        pp[3] = pack_bf16x2(s[6], s[7]);
+        pp[0] = pack_bf16x2(p[0], p[1]);
+        pp[1] = pack_bf16x2(p[2], p[3]);
+        pp[2] = pack_bf16x2(p[4], p[5]);
+        pp[3] = pack_bf16x2(p[6], p[7]);
         const bf16x8 pa = __builtin_bit_cast(bf16x8, pp);
 #pragma unroll
         for (int c = 0; c < NC16; ++c) {
@@ -439,13 +440,16 @@ template <int D, int RT>
 __device__ __forceinline__ void write_rows(const AttnArgs& a, const Seg& cur, int row0, const float (&m_run)[RT],
                                            const float (&l_run)[RT], const f32x4 (&o)[RT][D / 16]) {
     const int lane = threadIdx.x & 63, n16 = lane & 15, q4 = lane >> 4;
+    float l_row[RT];  // the row sums: the four lanes' shares added
+#pragma unroll
+    for (int t = 0; t < RT; ++t) l_row[t] = sum_across_rows(l_run[t]);
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
         const int r = row0 + t * 16 + n16;
         if (r >= a.R) continue;
         if (cur.direct) {
             const int node = r / a.G, hq = cur.g * a.G + r % a.G;
-            const float inv = l_run[t] > 0.f ? 1.f / l_run[t] : 0.f;
+            const float inv = l_row[t] > 0.f ? 1.f / l_row[t] : 0.f;
             uint16_t* orow =
                 static_cast<uint16_t*>(a.out) + ((static_cast<size_t>(cur.b) * a.N + node) * a.Hq + hq) * D;
 #pragma unroll
@@ -459,7 +463,7 @@ __device__ __forceinline__ void write_rows(const AttnArgs& a, const Seg& cur, in
             float* prow = a.ws_o + (static_cast<size_t>(cur.part) * a.R + r) * D;
 #pragma unroll
             for (int c = 0; c < D / 16; ++c) *reinterpret_cast<f32x4*>(prow + 16 * c + 4 * q4) = o[t][c];
-            if (q4 == 0) a.ws_ml[static_cast<size_t>(cur.part) * a.R + r] = make_float2(m_run[t], l_run[t]);
+            if (q4 == 0) a.ws_ml[static_cast<size_t>(cur.part) * a.R + r] = make_float2(m_run[t], l_row[t]);
         }
     }
 }

@@ -44,20 +44,6 @@ __device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) { return __builtin_amdg
 __device__ __forceinline__ uint32_t dpp_mirror8(uint32_t v) { return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false); }
 __device__ __forceinline__ uint32_t dpp_mirror16(uint32_t v) { return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false); }
 
-// Maxima of values that are never NaN (MFMA scores, -inf), straight to
-// v_max / v_max3: fmaxf in IEEE mode first quiets each input that the
-// compiler cannot prove canonical, one extra instruction per operand.
-__device__ __forceinline__ float vmax(float a, float b) {
-    float r;
-    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-    return r;
-}
-__device__ __forceinline__ float vmax3(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
-
 template <class F>
 __device__ __forceinline__ float xrow_combine16(float v, F op) {
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -71,7 +57,7 @@ __device__ __forceinline__ float xrow_combine32(float v, F op) {
 
 // Reduction over the four lanes n, n+16, n+32, n+48 (one per 16-lane row).
 __device__ __forceinline__ float max_across_rows(float v) {
-    auto mx = [](float x, float y) { return vmax(x, y); };
+    auto mx = [](float x, float y) { return fmaxf(x, y); };
     return xrow_combine32(xrow_combine16(v, mx), mx);
 }
 __device__ __forceinline__ float sum_across_rows(float v) {
