@@ -43,6 +43,8 @@ def _load():
         lib.oracle_tree_attn.restype = I
         lib.oracle_accept.argtypes = [I, I, I, I, P, P, P, P, P, P, D, D, D, P, P, P, P, P]
         lib.oracle_accept.restype = I
+        lib.oracle_accept_ex.argtypes = [I, I, I, I, P, P, P, P, P, P, D, D, D, I, D, P, P, P, P, P]
+        lib.oracle_accept_ex.restype = I
         lib.oracle_commit.argtypes = [I, I, I, I, I, P, P, P, P, P]
         lib.oracle_commit.restype = I
         lib.oracle_medusa_tree.argtypes = [I, I, P, I, I, P, P, P, P]
@@ -95,8 +97,9 @@ def tree_attn(q, k_cache, v_cache, prefix_len, parent, dtype, scale=None, rows=N
 
 
 def accept(rule, target_logits, tokens, parent, temperature, draft_probs=None, u_accept=None,
-           u_sample=None, epsilon=0.0, delta=0.0):
-    """Acceptance in fp64 ("reject" or "typical").
+           u_sample=None, epsilon=0.0, delta=0.0, top_k=0, top_p=1.0):
+    """Acceptance in fp64 ("reject" or "typical").  top_k / top_p truncate
+    the target distribution before the rejection rule (0 and 1.0: off).
 
     Returns dict(accept_len [B], path [B][N], out_tokens [B][N], margin [B],
     stop [B]).
@@ -114,9 +117,9 @@ def accept(rule, target_logits, tokens, parent, temperature, draft_probs=None, u
     out = np.empty((B, N), np.int32)
     margin = np.empty(B, np.float64)
     stop = np.empty(B, np.int32)
-    rc = _load().oracle_accept(B, N, V, r, _ptr(lg), _ptr(dp), _ptr(tk), _ptr(par), _ptr(ua), _ptr(us),
-                               float(temperature), float(epsilon), float(delta), _ptr(acc), _ptr(path),
-                               _ptr(out), _ptr(margin), _ptr(stop))
+    rc = _load().oracle_accept_ex(B, N, V, r, _ptr(lg), _ptr(dp), _ptr(tk), _ptr(par), _ptr(ua), _ptr(us),
+                                  float(temperature), float(epsilon), float(delta), int(top_k), float(top_p),
+                                  _ptr(acc), _ptr(path), _ptr(out), _ptr(margin), _ptr(stop))
     if rc != 0:
         raise ValueError("oracle_accept rejected its arguments")
     return dict(accept_len=acc, path=path, out_tokens=out, margin=margin, stop=stop)

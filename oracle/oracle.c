@@ -39,7 +39,12 @@
  *  - typical rule: the entropy uses the natural log and the temperature-
  *    scaled p; the root is accepted unconditionally and the step's last token
  *    is argmax p at the stop node;
- *  - temperature 0 makes p one-hot at the lowest-index argmax.
+ *  - temperature 0 makes p one-hot at the lowest-index argmax;
+ *  - top-k / nucleus truncation (rejection rule only, T > 0): top-k keeps
+ *    every token whose logit is at least the k-th largest (ties kept); the
+ *    nucleus then acts on the renormalised top-k distribution and keeps a
+ *    token iff the mass of the tokens with a strictly larger logit is below
+ *    top_p; the tests, residual and bonus use the renormalised result.
  */
 #include <math.h>
 #ifdef _OPENMP
@@ -166,6 +171,75 @@ static double target_probs(const float* row, int V, double T, double* p) {
     return H;
 }
 
+/* Top-k then nucleus (top-p) truncation of p = softmax(l / T), T > 0, in
+ * place and renormalised: the "Speculative Sampling" section of the same page
+ * lets top-k and nucleus sampling transform the probabilities before the
+ * rejection rule.  top_k <= 0 or >= V: no top-k; top_p >= 1: no nucleus.
+ * Top-k keeps every token whose logit is at least the k-th largest logit;
+ * the nucleus, on the renormalised top-k distribution, keeps a token iff the
+ * mass of the tokens with a strictly larger logit is below top_p (so tokens
+ * of equal logit are kept or dropped together).  Returns the nucleus margin:
+ * the smallest distance from top_p to the mass above a group of equal logits
+ * (INFINITY without a nucleus). */
+typedef struct {
+    float l;
+    int x;
+} LogitIdx;
+
+static int by_logit_desc(const void* a, const void* b) {
+    const LogitIdx* p = (const LogitIdx*)a;
+    const LogitIdx* q = (const LogitIdx*)b;
+    if (p->l > q->l) return -1;
+    if (p->l < q->l) return 1;
+    return (p->x > q->x) - (p->x < q->x);
+}
+
+static double truncate_probs(const float* row, int V, int top_k, double top_p, double* p) {
+    const int use_k = top_k > 0 && top_k < V, use_p = top_p < 1.0;
+    if (!use_k && !use_p) return INFINITY;
+    LogitIdx* s = (LogitIdx*)malloc(sizeof(LogitIdx) * (size_t)V);
+    for (int x = 0; x < V; ++x) {
+        s[x].l = row[x];
+        s[x].x = x;
+    }
+    qsort(s, (size_t)V, sizeof(LogitIdx), by_logit_desc);
+    int n = V; /* s[0 .. n) are kept */
+    if (use_k) {
+        n = top_k;
+        while (n < V && s[n].l == s[top_k - 1].l) ++n;
+    }
+    double margin = INFINITY;
+    if (use_p) {
+        double W = 0.0;
+        for (int i = 0; i < n; ++i) W += p[s[i].x];
+        double above = 0.0;
+        int kept = 0;
+        for (int i = 0; i < n;) {
+            int j = i;
+            double g = 0.0;
+            while (j < n && s[j].l == s[i].l) g += p[s[j++].x];
+            const double A = above / W;
+            if (fabs(A - top_p) < margin) margin = fabs(A - top_p);
+            if (!(A < top_p)) break;
+            above += g;
+            kept = j;
+            i = j;
+        }
+        n = kept;
+    }
+    char* keep = (char*)calloc((size_t)V, 1);
+    for (int i = 0; i < n; ++i) keep[s[i].x] = 1;
+    double S = 0.0;
+    for (int x = 0; x < V; ++x) {
+        if (!keep[x]) p[x] = 0.0;
+        S += p[x];
+    }
+    for (int x = 0; x < V; ++x) p[x] /= S;
+    free(keep);
+    free(s);
+    return margin;
+}
+
 /* Inverse-CDF draw from non-negative weights r (total S > 0) with uniform u.
  * *margin receives the distance, in the units of r, from u*S to the nearest
  * boundary of the chosen token's interval that borders another token of
@@ -225,18 +299,25 @@ static int draw(const double* r, int V, double S, double u, double* margin) {
  *     rejection, v has children: c = smallest child, r = max(0, p_v - q_c),
  *       r = p_v if sum r == 0, final = draw(r, u_sample[v]);
  *     rejection, v a leaf: final = draw(p_v, u_sample[v]).
+ *   With top_k / top_p (rejection rule, T > 0) every p_u above is first
+ *   truncated by truncate_probs.
  * Outputs accept_len[b] = a, path[b][0..a] then -1, out_tokens[b][0..a-1] =
  * tokens of path[1..a], out_tokens[b][a] = final, then -1.  margin[b] is the
  * smallest distance of any decision that can change the output from its
  * threshold (|min(1, p/q) - u|; |p - thr| / max(p, thr) for the typical
- * test; the draw margin in probability units); stop[b] = v.
+ * test; the draw margin in probability units; the nucleus margin of every
+ * truncated row); stop[b] = v.
  * ------------------------------------------------------------------------- */
-int oracle_accept(int B, int N, int V, int rule, const float* logits, const float* draft,
-                  const int32_t* tokens, const int32_t* parent, const float* u_accept,
-                  const float* u_sample, double T, double eps, double delta, int32_t* accept_len,
-                  int32_t* path, int32_t* out_tokens, double* margin, int32_t* stop) {
+int oracle_accept_ex(int B, int N, int V, int rule, const float* logits, const float* draft,
+                     const int32_t* tokens, const int32_t* parent, const float* u_accept,
+                     const float* u_sample, double T, double eps, double delta, int top_k, double top_p,
+                     int32_t* accept_len, int32_t* path, int32_t* out_tokens, double* margin,
+                     int32_t* stop) {
     if (B < 0 || N < 1 || N > 64 || V < 1 || (rule != 0 && rule != 1) || !(T >= 0.0)) return -1;
     if (rule == 0 && N > 1 && !draft) return -1;
+    if (top_k < 0 || !(top_p > 0.0 && top_p <= 1.0)) return -1;
+    const int truncate = rule == 0 && T > 0.0 && ((top_k > 0 && top_k < V) || top_p < 1.0);
+    if (rule == 1 && ((top_k > 0 && top_k < V) || top_p < 1.0)) return -1; /* rejection rule only */
 #pragma omp parallel for schedule(dynamic, 1)
     for (int b = 0; b < B; ++b) {
         int par[64], depth[64], has_child[64], acc[64];
@@ -249,14 +330,19 @@ int oracle_accept(int B, int N, int V, int rule, const float* logits, const floa
         double* P = (double*)calloc((size_t)N * V, sizeof(double));
         double H[64];
         int have[64];
+        double mg = INFINITY;
         for (int u = 0; u < N; ++u) {
             have[u] = 0;
             if (has_child[u]) {
                 H[u] = target_probs(logits + ((size_t)b * N + u) * V, V, T, P + (size_t)u * V);
+                if (truncate) {
+                    const double tm = truncate_probs(logits + ((size_t)b * N + u) * V, V, top_k, top_p,
+                                                     P + (size_t)u * V);
+                    if (tm < mg) mg = tm;
+                }
                 have[u] = 1;
             }
         }
-        double mg = INFINITY;
         acc[0] = 1;
         for (int i = 1; i < N; ++i) {
             const int u = par[i];
@@ -298,7 +384,13 @@ int oracle_accept(int B, int N, int V, int rule, const float* logits, const floa
         if (rule == 1) {
             final = row_argmax(lv, V);
         } else {
-            if (!have[v]) target_probs(lv, V, T, P + (size_t)v * V);
+            if (!have[v]) {
+                target_probs(lv, V, T, P + (size_t)v * V);
+                if (truncate) {
+                    const double tm = truncate_probs(lv, V, top_k, top_p, P + (size_t)v * V);
+                    if (tm < mg) mg = tm;
+                }
+            }
             const double* pv = P + (size_t)v * V;
             double* r = (double*)malloc(sizeof(double) * (size_t)V);
             double S = 0.0;
@@ -332,6 +424,14 @@ int oracle_accept(int B, int N, int V, int rule, const float* logits, const floa
         free(P);
     }
     return 0;
+}
+
+int oracle_accept(int B, int N, int V, int rule, const float* logits, const float* draft,
+                  const int32_t* tokens, const int32_t* parent, const float* u_accept,
+                  const float* u_sample, double T, double eps, double delta, int32_t* accept_len,
+                  int32_t* path, int32_t* out_tokens, double* margin, int32_t* stop) {
+    return oracle_accept_ex(B, N, V, rule, logits, draft, tokens, parent, u_accept, u_sample, T, eps, delta, 0,
+                            1.0, accept_len, path, out_tokens, margin, stop);
 }
 
 /* ---------------------------------------------------------------------------
