@@ -117,6 +117,27 @@ int spec_accept_reject(int32_t batch, int32_t num_nodes, int32_t vocab, const fl
                        int32_t* accept_len, int32_t* path, int32_t* out_tokens, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* Rejection-rule acceptance on a truncated target (the "Speculative
+ * Sampling" section of the same page lets top-k and nucleus sampling
+ * transform the probabilities before the rule).  Every p_u of
+ * spec_accept_reject is first truncated and renormalised: top-k keeps the
+ * tokens whose logit is at least the k-th largest logit of the row (ties
+ * kept); the nucleus then keeps, on the renormalised top-k distribution, the
+ * tokens for which the mass of the tokens with a strictly larger logit is
+ * below top_p.  The node tests, the residual and the bonus token use the
+ * truncated p_u; draft_probs is taken as given (the caller's draft sampler
+ * applies its own transform).  top_k == 0 or >= vocab: no top-k; top_p == 1:
+ * no nucleus; at T == 0 both are no-ops (the argmax is always kept).  The
+ * nucleus masses are summed in 2^-44 fixed point over fp32 terms, so a
+ * boundary within about 1e-6 of top_p may fall either way.  Arguments and
+ * outputs otherwise as spec_accept_reject, same workspace.
+ *   top_k >= 0; 0 < top_p <= 1, else SPEC_EINVAL */
+int spec_accept_reject_filtered(int32_t batch, int32_t num_nodes, int32_t vocab, const float* target_logits,
+                                const float* draft_probs, const int32_t* tokens, const int32_t* parent,
+                                const float* u_accept, const float* u_sample, float temperature, int32_t top_k,
+                                float top_p, int32_t* accept_len, int32_t* path, int32_t* out_tokens,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Typical acceptance (MEDUSA section, typical-acceptance paragraph of the
  * same page).  Node i >= 1 with parent u and token x passes when
  * p_u(x) > min(epsilon, delta * exp(-H(p_u))), H in nats with p_u =

@@ -42,11 +42,28 @@ struct RowStat {  // per (request, node row, chunk)
 enum { MODE_DONE = 0, MODE_RESID = 1, MODE_BONUS = 2, MODE_ARGMAX = 3 };
 
 struct Decision {  // per request
-    double S;      // stop row: sum exp((l - M)/T) over the whole row
+    double S;      // stop row: sum exp((l - M)/T) over the whole row (over its kept tokens when truncated)
     float M;       // stop row: max logit
     float u;       // u_sample at the stop node
     int mode, v, c, a;
+    uint32_t tau;  // stop row: key of its smallest kept logit (0: every token kept)
 };
+
+struct RowRec {    // per (request, node row), truncated target (top-k / nucleus)
+    double S;      // sum over the kept tokens of 2^((l - M) * log2(e) / T)
+    float M;       // max logit
+    uint32_t tau;  // a token is kept iff logit_key(l) >= tau
+    int arg;       // lowest index of the max
+    int pad;
+};
+
+// Order-preserving 32-bit key of a float (-0 and +0 share the key of +0):
+// a < b as floats iff logit_key(a) < logit_key(b), for non-NaN values.
+__device__ __forceinline__ uint32_t logit_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    u = u == 0x80000000u ? 0u : u;
+    return u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u);
+}
 
 struct ChunkStat {  // per (request, chunk) of the stop row
     double m1;      // residual mass | bonus mass relative to the chunk max
@@ -66,12 +83,15 @@ struct AcceptArgs {
     int32_t* path;
     int32_t* out_tokens;
     RowStat* rowstat;
+    RowRec* rowrec;  // truncated rows (aliases rowstat's space)
     Decision* dec;
     ChunkStat* cstat;
     int B, N, V, chunk, nchunk, rule;  // rule 0 = rejection, 1 = typical
     int lg_seg;                        // log2 of the lanes per row in the decision: 2^lg_seg >= min(nchunk, 64)
     int vec4;                          // rows are 16-byte aligned: 16-byte loads
     float T, eps, delta;
+    int top_k;    // 0: off
+    float top_p;  // 1: off
 };
 
 constexpr int kThreads = 256;
@@ -329,9 +349,9 @@ struct WaveRed {
 // lowest index of the max is the first element equal to it.  Each wave
 // reduces relative to its own max; one barrier, then wave 0 merges the four
 // waves (the results are valid in wave 0 only).
-template <int EPT>
+template <int EPT, bool FILT = false>
 __device__ __forceinline__ void chunk_stats(const float* row, int x0, int x1, bool vec4, float T, float& M, int& arg,
-                                            double& S, double& A2, WaveRed* s) {
+                                            double& S, double& A2, WaveRed* s, uint32_t tau = 0u) {
     const Vals<EPT> vals = load_chunk<EPT>(row, x0, x1, vec4, -INFINITY);
     const int tid = static_cast<int>(threadIdx.x);
     // Element e has token id first + off(e); it is in range iff off(e) < lim
@@ -354,7 +374,9 @@ __device__ __forceinline__ void chunk_stats(const float* row, int x0, int x1, bo
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
             const float t2 = (vals.v[e] - best) * c2;
-            const bool in = off(e) < lim;
+            // (truncated rows: only kept tokens carry mass; the max stays
+            // the chunk's, which is kept whenever any token of it is)
+            const bool in = off(e) < lim && (!FILT || logit_key(vals.v[e]) >= tau);
             ex[e] = in ? __builtin_amdgcn_exp2f(t2) : 0.f;
             ax[e] = in ? t2 * ex[e] : 0.f;
         }
@@ -432,13 +454,17 @@ __global__ __launch_bounds__(kThreads) void accept_rowstats(AcceptArgs a) {
 // Every load that depends on nothing else is issued first: the tree, the
 // drafted tokens and uniforms, and the chunk records of every row (a leaf's
 // records are stale and never used).
-template <int RPW>  // node rows per wave (N <= 4 * RPW)
+// FILT: the target rows are truncated (top-k / nucleus); their statistics
+// come whole from the per-row records, for every row (the stop row may be a
+// leaf).
+template <int RPW, bool FILT = false>  // node rows per wave (N <= 4 * RPW)
 __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, bool writer) {
     const int N = a.N, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __shared__ float s_M[kMaxNodes];
     __shared__ int s_arg[kMaxNodes];
     __shared__ double s_S[kMaxNodes], s_H[kMaxNodes];
     __shared__ int s_path[kMaxNodes];
+    __shared__ uint32_t s_tau[kMaxNodes];
     __shared__ Decision s_dec;
 
     int pi = -1, xi = 0;
@@ -449,12 +475,34 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
         xi = min(max(x, 0), a.V - 1);
         if (a.rule == 0 && a.u_acc) ui = a.u_acc[static_cast<size_t>(b) * N + lane];
     }
+    // The tested values, gathered at the drafted tokens as soon as they land
+    // (issued after the loads that depend on nothing).
+    float glf = 0.f;
+    double gq = 0.0;
+    auto gather = [&]() {
+        if (wave == 0 && lane >= 1 && lane < N && pi >= 0) {
+            glf = a.logits[(static_cast<size_t>(b) * N + pi) * a.V + xi];
+            if (a.rule == 0) gq = a.draft[(static_cast<size_t>(b) * N + lane) * a.V + xi];
+        }
+    };
+    const double T = a.T;
+    if constexpr (FILT) {
+        RowRec r{};
+        if (tid < N) r = a.rowrec[static_cast<size_t>(b) * N + tid];
+        gather();
+        if (tid < N) {
+            s_M[tid] = r.M;
+            s_arg[tid] = r.arg;
+            s_S[tid] = r.S;
+            s_H[tid] = 0.0;
+            s_tau[tid] = r.tau;
+        }
+    } else {
     // Whole-row statistics, several rows per pass: the chunks of a row sit
     // on an aligned segment of L = 2^lg_seg lanes (L >= chunks, at most 64),
     // so a wave combines 64 / L rows at once.  Wave w owns rows w, w + 4, ...,
     // taken 64 / L to a pass; vocabularies of more than 64 chunks loop over
     // the extra chunks on all 64 lanes (one row per pass).
-    const double T = a.T;
     const double c2 = T > 0.0 ? 1.4426950408889634 / T : 0.0;
     const int nrows = N - 1 + (a.parent != nullptr);
     const int lg = a.lg_seg, R = 64 >> lg, sr = lane >> lg, cc = lane & ((1 << lg) - 1);
@@ -470,12 +518,7 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
         for (int t = 0; t < RPW; ++t)
             rr[t] = a.rowstat[(static_cast<size_t>(b) * N + min(wave + 4 * (t * R + sr), N - 1)) * a.nchunk + cl];
     }
-    // The tested values, gathered at the drafted tokens as soon as they land.
-    double gl = 0.0, gq = 0.0;
-    if (wave == 0 && lane >= 1 && lane < N && pi >= 0) {
-        gl = a.logits[(static_cast<size_t>(b) * N + pi) * a.V + xi];
-        if (a.rule == 0) gq = a.draft[(static_cast<size_t>(b) * N + lane) * a.V + xi];
-    }
+    gather();
 #pragma unroll
     for (int t = 0; t < RPW; ++t) {
         if (t < passes) {  // wave-uniform
@@ -520,6 +563,8 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
             }
         }
     }
+    }  // row statistics
+    const double gl = glf;
     __syncthreads();
 
     if (wave == 0) {
@@ -528,7 +573,7 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
         if (lane >= 1 && lane < N && pi >= 0) {
             double pu;
             if (T > 0.0)
-                pu = exp((gl - static_cast<double>(s_M[pi])) / T) / s_S[pi];
+                pu = FILT && logit_key(glf) < s_tau[pi] ? 0.0 : exp((gl - static_cast<double>(s_M[pi])) / T) / s_S[pi];
             else
                 pu = xi == s_arg[pi] ? 1.0 : 0.0;
             if (a.rule == 0) {
@@ -580,8 +625,9 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
             d.c = v_has ? __ffsll(static_cast<long long>(kids)) - 1 : -1;
             d.a = dv;
             d.u = a.u_smp ? a.u_smp[static_cast<size_t>(b) * N + v] : 0.f;
-            d.M = v_has ? s_M[v] : 0.f;
-            d.S = v_has ? s_S[v] : 0.0;
+            d.M = v_has || FILT ? s_M[v] : 0.f;
+            d.S = v_has || FILT ? s_S[v] : 0.0;
+            d.tau = FILT ? s_tau[v] : 0u;
             if (a.rule == 1 || !(T > 0.0))
                 d.mode = v_has ? MODE_DONE : MODE_ARGMAX;
             else
@@ -607,12 +653,12 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
     return d;
 }
 
-template <int EPT, int RPW>
+template <int EPT, int RPW, bool FILT = false>
 __global__ __launch_bounds__(kThreads) void accept_sample(AcceptArgs a) {
     const int c = blockIdx.x, b = blockIdx.y;
     __shared__ WaveRed s_red;
     __shared__ double s_r2[8];
-    const Decision d = decide_request<RPW>(a, b, c == 0);
+    const Decision d = decide_request<RPW, FILT>(a, b, c == 0);
     if (d.mode == MODE_DONE) return;
     const float* row = a.logits + (static_cast<size_t>(b) * a.N + d.v) * a.V;
     const int x0 = c * a.chunk, x1 = min(x0 + a.chunk, a.V);
@@ -632,7 +678,7 @@ __global__ __launch_bounds__(kThreads) void accept_sample(AcceptArgs a) {
         float rv[EPT], pvv[EPT];
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
-            const bool in = elem_off(e, vec4) < lim;
+            const bool in = elem_off(e, vec4) < lim && (!FILT || logit_key(lvals.v[e]) >= d.tau);
             const float pv = in ? target_prob(lvals.v[e], d.M, c2, invS) : 0.f;
             pvv[e] = pv;
             rv[e] = in ? fmaxf(pv - qvals.v[e], 0.f) : 0.f;
@@ -647,7 +693,7 @@ __global__ __launch_bounds__(kThreads) void accept_sample(AcceptArgs a) {
         float M;
         int arg;
         double S, A2;
-        chunk_stats<EPT>(row, x0, x1, vec4, d.mode == MODE_BONUS ? a.T : 0.f, M, arg, S, A2, &s_red);
+        chunk_stats<EPT, FILT>(row, x0, x1, vec4, d.mode == MODE_BONUS ? a.T : 0.f, M, arg, S, A2, &s_red, d.tau);
         cs.M = M;
         cs.arg = arg;
         cs.m1 = S;
@@ -733,7 +779,7 @@ __device__ __forceinline__ void load_run2(const float* row, const float* qrow, i
 // weights (recomputed from the same fp32 terms accept_sample summed) locate
 // the token.  Zero-weight tokens are never drawn; if rounding leaves u*total
 // past the end, the last token with weight is taken.
-template <int EPT>
+template <int EPT, bool FILT = false>
 __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
     constexpr int CPT = kMaxChunks / kThreads;  // chunk records per thread
     const int b = blockIdx.x;
@@ -868,13 +914,15 @@ __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
         for (int e = 0; e < EPT; ++e) {
             const float pv = target_prob(lvals.v[e], d.M, c2, invS);
             const float wgt = usep ? pv : fmaxf(pv - qvals.v[e], 0.f);
-            wv[e] = first + e < x1 ? static_cast<double>(wgt) : 0.0;
+            const bool in = first + e < x1 && (!FILT || logit_key(lvals.v[e]) >= d.tau);
+            wv[e] = in ? static_cast<double>(wgt) : 0.0;
         }
     } else {
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
             const float wgt = __builtin_amdgcn_exp2f((lvals.v[e] - Mc) * c2);
-            wv[e] = first + e < x1 ? static_cast<double>(wgt) * scale : 0.0;
+            const bool in = first + e < x1 && (!FILT || logit_key(lvals.v[e]) >= d.tau);
+            wv[e] = in ? static_cast<double>(wgt) * scale : 0.0;
         }
     }
     // Mass before this thread's run: block exclusive scan of the run totals.
@@ -916,6 +964,205 @@ static int accept_ept(int B, int N, int V) {
     return ept;
 }
 
+// ---------------------------------------------------------------------------
+// Truncated target rows (top-k, then nucleus on the renormalised top-k
+// distribution), one workgroup per (request, node row): the row max with its
+// lowest index, the key threshold tau of the kept set and the kept mass.
+// The thresholds come from radix selection on the order-preserving logit
+// keys (11 + 11 + 10 bits) over LDS histograms: counts for top-k (the k-th
+// largest key, so ties with it are kept); for the nucleus, masses
+// 2^((l - M) * log2(e) / T) in 2^-44 fixed point (integer sums, independent
+// of the order of the atomics), the key at which the mass from the top first
+// reaches top_p of the top-k mass.
+constexpr int kFThreads = 512;
+constexpr int kFWaves = kFThreads / 64;
+constexpr int kFUnroll = 8;
+constexpr float kFixedOne = 17592186044416.0f;  // 2^44
+
+// f(x, l) for every element of the row, this thread's elements in ascending
+// order; kFUnroll loads are issued before the first f.
+template <class F>
+__device__ __forceinline__ void for_row(const float* row, int V, bool vec4, F f) {
+    const int tid = threadIdx.x;
+    if (vec4) {
+        for (int base = 4 * tid; base < V; base += 4 * kFThreads * kFUnroll) {
+            float4 v[kFUnroll];
+#pragma unroll
+            for (int u = 0; u < kFUnroll; ++u)
+                v[u] = *reinterpret_cast<const float4*>(row + min(base + 4 * kFThreads * u, V - 4));
+#pragma unroll
+            for (int u = 0; u < kFUnroll; ++u) {
+                const int x = base + 4 * kFThreads * u;
+                if (x < V) {
+                    f(x, v[u].x);
+                    f(x + 1, v[u].y);
+                    f(x + 2, v[u].z);
+                    f(x + 3, v[u].w);
+                }
+            }
+        }
+    } else {
+        for (int base = tid; base < V; base += kFThreads * kFUnroll) {
+            float v[kFUnroll];
+#pragma unroll
+            for (int u = 0; u < kFUnroll; ++u) v[u] = row[min(base + kFThreads * u, V - 1)];
+#pragma unroll
+            for (int u = 0; u < kFUnroll; ++u)
+                if (base + kFThreads * u < V) f(base + kFThreads * u, v[u]);
+        }
+    }
+}
+
+__device__ __forceinline__ unsigned long long block_incl_scan_u64(unsigned long long v, unsigned long long* s_w,
+                                                                  unsigned long long& total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long t = __shfl_up(v, o);
+        if (lane >= o) v += t;
+    }
+    __syncthreads();
+    if (lane == 63) s_w[wave] = v;
+    __syncthreads();
+    total = 0;
+    for (int k = 0; k < kFWaves; ++k) {
+        if (k < wave) v += s_w[k];
+        total += s_w[k];
+    }
+    return v;
+}
+
+// One radix step: h[0, nb) are the counts (or masses) of the candidate keys
+// by digit.  Scanning digits from the top, finds the digit d at which the
+// running total first reaches need; *above is the total of the digits above
+// d.  need_frac > 0: need = ceil(need_frac * total of the bins) (nucleus
+// first step).
+__device__ __forceinline__ void radix_step(const unsigned long long* h, int nb, unsigned long long& need,
+                                           double need_frac, int& d, unsigned long long& above,
+                                           unsigned long long* s_w, int* s_d, unsigned long long* s_above) {
+    const int tid = threadIdx.x, per = nb / kFThreads;
+    unsigned long long loc = 0;
+    for (int j = 0; j < per; ++j) loc += h[nb - 1 - per * tid - j];
+    unsigned long long total;
+    const unsigned long long incl = block_incl_scan_u64(loc, s_w, total);
+    if (need_frac > 0.0) {
+        const double want = ceil(need_frac * static_cast<double>(total));
+        need = want < 1.0 ? 1ull : (want > static_cast<double>(total) ? total : static_cast<unsigned long long>(want));
+    }
+    if (tid == 0) {
+        *s_d = 0;
+        *s_above = 0;
+    }
+    __syncthreads();
+    const unsigned long long excl = incl - loc;
+    if (excl < need && need <= incl) {  // the crossing lies in this thread's digits
+        unsigned long long run = excl;
+        for (int j = 0; j < per; ++j) {
+            const int bin = nb - 1 - per * tid - j;
+            if (run + h[bin] >= need) {
+                *s_d = bin;
+                *s_above = run;
+                break;
+            }
+            run += h[bin];
+        }
+    }
+    __syncthreads();
+    d = *s_d;
+    above = *s_above;
+}
+
+__global__ __launch_bounds__(kFThreads) void accept_filter(AcceptArgs a) {
+    const int rid = blockIdx.x;  // request * N + node
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float* row = a.logits + static_cast<size_t>(rid) * a.V;
+    const bool vec4 = a.vec4 != 0;
+    __shared__ unsigned long long s_hist[2048];
+    __shared__ unsigned long long s_w[kFWaves];
+    __shared__ float s_m[kFWaves];
+    __shared__ int s_i[kFWaves];
+    __shared__ double s_sum[kFWaves];
+    __shared__ int s_d;
+    __shared__ unsigned long long s_above;
+
+    // Row max and its lowest index.
+    float best = -INFINITY;
+    int bi = 0x7fffffff;
+    for_row(row, a.V, vec4, [&](int x, float l) {
+        if (l > best) {
+            best = l;
+            bi = x;
+        }
+    });
+    wave_argmax(best, bi);
+    if (lane == 0) {
+        s_m[wave] = best;
+        s_i[wave] = bi;
+    }
+    __syncthreads();
+    float M = s_m[0];
+    int arg = s_i[0];
+    for (int k = 1; k < kFWaves; ++k)
+        if (s_m[k] > M || (s_m[k] == M && s_i[k] < arg)) {
+            M = s_m[k];
+            arg = s_i[k];
+        }
+    const float c2 = 1.4426950408889634f / a.T;
+
+    // Radix selection: three digits of the key, the candidates being the keys
+    // that match the digits fixed so far (and, for the nucleus, the top-k).
+    constexpr int kShift[3] = {21, 10, 0};
+    constexpr int kBits[3] = {11, 11, 10};
+    auto select_key = [&](bool by_mass, uint32_t floor_key, unsigned long long need, double need_frac) {
+        uint32_t prefix = 0u, pmask = 0u;
+        for (int r = 0; r < 3; ++r) {
+            const int nb = 1 << kBits[r];
+            for (int i = tid; i < nb; i += kFThreads) s_hist[i] = 0ull;
+            __syncthreads();
+            for_row(row, a.V, vec4, [&](int, float l) {
+                const uint32_t key = logit_key(l);
+                if ((key & pmask) == prefix && key >= floor_key) {
+                    const unsigned long long w =
+                        by_mass ? __float2ull_rn(__builtin_amdgcn_exp2f((l - M) * c2) * kFixedOne) : 1ull;
+                    atomicAdd(&s_hist[(key >> kShift[r]) & (nb - 1)], w);
+                }
+            });
+            __syncthreads();
+            int d;
+            unsigned long long above;
+            radix_step(s_hist, nb, need, r == 0 ? need_frac : 0.0, d, above, s_w, &s_d, &s_above);
+            need -= above;
+            prefix |= static_cast<uint32_t>(d) << kShift[r];
+            pmask |= static_cast<uint32_t>(nb - 1) << kShift[r];
+            __syncthreads();
+        }
+        return prefix;
+    };
+    uint32_t tau = 0u;
+    if (a.top_k > 0 && a.top_k < a.V) tau = select_key(false, 0u, static_cast<unsigned long long>(a.top_k), 0.0);
+    if (a.top_p < 1.f) tau = select_key(true, tau, 0ull, static_cast<double>(a.top_p));
+
+    // Kept mass, fp64 per thread.
+    double S = 0.0;
+    for_row(row, a.V, vec4, [&](int, float l) {
+        if (logit_key(l) >= tau) S += static_cast<double>(__builtin_amdgcn_exp2f((l - M) * c2));
+    });
+    S = wave_sum(S);
+    if (lane == 0) s_sum[wave] = S;
+    __syncthreads();
+    if (tid == 0) {
+        double tot = 0.0;
+        for (int k = 0; k < kFWaves; ++k) tot += s_sum[k];
+        RowRec rr;
+        rr.S = tot;
+        rr.M = M;
+        rr.tau = tau;
+        rr.arg = arg;
+        rr.pad = 0;
+        a.rowrec[rid] = rr;
+    }
+}
+
 AcceptPlan plan_accept(int B, int N, int V) {
     AcceptPlan p{};
     p.chunk = accept_ept(B, N, V) * kThreads;
@@ -933,19 +1180,23 @@ AcceptPlan plan_accept(int B, int N, int V) {
 
 int max_accept_vocab() { return kMaxChunks * 32 * kThreads; }
 
-template <int EPT>
+template <int EPT, bool FILT>
 static int launch_accept_ept(const AcceptArgs& a, const AcceptPlan& p, hipStream_t stream) {
-    if (a.N > 1) {
+    if (FILT) {  // every row's truncation (the stop row may be a leaf)
+        hipLaunchKernelGGL(accept_filter, dim3(a.B * a.N), dim3(kFThreads), 0, stream, a);
+        if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+    } else if (a.N > 1) {
         hipLaunchKernelGGL((accept_rowstats<EPT>), dim3(p.nchunk, a.N, a.B), dim3(kThreads), 0, stream, a);
         if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     }
     // Few rows need fewer registers for the decision: more workgroups per CU.
     if (a.N <= 16)
-        hipLaunchKernelGGL((accept_sample<EPT, 4>), dim3(p.nchunk, a.B), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((accept_sample<EPT, 4, FILT>), dim3(p.nchunk, a.B), dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL((accept_sample<EPT, kRowsPerWave>), dim3(p.nchunk, a.B), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((accept_sample<EPT, kRowsPerWave, FILT>), dim3(p.nchunk, a.B), dim3(kThreads), 0, stream,
+                           a);
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-    hipLaunchKernelGGL((accept_select<EPT>), dim3(a.B), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((accept_select<EPT, FILT>), dim3(a.B), dim3(kThreads), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     return SPEC_OK;
 }
@@ -954,7 +1205,7 @@ int launch_accept(int rule, int B, int N, int V, const float* logits, const floa
                   const int32_t* tokens, const int32_t* parent, const float* u_accept,
                   const float* u_sample, float temperature, float epsilon, float delta,
                   int32_t* accept_len, int32_t* path, int32_t* out_tokens, void* workspace,
-                  const AcceptPlan& p, hipStream_t stream) {
+                  const AcceptPlan& p, hipStream_t stream, int top_k, float top_p) {
     AcceptArgs a;
     a.logits = logits;
     a.draft = draft;
@@ -967,6 +1218,7 @@ int launch_accept(int rule, int B, int N, int V, const float* logits, const floa
     a.out_tokens = out_tokens;
     char* ws = static_cast<char*>(workspace);
     a.rowstat = reinterpret_cast<RowStat*>(ws + p.off_rowstat);
+    a.rowrec = reinterpret_cast<RowRec*>(ws + p.off_rowstat);  // B*N records fit in B*N*nchunk RowStats
     a.dec = reinterpret_cast<Decision*>(ws + p.off_dec);
     a.cstat = reinterpret_cast<ChunkStat*>(ws + p.off_cstat);
     a.B = B;
@@ -982,10 +1234,16 @@ int launch_accept(int rule, int B, int N, int V, const float* logits, const floa
     a.T = temperature;
     a.eps = epsilon;
     a.delta = delta;
+    a.top_k = top_k > 0 && top_k < V ? top_k : 0;
+    a.top_p = top_p < 1.f ? top_p : 1.f;
+    // Truncation applies to the rejection rule at T > 0 (at T = 0 the target
+    // is the argmax, which every truncation keeps).
+    const bool filt = rule == 0 && temperature > 0.f && (a.top_k > 0 || a.top_p < 1.f);
+    static_assert(sizeof(RowRec) <= sizeof(RowStat), "row records reuse the row-statistics space");
     switch (p.chunk / kThreads) {
-        case 8: return launch_accept_ept<8>(a, p, stream);
-        case 16: return launch_accept_ept<16>(a, p, stream);
-        default: return launch_accept_ept<32>(a, p, stream);
+        case 8: return filt ? launch_accept_ept<8, true>(a, p, stream) : launch_accept_ept<8, false>(a, p, stream);
+        case 16: return filt ? launch_accept_ept<16, true>(a, p, stream) : launch_accept_ept<16, false>(a, p, stream);
+        default: return filt ? launch_accept_ept<32, true>(a, p, stream) : launch_accept_ept<32, false>(a, p, stream);
     }
 }
 

@@ -86,6 +86,25 @@ int spec_accept_reject(int32_t batch, int32_t num_nodes, int32_t vocab, const fl
                          static_cast<hipStream_t>(stream));
 }
 
+int spec_accept_reject_filtered(int32_t batch, int32_t num_nodes, int32_t vocab, const float* target_logits,
+                                const float* draft_probs, const int32_t* tokens, const int32_t* parent,
+                                const float* u_accept, const float* u_sample, float temperature, int32_t top_k,
+                                float top_p, int32_t* accept_len, int32_t* path, int32_t* out_tokens,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    if (batch < 0 || top_k < 0 || !(top_p > 0.f && top_p <= 1.f)) return SPEC_EINVAL;
+    if (batch == 0) return SPEC_OK;
+    int rc = accept_common_checks(batch, num_nodes, vocab, target_logits, tokens, accept_len, path, out_tokens,
+                                  temperature);
+    if (rc != SPEC_OK) return rc;
+    if ((num_nodes > 1 && (!draft_probs || !u_accept)) || !u_sample) return SPEC_EINVAL;
+    if (static_cast<long long>(batch) * num_nodes > 0x7fffffffLL) return SPEC_EUNSUPPORTED;
+    const AcceptPlan plan = plan_accept(batch, num_nodes, vocab);
+    if (!workspace || workspace_bytes < plan.ws_bytes) return SPEC_EWORKSPACE;
+    return launch_accept(0, batch, num_nodes, vocab, target_logits, draft_probs, tokens, parent, u_accept,
+                         u_sample, temperature, 0.f, 0.f, accept_len, path, out_tokens, workspace, plan,
+                         static_cast<hipStream_t>(stream), top_k, top_p);
+}
+
 int spec_accept_typical(int32_t batch, int32_t num_nodes, int32_t vocab, const float* target_logits,
                         const int32_t* tokens, const int32_t* parent, float temperature, float epsilon,
                         float delta, int32_t* accept_len, int32_t* path, int32_t* out_tokens, void* workspace,

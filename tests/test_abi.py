@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     lib = sv.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -111,6 +111,23 @@ def test_accept_argument_errors():
     assert _typ(ws_bytes=lib.spec_accept_workspace_bytes(2, 6, 1000) - 8) == EWORKSPACE
     assert _rej(B=0) == OK and _typ(B=0) == OK
     assert lib.spec_accept_workspace_bytes(0, 6, 10) == 0
+
+
+def _filt(B=2, N=6, V=1000, T=1.0, k=5, p=0.9, ws_bytes=1 << 30):
+    return sv.lib().spec_accept_reject_filtered(B, N, V, FAKE, FAKE, FAKE, None, FAKE, FAKE, T, k, p, FAKE, FAKE,
+                                                FAKE, FAKE, ws_bytes, None)
+
+
+def test_filtered_accept_errors():
+    assert _filt(k=-1) == EINVAL
+    assert _filt(p=0.0) == EINVAL
+    assert _filt(p=1.5) == EINVAL
+    assert _filt(p=float("nan")) == EINVAL
+    assert _filt(T=-1.0) == EINVAL
+    assert _filt(V=0) == EINVAL
+    assert _filt(N=65) == EINVAL
+    assert _filt(ws_bytes=sv.lib().spec_accept_workspace_bytes(2, 6, 1000) - 1) == EWORKSPACE
+    assert _filt(B=0) == OK
 
 
 def test_commit_and_helper_errors():

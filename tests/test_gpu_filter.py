@@ -1,0 +1,99 @@
+"""GPU parity of rejection-rule acceptance on a top-k / nucleus truncated
+target ("Speculative Sampling" section of the blog page "Fast Inference from
+Transformers via Speculative Decoding": top-k and nucleus sampling may
+transform the probabilities before the rule), through the C ABI, against
+the oracle on the same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import speculative_decoding_verification_tree_amd as sv
+from workloads import scaled, generate
+from tests.gpu_helpers import announce, check_accept, f32
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(w):
+    return dict(lg=torch.from_numpy(w.target_logits).cuda(), dp=torch.from_numpy(w.draft_probs).cuda(),
+                tk=torch.from_numpy(w.tokens).cuda(), ua=torch.from_numpy(w.u_accept).cuda(),
+                us=torch.from_numpy(w.u_sample).cuda(),
+                par=None if w.is_chain else torch.from_numpy(w.parent).cuda())
+
+
+def _run(w, d, k, p, T=None):
+    T = w.temperature if T is None else T
+    al, path, out = sv.spec_accept_reject_filtered(d["lg"], d["dp"], d["tk"], d["par"], d["ua"], d["us"], T,
+                                                   top_k=k, top_p=p)
+    torch.cuda.synchronize()
+    return dict(accept_len=al.cpu().numpy(), path=path.cpu().numpy(), out_tokens=out.cpu().numpy())
+
+
+def _ref(w, k, p, T=None):
+    T = w.temperature if T is None else T
+    return oracle.accept("reject", w.target_logits, w.tokens, None if w.is_chain else w.parent, f32(T),
+                         w.draft_probs, w.u_accept, w.u_sample, top_k=k, top_p=f32(p))
+
+
+def _kept_topk(row, k):
+    return row >= np.sort(row)[::-1][k - 1]
+
+
+CASES = [
+    # (config, overrides, top_k, top_p)
+    (2, dict(batch=12), 50, 1.0),
+    (2, dict(batch=12), 0, 0.9),
+    (2, dict(batch=12), 200, 0.8),
+    (4, dict(batch=16, prefix_len=(10, 40)), 20, 0.95),
+    (4, dict(batch=16, prefix_len=(10, 40)), 1, 1.0),            # top-1: greedy
+    (5, dict(batch=4, prefix_len=(0, 8)), 100, 1.0),             # 64-node tree
+    (5, dict(batch=4, prefix_len=(0, 8), vocab=5000), 0, 0.5),  # tree, small vocabulary
+    (1, dict(batch=32, vocab=1001), 7, 0.7),                     # V % 4 != 0 (scalar loads)
+    (1, dict(batch=16, drafts=0), 3, 1.0),                       # N = 1: bonus only
+]
+
+
+@pytest.mark.parametrize("cid,over,k,p", CASES)
+def test_filtered_accept_matches_oracle(cid, over, k, p):
+    w = generate(scaled(cid, **over), with_attention=False)
+    announce(f"filtered accept cfg{cid} {over} top_k={k} top_p={p} B={w.B} N={w.N} V={w.V}")
+    d = _dev(w)
+    gpu = _run(w, d, k, p)
+    ref = _ref(w, k, p)
+    excl = check_accept(w, gpu, ref)
+    announce(f"  near-tie requests excluded: {excl} of {w.B}")
+    assert excl <= max(2, w.B // 8), excl
+    # the last token always lies in the top-k set of the stop row
+    if k > 0:
+        for b in range(w.B):
+            a = int(gpu["accept_len"][b])
+            v = int(gpu["path"][b][a])
+            assert _kept_topk(w.target_logits[b, v], k)[gpu["out_tokens"][b][a]], b
+    # deterministic: a second call gives the same bits
+    again = _run(w, d, k, p)
+    for key in gpu:
+        np.testing.assert_array_equal(again[key], gpu[key])
+
+
+def test_filters_off_equal_plain_rule():
+    w = generate(scaled(4, batch=24, prefix_len=(10, 40)), with_attention=False)
+    announce("filtered accept with filters off vs plain rule")
+    d = _dev(w)
+    plain = sv.spec_accept_reject(d["lg"], d["dp"], d["tk"], d["par"], d["ua"], d["us"], w.temperature)
+    torch.cuda.synchronize()
+    for k, p in ((0, 1.0), (w.V, 1.0)):
+        got = _run(w, d, k, p)
+        for key, t in zip(("accept_len", "path", "out_tokens"), plain):
+            np.testing.assert_array_equal(got[key], t.cpu().numpy())
+
+
+def test_filters_at_temperature_zero_are_greedy():
+    w = generate(scaled(2, batch=10), with_attention=False)
+    announce("filtered accept at T = 0")
+    d = _dev(w)
+    greedy = _run(w, d, 0, 1.0, T=0.0)
+    got = _run(w, d, 5, 0.5, T=0.0)
+    for key in got:
+        np.testing.assert_array_equal(got[key], greedy[key])
+    check_accept(w, got, _ref(w, 0, 1.0, T=0.0))
