@@ -184,6 +184,15 @@ def main():
         else:
             sv.spec_tree_rope(c["q"], c["k"], c["pl"], c["parent"], rope_base)
 
+    # The rejection rule on a truncated target (top-k, then nucleus), timed on
+    # its own for rejection-rule workloads.
+    filt_k, filt_p = 50, 0.9
+
+    def accept_filtered(c):
+        sv.spec_accept_reject_filtered(c["logits"], c["draft"], c["tokens"], c["parent"], c["ua"], c["us"],
+                                       w.temperature, filt_k, filt_p, c["al"], c["path"], c["otok"],
+                                       workspace=acc_ws)
+
     # eager warm-up (also checks every call returns SPEC_OK)
     for i in range(max(args.warmup, ncopies)):
         step(copies[i % ncopies])
@@ -204,7 +213,14 @@ def main():
     g_acc = capture([accept])
     g_commit = capture([commit])
     g_rope = capture([tree_rope])
-    for g in (g_step, g_attn, g_acc, g_commit, g_rope):
+    graphs = [g_step, g_attn, g_acc, g_commit, g_rope]
+    g_filt = None
+    if w.rule == "reject" and w.temperature > 0:
+        for i in range(ncopies):
+            accept_filtered(copies[i])
+        g_filt = capture([accept_filtered])
+        graphs.append(g_filt)
+    for g in graphs:
         g.replay()
     torch.cuda.synchronize()
 
@@ -225,6 +241,10 @@ def main():
     accept_ms = timed(g_acc, reps)
     commit_ms = timed(g_commit, reps)
     rope_ms = timed(g_rope, reps)
+    filt_ms = timed(g_filt, reps) if g_filt is not None else None
+    # every target row once (leaf rows too: the stop row may be one), plus the
+    # stop row and one draft row per request for the residual
+    filt_bytes = (B * N * V + 2 * B * V) * 4
     esz = 2 if bf16 else 4
     rope_bytes = 2 * (B * N * w.Hq * w.D + B * w.Hkv * N * w.D) * esz  # read + write, q and tree K rows
 
@@ -293,6 +313,10 @@ def main():
                       "achieved_GBs": rope_bytes / (rope_ms * 1e-3) / 1e9,
                       "calls": ("spec_medusa_tree + " if cartesian else "") + "spec_tree_rope",
                       "note": "before the path; not part of ms_per_step"},
+        "filtered_accept": None if filt_ms is None else {
+            "us": filt_ms * 1e3, "top_k": filt_k, "top_p": filt_p, "bytes": filt_bytes,
+            "achieved_GBs": filt_bytes / (filt_ms * 1e-3) / 1e9, "calls": "spec_accept_reject_filtered",
+            "note": "the rejection rule on the top-k / nucleus truncated target; not part of ms_per_step"},
         "roofline": {
             "bound": "hbm",
             "kernel": "spec_verify_attn",

@@ -973,8 +973,9 @@ static int accept_ept(int B, int N, int V) {
 // largest key, so ties with it are kept); for the nucleus, masses
 // 2^((l - M) * log2(e) / T) in 2^-44 fixed point (integer sums, independent
 // of the order of the atomics), the key at which the mass from the top first
-// reaches top_p of the top-k mass.
-constexpr int kFThreads = 512;
+// reaches top_p of the top-k mass.  Every histogram also sums the
+// fixed-point masses, so the kept mass comes out of the selection itself.
+constexpr int kFThreads = 1024;
 constexpr int kFWaves = kFThreads / 64;
 constexpr int kFUnroll = 8;
 constexpr float kFixedOne = 17592186044416.0f;  // 2^44
@@ -1077,11 +1078,10 @@ __global__ __launch_bounds__(kFThreads) void accept_filter(AcceptArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float* row = a.logits + static_cast<size_t>(rid) * a.V;
     const bool vec4 = a.vec4 != 0;
-    __shared__ unsigned long long s_hist[2048];
+    __shared__ unsigned long long s_cnt[2048], s_mass[2048];
     __shared__ unsigned long long s_w[kFWaves];
     __shared__ float s_m[kFWaves];
     __shared__ int s_i[kFWaves];
-    __shared__ double s_sum[kFWaves];
     __shared__ int s_d;
     __shared__ unsigned long long s_above;
 
@@ -1110,28 +1110,46 @@ __global__ __launch_bounds__(kFThreads) void accept_filter(AcceptArgs a) {
     const float c2 = 1.4426950408889634f / a.T;
 
     // Radix selection: three digits of the key, the candidates being the keys
-    // that match the digits fixed so far (and, for the nucleus, the top-k).
+    // that match the digits fixed so far and are >= floor_key.  by_mass picks
+    // the key where the mass from the top reaches need (need_frac of the
+    // candidates' mass), else where the count does.  kept receives the
+    // fixed-point mass of the candidates >= the selected key.
     constexpr int kShift[3] = {21, 10, 0};
     constexpr int kBits[3] = {11, 11, 10};
-    auto select_key = [&](bool by_mass, uint32_t floor_key, unsigned long long need, double need_frac) {
+    auto select_key = [&](bool by_mass, uint32_t floor_key, unsigned long long need, double need_frac,
+                          unsigned long long& kept) {
         uint32_t prefix = 0u, pmask = 0u;
+        kept = 0ull;
         for (int r = 0; r < 3; ++r) {
             const int nb = 1 << kBits[r];
-            for (int i = tid; i < nb; i += kFThreads) s_hist[i] = 0ull;
+            for (int i = tid; i < nb; i += kFThreads) {
+                s_cnt[i] = 0ull;
+                s_mass[i] = 0ull;
+            }
             __syncthreads();
             for_row(row, a.V, vec4, [&](int, float l) {
                 const uint32_t key = logit_key(l);
                 if ((key & pmask) == prefix && key >= floor_key) {
-                    const unsigned long long w =
-                        by_mass ? __float2ull_rn(__builtin_amdgcn_exp2f((l - M) * c2) * kFixedOne) : 1ull;
-                    atomicAdd(&s_hist[(key >> kShift[r]) & (nb - 1)], w);
+                    const int bin = (key >> kShift[r]) & (nb - 1);
+                    atomicAdd(&s_mass[bin], __float2ull_rn(__builtin_amdgcn_exp2f((l - M) * c2) * kFixedOne));
+                    if (!by_mass) atomicAdd(&s_cnt[bin], 1ull);
                 }
             });
             __syncthreads();
             int d;
             unsigned long long above;
-            radix_step(s_hist, nb, need, r == 0 ? need_frac : 0.0, d, above, s_w, &s_d, &s_above);
+            radix_step(by_mass ? s_mass : s_cnt, nb, need, r == 0 ? need_frac : 0.0, d, above, s_w, &s_d, &s_above);
             need -= above;
+            if (by_mass) {
+                kept += above;
+            } else {  // the mass of the digits above d
+                unsigned long long mine = 0ull, tot;
+                for (int i = tid; i < nb; i += kFThreads)
+                    if (i > d) mine += s_mass[i];
+                (void)block_incl_scan_u64(mine, s_w, tot);
+                kept += tot;
+            }
+            if (r == 2) kept += s_mass[d];
             prefix |= static_cast<uint32_t>(d) << kShift[r];
             pmask |= static_cast<uint32_t>(nb - 1) << kShift[r];
             __syncthreads();
@@ -1139,22 +1157,13 @@ __global__ __launch_bounds__(kFThreads) void accept_filter(AcceptArgs a) {
         return prefix;
     };
     uint32_t tau = 0u;
-    if (a.top_k > 0 && a.top_k < a.V) tau = select_key(false, 0u, static_cast<unsigned long long>(a.top_k), 0.0);
-    if (a.top_p < 1.f) tau = select_key(true, tau, 0ull, static_cast<double>(a.top_p));
+    unsigned long long kept = 0ull;
+    if (a.top_k > 0 && a.top_k < a.V) tau = select_key(false, 0u, static_cast<unsigned long long>(a.top_k), 0.0, kept);
+    if (a.top_p < 1.f) tau = select_key(true, tau, 0ull, static_cast<double>(a.top_p), kept);
 
-    // Kept mass, fp64 per thread.
-    double S = 0.0;
-    for_row(row, a.V, vec4, [&](int, float l) {
-        if (logit_key(l) >= tau) S += static_cast<double>(__builtin_amdgcn_exp2f((l - M) * c2));
-    });
-    S = wave_sum(S);
-    if (lane == 0) s_sum[wave] = S;
-    __syncthreads();
     if (tid == 0) {
-        double tot = 0.0;
-        for (int k = 0; k < kFWaves; ++k) tot += s_sum[k];
         RowRec rr;
-        rr.S = tot;
+        rr.S = static_cast<double>(kept) * (1.0 / 17592186044416.0);  // 2^-44
         rr.M = M;
         rr.tau = tau;
         rr.arg = arg;
