@@ -50,10 +50,15 @@ def parse():
     return ap.parse_args()
 
 
+ATTN_SOURCES = ("attn.hip", "spec_common.h", "spec_internal.h")  # what the spec_verify_attn kernels compile from
+
+
 def kernel_source_hash():
+    """Hash of the attention kernels' sources: the stored traffic counters
+    describe a spec_verify_attn call and stay valid while these are unchanged."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "speculative_decoding_verification_tree_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in ATTN_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
