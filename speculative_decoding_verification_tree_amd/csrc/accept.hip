@@ -1073,19 +1073,53 @@ __device__ __forceinline__ void radix_step(const unsigned long long* h, int nb, 
     above = *s_above;
 }
 
+// Inverse of logit_key.
+__device__ __forceinline__ float key_logit(uint32_t key) {
+    return __uint_as_float(key ^ ((key >> 31) ? 0x80000000u : 0xFFFFFFFFu));
+}
+
+// Appends key to cand when match holds (wave-aggregated: one LDS atomic per
+// wave); positions past cap are counted but not stored.
+__device__ __forceinline__ void append_key(bool match, uint32_t key, uint32_t* cand, int* s_n, int cap) {
+    const uint64_t m = __ballot(match);
+    if (m == 0ull) return;
+    const int lane = threadIdx.x & 63, leader = __ffsll(static_cast<long long>(m)) - 1;
+    int base = 0;
+    if (lane == leader) base = atomicAdd(s_n, __popcll(m));
+    base = __shfl(base, leader);
+    const int off = __popcll(m & ((1ull << lane) - 1ull));
+    if (match && base + off < cap) cand[base + off] = key;
+}
+
+constexpr int kFCand = 16384;  // LDS candidate keys (64 KB)
+
 __global__ __launch_bounds__(kFThreads) void accept_filter(AcceptArgs a) {
     const int rid = blockIdx.x;  // request * N + node
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float* row = a.logits + static_cast<size_t>(rid) * a.V;
     const bool vec4 = a.vec4 != 0;
     __shared__ unsigned long long s_cnt[2048], s_mass[2048];
+    __shared__ uint32_t s_cand[kFCand];
     __shared__ unsigned long long s_w[kFWaves];
     __shared__ float s_m[kFWaves];
     __shared__ int s_i[kFWaves];
-    __shared__ int s_d;
+    __shared__ int s_d, s_n;
     __shared__ unsigned long long s_above;
+    const bool use_k = a.top_k > 0 && a.top_k < a.V, use_p = a.top_p < 1.f;
+    constexpr int kShift[3] = {21, 10, 0};
+    constexpr int kBits[3] = {11, 11, 10};
+    auto clear = [&](int nb) {
+        for (int i = tid; i < nb; i += kFThreads) {
+            s_cnt[i] = 0ull;
+            s_mass[i] = 0ull;
+        }
+    };
 
-    // Row max and its lowest index.
+    // Pass 1: the row max with its lowest index and, for top-k, the first
+    // digit's count histogram (counts need no max).
+    clear(2048);
+    if (tid == 0) s_n = 0;
+    __syncthreads();
     float best = -INFINITY;
     int bi = 0x7fffffff;
     for_row(row, a.V, vec4, [&](int x, float l) {
@@ -1093,6 +1127,7 @@ __global__ __launch_bounds__(kFThreads) void accept_filter(AcceptArgs a) {
             best = l;
             bi = x;
         }
+        if (use_k) atomicAdd(&s_cnt[logit_key(l) >> kShift[0]], 1ull);
     });
     wave_argmax(best, bi);
     if (lane == 0) {
@@ -1108,33 +1143,32 @@ __global__ __launch_bounds__(kFThreads) void accept_filter(AcceptArgs a) {
             arg = s_i[k];
         }
     const float c2 = 1.4426950408889634f / a.T;
+    auto mass_of = [&](float l) { return __float2ull_rn(__builtin_amdgcn_exp2f((l - M) * c2) * kFixedOne); };
 
-    // Radix selection: three digits of the key, the candidates being the keys
-    // that match the digits fixed so far and are >= floor_key.  by_mass picks
-    // the key where the mass from the top reaches need (need_frac of the
-    // candidates' mass), else where the count does.  kept receives the
-    // fixed-point mass of the candidates >= the selected key.
-    constexpr int kShift[3] = {21, 10, 0};
-    constexpr int kBits[3] = {11, 11, 10};
-    auto select_key = [&](bool by_mass, uint32_t floor_key, unsigned long long need, double need_frac,
-                          unsigned long long& kept) {
-        uint32_t prefix = 0u, pmask = 0u;
-        kept = 0ull;
-        for (int r = 0; r < 3; ++r) {
+    // The remaining digits of a selection, from round r0 on, over the keys
+    // matching (prefix, pmask) and >= floor_key: from the LDS candidates when
+    // they all fit (n <= kFCand), else from the row.  by_mass selects where the
+    // mass from the top reaches need, else where the count does.  Adds to kept
+    // the mass of the candidates >= the selected key.
+    auto finish = [&](int r0, uint32_t prefix, uint32_t pmask, bool by_mass, uint32_t floor_key,
+                      unsigned long long need, int n, unsigned long long& kept, double need_frac) {
+        const bool lds = n <= kFCand;
+        for (int r = r0; r < 3; ++r) {
             const int nb = 1 << kBits[r];
-            for (int i = tid; i < nb; i += kFThreads) {
-                s_cnt[i] = 0ull;
-                s_mass[i] = 0ull;
-            }
+            clear(nb);
             __syncthreads();
-            for_row(row, a.V, vec4, [&](int, float l) {
-                const uint32_t key = logit_key(l);
+            auto add = [&](uint32_t key, float l) {
                 if ((key & pmask) == prefix && key >= floor_key) {
                     const int bin = (key >> kShift[r]) & (nb - 1);
-                    atomicAdd(&s_mass[bin], __float2ull_rn(__builtin_amdgcn_exp2f((l - M) * c2) * kFixedOne));
+                    atomicAdd(&s_mass[bin], mass_of(l));
                     if (!by_mass) atomicAdd(&s_cnt[bin], 1ull);
                 }
-            });
+            };
+            if (lds) {
+                for (int i = tid; i < n; i += kFThreads) add(s_cand[i], key_logit(s_cand[i]));
+            } else {
+                for_row(row, a.V, vec4, [&](int, float l) { add(logit_key(l), l); });
+            }
             __syncthreads();
             int d;
             unsigned long long above;
@@ -1142,7 +1176,7 @@ __global__ __launch_bounds__(kFThreads) void accept_filter(AcceptArgs a) {
             need -= above;
             if (by_mass) {
                 kept += above;
-            } else {  // the mass of the digits above d
+            } else {
                 unsigned long long mine = 0ull, tot;
                 for (int i = tid; i < nb; i += kFThreads)
                     if (i > d) mine += s_mass[i];
@@ -1156,10 +1190,68 @@ __global__ __launch_bounds__(kFThreads) void accept_filter(AcceptArgs a) {
         }
         return prefix;
     };
+    // Pass over the row collecting the keys of first digit d0 (>= floor_key;
+    // with also_above every digit >= d0) into LDS and summing the mass of the
+    // keys above digit d0.
+    auto collect = [&](int d0, uint32_t floor_key, bool also_above, unsigned long long& mass_above) {
+        if (tid == 0) s_n = 0;
+        __syncthreads();
+        unsigned long long mine = 0ull;
+        for_row(row, a.V, vec4, [&](int, float l) {
+            const uint32_t key = logit_key(l);
+            const int dig = static_cast<int>(key >> kShift[0]);
+            if (dig > d0 && key >= floor_key) mine += mass_of(l);
+            append_key((also_above ? dig >= d0 : dig == d0) && key >= floor_key, key, s_cand, &s_n, kFCand);
+        });
+        unsigned long long tot;
+        (void)block_incl_scan_u64(mine, s_w, tot);  // (its barriers also publish s_n)
+        mass_above = tot;
+        return s_n;
+    };
+
     uint32_t tau = 0u;
     unsigned long long kept = 0ull;
-    if (a.top_k > 0 && a.top_k < a.V) tau = select_key(false, 0u, static_cast<unsigned long long>(a.top_k), 0.0, kept);
-    if (a.top_p < 1.f) tau = select_key(true, tau, 0ull, static_cast<double>(a.top_p), kept);
+    int n_k = kFCand + 1;  // keys >= the top-k threshold held in LDS (when <= kFCand)
+    if (use_k) {
+        // first digit from the pass-1 counts, then the rest from its keys;
+        // with a nucleus to follow, the keys above the digit (fewer than k)
+        // are collected too, so that the nucleus needs no further pass
+        unsigned long long need = static_cast<unsigned long long>(a.top_k);
+        int d0;
+        unsigned long long above;
+        radix_step(s_cnt, 2048, need, 0.0, d0, above, s_w, &s_d, &s_above);
+        need -= above;
+        unsigned long long mass_above;
+        const int n = collect(d0, 0u, use_p, mass_above);
+        kept = mass_above;
+        tau = finish(1, static_cast<uint32_t>(d0) << kShift[0], 0x7FFu << kShift[0], false, 0u, need, n, kept, 0.0);
+        if (use_p) n_k = n;
+    }
+    if (use_p && n_k <= kFCand) {
+        // the nucleus over the top-k-kept keys, all in LDS
+        kept = 0ull;
+        tau = finish(0, 0u, 0u, true, tau, 0ull, n_k, kept, static_cast<double>(a.top_p));
+    } else if (use_p) {
+        // first digit from a mass histogram of the top-k-kept keys
+        clear(2048);
+        __syncthreads();
+        const uint32_t floor_key = tau;
+        for_row(row, a.V, vec4, [&](int, float l) {
+            const uint32_t key = logit_key(l);
+            if (key >= floor_key) atomicAdd(&s_mass[key >> kShift[0]], mass_of(l));
+        });
+        __syncthreads();
+        unsigned long long need = 0ull;
+        int d0;
+        unsigned long long above;
+        radix_step(s_mass, 2048, need, static_cast<double>(a.top_p), d0, above, s_w, &s_d, &s_above);
+        need -= above;
+        unsigned long long mass_above;
+        const int n = collect(d0, floor_key, false, mass_above);
+        kept = mass_above;
+        tau = finish(1, static_cast<uint32_t>(d0) << kShift[0], 0x7FFu << kShift[0], true, floor_key, need, n, kept,
+                     0.0);
+    }
 
     if (tid == 0) {
         RowRec rr;

@@ -97,3 +97,35 @@ def test_filters_at_temperature_zero_are_greedy():
     for key in got:
         np.testing.assert_array_equal(got[key], greedy[key])
     check_accept(w, got, _ref(w, 0, 1.0, T=0.0))
+
+
+@pytest.mark.parametrize("kind,k,p", [
+    ("near_uniform", 1000, 1.0),   # every key in one first digit: more candidates than LDS holds
+    ("dense_top", 0, 0.5),         # nucleus boundary inside a first digit holding 20000 keys
+    ("dense_top", 30000, 0.8),     # top-k set larger than LDS holds, then the nucleus from the row
+    ("quantised", 100, 1.0),       # four distinct logits: ~32k tokens tie with the 100th largest
+    ("quantised", 100, 0.6),
+])
+def test_filtered_accept_dense_bins(kind, k, p):
+    # Near-uniform masses would put nucleus and draw boundaries within the
+    # near-tie band everywhere; these shapes keep the masses distinct.
+    w = generate(scaled(2, batch=6), with_attention=False)
+    rng = np.random.default_rng(7)
+    shape = w.target_logits.shape
+    if kind == "near_uniform":
+        w.target_logits[:] = rng.uniform(0.0, 0.01, size=shape).astype(np.float32)
+    elif kind == "dense_top":
+        lg = rng.standard_normal(shape).astype(np.float32)
+        for b in range(shape[0]):
+            for i in range(shape[1]):
+                top = rng.choice(shape[2], 20000, replace=False)
+                lg[b, i, top] = rng.uniform(8.0, 10.0, size=20000).astype(np.float32)
+        w.target_logits[:] = lg
+    else:
+        w.target_logits[:] = rng.integers(0, 4, size=shape).astype(np.float32)
+    announce(f"filtered accept, {kind} logits, top_k={k} top_p={p}")
+    d = _dev(w)
+    gpu = _run(w, d, k, p)
+    excl = check_accept(w, gpu, _ref(w, k, p))
+    announce(f"  near-tie requests excluded: {excl} of {w.B}")
+    assert excl <= 2, excl
