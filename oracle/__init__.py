@@ -45,6 +45,8 @@ def _load():
         lib.oracle_accept.restype = I
         lib.oracle_accept_ex.argtypes = [I, I, I, I, P, P, P, P, P, P, D, D, D, I, D, P, P, P, P, P]
         lib.oracle_accept_ex.restype = I
+        lib.oracle_accept_multidraft.argtypes = [I, I, I, P, P, P, P, P, P, D, P, P, P, P, P]
+        lib.oracle_accept_multidraft.restype = I
         lib.oracle_commit.argtypes = [I, I, I, I, I, P, P, P, P, P]
         lib.oracle_commit.restype = I
         lib.oracle_medusa_tree.argtypes = [I, I, P, I, I, P, P, P, P]
@@ -122,6 +124,32 @@ def accept(rule, target_logits, tokens, parent, temperature, draft_probs=None, u
                                   _ptr(acc), _ptr(path), _ptr(out), _ptr(margin), _ptr(stop))
     if rc != 0:
         raise ValueError("oracle_accept rejected its arguments")
+    return dict(accept_len=acc, path=path, out_tokens=out, margin=margin, stop=stop)
+
+
+def accept_multidraft(target_logits, tokens, parent, temperature, draft_probs, u_accept, u_sample):
+    """Rejection over a tree by recursive residuals (children tested in index
+    order, each against the residual of its rejected elder siblings); fp64.
+
+    Returns dict(accept_len, path, out_tokens, margin, stop) as accept().
+    """
+    B, N, V = target_logits.shape
+    lg = _c(target_logits, np.float32)
+    dp = _c(draft_probs, np.float32)
+    tk = _c(tokens, np.int32)
+    par = _c(parent, np.int32)
+    ua = _c(u_accept, np.float32)
+    us = _c(u_sample, np.float32)
+    acc = np.empty(B, np.int32)
+    path = np.empty((B, N), np.int32)
+    out = np.empty((B, N), np.int32)
+    margin = np.empty(B, np.float64)
+    stop = np.empty(B, np.int32)
+    rc = _load().oracle_accept_multidraft(B, N, V, _ptr(lg), _ptr(dp), _ptr(tk), _ptr(par), _ptr(ua), _ptr(us),
+                                          float(temperature), _ptr(acc), _ptr(path), _ptr(out), _ptr(margin),
+                                          _ptr(stop))
+    if rc != 0:
+        raise ValueError("oracle_accept_multidraft rejected its arguments")
     return dict(accept_len=acc, path=path, out_tokens=out, margin=margin, stop=stop)
 
 

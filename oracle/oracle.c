@@ -435,6 +435,93 @@ int oracle_accept(int B, int N, int V, int rule, const float* logits, const floa
 }
 
 /* ---------------------------------------------------------------------------
+ * Rejection over a tree with several drafts per node, by recursive residuals
+ * (a reading: the pages give the single-draft rule and say that tree
+ * candidates can reuse it, without a multi-draft scheme).  Per request b,
+ * starting at the root v = 0:
+ *   r = p_v = softmax(l_v / T);
+ *   for the children c of v in ascending index, token x = tokens[c]:
+ *     accept c iff u_accept[c] * q_c(x) < r(x); then v = c and repeat;
+ *     else r = norm(max(0, r - q_c)) (r unchanged if that is all zero);
+ *   every child rejected: final = draw(r, u_sample[v]); v a leaf: final =
+ *   draw(p_v, u_sample[v]).
+ * Each step emits a token distributed as p_v when the children's tokens are
+ * drawn from their q (this is the point of the residual chain), and on a
+ * chain the rule is the single-draft rule.  Outputs and margin as
+ * oracle_accept (margins |min(1, r/q) - u| of the tests taken, and the draw).
+ * ------------------------------------------------------------------------- */
+int oracle_accept_multidraft(int B, int N, int V, const float* logits, const float* draft,
+                             const int32_t* tokens, const int32_t* parent, const float* u_accept,
+                             const float* u_sample, double T, int32_t* accept_len, int32_t* path,
+                             int32_t* out_tokens, double* margin, int32_t* stop) {
+    if (B < 0 || N < 1 || N > 64 || V < 1 || !(T >= 0.0)) return -1;
+    if (N > 1 && !draft) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+        int par[64];
+        for (int i = 0; i < N; ++i) par[i] = parent_of(parent, N, b, i);
+        double* p = (double*)malloc(sizeof(double) * (size_t)V);
+        double* r = (double*)malloc(sizeof(double) * (size_t)V);
+        double* t = (double*)malloc(sizeof(double) * (size_t)V);
+        int32_t* pth = path + (size_t)b * N;
+        int32_t* ot = out_tokens + (size_t)b * N;
+        for (int i = 0; i < N; ++i) pth[i] = ot[i] = -1;
+        pth[0] = 0;
+        double mg = INFINITY;
+        int v = 0, a = 0, final = -1;
+        for (;;) {
+            target_probs(logits + ((size_t)b * N + v) * V, V, T, p);
+            for (int x = 0; x < V; ++x) r[x] = p[x];
+            int next = -1, any_child = 0;
+            for (int c = 1; c < N && next < 0; ++c) {
+                if (par[c] != v) continue;
+                any_child = 1;
+                const int x = tokens[(size_t)b * N + c];
+                const float* qc = draft + ((size_t)b * N + c) * V;
+                const double qx = qc[x], ua = u_accept[(size_t)b * N + c];
+                const double ratio = qx > 0.0 ? r[x] / qx : (r[x] > 0.0 ? INFINITY : 0.0);
+                const double d = fabs(fmin(1.0, ratio) - ua);
+                if (d < mg) mg = d;
+                if (ua * qx < r[x]) {
+                    next = c;
+                    break;
+                }
+                double Z = 0.0;
+                for (int y = 0; y < V; ++y) {
+                    const double e = r[y] - (double)qc[y];
+                    t[y] = e > 0.0 ? e : 0.0;
+                    Z += t[y];
+                }
+                if (Z > 0.0)
+                    for (int y = 0; y < V; ++y) r[y] = t[y] / Z;
+            }
+            if (next >= 0) {
+                v = next;
+                ++a;
+                pth[a] = v;
+                ot[a - 1] = tokens[(size_t)b * N + v];
+                continue;
+            }
+            double S = 0.0;
+            for (int x = 0; x < V; ++x) S += r[x];
+            double dm;
+            final = draw(r, V, S, (double)u_sample[(size_t)b * N + v], &dm);
+            if (dm < mg) mg = dm;
+            (void)any_child;
+            break;
+        }
+        ot[a] = final;
+        accept_len[b] = a;
+        if (margin) margin[b] = mg;
+        if (stop) stop[b] = v;
+        free(p);
+        free(r);
+        free(t);
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
  * Commit: for every request b and kv-head, the accepted path's rows
  * L_b + path[d] (d = 0..a) move to L_b + d; every source row is read before
  * any row is written.  prefix_len[b] becomes L_b + a + 1.  row_bytes = D *
