@@ -138,6 +138,30 @@ int spec_accept_reject_filtered(int32_t batch, int32_t num_nodes, int32_t vocab,
                                 float top_p, int32_t* accept_len, int32_t* path, int32_t* out_tokens,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Rejection over a tree with several drafts per node, by recursive
+ * residuals (a reading: the "Speculative Sampling" section gives the
+ * single-draft rule and the MEDUSA section says tree candidates can reuse
+ * it, with no multi-draft scheme).  Starting at the root v, with r = p_v
+ * (p as in spec_accept_reject): the children c of v are tested in ascending
+ * index, c with token x passing when u_accept[b][c] * q_c(x) < r(x); a
+ * rejected child replaces r by norm(max(0, r - q_c)) (r is kept if that is
+ * all zero) and the next child is tested against it.  The first passing
+ * child becomes v and the walk repeats from it.  When every child of v is
+ * rejected the last token is drawn from r, and at a leaf from p_v (inverse
+ * CDF, ascending token ids, uniform u_sample[b][v]).  Each emitted token is
+ * then distributed as the target when every child's token was drawn from its
+ * q (siblings may share one q, drawn i.i.d.), which the single-residual rule
+ * of spec_accept_reject does not give for nodes with several children.  On
+ * a chain both rules agree.  Arguments and outputs as spec_accept_reject;
+ * workspace >= spec_accept_multidraft_workspace_bytes(batch, vocab) (two
+ * residual rows per request; contents need no initialisation). */
+size_t spec_accept_multidraft_workspace_bytes(int32_t batch, int32_t vocab);
+int spec_accept_multidraft(int32_t batch, int32_t num_nodes, int32_t vocab, const float* target_logits,
+                           const float* draft_probs, const int32_t* tokens, const int32_t* parent,
+                           const float* u_accept, const float* u_sample, float temperature, int32_t* accept_len,
+                           int32_t* path, int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* Typical acceptance (MEDUSA section, typical-acceptance paragraph of the
  * same page).  Node i >= 1 with parent u and token x passes when
  * p_u(x) > min(epsilon, delta * exp(-H(p_u))), H in nats with p_u =

@@ -8,6 +8,8 @@ include/spec_verify.h.  This package is the thin PyTorch binding of that ABI.
 from .api import (
     SpecError,
     attn_desc,
+    spec_accept_multidraft,
+    spec_accept_multidraft_workspace_bytes,
     spec_accept_reject,
     spec_accept_reject_filtered,
     spec_accept_typical,
@@ -24,7 +26,8 @@ from .api import (
 from ._native import LIB_PATH, SIGNATURES, lib, status_string
 
 __all__ = [
-    "SpecError", "attn_desc", "spec_accept_reject", "spec_accept_reject_filtered", "spec_accept_typical", "spec_accept_workspace_bytes",
+    "SpecError", "attn_desc", "spec_accept_multidraft", "spec_accept_multidraft_workspace_bytes", "spec_accept_reject",
+    "spec_accept_reject_filtered", "spec_accept_typical", "spec_accept_workspace_bytes",
     "spec_commit_kv", "spec_medusa_tree", "spec_medusa_tree_nodes", "spec_tree_positions", "spec_tree_rope",
     "spec_validate_tree", "spec_verify_attn",
     "spec_verify_attn_workspace_bytes", "LIB_PATH", "SIGNATURES", "lib", "status_string",

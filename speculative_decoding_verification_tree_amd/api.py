@@ -153,6 +153,33 @@ def spec_accept_reject_filtered(target_logits, draft_probs, tokens, parent, u_ac
     return accept_len, path, out_tokens
 
 
+def spec_accept_multidraft_workspace_bytes(batch, vocab):
+    return int(_native.lib().spec_accept_multidraft_workspace_bytes(int(batch), int(vocab)))
+
+
+def spec_accept_multidraft(target_logits, draft_probs, tokens, parent, u_accept, u_sample, temperature,
+                           accept_len=None, path=None, out_tokens=None, workspace=None, stream=None):
+    """Multi-draft tree rejection by recursive residuals; returns
+    (accept_len, path, out_tokens)."""
+    B, N, V = target_logits.shape
+    _dev(target_logits, "target_logits", torch.float32)
+    _dev(draft_probs, "draft_probs", torch.float32)
+    _dev(tokens, "tokens", torch.int32)
+    _dev(parent, "parent", torch.int32)
+    _dev(u_accept, "u_accept", torch.float32)
+    _dev(u_sample, "u_sample", torch.float32)
+    accept_len, path, out_tokens = _accept_outputs(B, N, target_logits.device, accept_len, path, out_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(spec_accept_multidraft_workspace_bytes(B, V), 1), dtype=torch.uint8,
+                                device=target_logits.device)
+    rc = _native.lib().spec_accept_multidraft(B, N, V, _ptr(target_logits), _ptr(draft_probs), _ptr(tokens),
+                                              _ptr(parent), _ptr(u_accept), _ptr(u_sample), float(temperature),
+                                              _ptr(accept_len), _ptr(path), _ptr(out_tokens), _ptr(workspace),
+                                              workspace.numel(), _stream(stream))
+    _check("spec_accept_multidraft", rc)
+    return accept_len, path, out_tokens
+
+
 def spec_accept_typical(target_logits, tokens, parent, temperature, epsilon, delta, accept_len=None,
                         path=None, out_tokens=None, workspace=None, stream=None):
     """Typical acceptance; returns (accept_len, path, out_tokens)."""

@@ -60,6 +60,11 @@ size_t spec_accept_workspace_bytes(int32_t batch, int32_t num_nodes, int32_t voc
     return plan_accept(batch, num_nodes, vocab).ws_bytes;
 }
 
+size_t spec_accept_multidraft_workspace_bytes(int32_t batch, int32_t vocab) {
+    if (batch < 1 || batch > 65535 || vocab < 1 || vocab > max_accept_vocab()) return 0;
+    return multidraft_workspace_bytes(batch, vocab);
+}
+
 static int accept_common_checks(int32_t B, int32_t N, int32_t V, const float* logits, const int32_t* tokens,
                                 int32_t* accept_len, int32_t* path, int32_t* out_tokens, float T) {
     if (B > 65535 || N < 1 || N > kMaxNodes || V < 1 || V > max_accept_vocab()) return SPEC_EINVAL;
@@ -103,6 +108,23 @@ int spec_accept_reject_filtered(int32_t batch, int32_t num_nodes, int32_t vocab,
     return launch_accept(0, batch, num_nodes, vocab, target_logits, draft_probs, tokens, parent, u_accept,
                          u_sample, temperature, 0.f, 0.f, accept_len, path, out_tokens, workspace, plan,
                          static_cast<hipStream_t>(stream), top_k, top_p);
+}
+
+int spec_accept_multidraft(int32_t batch, int32_t num_nodes, int32_t vocab, const float* target_logits,
+                           const float* draft_probs, const int32_t* tokens, const int32_t* parent,
+                           const float* u_accept, const float* u_sample, float temperature, int32_t* accept_len,
+                           int32_t* path, int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    if (batch < 0) return SPEC_EINVAL;
+    if (batch == 0) return SPEC_OK;
+    int rc = accept_common_checks(batch, num_nodes, vocab, target_logits, tokens, accept_len, path, out_tokens,
+                                  temperature);
+    if (rc != SPEC_OK) return rc;
+    if ((num_nodes > 1 && (!draft_probs || !u_accept)) || !u_sample) return SPEC_EINVAL;
+    if (!workspace || workspace_bytes < multidraft_workspace_bytes(batch, vocab)) return SPEC_EWORKSPACE;
+    return launch_accept_multidraft(batch, num_nodes, vocab, target_logits, draft_probs, tokens, parent, u_accept,
+                                    u_sample, temperature, accept_len, path, out_tokens, workspace,
+                                    static_cast<hipStream_t>(stream));
 }
 
 int spec_accept_typical(int32_t batch, int32_t num_nodes, int32_t vocab, const float* target_logits,

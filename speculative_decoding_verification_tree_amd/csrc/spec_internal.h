@@ -47,6 +47,12 @@ int launch_accept(int rule, int B, int N, int V, const float* logits, const floa
                   int32_t* accept_len, int32_t* path, int32_t* out_tokens, void* workspace,
                   const AcceptPlan& plan, hipStream_t stream, int top_k = 0, float top_p = 1.f);
 
+size_t multidraft_workspace_bytes(int B, int V);
+int launch_accept_multidraft(int B, int N, int V, const float* logits, const float* draft, const int32_t* tokens,
+                             const int32_t* parent, const float* u_accept, const float* u_sample, float temperature,
+                             int32_t* accept_len, int32_t* path, int32_t* out_tokens, void* workspace,
+                             hipStream_t stream);
+
 int launch_commit(const spec_attn_desc& d, void* k, void* v, int32_t* prefix_len, const int32_t* path,
                   const int32_t* accept_len, hipStream_t stream);
 

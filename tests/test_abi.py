@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     lib = sv.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -128,6 +128,24 @@ def test_filtered_accept_errors():
     assert _filt(N=65) == EINVAL
     assert _filt(ws_bytes=sv.lib().spec_accept_workspace_bytes(2, 6, 1000) - 1) == EWORKSPACE
     assert _filt(B=0) == OK
+
+
+def test_multidraft_errors():
+    lib = sv.lib()
+    need = lib.spec_accept_multidraft_workspace_bytes(2, 1000)
+    assert need == 2 * 2 * 1000 * 4
+    assert lib.spec_accept_multidraft_workspace_bytes(0, 1000) == 0
+    assert lib.spec_accept_multidraft_workspace_bytes(2, 0) == 0
+
+    def md(B=2, N=6, V=1000, T=1.0, ws_bytes=need, draft=FAKE):
+        return lib.spec_accept_multidraft(B, N, V, FAKE, draft, FAKE, None, FAKE, FAKE, T, FAKE, FAKE, FAKE, FAKE,
+                                          ws_bytes, None)
+    assert md(ws_bytes=need - 1) == EWORKSPACE
+    assert md(T=-1.0) == EINVAL
+    assert md(N=65) == EINVAL
+    assert md(draft=None) == EINVAL
+    assert md(B=-1) == EINVAL
+    assert md(B=0) == OK
 
 
 def test_commit_and_helper_errors():
