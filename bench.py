@@ -198,6 +198,16 @@ def main():
                                        w.temperature, filt_k, filt_p, c["al"], c["path"], c["otok"],
                                        workspace=acc_ws)
 
+    # Multi-draft tree rejection (recursive residuals), timed on its own for
+    # rejection-rule tree workloads.
+    md_ws = None
+    if w.rule == "reject" and not w.is_chain:
+        md_ws = torch.empty(max(sv.spec_accept_multidraft_workspace_bytes(B, V), 1), dtype=torch.uint8, device=dev)
+
+    def accept_multidraft(c):
+        sv.spec_accept_multidraft(c["logits"], c["draft"], c["tokens"], c["parent"], c["ua"], c["us"],
+                                  w.temperature, c["al"], c["path"], c["otok"], workspace=md_ws)
+
     # eager warm-up (also checks every call returns SPEC_OK)
     for i in range(max(args.warmup, ncopies)):
         step(copies[i % ncopies])
@@ -225,6 +235,12 @@ def main():
             accept_filtered(copies[i])
         g_filt = capture([accept_filtered])
         graphs.append(g_filt)
+    g_md = None
+    if md_ws is not None:
+        for i in range(ncopies):
+            accept_multidraft(copies[i])
+        g_md = capture([accept_multidraft])
+        graphs.append(g_md)
     for g in graphs:
         g.replay()
     torch.cuda.synchronize()
@@ -247,6 +263,7 @@ def main():
     commit_ms = timed(g_commit, reps)
     rope_ms = timed(g_rope, reps)
     filt_ms = timed(g_filt, reps) if g_filt is not None else None
+    md_ms = timed(g_md, reps) if g_md is not None else None
     # every target row once (leaf rows too: the stop row may be one), plus the
     # stop row and one draft row per request for the residual
     filt_bytes = (B * N * V + 2 * B * V) * 4
@@ -322,6 +339,9 @@ def main():
             "us": filt_ms * 1e3, "top_k": filt_k, "top_p": filt_p, "bytes": filt_bytes,
             "achieved_GBs": filt_bytes / (filt_ms * 1e-3) / 1e9, "calls": "spec_accept_reject_filtered",
             "note": "the rejection rule on the top-k / nucleus truncated target; not part of ms_per_step"},
+        "multidraft_accept": None if md_ms is None else {
+            "us": md_ms * 1e3, "calls": "spec_accept_multidraft",
+            "note": "tree rejection by recursive residuals over each node's children; not part of ms_per_step"},
         "roofline": {
             "bound": "hbm",
             "kernel": "spec_verify_attn",
