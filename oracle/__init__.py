@@ -47,6 +47,10 @@ def _load():
         lib.oracle_accept_ex.restype = I
         lib.oracle_accept_multidraft.argtypes = [I, I, I, P, P, P, P, P, P, D, P, P, P, P, P]
         lib.oracle_accept_multidraft.restype = I
+        lib.oracle_la_verify.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P]
+        lib.oracle_la_verify.restype = I
+        lib.oracle_la_commit.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P]
+        lib.oracle_la_commit.restype = I
         lib.oracle_commit.argtypes = [I, I, I, I, I, P, P, P, P, P]
         lib.oracle_commit.restype = I
         lib.oracle_medusa_tree.argtypes = [I, I, P, I, I, P, P, P, P]
@@ -151,6 +155,41 @@ def accept_multidraft(target_logits, tokens, parent, temperature, draft_probs, u
     if rc != 0:
         raise ValueError("oracle_accept_multidraft rejected its arguments")
     return dict(accept_len=acc, path=path, out_tokens=out, margin=margin, stop=stop)
+
+
+def _dt(dtype):
+    return {"f32": 0, "bf16": 1}[dtype]
+
+
+def la_verify(state, q, k, v, alpha, parent, dtype):
+    """Linear-attention tree verification in fp64: out [B][N][H][Dv].
+    state [B][H][Dv][Dk] fp32; q, k [B][N][H][Dk] and v [B][N][H][Dv] as
+    float32 or bf16 bits (uint16); alpha [B][N][H] or None; parent or None."""
+    B, N, H, Dk = q.shape
+    Dv = v.shape[3]
+    st = _c(state, np.float32)
+    el = np.uint16 if dtype == "bf16" else np.float32
+    out = np.empty((B, N, H, Dv), np.float64)
+    rc = _load().oracle_la_verify(B, N, H, Dk, Dv, _dt(dtype), _ptr(st), _ptr(_c(q, el)), _ptr(_c(k, el)),
+                                  _ptr(_c(v, el)), _ptr(_c(alpha, np.float32)), _ptr(_c(parent, np.int32)),
+                                  _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_la_verify rejected its arguments")
+    return out
+
+
+def la_commit(state, k, v, alpha, parent, path, accept_len, dtype):
+    """The state after committing the accepted path (a new fp32 array)."""
+    B, N, H, Dk = k.shape
+    Dv = v.shape[3]
+    st = np.array(state, np.float32, copy=True, order="C")
+    el = np.uint16 if dtype == "bf16" else np.float32
+    rc = _load().oracle_la_commit(B, N, H, Dk, Dv, _dt(dtype), _ptr(st), _ptr(_c(k, el)), _ptr(_c(v, el)),
+                                  _ptr(_c(alpha, np.float32)), _ptr(_c(parent, np.int32)),
+                                  _ptr(_c(path, np.int32)), _ptr(_c(accept_len, np.int32)))
+    if rc != 0:
+        raise ValueError("oracle_la_commit rejected its arguments")
+    return st
 
 
 def commit(k_cache, v_cache, prefix_len, path, accept_len):

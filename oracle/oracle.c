@@ -522,6 +522,100 @@ int oracle_accept_multidraft(int B, int N, int V, const float* logits, const flo
 }
 
 /* ---------------------------------------------------------------------------
+ * Linear-attention verification and state commit (SpecLA paragraphs of the
+ * gist.science summary "SpecLA: Efficient Speculative Decoding for
+ * Linear-Attention Models": a stateful linear-attention model verifies a
+ * chain or a tree of drafts against its summary state, with a tree mask for
+ * branches, and afterwards recovers the state from compact factors).  The
+ * pages give no recurrence; the reading is a matrix state per (request, head)
+ * with a scalar decay per token:
+ *     S_t = alpha_t S_{t-1} + v_t k_t^T,   o_t = S_t q_t
+ * (alpha = 1: plain linear attention).  Node i of the tree follows its root
+ * path: with A(j -> i] the product of alpha over the path nodes after j up
+ * to i (and A(-> i] over the whole path root .. i),
+ *     o_i = A(-> i] S q_i + sum_{j in anc(i)} A(j -> i] (q_i . k_j) v_j,
+ * anc(i) including i.  The commit for accepted stop node v is S_v itself:
+ *     S' = A(-> v] S + sum_{j on the path} A(j -> v] v_j k_j^T.
+ * Layouts: S [B][H][Dv][Dk], q/k [B][N][H][Dk], v/out [B][N][H][Dv],
+ * alpha [B][N][H] (NULL = 1), parent [B][N] (NULL = chain).
+ * ------------------------------------------------------------------------- */
+static double path_decay(const int* par, const double* al, int j, int i) {
+    /* product of alpha over the path nodes after j up to i (j = -1: whole
+       path); j must be an ancestor-or-self of i */
+    double d = 1.0;
+    for (int n = i; n != j; n = par[n]) d *= al[n];
+    return d;
+}
+
+int oracle_la_verify(int B, int N, int H, int Dk, int Dv, int dtype, const float* state, const void* q,
+                     const void* k, const void* v, const float* alpha, const int32_t* parent, double* out) {
+    if (B < 0 || N < 1 || N > 64 || H < 1 || Dk < 1 || Dv < 1) return -1;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            int par[64];
+            double al[64];
+            for (int i = 0; i < N; ++i) {
+                par[i] = parent_of(parent, N, b, i);
+                al[i] = alpha ? alpha[((size_t)b * N + i) * H + h] : 1.0;
+            }
+            const float* S = state + ((size_t)b * H + h) * Dv * Dk;
+            for (int i = 0; i < N; ++i) {
+                const size_t qo = (((size_t)b * N + i) * H + h) * Dk;
+                double* o = out + (((size_t)b * N + i) * H + h) * Dv;
+                const double Ai = path_decay(par, al, -1, i);
+                for (int e = 0; e < Dv; ++e) {
+                    double acc = 0.0;
+                    for (int d = 0; d < Dk; ++d) acc += (double)S[(size_t)e * Dk + d] * load_elem(q, dtype, qo + d);
+                    o[e] = Ai * acc;
+                }
+                for (int j = i; j >= 0; j = par[j]) {
+                    const size_t ko = (((size_t)b * N + j) * H + h) * Dk;
+                    const size_t vo = (((size_t)b * N + j) * H + h) * Dv;
+                    double qk = 0.0;
+                    for (int d = 0; d < Dk; ++d) qk += load_elem(q, dtype, qo + d) * load_elem(k, dtype, ko + d);
+                    const double w = path_decay(par, al, j, i) * qk;
+                    for (int e = 0; e < Dv; ++e) o[e] += w * load_elem(v, dtype, vo + e);
+                }
+            }
+        }
+    return 0;
+}
+
+/* In-place commit of the accepted path (path[b][0 .. accept_len[b]]) into
+ * the state; the factors are the path nodes' k, v and alpha. */
+int oracle_la_commit(int B, int N, int H, int Dk, int Dv, int dtype, float* state, const void* k, const void* v,
+                     const float* alpha, const int32_t* parent, const int32_t* path, const int32_t* accept_len) {
+    if (B < 0 || N < 1 || N > 64 || H < 1 || Dk < 1 || Dv < 1) return -1;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            int par[64];
+            double al[64];
+            for (int i = 0; i < N; ++i) {
+                par[i] = parent_of(parent, N, b, i);
+                al[i] = alpha ? alpha[((size_t)b * N + i) * H + h] : 1.0;
+            }
+            const int a = accept_len[b];
+            const int vstop = path[(size_t)b * N + a];
+            float* S = state + ((size_t)b * H + h) * Dv * Dk;
+            const double Av = path_decay(par, al, -1, vstop);
+            for (int e = 0; e < Dv; ++e)
+                for (int d = 0; d < Dk; ++d) {
+                    double acc = Av * (double)S[(size_t)e * Dk + d];
+                    for (int t = 0; t <= a; ++t) {
+                        const int j = path[(size_t)b * N + t];
+                        acc += path_decay(par, al, j, vstop) *
+                               load_elem(v, dtype, (((size_t)b * N + j) * H + h) * Dv + e) *
+                               load_elem(k, dtype, (((size_t)b * N + j) * H + h) * Dk + d);
+                    }
+                    S[(size_t)e * Dk + d] = (float)acc;
+                }
+        }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
  * Commit: for every request b and kv-head, the accepted path's rows
  * L_b + path[d] (d = 0..a) move to L_b + d; every source row is read before
  * any row is written.  prefix_len[b] becomes L_b + a + 1.  row_bytes = D *
