@@ -236,6 +236,58 @@ int spec_tree_rope(const spec_attn_desc* desc, void* q, void* k_cache, const int
 /* Static string naming a spec_status value. */
 const char* spec_status_string(int status);
 
+/* Linear-attention verification (SpecLA paragraphs of the summary "SpecLA:
+ * Efficient Speculative Decoding for Linear-Attention Models": the drafts of
+ * a stateful linear-attention model are verified against its summary state,
+ * a tree mask separating branches, and the state is recovered afterwards
+ * from the accepted tokens' compact factors, the final update deferred to
+ * the next step).  The summary gives no recurrence; the one implemented is a
+ * matrix state per (request, head) with a scalar decay per token,
+ *     S_t = alpha_t S_{t-1} + v_t k_t^T,   o_t = S_t q_t
+ * (alpha = 1: plain linear attention), each tree node following its root
+ * path from the committed state.  fp32 state and arithmetic. */
+typedef struct {
+    int32_t batch;
+    int32_t num_nodes;   /* N, the nodes of this step's tree, 1..64 */
+    int32_t num_heads;   /* H >= 1 */
+    int32_t key_dim;     /* Dk: 64 or 128 */
+    int32_t value_dim;   /* Dv: 64 or 128 */
+    spec_dtype dtype;    /* q, k, v and out: fp32 or bf16 */
+} spec_la_desc;
+
+/* The factors of one step's accepted path: that step's tree (its k, v,
+ * decays and parents, num_nodes nodes) and its accepted path, as the
+ * acceptance calls return it (path[b][0 .. accept_len[b]]). */
+typedef struct {
+    int32_t num_nodes;
+    const void* k;          /* [B][N'][H][Dk] (dtype) */
+    const void* v;          /* [B][N'][H][Dv] (dtype) */
+    const float* alpha;     /* [B][N'][H] decays in (0, 1], or NULL (all 1) */
+    const int32_t* parent;  /* [B][N'] or NULL (chain) */
+    const int32_t* path;    /* [B][N'] */
+    const int32_t* accept_len; /* [B] */
+} spec_la_factors;
+
+/* Outputs of every node of the tree: out[b][i][h] = A(-> i] S q_i +
+ * sum over j on i's root path of A(j -> i] (q_i . k_j) v_j, where A(j -> i]
+ * is the product of the decays of the path nodes after j up to i (A(-> i]:
+ * the whole path root .. i).
+ *   state  [B][H][Dv][Dk] fp32, device: the committed state (read); with
+ *          pending != NULL it is first advanced in place by that step's
+ *          accepted factors (the deferred commit), then read
+ *   q, k   [B][N][H][Dk], v and out [B][N][H][Dv] (dtype), device
+ *   alpha  [B][N][H] fp32 decays in (0, 1] or NULL; parent [B][N] or NULL
+ * Errors: SPEC_EINVAL (null pointers, sizes), SPEC_EUNSUPPORTED (Dk, Dv). */
+int spec_la_verify(const spec_la_desc* desc, float* state, const void* q, const void* k, const void* v,
+                   const float* alpha, const int32_t* parent, void* out, const spec_la_factors* pending,
+                   void* stream);
+
+/* The commit alone: state <- A(-> v] state + sum over j on the accepted path
+ * of A(j -> v] v_j k_j^T (v the stop node), in place, from the factors; the
+ * same update spec_la_verify applies for its pending argument.  desc gives
+ * B, H, Dk, Dv and dtype (its num_nodes is not used). */
+int spec_la_commit(const spec_la_desc* desc, float* state, const spec_la_factors* accepted, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

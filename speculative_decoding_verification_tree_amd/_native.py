@@ -31,6 +31,8 @@ SIGNATURES = {
     "spec_medusa_tree": (ctypes.c_int, [_I, _I, _P, _I, _P, _P, _P, _P, _P]),
     "spec_tree_rope": (ctypes.c_int, [_P, _P, _P, _P, _P, _F, _P]),
     "spec_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "spec_la_verify": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "spec_la_commit": (ctypes.c_int, [_P, _P, _P, _P]),
 }
 
 SPEC_OK, SPEC_EINVAL, SPEC_EUNSUPPORTED, SPEC_EWORKSPACE, SPEC_EHIP = 0, -1, -2, -3, -4
@@ -48,6 +50,31 @@ class AttnDesc(ctypes.Structure):
         ("kv_capacity", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
+    ]
+
+
+class LaDesc(ctypes.Structure):
+    """Mirror of spec_la_desc."""
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_nodes", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("key_dim", ctypes.c_int32),
+        ("value_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+class LaFactors(ctypes.Structure):
+    """Mirror of spec_la_factors."""
+    _fields_ = [
+        ("num_nodes", ctypes.c_int32),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("alpha", ctypes.c_void_p),
+        ("parent", ctypes.c_void_p),
+        ("path", ctypes.c_void_p),
+        ("accept_len", ctypes.c_void_p),
     ]
 
 

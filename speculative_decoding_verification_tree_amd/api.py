@@ -13,7 +13,7 @@ import ctypes
 import torch
 
 from . import _native
-from ._native import AttnDesc, SPEC_BF16, SPEC_F32
+from ._native import AttnDesc, LaDesc, LaFactors, SPEC_BF16, SPEC_F32
 
 
 class SpecError(RuntimeError):
@@ -282,3 +282,48 @@ def spec_tree_rope(q, k_cache, prefix_len, parent, rope_base, stream=None):
     rc = _native.lib().spec_tree_rope(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(prefix_len), _ptr(parent),
                                       float(rope_base), _stream(stream))
     _check("spec_tree_rope", rc)
+
+
+def _la_factors(k, v, alpha, parent, path, accept_len):
+    for t, n in ((path, "path"), (accept_len, "accept_len")):
+        _dev(t, n, torch.int32)
+    _dev(parent, "parent", torch.int32)
+    _dev(alpha, "alpha", torch.float32)
+    return LaFactors(k.shape[1], _ptr(k), _ptr(v), _ptr(alpha), _ptr(parent), _ptr(path), _ptr(accept_len))
+
+
+def spec_la_verify(state, q, k, v, alpha=None, parent=None, out=None, pending=None, stream=None):
+    """Linear-attention verification of a tree (or chain) of drafts: returns
+    out [B][N][H][Dv].  state [B][H][Dv][Dk] fp32 (advanced in place first by
+    ``pending`` = (k, v, alpha, parent, path, accept_len) of the previous
+    step, the deferred commit); q, k [B][N][H][Dk], v [B][N][H][Dv] (fp32 or
+    bf16); alpha [B][N][H] fp32 decays or None; parent [B][N] or None."""
+    B, N, H, Dk = q.shape
+    Dv = v.shape[3]
+    _dev(state, "state", torch.float32)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n, q.dtype)
+    _dev(alpha, "alpha", torch.float32)
+    _dev(parent, "parent", torch.int32)
+    if out is None:
+        out = torch.empty(B, N, H, Dv, dtype=q.dtype, device=q.device)
+    desc = LaDesc(B, N, H, Dk, Dv, _dtype_code(q.dtype))
+    f = _la_factors(*pending) if pending is not None else None
+    rc = _native.lib().spec_la_verify(ctypes.byref(desc), _ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                      _ptr(parent), _ptr(out), ctypes.byref(f) if f is not None else None,
+                                      _stream(stream))
+    _check("spec_la_verify", rc)
+    return out
+
+
+def spec_la_commit(state, k, v, alpha, parent, path, accept_len, stream=None):
+    """Commit of the accepted path into the linear-attention state, in place,
+    from the step's factors (k, v, alpha, parent) and its accepted path."""
+    B, Np, H, Dk = k.shape
+    Dv = v.shape[3]
+    _dev(state, "state", torch.float32)
+    desc = LaDesc(B, Np, H, Dk, Dv, _dtype_code(k.dtype))
+    f = _la_factors(k, v, alpha, parent, path, accept_len)
+    rc = _native.lib().spec_la_commit(ctypes.byref(desc), _ptr(state), ctypes.byref(f), _stream(stream))
+    _check("spec_la_commit", rc)
+    return state

@@ -238,4 +238,71 @@ const char* spec_status_string(int status) {
     }
 }
 
+static int la_desc_ok(const spec_la_desc* d) {
+    if (!d) return SPEC_EINVAL;
+    if (d->batch < 0 || d->batch > 65535 || d->num_heads < 1 || d->num_heads > 65535) return SPEC_EINVAL;
+    if (d->dtype != SPEC_F32 && d->dtype != SPEC_BF16) return SPEC_EUNSUPPORTED;
+    if ((d->key_dim != 64 && d->key_dim != 128) || (d->value_dim != 64 && d->value_dim != 128))
+        return d->key_dim < 1 || d->value_dim < 1 ? SPEC_EINVAL : SPEC_EUNSUPPORTED;
+    return SPEC_OK;
+}
+
+static bool la_factors_ok(const spec_la_factors* f) {
+    return f && f->num_nodes >= 1 && f->num_nodes <= kMaxNodes && f->k && f->v && f->path && f->accept_len;
+}
+
+static LaArgs la_args(const spec_la_desc* d, float* state) {
+    LaArgs a{};
+    a.state = state;
+    a.B = d->batch;
+    a.H = d->num_heads;
+    a.Dk = d->key_dim;
+    a.Dv = d->value_dim;
+    a.bf16 = d->dtype == SPEC_BF16;
+    return a;
+}
+
+static void la_set_factors(LaArgs& a, const spec_la_factors* f) {
+    a.pN = f->num_nodes;
+    a.pk = f->k;
+    a.pv = f->v;
+    a.palpha = f->alpha;
+    a.pparent = f->parent;
+    a.ppath = f->path;
+    a.pacc = f->accept_len;
+    a.do_commit = 1;
+}
+
+int spec_la_verify(const spec_la_desc* desc, float* state, const void* q, const void* k, const void* v,
+                   const float* alpha, const int32_t* parent, void* out, const spec_la_factors* pending,
+                   void* stream) {
+    int rc = la_desc_ok(desc);
+    if (rc != SPEC_OK) return rc;
+    if (desc->num_nodes < 1 || desc->num_nodes > kMaxNodes) return SPEC_EINVAL;
+    if (desc->batch == 0) return SPEC_OK;
+    if (!state || !q || !k || !v || !out) return SPEC_EINVAL;
+    if (pending && !la_factors_ok(pending)) return SPEC_EINVAL;
+    LaArgs a = la_args(desc, state);
+    a.N = desc->num_nodes;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.alpha = alpha;
+    a.parent = parent;
+    a.out = out;
+    a.do_verify = 1;
+    if (pending) la_set_factors(a, pending);
+    return launch_la(a, static_cast<hipStream_t>(stream));
+}
+
+int spec_la_commit(const spec_la_desc* desc, float* state, const spec_la_factors* accepted, void* stream) {
+    int rc = la_desc_ok(desc);
+    if (rc != SPEC_OK) return rc;
+    if (desc->batch == 0) return SPEC_OK;
+    if (!state || !la_factors_ok(accepted)) return SPEC_EINVAL;
+    LaArgs a = la_args(desc, state);
+    la_set_factors(a, accepted);
+    return launch_la(a, static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

@@ -1,0 +1,176 @@
+// Linear-attention verification and state commit for gfx950 (SpecLA
+// paragraphs of the summary "SpecLA: Efficient Speculative Decoding for
+// Linear-Attention Models": drafts are verified against the recurrent summary
+// state kept on chip, branches under a tree mask, and the state is recovered
+// afterwards from the accepted tokens' compact factors, the final update
+// deferred to the next step).  Recurrence (a reading; the summary gives
+// none): S_t = alpha_t S_{t-1} + v_t k_t^T, o_t = S_t q_t, per (request,
+// head), S [Dv][Dk] fp32.
+//
+// One 256-thread workgroup per (head, request), two optional phases:
+//   commit: S <- A(-> v] S + sum_{j on the accepted path} A(j -> v] v_j k_j^T,
+//           the path's k, v and decay weights in LDS, every state element
+//           written once (in place; the workgroup owns its slab);
+//   verify: o_i = A(-> i] S q_i + sum_{j in anc(i)} A(j -> i] (q_i . k_j) v_j
+//           with Q, K, V in LDS, the N x N decayed, masked scores in LDS and
+//           the state streamed through LDS in 32-column chunks.
+// Both phases in one launch are the deferred update: the previous step's
+// commit folded into this step's verification (one state read and write).
+// Decay products are exp2 of differences of log2 prefix sums along root paths.
+#include "spec_common.h"
+#include "spec_internal.h"
+
+namespace specv {
+
+constexpr int kLaThreads = 256;
+constexpr int kLaMaxD = 128;
+constexpr int kLaChunk = 32;
+
+__device__ __forceinline__ float la_load(const void* p, bool bf16, size_t i) {
+    if (bf16) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
+    return static_cast<const float*>(p)[i];
+}
+
+// Root-path structure of request b's tree of N nodes (thread 0, nodes in
+// index order, parents first): L[i] = log2 of the decay product over the
+// path root .. i, anc[i] = the path's node mask.
+__device__ __forceinline__ void la_tree(const int32_t* parent, const float* alpha, int b, int N, int H, int h,
+                                        int* s_par, float* s_L, uint64_t* s_anc) {
+    if (threadIdx.x == 0) {
+        for (int i = 0; i < N; ++i) {
+            const int p = tree_parent(parent, N, b, i);
+            const int pp = p >= 0 && p < i ? p : -1;  // out-of-contract parents read as roots
+            s_par[i] = pp;
+            const float lg = alpha ? __log2f(alpha[(static_cast<size_t>(b) * N + i) * H + h]) : 0.f;
+            s_L[i] = (pp >= 0 ? s_L[pp] : 0.f) + lg;
+            s_anc[i] = (pp >= 0 ? s_anc[pp] : 0ull) | (1ull << i);
+        }
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int Dk = a.Dk, Dv = a.Dv, H = a.H;
+    const bool bf16 = a.bf16 != 0;
+    // carved per phase: verify needs 2 * 64 * 129 (Q, K) + 64 * 128 (V) +
+    // 64 * 64 (W) + 128 * 33 (state chunk) floats; commit 2 * 64 * 128
+    constexpr int kLds = 2 * kMaxNodes * (kLaMaxD + 1) + kMaxNodes * kLaMaxD + kMaxNodes * kMaxNodes +
+                         kLaMaxD * (kLaChunk + 1);
+    __shared__ float lds[kLds];  // 129 KB
+    __shared__ int s_par[kMaxNodes];
+    __shared__ float s_L[kMaxNodes];
+    __shared__ uint64_t s_anc[kMaxNodes];
+    __shared__ float s_c[kMaxNodes];
+    __shared__ int s_j[kMaxNodes];
+    float* S = a.state + (static_cast<size_t>(b) * H + h) * Dv * Dk;
+
+    if (a.do_commit) {
+        const int N = a.pN;
+        la_tree(a.pparent, a.palpha, b, N, H, h, s_par, s_L, s_anc);
+        // (device data: out-of-range entries are clamped into the tree)
+        const int acc = min(max(a.pacc[b], 0), N - 1);
+        const int vstop = min(max(a.ppath[static_cast<size_t>(b) * N + acc], 0), N - 1);
+        if (tid <= acc) {
+            const int j = min(max(a.ppath[static_cast<size_t>(b) * N + tid], 0), N - 1);
+            s_j[tid] = j;
+            s_c[tid] = exp2f(s_L[vstop] - s_L[j]);
+        }
+        __syncthreads();
+        float* kf = lds;                      // [acc + 1][Dk]
+        float* vf = lds + kLaMaxD * kMaxNodes;  // [acc + 1][Dv]
+        for (int x = tid; x < (acc + 1) * Dk; x += kLaThreads) {
+            const int t = x / Dk, d = x - t * Dk;
+            kf[x] = la_load(a.pk, bf16, ((static_cast<size_t>(b) * N + s_j[t]) * H + h) * Dk + d);
+        }
+        for (int x = tid; x < (acc + 1) * Dv; x += kLaThreads) {
+            const int t = x / Dv, e = x - t * Dv;
+            vf[x] = la_load(a.pv, bf16, ((static_cast<size_t>(b) * N + s_j[t]) * H + h) * Dv + e);
+        }
+        __syncthreads();
+        const float Av = exp2f(s_L[vstop]);
+        const int d = tid % Dk, e0 = tid / Dk, estep = kLaThreads / Dk;
+        for (int e = e0; e < Dv; e += estep) {
+            float s = Av * S[static_cast<size_t>(e) * Dk + d];
+            for (int t = 0; t <= acc; ++t) s = fmaf(s_c[t] * vf[t * Dv + e], kf[t * Dk + d], s);
+            S[static_cast<size_t>(e) * Dk + d] = s;
+        }
+        __syncthreads();  // the workgroup's own state writes before its reads below
+    }
+    if (!a.do_verify) return;
+
+    const int N = a.N;
+    la_tree(a.parent, a.alpha, b, N, H, h, s_par, s_L, s_anc);
+    const int DkP = Dk + 1;               // padded rows: lanes on different rows hit different banks
+    float* Qs = lds;                      // [N][Dk + 1]
+    float* Ks = Qs + kMaxNodes * (kLaMaxD + 1);
+    float* Vs = Ks + kMaxNodes * (kLaMaxD + 1);  // [N][Dv]
+    float* W = Vs + kMaxNodes * kLaMaxD;         // [N][N]
+    float* Sc = W + kMaxNodes * kMaxNodes;       // [Dv][kLaChunk + 1]
+    for (int x = tid; x < N * Dk; x += kLaThreads) {
+        const int i = x / Dk, d = x - i * Dk;
+        const size_t g = ((static_cast<size_t>(b) * N + i) * H + h) * Dk + d;
+        Qs[i * DkP + d] = la_load(a.q, bf16, g);
+        Ks[i * DkP + d] = la_load(a.k, bf16, g);
+    }
+    for (int x = tid; x < N * Dv; x += kLaThreads) {
+        const int i = x / Dv, e = x - i * Dv;
+        Vs[x] = la_load(a.v, bf16, ((static_cast<size_t>(b) * N + i) * H + h) * Dv + e);
+    }
+    __syncthreads();
+    // W[i][j] = A(j -> i] (q_i . k_j) for j on i's root path, else 0.
+    for (int x = tid; x < N * N; x += kLaThreads) {
+        const int i = x / N, j = x - i * N;
+        float w = 0.f;
+        if ((s_anc[i] >> j) & 1ull) {
+            float dot = 0.f;
+            for (int d = 0; d < Dk; ++d) dot = fmaf(Qs[i * DkP + d], Ks[j * DkP + d], dot);
+            w = exp2f(s_L[i] - s_L[j]) * dot;
+        }
+        W[x] = w;
+    }
+    // Thread (e, group g): nodes g, g + G, ... with G = 256 / Dv groups.
+    const int e = tid % Dv, g = tid / Dv, G = kLaThreads / Dv;
+    float acc[kMaxNodes / 2];  // up to 32 nodes per thread (Dv = 128); 16 for Dv = 64
+#pragma unroll
+    for (int n = 0; n < kMaxNodes / 2; ++n) acc[n] = 0.f;
+    for (int c0 = 0; c0 < Dk; c0 += kLaChunk) {
+        __syncthreads();  // the previous chunk is consumed (and W is complete)
+        for (int x = tid; x < Dv * kLaChunk; x += kLaThreads) {
+            const int r = x / kLaChunk, cc = x - r * kLaChunk;
+            Sc[r * (kLaChunk + 1) + cc] = S[static_cast<size_t>(r) * Dk + c0 + cc];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int n = 0; n < kMaxNodes / 2; ++n) {
+            const int i = g + n * G;
+            if (i < N) {
+                float s = acc[n];
+                for (int cc = 0; cc < kLaChunk; ++cc) s = fmaf(Sc[e * (kLaChunk + 1) + cc], Qs[i * DkP + c0 + cc], s);
+                acc[n] = s;
+            }
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < kMaxNodes / 2; ++n) {
+        const int i = g + n * G;
+        if (i < N) {
+            float o = exp2f(s_L[i]) * acc[n];
+            const uint64_t m = s_anc[i];
+            for (int j = 0; j <= i; ++j)
+                if ((m >> j) & 1ull) o = fmaf(W[i * N + j], Vs[j * Dv + e], o);
+            const size_t oi = ((static_cast<size_t>(b) * N + i) * H + h) * Dv + e;
+            if (bf16)
+                static_cast<uint16_t*>(a.out)[oi] = static_cast<uint16_t>(f32_to_bf16_bits(o));
+            else
+                static_cast<float*>(a.out)[oi] = o;
+        }
+    }
+}
+
+int launch_la(const LaArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(la_kernel, dim3(a.H, a.B), dim3(kLaThreads), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
+}
+
+}  // namespace specv

@@ -86,4 +86,26 @@ int launch_tree_rope(const TreeRopeArgs& a, int B, bool bf16, hipStream_t stream
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Linear-attention verification / commit (one launch, either or both phases).
+struct LaArgs {
+    float* state;  // [B][H][Dv][Dk] fp32
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const int32_t* parent;
+    void* out;
+    int B, N, H, Dk, Dv, bf16;
+    // the accepted path committed before verification (or alone)
+    int pN;
+    const void* pk;
+    const void* pv;
+    const float* palpha;
+    const int32_t* pparent;
+    const int32_t* ppath;
+    const int32_t* pacc;
+    int do_commit, do_verify;
+};
+int launch_la(const LaArgs& a, hipStream_t stream);
+
 }  // namespace specv

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     lib = sv.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -146,6 +146,35 @@ def test_multidraft_errors():
     assert md(draft=None) == EINVAL
     assert md(B=-1) == EINVAL
     assert md(B=0) == OK
+
+
+def test_linear_attention_errors():
+    from speculative_decoding_verification_tree_amd._native import LaDesc, LaFactors
+    lib = sv.lib()
+
+    def d(**kw):
+        x = dict(batch=2, num_nodes=6, num_heads=4, key_dim=128, value_dim=128, dtype=0)
+        x.update(kw)
+        return LaDesc(**x)
+
+    def ver(desc, state=FAKE, pending=None):
+        return lib.spec_la_verify(ctypes.byref(desc), state, FAKE, FAKE, FAKE, None, None, FAKE,
+                                  ctypes.byref(pending) if pending is not None else None, None)
+    assert ver(d(key_dim=96)) == EUNSUPPORTED
+    assert ver(d(value_dim=256)) == EUNSUPPORTED
+    assert ver(d(key_dim=0)) == EINVAL
+    assert ver(d(dtype=5)) == EUNSUPPORTED
+    assert ver(d(num_nodes=65)) == EINVAL
+    assert ver(d(num_heads=0)) == EINVAL
+    assert ver(d(batch=-1)) == EINVAL
+    assert ver(d(), state=None) == EINVAL
+    assert ver(d(), pending=LaFactors(0, FAKE, FAKE, None, None, FAKE, FAKE)) == EINVAL
+    assert ver(d(batch=0), state=None) == OK
+    assert lib.spec_la_verify(None, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, None) == EINVAL
+    good = LaFactors(6, FAKE, FAKE, None, None, FAKE, FAKE)
+    assert lib.spec_la_commit(ctypes.byref(d()), None, ctypes.byref(good), None) == EINVAL
+    assert lib.spec_la_commit(ctypes.byref(d()), FAKE, None, None) == EINVAL
+    assert lib.spec_la_commit(ctypes.byref(d(key_dim=32)), FAKE, ctypes.byref(good), None) == EUNSUPPORTED
 
 
 def test_commit_and_helper_errors():
