@@ -208,6 +208,29 @@ def main():
         sv.spec_accept_multidraft(c["logits"], c["draft"], c["tokens"], c["parent"], c["ua"], c["us"],
                                   w.temperature, c["al"], c["path"], c["otok"], workspace=md_ws)
 
+    # Linear-attention verification of the same trees (16 heads, Dk = Dv =
+    # 128, bf16 q/k/v, fp32 state), its factor commit, and the two fused (the
+    # deferred commit), timed on their own.
+    LH, LD = 16, 128
+    la_state = torch.randn(B, LH, LD, LD, device=dev) / LD ** 0.5
+    la_q = (torch.randn(B, N, LH, LD, device=dev) / LD ** 0.5).to(torch.bfloat16)
+    la_k = torch.randn(B, N, LH, LD, device=dev).to(torch.bfloat16)
+    la_v = torch.randn(B, N, LH, LD, device=dev).to(torch.bfloat16)
+    la_alpha = torch.rand(B, N, LH, device=dev) * 0.4 + 0.6
+    la_out = torch.empty_like(la_v)
+    la_path = copies[0]["path"]
+    la_acc = copies[0]["al"]
+    la_pending = (la_k, la_v, la_alpha, copies[0]["parent"], la_path, la_acc)
+
+    def la_verify(c):
+        sv.spec_la_verify(la_state, la_q, la_k, la_v, la_alpha, c["parent"], out=la_out)
+
+    def la_commit(c):
+        sv.spec_la_commit(la_state, *la_pending)
+
+    def la_fused(c):
+        sv.spec_la_verify(la_state, la_q, la_k, la_v, la_alpha, c["parent"], out=la_out, pending=la_pending)
+
     # eager warm-up (also checks every call returns SPEC_OK)
     for i in range(max(args.warmup, ncopies)):
         step(copies[i % ncopies])
@@ -235,6 +258,11 @@ def main():
             accept_filtered(copies[i])
         g_filt = capture([accept_filtered])
         graphs.append(g_filt)
+    for fn in (la_verify, la_commit, la_fused):
+        fn(copies[0])
+    torch.cuda.synchronize()
+    g_lav, g_lac, g_laf = capture([la_verify]), capture([la_commit]), capture([la_fused])
+    graphs += [g_lav, g_lac, g_laf]
     g_md = None
     if md_ws is not None:
         for i in range(ncopies):
@@ -264,6 +292,11 @@ def main():
     rope_ms = timed(g_rope, reps)
     filt_ms = timed(g_filt, reps) if g_filt is not None else None
     md_ms = timed(g_md, reps) if g_md is not None else None
+    lav_ms, lac_ms, laf_ms = timed(g_lav, reps), timed(g_lac, reps), timed(g_laf, reps)
+    la_state_b = B * LH * LD * LD * 4
+    la_io_b = B * N * LH * LD * 2 * 4  # q, k, v in and out, bf16
+    la_verify_b = la_state_b + la_io_b
+    la_commit_b = 2 * la_state_b  # the state read and written (the path's factors are small)
     # every target row once (leaf rows too: the stop row may be one), plus the
     # stop row and one draft row per request for the residual
     filt_bytes = (B * N * V + 2 * B * V) * 4
@@ -339,6 +372,13 @@ def main():
             "us": filt_ms * 1e3, "top_k": filt_k, "top_p": filt_p, "bytes": filt_bytes,
             "achieved_GBs": filt_bytes / (filt_ms * 1e-3) / 1e9, "calls": "spec_accept_reject_filtered",
             "note": "the rejection rule on the top-k / nucleus truncated target; not part of ms_per_step"},
+        "linear_attention": {
+            "heads": LH, "key_dim": LD, "value_dim": LD,
+            "verify_us": lav_ms * 1e3, "verify_GBs": la_verify_b / (lav_ms * 1e-3) / 1e9,
+            "commit_us": lac_ms * 1e3, "commit_GBs": la_commit_b / (lac_ms * 1e-3) / 1e9,
+            "fused_us": laf_ms * 1e3, "fused_GBs": (la_verify_b + la_state_b) / (laf_ms * 1e-3) / 1e9,
+            "calls": "spec_la_verify, spec_la_commit, spec_la_verify with pending factors",
+            "note": "same trees as the workload, bf16 q/k/v, fp32 state; not part of ms_per_step"},
         "multidraft_accept": None if md_ms is None else {
             "us": md_ms * 1e3, "calls": "spec_accept_multidraft",
             "note": "tree rejection by recursive residuals over each node's children; not part of ms_per_step"},

@@ -49,15 +49,24 @@ __device__ __forceinline__ void la_tree(const int32_t* parent, const float* alph
     __syncthreads();
 }
 
+// LDS floats for trees of at most NMAX nodes: commit (path factors k, v)
+// or verify (Q and K rows padded by one, V, the scores W, a 32-column chunk
+// of the state), whichever is larger.
+template <int NMAX, bool COMMIT>
+constexpr int la_lds_floats() {
+    constexpr int commit = COMMIT ? kMaxNodes * 2 * kLaMaxD : 0;
+    constexpr int verify = 2 * NMAX * (kLaMaxD + 1) + NMAX * kLaMaxD + NMAX * NMAX + kLaMaxD * (kLaChunk + 1);
+    return commit > verify ? commit : verify;
+}
+
+// COMMIT: the launch may commit (alone or before verifying); without it the
+// LDS is sized for verification only.
+template <int NMAX, bool COMMIT>
 __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int Dk = a.Dk, Dv = a.Dv, H = a.H;
     const bool bf16 = a.bf16 != 0;
-    // carved per phase: verify needs 2 * 64 * 129 (Q, K) + 64 * 128 (V) +
-    // 64 * 64 (W) + 128 * 33 (state chunk) floats; commit 2 * 64 * 128
-    constexpr int kLds = 2 * kMaxNodes * (kLaMaxD + 1) + kMaxNodes * kLaMaxD + kMaxNodes * kMaxNodes +
-                         kLaMaxD * (kLaChunk + 1);
-    __shared__ float lds[kLds];  // 129 KB
+    __shared__ float lds[la_lds_floats<NMAX, COMMIT>()];
     __shared__ int s_par[kMaxNodes];
     __shared__ float s_L[kMaxNodes];
     __shared__ uint64_t s_anc[kMaxNodes];
@@ -65,7 +74,7 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
     __shared__ int s_j[kMaxNodes];
     float* S = a.state + (static_cast<size_t>(b) * H + h) * Dv * Dk;
 
-    if (a.do_commit) {
+    if (COMMIT && a.do_commit) {
         const int N = a.pN;
         la_tree(a.pparent, a.palpha, b, N, H, h, s_par, s_L, s_anc);
         // (device data: out-of-range entries are clamped into the tree)
@@ -77,8 +86,8 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
             s_c[tid] = exp2f(s_L[vstop] - s_L[j]);
         }
         __syncthreads();
-        float* kf = lds;                      // [acc + 1][Dk]
-        float* vf = lds + kLaMaxD * kMaxNodes;  // [acc + 1][Dv]
+        float* kf = lds;                 // [acc + 1][Dk]
+        float* vf = lds + (acc + 1) * Dk;  // [acc + 1][Dv]
         for (int x = tid; x < (acc + 1) * Dk; x += kLaThreads) {
             const int t = x / Dk, d = x - t * Dk;
             kf[x] = la_load(a.pk, bf16, ((static_cast<size_t>(b) * N + s_j[t]) * H + h) * Dk + d);
@@ -88,12 +97,25 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
             vf[x] = la_load(a.pv, bf16, ((static_cast<size_t>(b) * N + s_j[t]) * H + h) * Dv + e);
         }
         __syncthreads();
+        // This thread's column d, rows e0, e0 + estep, ...: every load issued
+        // before the first update.
         const float Av = exp2f(s_L[vstop]);
         const int d = tid % Dk, e0 = tid / Dk, estep = kLaThreads / Dk;
-        for (int e = e0; e < Dv; e += estep) {
-            float s = Av * S[static_cast<size_t>(e) * Dk + d];
-            for (int t = 0; t <= acc; ++t) s = fmaf(s_c[t] * vf[t * Dv + e], kf[t * Dk + d], s);
-            S[static_cast<size_t>(e) * Dk + d] = s;
+        constexpr int kRows = kLaMaxD * kLaMaxD / kLaThreads;  // 64 at most
+        float sv[kRows];
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            const int e = e0 + r * estep;
+            sv[r] = e < Dv ? S[static_cast<size_t>(e) * Dk + d] : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            const int e = e0 + r * estep;
+            if (e < Dv) {
+                float s = Av * sv[r];
+                for (int t = 0; t <= acc; ++t) s = fmaf(s_c[t] * vf[t * Dv + e], kf[t * Dk + d], s);
+                S[static_cast<size_t>(e) * Dk + d] = s;
+            }
         }
         __syncthreads();  // the workgroup's own state writes before its reads below
     }
@@ -103,10 +125,10 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
     la_tree(a.parent, a.alpha, b, N, H, h, s_par, s_L, s_anc);
     const int DkP = Dk + 1;               // padded rows: lanes on different rows hit different banks
     float* Qs = lds;                      // [N][Dk + 1]
-    float* Ks = Qs + kMaxNodes * (kLaMaxD + 1);
-    float* Vs = Ks + kMaxNodes * (kLaMaxD + 1);  // [N][Dv]
-    float* W = Vs + kMaxNodes * kLaMaxD;         // [N][N]
-    float* Sc = W + kMaxNodes * kMaxNodes;       // [Dv][kLaChunk + 1]
+    float* Ks = Qs + NMAX * (kLaMaxD + 1);
+    float* Vs = Ks + NMAX * (kLaMaxD + 1);  // [N][Dv]
+    float* W = Vs + NMAX * kLaMaxD;         // [N][N]
+    float* Sc = W + NMAX * NMAX;            // [Dv][kLaChunk + 1]
     for (int x = tid; x < N * Dk; x += kLaThreads) {
         const int i = x / Dk, d = x - i * Dk;
         const size_t g = ((static_cast<size_t>(b) * N + i) * H + h) * Dk + d;
@@ -131,9 +153,10 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
     }
     // Thread (e, group g): nodes g, g + G, ... with G = 256 / Dv groups.
     const int e = tid % Dv, g = tid / Dv, G = kLaThreads / Dv;
-    float acc[kMaxNodes / 2];  // up to 32 nodes per thread (Dv = 128); 16 for Dv = 64
+    constexpr int kPer = NMAX / 2 > 1 ? NMAX / 2 : 1;  // nodes per thread: NMAX / G, G >= 2
+    float acc[kPer];
 #pragma unroll
-    for (int n = 0; n < kMaxNodes / 2; ++n) acc[n] = 0.f;
+    for (int n = 0; n < kPer; ++n) acc[n] = 0.f;
     for (int c0 = 0; c0 < Dk; c0 += kLaChunk) {
         __syncthreads();  // the previous chunk is consumed (and W is complete)
         for (int x = tid; x < Dv * kLaChunk; x += kLaThreads) {
@@ -142,7 +165,7 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
         }
         __syncthreads();
 #pragma unroll
-        for (int n = 0; n < kMaxNodes / 2; ++n) {
+        for (int n = 0; n < kPer; ++n) {
             const int i = g + n * G;
             if (i < N) {
                 float s = acc[n];
@@ -152,7 +175,7 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
         }
     }
 #pragma unroll
-    for (int n = 0; n < kMaxNodes / 2; ++n) {
+    for (int n = 0; n < kPer; ++n) {
         const int i = g + n * G;
         if (i < N) {
             float o = exp2f(s_L[i]) * acc[n];
@@ -169,7 +192,19 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
 }
 
 int launch_la(const LaArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(la_kernel, dim3(a.H, a.B), dim3(kLaThreads), 0, stream, a);
+    const dim3 grid(a.H, a.B);
+    const bool small = !a.do_verify || a.N <= 16;
+    if (a.do_commit) {
+        if (small)
+            hipLaunchKernelGGL((la_kernel<16, true>), grid, dim3(kLaThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((la_kernel<kMaxNodes, true>), grid, dim3(kLaThreads), 0, stream, a);
+    } else {
+        if (small)
+            hipLaunchKernelGGL((la_kernel<16, false>), grid, dim3(kLaThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((la_kernel<kMaxNodes, false>), grid, dim3(kLaThreads), 0, stream, a);
+    }
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
 
