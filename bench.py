@@ -32,6 +32,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 ROTATE_BYTES = 640 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_llama3_8b_chain_traffic.json")
+READ_PEAK_FILE = os.path.join(ROOT, "profiles", "hbm_read_peak.json")
+READ_PROBE = os.path.join(ROOT, "speculative_decoding_verification_tree_amd", "hbm_read_probe")
 
 
 def parse():
@@ -47,6 +49,8 @@ def parse():
                          "0 keeps two copies, i.e. cache-warm)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--read-peak", action="store_true",
+                    help="only run the streaming-read calibration program (measured HBM read bandwidth)")
     return ap.parse_args()
 
 
@@ -73,12 +77,46 @@ def attn_bytes(w):
     return kv + qo
 
 
+def accept_bytes(w, accept_len, path):
+    """Algorithmic bytes of one acceptance call with the given outcome: the
+    logits row of every node with children read once, the stop row when it is
+    a leaf, and for the rejection rule the draft row of the stop node's first
+    child when it has one; plus the per-node gathers and the outputs."""
+    import numpy as np
+
+    B, N, V = w.B, w.N, w.V
+    par = w.parent if w.parent is not None else np.tile(np.arange(-1, N - 1, dtype=np.int32), (B, 1))
+    rows = 0
+    for b in range(B):
+        has_child = np.zeros(N, dtype=bool)
+        has_child[par[b][1:]] = True
+        rows += int(has_child.sum())
+        v = int(path[b][int(accept_len[b])])
+        if not has_child[v]:
+            rows += 1
+        elif w.rule == "reject":
+            rows += 1
+    gathers = B * (N - 1) * (4 + 4 + 4 + 4 + 4)  # token, parent, u, draft prob and logit at the token
+    outputs = B * (1 + 2 * N) * 4
+    return rows * V * 4 + gathers + outputs
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part of this "
               "build", file=sys.stderr)
         sys.exit(2)
+
+    if args.read_peak:
+        # A child process of its own (nothing here has touched the GPU yet).
+        import subprocess
+        if not os.path.exists(READ_PROBE):
+            sys.exit(f"{READ_PROBE} is not built (run __graft_entry__.build())")
+        res = subprocess.run([READ_PROBE], capture_output=True, text=True)
+        sys.stderr.write(res.stderr)
+        print(res.stdout.strip(), flush=True)
+        sys.exit(res.returncode)
 
     import numpy as np
     import torch
@@ -305,6 +343,11 @@ def main():
 
     a_bytes = attn_bytes(w)
     achieved = a_bytes / (attn_ms * 1e-3) / 1e9
+    acc_bytes = accept_bytes(w, copies[0]["al"].cpu().numpy(), copies[0]["path"].cpu().numpy())
+    read_peak = None
+    if os.path.exists(READ_PEAK_FILE):
+        with open(READ_PEAK_FILE) as f:
+            read_peak = json.load(f).get("kv_read_GBs")
     traffic = None
     khash = kernel_source_hash()
     if os.path.exists(TRAFFIC_FILE):
@@ -392,6 +435,17 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": a_bytes,
             "kernel_source_hash": khash,
+            "measured_read_peak": read_peak,
+            "frac_of_measured_read_peak": None if read_peak is None else achieved / read_peak,
+        },
+        "accept_roofline": {
+            "bound": "hbm",
+            "calls": "spec_accept_reject" if w.rule == "reject" else "spec_accept_typical",
+            "achieved": acc_bytes / (accept_ms * 1e-3) / 1e9,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": acc_bytes / (accept_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes_per_call": acc_bytes,
         },
         "cpu_baseline": cpu,
         "accept_len_last_step": al.tolist()[:8],
