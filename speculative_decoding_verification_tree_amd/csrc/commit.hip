@@ -7,50 +7,68 @@
 // a + 1 (the root and the a accepted drafts).
 //
 // In-place safety: path is strictly increasing with path[d] >= d, so for
-// d' > d the source L_b + path[d'] lies above the destination L_b + d.  One
-// thread owns one 16-byte column of every row of a (request, kv head,
-// K-or-V) slab and walks d upwards, reading each source before the write that
-// could cover it; columns never overlap between threads.  A chain
-// (path[d] == d) moves nothing.
+// d' > d the source L_b + path[d'] lies above the destination L_b + d: no
+// source is ever a destination of a smaller d.  One workgroup per request;
+// a thread owns 16-byte columns of the (kv head, K-or-V) slabs and takes
+// each column's moves d = 1..a in ascending batches, every load of a batch
+// issued before its first store (the loads of a batch are in flight
+// together instead of one dependent round trip per row; a batch past d = a
+// re-reads row a, never stored).  Columns never overlap between threads.  A
+// chain (path[d] == d) moves nothing.
+#include <algorithm>
+
 #include "spec_common.h"
 #include "spec_internal.h"
 
 namespace specv {
 
-__global__ __launch_bounds__(256) void commit_kv(void* k, void* v, int32_t* prefix_len, const int32_t* path,
-                                                 const int32_t* accept_len, int N, int Hkv, int cap,
-                                                 int row_bytes) {
+constexpr int kCommitThreads = 1024;
+constexpr int kCommitBatch = 8;
+
+__global__ __launch_bounds__(kCommitThreads) void commit_kv(void* k, void* v, int32_t* prefix_len, const int32_t* path,
+                                                            const int32_t* accept_len, int N, int Hkv, int cap,
+                                                            int row_bytes) {
     const int b = blockIdx.x;
     const int L = prefix_len[b];
-    int acount = accept_len[b];
+    const int acount = accept_len[b];
     __shared__ int s_src[kMaxNodes];
-    __shared__ int s_ok;
-    if (threadIdx.x == 0) {
-        s_ok = (L >= 0 && L + N <= cap && acount >= 0 && acount < N) ? 1 : 0;
-    }
+    __shared__ int s_nmove;
+    if (!(L >= 0 && L + N <= cap && acount >= 0 && acount < N)) return;  // uniform across the workgroup
+    if (threadIdx.x == 0) s_nmove = 0;
     __syncthreads();
-    if (!s_ok) return;
     if (threadIdx.x <= acount) {
-        int p = path[static_cast<size_t>(b) * N + threadIdx.x];
-        s_src[threadIdx.x] = (p >= 0 && p < N) ? p : static_cast<int>(threadIdx.x);
+        const int p = path[static_cast<size_t>(b) * N + threadIdx.x];
+        const int src = (p >= 0 && p < N) ? p : static_cast<int>(threadIdx.x);
+        s_src[threadIdx.x] = src;
+        if (src != static_cast<int>(threadIdx.x)) atomicAdd(&s_nmove, 1);
     }
     __syncthreads();
-    const int cols = row_bytes / 16;
-    const int total = 2 * Hkv * cols;
-    for (int col = threadIdx.x; col < total; col += blockDim.x) {
-        const int which = col / (Hkv * cols);
-        const int g = (col / cols) % Hkv;
-        const int cc = col % cols;
-        unsigned char* base = static_cast<unsigned char*>(which ? v : k) +
-                              (static_cast<size_t>(b) * Hkv + g) * cap * static_cast<size_t>(row_bytes) + cc * 16;
-        for (int d = 1; d <= acount; ++d) {
-            const int s = s_src[d];
-            if (s == d) continue;
-            const u32x4 x = *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(L + s) * row_bytes);
-            *reinterpret_cast<u32x4*>(base + static_cast<size_t>(L + d) * row_bytes) = x;
+    if (s_nmove > 0) {
+        const int cols = row_bytes / 16;
+        const int total = 2 * Hkv * cols;
+        for (int col = threadIdx.x; col < total; col += blockDim.x) {
+            const int which = col / (Hkv * cols);
+            const int g = (col / cols) % Hkv;
+            unsigned char* base = static_cast<unsigned char*>(which ? v : k) +
+                                  (static_cast<size_t>(b) * Hkv + g) * cap * static_cast<size_t>(row_bytes) +
+                                  (col % cols) * 16;
+            for (int d0 = 1; d0 <= acount; d0 += kCommitBatch) {
+                u32x4 x[kCommitBatch];
+#pragma unroll
+                for (int j = 0; j < kCommitBatch; ++j) {
+                    const int d = min(d0 + j, acount);
+                    x[j] = *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(L + s_src[d]) * row_bytes);
+                }
+#pragma unroll
+                for (int j = 0; j < kCommitBatch; ++j) {
+                    const int d = d0 + j;
+                    if (d <= acount && s_src[d] != d)
+                        *reinterpret_cast<u32x4*>(base + static_cast<size_t>(L + d) * row_bytes) = x[j];
+                }
+            }
         }
     }
-    __syncthreads();
+    __syncthreads();  // every thread has read L before it changes
     if (threadIdx.x == 0) prefix_len[b] = L + acount + 1;
 }
 
@@ -81,7 +99,10 @@ __global__ __launch_bounds__(64) void validate_tree(const int32_t* parent, int N
 int launch_commit(const spec_attn_desc& d, void* k, void* v, int32_t* prefix_len, const int32_t* path,
                   const int32_t* accept_len, hipStream_t stream) {
     const int es = d.dtype == SPEC_BF16 ? 2 : 4;
-    hipLaunchKernelGGL(commit_kv, dim3(d.batch), dim3(256), 0, stream, k, v, prefix_len, path, accept_len,
+    // One thread per 16-byte column of the request's slabs, up to 1024.
+    const long cols = 2L * d.num_kv_heads * (d.head_dim * es / 16);
+    const int threads = static_cast<int>(std::min<long>(kCommitThreads, std::max<long>(64, (cols + 63) / 64 * 64)));
+    hipLaunchKernelGGL(commit_kv, dim3(d.batch), dim3(threads), 0, stream, k, v, prefix_len, path, accept_len,
                        d.num_nodes, d.num_kv_heads, d.kv_capacity, d.head_dim * es);
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }

@@ -200,6 +200,41 @@ def test_commit_matches_oracle(cid, over):
     np.testing.assert_array_equal(vv.view(np.uint8), v.view(view).view(np.uint8))
 
 
+@pytest.mark.parametrize("dtype,hkv", [("bf16", 40), ("f32", 24)])
+def test_commit_long_paths_many_columns(dtype, hkv):
+    """Commit with more 16-byte columns than threads (several per thread) and
+    paths longer than one load batch, against the oracle's read-all-then-write
+    copy.  Paths are supplied directly: every second node (0, 2, 4, ...), so
+    every row moves and each source lies two rows above its destination."""
+    from tests.gpu_helpers import dev_kv
+    announce(f"commit long paths dtype={dtype} hkv={hkv}")
+    rng = np.random.default_rng([7, 11])
+    B, N, D, cap = 4, 26, 128, 96
+    if dtype == "bf16":
+        k = rng.integers(0, 1 << 16, size=(B, hkv, cap, D), dtype=np.uint16)
+        v = rng.integers(0, 1 << 16, size=(B, hkv, cap, D), dtype=np.uint16)
+    else:
+        k = rng.standard_normal((B, hkv, cap, D)).astype(np.float32)
+        v = rng.standard_normal((B, hkv, cap, D)).astype(np.float32)
+    prefix = np.array([0, 17, 40, 70], dtype=np.int32)
+    accept = np.array([12, 0, 9, 3], dtype=np.int32)
+    path = np.full((B, N), -1, dtype=np.int32)
+    for b in range(B):
+        path[b, : accept[b] + 1] = 2 * np.arange(accept[b] + 1)
+    kd, vd = dev_kv(k, dtype), dev_kv(v, dtype)
+    pl = torch.from_numpy(prefix.copy()).cuda()
+    sv.spec_commit_kv(kd, vd, pl, torch.from_numpy(path).cuda(), torch.from_numpy(accept).cuda())
+    torch.cuda.synchronize()
+    kk, vv = k.copy(), v.copy()
+    pl_ref = oracle.commit(kk, vv, prefix.copy(), path, accept)
+    np.testing.assert_array_equal(pl.cpu().numpy(), pl_ref)
+    view = np.int16 if dtype == "bf16" else np.float32
+    got_k = kd.view(torch.int16).cpu().numpy() if dtype == "bf16" else kd.cpu().numpy()
+    got_v = vd.view(torch.int16).cpu().numpy() if dtype == "bf16" else vd.cpu().numpy()
+    np.testing.assert_array_equal(got_k.view(np.uint8), kk.view(view).view(np.uint8))
+    np.testing.assert_array_equal(got_v.view(np.uint8), vv.view(view).view(np.uint8))
+
+
 def test_positions_and_validate():
     announce("positions / validate")
     w = generate(scaled(5, batch=5, prefix_len=(0, 100), vocab=10), with_attention=False, with_accept=False)
