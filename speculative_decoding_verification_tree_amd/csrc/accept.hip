@@ -350,7 +350,10 @@ struct WaveRed {
 // lowest index of the max is the first element equal to it.  Each wave
 // reduces relative to its own max; one barrier, then wave 0 merges the four
 // waves (the results are valid in wave 0 only).
-template <int EPT, bool FILT = false>
+// ARG = false skips the lowest argmax (arg is left at 0x7fffffff) and ENT =
+// false the entropy sum (A2 stays 0): the rejection rule at T > 0 uses
+// neither, and both cost VALU work per element in a VALU-heavy pass.
+template <int EPT, bool FILT = false, bool ARG = true, bool ENT = true>
 __device__ __forceinline__ void chunk_stats(const float* row, int x0, int x1, bool vec4, float T, float& M, int& arg,
                                             double& S, double& A2, WaveRed* s, uint32_t tau = 0u) {
     const Vals<EPT> vals = load_chunk<EPT>(row, x0, x1, vec4, -INFINITY);
@@ -363,9 +366,13 @@ __device__ __forceinline__ void chunk_stats(const float* row, int x0, int x1, bo
 #pragma unroll
     for (int e = 0; e < EPT; ++e) best = fmaxf(best, vals.v[e]);
     int bi = 0x7fffffff;
+    if constexpr (ARG) {
 #pragma unroll
-    for (int e = EPT - 1; e >= 0; --e) bi = vals.v[e] == best && off(e) < lim ? first + off(e) : bi;
-    wave_argmax(best, bi);
+        for (int e = EPT - 1; e >= 0; --e) bi = vals.v[e] == best && off(e) < lim ? first + off(e) : bi;
+        wave_argmax(best, bi);
+    } else {
+        best = wave_max(best);
+    }
     double sw = 0.0, aw = 0.0;
     if (T > 0.f && best > -INFINITY) {
         // The thread's terms are summed pairwise in fp32 (same-sign terms:
@@ -379,12 +386,14 @@ __device__ __forceinline__ void chunk_stats(const float* row, int x0, int x1, bo
             // the chunk's, which is kept whenever any token of it is)
             const bool in = off(e) < lim && (!FILT || logit_key(vals.v[e]) >= tau);
             ex[e] = in ? __builtin_amdgcn_exp2f(t2) : 0.f;
-            ax[e] = in ? t2 * ex[e] : 0.f;
+            ax[e] = ENT && in ? t2 * ex[e] : 0.f;
         }
         pairwise_sum<EPT>(ex);
-        pairwise_sum<EPT>(ax);
         sw = wave_sum(static_cast<double>(ex[0]));
-        aw = wave_sum(static_cast<double>(ax[0]));
+        if constexpr (ENT) {
+            pairwise_sum<EPT>(ax);
+            aw = wave_sum(static_cast<double>(ax[0]));
+        }
     }
     const int lane = tid & 63, wv = tid >> 6;
     if (lane == 0) {
@@ -428,7 +437,7 @@ __device__ __forceinline__ bool row_has_children(const AcceptArgs& a, int b, int
     return __ballot(p == u) != 0ull;
 }
 
-template <int EPT>
+template <int EPT, bool ARG, bool ENT>
 __global__ __launch_bounds__(kThreads) void accept_rowstats(AcceptArgs a) {
     const int c = blockIdx.x, u = blockIdx.y, b = blockIdx.z;
     __shared__ WaveRed s_red;
@@ -438,7 +447,7 @@ __global__ __launch_bounds__(kThreads) void accept_rowstats(AcceptArgs a) {
     float M;
     int arg;
     double S, A2;
-    chunk_stats<EPT>(row, x0, x1, a.vec4 != 0, a.T, M, arg, S, A2, &s_red);
+    chunk_stats<EPT, false, ARG, ENT>(row, x0, x1, a.vec4 != 0, a.T, M, arg, S, A2, &s_red);
     if (threadIdx.x == 0) {
         RowStat rs;
         rs.S = S;
@@ -1526,7 +1535,14 @@ static int launch_accept_ept(const AcceptArgs& a, const AcceptPlan& p, hipStream
         hipLaunchKernelGGL(accept_filter, dim3(a.B * a.N), dim3(kFThreads), 0, stream, a);
         if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     } else if (a.N > 1) {
-        hipLaunchKernelGGL((accept_rowstats<EPT>), dim3(p.nchunk, a.N, a.B), dim3(kThreads), 0, stream, a);
+        // The rejection rule at T > 0 needs neither the argmax (one-hot at
+        // T = 0, greedy final token of the typical rule) nor the entropy.
+        if (a.rule == 0 && a.T > 0.f)
+            hipLaunchKernelGGL((accept_rowstats<EPT, false, false>), dim3(p.nchunk, a.N, a.B), dim3(kThreads), 0, stream,
+                               a);
+        else
+            hipLaunchKernelGGL((accept_rowstats<EPT, true, true>), dim3(p.nchunk, a.N, a.B), dim3(kThreads), 0, stream,
+                               a);
         if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     }
     // Few rows need fewer registers for the decision: more workgroups per CU.
