@@ -377,23 +377,28 @@ __device__ __forceinline__ void block_update(const KRead& kread, const unsigned 
             const uint32_t pre = (1u << npre) - 1u;
             kmask = ((tree & 0xFFu) | pre) & ((1u << nend) - 1u);
         }
-        // Scores scaled to log2 units (masked to -inf only in blocks that
-        // reach past the prefix: a wave-uniform branch).
+        // Raw scores (masked to -inf only in blocks that reach past the
+        // prefix: a wave-uniform branch).  The softmax scale (times log2 e,
+        // > 0) is applied once to the lane's max -- rounding is monotonic, so
+        // max(s) * c == max(s * c) exactly -- and folded into the exponent's
+        // fma below, instead of one multiply per score.
         float s[8];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) s[4 * h + ii] = st[h][ii] * scale_log2;
+            for (int ii = 0; ii < 4; ++ii) s[4 * h + ii] = st[h][ii];
         if (!interior) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) s[e] = ((kmask >> e) & 1u) ? s[e] : -INFINITY;
         }
-        // Lazy rescale: keep the running max unless a row's block max exceeds
-        // it by more than 8 (probabilities stay <= 2^8, exact in fp32 and as
-        // precise in bf16).  A row's max exceeds it iff one of its four lanes'
-        // does, so the wave-uniform test takes each lane's own max; the row
-        // maxima are formed only when some row rescales.
-        float bm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+        // Lazy rescale: keep the running max (log2 units) unless a row's
+        // block max exceeds it by more than 8 (probabilities stay <= 2^8,
+        // exact in fp32 and as precise in bf16).  A row's max exceeds it iff
+        // one of its four lanes' does, so the wave-uniform test takes each
+        // lane's own max; the row maxima are formed only when some row
+        // rescales.
+        float bm =
+            fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]))) * scale_log2;
         if (__builtin_amdgcn_ballot_w64(bm > m_run[t] + 8.f) != 0ull) {
             bm = max_across_rows(bm);
             const float mn = fmaxf(m_run[t], bm);
@@ -407,7 +412,7 @@ __device__ __forceinline__ void block_update(const KRead& kread, const unsigned 
         float p[8], rs = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(s[e] - mu);
+            p[e] = __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, -mu));
             rs += p[e];
         }
         l_run[t] += rs;  // this lane's share of the row sum; the four shares are added at the end
