@@ -912,8 +912,11 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int bf16_out) {
     const int r = static_cast<int>(id % a.R);
     const int bg = static_cast<int>(id / a.R);
     const int b = bg / a.Hkv, g = bg % a.Hkv;
-    if (request_blocks(a, a.prefix_len[b]) == 0) return;  // outside the contract: out left unwritten
+    // The slab record and the prefix length are independent: both loads go out together.
+    const int L = a.prefix_len[b];
     const int2 sp = a.seg[bg];
+    __builtin_amdgcn_sched_barrier(0);
+    if (request_blocks(a, L) == 0) return;  // outside the contract: out left unwritten
     const int first = sp.x, count = sp.y;
     if (count <= 1) return;  // written by its only segment
     // Running (max, sum, O) over batches of SB partials, each batch one round of loads.
@@ -958,6 +961,90 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int bf16_out) {
     const size_t ob = ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D;
 #pragma unroll
     for (int j = 0; j < DPL; ++j) store_out(a.out, bf16_out != 0, ob + lane + 64 * j, acc[j] * inv);
+}
+
+// Split combine for slabs of few partials: a wavefront merges four rows at
+// once (16 lanes per row, D/16 consecutive dims per lane), so the whole grid
+// is resident in one round and every row pays the dependent chain (prefix
+// length, slab record, partials, store) once, with SB partials of each of
+// its four rows in flight together.  Loads come from clamped indexes and
+// are selected afterwards (none under a branch).
+template <int D, int SB>
+__global__ __launch_bounds__(256) void attn_combine4(AttnArgs a, int bf16_out) {
+    constexpr int EPL = D / 16;  // dims per lane
+    constexpr int NV = EPL / 4;  // 16-byte vectors per lane
+    const int lane = threadIdx.x & 63, grp = lane >> 4, sl = lane & 15;
+    const long total = static_cast<long>(a.B) * a.Hkv * a.R;
+    const long id = (static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * 4 + grp;
+    const long idc = id < total ? id : total - 1;
+    const int r = static_cast<int>(idc % a.R);
+    const int bg = static_cast<int>(idc / a.R);
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
+    const int2 sp = a.seg[bg];
+    const bool live = id < total && request_blocks(a, a.prefix_len[b]) != 0 && sp.y > 1;
+    // Rows outside the contract or of a directly written slab read partial 0
+    // (their slab record may be stale) and store nothing.
+    const int first = live ? sp.x : 0, count = live ? sp.y : 0;
+    float M = -INFINITY, lsum = 0.f;
+    float acc[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) acc[j] = 0.f;
+    for (int s0 = 0; __builtin_amdgcn_ballot_w64(s0 < count) != 0ull; s0 += SB) {
+        float2 ml[SB];
+        f32x4 ov[SB][NV];
+#pragma unroll
+        for (int k = 0; k < SB; ++k) {
+            const size_t pi = static_cast<size_t>(first + max(min(s0 + k, count - 1), 0));
+            ml[k] = a.ws_ml[pi * a.R + r];
+            const float* prow = a.ws_o + (pi * a.R + r) * D + sl * EPL;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) ov[k][v] = *reinterpret_cast<const f32x4*>(prow + 4 * v);
+        }
+        // Keep the scheduler from sinking the partials' loads towards their
+        // uses (it would trade them for registers one round trip at a time).
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < SB; ++k)
+            if (s0 + k >= count) ml[k] = make_float2(-INFINITY, 0.f);
+        float Mn = M;
+#pragma unroll
+        for (int k = 0; k < SB; ++k) Mn = fmaxf(Mn, ml[k].x);
+        const float Mu = Mn == -INFINITY ? 0.f : Mn;
+        const float sc = exp2f(M - Mu);
+        lsum *= sc;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) acc[j] *= sc;
+#pragma unroll
+        for (int k = 0; k < SB; ++k) {
+            const float wgt = ml[k].x == -INFINITY ? 0.f : exp2f(ml[k].x - Mu);
+            lsum += wgt * ml[k].y;
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[4 * v + e] += wgt * ov[k][v][e];
+        }
+        M = Mn;
+    }
+    if (!live) return;
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const int node = r / a.G, hq = g * a.G + r % a.G;
+    const size_t ob = ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D + sl * EPL;
+    if (bf16_out) {
+        uint32_t w[EPL / 2];
+#pragma unroll
+        for (int j = 0; j < EPL / 2; ++j) w[j] = pack_bf16x2(acc[2 * j] * inv, acc[2 * j + 1] * inv);
+        uint16_t* o16 = static_cast<uint16_t*>(a.out) + ob;
+#pragma unroll
+        for (int v = 0; v < EPL / 8; ++v)
+            *reinterpret_cast<u32x4*>(o16 + 8 * v) = u32x4{w[4 * v], w[4 * v + 1], w[4 * v + 2], w[4 * v + 3]};
+        if constexpr (EPL % 8 != 0) *reinterpret_cast<uint2*>(o16) = make_uint2(w[0], w[1]);
+    } else {
+        float* o32 = static_cast<float*>(a.out) + ob;
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+            *reinterpret_cast<f32x4*>(o32 + 4 * v) =
+                f32x4{acc[4 * v] * inv, acc[4 * v + 1] * inv, acc[4 * v + 2] * inv, acc[4 * v + 3] * inv};
+    }
 }
 
 // ----------------------------------------------------------------------------
@@ -1186,12 +1273,16 @@ int launch_verify_attn(const spec_attn_desc& d, const AttnPlan& p, const void* q
             most = p.nsplit_max;
         }
         const bool wide = most > 16;  // 32 partials per round (more registers)
-        if (d.head_dim == 128) {
-            if (wide) hipLaunchKernelGGL((attn_combine<128, 32>), cgrid, dim3(256), 0, stream, a, bf16_out);
-            else hipLaunchKernelGGL((attn_combine<128, 16>), cgrid, dim3(256), 0, stream, a, bf16_out);
+        if (!wide) {  // four rows per wavefront, the grid resident at once
+            const dim3 cgrid4(static_cast<unsigned>((rows + 15) / 16));
+            if (d.head_dim == 128)
+                hipLaunchKernelGGL((attn_combine4<128, 8>), cgrid4, dim3(256), 0, stream, a, bf16_out);
+            else
+                hipLaunchKernelGGL((attn_combine4<64, 8>), cgrid4, dim3(256), 0, stream, a, bf16_out);
+        } else if (d.head_dim == 128) {
+            hipLaunchKernelGGL((attn_combine<128, 32>), cgrid, dim3(256), 0, stream, a, bf16_out);
         } else {
-            if (wide) hipLaunchKernelGGL((attn_combine<64, 32>), cgrid, dim3(256), 0, stream, a, bf16_out);
-            else hipLaunchKernelGGL((attn_combine<64, 16>), cgrid, dim3(256), 0, stream, a, bf16_out);
+            hipLaunchKernelGGL((attn_combine<64, 32>), cgrid, dim3(256), 0, stream, a, bf16_out);
         }
         if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     }
