@@ -477,19 +477,45 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
     __shared__ uint32_t s_tau[kMaxNodes];
     __shared__ Decision s_dec;
 
+    // The node's parent entry, token and uniform: three independent loads
+    // with no branch between them (a chain's absent parent array and an
+    // absent uniform array read the tokens instead, selected away later).
+    // Their uses wait until the chunk records are in flight as well.
+    // Every thread loads (lanes past N read node N - 1's entries): a load
+    // under a branch would pull the uses into the branch, ahead of the chunk
+    // records' loads.
+    int praw, xraw;
+    float uraw;
+    {
+        const size_t o = static_cast<size_t>(b) * N + min(lane, N - 1);
+        const int32_t* psrc = a.parent ? a.parent : a.tokens;
+        const float* usrc = a.rule == 0 && a.u_acc ? a.u_acc : reinterpret_cast<const float*>(a.tokens);
+        praw = psrc[o];
+        xraw = a.tokens[o];
+        uraw = usrc[o];
+    }
     int pi = -1, xi = 0;
     float ui = 0.f;
-    if (wave == 0 && lane < N) {
-        pi = tree_parent(a.parent, N, b, lane);
-        const int x = a.tokens[static_cast<size_t>(b) * N + lane];
-        xi = min(max(x, 0), a.V - 1);
-        if (a.rule == 0 && a.u_acc) ui = a.u_acc[static_cast<size_t>(b) * N + lane];
-    }
+    auto node_inputs = [&]() {  // same as tree_parent(), the token clamped into the vocabulary
+        // (selects rather than a branch, so the compiler keeps the uses here,
+        // behind the chunk records' loads)
+        // (integer masks: a select on a uniform flag becomes a branch, and
+        // the compiler then sinks the loads into it)
+        const int mine = -static_cast<int>(wave == 0 && lane < N);
+        const int tree = -static_cast<int>(a.parent != nullptr);
+        const int ptree = (praw >= 0 && praw < lane) ? praw : -2;
+        const int p = (ptree & tree) | ((lane - 1) & ~tree);
+        pi = (p & mine) | (-1 & ~mine);
+        xi = min(max(xraw, 0), a.V - 1) & mine;
+        const int uon = mine & -static_cast<int>(a.rule == 0 && a.u_acc != nullptr);
+        ui = __int_as_float(__float_as_int(uraw) & uon);
+    };
     // The tested values, gathered at the drafted tokens as soon as they land
     // (issued after the loads that depend on nothing).
     float glf = 0.f;
     double gq = 0.0;
     auto gather = [&]() {
+        node_inputs();
         if (wave == 0 && lane >= 1 && lane < N && pi >= 0) {
             glf = a.logits[(static_cast<size_t>(b) * N + pi) * a.V + xi];
             if (a.rule == 0) gq = a.draft[(static_cast<size_t>(b) * N + lane) * a.V + xi];
