@@ -781,11 +781,15 @@ __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, size_t i
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_valu(AttnArgs a) {
-    constexpr int DP = D + 1;
-    __shared__ float s_q[32][DP];
-    __shared__ float s_k[32][DP];
-    __shared__ float s_v[32][DP];
-    __shared__ float s_p[32][33];
+    // Row stride D + 4: 16-byte aligned rows, and the eight rows that a row
+    // group's lanes read at once start on distinct banks.
+    constexpr int DP = D + 4;
+    constexpr int DPL = D / 8;            // dims per thread, contiguous
+    constexpr int NV4 = 32 * D / 4 / 256;  // 16-byte vectors per thread of a 32-row tile
+    __shared__ __attribute__((aligned(16))) float s_q[32][DP];
+    __shared__ __attribute__((aligned(16))) float s_k[32][DP];
+    __shared__ __attribute__((aligned(16))) float s_v[32][DP];
+    __shared__ __attribute__((aligned(16))) float s_p[32][36];
     __shared__ uint64_t s_anc[kMaxNodes];
 
     int unit, rg;
@@ -808,26 +812,46 @@ __global__ __launch_bounds__(256) void attn_valu(AttnArgs a) {
         if (tid < a.N) s_anc[tid] = m;
     }
     const T* qp = static_cast<const T*>(a.q);
-    for (int e = tid; e < 32 * D; e += 256) {
-        const int lr = e / D, d = e % D;
-        const int r = rg * 32 + lr;
-        float x = 0.f;
-        if (r < a.R) {
+    if constexpr (sizeof(T) == 4) {
+        // fp32: 16-byte loads, all of a thread's issued before its LDS stores
+        float4 qr[NV4];
+#pragma unroll
+        for (int i = 0; i < NV4; ++i) {
+            const int e4 = tid + 256 * i, lr = e4 / (D / 4), d4 = e4 % (D / 4);
+            const int r = min(rg * 32 + lr, a.R - 1);
             const int node = r / a.G, hq = g * a.G + r % a.G;
-            x = load_elem(qp, ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D + d);
+            qr[i] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(qp) +
+                                                     ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D + 4 * d4);
         }
-        s_q[lr][d] = x;
+#pragma unroll
+        for (int i = 0; i < NV4; ++i) {
+            const int e4 = tid + 256 * i, lr = e4 / (D / 4), d4 = e4 % (D / 4);
+            *reinterpret_cast<float4*>(&s_q[lr][4 * d4]) = rg * 32 + lr < a.R ? qr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    } else {
+        for (int e = tid; e < 32 * D; e += 256) {
+            const int lr = e / D, d = e % D;
+            const int r = rg * 32 + lr;
+            float x = 0.f;
+            if (r < a.R) {
+                const int node = r / a.G, hq = g * a.G + r % a.G;
+                x = load_elem(qp, ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D + d);
+            }
+            s_q[lr][d] = x;
+        }
     }
     __syncthreads();
 
+    // Thread (sr, sk): query row sr of the tile, keys sk + 8*jj of each
+    // 32-key tile, output dims sk*DPL .. sk*DPL + DPL - 1.
     const int sr = tid >> 3, sk = tid & 7;
     const int r = rg * 32 + sr;
     const bool rvalid = r < a.R;
     const uint64_t anc = rvalid ? s_anc[r / a.G] : ~0ull;
     float m_run = -INFINITY, l_run = 0.f;
-    float o[D / 8];
+    float o[DPL];
 #pragma unroll
-    for (int j = 0; j < D / 8; ++j) o[j] = 0.f;
+    for (int j = 0; j < DPL; ++j) o[j] = 0.f;
 
     const size_t head = (static_cast<size_t>(b) * a.Hkv + g) * a.cap;
     const T* kp = static_cast<const T*>(a.k) + head * D;
@@ -835,24 +859,53 @@ __global__ __launch_bounds__(256) void attn_valu(AttnArgs a) {
 
     for (int kb = k0; kb < k1; kb += 32) {
         __syncthreads();
-        for (int e = tid; e < 32 * D; e += 256) {
-            const int kk = e / D, d = e % D;
-            const size_t row = static_cast<size_t>(min(kb + kk, Tk - 1));
-            s_k[kk][d] = load_elem(kp, row * D + d);
-            s_v[kk][d] = load_elem(vp, row * D + d);
+        if constexpr (sizeof(T) == 4) {
+            // every 16-byte load of the tile in flight before the first LDS store
+            float4 kr[NV4], vr[NV4];
+#pragma unroll
+            for (int i = 0; i < NV4; ++i) {
+                const int e4 = tid + 256 * i, kk = e4 / (D / 4), d4 = e4 % (D / 4);
+                const size_t off = static_cast<size_t>(min(kb + kk, Tk - 1)) * D + 4 * d4;
+                kr[i] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(kp) + off);
+                vr[i] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(vp) + off);
+            }
+#pragma unroll
+            for (int i = 0; i < NV4; ++i) {
+                const int e4 = tid + 256 * i, kk = e4 / (D / 4), d4 = e4 % (D / 4);
+                *reinterpret_cast<float4*>(&s_k[kk][4 * d4]) = kr[i];
+                *reinterpret_cast<float4*>(&s_v[kk][4 * d4]) = vr[i];
+            }
+        } else {
+            for (int e = tid; e < 32 * D; e += 256) {
+                const int kk = e / D, d = e % D;
+                const size_t row = static_cast<size_t>(min(kb + kk, Tk - 1));
+                s_k[kk][d] = load_elem(kp, row * D + d);
+                s_v[kk][d] = load_elem(vp, row * D + d);
+            }
         }
         __syncthreads();
+        // Scores of keys sk + 8*jj: 16-byte LDS reads, the query row's
+        // (a broadcast within the row's eight lanes) shared by the four keys.
+        float dot[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int d = 0; d < D; d += 4) {
+            const float4 qd = *reinterpret_cast<const float4*>(&s_q[sr][d]);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const float4 kv = *reinterpret_cast<const float4*>(&s_k[sk + 8 * jj][d]);
+                dot[jj] = fmaf(qd.x, kv.x, dot[jj]);
+                dot[jj] = fmaf(qd.y, kv.y, dot[jj]);
+                dot[jj] = fmaf(qd.z, kv.z, dot[jj]);
+                dot[jj] = fmaf(qd.w, kv.w, dot[jj]);
+            }
+        }
         float s[4];
         float bm = -INFINITY;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-            const int kk = sk + 8 * jj;
-            const int key = kb + kk;
-            float dot = 0.f;
-#pragma unroll 8
-            for (int d = 0; d < D; ++d) dot = fmaf(s_q[sr][d], s_k[kk][d], dot);
+            const int key = kb + sk + 8 * jj;
             const bool ok = key < k1 && (key < L || ((anc >> (key - L)) & 1ull));
-            s[jj] = ok ? dot * a.scale_log2 : -INFINITY;
+            s[jj] = ok ? dot[jj] * a.scale_log2 : -INFINITY;
             bm = fmaxf(bm, s[jj]);
         }
         // reductions over the 8 lanes of a row (xor 1, xor 2, mirror within 8)
@@ -875,12 +928,23 @@ __global__ __launch_bounds__(256) void attn_valu(AttnArgs a) {
         l_run = l_run * alpha + rs;
         m_run = mn;
 #pragma unroll
-        for (int j = 0; j < D / 8; ++j) o[j] *= alpha;
+        for (int j = 0; j < DPL; ++j) o[j] *= alpha;
         __syncthreads();
-        for (int kk = 0; kk < 32; ++kk) {
-            const float p = s_p[sr][kk];
+#pragma unroll 2
+        for (int k4 = 0; k4 < 32; k4 += 4) {
+            const float4 p4 = *reinterpret_cast<const float4*>(&s_p[sr][k4]);
+            const float pk[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
-            for (int j = 0; j < D / 8; ++j) o[j] = fmaf(p, s_v[kk][sk + 8 * j], o[j]);
+            for (int u = 0; u < 4; ++u) {
+#pragma unroll
+                for (int j = 0; j < DPL; j += 4) {
+                    const float4 vv = *reinterpret_cast<const float4*>(&s_v[k4 + u][sk * DPL + j]);
+                    o[j] = fmaf(pk[u], vv.x, o[j]);
+                    o[j + 1] = fmaf(pk[u], vv.y, o[j + 1]);
+                    o[j + 2] = fmaf(pk[u], vv.z, o[j + 2]);
+                    o[j + 3] = fmaf(pk[u], vv.w, o[j + 3]);
+                }
+            }
         }
     }
     if (sg.table && rg == 0 && tid == 0 && a.seg) a.seg[b * a.Hkv + g] = make_int2(sg.first, sg.count);
@@ -888,13 +952,14 @@ __global__ __launch_bounds__(256) void attn_valu(AttnArgs a) {
     const int node = r / a.G, hq = g * a.G + r % a.G;
     const bool bf16_out = sizeof(T) == 2;
     if (sg.direct) {
-        const size_t ob = ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D;
+        const size_t ob = ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D + sk * DPL;
 #pragma unroll
-        for (int j = 0; j < D / 8; ++j) store_out(a.out, bf16_out, ob + sk + 8 * j, l_run > 0.f ? o[j] / l_run : 0.f);
+        for (int j = 0; j < DPL; ++j) store_out(a.out, bf16_out, ob + j, l_run > 0.f ? o[j] / l_run : 0.f);
     } else {
         const size_t pi = static_cast<size_t>(sg.part);
+        float* prow = a.ws_o + (pi * a.R + r) * D + sk * DPL;
 #pragma unroll
-        for (int j = 0; j < D / 8; ++j) a.ws_o[(pi * a.R + r) * D + sk + 8 * j] = o[j];
+        for (int j = 0; j < DPL; j += 4) *reinterpret_cast<f32x4*>(prow + j) = f32x4{o[j], o[j + 1], o[j + 2], o[j + 3]};
         if (sk == 0) a.ws_ml[pi * a.R + r] = make_float2(m_run, l_run);
     }
 }
