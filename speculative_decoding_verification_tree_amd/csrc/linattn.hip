@@ -26,9 +26,42 @@ constexpr int kLaThreads = 256;
 constexpr int kLaMaxD = 128;
 constexpr int kLaChunk = 32;
 
-__device__ __forceinline__ float la_load(const void* p, bool bf16, size_t i) {
-    if (bf16) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
-    return static_cast<const float*>(p)[i];
+// Rows [0, rows) of `cols` elements (bf16 or fp32, row t at global element
+// offset row_off(t)) into LDS dst[t * ldst + c], in rounds of kLaBatch
+// elements per thread: every load of a round issued before its first LDS
+// store (a load followed by its store in one loop body costs one round trip
+// per element).
+constexpr int kLaBatch = 8;
+
+template <class RowOff>
+__device__ __forceinline__ void la_rows_to_lds(const void* src, bool bf16, int rows, int cols, RowOff row_off, float* dst,
+                                               int ldst) {
+    const int tid = threadIdx.x, n = rows * cols;
+    for (int base = 0; base < n; base += kLaBatch * kLaThreads) {
+        float v[kLaBatch];
+        if (bf16) {
+#pragma unroll
+            for (int j = 0; j < kLaBatch; ++j) {
+                const int x = min(base + tid + j * kLaThreads, n - 1), t = x / cols;
+                v[j] = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(src)[row_off(t) + (x - t * cols)])
+                                       << 16);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kLaBatch; ++j) {
+                const int x = min(base + tid + j * kLaThreads, n - 1), t = x / cols;
+                v[j] = static_cast<const float*>(src)[row_off(t) + (x - t * cols)];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kLaBatch; ++j) {
+            const int x = base + tid + j * kLaThreads;
+            if (x < n) {
+                const int t = x / cols;
+                dst[t * ldst + (x - t * cols)] = v[j];
+            }
+        }
+    }
 }
 
 // Root-path structure of request b's tree of N nodes (thread 0, nodes in
@@ -88,14 +121,10 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
         __syncthreads();
         float* kf = lds;                 // [acc + 1][Dk]
         float* vf = lds + (acc + 1) * Dk;  // [acc + 1][Dv]
-        for (int x = tid; x < (acc + 1) * Dk; x += kLaThreads) {
-            const int t = x / Dk, d = x - t * Dk;
-            kf[x] = la_load(a.pk, bf16, ((static_cast<size_t>(b) * N + s_j[t]) * H + h) * Dk + d);
-        }
-        for (int x = tid; x < (acc + 1) * Dv; x += kLaThreads) {
-            const int t = x / Dv, e = x - t * Dv;
-            vf[x] = la_load(a.pv, bf16, ((static_cast<size_t>(b) * N + s_j[t]) * H + h) * Dv + e);
-        }
+        la_rows_to_lds(a.pk, bf16, acc + 1, Dk,
+                              [&](int t) { return ((static_cast<size_t>(b) * N + s_j[t]) * H + h) * Dk; }, kf, Dk);
+        la_rows_to_lds(a.pv, bf16, acc + 1, Dv,
+                              [&](int t) { return ((static_cast<size_t>(b) * N + s_j[t]) * H + h) * Dv; }, vf, Dv);
         __syncthreads();
         // This thread's column d, rows e0, e0 + estep, ...: every load issued
         // before the first update.
@@ -129,15 +158,12 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
     float* Vs = Ks + NMAX * (kLaMaxD + 1);  // [N][Dv]
     float* W = Vs + NMAX * kLaMaxD;         // [N][N]
     float* Sc = W + NMAX * NMAX;            // [Dv][kLaChunk + 1]
-    for (int x = tid; x < N * Dk; x += kLaThreads) {
-        const int i = x / Dk, d = x - i * Dk;
-        const size_t g = ((static_cast<size_t>(b) * N + i) * H + h) * Dk + d;
-        Qs[i * DkP + d] = la_load(a.q, bf16, g);
-        Ks[i * DkP + d] = la_load(a.k, bf16, g);
-    }
-    for (int x = tid; x < N * Dv; x += kLaThreads) {
-        const int i = x / Dv, e = x - i * Dv;
-        Vs[x] = la_load(a.v, bf16, ((static_cast<size_t>(b) * N + i) * H + h) * Dv + e);
+    {
+        auto rk = [&](int i) { return ((static_cast<size_t>(b) * N + i) * H + h) * Dk; };
+        auto rv = [&](int i) { return ((static_cast<size_t>(b) * N + i) * H + h) * Dv; };
+        la_rows_to_lds(a.q, bf16, N, Dk, rk, Qs, DkP);
+        la_rows_to_lds(a.k, bf16, N, Dk, rk, Ks, DkP);
+        la_rows_to_lds(a.v, bf16, N, Dv, rv, Vs, Dv);
     }
     __syncthreads();
     // W[i][j] = A(j -> i] (q_i . k_j) for j on i's root path, else 0.
@@ -157,12 +183,34 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
     float acc[kPer];
 #pragma unroll
     for (int n = 0; n < kPer; ++n) acc[n] = 0.f;
+    // The state's 32-column chunks as 16-byte loads (four per thread for Dv =
+    // 128), the next chunk loaded while the current one is used.
+    constexpr int kS4 = kLaMaxD * kLaChunk / 4 / kLaThreads;
+    const int n4 = Dv * (kLaChunk / 4);
+    float4 sreg[kS4];
+    auto load_chunk = [&](int c0) {
+#pragma unroll
+        for (int j = 0; j < kS4; ++j) {
+            const int x = min(tid + j * kLaThreads, n4 - 1), r = x / (kLaChunk / 4), c4 = x - r * (kLaChunk / 4);
+            sreg[j] = *reinterpret_cast<const float4*>(S + static_cast<size_t>(r) * Dk + c0 + 4 * c4);
+        }
+    };
+    load_chunk(0);
     for (int c0 = 0; c0 < Dk; c0 += kLaChunk) {
         __syncthreads();  // the previous chunk is consumed (and W is complete)
-        for (int x = tid; x < Dv * kLaChunk; x += kLaThreads) {
-            const int r = x / kLaChunk, cc = x - r * kLaChunk;
-            Sc[r * (kLaChunk + 1) + cc] = S[static_cast<size_t>(r) * Dk + c0 + cc];
+#pragma unroll
+        for (int j = 0; j < kS4; ++j) {
+            const int x = tid + j * kLaThreads;
+            if (x < n4) {
+                const int r = x / (kLaChunk / 4), c4 = x - r * (kLaChunk / 4);
+                float* dst = Sc + r * (kLaChunk + 1) + 4 * c4;
+                dst[0] = sreg[j].x;
+                dst[1] = sreg[j].y;
+                dst[2] = sreg[j].z;
+                dst[3] = sreg[j].w;
+            }
         }
+        if (c0 + kLaChunk < Dk) load_chunk(c0 + kLaChunk);
         __syncthreads();
 #pragma unroll
         for (int n = 0; n < kPer; ++n) {
