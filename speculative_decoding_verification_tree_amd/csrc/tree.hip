@@ -100,20 +100,31 @@ __global__ __launch_bounds__(256) void tree_rope(TreeRopeArgs a) {
     sincos(theta, &sn, &cs);
     T* q = static_cast<T*>(a.q);
     T* k = static_cast<T*>(a.k);
-    const int rows = a.Hq + a.Hkv, step = 256 / half;
-    for (int r = tid / half; r < rows; r += step) {
-        size_t base;
-        T* p;
-        if (r < a.Hq) {
-            p = q;
-            base = ((static_cast<size_t>(b) * a.N + i) * a.Hq + r) * a.D;
-        } else {
-            p = k;
-            base = ((static_cast<size_t>(b) * a.Hkv + (r - a.Hq)) * a.cap + L + i) * a.D;
+    const int rows = a.Hq + a.Hkv, step = 256 / half, r0 = tid / half;
+    if (r0 >= rows) return;
+    const int nr = (rows - r0 + step - 1) / step;  // rows of this thread: r0, r0 + step, ...
+    // Rounds of kRopeBatch rows: every load of a round issued before its
+    // first store (rows never overlap, so no store feeds a later load).
+    constexpr int kRopeBatch = 8;
+    for (int it0 = 0; it0 < nr; it0 += kRopeBatch) {
+        T* ptr[kRopeBatch];
+        double x[kRopeBatch], y[kRopeBatch];
+#pragma unroll
+        for (int u = 0; u < kRopeBatch; ++u) {
+            const int r = r0 + min(it0 + u, nr - 1) * step;  // past the end: this thread's last row, reloaded
+            T* p = r < a.Hq ? q + ((static_cast<size_t>(b) * a.N + i) * a.Hq + r) * a.D
+                            : k + ((static_cast<size_t>(b) * a.Hkv + (r - a.Hq)) * a.cap + L + i) * a.D;
+            ptr[u] = p;
+            x[u] = rope_load(p, j);
+            y[u] = rope_load(p, j + half);
         }
-        const double x = rope_load(p, base + j), y = rope_load(p, base + j + half);
-        rope_store(p, base + j, x * cs - y * sn);
-        rope_store(p, base + j + half, x * sn + y * cs);
+#pragma unroll
+        for (int u = 0; u < kRopeBatch; ++u) {
+            if (it0 + u < nr) {
+                rope_store(ptr[u], j, x[u] * cs - y[u] * sn);
+                rope_store(ptr[u], j + half, x[u] * sn + y[u] * cs);
+            }
+        }
     }
 }
 
