@@ -66,6 +66,7 @@ struct AttnArgs {
     int split_blocks;  // fixed: 32-key blocks per split
     int max_keys;      // host bound on L_b + N
     float scale_log2;  // softmax scale * log2(e)
+    int bf16p;         // MFMA partials stored as bf16 (slabs of few partials, merged by attn_combine4)
 };
 
 // Largest batch the balanced mode serves (its block-count scan lives in LDS).
@@ -441,7 +442,7 @@ __device__ __forceinline__ void block_update(const KRead& kread, const unsigned 
 // registers: lane (n, q) holds row n of each tile (dims 16c + 4q .. +3 of O
 // and the row's running max and sum).  The normalised output when the
 // segment covers its slab, else the partial.
-template <int D, int RT>
+template <int D, int RT, bool BF16P = true>  // BF16P = false: the caller never stores bf16 partials
 __device__ __forceinline__ void write_rows(const AttnArgs& a, const Seg& cur, int row0, const float (&m_run)[RT],
                                            const float (&l_run)[RT], const f32x4 (&o)[RT][D / 16]) {
     const int lane = threadIdx.x & 63, n16 = lane & 15, q4 = lane >> 4;
@@ -465,9 +466,18 @@ __device__ __forceinline__ void write_rows(const AttnArgs& a, const Seg& cur, in
                 *reinterpret_cast<uint2*>(orow + 16 * c + 4 * q4) = pk;
             }
         } else {
-            float* prow = a.ws_o + (static_cast<size_t>(cur.part) * a.R + r) * D;
+            const size_t po = (static_cast<size_t>(cur.part) * a.R + r) * D;
+            if (BF16P && a.bf16p) {  // half the bytes: the partials compete with the KV stream for HBM
+                uint16_t* prow = reinterpret_cast<uint16_t*>(a.ws_o) + po;
 #pragma unroll
-            for (int c = 0; c < D / 16; ++c) *reinterpret_cast<f32x4*>(prow + 16 * c + 4 * q4) = o[t][c];
+                for (int c = 0; c < D / 16; ++c)
+                    *reinterpret_cast<uint2*>(prow + 16 * c + 4 * q4) =
+                        make_uint2(pack_bf16x2(o[t][c][0], o[t][c][1]), pack_bf16x2(o[t][c][2], o[t][c][3]));
+            } else {
+                float* prow = a.ws_o + po;
+#pragma unroll
+                for (int c = 0; c < D / 16; ++c) *reinterpret_cast<f32x4*>(prow + 16 * c + 4 * q4) = o[t][c];
+            }
             if (q4 == 0) a.ws_ml[static_cast<size_t>(cur.part) * a.R + r] = make_float2(m_run[t], l_row[t]);
         }
     }
@@ -759,7 +769,7 @@ __global__ __launch_bounds__(64 * WK) __attribute__((amdgpu_waves_per_eu(2))) vo
             bi ^= 1;
             sel ^= 1;
         }
-        write_rows<D, RT>(a, cur, row0, m_run, l_run, o);
+        write_rows<D, RT, false>(a, cur, row0, m_run, l_run, o);
         if (cur.table && rg == 0 && tid == 0 && a.seg) a.seg[b * a.Hkv + g] = make_int2(cur.first, cur.count);
         if (!next_segment(a, it, s_cum, s_len, cur)) break;
     }
@@ -1034,7 +1044,7 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int bf16_out) {
 // length, slab record, partials, store) once, with SB partials of each of
 // its four rows in flight together.  Loads come from clamped indexes and
 // are selected afterwards (none under a branch).
-template <int D, int SB>
+template <int D, int SB, bool BP>  // BP: bf16 partials
 __global__ __launch_bounds__(256) void attn_combine4(AttnArgs a, int bf16_out) {
     constexpr int EPL = D / 16;  // dims per lane
     constexpr int NV = EPL / 4;  // 16-byte vectors per lane
@@ -1061,9 +1071,29 @@ __global__ __launch_bounds__(256) void attn_combine4(AttnArgs a, int bf16_out) {
         for (int k = 0; k < SB; ++k) {
             const size_t pi = static_cast<size_t>(first + max(min(s0 + k, count - 1), 0));
             ml[k] = a.ws_ml[pi * a.R + r];
-            const float* prow = a.ws_o + (pi * a.R + r) * D + sl * EPL;
+            if constexpr (BP) {  // EPL bf16 values: one 16-byte load (D = 128) or 8-byte load (D = 64)
+                const uint16_t* prow = reinterpret_cast<const uint16_t*>(a.ws_o) + (pi * a.R + r) * D + sl * EPL;
+                uint32_t w[EPL / 2];
+                if constexpr (EPL == 8) {
+                    const u32x4 u = *reinterpret_cast<const u32x4*>(prow);
+                    w[0] = u[0];
+                    w[1] = u[1];
+                    w[2] = u[2];
+                    w[3] = u[3];
+                } else {
+                    const uint2 u = *reinterpret_cast<const uint2*>(prow);
+                    w[0] = u.x;
+                    w[1] = u.y;
+                }
 #pragma unroll
-            for (int v = 0; v < NV; ++v) ov[k][v] = *reinterpret_cast<const f32x4*>(prow + 4 * v);
+                for (int v = 0; v < NV; ++v)
+                    ov[k][v] = f32x4{__uint_as_float(w[2 * v] << 16), __uint_as_float(w[2 * v] & 0xFFFF0000u),
+                                     __uint_as_float(w[2 * v + 1] << 16), __uint_as_float(w[2 * v + 1] & 0xFFFF0000u)};
+            } else {
+                const float* prow = a.ws_o + (pi * a.R + r) * D + sl * EPL;
+#pragma unroll
+                for (int v = 0; v < NV; ++v) ov[k][v] = *reinterpret_cast<const f32x4*>(prow + 4 * v);
+            }
         }
         // Keep the scheduler from sinking the partials' loads towards their
         // uses (it would trade them for registers one round trip at a time).
@@ -1292,6 +1322,20 @@ int launch_verify_attn(const spec_attn_desc& d, const AttnPlan& p, const void* q
         units = slabs * p.nsplit_max;
         combine = p.nsplit_max > 1;
     }
+    // Partials of the longest slab: its blocks over the blocks per range
+    // (plus one for a range that starts inside it), or its splits.  Up to 16
+    // go to attn_combine4, which takes MFMA partials in bf16.
+    long most;
+    if (p.balanced) {
+        const long per = (slabs * ((static_cast<long>(p.max_keys) + 31) / 32)) / a.nparts;
+        most = per > 0 ? ((p.max_keys + 31) / 32 + per - 1) / per + 1 : a.nparts;
+    } else {
+        most = p.nsplit_max;
+    }
+    const bool wide = most > 16;  // one row per wavefront, 32 partials per round (more registers)
+    // (the many-row kernel keeps fp32 partials: the bf16 store path cost it
+    // registers and time)
+    a.bf16p = combine && p.mfma && p.waves == 1 && !wide ? 1 : 0;
     if (combine) {
         const long parts = p.balanced ? p.parts_max + slabs : slabs * p.nsplit_max;
         char* ws = static_cast<char*>(workspace);
@@ -1328,22 +1372,18 @@ int launch_verify_attn(const spec_attn_desc& d, const AttnPlan& p, const void* q
         const long rows = slabs * p.rows;
         const dim3 cgrid(static_cast<unsigned>((rows + 3) / 4));
         const int bf16_out = d.dtype == SPEC_BF16;
-        // Partials of the longest slab: its blocks over the blocks per range
-        // (plus one for a range that starts inside it), or its splits.
-        long most;
-        if (p.balanced) {
-            const long per = (slabs * ((static_cast<long>(p.max_keys) + 31) / 32)) / a.nparts;
-            most = per > 0 ? ((p.max_keys + 31) / 32 + per - 1) / per + 1 : a.nparts;
-        } else {
-            most = p.nsplit_max;
-        }
-        const bool wide = most > 16;  // 32 partials per round (more registers)
         if (!wide) {  // four rows per wavefront, the grid resident at once
             const dim3 cgrid4(static_cast<unsigned>((rows + 15) / 16));
-            if (d.head_dim == 128)
-                hipLaunchKernelGGL((attn_combine4<128, 8>), cgrid4, dim3(256), 0, stream, a, bf16_out);
-            else
-                hipLaunchKernelGGL((attn_combine4<64, 8>), cgrid4, dim3(256), 0, stream, a, bf16_out);
+            if (a.bf16p) {
+                if (d.head_dim == 128)
+                    hipLaunchKernelGGL((attn_combine4<128, 8, true>), cgrid4, dim3(256), 0, stream, a, bf16_out);
+                else
+                    hipLaunchKernelGGL((attn_combine4<64, 8, true>), cgrid4, dim3(256), 0, stream, a, bf16_out);
+            } else if (d.head_dim == 128) {
+                hipLaunchKernelGGL((attn_combine4<128, 8, false>), cgrid4, dim3(256), 0, stream, a, bf16_out);
+            } else {
+                hipLaunchKernelGGL((attn_combine4<64, 8, false>), cgrid4, dim3(256), 0, stream, a, bf16_out);
+            }
         } else if (d.head_dim == 128) {
             hipLaunchKernelGGL((attn_combine<128, 32>), cgrid, dim3(256), 0, stream, a, bf16_out);
         } else {
