@@ -22,9 +22,11 @@
 //   fixed    : split s of slab q takes blocks [s*C, (s+1)*C) (large batches,
 //              where slabs far outnumber resident workgroups; VALU path).
 // A slab covered by one segment is written straight to out; otherwise each
-// segment writes its unnormalised partial (O, max, sum) and attn_combine
-// merges a slab's partials with an exact log-sum-exp rescale, from the
-// (first partial, count) table the segments leave in the workspace.
+// segment writes its unnormalised partial (O, max, sum) -- O in bf16 when
+// attn_combine4 merges few partials per slab, else fp32 -- and attn_combine4
+// or attn_combine merges a slab's partials with an exact log-sum-exp
+// rescale, from the (first partial, count) table the segments leave in the
+// workspace.
 //
 // The MFMA path runs one wavefront per workgroup: the wave streams its range
 // with nothing to wait for but its own loads (no workgroup barrier, no
