@@ -81,7 +81,9 @@ size_t spec_verify_attn_workspace_bytes(const spec_attn_desc* desc, int32_t max_
  *   prefix_len      [B] int32, device
  *   parent          [B][N] int32 or NULL (chain)
  *   out             [B][N][Hq][D] (dtype), written
- *   workspace       >= spec_verify_attn_workspace_bytes(desc, max_prefix_len) */
+ *   workspace       >= spec_verify_attn_workspace_bytes(desc, max_prefix_len)
+ * q, k_cache, v_cache, out and a non-empty workspace must be 16-byte aligned
+ * (the kernels move them in 16-byte vectors), else SPEC_EINVAL. */
 int spec_verify_attn(const spec_attn_desc* desc, int32_t max_prefix_len, const void* q,
                      const void* k_cache, const void* v_cache, const int32_t* prefix_len,
                      const int32_t* parent, void* out, void* workspace, size_t workspace_bytes,
@@ -277,7 +279,8 @@ typedef struct {
  *          accepted factors (the deferred commit), then read
  *   q, k   [B][N][H][Dk], v and out [B][N][H][Dv] (dtype), device
  *   alpha  [B][N][H] fp32 decays in (0, 1] or NULL; parent [B][N] or NULL
- * Errors: SPEC_EINVAL (null pointers, sizes), SPEC_EUNSUPPORTED (Dk, Dv). */
+ * Errors: SPEC_EINVAL (null pointers, sizes, a state pointer not 16-byte
+ * aligned), SPEC_EUNSUPPORTED (Dk, Dv). */
 int spec_la_verify(const spec_la_desc* desc, float* state, const void* q, const void* k, const void* v,
                    const float* alpha, const int32_t* parent, void* out, const spec_la_factors* pending,
                    void* stream);
@@ -285,7 +288,8 @@ int spec_la_verify(const spec_la_desc* desc, float* state, const void* q, const 
 /* The commit alone: state <- A(-> v] state + sum over j on the accepted path
  * of A(j -> v] v_j k_j^T (v the stop node), in place, from the factors; the
  * same update spec_la_verify applies for its pending argument.  desc gives
- * B, H, Dk, Dv and dtype (its num_nodes is not used). */
+ * B, H, Dk, Dv and dtype (its num_nodes is not used).  state must be 16-byte
+ * aligned, else SPEC_EINVAL. */
 int spec_la_commit(const spec_la_desc* desc, float* state, const spec_la_factors* accepted, void* stream);
 
 #ifdef __cplusplus

@@ -29,6 +29,8 @@ static bool desc_ok(const spec_attn_desc* d, int* err) {
     return true;
 }
 
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 extern "C" {
 
 size_t spec_verify_attn_workspace_bytes(const spec_attn_desc* desc, int32_t max_prefix_len) {
@@ -47,8 +49,11 @@ int spec_verify_attn(const spec_attn_desc* desc, int32_t max_prefix_len, const v
     if (max_prefix_len < 0 || static_cast<long>(max_prefix_len) + desc->num_nodes > desc->kv_capacity)
         return SPEC_EINVAL;
     if (!q || !k_cache || !v_cache || !prefix_len || !out) return SPEC_EINVAL;
+    // the kernels move q, the caches, out and the partials in 16-byte vectors
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return SPEC_EINVAL;
     const AttnPlan plan = plan_attn(*desc, max_prefix_len);
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes)) return SPEC_EWORKSPACE;
+    if (plan.ws_bytes > 0 && !aligned16(workspace)) return SPEC_EINVAL;
     return launch_verify_attn(*desc, plan, q, k_cache, v_cache, prefix_len, parent, out, workspace,
                               static_cast<hipStream_t>(stream));
 }
@@ -281,6 +286,7 @@ int spec_la_verify(const spec_la_desc* desc, float* state, const void* q, const 
     if (desc->num_nodes < 1 || desc->num_nodes > kMaxNodes) return SPEC_EINVAL;
     if (desc->batch == 0) return SPEC_OK;
     if (!state || !q || !k || !v || !out) return SPEC_EINVAL;
+    if (!aligned16(state)) return SPEC_EINVAL;  // the state moves in 16-byte vectors
     if (pending && !la_factors_ok(pending)) return SPEC_EINVAL;
     LaArgs a = la_args(desc, state);
     a.N = desc->num_nodes;
@@ -300,6 +306,7 @@ int spec_la_commit(const spec_la_desc* desc, float* state, const spec_la_factors
     if (rc != SPEC_OK) return rc;
     if (desc->batch == 0) return SPEC_OK;
     if (!state || !la_factors_ok(accepted)) return SPEC_EINVAL;
+    if (!aligned16(state)) return SPEC_EINVAL;
     LaArgs a = la_args(desc, state);
     la_set_factors(a, accepted);
     return launch_la(a, static_cast<hipStream_t>(stream));

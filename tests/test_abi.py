@@ -75,6 +75,15 @@ def test_attention_null_and_workspace_errors():
     assert _attn(d, ws=None) == EWORKSPACE
     assert lib.spec_verify_attn(ctypes.byref(d), 2048, None, FAKE, FAKE, FAKE, None, FAKE, FAKE, need, None) == EINVAL
     assert _attn(d, mpl=-1) == EINVAL
+    # 16-byte vectors: every tensor and the workspace must be 16-byte aligned
+    odd = ctypes.c_void_p(0x10000 + 8)
+    call = lambda q=FAKE, k=FAKE, v=FAKE, o=FAKE, ws=FAKE: lib.spec_verify_attn(
+        ctypes.byref(d), 2048, q, k, v, FAKE, None, o, ws, need, None)
+    assert call(q=odd) == EINVAL
+    assert call(k=odd) == EINVAL
+    assert call(v=odd) == EINVAL
+    assert call(o=odd) == EINVAL
+    assert call(ws=odd) == EINVAL
     # empty batch: nothing to do, nothing launched
     assert _attn(_desc(batch=0)) == OK
     assert lib.spec_verify_attn_workspace_bytes(ctypes.byref(_desc(head_dim=96)), 10) == 0
@@ -175,6 +184,9 @@ def test_linear_attention_errors():
     assert lib.spec_la_commit(ctypes.byref(d()), None, ctypes.byref(good), None) == EINVAL
     assert lib.spec_la_commit(ctypes.byref(d()), FAKE, None, None) == EINVAL
     assert lib.spec_la_commit(ctypes.byref(d(key_dim=32)), FAKE, ctypes.byref(good), None) == EUNSUPPORTED
+    odd = ctypes.c_void_p(0x10000 + 4)  # the state moves in 16-byte vectors
+    assert ver(d(), state=odd) == EINVAL
+    assert lib.spec_la_commit(ctypes.byref(d()), odd, ctypes.byref(good), None) == EINVAL
 
 
 def test_commit_and_helper_errors():
