@@ -69,14 +69,21 @@ __device__ __forceinline__ void la_rows_to_lds(const void* src, bool bf16, int r
 // path root .. i, anc[i] = the path's node mask.
 __device__ __forceinline__ void la_tree(const int32_t* parent, const float* alpha, int b, int N, int H, int h,
                                         int* s_par, float* s_L, uint64_t* s_anc) {
+    // Every node's parent and log2 decay loaded at once (one thread per
+    // node), then one thread walks the nodes in index order from LDS: the
+    // walk's loads would otherwise be one dependent round trip per node.
+    const int i = threadIdx.x;
+    if (i < N) {
+        const int p = tree_parent(parent, N, b, i);
+        s_par[i] = p >= 0 && p < i ? p : -1;  // out-of-contract parents read as roots
+        s_L[i] = alpha ? __log2f(alpha[(static_cast<size_t>(b) * N + i) * H + h]) : 0.f;
+    }
+    __syncthreads();
     if (threadIdx.x == 0) {
-        for (int i = 0; i < N; ++i) {
-            const int p = tree_parent(parent, N, b, i);
-            const int pp = p >= 0 && p < i ? p : -1;  // out-of-contract parents read as roots
-            s_par[i] = pp;
-            const float lg = alpha ? __log2f(alpha[(static_cast<size_t>(b) * N + i) * H + h]) : 0.f;
-            s_L[i] = (pp >= 0 ? s_L[pp] : 0.f) + lg;
-            s_anc[i] = (pp >= 0 ? s_anc[pp] : 0ull) | (1ull << i);
+        for (int n = 0; n < N; ++n) {
+            const int pp = s_par[n];
+            s_L[n] += pp >= 0 ? s_L[pp] : 0.f;
+            s_anc[n] = (pp >= 0 ? s_anc[pp] : 0ull) | (1ull << n);
         }
     }
     __syncthreads();
