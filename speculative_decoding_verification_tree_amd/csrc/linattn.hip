@@ -178,9 +178,20 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
         const int i = x / N, j = x - i * N;
         float w = 0.f;
         if ((s_anc[i] >> j) & 1ull) {
-            float dot = 0.f;
-            for (int d = 0; d < Dk; ++d) dot = fmaf(Qs[i * DkP + d], Ks[j * DkP + d], dot);
-            w = exp2f(s_L[i] - s_L[j]) * dot;
+            // four independent partial sums, eight LDS reads per round in
+            // flight (one wave per SIMD here: a single dependent chain
+            // waited out every read's latency)
+            float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+            const float* qi = Qs + i * DkP;
+            const float* kj = Ks + j * DkP;
+#pragma unroll 4
+            for (int d = 0; d < Dk; d += 4) {
+                d0 = fmaf(qi[d], kj[d], d0);
+                d1 = fmaf(qi[d + 1], kj[d + 1], d1);
+                d2 = fmaf(qi[d + 2], kj[d + 2], d2);
+                d3 = fmaf(qi[d + 3], kj[d + 3], d3);
+            }
+            w = exp2f(s_L[i] - s_L[j]) * ((d0 + d1) + (d2 + d3));
         }
         W[x] = w;
     }
@@ -219,13 +230,31 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
         }
         if (c0 + kLaChunk < Dk) load_chunk(c0 + kLaChunk);
         __syncthreads();
+        if constexpr (NMAX > 16) {
+            // Large trees, column by column: one state value feeds this
+            // thread's kPer nodes as independent chains (a per-node branch
+            // kept each node's 32-step chain apart, every step waiting out
+            // its LDS reads).  Rows past N hold stale LDS; their sums are
+            // never used.
+#pragma unroll 4
+            for (int cc = 0; cc < kLaChunk; ++cc) {
+                const float sv = Sc[e * (kLaChunk + 1) + cc];
 #pragma unroll
-        for (int n = 0; n < kPer; ++n) {
-            const int i = g + n * G;
-            if (i < N) {
-                float s = acc[n];
-                for (int cc = 0; cc < kLaChunk; ++cc) s = fmaf(Sc[e * (kLaChunk + 1) + cc], Qs[i * DkP + c0 + cc], s);
-                acc[n] = s;
+                for (int n = 0; n < kPer; ++n) {
+                    const int i = min(g + n * G, NMAX - 1);
+                    acc[n] = fmaf(sv, Qs[i * DkP + c0 + cc], acc[n]);
+                }
+            }
+        } else {  // small trees: only the nodes that exist
+#pragma unroll
+            for (int n = 0; n < kPer; ++n) {
+                const int i = g + n * G;
+                if (i < N) {
+                    float s = acc[n];
+                    for (int cc = 0; cc < kLaChunk; ++cc)
+                        s = fmaf(Sc[e * (kLaChunk + 1) + cc], Qs[i * DkP + c0 + cc], s);
+                    acc[n] = s;
+                }
             }
         }
     }
