@@ -112,6 +112,22 @@ def test_attention_loose_prefix_bound():
     check_attention(gpu, ref, "loose bound")
 
 
+@pytest.mark.parametrize("cid,L,bound", [
+    (2, 700, 700),    # one request, exact bound
+    (2, 700, 1900),   # one request, loose bound
+    (5, 333, 2000),   # one request, tree, loose bound
+    (2, 0, 500),      # one request with an empty prefix
+])
+def test_attention_single_request_bounds(cid, L, bound):
+    """One request: the KV ranges are cut from the real prefix length, so the
+    output must not depend on how loose the host's prefix bound is."""
+    w = generate(scaled(cid, batch=1, prefix_len=L), with_accept=False, capacity=bound + 80)
+    announce(f"attention single request cfg{cid} L={L} bound={bound}")
+    gpu = run_attention(w, max_prefix_len=bound)
+    ref = oracle.tree_attn(w.q, w.k_cache, w.v_cache, w.prefix_len, None if w.is_chain else w.parent, w.dtype)
+    check_attention(gpu, ref, f"single request L={L} bound={bound}")
+
+
 def test_attention_empty_batch():
     announce("attention B=0")
     q = torch.empty(0, 6, 32, 128, dtype=torch.bfloat16, device="cuda")
