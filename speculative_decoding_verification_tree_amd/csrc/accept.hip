@@ -476,6 +476,7 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
     __shared__ int s_path[kMaxNodes];
     __shared__ uint32_t s_tau[kMaxNodes];
     __shared__ Decision s_dec;
+    __shared__ int s_tok[kMaxNodes];  // the drafted tokens, for the writer's accepted-token list
 
     // The node's parent entry, token and uniform: three independent loads
     // with no branch between them (a chain's absent parent array and an
@@ -601,6 +602,7 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
     }
     }  // row statistics
     const double gl = glf;
+    if (wave == 0 && lane < N) s_tok[lane] = xraw;
     __syncthreads();
 
     if (wave == 0) {
@@ -677,7 +679,7 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
         if (tid < N) {
             const size_t o = static_cast<size_t>(b) * N + tid;
             a.path[o] = tid <= d.a ? s_path[tid] : -1;
-            int tok = tid < d.a ? a.tokens[static_cast<size_t>(b) * N + s_path[tid + 1]] : -1;
+            int tok = tid < d.a ? s_tok[s_path[tid + 1]] : -1;  // from LDS: no dependent load after the decision
             if (tid == d.a && d.mode == MODE_DONE) tok = s_arg[d.v];
             a.out_tokens[o] = tok;
         }
