@@ -1,0 +1,59 @@
+"""Host-side byte accounting that bench.py's roofline fractions rest on (no
+GPU): the algorithmic bytes of the attention and acceptance calls, on shapes
+small enough to count by hand."""
+import os
+import sys
+from types import SimpleNamespace
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def _w(rule="reject", parent=None, B=1, N=3, V=10):
+    return SimpleNamespace(B=B, N=N, V=V, rule=rule, parent=parent)
+
+
+GATHERS = 1 * 2 * 20        # B (N - 1) nodes x (token, parent, u, draft prob, logit)
+OUTPUTS = 1 * (1 + 2 * 3) * 4  # accept_len, path, out_tokens
+
+
+def test_reject_first_draft_rejected():
+    # chain 0-1-2: rows 0 and 1 have children; stop at the root, which has a
+    # child, so its first child's draft row is read too
+    path = np.array([[0, -1, -1]], dtype=np.int32)
+    got = bench.accept_bytes(_w(), np.array([0]), path)
+    assert got == 3 * 10 * 4 + GATHERS + OUTPUTS
+
+
+def test_reject_all_accepted_reads_the_leaf_row():
+    path = np.array([[0, 1, 2]], dtype=np.int32)
+    got = bench.accept_bytes(_w(), np.array([2]), path)
+    assert got == 3 * 10 * 4 + GATHERS + OUTPUTS  # two internal rows + the leaf stop row
+
+
+def test_typical_stop_inside_reads_no_extra_row():
+    path = np.array([[0, 1, -1]], dtype=np.int32)
+    got = bench.accept_bytes(_w(rule="typical"), np.array([1]), path)
+    assert got == 2 * 10 * 4 + GATHERS + OUTPUTS
+
+
+def test_tree_internal_rows_counted_once():
+    # root with children 1 and 2; node 1 with child 3 (N = 4): internal rows 0, 1
+    parent = np.array([[-1, 0, 0, 1]], dtype=np.int32)
+    path = np.array([[0, 2, -1, -1]], dtype=np.int32)  # stops at leaf 2
+    w = _w(parent=parent, N=4)
+    got = bench.accept_bytes(w, np.array([1]), path)
+    gathers = 1 * 3 * 20
+    outputs = 1 * (1 + 2 * 4) * 4
+    assert got == 3 * 10 * 4 + gathers + outputs  # rows 0, 1 and the leaf stop row 2
+
+
+def test_attention_bytes_count_each_kv_row_once():
+    w = SimpleNamespace(dtype="bf16", prefix_len=np.array([5, 9]), N=3, Hkv=2, D=4, B=2, Hq=4)
+    kv = (5 + 3 + 9 + 3) * 2 * 4 * 2 * 2  # rows x heads x D x bf16 x (K and V)
+    qo = 2 * 2 * 3 * 4 * 4 * 2            # q read and out written, bf16
+    assert bench.attn_bytes(w) == kv + qo
