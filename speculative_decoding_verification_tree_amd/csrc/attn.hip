@@ -400,8 +400,11 @@ __device__ __forceinline__ void block_update(const KRead& kread, const unsigned 
         // one of its four lanes' does, so the wave-uniform test takes each
         // lane's own max; the row maxima are formed only when some row
         // rescales.
-        float bm =
-            fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]))) * scale_log2;
+        // IEEE maximum (gfx950 v_maximum3_f32): unlike fmaxf it needs no
+        // canonicalising v_max_f32 x, x per matrix-core result.  The scores
+        // hold no NaN, where the two agree.
+        auto vmax = [](float x, float y) { return __builtin_elementwise_maximum(x, y); };
+        float bm = vmax(vmax(vmax(vmax(s[0], s[1]), s[2]), vmax(vmax(s[3], s[4]), s[5])), vmax(s[6], s[7])) * scale_log2;
         if (__builtin_amdgcn_ballot_w64(bm > m_run[t] + 8.f) != 0ull) {
             bm = max_across_rows(bm);
             const float mn = fmaxf(m_run[t], bm);
@@ -607,8 +610,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(RT <= 2 ? 2 
 // LDS and wave w owns row tiles [w*RT, (w+1)*RT) of the workgroup's rows, so
 // a block is read once per WK*RT*16 rows and no cross-wave merge is needed.
 // The workgroup loads each 32-key block cooperatively (coalesced 16-byte
-// chunks), two blocks ahead in registers, into a double-buffered LDS stage;
-// one barrier per block.
+// chunks) into a double-buffered LDS stage, one block in LDS and the next in
+// flight in registers; one barrier per block.
 // ----------------------------------------------------------------------------
 // K of one block in LDS: row-major 32 keys x D, 16-byte chunks XOR-swizzled
 // so that the 16 rows one A-operand read touches (paired-half key order)
@@ -701,8 +704,8 @@ __global__ __launch_bounds__(64 * WK) __attribute__((amdgpu_waves_per_eu(2))) vo
 
     if (wave == 0) (void)begin_segments(a, unit, s_cum, s_len, true);
     __syncthreads();
-    // Two cursors over the same segment walk: one computes, one loads two
-    // blocks ahead (through segment ends too).
+    // Two cursors over the same segment walk: one computes, one loads ahead
+    // (through segment ends too).
     SegIter it = begin_segments(a, unit, s_cum, s_len, false);
     SegIter lit = it;
     Seg cur, lseg;
@@ -724,14 +727,14 @@ __global__ __launch_bounds__(64 * WK) __attribute__((amdgpu_waves_per_eu(2))) vo
             }
         }
     };
-    // Two register sets take turns: at block i the set holding block i+1 is
-    // staged and then refilled with block i+3.
-    SharedKV<D, WK> R0, R1;
-    load_next(R0);
-    load_next(R1);
-    int bi = 0, sel = 1;
-    stage_shared_kv<D, WK>(R0, s_stage, s_stage + KS_BYTES);
-    load_next(R0);
+    // One register set: at block i it holds block i+1, which is staged into
+    // the other LDS buffer, and then takes block i+2's loads, which have
+    // block i+1's computation to land.
+    SharedKV<D, WK> R;
+    load_next(R);
+    int bi = 0;
+    stage_shared_kv<D, WK>(R, s_stage, s_stage + KS_BYTES);
+    load_next(R);
     __syncthreads();
 
     for (;;) {
@@ -740,6 +743,15 @@ __global__ __launch_bounds__(64 * WK) __attribute__((amdgpu_waves_per_eu(2))) vo
         bf16x8 qf[RT][NC32];
         uint64_t anc[RT];
         load_q<D, RT>(a, b, g, row0, anc_mask(a, b), qf, anc);
+        // Wait for the queries here, once per segment: left pending into the
+        // block loop, the wait at the loop head would also cover the KV
+        // prefetch issued after them (loads retire in order) on every block.
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+#pragma unroll
+            for (int c = 0; c < NC32; ++c) asm volatile("" ::"v"(qf[t][c]));
+            asm volatile("" ::"v"(anc[t]));
+        }
         float m_run[RT], l_run[RT];
         f32x4 o[RT][NC16];
 #pragma unroll
@@ -760,16 +772,10 @@ __global__ __launch_bounds__(64 * WK) __attribute__((amdgpu_waves_per_eu(2))) vo
             // The next block into the other buffer (its previous block was
             // finished by every wave before the last barrier), then refill.
             unsigned char* nks = s_stage + (bi ^ 1) * STAGE;
-            if (sel) {
-                stage_shared_kv<D, WK>(R1, nks, nks + KS_BYTES);
-                load_next(R1);
-            } else {
-                stage_shared_kv<D, WK>(R0, nks, nks + KS_BYTES);
-                load_next(R0);
-            }
+            stage_shared_kv<D, WK>(R, nks, nks + KS_BYTES);
+            load_next(R);
             __syncthreads();
             bi ^= 1;
-            sel ^= 1;
         }
         write_rows<D, RT, false>(a, cur, row0, m_run, l_run, o);
         if (cur.table && rg == 0 && tid == 0 && a.seg) a.seg[b * a.Hkv + g] = make_int2(cur.first, cur.count);
