@@ -415,12 +415,10 @@ __device__ __forceinline__ void block_update(const KRead& kread, const unsigned 
             m_run[t] = mn;
         }
         const float mu = m_run[t] == -INFINITY ? 0.f : m_run[t];
-        float p[8], rs = 0.f;
+        float p[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, -mu));
-            rs += p[e];
-        }
+        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, -mu));
+        const float rs = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         l_run[t] += rs;  // this lane's share of the row sum; the four shares are added at the end
         u32x4 pp;
         pp[0] = pack_bf16x2(p[0], p[1]);
@@ -672,14 +670,20 @@ __device__ __forceinline__ void stage_shared_kv(const SharedKV<D, WK>& s, unsign
         if (vtask >= S::VTASK) continue;
         const int kp = vtask / S::CPR, ch = vtask % S::CPR;
         const int key0 = 2 * kp;
-        const u32x4 v0 = s.kb + key0 < s.Tk ? s.v[j][0] : u32x4{0u, 0u, 0u, 0u};
-        const u32x4 v1 = s.kb + key0 + 1 < s.Tk ? s.v[j][1] : u32x4{0u, 0u, 0u, 0u};
+        auto put = [&](const u32x4& v0, const u32x4& v1) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int d = 8 * ch + t;
-            const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
-            const uint32_t w = __builtin_amdgcn_perm(v1[t >> 1], v0[t >> 1], sel);
-            *reinterpret_cast<uint32_t*>(vt + d * 64 + (((key0 >> 3) ^ vt_swz(d)) * 16) + (key0 & 7) * 2) = w;
+            for (int t = 0; t < 8; ++t) {
+                const int d = 8 * ch + t;
+                const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+                const uint32_t w = __builtin_amdgcn_perm(v1[t >> 1], v0[t >> 1], sel);
+                *reinterpret_cast<uint32_t*>(vt + d * 64 + (((key0 >> 3) ^ vt_swz(d)) * 16) + (key0 & 7) * 2) = w;
+            }
+        };
+        if (s.kb + 32 <= s.Tk) {  // workgroup-uniform: no key of the block is past the slab end
+            put(s.v[j][0], s.v[j][1]);
+        } else {
+            const u32x4 zero = {0u, 0u, 0u, 0u};
+            put(s.kb + key0 < s.Tk ? s.v[j][0] : zero, s.kb + key0 + 1 < s.Tk ? s.v[j][1] : zero);
         }
     }
 }
