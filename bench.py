@@ -31,7 +31,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 ROTATE_BYTES = 640 << 20
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_llama3_8b_chain_traffic.json")
+def traffic_file(name):
+    """Stored HBM counters of one attention call on the named workload."""
+    return os.path.join(ROOT, "profiles", f"attn_{name}_traffic.json")
 READ_PEAK_FILE = os.path.join(ROOT, "profiles", "hbm_read_peak.json")
 READ_PROBE = os.path.join(ROOT, "speculative_decoding_verification_tree_amd", "hbm_read_probe")
 
@@ -350,8 +352,8 @@ def main():
             read_peak = json.load(f).get("kv_read_GBs")
     traffic = None
     khash = kernel_source_hash()
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
+    if os.path.exists(traffic_file(cfg["name"])):
+        with open(traffic_file(cfg["name"])) as f:
             tr = json.load(f)
         if tr.get("kernel_source_hash") == khash and tr.get("config") == args.config:
             traffic = tr.get("bytes_per_launch")
