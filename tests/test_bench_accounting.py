@@ -57,3 +57,22 @@ def test_attention_bytes_count_each_kv_row_once():
     kv = (5 + 3 + 9 + 3) * 2 * 4 * 2 * 2  # rows x heads x D x bf16 x (K and V)
     qo = 2 * 2 * 3 * 4 * 4 * 2            # q read and out written, bf16
     assert bench.attn_bytes(w) == kv + qo
+
+
+def test_stored_traffic_matches_each_workload():
+    # Every stored attention traffic file names the configuration it was
+    # measured on, and the bench looks it up by that workload's name.
+    from workloads.configs import config
+    import json
+    found = 0
+    for cid in (1, 2, 3, 4, 5):
+        path = bench.traffic_file(config(cid)["name"])
+        if not os.path.exists(path):
+            continue
+        found += 1
+        with open(path) as f:
+            tr = json.load(f)
+        assert tr["config"] == cid
+        assert tr["bytes_per_launch"] > 0
+        assert len(tr["kernel_source_hash"]) == len(bench.kernel_source_hash())
+    assert found >= 1
