@@ -42,9 +42,13 @@ def test_shared_workspaces_across_calls():
         check_accept(w, gpu, oracle_accept(w))
 
 
-def test_graph_replay_matches_eager():
-    w = generate(scaled(4, batch=6, prefix_len=(100, 2500), vocab=12000))
-    announce("graph replay: cfg4 B=6")
+@pytest.mark.parametrize("cid,over", [
+    (4, dict(batch=6, prefix_len=(100, 2500), vocab=12000)),   # one-wave kernel, chains
+    (5, dict(batch=2, prefix_len=(100, 1500), vocab=9000)),    # shared-KV kernel, 64-node trees
+])
+def test_graph_replay_matches_eager(cid, over):
+    w = generate(scaled(cid, **over))
+    announce(f"graph replay: cfg{cid} B={w.B} N={w.N} Hq={w.Hq}")
     d = _dev_inputs(w)
     ws_attn = torch.zeros(max(sv.spec_verify_attn_workspace_bytes(
         sv.attn_desc(w.B, w.N, w.Hq, w.Hkv, w.D, w.cap, torch.bfloat16), w.max_prefix_len), 1),
@@ -76,5 +80,5 @@ def test_graph_replay_matches_eager():
         assert torch.equal(al, eager[1]) and torch.equal(path, eager[2]) and torch.equal(otok, eager[3]), rep
         step()  # eager work between replays
         torch.cuda.synchronize()
-    ref = oracle.tree_attn(w.q, w.k_cache, w.v_cache, w.prefix_len, None, w.dtype)
-    check_attention(host_f64(eager[0]), ref, "graph")
+    ref = oracle.tree_attn(w.q, w.k_cache, w.v_cache, w.prefix_len, None if w.is_chain else w.parent, w.dtype)
+    check_attention(host_f64(eager[0]), ref, f"graph cfg{cid}")
