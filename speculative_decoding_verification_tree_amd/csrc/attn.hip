@@ -623,10 +623,18 @@ struct SharedKV {
     static constexpr int KPT = 32 * CPR / NT;         // K chunks per thread
     static constexpr int VTASK = 16 * CPR;             // (key pair, chunk) tasks of V
     static constexpr int VPT = (VTASK + NT - 1) / NT;  // V tasks per thread
+    static_assert(KPT >= 1 && KPT * NT == 32 * CPR, "every thread loads whole K chunks");
     u32x4 k[KPT];
     u32x4 v[VPT][2];
     int kb, Tk;  // the block's first key and its slab's key count
 };
+
+// Waves per shared-KV workgroup: eight for D = 128 (256 rows share each KV
+// block); four for D = 64, where a 32-key block has 256 K chunks.
+template <int D>
+constexpr int wg_waves() {
+    return D == 128 ? 8 : 4;
+}
 
 template <int D, int WK>
 __device__ __forceinline__ void load_shared_kv(SharedKV<D, WK>& s, const uint16_t* kbase, const uint16_t* vbase, int kb,
@@ -1181,10 +1189,10 @@ AttnPlan plan_attn(const spec_attn_desc& d, int max_prefix_len) {
             p.row_tiles = (p.rows + 15) / 16;
             p.row_groups = 1;
             p.waves = 1;
-        } else {  // four waves of 32 rows share each KV block
+        } else {  // wg_waves<D>() waves of 32 rows share each KV block
             p.row_tiles = 2;
-            p.waves = 4;
-            p.row_groups = (p.rows + 127) / 128;
+            p.waves = d.head_dim == 128 ? wg_waves<128>() : wg_waves<64>();
+            p.row_groups = (p.rows + 32 * p.waves - 1) / (32 * p.waves);
         }
     } else {
         p.mfma = false;
@@ -1264,7 +1272,7 @@ static int mfma_resident() {
 template <int D>
 static int mfma_wg_resident() {
     static int n = 0;
-    if (n == 0) n = resident_per_cu(attn_mfma_wg<D, 2, 4>, 256);
+    if (n == 0) n = resident_per_cu(attn_mfma_wg<D, 2, wg_waves<D>()>, 64 * wg_waves<D>());
     return n;
 }
 
@@ -1282,7 +1290,7 @@ static int mfma_resident_rt(int rt, int waves) {
 template <int D>
 static void launch_mfma_rt(const AttnPlan& p, const AttnArgs& a, dim3 grid, hipStream_t st) {
     if (p.waves > 1) {
-        hipLaunchKernelGGL((attn_mfma_wg<D, 2, 4>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((attn_mfma_wg<D, 2, wg_waves<D>()>), grid, dim3(64 * wg_waves<D>()), 0, st, a);
         return;
     }
     switch (p.row_tiles) {

@@ -77,6 +77,8 @@ def test_attention_edge_cases(over):
     dict(nodes=2, prefix_len=5),
     dict(dtype="f32", head_dim=64, nodes=20),         # fp32 tree
     dict(num_q_heads=8, num_kv_heads=8, nodes=33, head_dim=64),
+    dict(nodes=40, head_dim=64),                      # D = 64 with R = 160: shared-KV kernel
+    dict(nodes=50, num_q_heads=32, num_kv_heads=4),   # R = 400: two shared-KV row groups
 ])
 def test_attention_tree_edge_cases(over):
     base = dict(batch=3, prefix_len=(0, 600), num_q_heads=16, num_kv_heads=4)
