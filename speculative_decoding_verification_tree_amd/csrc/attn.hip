@@ -620,13 +620,18 @@ template <int D, int WK>
 struct SharedKV {
     static constexpr int CPR = D / 8;
     static constexpr int NT = 64 * WK;
-    static constexpr int KPT = 32 * CPR / NT;         // K chunks per thread
-    static constexpr int VTASK = 16 * CPR;             // (key pair, chunk) tasks of V
-    static constexpr int VPT = (VTASK + NT - 1) / NT;  // V tasks per thread
-    static_assert(KPT >= 1 && KPT * NT == 32 * CPR, "every thread loads whole K chunks");
-    u32x4 k[KPT];
-    u32x4 v[VPT][2];
-    int kb, Tk;  // the block's first key and its slab's key count
+    static constexpr int KCH = 32 * CPR;    // K chunks of a block
+    static constexpr int VTASK = 16 * CPR;  // (key pair, chunk) tasks of V
+    // SPLIT: waves [0, WK/2) move V (one key pair each thread) and the rest
+    // K (two chunks each), so no thread loads more than two chunks or any
+    // chunk twice.  Otherwise every thread takes KPT K chunks and VPT V tasks.
+    static constexpr bool SPLIT = NT == 2 * VTASK && KCH == 2 * VTASK;
+    static constexpr int KPT = SPLIT ? 2 : KCH / NT;
+    static constexpr int VPT = SPLIT ? 1 : (VTASK + NT - 1) / NT;
+    static constexpr int NR = SPLIT ? 2 : KPT + 2 * VPT;
+    static_assert(SPLIT || (KPT >= 1 && KPT * NT == KCH), "every thread loads whole K chunks");
+    u32x4 r[NR];  // SPLIT: a V key pair or two K chunks; else K chunks, then V pairs
+    int kb, Tk;   // the block's first key and its slab's key count
 };
 
 // Waves per shared-KV workgroup: eight for D = 128 (256 rows share each KV
@@ -636,6 +641,12 @@ constexpr int wg_waves() {
     return D == 128 ? 8 : 4;
 }
 
+template <int D>
+__device__ __forceinline__ u32x4 kv_chunk(const uint16_t* base, int kb, int r, int ch, int Tk) {
+    const int row = min(kb + r, Tk - 1);
+    return *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(row) * D + ch * 8);
+}
+
 template <int D, int WK>
 __device__ __forceinline__ void load_shared_kv(SharedKV<D, WK>& s, const uint16_t* kbase, const uint16_t* vbase, int kb,
                                                int Tk) {
@@ -643,55 +654,85 @@ __device__ __forceinline__ void load_shared_kv(SharedKV<D, WK>& s, const uint16_
     const int tid = threadIdx.x;
     s.kb = kb;
     s.Tk = Tk;
+    if constexpr (S::SPLIT) {
+        if (tid < S::VTASK) {  // wave-uniform
+            const int kp = tid / S::CPR, ch = tid % S::CPR;
+            s.r[0] = kv_chunk<D>(vbase, kb, 2 * kp, ch, Tk);
+            s.r[1] = kv_chunk<D>(vbase, kb, 2 * kp + 1, ch, Tk);
+        } else {
 #pragma unroll
-    for (int j = 0; j < S::KPT; ++j) {
-        const int ci = tid + S::NT * j;
-        const int row = min(kb + ci / S::CPR, Tk - 1);
-        s.k[j] = *reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(row) * D + (ci % S::CPR) * 8);
-    }
+            for (int j = 0; j < 2; ++j) {
+                const int ci = tid - S::VTASK + S::VTASK * j;
+                s.r[j] = kv_chunk<D>(kbase, kb, ci / S::CPR, ci % S::CPR, Tk);
+            }
+        }
+    } else {
 #pragma unroll
-    for (int j = 0; j < S::VPT; ++j) {
-        const int vt = tid + S::NT * j;
-        const int task = vt < S::VTASK ? vt : 0;  // spare lanes re-read task 0 and never stage it
-        const int kp = task / S::CPR, ch = task % S::CPR;
-        const int r0 = min(kb + 2 * kp, Tk - 1), r1 = min(kb + 2 * kp + 1, Tk - 1);
-        s.v[j][0] = *reinterpret_cast<const u32x4*>(vbase + static_cast<size_t>(r0) * D + ch * 8);
-        s.v[j][1] = *reinterpret_cast<const u32x4*>(vbase + static_cast<size_t>(r1) * D + ch * 8);
+        for (int j = 0; j < S::KPT; ++j) {
+            const int ci = tid + S::NT * j;
+            s.r[j] = kv_chunk<D>(kbase, kb, ci / S::CPR, ci % S::CPR, Tk);
+        }
+#pragma unroll
+        for (int j = 0; j < S::VPT; ++j) {
+            const int vt = tid + S::NT * j;
+            const int task = vt < S::VTASK ? vt : 0;  // spare lanes re-read task 0 and never stage it
+            const int kp = task / S::CPR, ch = task % S::CPR;
+            s.r[S::KPT + 2 * j] = kv_chunk<D>(vbase, kb, 2 * kp, ch, Tk);
+            s.r[S::KPT + 2 * j + 1] = kv_chunk<D>(vbase, kb, 2 * kp + 1, ch, Tk);
+        }
     }
 }
 
-// K row-major (swizzled chunks), V transposed; V keys at or past the slab
-// end are zeroed so no stale value reaches P*V.
+// K row-major (swizzled chunks) and V transposed.  V keys at or past the
+// slab end are zeroed so no stale value reaches P*V.
+template <int D>
+__device__ __forceinline__ void stage_k_chunk(unsigned char* ks, int ci, const u32x4& c) {
+    constexpr int CPR = D / 8;
+    const int row = ci / CPR, col = ci % CPR;
+    *reinterpret_cast<u32x4*>(ks + row * (2 * D) + ((col ^ k_swz(row)) & (CPR - 1)) * 16) = c;
+}
+
+template <int D>
+__device__ __forceinline__ void stage_v_pair(unsigned char* vt, int task, const u32x4& v0, const u32x4& v1, int kb,
+                                             int Tk) {
+    constexpr int CPR = D / 8;
+    const int kp = task / CPR, ch = task % CPR;
+    const int key0 = 2 * kp;
+    auto put = [&](const u32x4& w0, const u32x4& w1) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int d = 8 * ch + t;
+            const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+            const uint32_t w = __builtin_amdgcn_perm(w1[t >> 1], w0[t >> 1], sel);
+            *reinterpret_cast<uint32_t*>(vt + d * 64 + (((key0 >> 3) ^ vt_swz(d)) * 16) + (key0 & 7) * 2) = w;
+        }
+    };
+    if (kb + 32 <= Tk) {  // workgroup-uniform: no key of the block is past the slab end
+        put(v0, v1);
+    } else {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        put(kb + key0 < Tk ? v0 : zero, kb + key0 + 1 < Tk ? v1 : zero);
+    }
+}
+
 template <int D, int WK>
 __device__ __forceinline__ void stage_shared_kv(const SharedKV<D, WK>& s, unsigned char* ks, unsigned char* vt) {
     using S = SharedKV<D, WK>;
     const int tid = threadIdx.x;
-#pragma unroll
-    for (int j = 0; j < S::KPT; ++j) {
-        const int ci = tid + S::NT * j;
-        const int row = ci / S::CPR, col = ci % S::CPR;
-        *reinterpret_cast<u32x4*>(ks + row * (2 * D) + ((col ^ k_swz(row)) & (S::CPR - 1)) * 16) = s.k[j];
-    }
-#pragma unroll
-    for (int j = 0; j < S::VPT; ++j) {
-        const int vtask = tid + S::NT * j;
-        if (vtask >= S::VTASK) continue;
-        const int kp = vtask / S::CPR, ch = vtask % S::CPR;
-        const int key0 = 2 * kp;
-        auto put = [&](const u32x4& v0, const u32x4& v1) {
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int d = 8 * ch + t;
-                const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
-                const uint32_t w = __builtin_amdgcn_perm(v1[t >> 1], v0[t >> 1], sel);
-                *reinterpret_cast<uint32_t*>(vt + d * 64 + (((key0 >> 3) ^ vt_swz(d)) * 16) + (key0 & 7) * 2) = w;
-            }
-        };
-        if (s.kb + 32 <= s.Tk) {  // workgroup-uniform: no key of the block is past the slab end
-            put(s.v[j][0], s.v[j][1]);
+    if constexpr (S::SPLIT) {
+        if (tid < S::VTASK) {  // wave-uniform
+            stage_v_pair<D>(vt, tid, s.r[0], s.r[1], s.kb, s.Tk);
         } else {
-            const u32x4 zero = {0u, 0u, 0u, 0u};
-            put(s.kb + key0 < s.Tk ? s.v[j][0] : zero, s.kb + key0 + 1 < s.Tk ? s.v[j][1] : zero);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) stage_k_chunk<D>(ks, tid - S::VTASK + S::VTASK * j, s.r[j]);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < S::KPT; ++j) stage_k_chunk<D>(ks, tid + S::NT * j, s.r[j]);
+#pragma unroll
+        for (int j = 0; j < S::VPT; ++j) {
+            const int vtask = tid + S::NT * j;
+            if (vtask < S::VTASK) stage_v_pair<D>(vt, vtask, s.r[S::KPT + 2 * j], s.r[S::KPT + 2 * j + 1], s.kb, s.Tk);
         }
     }
 }
