@@ -134,6 +134,7 @@ struct Seg {
 
 struct SegIter {
     int x, hi, nb_total;  // balanced: next block, end of range, all blocks
+    int P;                // balanced: ranges in use (a.nparts capped by the actual blocks)
     int unit;
     bool done;
 };
@@ -164,12 +165,19 @@ __device__ __forceinline__ SegIter begin_segments(const AttnArgs& a, int unit, i
     it.unit = unit;
     it.done = false;
     it.x = it.hi = it.nb_total = 0;
+    it.P = 1;
     if (a.balanced) {
         if (scan) scan_request_blocks(a, s_cum, s_len);
         it.nb_total = a.Hkv * s_cum[a.B];
-        if (unit < a.nparts) {
-            it.x = floor_div(static_cast<long>(unit) * it.nb_total, a.nparts);
-            it.hi = floor_div(static_cast<long>(unit + 1) * it.nb_total, a.nparts);
+        // The host sized P from its prefix bound; the actual blocks may be
+        // fewer (ragged or loose bounds).  Capping P at nb_total / split_blocks
+        // keeps every range non-empty (at least split_blocks blocks when there
+        // are that many): an empty range inside a slab would leave a partial
+        // slot between the slab's first and last partial unwritten.
+        it.P = max(1, min(a.nparts, it.nb_total / a.split_blocks));
+        if (unit < it.P) {
+            it.x = floor_div(static_cast<long>(unit) * it.nb_total, it.P);
+            it.hi = floor_div(static_cast<long>(unit + 1) * it.nb_total, it.P);
         }
     }
     return it;
@@ -193,7 +201,7 @@ __device__ __forceinline__ bool next_segment(const AttnArgs& a, SegIter& it, con
         const int begin = it.x - off, end = begin + nb;
         const int x1 = end < it.hi ? end : it.hi;
         const int q = b * a.Hkv + g;
-        const int pf = part_of(begin, it.nb_total, a.nparts), pl = part_of(end - 1, it.nb_total, a.nparts);
+        const int pf = part_of(begin, it.nb_total, it.P), pl = part_of(end - 1, it.nb_total, it.P);
         sg.b = b;
         sg.L = uniform(s_len[b]);
         sg.g = uniform(g);
@@ -1206,12 +1214,6 @@ __global__ __launch_bounds__(256) void attn_combine4(AttnArgs a, int bf16_out) {
 // ----------------------------------------------------------------------------
 // Host side
 // ----------------------------------------------------------------------------
-static int env_int(const char* name) {
-    const char* s = getenv(name);
-    const int v = s ? atoi(s) : 0;
-    return v > 0 ? v : 0;
-}
-
 // Upper bound on resident workgroups of one launch (4 per CU on 256 CUs);
 // sizes the balanced-mode partials independently of the device.
 constexpr int kMaxResident = 2048;
@@ -1249,7 +1251,7 @@ AttnPlan plan_attn(const spec_attn_desc& d, int max_prefix_len) {
     if (p.balanced) {
         // P is picked per launch from the device (resident workgroups); the
         // workspace holds the most partials any device can ask for.
-        if (env_int("SPEC_VERIFY_MIN_BLOCKS")) min_blocks = env_int("SPEC_VERIFY_MIN_BLOCKS");
+        if (d.kv_split_keys > 0) min_blocks = (d.kv_split_keys + 31) / 32;
         long pcap = kMaxResident / p.row_groups;
         if (pcap < 8) pcap = 8;
         const long by_work = (slabs * blocks_max + min_blocks - 1) / min_blocks;
@@ -1265,8 +1267,7 @@ AttnPlan plan_attn(const spec_attn_desc& d, int max_prefix_len) {
         long chunk_blocks = (blocks_max + want - 1) / want;
         // At least 8 blocks per MFMA split; the VALU path (one tile per
         // barrier round) spreads small problems down to one block per split.
-        const long min_split = env_int("SPEC_VERIFY_KV_CHUNK") ? (env_int("SPEC_VERIFY_KV_CHUNK") + 31) / 32
-                                                               : (p.mfma ? 8 : 1);
+        const long min_split = d.kv_split_keys > 0 ? (d.kv_split_keys + 31) / 32 : (p.mfma ? 8 : 1);
         if (chunk_blocks < min_split) chunk_blocks = min_split;
         p.split_blocks = static_cast<int>(chunk_blocks);
         p.nsplit_max = static_cast<int>((blocks_max + chunk_blocks - 1) / chunk_blocks);

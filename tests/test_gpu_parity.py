@@ -8,15 +8,16 @@ import torch
 import oracle
 import speculative_decoding_verification_tree_amd as sv
 from workloads import generate, scaled
-from tests.gpu_helpers import (announce, check_accept, check_attention, oracle_accept, run_accept, run_attention)
+from tests.gpu_helpers import (announce, check_accept, check_attention, dev_kv, host_f64, oracle_accept, run_accept,
+                               run_attention)
 
 pytestmark = pytest.mark.gpu
 
 
-def _attn_all_rows(w, what):
+def _attn_all_rows(w, what, kv_split_keys=0):
     announce(f"attention all rows: {what} B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} D={w.D} "
-             f"L={w.prefix_len.min()}..{w.prefix_len.max()} {w.dtype}")
-    gpu = run_attention(w)
+             f"L={w.prefix_len.min()}..{w.prefix_len.max()} {w.dtype} split={kv_split_keys}")
+    gpu = run_attention(w, kv_split_keys=kv_split_keys)
     ref = oracle.tree_attn(w.q, w.k_cache, w.v_cache, w.prefix_len, None if w.is_chain else w.parent, w.dtype)
     return check_attention(gpu, ref, what)
 
@@ -95,14 +96,37 @@ def test_attention_batch_mode_edge(batch):
     _attn_all_rows(w, f"batch-mode edge B={batch}")
 
 
-def test_attention_many_short_segments(monkeypatch):
-    # One block per range: ranges cross slab ends everywhere and slabs merge
-    # many partials.
-    monkeypatch.setenv("SPEC_VERIFY_MIN_BLOCKS", "1")
+@pytest.mark.parametrize("cid,over,bound", [
+    (4, dict(batch=6, prefix_len=(100, 1500)), None),   # ragged: fewer blocks than the bound's ranges
+    (4, dict(batch=5, prefix_len=(0, 200)), 4000),      # loose host bound: far fewer blocks than ranges
+    (5, dict(batch=3, prefix_len=(0, 900), nodes=40), None),
+])
+def test_attention_workspace_garbage(cid, over, bound):
+    """The workspace starts filled with NaN bytes: no partial slot the merge
+    reads may be left unwritten by the call (ranges are sized from the real
+    block count, not only from the host's prefix bound)."""
+    w = generate(scaled(cid, **over), with_accept=False, capacity=None if bound is None else bound + 80)
+    mpl = w.max_prefix_len if bound is None else bound
+    announce(f"attention garbage workspace cfg{cid} {over} bound={mpl}")
+    q, k, v = dev_kv(w.q, w.dtype), dev_kv(w.k_cache, w.dtype), dev_kv(w.v_cache, w.dtype)
+    pl = torch.from_numpy(w.prefix_len).cuda()
+    par = None if w.is_chain else torch.from_numpy(w.parent).cuda()
+    desc = sv.attn_desc(w.B, w.N, w.Hq, w.Hkv, w.D, k.shape[2], q.dtype)
+    ws = torch.full((max(sv.spec_verify_attn_workspace_bytes(desc, mpl), 16),), 0xFF, dtype=torch.uint8,
+                    device="cuda")
+    out = sv.spec_verify_attn(q, k, v, pl, par, mpl, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.tree_attn(w.q, w.k_cache, w.v_cache, w.prefix_len, None if w.is_chain else w.parent, w.dtype)
+    check_attention(host_f64(out), ref, f"garbage workspace cfg{cid}")
+
+
+def test_attention_many_short_segments():
+    # One block per range (kv_split_keys = 32): ranges cross slab ends
+    # everywhere and slabs merge many partials.
     w = generate(scaled(4, batch=6, prefix_len=(0, 1500)), with_accept=False)
-    _attn_all_rows(w, "min blocks 1, ragged")
+    _attn_all_rows(w, "min blocks 1, ragged", kv_split_keys=32)
     w = generate(scaled(5, batch=3, prefix_len=(0, 900), nodes=40), with_accept=False)
-    _attn_all_rows(w, "min blocks 1, tree")
+    _attn_all_rows(w, "min blocks 1, tree", kv_split_keys=32)
 
 
 def test_attention_loose_prefix_bound():

@@ -1,6 +1,7 @@
-"""GPU: workspaces reused across calls (the completion counters must come back
-to zero after every call) and the step replayed from a HIP graph (each replay,
-with eager work in between, must reproduce the eager result)."""
+"""GPU: workspaces reused across calls of different shapes (they start filled
+with a garbage byte pattern: no call may depend on their initial contents) and
+the step replayed from a HIP graph (each replay, with eager work in between,
+must reproduce the eager result)."""
 import numpy as np
 import pytest
 import torch
@@ -24,8 +25,8 @@ def _dev_inputs(w):
 
 
 def test_shared_workspaces_across_calls():
-    ws_attn = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
-    ws_acc = torch.zeros(16 << 20, dtype=torch.uint8, device="cuda")
+    ws_attn = torch.full((64 << 20,), 0xA5, dtype=torch.uint8, device="cuda")
+    ws_acc = torch.full((16 << 20,), 0x5A, dtype=torch.uint8, device="cuda")
     cases = [scaled(2, prefix_len=900), scaled(5, batch=2, prefix_len=700, vocab=9000),
              scaled(4, batch=5, prefix_len=(50, 1300), vocab=7000), scaled(2, prefix_len=900)]
     for i, cfg in enumerate(cases):
