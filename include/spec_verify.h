@@ -49,7 +49,12 @@ typedef enum spec_dtype { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
 /* Shape of the attention problem.  q/out are [B][N][Hq][D]; the caches are
  * [B][Hkv][kv_capacity][D].  Hq % Hkv == 0; query head h reads kv head
  * h / (Hq / Hkv).  head_dim is 64 or 128.  1 <= num_nodes <= 64.
- * softmax_scale <= 0 selects 1/sqrt(head_dim). */
+ * softmax_scale <= 0 selects 1/sqrt(head_dim).
+ * kv_split_keys: 0 lets the library choose how finely the KV axis is split
+ * across workgroups; a positive value sets the least number of keys per KV
+ * range (rounded up to whole 32-key blocks), for tuning and for tests that
+ * need many short ranges.  It changes the work split and the workspace size,
+ * not the result beyond rounding order.  Negative: SPEC_EINVAL. */
 typedef struct spec_attn_desc {
     int32_t batch;
     int32_t num_nodes;
@@ -59,6 +64,7 @@ typedef struct spec_attn_desc {
     int32_t kv_capacity; /* rows per (b, kv head); must be >= max_prefix_len + num_nodes */
     int32_t dtype;       /* spec_dtype of q, the caches and out */
     float softmax_scale;
+    int32_t kv_split_keys; /* 0: automatic */
 } spec_attn_desc;
 
 /* Workspace bytes spec_verify_attn needs for this shape and prefix bound

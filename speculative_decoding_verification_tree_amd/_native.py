@@ -50,6 +50,7 @@ class AttnDesc(ctypes.Structure):
         ("kv_capacity", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
+        ("kv_split_keys", ctypes.c_int32),
     ]
 
 

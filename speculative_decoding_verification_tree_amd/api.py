@@ -5,8 +5,8 @@ arguments: it checks that the tensors are contiguous device tensors of the
 right dtype, passes their data pointers and the current HIP stream, and raises
 on a non-zero status.  All arithmetic runs in the HIP kernels.  Output and
 workspace tensors may be passed in (no allocation) or are created with
-``torch.empty`` (outputs) / ``torch.zeros`` (workspaces, whose completion
-counters must start at zero) when omitted.
+``torch.empty`` when omitted (no workspace needs initialisation: every call
+writes what it later reads).
 """
 import ctypes
 
@@ -55,9 +55,11 @@ def _dtype_code(dt):
     raise ValueError(f"unsupported dtype {dt}")
 
 
-def attn_desc(batch, num_nodes, num_q_heads, num_kv_heads, head_dim, kv_capacity, dtype, softmax_scale=0.0):
+def attn_desc(batch, num_nodes, num_q_heads, num_kv_heads, head_dim, kv_capacity, dtype, softmax_scale=0.0,
+              kv_split_keys=0):
     return AttnDesc(batch, num_nodes, num_q_heads, num_kv_heads, head_dim, kv_capacity,
-                    _dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype), float(softmax_scale))
+                    _dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype), float(softmax_scale),
+                    int(kv_split_keys))
 
 
 def spec_verify_attn_workspace_bytes(desc, max_prefix_len):
@@ -65,23 +67,24 @@ def spec_verify_attn_workspace_bytes(desc, max_prefix_len):
 
 
 def spec_verify_attn(q, k_cache, v_cache, prefix_len, parent, max_prefix_len, out=None, workspace=None,
-                     softmax_scale=0.0, stream=None):
+                     softmax_scale=0.0, stream=None, kv_split_keys=0):
     """Tree-verify attention.  q [B][N][Hq][D]; caches [B][Hkv][cap][D] (same
     dtype, bf16 or fp32); prefix_len [B] int32; parent [B][N] int32 or None
-    (chain); max_prefix_len: host int >= every prefix length."""
+    (chain); max_prefix_len: host int >= every prefix length; kv_split_keys:
+    least keys per KV range (0: automatic)."""
     B, N, Hq, D = q.shape
     Hkv, cap = k_cache.shape[1], k_cache.shape[2]
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _dev(t, n, q.dtype)
     _dev(prefix_len, "prefix_len", torch.int32)
     _dev(parent, "parent", torch.int32)
-    desc = attn_desc(B, N, Hq, Hkv, D, cap, q.dtype, softmax_scale)
+    desc = attn_desc(B, N, Hq, Hkv, D, cap, q.dtype, softmax_scale, kv_split_keys)
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out", q.dtype)
     need = spec_verify_attn_workspace_bytes(desc, max_prefix_len)
     if workspace is None and need:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)  # counters start at zero
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = _native.lib().spec_verify_attn(ctypes.byref(desc), int(max_prefix_len), _ptr(q), _ptr(k_cache),
                                         _ptr(v_cache), _ptr(prefix_len), _ptr(parent), _ptr(out),
@@ -118,8 +121,8 @@ def spec_accept_reject(target_logits, draft_probs, tokens, parent, u_accept, u_s
     _dev(u_sample, "u_sample", torch.float32)
     accept_len, path, out_tokens = _accept_outputs(B, N, target_logits.device, accept_len, path, out_tokens)
     if workspace is None:
-        workspace = torch.zeros(max(spec_accept_workspace_bytes(B, N, V), 1), dtype=torch.uint8,
-                                device=target_logits.device)  # counters start at zero
+        workspace = torch.empty(max(spec_accept_workspace_bytes(B, N, V), 1), dtype=torch.uint8,
+                                device=target_logits.device)
     rc = _native.lib().spec_accept_reject(B, N, V, _ptr(target_logits), _ptr(draft_probs), _ptr(tokens),
                                           _ptr(parent), _ptr(u_accept), _ptr(u_sample), float(temperature),
                                           _ptr(accept_len), _ptr(path), _ptr(out_tokens), _ptr(workspace),
@@ -189,8 +192,8 @@ def spec_accept_typical(target_logits, tokens, parent, temperature, epsilon, del
     _dev(parent, "parent", torch.int32)
     accept_len, path, out_tokens = _accept_outputs(B, N, target_logits.device, accept_len, path, out_tokens)
     if workspace is None:
-        workspace = torch.zeros(max(spec_accept_workspace_bytes(B, N, V), 1), dtype=torch.uint8,
-                                device=target_logits.device)  # counters start at zero
+        workspace = torch.empty(max(spec_accept_workspace_bytes(B, N, V), 1), dtype=torch.uint8,
+                                device=target_logits.device)
     rc = _native.lib().spec_accept_typical(B, N, V, _ptr(target_logits), _ptr(tokens), _ptr(parent),
                                            float(temperature), float(epsilon), float(delta), _ptr(accept_len),
                                            _ptr(path), _ptr(out_tokens), _ptr(workspace), workspace.numel(),

@@ -44,14 +44,14 @@ def f32(x):
     return float(np.float32(x))
 
 
-def run_attention(w, max_prefix_len=None, stream=None):
+def run_attention(w, max_prefix_len=None, stream=None, kv_split_keys=0):
     q = dev_kv(w.q, w.dtype)
     k = dev_kv(w.k_cache, w.dtype)
     v = dev_kv(w.v_cache, w.dtype)
     pl = torch.from_numpy(w.prefix_len).cuda()
     par = None if w.is_chain else torch.from_numpy(w.parent).cuda()
     mpl = w.max_prefix_len if max_prefix_len is None else max_prefix_len
-    out = sv.spec_verify_attn(q, k, v, pl, par, mpl, stream=stream)
+    out = sv.spec_verify_attn(q, k, v, pl, par, mpl, stream=stream, kv_split_keys=kv_split_keys)
     torch.cuda.synchronize()
     return host_f64(out)
 

@@ -34,12 +34,12 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_struct_layout_matches_header():
-    assert ctypes.sizeof(AttnDesc) == 32
+    assert ctypes.sizeof(AttnDesc) == 36
 
 
 def _desc(**kw):
     d = dict(batch=1, num_nodes=6, num_q_heads=32, num_kv_heads=8, head_dim=128, kv_capacity=2054, dtype=1,
-             softmax_scale=0.0)
+             softmax_scale=0.0, kv_split_keys=0)
     d.update(kw)
     return AttnDesc(**d)
 
@@ -60,6 +60,7 @@ def _attn(desc, mpl=2048, ws_bytes=1 << 30, ws=FAKE):
     (dict(kv_capacity=2053), EINVAL),
     (dict(batch=-1), EINVAL),
     (dict(softmax_scale=float("nan")), EINVAL),
+    (dict(kv_split_keys=-1), EINVAL),
 ])
 def test_attention_argument_errors(kw, want):
     assert _attn(_desc(**kw)) == want
@@ -87,6 +88,17 @@ def test_attention_null_and_workspace_errors():
     # empty batch: nothing to do, nothing launched
     assert _attn(_desc(batch=0)) == OK
     assert lib.spec_verify_attn_workspace_bytes(ctypes.byref(_desc(head_dim=96)), 10) == 0
+
+
+def test_attention_split_granularity_sizes_workspace():
+    # Finer KV ranges mean more partials: the workspace grows, and one
+    # 32-key block per range is the finest split.
+    lib = sv.lib()
+    auto = lib.spec_verify_attn_workspace_bytes(ctypes.byref(_desc(batch=4)), 2048)
+    fine = lib.spec_verify_attn_workspace_bytes(ctypes.byref(_desc(batch=4, kv_split_keys=32)), 2048)
+    one = lib.spec_verify_attn_workspace_bytes(ctypes.byref(_desc(batch=4, kv_split_keys=1)), 2048)
+    assert fine >= auto > 0
+    assert one == fine
 
 
 def _rej(B=2, N=6, V=1000, T=1.0, ws_bytes=1 << 30, ws=FAKE, draft=FAKE, us=FAKE):
