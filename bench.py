@@ -1,28 +1,39 @@
-"""Benchmark of one speculative-decoding verification step on one MI355X.
+"""Benchmark of the speculative-decoding verification step on one MI355X.
 
 A step is the whole hot path over one batch: tree-verify attention
 (spec_verify_attn), acceptance (spec_accept_reject / spec_accept_typical) and
 the KV commit (spec_commit_kv).  Every step runs all three on the same fixed
 workload: the commit moves the accepted rows and advances its own copy of the
 prefix lengths inside spare cache capacity, while attention keeps reading the
-workload's prefix lengths.  The default workload is the Llama-3-8B-shaped
-chain (batch 1, 32 query / 8 KV heads, head dim 128, bf16 KV prefix 2048,
-K = 5 drafts, vocabulary 128256, T = 1, rejection rule).
+workload's prefix lengths.
+
+The headline workload is the largest one that fits one GPU, the ragged serving
+batch (64 requests, 32 query / 8 KV heads, head dim 128, bf16 KV prefixes
+512..8192, K = 7 chain drafts, vocabulary 128256, T = 0.8, rejection rule and
+commit).  By default every one of the five workloads is measured as well and
+reported under "configs"; --only measures the headline alone.
 
 Inputs are seeded synthetic tensors, generated once and copied to the GPU;
 enough copies are rotated that consecutive reuses of one copy are more than
 512 MB of traffic apart, so the 256 MB Infinity Cache cannot serve them.
 
+Timing: each phase (the step, and each call alone) is captured in a HIP graph
+of at least 32 steps; the graph is replayed at least 5 times and at least 100
+steps in total, each replay bracketed by HIP events on the launch stream, and
+the median per-step time over the replays is reported (with min and max).
+
 Prints ONE JSON line: the metric (verified draft tokens per second =
-B * (N - 1) / step time), the attention kernel's achieved algorithmic HBM
-bandwidth against the 8 TB/s peak (timed live with HIP events on the launch
-stream), and the fp64 CPU oracle timed on a bounded sample of the same step.
+B * (N - 1) / step time, every non-root node of the tree counted as one
+adjudicated draft), the dominant kernel's roofline fraction, and the fp64 CPU
+oracle timed on a bounded sample of the same step (all host threads, and one
+thread).
 """
 import argparse
 import hashlib
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -30,22 +41,35 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
 ROTATE_BYTES = 640 << 20
-def traffic_file(name):
-    """Stored HBM counters of one attention call on the named workload."""
-    return os.path.join(ROOT, "profiles", f"attn_{name}_traffic.json")
+HEADLINE = 4
 READ_PEAK_FILE = os.path.join(ROOT, "profiles", "hbm_read_peak.json")
-READ_PROBE = os.path.join(ROOT, "speculative_decoding_verification_tree_amd", "hbm_read_probe")
+READ_PROBE = os.path.join(ROOT, "hbm_read_probe")
+CSRC = os.path.join(ROOT, "speculative_decoding_verification_tree_amd", "csrc")
+
+# What the stored counter files describe: the kernels of one call, compiled
+# from these sources.
+ATTN_SOURCES = ("attn.hip", "spec_common.h", "spec_internal.h")
+ACCEPT_SOURCES = ("accept.hip", "spec_common.h", "spec_internal.h")
 
 
-def parse():
+def traffic_file(kind, name):
+    """Stored HBM counters of one call (kind 'attn' | 'accept') on the named workload."""
+    return os.path.join(ROOT, "profiles", f"{kind}_{name}_traffic.json")
+
+
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (default: the Llama-3-8B chain)")
+    ap.add_argument("--steps", type=int, default=100, help="least number of timed steps (at least 100 are timed)")
+    ap.add_argument("--warmup", type=int, default=10, help="eager warm-up steps (at least 10)")
+    ap.add_argument("--config", type=int, default=HEADLINE, help="headline workload id 1..5 (default: the ragged batch)")
+    ap.add_argument("--only", action="store_true", help="measure the headline workload alone (no 'configs' map)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the calls beside the path (truncated / multi-draft acceptance, RoPE, linear attention)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline sample budget")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline sample budget (all threads)")
     ap.add_argument("--rotate-mb", type=int, default=ROTATE_BYTES >> 20,
                     help="input bytes cycled between reuses of one copy (default beats the 256 MB Infinity Cache; "
                          "0 keeps two copies, i.e. cache-warm)")
@@ -53,21 +77,24 @@ def parse():
                     help="only run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--read-peak", action="store_true",
                     help="only run the streaming-read calibration program (measured HBM read bandwidth)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
-ATTN_SOURCES = ("attn.hip", "spec_common.h", "spec_internal.h")  # what the spec_verify_attn kernels compile from
+def source_hash(names):
+    """Hash of kernel sources: stored counters stay valid while these are unchanged."""
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
 
 
 def kernel_source_hash():
-    """Hash of the attention kernels' sources: the stored traffic counters
-    describe a spec_verify_attn call and stay valid while these are unchanged."""
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "speculative_decoding_verification_tree_amd", "csrc")
-    for name in ATTN_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
-    return h.hexdigest()[:16]
+    return source_hash(ATTN_SOURCES)
+
+
+def accept_source_hash():
+    return source_hash(ACCEPT_SOURCES)
 
 
 def attn_bytes(w):
@@ -77,6 +104,25 @@ def attn_bytes(w):
     kv = sum(int(L) + w.N for L in w.prefix_len) * w.Hkv * w.D * es * 2
     qo = 2 * w.B * w.N * w.Hq * w.D * es
     return kv + qo
+
+
+def node_depths(parent_row):
+    d = [0] * len(parent_row)
+    for i in range(1, len(parent_row)):
+        d[i] = d[int(parent_row[i])] + 1
+    return d
+
+
+def attn_flops(w):
+    """Algorithmic FLOPs of one attention launch: 4 * D per (query row, key),
+    a node's keys being the prefix and its root path (itself included)."""
+    import numpy as np
+
+    par = w.parent if not w.is_chain else np.tile(np.arange(-1, w.N - 1, dtype=np.int32), (w.B, 1))
+    keys = 0
+    for b in range(w.B):
+        keys += sum(int(w.prefix_len[b]) + d + 1 for d in node_depths(par[b]))
+    return 4 * w.D * w.Hq * keys
 
 
 def accept_bytes(w, accept_len, path):
@@ -103,58 +149,142 @@ def accept_bytes(w, accept_len, path):
     return rows * V * 4 + gathers + outputs
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part of this "
-              "build", file=sys.stderr)
-        sys.exit(2)
+def stored_traffic(kind, name, cid, khash):
+    """Per-call HBM bytes from the stored counter file, or None when the file
+    is missing or describes other kernel sources."""
+    path = traffic_file(kind, name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tr = json.load(f)
+    if tr.get("kernel_source_hash") == khash and tr.get("config") == cid:
+        return tr.get("bytes_per_launch")
+    return None
 
-    if args.read_peak:
-        # A child process of its own (nothing here has touched the GPU yet).
-        import subprocess
-        if not os.path.exists(READ_PROBE):
-            sys.exit(f"{READ_PROBE} is not built (run __graft_entry__.build())")
-        res = subprocess.run([READ_PROBE], capture_output=True, text=True)
-        sys.stderr.write(res.stderr)
-        print(res.stdout.strip(), flush=True)
-        sys.exit(res.returncode)
 
+def oracle_step(oracle, w, kk, vv, zero_len):
+    """One full oracle step: attention of every row, acceptance, and the
+    commit of the accepted path.  The commit moves rows of the tree region
+    only, so it runs on a compact copy of that region (kk, vv: the N tree rows
+    of every (request, KV head), prefix lengths 0): the same row moves as on
+    the whole cache, without copying the prefix."""
+    import numpy as np
+
+    par = None if w.is_chain else w.parent
+    T32 = float(np.float32(w.temperature))
+    oracle.tree_attn(w.q, w.k_cache, w.v_cache, w.prefix_len, par, w.dtype)
+    r = oracle.accept(w.rule, w.target_logits, w.tokens, par, T32, w.draft_probs, w.u_accept, w.u_sample,
+                      float(np.float32(w.epsilon)), float(np.float32(w.delta)))
+    oracle.commit(kk, vv, zero_len.copy(), r["path"], r["accept_len"])
+
+
+def request_slice(w, nreq):
+    """The first nreq requests of a workload (a bounded sample of it)."""
+    import copy
+
+    s = copy.copy(w)
+    s.B = nreq
+    for f in ("q", "k_cache", "v_cache", "prefix_len", "parent", "tokens", "target_logits", "draft_probs",
+              "u_accept", "u_sample"):
+        a = getattr(w, f)
+        if a is not None:
+            setattr(s, f, a[:nreq])
+    return s
+
+
+def cpu_sample(w, budget_s, nreq):
+    """Time oracle steps on the first nreq requests until budget_s has passed
+    (at least one step).  Returns (steps, seconds, requests)."""
+    import numpy as np
+
+    import oracle
+
+    s = request_slice(w, nreq) if nreq < w.B else w
+    # the tree region of the caches, outside the timed region
+    rows = np.stack([np.arange(int(L), int(L) + s.N) for L in s.prefix_len])  # [B][N]
+    kk = np.ascontiguousarray(np.stack([s.k_cache[b][:, rows[b]] for b in range(s.B)]))
+    vv = np.ascontiguousarray(np.stack([s.v_cache[b][:, rows[b]] for b in range(s.B)]))
+    zero_len = np.zeros(s.B, dtype=np.int32)
+    n, t = 0, 0.0
+    while n == 0 or t < budget_s:
+        t0 = time.perf_counter()
+        oracle_step(oracle, s, kk, vv, zero_len)
+        t += time.perf_counter() - t0
+        n += 1
+        if n >= 1000:
+            break
+    return n, t, s.B
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle on the host: all threads on whole steps, and one thread on
+    the first requests of the workload."""
+    import oracle
+
+    per_req = w.N - 1
+    nth = oracle.num_threads()
+    n, t, b = cpu_sample(w, budget_s, w.B)
+    res = {"value": per_req * b * n / t, "unit": "verified draft tokens/s", "cores": nth, "kind": "oracle",
+           "sample": f"{n} full step(s) of the same workload ({b} requests: attention of every row, acceptance, "
+                     f"commit), {t:.1f} s on the host with {nth} OpenMP threads"}
+    # one thread: as many leading requests as fit the budget at the measured rate
+    nreq = max(1, min(w.B, int(budget_s / max(t / n / b * nth, 1e-9))))
+    oracle.set_num_threads(1)
+    try:
+        n1, t1, b1 = cpu_sample(w, budget_s, nreq)
+    finally:
+        oracle.set_num_threads(nth)
+    res["single_thread"] = {"value": per_req * b1 * n1 / t1, "unit": "verified draft tokens/s", "cores": 1,
+                            "sample": f"{n1} step(s) of the first {b1} request(s) of the workload, "
+                                      f"{t1:.1f} s on one host thread"}
+    return res
+
+
+class Timer:
+    """Median per-step time of graph replays, HIP events on the launch stream."""
+
+    def __init__(self, torch, spg, reps):
+        self.torch, self.spg, self.reps = torch, spg, reps
+
+    def __call__(self, g):
+        torch = self.torch
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(self.reps)]
+        torch.cuda.synchronize()
+        for e0, e1 in ev:
+            e0.record()
+            g.replay()
+            e1.record()
+        torch.cuda.synchronize()
+        per = sorted(e0.elapsed_time(e1) / self.spg for e0, e1 in ev)
+        m = len(per) // 2
+        med = per[m] if len(per) % 2 else 0.5 * (per[m - 1] + per[m])
+        return {"median_ms": med, "min_ms": per[0], "max_ms": per[-1]}
+
+
+def measure(cid, args, dev, with_extras):
+    """Everything measured on workload cid; returns the per-workload record."""
     import numpy as np
     import torch
 
     import speculative_decoding_verification_tree_amd as sv
     from workloads import config, generate
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    sv.lib()  # fails loudly if the HIP library is not built
-
-    if args.copy_calibration:
-        n = 256 << 20
-        a = torch.empty(n, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": n}))
-        return
-
-    cfg = config(args.config)
+    cfg = config(cid)
     w = generate(cfg, poison=False)
     B, N, V = w.B, w.N, w.V
     touched = attn_bytes(w) + (N * V * 4) * (2 if w.draft_probs is not None else 1)
     ncopies = max(2, math.ceil((args.rotate_mb << 20) / max(touched, 1)))
-    # One graph replay runs `spg` steps over the copies in rotation; at least
-    # 32 steps per replay so the per-replay launch cost is amortised.
+    # One graph replay runs spg steps over the copies in rotation (at least 32
+    # so the per-replay launch cost is amortised); at least 5 replays and at
+    # least max(--steps, 100) timed steps.
     spg = ncopies * math.ceil(32 / ncopies)
-    reps = max(1, math.ceil(args.steps / spg))
+    reps = max(5, math.ceil(max(args.steps, 100) / spg))
+    warmup = max(args.warmup, 10)
     # The commit advances its own copy of the prefix lengths by at most N rows
     # per use (attention keeps reading the fixed workload's lengths), so the
-    # cache gets headroom for every use: eager warm-up, then (1 + reps)
-    # replays each of the step and commit graphs.
-    uses = math.ceil(max(args.warmup, ncopies) / ncopies) + 2 * (reps + 1) * (spg // ncopies) + 1
+    # cache gets headroom for every use: eager warm-up, then one warm and reps
+    # timed replays of the step and commit graphs.
+    uses = math.ceil(max(warmup, ncopies) / ncopies) + 2 * (reps + 1) * (spg // ncopies) + 1
     mpl = int(w.prefix_len.max())
     cap = mpl + (uses + 1) * N
 
@@ -164,22 +294,21 @@ def main():
         return t.view(torch.bfloat16) if bf16 else t
 
     bf16 = w.dtype == "bf16"
-    kpad = np.zeros((B, w.Hkv, cap, w.D), dtype=w.k_cache.dtype)
-    vpad = np.zeros_like(kpad)
-    kpad[:, :, : w.cap] = w.k_cache
-    vpad[:, :, : w.cap] = w.v_cache
+    kd = torch.zeros((B, w.Hkv, cap, w.D), dtype=torch.bfloat16 if bf16 else torch.float32, device=dev)
+    vd = torch.zeros_like(kd)
+    kd[:, :, : w.cap] = to_dev(w.k_cache, bf16)
+    vd[:, :, : w.cap] = to_dev(w.v_cache, bf16)
     base = dict(
-        q=to_dev(w.q, bf16), k=to_dev(kpad, bf16), v=to_dev(vpad, bf16),
+        q=to_dev(w.q, bf16), k=kd, v=vd,
         logits=torch.from_numpy(w.target_logits).to(dev),
         draft=torch.from_numpy(w.draft_probs).to(dev) if w.draft_probs is not None else None,
         tokens=torch.from_numpy(w.tokens).to(dev),
         parent=None if w.is_chain else torch.from_numpy(w.parent).to(dev),
         ua=torch.from_numpy(w.u_accept).to(dev), us=torch.from_numpy(w.u_sample).to(dev),
     )
-    del kpad, vpad
     copies = []
-    for _ in range(ncopies):
-        c = {k: (t.clone() if t is not None else None) for k, t in base.items()}
+    for i in range(ncopies):
+        c = {k: (t.clone() if (t is not None and i > 0) else t) for k, t in base.items()}
         c["pl"] = torch.from_numpy(w.prefix_len.copy()).to(dev)        # read by attention
         c["pl_commit"] = torch.from_numpy(w.prefix_len.copy()).to(dev)  # advanced by the commit
         c["out"] = torch.empty_like(c["q"])
@@ -187,9 +316,10 @@ def main():
         c["path"] = torch.empty(B, N, dtype=torch.int32, device=dev)
         c["otok"] = torch.empty(B, N, dtype=torch.int32, device=dev)
         copies.append(c)
+    del base, kd, vd
     desc = sv.attn_desc(B, N, w.Hq, w.Hkv, w.D, cap, torch.bfloat16 if bf16 else torch.float32)
-    attn_ws = torch.zeros(max(sv.spec_verify_attn_workspace_bytes(desc, mpl), 1), dtype=torch.uint8, device=dev)
-    acc_ws = torch.zeros(max(sv.spec_accept_workspace_bytes(B, N, V), 1), dtype=torch.uint8, device=dev)
+    attn_ws = torch.empty(max(sv.spec_verify_attn_workspace_bytes(desc, mpl), 16), dtype=torch.uint8, device=dev)
+    acc_ws = torch.empty(max(sv.spec_accept_workspace_bytes(B, N, V), 16), dtype=torch.uint8, device=dev)
 
     def attn(c):
         sv.spec_verify_attn(c["q"], c["k"], c["v"], c["pl"], c["parent"], mpl, out=c["out"], workspace=attn_ws)
@@ -205,14 +335,118 @@ def main():
     def commit(c):
         sv.spec_commit_kv(c["k"], c["v"], c["pl_commit"], c["path"], c["al"])
 
-    def step(c):
+    # eager warm-up (also checks every call returns SPEC_OK)
+    for i in range(max(warmup, ncopies)):
+        c = copies[i % ncopies]
         attn(c)
         accept(c)
         commit(c)
+    torch.cuda.synchronize()
 
-    # The step before the path, timed on its own: the Medusa candidate tree
-    # (tree workloads built as a Cartesian product) and the depth-position
-    # rotary embedding of q and the tree's K rows, in place.
+    def capture(fns):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(spg):
+                for fn in fns:
+                    fn(copies[i % ncopies])
+        return g
+
+    timer = Timer(torch, spg, reps)
+    phases = {"step": [attn, accept, commit], "attn_accept": [attn, accept], "attention": [attn],
+              "accept": [accept], "commit": [commit]}
+    graphs = {k: capture(f) for k, f in phases.items()}
+    for g in graphs.values():
+        g.replay()
+    torch.cuda.synchronize()
+    t = {k: timer(g) for k, g in graphs.items()}
+    del graphs
+
+    al = copies[0]["al"].cpu().numpy()
+    path = copies[0]["path"].cpu().numpy()
+    step_ms = t["step"]["median_ms"]
+    attn_ms, acc_ms = t["attention"]["median_ms"], t["accept"]["median_ms"]
+    verified = B * (N - 1)
+    emitted = int(al.sum()) + B
+
+    a_bytes = attn_bytes(w)
+    a_flops = attn_flops(w)
+    acc_b = accept_bytes(w, al, path)
+    khash, ahash = kernel_source_hash(), accept_source_hash()
+    attn_traffic = stored_traffic("attn", cfg["name"], cid, khash)
+    acc_traffic = stored_traffic("accept", cfg["name"], cid, ahash)
+    read_peak = None
+    if os.path.exists(READ_PEAK_FILE):
+        with open(READ_PEAK_FILE) as f:
+            read_peak = json.load(f).get("kv_read_GBs")
+    attn_gbs = a_bytes / (attn_ms * 1e-3) / 1e9
+    attn_roof = {"bound": "hbm", "kernel": "spec_verify_attn", "achieved": attn_gbs, "peak": HBM_PEAK_GBS,
+                 "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS, "traffic": attn_traffic,
+                 "algorithmic_bytes_per_launch": a_bytes, "kernel_source_hash": khash,
+                 "measured_read_peak": read_peak,
+                 "frac_of_measured_read_peak": None if read_peak is None else attn_gbs / read_peak}
+    tflops = a_flops / (attn_ms * 1e-3) / 1e12
+    mfma_roof = {"bound": "mfma", "kernel": "spec_verify_attn", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS,
+                 "unit": "TFLOP/s", "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "traffic": attn_traffic,
+                 "algorithmic_flops_per_launch": a_flops, "kernel_source_hash": khash,
+                 "hbm_GBs": attn_gbs, "hbm_frac": attn_gbs / HBM_PEAK_GBS}
+    acc_gbs = acc_b / (acc_ms * 1e-3) / 1e9
+    acc_roof = {"bound": "hbm", "calls": "spec_accept_reject" if w.rule == "reject" else "spec_accept_typical",
+                "achieved": acc_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": acc_gbs / HBM_PEAK_GBS,
+                "traffic": acc_traffic, "algorithmic_bytes_per_call": acc_b, "kernel_source_hash": ahash}
+    # Attention of the many-row tree workload is bound by the matrix cores
+    # (512 FLOP per KV byte); the others by HBM.
+    mfma_bound = cid == 5
+    rec = {
+        "workload": f"{cfg['name']}: B={B}, Hq={w.Hq}/Hkv={w.Hkv}, D={w.D}, {w.dtype} KV prefix "
+                    f"{int(w.prefix_len.min())}..{int(w.prefix_len.max())}, N={N} nodes "
+                    f"({'chain' if w.is_chain else 'tree'}), V={V}, T={w.temperature}, {w.rule} rule",
+        "us_per_step": step_ms * 1e3,
+        "us_per_step_min": t["step"]["min_ms"] * 1e3,
+        "us_per_step_max": t["step"]["max_ms"] * 1e3,
+        "verified_tok_s": verified / (step_ms * 1e-3),
+        "emitted_tok_s": emitted / (step_ms * 1e-3),
+        "verified_per_step": verified,
+        "emitted_per_step": emitted,
+        "breakdown_us": {"attention": attn_ms * 1e3, "accept": acc_ms * 1e3,
+                         "commit": t["commit"]["median_ms"] * 1e3,
+                         "attention_plus_accept": t["attn_accept"]["median_ms"] * 1e3},
+        "roofline": mfma_roof if mfma_bound else attn_roof,
+        "attn_hbm_roofline": attn_roof,
+        "accept_roofline": acc_roof,
+        "timing": {"replays": reps, "steps_per_replay": spg, "timed_steps": reps * spg, "warmup_steps": warmup,
+                   "rotated_copies": ncopies, "mb_between_reuses": ncopies * touched / 2 ** 20},
+        "accept_len_first": al.tolist()[:8],
+    }
+    if with_extras:
+        rec["extras"] = measure_extras(cfg, w, copies, acc_ws, Timer(torch, spg, reps), spg, dev)
+    del copies, attn_ws, acc_ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec, w
+
+
+def measure_extras(cfg, w, copies, acc_ws, timer, spg, dev):
+    """The calls beside the path, each timed on its own on the same workload."""
+    import torch
+
+    import speculative_decoding_verification_tree_amd as sv
+
+    B, N, V = w.B, w.N, w.V
+    ncopies = len(copies)
+    bf16 = w.dtype == "bf16"
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(spg):
+                fn(copies[i % ncopies])
+        g.replay()
+        torch.cuda.synchronize()
+        return g
+
+    out = {}
+    # The step before the path: the Medusa candidate tree (Cartesian trees) and
+    # the depth-position rotary embedding of q and the tree's K rows, in place.
     rope_base = 500000.0
     cartesian = cfg["tree"] == "cartesian"
     if cartesian:
@@ -229,228 +463,154 @@ def main():
         else:
             sv.spec_tree_rope(c["q"], c["k"], c["pl"], c["parent"], rope_base)
 
-    # The rejection rule on a truncated target (top-k, then nucleus), timed on
-    # its own for rejection-rule workloads.
-    filt_k, filt_p = 50, 0.9
+    tree_rope(copies[0])
+    ms = timer(capture(tree_rope))["median_ms"]
+    esz = 2 if bf16 else 4
+    rb = 2 * (B * N * w.Hq * w.D + B * w.Hkv * N * w.D) * esz  # read + write, q and tree K rows
+    out["tree_rope"] = {"us": ms * 1e3, "bytes": rb, "achieved_GBs": rb / (ms * 1e-3) / 1e9,
+                        "calls": ("spec_medusa_tree + " if cartesian else "") + "spec_tree_rope"}
 
-    def accept_filtered(c):
-        sv.spec_accept_reject_filtered(c["logits"], c["draft"], c["tokens"], c["parent"], c["ua"], c["us"],
-                                       w.temperature, filt_k, filt_p, c["al"], c["path"], c["otok"],
-                                       workspace=acc_ws)
+    if w.rule == "reject" and w.temperature > 0:
+        fk, fp = 50, 0.9
 
-    # Multi-draft tree rejection (recursive residuals), timed on its own for
-    # rejection-rule tree workloads.
-    md_ws = None
+        def accept_filtered(c):
+            sv.spec_accept_reject_filtered(c["logits"], c["draft"], c["tokens"], c["parent"], c["ua"], c["us"],
+                                           w.temperature, fk, fp, c["al"], c["path"], c["otok"], workspace=acc_ws)
+
+        for c in copies:
+            accept_filtered(c)
+        ms = timer(capture(accept_filtered))["median_ms"]
+        fb = (B * N * V + 2 * B * V) * 4  # every target row, the stop row and one draft row per request
+        out["filtered_accept"] = {"us": ms * 1e3, "top_k": fk, "top_p": fp, "bytes": fb,
+                                  "achieved_GBs": fb / (ms * 1e-3) / 1e9, "calls": "spec_accept_reject_filtered"}
+
     if w.rule == "reject" and not w.is_chain:
-        md_ws = torch.empty(max(sv.spec_accept_multidraft_workspace_bytes(B, V), 1), dtype=torch.uint8, device=dev)
+        md_ws = torch.empty(max(sv.spec_accept_multidraft_workspace_bytes(B, V), 16), dtype=torch.uint8, device=dev)
 
-    def accept_multidraft(c):
-        sv.spec_accept_multidraft(c["logits"], c["draft"], c["tokens"], c["parent"], c["ua"], c["us"],
-                                  w.temperature, c["al"], c["path"], c["otok"], workspace=md_ws)
+        def accept_multidraft(c):
+            sv.spec_accept_multidraft(c["logits"], c["draft"], c["tokens"], c["parent"], c["ua"], c["us"],
+                                      w.temperature, c["al"], c["path"], c["otok"], workspace=md_ws)
+
+        for c in copies:
+            accept_multidraft(c)
+        ms = timer(capture(accept_multidraft))["median_ms"]
+        out["multidraft_accept"] = {"us": ms * 1e3, "calls": "spec_accept_multidraft"}
 
     # Linear-attention verification of the same trees (16 heads, Dk = Dv =
-    # 128, bf16 q/k/v, fp32 state), its factor commit, and the two fused (the
-    # deferred commit), timed on their own.
+    # 128, bf16 q/k/v, fp32 state), its factor commit, and both fused.
     LH, LD = 16, 128
-    la_state = torch.randn(B, LH, LD, LD, device=dev) / LD ** 0.5
-    la_q = (torch.randn(B, N, LH, LD, device=dev) / LD ** 0.5).to(torch.bfloat16)
-    la_k = torch.randn(B, N, LH, LD, device=dev).to(torch.bfloat16)
-    la_v = torch.randn(B, N, LH, LD, device=dev).to(torch.bfloat16)
-    la_alpha = torch.rand(B, N, LH, device=dev) * 0.4 + 0.6
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    la_state = torch.randn(B, LH, LD, LD, device=dev, generator=g) / LD ** 0.5
+    la_q = (torch.randn(B, N, LH, LD, device=dev, generator=g) / LD ** 0.5).to(torch.bfloat16)
+    la_k = torch.randn(B, N, LH, LD, device=dev, generator=g).to(torch.bfloat16)
+    la_v = torch.randn(B, N, LH, LD, device=dev, generator=g).to(torch.bfloat16)
+    la_alpha = torch.rand(B, N, LH, device=dev, generator=g) * 0.4 + 0.6
     la_out = torch.empty_like(la_v)
-    la_path = copies[0]["path"]
-    la_acc = copies[0]["al"]
-    la_pending = (la_k, la_v, la_alpha, copies[0]["parent"], la_path, la_acc)
-
-    def la_verify(c):
-        sv.spec_la_verify(la_state, la_q, la_k, la_v, la_alpha, c["parent"], out=la_out)
-
-    def la_commit(c):
-        sv.spec_la_commit(la_state, *la_pending)
-
-    def la_fused(c):
-        sv.spec_la_verify(la_state, la_q, la_k, la_v, la_alpha, c["parent"], out=la_out, pending=la_pending)
-
-    # eager warm-up (also checks every call returns SPEC_OK)
-    for i in range(max(args.warmup, ncopies)):
-        step(copies[i % ncopies])
-    torch.cuda.synchronize()
-
-    # One HIP graph per phase covering every rotated copy once: replaying it
-    # launches the kernels back to back without per-call host overhead.
-    def capture(fns):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(spg):
-                for fn in fns:
-                    fn(copies[i % ncopies])
-        return g
-
-    g_step = capture([attn, accept, commit])
-    g_attn = capture([attn])
-    g_acc = capture([accept])
-    g_commit = capture([commit])
-    g_rope = capture([tree_rope])
-    graphs = [g_step, g_attn, g_acc, g_commit, g_rope]
-    g_filt = None
-    if w.rule == "reject" and w.temperature > 0:
-        for i in range(ncopies):
-            accept_filtered(copies[i])
-        g_filt = capture([accept_filtered])
-        graphs.append(g_filt)
-    for fn in (la_verify, la_commit, la_fused):
+    pend = (la_k, la_v, la_alpha, copies[0]["parent"], copies[0]["path"], copies[0]["al"])
+    fns = {
+        "verify": lambda c: sv.spec_la_verify(la_state, la_q, la_k, la_v, la_alpha, c["parent"], out=la_out),
+        "commit": lambda c: sv.spec_la_commit(la_state, *pend),
+        "fused": lambda c: sv.spec_la_verify(la_state, la_q, la_k, la_v, la_alpha, c["parent"], out=la_out,
+                                             pending=pend),
+    }
+    st = B * LH * LD * LD * 4
+    io = B * N * LH * LD * 2 * 4
+    la_b = {"verify": st + io, "commit": 2 * st, "fused": 2 * st + io}
+    la = {"heads": LH, "key_dim": LD, "value_dim": LD}
+    for k, fn in fns.items():
         fn(copies[0])
-    torch.cuda.synchronize()
-    g_lav, g_lac, g_laf = capture([la_verify]), capture([la_commit]), capture([la_fused])
-    graphs += [g_lav, g_lac, g_laf]
-    g_md = None
-    if md_ws is not None:
-        for i in range(ncopies):
-            accept_multidraft(copies[i])
-        g_md = capture([accept_multidraft])
-        graphs.append(g_md)
-    for g in graphs:
-        g.replay()
-    torch.cuda.synchronize()
+        ms = timer(capture(fn))["median_ms"]
+        la[f"{k}_us"] = ms * 1e3
+        la[f"{k}_GBs"] = la_b[k] / (ms * 1e-3) / 1e9
+    la["calls"] = "spec_la_verify, spec_la_commit, spec_la_verify with pending factors"
+    out["linear_attention"] = la
+    out["note"] = "beside the path, each timed alone; not part of the step"
+    return out
 
-    def timed(g, reps):
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); runs on several GPUs are not part of "
+              "this path's measurement", file=sys.stderr)
+        sys.exit(2)
+
+    if args.read_peak:
+        # A child process of its own (nothing here has touched the GPU yet).
+        if not os.path.exists(READ_PROBE):
+            sys.exit(f"{READ_PROBE} is not built (run __graft_entry__.build())")
+        res = subprocess.run([READ_PROBE], capture_output=True, text=True)
+        sys.stderr.write(res.stderr)
+        print(res.stdout.strip(), flush=True)
+        sys.exit(res.returncode)
+
+    import torch
+
+    import speculative_decoding_verification_tree_amd as sv
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sv.lib()  # fails loudly if the HIP library is not built
+
+    if args.copy_calibration:
+        n = 256 << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
         torch.cuda.synchronize()
-        t0.record()
-        for _ in range(reps):
-            g.replay()
-        t1.record()
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / (reps * spg)
+        print(json.dumps({"copy_calibration_bytes": n}))
+        return
 
-    K = reps * spg
-    ms_step = timed(g_step, reps)
-    attn_ms = timed(g_attn, reps)
-    accept_ms = timed(g_acc, reps)
-    commit_ms = timed(g_commit, reps)
-    rope_ms = timed(g_rope, reps)
-    filt_ms = timed(g_filt, reps) if g_filt is not None else None
-    md_ms = timed(g_md, reps) if g_md is not None else None
-    lav_ms, lac_ms, laf_ms = timed(g_lav, reps), timed(g_lac, reps), timed(g_laf, reps)
-    la_state_b = B * LH * LD * LD * 4
-    la_io_b = B * N * LH * LD * 2 * 4  # q, k, v in and out, bf16
-    la_verify_b = la_state_b + la_io_b
-    la_commit_b = 2 * la_state_b  # the state read and written (the path's factors are small)
-    # every target row once (leaf rows too: the stop row may be one), plus the
-    # stop row and one draft row per request for the residual
-    filt_bytes = (B * N * V + 2 * B * V) * 4
-    esz = 2 if bf16 else 4
-    rope_bytes = 2 * (B * N * w.Hq * w.D + B * w.Hkv * N * w.D) * esz  # read + write, q and tree K rows
+    from workloads import config
 
-    a_bytes = attn_bytes(w)
-    achieved = a_bytes / (attn_ms * 1e-3) / 1e9
-    acc_bytes = accept_bytes(w, copies[0]["al"].cpu().numpy(), copies[0]["path"].cpu().numpy())
-    read_peak = None
-    if os.path.exists(READ_PEAK_FILE):
-        with open(READ_PEAK_FILE) as f:
-            read_peak = json.load(f).get("kv_read_GBs")
-    traffic = None
-    khash = kernel_source_hash()
-    if os.path.exists(traffic_file(cfg["name"])):
-        with open(traffic_file(cfg["name"])) as f:
-            tr = json.load(f)
-        if tr.get("kernel_source_hash") == khash and tr.get("config") == args.config:
-            traffic = tr.get("bytes_per_launch")
-
-    verified = B * (N - 1)
-    value = verified / (ms_step * 1e-3)
-    al = copies[0]["al"].cpu().numpy()
-
+    head = args.config
+    order = [head] if args.only else [head] + [c for c in (1, 2, 3, 4, 5) if c != head]
+    recs = {}
     cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
+    for cid in order:
+        t0 = time.time()
+        rec, w = measure(cid, args, dev, with_extras=not args.no_extras)
+        recs[cid] = rec
+        if cid == head and not args.no_cpu_baseline:
+            cpu = cpu_baseline(w, args.cpu_seconds)
+        del w
+        print(f"[bench] {config(cid)['name']}: {rec['us_per_step']:.1f} us/step "
+              f"({time.time() - t0:.0f} s)", file=sys.stderr, flush=True)
 
-        par = None if w.is_chain else w.parent
-        n_done, t_cpu = 0, 0.0
-        T32 = float(np.float32(w.temperature))
-        while n_done == 0 or t_cpu < args.cpu_seconds:
-            s0 = time.perf_counter()
-            oracle.tree_attn(w.q, w.k_cache, w.v_cache, w.prefix_len, par, w.dtype)
-            r = oracle.accept(w.rule, w.target_logits, w.tokens, par, T32, w.draft_probs, w.u_accept,
-                              w.u_sample, float(np.float32(w.epsilon)), float(np.float32(w.delta)))
-            kk, vv = w.k_cache.copy(), w.v_cache.copy()
-            oracle.commit(kk, vv, w.prefix_len.copy(), r["path"], r["accept_len"])
-            t_cpu += time.perf_counter() - s0
-            n_done += 1
-            if n_done >= 1000:
-                break
-        cpu = {"value": verified * n_done / t_cpu, "unit": "verified draft tokens/s", "cores": oracle.num_threads(),
-               "kind": "oracle",
-               "sample": f"{n_done} full steps (attention all rows, acceptance, commit) of the same workload, "
-                         f"{t_cpu:.1f} s on the host"}
-
-    name = cfg["name"]
+    h = recs[head]
+    hc = config(head)
     line = {
-        "metric": "verified draft tokens/s per verify step (attn+accept)",
-        "value": value,
+        "metric": "verified draft tokens/s per verify step (attn+accept); % of HBM peak",
+        "value": h["verified_tok_s"],
         "unit": "verified draft tokens/s",
         "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "steps": h["timing"]["timed_steps"],
+        "warmup": h["timing"]["warmup_steps"],
+        "ms_per_step": h["us_per_step"] * 1e-3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if bf16 else "f32",
-        "data": f"synthetic (seeded; inputs resident in HBM, rotated over {ncopies} copies, "
-                f"{ncopies * touched / 2**20:.0f} MB between reuses of one copy)",
-        "config": {
-            "workload": f"{name}: B={B}, Hq={w.Hq}/Hkv={w.Hkv}, D={w.D}, {w.dtype} KV prefix "
-                        f"{int(w.prefix_len.min())}..{int(w.prefix_len.max())}, N={N} nodes "
-                        f"({'chain' if w.is_chain else 'tree'}), V={V}, T={w.temperature}, {w.rule} rule",
-            "global_batch": B,
-            "parallelism": "single GPU",
-        },
-        "breakdown_us": {"attention": attn_ms * 1e3, "accept": accept_ms * 1e3, "commit": commit_ms * 1e3,
-                         "tree_rope": rope_ms * 1e3},
-        "tree_rope": {"us": rope_ms * 1e3, "bytes": rope_bytes,
-                      "achieved_GBs": rope_bytes / (rope_ms * 1e-3) / 1e9,
-                      "calls": ("spec_medusa_tree + " if cartesian else "") + "spec_tree_rope",
-                      "note": "before the path; not part of ms_per_step"},
-        "filtered_accept": None if filt_ms is None else {
-            "us": filt_ms * 1e3, "top_k": filt_k, "top_p": filt_p, "bytes": filt_bytes,
-            "achieved_GBs": filt_bytes / (filt_ms * 1e-3) / 1e9, "calls": "spec_accept_reject_filtered",
-            "note": "the rejection rule on the top-k / nucleus truncated target; not part of ms_per_step"},
-        "linear_attention": {
-            "heads": LH, "key_dim": LD, "value_dim": LD,
-            "verify_us": lav_ms * 1e3, "verify_GBs": la_verify_b / (lav_ms * 1e-3) / 1e9,
-            "commit_us": lac_ms * 1e3, "commit_GBs": la_commit_b / (lac_ms * 1e-3) / 1e9,
-            "fused_us": laf_ms * 1e3, "fused_GBs": (la_verify_b + la_state_b) / (laf_ms * 1e-3) / 1e9,
-            "calls": "spec_la_verify, spec_la_commit, spec_la_verify with pending factors",
-            "note": "same trees as the workload, bf16 q/k/v, fp32 state; not part of ms_per_step"},
-        "multidraft_accept": None if md_ms is None else {
-            "us": md_ms * 1e3, "calls": "spec_accept_multidraft",
-            "note": "tree rejection by recursive residuals over each node's children; not part of ms_per_step"},
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "spec_verify_attn",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": a_bytes,
-            "kernel_source_hash": khash,
-            "measured_read_peak": read_peak,
-            "frac_of_measured_read_peak": None if read_peak is None else achieved / read_peak,
-        },
-        "accept_roofline": {
-            "bound": "hbm",
-            "calls": "spec_accept_reject" if w.rule == "reject" else "spec_accept_typical",
-            "achieved": acc_bytes / (accept_ms * 1e-3) / 1e9,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": acc_bytes / (accept_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "algorithmic_bytes_per_call": acc_bytes,
-        },
+        "dtype": hc["dtype"],
+        "data": f"synthetic (seeded; inputs resident in HBM, rotated over {h['timing']['rotated_copies']} copies, "
+                f"{h['timing']['mb_between_reuses']:.0f} MB between reuses of one copy)",
+        "config": {"workload": h["workload"], "global_batch": hc["batch"], "parallelism": "single GPU"},
+        "step_includes": "spec_verify_attn + spec_accept_* + spec_commit_kv (the whole verification step); "
+                         "breakdown_us.attention_plus_accept times the first two alone",
+        "verified_definition": "B * (N - 1) per step: every non-root node of the chain or tree is a draft the "
+                               "step adjudicates; emitted_tok_s counts the tokens the step outputs "
+                               "(accepted drafts plus the final token)",
+        "ms_per_step_min": h["us_per_step_min"] * 1e-3,
+        "ms_per_step_max": h["us_per_step_max"] * 1e-3,
+        "emitted_tok_s": h["emitted_tok_s"],
+        "breakdown_us": h["breakdown_us"],
+        "roofline": h["roofline"],
+        "accept_roofline": h["accept_roofline"],
         "cpu_baseline": cpu,
-        "accept_len_last_step": al.tolist()[:8],
+        "timing": h["timing"],
+        "configs": {config(c)["name"]: recs[c] for c in sorted(recs)},
     }
     print(json.dumps(line), flush=True)
 

@@ -59,6 +59,8 @@ def _load():
         lib.oracle_tree_rope.restype = I
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = I
+        lib.oracle_set_num_threads.argtypes = [I]
+        lib.oracle_set_num_threads.restype = I
         _lib = lib
     return _lib
 
@@ -259,6 +261,11 @@ def tree_rope(q, k_cache, prefix_len, parent, dtype, base):
 def num_threads():
     """OpenMP threads the oracle runs with."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n):
+    """Sets the oracle's OpenMP thread count; returns the count in effect."""
+    return int(_load().oracle_set_num_threads(int(n)))
 
 
 def run_workload(w, rows=None, attention=True, accept_=True):

@@ -748,3 +748,12 @@ int oracle_num_threads(void) {
     return 1;
 #endif
 }
+
+/* Sets the thread count of the OpenMP loops above (n >= 1); returns the
+ * count now in effect. */
+int oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#endif
+    return oracle_num_threads();
+}

@@ -16,21 +16,6 @@ FLAGS = [
 ]
 
 
-PROBE_SRC = os.path.join(CSRC, "hbm_read_probe.hip")
-PROBE = os.path.join(HERE, "hbm_read_probe")
-
-
-def build_probe(verbose=False):
-    """Compile the streaming-read calibration program (bench.py --read-peak)."""
-    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", PROBE_SRC, "-o", PROBE + ".tmp"]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + res.stderr)
-    os.replace(PROBE + ".tmp", PROBE)
-    return PROBE
-
-
 def build(verbose=False):
     """Compile every HIP source into libspecverify.so (always recompiles)."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
@@ -45,7 +30,6 @@ def build(verbose=False):
     if verbose and err.strip():
         print(err, file=sys.stderr)
     os.replace(tmp, LIB)
-    build_probe(verbose)
     return LIB
 
 

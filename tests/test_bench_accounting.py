@@ -60,19 +60,33 @@ def test_attention_bytes_count_each_kv_row_once():
 
 
 def test_stored_traffic_matches_each_workload():
-    # Every stored attention traffic file names the configuration it was
-    # measured on, and the bench looks it up by that workload's name.
+    # Every stored traffic file (attention and acceptance calls) names the
+    # configuration it was measured on, and the bench looks it up by that
+    # workload's name.
     from workloads.configs import config
     import json
     found = 0
-    for cid in (1, 2, 3, 4, 5):
-        path = bench.traffic_file(config(cid)["name"])
-        if not os.path.exists(path):
-            continue
-        found += 1
-        with open(path) as f:
-            tr = json.load(f)
-        assert tr["config"] == cid
-        assert tr["bytes_per_launch"] > 0
-        assert len(tr["kernel_source_hash"]) == len(bench.kernel_source_hash())
+    for kind in ("attn", "accept"):
+        for cid in (1, 2, 3, 4, 5):
+            path = bench.traffic_file(kind, config(cid)["name"])
+            if not os.path.exists(path):
+                continue
+            found += 1
+            with open(path) as f:
+                tr = json.load(f)
+            assert tr["config"] == cid
+            assert tr["bytes_per_launch"] > 0
+            assert len(tr["kernel_source_hash"]) == len(bench.kernel_source_hash())
     assert found >= 1
+
+
+def test_attention_flops_follow_root_paths():
+    # chain of 3 over prefixes 5 and 9: node i sees L + i + 1 keys
+    w = SimpleNamespace(dtype="bf16", prefix_len=np.array([5, 9]), N=3, Hkv=2, D=4, B=2, Hq=4, is_chain=True,
+                        parent=None)
+    keys = (5 + 1) + (5 + 2) + (5 + 3) + (9 + 1) + (9 + 2) + (9 + 3)
+    assert bench.attn_flops(w) == 4 * 4 * 4 * keys
+    # tree 0 <- 1, 0 <- 2, 1 <- 3: depths 0, 1, 1, 2
+    t = SimpleNamespace(dtype="bf16", prefix_len=np.array([7]), N=4, Hkv=1, D=8, B=1, Hq=2, is_chain=False,
+                        parent=np.array([[-1, 0, 0, 1]]))
+    assert bench.attn_flops(t) == 4 * 8 * 2 * (4 * 7 + 1 + 2 + 2 + 3)

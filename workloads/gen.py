@@ -25,10 +25,24 @@ BF16_NAN = np.uint16(0x7FC0)
 
 
 def bf16_bits(x):
-    """float32 -> bfloat16 bit patterns (uint16), round to nearest even."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    rnd = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
-    return ((u + rnd) >> np.uint32(16)).astype(np.uint16)
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even.
+
+    Worked in slices of 4M elements with in-place uint32 arithmetic (the same
+    operations on every element as one whole-array expression, without its
+    full-size temporaries)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.reshape(-1).view(np.uint32)
+    out = np.empty(u.size, dtype=np.uint16)
+    step = 1 << 22
+    for s in range(0, u.size, step):
+        c = u[s:s + step]
+        t = c >> np.uint32(16)
+        t &= np.uint32(1)
+        t += np.uint32(0x7FFF)
+        t += c
+        t >>= np.uint32(16)
+        out[s:s + step] = t
+    return out.reshape(x.shape)
 
 
 def bf16_to_f32(b):
@@ -167,21 +181,20 @@ def generate(cfg, variant=0, poison=True, with_attention=True, with_accept=True,
 
     q = k_cache = v_cache = None
     if with_attention:
-        qf = _normal_f32(_rng(cid, S_Q, variant), (B, N, Hq, D))
-        kf = np.empty((B, Hkv, cap, D), dtype=np.float32)
-        vf = np.empty((B, Hkv, cap, D), dtype=np.float32)
+        bf16 = cfg["dtype"] == "bf16"
+        conv = bf16_bits if bf16 else (lambda a: a)
+        q = conv(_normal_f32(_rng(cid, S_Q, variant), (B, N, Hq, D)))
+        et = np.uint16 if bf16 else np.float32
+        fill = (BF16_NAN if poison else np.uint16(0)) if bf16 else (np.float32(np.nan) if poison else np.float32(0))
+        k_cache = np.empty((B, Hkv, cap, D), dtype=et)
+        v_cache = np.empty((B, Hkv, cap, D), dtype=et)
         rk, rv = _rng(cid, S_K, variant), _rng(cid, S_V, variant)
-        for b in range(B):
+        for b in range(B):  # per request: the same draws, converted as they come
             rows = int(prefix_len[b]) + N
-            kf[b, :, :rows] = _normal_f32(rk, (Hkv, rows, D))
-            vf[b, :, :rows] = _normal_f32(rv, (Hkv, rows, D))
-            kf[b, :, rows:] = np.nan if poison else 0.0
-            vf[b, :, rows:] = np.nan if poison else 0.0
-        if cfg["dtype"] == "bf16":
-            q, k_cache, v_cache = bf16_bits(qf), bf16_bits(kf), bf16_bits(vf)
-        else:
-            q, k_cache, v_cache = qf, kf, vf
-        del qf, kf, vf
+            k_cache[b, :, :rows] = conv(_normal_f32(rk, (Hkv, rows, D)))
+            v_cache[b, :, :rows] = conv(_normal_f32(rv, (Hkv, rows, D)))
+            k_cache[b, :, rows:] = fill
+            v_cache[b, :, rows:] = fill
 
     tokens = np.zeros((B, N), dtype=np.int32)
     logits = draft = u_acc = u_smp = None
