@@ -125,6 +125,23 @@ int spec_accept_reject(int32_t batch, int32_t num_nodes, int32_t vocab, const fl
                        int32_t* accept_len, int32_t* path, int32_t* out_tokens, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* spec_accept_reject without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same rule, arguments, outputs and
+ * kernels as spec_accept_reject; the scratch it needs lives in one array per
+ * GPU inside the library (SPEC_ACCEPT_NOALLOC_MAX_WORKSPACE bytes, held
+ * until the process ends).  Shapes whose spec_accept_workspace_bytes exceeds
+ * that return SPEC_EWORKSPACE before any launch.  Nothing is allocated or
+ * freed.  Every call on one GPU uses that GPU's array: two calls that overlap
+ * in time on one GPU (different streams, or other host threads) race and
+ * give undefined results; calls ordered on one stream are safe.  Device: the
+ * current HIP device (SPEC_EUNSUPPORTED for an ordinal >= 64). */
+#define SPEC_ACCEPT_NOALLOC_MAX_WORKSPACE (8u << 20)
+int spec_accept_reject_noalloc(int32_t batch, int32_t num_nodes, int32_t vocab, const float* target_logits,
+                               const float* draft_probs, const int32_t* tokens, const int32_t* parent,
+                               const float* u_accept, const float* u_sample, float temperature,
+                               int32_t* accept_len, int32_t* path, int32_t* out_tokens, void* stream);
+
 /* Rejection-rule acceptance on a truncated target (the "Speculative
  * Sampling" section of the same page lets top-k and nucleus sampling
  * transform the probabilities before the rule).  Every p_u of

@@ -131,6 +131,28 @@ def spec_accept_reject(target_logits, draft_probs, tokens, parent, u_accept, u_s
     return accept_len, path, out_tokens
 
 
+def spec_accept_reject_noalloc(target_logits, draft_probs, tokens, parent, u_accept, u_sample, temperature,
+                               accept_len, path, out_tokens, stream=None):
+    """spec_accept_reject with the library's per-GPU scratch instead of a
+    workspace; the outputs must be passed in (nothing is allocated)."""
+    B, N, V = target_logits.shape
+    _dev(target_logits, "target_logits", torch.float32)
+    _dev(draft_probs, "draft_probs", torch.float32)
+    _dev(tokens, "tokens", torch.int32)
+    _dev(parent, "parent", torch.int32)
+    _dev(u_accept, "u_accept", torch.float32)
+    _dev(u_sample, "u_sample", torch.float32)
+    for t, n in ((accept_len, "accept_len"), (path, "path"), (out_tokens, "out_tokens")):
+        if t is None:
+            raise ValueError(f"{n} must be passed in")
+        _dev(t, n, torch.int32)
+    rc = _native.lib().spec_accept_reject_noalloc(B, N, V, _ptr(target_logits), _ptr(draft_probs), _ptr(tokens),
+                                                  _ptr(parent), _ptr(u_accept), _ptr(u_sample), float(temperature),
+                                                  _ptr(accept_len), _ptr(path), _ptr(out_tokens), _stream(stream))
+    _check("spec_accept_reject_noalloc", rc)
+    return accept_len, path, out_tokens
+
+
 def spec_accept_reject_filtered(target_logits, draft_probs, tokens, parent, u_accept, u_sample, temperature,
                                 top_k=0, top_p=1.0, accept_len=None, path=None, out_tokens=None, workspace=None,
                                 stream=None):

@@ -2,6 +2,8 @@
 // Nothing here allocates, frees or synchronises.
 #include <math.h>
 
+#include <mutex>
+
 #include "spec_common.h"
 #include "spec_internal.h"
 
@@ -30,6 +32,30 @@ static bool desc_ok(const spec_attn_desc* d, int* err) {
 }
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Scratch of spec_accept_reject_noalloc: one array per GPU, in the library's
+// code object, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: kernels and copies get the device
+// address that hipGetSymbolAddress returns for the current device, looked
+// up once per device and cached.
+constexpr int kMaxScratchDevices = 64;
+static __device__ __align__(256) unsigned char scratch[SPEC_ACCEPT_NOALLOC_MAX_WORKSPACE];
+static std::mutex g_scratch_mutex;
+static void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+static int device_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return SPEC_EHIP;
+    if (dev < 0 || dev >= kMaxScratchDevices) return SPEC_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SPEC_EHIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SPEC_OK;
+}
 
 extern "C" {
 
@@ -93,6 +119,26 @@ int spec_accept_reject(int32_t batch, int32_t num_nodes, int32_t vocab, const fl
     if (!workspace || workspace_bytes < plan.ws_bytes) return SPEC_EWORKSPACE;
     return launch_accept(0, batch, num_nodes, vocab, target_logits, draft_probs, tokens, parent, u_accept,
                          u_sample, temperature, 0.f, 0.f, accept_len, path, out_tokens, workspace, plan,
+                         static_cast<hipStream_t>(stream));
+}
+
+int spec_accept_reject_noalloc(int32_t batch, int32_t num_nodes, int32_t vocab, const float* target_logits,
+                               const float* draft_probs, const int32_t* tokens, const int32_t* parent,
+                               const float* u_accept, const float* u_sample, float temperature, int32_t* accept_len,
+                               int32_t* path, int32_t* out_tokens, void* stream) {
+    if (batch < 0) return SPEC_EINVAL;
+    if (batch == 0) return SPEC_OK;
+    int rc = accept_common_checks(batch, num_nodes, vocab, target_logits, tokens, accept_len, path, out_tokens,
+                                  temperature);
+    if (rc != SPEC_OK) return rc;
+    if ((num_nodes > 1 && (!draft_probs || !u_accept)) || !u_sample) return SPEC_EINVAL;
+    const AcceptPlan plan = plan_accept(batch, num_nodes, vocab);
+    if (plan.ws_bytes > SPEC_ACCEPT_NOALLOC_MAX_WORKSPACE) return SPEC_EWORKSPACE;
+    void* ws = nullptr;
+    rc = device_scratch(&ws);
+    if (rc != SPEC_OK) return rc;
+    return launch_accept(0, batch, num_nodes, vocab, target_logits, draft_probs, tokens, parent, u_accept,
+                         u_sample, temperature, 0.f, 0.f, accept_len, path, out_tokens, ws, plan,
                          static_cast<hipStream_t>(stream));
 }
 

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     lib = sv.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -137,6 +137,21 @@ def test_accept_argument_errors():
 def _filt(B=2, N=6, V=1000, T=1.0, k=5, p=0.9, ws_bytes=1 << 30):
     return sv.lib().spec_accept_reject_filtered(B, N, V, FAKE, FAKE, FAKE, None, FAKE, FAKE, T, k, p, FAKE, FAKE,
                                                 FAKE, FAKE, ws_bytes, None)
+
+
+def test_noalloc_accept_errors():
+    # Host-side checks only: none of these reach a device call.
+    lib = sv.lib()
+    call = lambda B=2, N=6, V=1000, T=1.0, us=FAKE: lib.spec_accept_reject_noalloc(
+        B, N, V, FAKE, FAKE, FAKE, None, FAKE, us, T, FAKE, FAKE, FAKE, None)
+    assert call(B=-1) == EINVAL
+    assert call(B=0) == OK
+    assert call(N=65) == EINVAL
+    assert call(T=float("nan")) == EINVAL
+    assert call(us=None) == EINVAL
+    # a shape whose workspace exceeds the library's scratch array
+    assert sv.spec_accept_workspace_bytes(4096, 64, 128256) > (8 << 20)
+    assert call(B=4096, N=64, V=128256) == EWORKSPACE
 
 
 def test_filtered_accept_errors():
