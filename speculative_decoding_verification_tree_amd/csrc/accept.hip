@@ -252,14 +252,15 @@ struct Vals {
 // at once; a load under a branch would make the compiler wait for it before
 // the next.  With 16-byte rows x1 is a multiple of 4, like every x here, so
 // a run of four is either wholly inside the chunk or wholly outside.
-template <int EPT>
+template <int EPT, bool NT = false>
 __device__ __forceinline__ Vals<EPT> load_chunk(const float* row, int x0, int x1, bool vec4, float fill) {
     Vals<EPT> r;
     if (vec4) {
 #pragma unroll
         for (int j = 0; j < EPT / 4; ++j) {
             const int x = x0 + 4 * (static_cast<int>(threadIdx.x) + kThreads * j);
-            const float4 v = *reinterpret_cast<const float4*>(row + static_cast<unsigned>(min(x, x1 - 4)));
+            const float* src = row + static_cast<unsigned>(min(x, x1 - 4));
+            const float4 v = NT ? ld_stream_f4(src) : *reinterpret_cast<const float4*>(src);
             const bool in = x < x1;
             r.v[4 * j] = in ? v.x : fill;
             r.v[4 * j + 1] = in ? v.y : fill;
@@ -353,10 +354,10 @@ struct WaveRed {
 // ARG = false skips the lowest argmax (arg is left at 0x7fffffff) and ENT =
 // false the entropy sum (A2 stays 0): the rejection rule at T > 0 uses
 // neither, and both cost VALU work per element in a VALU-heavy pass.
-template <int EPT, bool FILT = false, bool ARG = true, bool ENT = true>
+template <int EPT, bool FILT = false, bool ARG = true, bool ENT = true, bool NT = false>
 __device__ __forceinline__ void chunk_stats(const float* row, int x0, int x1, bool vec4, float T, float& M, int& arg,
                                             double& S, double& A2, WaveRed* s, uint32_t tau = 0u) {
-    const Vals<EPT> vals = load_chunk<EPT>(row, x0, x1, vec4, -INFINITY);
+    const Vals<EPT> vals = load_chunk<EPT, NT>(row, x0, x1, vec4, -INFINITY);
     const int tid = static_cast<int>(threadIdx.x);
     // Element e has token id first + off(e); it is in range iff off(e) < lim
     // (with 16-byte rows a run of four is wholly in or out).
@@ -447,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void accept_rowstats(AcceptArgs a) {
     float M;
     int arg;
     double S, A2;
-    chunk_stats<EPT, false, ARG, ENT>(row, x0, x1, a.vec4 != 0, a.T, M, arg, S, A2, &s_red);
+    chunk_stats<EPT, false, ARG, ENT, true>(row, x0, x1, a.vec4 != 0, a.T, M, arg, S, A2, &s_red);
     if (threadIdx.x == 0) {
         RowStat rs;
         rs.S = S;

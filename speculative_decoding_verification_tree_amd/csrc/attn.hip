@@ -298,12 +298,12 @@ __device__ __forceinline__ void load_kv_block(KVBlock<D>& blk, const uint16_t* k
         const int row = min(kb + 8 * (n16 >> 2) + 4 * h + (n16 & 3), row_max);
 #pragma unroll
         for (int c = 0; c < KVBlock<D>::NC32; ++c)
-            blk.kf[h][c] = *reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(row) * D + 32 * c + 8 * q4);
+            blk.kf[h][c] = ld_stream(kbase + static_cast<size_t>(row) * D + 32 * c + 8 * q4);
     }
 #pragma unroll
     for (int jj = 0; jj < KVBlock<D>::KPL; ++jj) {
         const int row = min(kb + vkg * KVBlock<D>::KPL + jj, row_max);
-        blk.vr[jj] = *reinterpret_cast<const u32x4*>(vbase + static_cast<size_t>(row) * D + 8 * vch);
+        blk.vr[jj] = ld_stream(vbase + static_cast<size_t>(row) * D + 8 * vch);
     }
 }
 
@@ -652,7 +652,7 @@ constexpr int wg_waves() {
 template <int D>
 __device__ __forceinline__ u32x4 kv_chunk(const uint16_t* base, int kb, int r, int ch, int Tk) {
     const int row = min(kb + r, Tk - 1);
-    return *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(row) * D + ch * 8);
+    return ld_stream(base + static_cast<size_t>(row) * D + ch * 8);
 }
 
 template <int D, int WK>
