@@ -8,6 +8,8 @@
 //         walks 32-row blocks of two separate 256-byte-row tensors (K and V,
 //         one block of each prefetched ahead), eight 128-byte lines of K per
 //         load instruction and four whole rows of V.
+// Both run twice: with plain loads and with the non-temporal hint (nt), which
+// streams faster on this chip.
 // Every workgroup's range lies inside the buffers (checked on the host before
 // each launch).  Output: one JSON line with the best rate of each kernel.
 #include <hip/hip_runtime.h>
@@ -19,28 +21,32 @@
 
 namespace {
 
-struct __attribute__((aligned(16))) U4 {
-    unsigned x, y, z, w;
-};
+typedef unsigned U4 __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ U4 ld(const U4* p) {
+    return NT ? __builtin_nontemporal_load(p) : *p;
+}
 
 constexpr int kFlatU = 4;  // 16-byte loads per lane per step
 
+template <bool NT>
 __global__ __launch_bounds__(64) void flat_read(const U4* __restrict__ buf, size_t per_wg, unsigned* out) {
     const U4* p = buf + blockIdx.x * per_wg + threadIdx.x;
     const size_t steps = per_wg / (64 * kFlatU);  // even, >= 2
     U4 a[kFlatU], b[kFlatU];
     unsigned acc = 0;
 #pragma unroll
-    for (int u = 0; u < kFlatU; ++u) a[u] = p[u * 64];
+    for (int u = 0; u < kFlatU; ++u) a[u] = ld<NT>(p + u * 64);
     for (size_t i = 0; i < steps; i += 2) {
         const size_t nb = (i + 1) * 64 * kFlatU;
 #pragma unroll
-        for (int u = 0; u < kFlatU; ++u) b[u] = p[nb + u * 64];
+        for (int u = 0; u < kFlatU; ++u) b[u] = ld<NT>(p + nb + u * 64);
 #pragma unroll
         for (int u = 0; u < kFlatU; ++u) acc ^= a[u].x ^ a[u].y ^ a[u].z ^ a[u].w;
         const size_t na = (i + 2 < steps ? i + 2 : i) * 64 * kFlatU;
 #pragma unroll
-        for (int u = 0; u < kFlatU; ++u) a[u] = p[na + u * 64];
+        for (int u = 0; u < kFlatU; ++u) a[u] = ld<NT>(p + na + u * 64);
 #pragma unroll
         for (int u = 0; u < kFlatU; ++u) acc ^= b[u].x ^ b[u].y ^ b[u].z ^ b[u].w;
     }
@@ -48,27 +54,29 @@ __global__ __launch_bounds__(64) void flat_read(const U4* __restrict__ buf, size
 }
 
 // One 32-row block of K and V (rows of 16 chunks of 16 bytes).
+template <bool NT>
 __device__ __forceinline__ void kv_block(U4 (&kf)[8], U4 (&vr)[8], const U4* K, const U4* V, long row0, int lane) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) kf[i] = K[(row0 + 8 * (i >> 1) + (lane >> 3)) * 16 + (i & 1) * 8 + (lane & 7)];
+    for (int i = 0; i < 8; ++i) kf[i] = ld<NT>(K + (row0 + 8 * (i >> 1) + (lane >> 3)) * 16 + (i & 1) * 8 + (lane & 7));
 #pragma unroll
-    for (int j = 0; j < 8; ++j) vr[j] = V[(row0 + 8 * (lane >> 4) + j) * 16 + (lane & 15)];
+    for (int j = 0; j < 8; ++j) vr[j] = ld<NT>(V + (row0 + 8 * (lane >> 4) + j) * 16 + (lane & 15));
 }
 
+template <bool NT>
 __global__ __launch_bounds__(64) void kv_read(const U4* __restrict__ K, const U4* __restrict__ V, long blocks_per_wg,
                                               unsigned* out) {
     const int lane = threadIdx.x;
     long row0 = static_cast<long>(blockIdx.x) * blocks_per_wg * 32;
     U4 kf[8], vr[8];
     unsigned acc = 0;
-    kv_block(kf, vr, K, V, row0, lane);
+    kv_block<NT>(kf, vr, K, V, row0, lane);
     for (long b = 0; b < blocks_per_wg; ++b) {
         unsigned t = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) t ^= kf[i].x ^ kf[i].w ^ vr[i].y ^ vr[i].z;
         acc += t;
         const long next = b + 1 < blocks_per_wg ? row0 + 32 : row0;
-        kv_block(kf, vr, K, V, next, lane);
+        kv_block<NT>(kf, vr, K, V, next, lane);
         row0 = next;
     }
     out[blockIdx.x * 64 + lane] = acc;
@@ -121,39 +129,53 @@ int main() {
     int cus = 0;
     check(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0), "attribute");
 
-    double best_flat = 0.0, best_kv = 0.0;
-    int flat_grid = 0, kv_grid = 0;
-    // flat: one 2 GiB buffer, one contiguous range per workgroup
-    for (int per_cu : {4, 8, 16}) {
-        const int grid = std::min(per_cu * cus, kMaxGrid);
-        const size_t n16 = half / 16;
-        size_t per_wg = n16 / grid / (128 * kFlatU) * (128 * kFlatU);
-        if (per_wg < 128 * kFlatU || static_cast<size_t>(grid) * per_wg > n16) continue;
-        const float ms = time_ms([&] { hipLaunchKernelGGL(flat_read, dim3(grid), dim3(64), 0, nullptr, a, per_wg, out); },
-                                 10);
-        const double gbs = static_cast<double>(grid) * per_wg * 16 / (ms * 1e6);
-        if (gbs > best_flat) {
-            best_flat = gbs;
-            flat_grid = grid;
+    // best[nt][kind]: kind 0 = flat, 1 = kv
+    double best[2][2] = {{0.0, 0.0}, {0.0, 0.0}};
+    int best_grid[2][2] = {{0, 0}, {0, 0}};
+    for (int nt = 0; nt < 2; ++nt) {
+        // flat: one 2 GiB buffer, one contiguous range per workgroup
+        for (int per_cu : {4, 8, 16}) {
+            const int grid = std::min(per_cu * cus, kMaxGrid);
+            const size_t n16 = half / 16;
+            size_t per_wg = n16 / grid / (128 * kFlatU) * (128 * kFlatU);
+            if (per_wg < 128 * kFlatU || static_cast<size_t>(grid) * per_wg > n16) continue;
+            const float ms = time_ms(
+                [&] {
+                    if (nt) hipLaunchKernelGGL(flat_read<true>, dim3(grid), dim3(64), 0, nullptr, a, per_wg, out);
+                    else hipLaunchKernelGGL(flat_read<false>, dim3(grid), dim3(64), 0, nullptr, a, per_wg, out);
+                },
+                10);
+            const double gbs = static_cast<double>(grid) * per_wg * 16 / (ms * 1e6);
+            if (gbs > best[nt][0]) {
+                best[nt][0] = gbs;
+                best_grid[nt][0] = grid;
+            }
         }
-    }
-    for (int per_cu : {4, 8}) {
-        const int grid = std::min(per_cu * cus, kMaxGrid);
-        const long rows = static_cast<long>(half / 256);
-        const long bpw = rows / 32 / grid;
-        if (bpw < 1 || static_cast<long>(grid) * bpw * 32 > rows) continue;
-        const float ms = time_ms([&] { hipLaunchKernelGGL(kv_read, dim3(grid), dim3(64), 0, nullptr, a, b, bpw, out); },
-                                 10);
-        const double gbs = static_cast<double>(grid) * bpw * 32 * 256 * 2 / (ms * 1e6);
-        if (gbs > best_kv) {
-            best_kv = gbs;
-            kv_grid = grid;
+        // kv: the attention kernels' access shape over two 2 GiB tensors
+        for (int per_cu : {4, 8}) {
+            const int grid = std::min(per_cu * cus, kMaxGrid);
+            const long rows = static_cast<long>(half / 256);
+            const long bpw = rows / 32 / grid;
+            if (bpw < 1 || static_cast<long>(grid) * bpw * 32 > rows) continue;
+            const float ms = time_ms(
+                [&] {
+                    if (nt) hipLaunchKernelGGL(kv_read<true>, dim3(grid), dim3(64), 0, nullptr, a, b, bpw, out);
+                    else hipLaunchKernelGGL(kv_read<false>, dim3(grid), dim3(64), 0, nullptr, a, b, bpw, out);
+                },
+                10);
+            const double gbs = static_cast<double>(grid) * bpw * 32 * 256 * 2 / (ms * 1e6);
+            if (gbs > best[nt][1]) {
+                best[nt][1] = gbs;
+                best_grid[nt][1] = grid;
+            }
         }
     }
     check(hipFree(a), "free");
     check(hipFree(b), "free");
     check(hipFree(out), "free");
-    std::printf("{\"flat_read_GBs\": %.1f, \"flat_grid\": %d, \"kv_read_GBs\": %.1f, \"kv_grid\": %d, \"cus\": %d}\n",
-                best_flat, flat_grid, best_kv, kv_grid, cus);
+    const double kv = std::max(best[0][1], best[1][1]);
+    std::printf("{\"flat_read_GBs\": %.1f, \"flat_nt_read_GBs\": %.1f, \"kv_plain_read_GBs\": %.1f, "
+                "\"kv_nt_read_GBs\": %.1f, \"kv_read_GBs\": %.1f, \"flat_grid\": %d, \"kv_grid\": %d, \"cus\": %d}\n",
+                best[0][0], best[1][0], best[0][1], best[1][1], kv, best_grid[1][0], best_grid[1][1], cus);
     return 0;
 }
