@@ -277,7 +277,7 @@ typedef struct {
     int32_t num_heads;   /* H >= 1 */
     int32_t key_dim;     /* Dk: 64 or 128 */
     int32_t value_dim;   /* Dv: 64 or 128 */
-    spec_dtype dtype;    /* q, k, v and out: fp32 or bf16 */
+    int32_t dtype;       /* spec_dtype of q, k, v and out: fp32 or bf16 */
 } spec_la_desc;
 
 /* The factors of one step's accepted path: that step's tree (its k, v,

@@ -22,8 +22,14 @@ _lib = None
 
 
 def build(force=True):
-    """Compile oracle.c into liboracle.so with gcc (OpenMP, no fast-math)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", _LIB + ".tmp", "-lm"]
+    """Compile oracle.c into liboracle.so with gcc (OpenMP, no fast-math).
+
+    ORACLE_CC and ORACLE_CFLAGS replace the compiler and add flags (the CPU
+    sanitizer run, tests/sanitize_cpu.sh, builds it with clang and
+    address/undefined-behaviour checks)."""
+    cc = os.environ.get("ORACLE_CC", "gcc")
+    extra = os.environ.get("ORACLE_CFLAGS", "").split()
+    cmd = [cc, "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", *extra, _SRC, "-o", _LIB + ".tmp", "-lm"]
     if force or not os.path.exists(_LIB):
         subprocess.run(cmd, check=True)
         os.replace(_LIB + ".tmp", _LIB)

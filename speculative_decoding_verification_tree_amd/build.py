@@ -17,10 +17,17 @@ FLAGS = [
 
 
 def build(verbose=False):
-    """Compile every HIP source into libspecverify.so (always recompiles)."""
+    """Compile every HIP source into libspecverify.so (always recompiles).
+
+    SPEC_HOST_FLAGS (whitespace-separated) adds flags for the host side, each
+    passed behind -Xarch_host so device code is untouched; the CPU sanitizer
+    run (tests/sanitize_cpu.sh) uses it."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp]
+    host = []
+    for f in os.environ.get("SPEC_HOST_FLAGS", "").split():
+        host += ["-Xarch_host", f]
+    cmd = [HIPCC, *FLAGS, *host, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
