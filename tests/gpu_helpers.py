@@ -110,4 +110,7 @@ def check_accept(w, gpu, ref):
         assert a == ref["accept_len"][b], (b, a, ref["accept_len"][b], ref["margin"][b])
         np.testing.assert_array_equal(pth, ref["path"][b], err_msg=f"path b={b}")
         np.testing.assert_array_equal(out, ref["out_tokens"][b], err_msg=f"out_tokens b={b}")
+    # A case whose every request is a near-tie would pass without comparing
+    # anything bit for bit.
+    assert B == 0 or excluded < B, f"all {B} requests are near-ties: nothing was compared"
     return excluded
