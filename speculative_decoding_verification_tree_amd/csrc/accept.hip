@@ -354,10 +354,9 @@ struct WaveRed {
 // ARG = false skips the lowest argmax (arg is left at 0x7fffffff) and ENT =
 // false the entropy sum (A2 stays 0): the rejection rule at T > 0 uses
 // neither, and both cost VALU work per element in a VALU-heavy pass.
-template <int EPT, bool FILT = false, bool ARG = true, bool ENT = true, bool NT = false>
-__device__ __forceinline__ void chunk_stats(const float* row, int x0, int x1, bool vec4, float T, float& M, int& arg,
-                                            double& S, double& A2, WaveRed* s, uint32_t tau = 0u) {
-    const Vals<EPT> vals = load_chunk<EPT, NT>(row, x0, x1, vec4, -INFINITY);
+template <int EPT, bool FILT = false, bool ARG = true, bool ENT = true>
+__device__ __forceinline__ void chunk_reduce(const Vals<EPT>& vals, int x0, int x1, bool vec4, float T, float& M,
+                                             int& arg, double& S, double& A2, WaveRed* s, uint32_t tau = 0u) {
     const int tid = static_cast<int>(threadIdx.x);
     // Element e has token id first + off(e); it is in range iff off(e) < lim
     // (with 16-byte rows a run of four is wholly in or out).
@@ -430,6 +429,13 @@ __device__ __forceinline__ void chunk_stats(const float* row, int x0, int x1, bo
     }
 }
 
+template <int EPT, bool FILT = false, bool ARG = true, bool ENT = true, bool NT = false>
+__device__ __forceinline__ void chunk_stats(const float* row, int x0, int x1, bool vec4, float T, float& M, int& arg,
+                                            double& S, double& A2, WaveRed* s, uint32_t tau = 0u) {
+    const Vals<EPT> vals = load_chunk<EPT, NT>(row, x0, x1, vec4, -INFINITY);
+    chunk_reduce<EPT, FILT, ARG, ENT>(vals, x0, x1, vec4, T, M, arg, S, A2, s, tau);
+}
+
 // Does node u of request b have a child?  (Wave-uniform; chains need no load.)
 __device__ __forceinline__ bool row_has_children(const AcceptArgs& a, int b, int u) {
     if (!a.parent) return u < a.N - 1;
@@ -468,16 +474,125 @@ __global__ __launch_bounds__(kThreads) void accept_rowstats(AcceptArgs a) {
 // FILT: the target rows are truncated (top-k / nucleus); their statistics
 // come whole from the per-row records, for every row (the stop row may be a
 // leaf).
+// LDS state of one request's decision: per node row, the row max M, its
+// lowest argmax, S = sum exp((l - M)/T) and the entropy H (natural log) of
+// p = softmax(l/T); the accepted path, the drafted tokens and the record.
+struct DecLds {
+    float M[kMaxNodes];
+    int arg[kMaxNodes];
+    double S[kMaxNodes], H[kMaxNodes];
+    int path[kMaxNodes];
+    uint32_t tau[kMaxNodes];
+    int tok[kMaxNodes];
+    Decision dec;
+};
+
+// The decision of request b, by wave 0 alone, from the row statistics in L
+// (rows with children; every row when truncated) and lane i's node inputs:
+// parent pi (-1 root, -2 unreachable), token xi (clamped), accept uniform
+// ui, the logit of the parent row at the token glf and the draft
+// probability gq.  Node tests in fp64; a node is accepted when every node
+// on its root path passed; the stop node v is the deepest accepted node,
+// the lowest index among equals.  Lane 0 writes L.dec, the lanes on the
+// path L.path.
+template <bool FILT>
+__device__ __forceinline__ void decide_core(const AcceptArgs& a, int b, int pi, int xi, float ui, float usi, float glf,
+                                            double gq, DecLds& L) {
+    const int N = a.N, lane = threadIdx.x & 63;
+    const double T = a.T;
+    const double gl = glf;
+    // Node tests in fp64 from the gathered values.
+    bool ok = false;
+    if (lane >= 1 && lane < N && pi >= 0) {
+        double pu;
+        if (T > 0.0)
+            pu = FILT && logit_key(glf) < L.tau[pi] ? 0.0 : exp((gl - static_cast<double>(L.M[pi])) / T) / L.S[pi];
+        else
+            pu = xi == L.arg[pi] ? 1.0 : 0.0;
+        if (a.rule == 0) {
+            ok = static_cast<double>(ui) * gq < pu;
+        } else {
+            const double thr = fmin(static_cast<double>(a.eps), static_cast<double>(a.delta) * exp(-L.H[pi]));
+            ok = pu > thr;
+        }
+    }
+    const uint64_t okm = __ballot(ok) | 1ull;  // the root is always accepted
+    // Root paths by pointer doubling: after round k a lane holds its
+    // first 2^k path nodes and its 2^k-th ancestor.
+    const int me = lane < N ? lane : 0;
+    uint64_t anc;
+    if (!a.parent) {  // chain: nodes 0..me
+        anc = me == 63 ? ~0ull : (2ull << me) - 1ull;
+    } else {
+        int up = lane < N ? pi : -1;
+        anc = 1ull << me;
+#pragma unroll
+        for (int r = 0; r < 6; ++r) {
+            const int src = up >= 0 ? up : 0;
+            const uint32_t lo = __shfl(static_cast<uint32_t>(anc), src),
+                           hi = __shfl(static_cast<uint32_t>(anc >> 32), src);
+            const int upup = __shfl(up, src);
+            if (up >= 0) {
+                anc |= static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
+                up = upup;
+            }
+        }
+    }
+    // Accepted: every node on the root path passed.  The stop node is the
+    // deepest accepted node, the lowest index among equals.
+    const bool accepted = lane < N && (anc & ~okm) == 0ull;
+    const int depth = __popcll(anc) - 1;
+    // deepest accepted node, lowest index among equals: one integer max
+    int key = accepted ? (depth << 6) | (63 - lane) : -1, unused = 0;
+    wave_min_max_i(unused, key);
+    const int v = 63 - (key & 63);
+    const int dv = key >> 6;
+    const uint32_t vlo = __shfl(static_cast<uint32_t>(anc), v), vhi = __shfl(static_cast<uint32_t>(anc >> 32), v);
+    const uint64_t anc_v = static_cast<uint64_t>(vlo) | (static_cast<uint64_t>(vhi) << 32);
+    if (lane < N && ((anc_v >> lane) & 1ull)) L.path[depth] = lane;
+    const uint64_t kids = __ballot(lane >= 1 && lane < N && pi == v);
+    const bool v_has = kids != 0ull;
+    const float uv = __shfl(usi, v);  // the stop node's sample uniform, loaded with the node inputs
+    if (lane == 0) {
+        Decision d;
+        d.v = v;
+        d.c = v_has ? __ffsll(static_cast<long long>(kids)) - 1 : -1;
+        d.a = dv;
+        d.u = uv;
+        d.M = v_has || FILT ? L.M[v] : 0.f;
+        d.S = v_has || FILT ? L.S[v] : 0.0;
+        d.tau = FILT ? L.tau[v] : 0u;
+        if (a.rule == 1 || !(T > 0.0))
+            d.mode = v_has ? MODE_DONE : MODE_ARGMAX;
+        else
+            d.mode = v_has ? MODE_RESID : MODE_BONUS;
+        L.dec = d;
+    }
+}
+
+// path, accepted tokens (and the last token when the decision fixes it)
+// and accept_len of request b, by threads 0..N-1.
+__device__ __forceinline__ void write_decision(const AcceptArgs& a, int b, const Decision& d, const DecLds& L) {
+    const int tid = threadIdx.x, N = a.N;
+    if (tid < N) {
+        const size_t o = static_cast<size_t>(b) * N + tid;
+        a.path[o] = tid <= d.a ? L.path[tid] : -1;
+        int tok = tid < d.a ? L.tok[L.path[tid + 1]] : -1;  // from LDS: no dependent load after the decision
+        if (tid == d.a && d.mode == MODE_DONE) tok = L.arg[d.v];
+        a.out_tokens[o] = tok;
+    }
+    if (tid == 0) a.accept_len[b] = d.a;
+}
+
 template <int RPW, bool FILT = false>  // node rows per wave (N <= 4 * RPW)
 __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, bool writer) {
     const int N = a.N, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    __shared__ float s_M[kMaxNodes];
-    __shared__ int s_arg[kMaxNodes];
-    __shared__ double s_S[kMaxNodes], s_H[kMaxNodes];
-    __shared__ int s_path[kMaxNodes];
-    __shared__ uint32_t s_tau[kMaxNodes];
-    __shared__ Decision s_dec;
-    __shared__ int s_tok[kMaxNodes];  // the drafted tokens, for the writer's accepted-token list
+    __shared__ DecLds L;
+    float* s_M = L.M;
+    int* s_arg = L.arg;
+    double* s_S = L.S;
+    double* s_H = L.H;
+    uint32_t* s_tau = L.tau;
 
     // The node's parent entry, token and uniform: three independent loads
     // with no branch between them (a chain's absent parent array and an
@@ -487,7 +602,7 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
     // under a branch would pull the uses into the branch, ahead of the chunk
     // records' loads.
     int praw, xraw;
-    float uraw;
+    float uraw, usraw;
     {
         const size_t o = static_cast<size_t>(b) * N + min(lane, N - 1);
         const int32_t* psrc = a.parent ? a.parent : a.tokens;
@@ -495,6 +610,7 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
         praw = psrc[o];
         xraw = a.tokens[o];
         uraw = usrc[o];
+        usraw = a.u_smp ? a.u_smp[o] : 0.f;
     }
     int pi = -1, xi = 0;
     float ui = 0.f;
@@ -602,103 +718,25 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
         }
     }
     }  // row statistics
-    const double gl = glf;
-    if (wave == 0 && lane < N) s_tok[lane] = xraw;
+    if (wave == 0 && lane < N) L.tok[lane] = xraw;
     __syncthreads();
-
-    if (wave == 0) {
-        // Node tests in fp64 from the gathered values.
-        bool ok = false;
-        if (lane >= 1 && lane < N && pi >= 0) {
-            double pu;
-            if (T > 0.0)
-                pu = FILT && logit_key(glf) < s_tau[pi] ? 0.0 : exp((gl - static_cast<double>(s_M[pi])) / T) / s_S[pi];
-            else
-                pu = xi == s_arg[pi] ? 1.0 : 0.0;
-            if (a.rule == 0) {
-                ok = static_cast<double>(ui) * gq < pu;
-            } else {
-                const double thr = fmin(static_cast<double>(a.eps), static_cast<double>(a.delta) * exp(-s_H[pi]));
-                ok = pu > thr;
-            }
-        }
-        const uint64_t okm = __ballot(ok) | 1ull;  // the root is always accepted
-        // Root paths by pointer doubling: after round k a lane holds its
-        // first 2^k path nodes and its 2^k-th ancestor.
-        const int me = lane < N ? lane : 0;
-        uint64_t anc;
-        if (!a.parent) {  // chain: nodes 0..me
-            anc = me == 63 ? ~0ull : (2ull << me) - 1ull;
-        } else {
-            int up = lane < N ? pi : -1;
-            anc = 1ull << me;
-#pragma unroll
-            for (int r = 0; r < 6; ++r) {
-                const int src = up >= 0 ? up : 0;
-                const uint32_t lo = __shfl(static_cast<uint32_t>(anc), src),
-                               hi = __shfl(static_cast<uint32_t>(anc >> 32), src);
-                const int upup = __shfl(up, src);
-                if (up >= 0) {
-                    anc |= static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
-                    up = upup;
-                }
-            }
-        }
-        // Accepted: every node on the root path passed.  The stop node is the
-        // deepest accepted node, the lowest index among equals.
-        const bool accepted = lane < N && (anc & ~okm) == 0ull;
-        const int depth = __popcll(anc) - 1;
-        // deepest accepted node, lowest index among equals: one integer max
-        int key = accepted ? (depth << 6) | (63 - lane) : -1, unused = 0;
-        wave_min_max_i(unused, key);
-        const int v = 63 - (key & 63);
-        const int dv = key >> 6;
-        const uint32_t vlo = __shfl(static_cast<uint32_t>(anc), v), vhi = __shfl(static_cast<uint32_t>(anc >> 32), v);
-        const uint64_t anc_v = static_cast<uint64_t>(vlo) | (static_cast<uint64_t>(vhi) << 32);
-        if (lane < N && ((anc_v >> lane) & 1ull)) s_path[depth] = lane;
-        const uint64_t kids = __ballot(lane >= 1 && lane < N && pi == v);
-        const bool v_has = kids != 0ull;
-        if (lane == 0) {
-            Decision d;
-            d.v = v;
-            d.c = v_has ? __ffsll(static_cast<long long>(kids)) - 1 : -1;
-            d.a = dv;
-            d.u = a.u_smp ? a.u_smp[static_cast<size_t>(b) * N + v] : 0.f;
-            d.M = v_has || FILT ? s_M[v] : 0.f;
-            d.S = v_has || FILT ? s_S[v] : 0.0;
-            d.tau = FILT ? s_tau[v] : 0u;
-            if (a.rule == 1 || !(T > 0.0))
-                d.mode = v_has ? MODE_DONE : MODE_ARGMAX;
-            else
-                d.mode = v_has ? MODE_RESID : MODE_BONUS;
-            s_dec = d;
-        }
-    }
+    if (wave == 0) decide_core<FILT>(a, b, pi, xi, ui, usraw, glf, gq, L);
     __syncthreads();
-    const Decision d = s_dec;
+    const Decision d = L.dec;
     if (writer) {
-        if (tid < N) {
-            const size_t o = static_cast<size_t>(b) * N + tid;
-            a.path[o] = tid <= d.a ? s_path[tid] : -1;
-            int tok = tid < d.a ? s_tok[s_path[tid + 1]] : -1;  // from LDS: no dependent load after the decision
-            if (tid == d.a && d.mode == MODE_DONE) tok = s_arg[d.v];
-            a.out_tokens[o] = tok;
-        }
-        if (tid == 0) {
-            a.accept_len[b] = d.a;
-            a.dec[b] = d;
-        }
+        write_decision(a, b, d, L);
+        if (tid == 0) a.dec[b] = d;
     }
     return d;
 }
 
-template <int EPT, int RPW, bool FILT = false>
-__global__ __launch_bounds__(kThreads) void accept_sample(AcceptArgs a) {
-    const int c = blockIdx.x, b = blockIdx.y;
-    __shared__ WaveRed s_red;
-    __shared__ double s_r2[8];
-    const Decision d = decide_request<RPW, FILT>(a, b, c == 0);
-    if (d.mode == MODE_DONE) return;
+// Chunk c of the stop row of request b, as decision d requires (valid in
+// thread 0): the residual mass sum max(0, p_v - q_c) and the plain mass
+// sum p_v (MODE_RESID), or the chunk max with its lowest index and
+// sum 2^((l - max) * log2(e) / T) (MODE_BONUS), or only the max (MODE_ARGMAX).
+template <int EPT, bool FILT = false>
+__device__ __forceinline__ ChunkStat chunk_work(const AcceptArgs& a, int b, const Decision& d, int c, WaveRed* s_red,
+                                                double* s_r2) {
     const float* row = a.logits + (static_cast<size_t>(b) * a.N + d.v) * a.V;
     const int x0 = c * a.chunk, x1 = min(x0 + a.chunk, a.V);
     ChunkStat cs;
@@ -732,11 +770,22 @@ __global__ __launch_bounds__(kThreads) void accept_sample(AcceptArgs a) {
         float M;
         int arg;
         double S, A2;
-        chunk_stats<EPT, FILT>(row, x0, x1, vec4, d.mode == MODE_BONUS ? a.T : 0.f, M, arg, S, A2, &s_red, d.tau);
+        chunk_stats<EPT, FILT>(row, x0, x1, vec4, d.mode == MODE_BONUS ? a.T : 0.f, M, arg, S, A2, s_red, d.tau);
         cs.M = M;
         cs.arg = arg;
         cs.m1 = S;
     }
+    return cs;
+}
+
+template <int EPT, int RPW, bool FILT = false>
+__global__ __launch_bounds__(kThreads) void accept_sample(AcceptArgs a) {
+    const int c = blockIdx.x, b = blockIdx.y;
+    __shared__ WaveRed s_red;
+    __shared__ double s_r2[8];
+    const Decision d = decide_request<RPW, FILT>(a, b, c == 0);
+    if (d.mode == MODE_DONE) return;
+    const ChunkStat cs = chunk_work<EPT, FILT>(a, b, d, c, &s_red, s_r2);
     if (threadIdx.x == 0) a.cstat[static_cast<size_t>(b) * a.nchunk + c] = cs;
 }
 
@@ -813,10 +862,10 @@ __device__ __forceinline__ void load_run2(const float* row, const float* qrow, i
 // weights (recomputed from the same fp32 terms accept_sample summed) locate
 // the token.  Zero-weight tokens are never drawn; if rounding leaves u*total
 // past the end, the last token with weight is taken.
-template <int EPT, bool FILT = false>
-__global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
+// load_cs(i) gives chunk record i of the request (i < a.nchunk).
+template <int EPT, bool FILT, class LoadCS>
+__device__ __forceinline__ void select_token(const AcceptArgs& a, int b, const Decision& d, LoadCS load_cs) {
     constexpr int CPT = kMaxChunks / kThreads;  // chunk records per thread
-    const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __shared__ float s_v[4];
     __shared__ int s_i[4];
@@ -826,12 +875,10 @@ __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
     __shared__ double s_base;
     __shared__ int s_mn[4], s_mx[4];
 
-    // The decision and this thread's run of chunk records, loaded together.
-    const Decision d = a.dec[b];
-    const ChunkStat* csb = a.cstat + static_cast<size_t>(b) * a.nchunk;
+    // This thread's run of chunk records.
     ChunkStat cs[CPT];
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) cs[k] = csb[min(tid * CPT + k, a.nchunk - 1)];  // clamped: no load under a branch
+    for (int k = 0; k < CPT; ++k) cs[k] = load_cs(min(tid * CPT + k, a.nchunk - 1));  // clamped: no load under a branch
 #pragma unroll
     for (int k = 0; k < CPT; ++k)
         if (tid * CPT + k >= a.nchunk) {
@@ -986,6 +1033,15 @@ __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
         if (final < 0) final = x0;
         *out = final;
     }
+}
+
+template <int EPT, bool FILT = false>
+__global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
+    const int b = blockIdx.x;
+    // The decision and the chunk records, loaded together.
+    const Decision d = a.dec[b];
+    const ChunkStat* csb = a.cstat + static_cast<size_t>(b) * a.nchunk;
+    select_token<EPT, FILT>(a, b, d, [&](int i) { return csb[i]; });
 }
 
 // ---------------------------------------------------------------------------
