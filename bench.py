@@ -470,6 +470,28 @@ def measure_extras(cfg, w, copies, acc_ws, timer, spg, dev):
     out["tree_rope"] = {"us": ms * 1e3, "bytes": rb, "achieved_GBs": rb / (ms * 1e-3) / 1e9,
                         "calls": ("spec_medusa_tree + " if cartesian else "") + "spec_tree_rope"}
 
+    # Depth-position RoPE fused into the attention (q and the tree's K rows
+    # turned as they are read) against the separate rotation pass followed by
+    # the plain attention.
+    mpl = int(w.prefix_len.max())
+    desc = sv.attn_desc(B, N, w.Hq, w.Hkv, w.D, copies[0]["k"].shape[2], copies[0]["q"].dtype)
+    rws = torch.empty(max(sv.spec_verify_attn_workspace_bytes(desc, mpl), 16), dtype=torch.uint8, device=dev)
+
+    def attn_fused(c):
+        sv.spec_verify_attn(c["q"], c["k"], c["v"], c["pl"], c["parent"], mpl, out=c["out"], workspace=rws,
+                            rope_base=rope_base)
+
+    def attn_unfused(c):
+        sv.spec_tree_rope(c["q"], c["k"], c["pl"], c["parent"], rope_base)
+        sv.spec_verify_attn(c["q"], c["k"], c["v"], c["pl"], c["parent"], mpl, out=c["out"], workspace=rws)
+
+    attn_fused(copies[0])
+    fused_ms = timer(capture(attn_fused))["median_ms"]
+    attn_unfused(copies[0])
+    unfused_ms = timer(capture(attn_unfused))["median_ms"]
+    out["rope_attention"] = {"fused_us": fused_ms * 1e3, "unfused_us": unfused_ms * 1e3,
+                             "calls": "spec_verify_attn with rope_base, against spec_tree_rope + spec_verify_attn"}
+
     if w.rule == "reject" and w.temperature > 0:
         fk, fp = 50, 0.9
 

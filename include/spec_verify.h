@@ -54,7 +54,20 @@ typedef enum spec_dtype { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
  * across workgroups; a positive value sets the least number of keys per KV
  * range (rounded up to whole 32-key blocks), for tuning and for tests that
  * need many short ranges.  It changes the work split and the workspace size,
- * not the result beyond rounding order.  Negative: SPEC_EINVAL. */
+ * not the result beyond rounding order.  Negative: SPEC_EINVAL.
+ * rope_base: 0 means q and the tree's K rows arrive already rotated.  A
+ * positive value fuses the depth-position rotary embedding (MEDUSA section,
+ * tree-attention paragraph: position indices follow tree depth) into
+ * spec_verify_attn and spec_commit_kv: q and the tree's K rows
+ * [L_b, L_b + N) are given unrotated, the prefix rows [0, L_b) rotated at
+ * their positions; the attention turns q of node i and the K row of node i
+ * by position L_b + depth(i) as it reads them (the cache is not written),
+ * and the commit writes the accepted K rows rotated at their new positions
+ * L_b + d, so that the grown prefix is rotated.  The rotation is the one
+ * spec_tree_rope applies (Llama rotate-half pairs (x_j, x_{j + D/2}) turned
+ * by pos * rope_base^(-2j/D)); angles in fp64 turns, sine and cosine and the
+ * products in fp32, rounded to the dtype.  V is never rotated.  Negative or
+ * not finite: SPEC_EINVAL. */
 typedef struct spec_attn_desc {
     int32_t batch;
     int32_t num_nodes;
@@ -65,6 +78,7 @@ typedef struct spec_attn_desc {
     int32_t dtype;       /* spec_dtype of q, the caches and out */
     float softmax_scale;
     int32_t kv_split_keys; /* 0: automatic */
+    float rope_base;       /* 0: inputs already rotated; > 0: fused depth-position RoPE */
 } spec_attn_desc;
 
 /* Workspace bytes spec_verify_attn needs for this shape and prefix bound
@@ -204,8 +218,11 @@ int spec_accept_typical(int32_t batch, int32_t num_nodes, int32_t vocab, const f
  * speculative-decoding loop prescribes): for every request b and kv head the
  * cache rows L_b + path[b][d], d = 0..accept_len[b], move to L_b + d, in
  * place (all sources are read before they can be overwritten), then
- * prefix_len[b] += accept_len[b] + 1.  For a chain nothing moves.  Uses the
- * desc fields batch, num_nodes, num_kv_heads, head_dim, kv_capacity, dtype. */
+ * prefix_len[b] += accept_len[b] + 1.  For a chain nothing moves.  With
+ * desc->rope_base > 0 the K rows of the accepted path are also rotated at
+ * their new positions L_b + d as they are written (every d, moved or not).
+ * Uses the desc fields batch, num_nodes, num_kv_heads, head_dim,
+ * kv_capacity, dtype and rope_base. */
 int spec_commit_kv(const spec_attn_desc* desc, void* k_cache, void* v_cache, int32_t* prefix_len,
                    const int32_t* path, const int32_t* accept_len, void* stream);
 

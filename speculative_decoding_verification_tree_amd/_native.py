@@ -52,6 +52,7 @@ class AttnDesc(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
         ("kv_split_keys", ctypes.c_int32),
+        ("rope_base", ctypes.c_float),
     ]
 
 

@@ -56,10 +56,10 @@ def _dtype_code(dt):
 
 
 def attn_desc(batch, num_nodes, num_q_heads, num_kv_heads, head_dim, kv_capacity, dtype, softmax_scale=0.0,
-              kv_split_keys=0):
+              kv_split_keys=0, rope_base=0.0):
     return AttnDesc(batch, num_nodes, num_q_heads, num_kv_heads, head_dim, kv_capacity,
                     _dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype), float(softmax_scale),
-                    int(kv_split_keys))
+                    int(kv_split_keys), float(rope_base))
 
 
 def spec_verify_attn_workspace_bytes(desc, max_prefix_len):
@@ -67,18 +67,19 @@ def spec_verify_attn_workspace_bytes(desc, max_prefix_len):
 
 
 def spec_verify_attn(q, k_cache, v_cache, prefix_len, parent, max_prefix_len, out=None, workspace=None,
-                     softmax_scale=0.0, stream=None, kv_split_keys=0):
+                     softmax_scale=0.0, stream=None, kv_split_keys=0, rope_base=0.0):
     """Tree-verify attention.  q [B][N][Hq][D]; caches [B][Hkv][cap][D] (same
     dtype, bf16 or fp32); prefix_len [B] int32; parent [B][N] int32 or None
     (chain); max_prefix_len: host int >= every prefix length; kv_split_keys:
-    least keys per KV range (0: automatic)."""
+    least keys per KV range (0: automatic); rope_base > 0: q and the tree's K
+    rows are rotated at their depth positions as they are read."""
     B, N, Hq, D = q.shape
     Hkv, cap = k_cache.shape[1], k_cache.shape[2]
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _dev(t, n, q.dtype)
     _dev(prefix_len, "prefix_len", torch.int32)
     _dev(parent, "parent", torch.int32)
-    desc = attn_desc(B, N, Hq, Hkv, D, cap, q.dtype, softmax_scale, kv_split_keys)
+    desc = attn_desc(B, N, Hq, Hkv, D, cap, q.dtype, softmax_scale, kv_split_keys, rope_base)
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out", q.dtype)
@@ -224,8 +225,10 @@ def spec_accept_typical(target_logits, tokens, parent, temperature, epsilon, del
     return accept_len, path, out_tokens
 
 
-def spec_commit_kv(k_cache, v_cache, prefix_len, path, accept_len, stream=None):
-    """In-place commit of the accepted path's KV rows; advances prefix_len."""
+def spec_commit_kv(k_cache, v_cache, prefix_len, path, accept_len, stream=None, rope_base=0.0):
+    """In-place commit of the accepted path's KV rows; advances prefix_len.
+    rope_base > 0: the accepted K rows are written rotated at their new
+    positions (the fused-RoPE attention's convention)."""
     B, Hkv, cap, D = k_cache.shape
     N = path.shape[1]
     _dev(k_cache, "k_cache")
@@ -233,7 +236,7 @@ def spec_commit_kv(k_cache, v_cache, prefix_len, path, accept_len, stream=None):
     _dev(prefix_len, "prefix_len", torch.int32)
     _dev(path, "path", torch.int32)
     _dev(accept_len, "accept_len", torch.int32)
-    desc = attn_desc(B, N, Hkv, Hkv, D, cap, k_cache.dtype)
+    desc = attn_desc(B, N, Hkv, Hkv, D, cap, k_cache.dtype, rope_base=rope_base)
     rc = _native.lib().spec_commit_kv(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(prefix_len),
                                       _ptr(path), _ptr(accept_len), _stream(stream))
     _check("spec_commit_kv", rc)

@@ -16,7 +16,8 @@ static bool desc_ok(const spec_attn_desc* d, int* err) {
     }
     if (d->batch < 0 || d->num_nodes < 1 || d->num_nodes > kMaxNodes || d->num_q_heads < 1 ||
         d->num_kv_heads < 1 || d->num_q_heads % d->num_kv_heads != 0 || d->kv_capacity < 1 || d->kv_split_keys < 0 ||
-        !(d->softmax_scale == d->softmax_scale) || isinf(d->softmax_scale)) {
+        !(d->softmax_scale == d->softmax_scale) || isinf(d->softmax_scale) || !(d->rope_base >= 0.f) ||
+        isinf(d->rope_base)) {
         *err = SPEC_EINVAL;
         return false;
     }

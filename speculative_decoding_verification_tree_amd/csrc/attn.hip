@@ -69,7 +69,50 @@ struct AttnArgs {
     int max_keys;      // host bound on L_b + N
     float scale_log2;  // softmax scale * log2(e)
     int bf16p;         // MFMA partials stored as bf16 (slabs of few partials, merged by attn_combine4)
+    int rope;          // fused depth-position rotary embedding of q and the tree's K rows
+    RopeTable rope_tab;
 };
+
+// The rotary table into LDS (threads 0 .. D/2 - 1): each takes its entry by
+// selects over the unrolled constant indices, so the kernel argument is never
+// indexed per lane.
+template <int D>
+__device__ __forceinline__ void rope_table_to_lds(const AttnArgs& a, double* s_rev) {
+    const int t = threadIdx.x;
+    if (t < D / 2) {
+        double v = 0.0;
+#pragma unroll
+        for (int j = 0; j < D / 2; ++j) v = t == j ? a.rope_tab.rev[j] : v;
+        s_rev[t] = v;
+    }
+}
+
+// Depth of every node of request b (lane i: node i) into LDS, from the
+// ancestor-or-self masks.
+__device__ __forceinline__ void depths_to_lds(const AttnArgs& a, uint64_t node_anc, int* s_depth) {
+    const int lane = threadIdx.x & 63;
+    if (lane < a.N) s_depth[lane] = __popcll(node_anc) - 1;
+}
+
+// q fragments of RT row tiles rotated at their rows' positions L + depth
+// (anc[t]: the lane's row's ancestor mask; rows past R hold zeros).
+template <int D, int RT>
+__device__ __forceinline__ void rope_q_frags(bf16x8 (&qf)[RT][D / 32], const uint64_t (&anc)[RT], int L,
+                                             const double* s_rev) {
+    constexpr int H = D / 64;  // k-chunks holding the low half of the dims
+    const int q4 = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        const int pos = L + __popcll(anc[t]) - 1;
+#pragma unroll
+        for (int c = 0; c < H; ++c) {
+            u32x4 lo = __builtin_bit_cast(u32x4, qf[t][c]), hi = __builtin_bit_cast(u32x4, qf[t][c + H]);
+            rope_bf16x8(lo, hi, pos, s_rev, 32 * c + 8 * q4);
+            qf[t][c] = __builtin_bit_cast(bf16x8, lo);
+            qf[t][c + H] = __builtin_bit_cast(bf16x8, hi);
+        }
+    }
+}
 
 // Largest batch the balanced mode serves (its block-count scan lives in LDS).
 constexpr int kMaxBalancedBatch = 480;
@@ -494,7 +537,7 @@ __device__ __forceinline__ void write_rows(const AttnArgs& a, const Seg& cur, in
     }
 }
 
-template <int D, int RT>
+template <int D, int RT, bool ROPE>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(RT <= 2 ? 2 : 1))) void attn_mfma(AttnArgs a) {
     constexpr int NC32 = D / 32;  // k-steps of the QK product
     constexpr int NC16 = D / 16;  // n-tiles of the PV product
@@ -505,12 +548,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(RT <= 2 ? 2 
     __shared__ __attribute__((aligned(16))) unsigned char s_stage[KS_BYTES + VT_BYTES];
     __shared__ int s_cum[kMaxBalancedBatch + 1];
     __shared__ int s_len[kMaxBalancedBatch];
+    __shared__ double s_rev[kRopeMaxPairs];
+    __shared__ int s_depth[kMaxNodes];
 
     int unit, rg;
     decode_unit(a, unit, rg);
     const int lane = threadIdx.x;
     const int n16 = lane & 15, q4 = lane >> 4;
     const int vch = lane % CPR, vkg = lane / CPR;
+    if constexpr (ROPE) rope_table_to_lds<D>(a, s_rev);
     unsigned char* ks = s_stage;
     unsigned char* vt = s_stage + KS_BYTES;
     const uint16_t* kc = static_cast<const uint16_t*>(a.k);
@@ -540,7 +586,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(RT <= 2 ? 2 
 
         bf16x8 qf[RT][NC32];
         uint64_t anc[RT];
-        load_q<D, RT>(a, b, g, rg * RT * 16, anc_mask(a, b), qf, anc);
+        {
+            const uint64_t node_anc = anc_mask(a, b);
+            load_q<D, RT>(a, b, g, rg * RT * 16, node_anc, qf, anc);
+            if constexpr (ROPE) {
+                depths_to_lds(a, node_anc, s_depth);
+                rope_q_frags<D, RT>(qf, anc, L, s_rev);
+            }
+        }
         float m_run[RT], l_run[RT];
         f32x4 o[RT][NC16];
 #pragma unroll
@@ -583,6 +636,29 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(RT <= 2 ? 2 
                     wv.x = __builtin_amdgcn_perm(R.vr[1][t >> 1], R.vr[0][t >> 1], sel);
                     wv.y = __builtin_amdgcn_perm(R.vr[3][t >> 1], R.vr[2][t >> 1], sel);
                     *reinterpret_cast<uint2*>(dst) = wv;
+                }
+            }
+            // Tree keys of a fused-RoPE call: each lane turns the K rows of
+            // its own staged fragments that are tree nodes, at L + depth
+            // (the block's registers are free here, about to take the next
+            // block's loads).
+            if (ROPE && kb + 32 > L) {  // wave-uniform
+                wave_lds_sync();
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int n = kb + 8 * (n16 >> 2) + 4 * h + (n16 & 3) - L;
+                    if (n >= 0 && n < a.N) {
+                        const int pos = L + s_depth[n];
+#pragma unroll
+                        for (int c = 0; c < NC32 / 2; ++c) {
+                            u32x4* lo = reinterpret_cast<u32x4*>(ks + ((h * NC32 + c) * 64 + lane) * 16);
+                            u32x4* hi = reinterpret_cast<u32x4*>(ks + ((h * NC32 + c + NC32 / 2) * 64 + lane) * 16);
+                            u32x4 x = *lo, y = *hi;
+                            rope_bf16x8(x, y, pos, s_rev, 32 * c + 8 * q4);
+                            *lo = x;
+                            *hi = y;
+                        }
+                    }
                 }
             }
             // The registers are free: load the next block -- this segment's,
@@ -745,7 +821,7 @@ __device__ __forceinline__ void stage_shared_kv(const SharedKV<D, WK>& s, unsign
     }
 }
 
-template <int D, int RT, int WK>
+template <int D, int RT, int WK, bool ROPE>
 __global__ __launch_bounds__(64 * WK) __attribute__((amdgpu_waves_per_eu(2))) void attn_mfma_wg(AttnArgs a) {
     constexpr int NC32 = D / 32, NC16 = D / 16, CPR = D / 8;
     constexpr int KS_BYTES = 32 * D * 2;  // K of one block, row-major
@@ -754,6 +830,8 @@ __global__ __launch_bounds__(64 * WK) __attribute__((amdgpu_waves_per_eu(2))) vo
     __shared__ __attribute__((aligned(16))) unsigned char s_stage[2 * STAGE];
     __shared__ int s_cum[kMaxBalancedBatch + 1];
     __shared__ int s_len[kMaxBalancedBatch];
+    __shared__ double s_rev[kRopeMaxPairs];
+    __shared__ int s_depth[kMaxNodes];
 
     int unit, rg;
     decode_unit(a, unit, rg);
@@ -762,6 +840,7 @@ __global__ __launch_bounds__(64 * WK) __attribute__((amdgpu_waves_per_eu(2))) vo
     const uint16_t* kc = static_cast<const uint16_t*>(a.k);
     const uint16_t* vc = static_cast<const uint16_t*>(a.v);
     const int row0 = (rg * WK + wave) * RT * 16;
+    if constexpr (ROPE) rope_table_to_lds<D>(a, s_rev);
 
     if (wave == 0) (void)begin_segments(a, unit, s_cum, s_len, true);
     __syncthreads();
@@ -803,7 +882,14 @@ __global__ __launch_bounds__(64 * WK) __attribute__((amdgpu_waves_per_eu(2))) vo
         const int L = cur.L, Tk = L + a.N;
         bf16x8 qf[RT][NC32];
         uint64_t anc[RT];
-        load_q<D, RT>(a, b, g, row0, anc_mask(a, b), qf, anc);
+        {
+            const uint64_t node_anc = anc_mask(a, b);
+            load_q<D, RT>(a, b, g, row0, node_anc, qf, anc);
+            if constexpr (ROPE) {
+                depths_to_lds(a, node_anc, s_depth);  // every wave writes the same values
+                rope_q_frags<D, RT>(qf, anc, L, s_rev);
+            }
+        }
         // Wait for the queries here, once per segment: left pending into the
         // block loop, the wait at the loop head would also cover the KV
         // prefetch issued after them (loads retire in order) on every block.
@@ -825,6 +911,26 @@ __global__ __launch_bounds__(64 * WK) __attribute__((amdgpu_waves_per_eu(2))) vo
         for (int xb = cur.blk0; xb < cur.blk1; ++xb) {
             const unsigned char* ks = s_stage + bi * STAGE;
             const unsigned char* vt = ks + KS_BYTES;
+            if (ROPE && xb * 32 + 32 > L) {  // workgroup-uniform: a block holding tree keys
+                // Turn the staged K rows of tree nodes at L + depth: one
+                // thread per (row, pair of 16-byte chunks D/2 apart).
+                __syncthreads();  // the depths of this segment are in LDS
+                unsigned char* kw = s_stage + bi * STAGE;
+                for (int task = tid; task < 32 * (CPR / 2); task += 64 * WK) {
+                    const int row = task / (CPR / 2), col = task % (CPR / 2);
+                    const int n = xb * 32 + row - L;
+                    if (n >= 0 && n < a.N) {
+                        u32x4* lo = reinterpret_cast<u32x4*>(kw + row * (2 * D) + ((col ^ k_swz(row)) & (CPR - 1)) * 16);
+                        u32x4* hi = reinterpret_cast<u32x4*>(kw + row * (2 * D) +
+                                                             (((col + CPR / 2) ^ k_swz(row)) & (CPR - 1)) * 16);
+                        u32x4 x = *lo, y = *hi;
+                        rope_bf16x8(x, y, L + s_depth[n], s_rev, 8 * col);
+                        *lo = x;
+                        *hi = y;
+                    }
+                }
+                __syncthreads();
+            }
             auto kread = [&](int h, int c) {
                 const int row = 8 * (n16 >> 2) + 4 * h + (n16 & 3);
                 return *reinterpret_cast<const u32x4*>(ks + row * (2 * D) + (((4 * c + q4) ^ k_swz(row)) & (CPR - 1)) * 16);
@@ -870,6 +976,7 @@ __global__ __launch_bounds__(256) void attn_valu(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) float s_v[32][DP];
     __shared__ __attribute__((aligned(16))) float s_p[32][36];
     __shared__ uint64_t s_anc[kMaxNodes];
+    __shared__ double s_rev[kRopeMaxPairs];
 
     int unit, rg;
     decode_unit(a, unit, rg);
@@ -890,6 +997,27 @@ __global__ __launch_bounds__(256) void attn_valu(AttnArgs a) {
         const uint64_t m = anc_mask(a, b);
         if (tid < a.N) s_anc[tid] = m;
     }
+    if (a.rope) rope_table_to_lds<D>(a, s_rev);
+    // Fused RoPE: rows of the LDS tile rot[0..32) turn at L + depth(node),
+    // node(r) giving each row's node (or -1: left as is).
+    auto rope_rows = [&](float (*rot)[DP], auto node_of) {
+        for (int task = tid; task < 32 * (D / 2); task += 256) {
+            const int row = task / (D / 2), j = task % (D / 2);
+            const int n = node_of(row);
+            if (n >= 0) {
+                float c, sn;
+                rope_cs(L + __popcll(s_anc[n]) - 1, s_rev[j], c, sn);
+                float x = rot[row][j], y = rot[row][j + D / 2];
+                rope_pair(x, y, c, sn);
+                if constexpr (sizeof(T) == 2) {  // bf16 tensors: the rotated value rounded as the MFMA paths do
+                    x = bf16_bits_to_f32(static_cast<uint16_t>(f32_to_bf16_bits(x)));
+                    y = bf16_bits_to_f32(static_cast<uint16_t>(f32_to_bf16_bits(y)));
+                }
+                rot[row][j] = x;
+                rot[row][j + D / 2] = y;
+            }
+        }
+    };
     const T* qp = static_cast<const T*>(a.q);
     if constexpr (sizeof(T) == 4) {
         // fp32: 16-byte loads, all of a thread's issued before its LDS stores
@@ -920,6 +1048,10 @@ __global__ __launch_bounds__(256) void attn_valu(AttnArgs a) {
         }
     }
     __syncthreads();
+    if (a.rope) {
+        rope_rows(s_q, [&](int lr) { return rg * 32 + lr < a.R ? (rg * 32 + lr) / a.G : -1; });
+        __syncthreads();
+    }
 
     // Thread (sr, sk): query row sr of the tile, keys sk + 8*jj of each
     // 32-key tile, output dims sk*DPL .. sk*DPL + DPL - 1.
@@ -963,6 +1095,13 @@ __global__ __launch_bounds__(256) void attn_valu(AttnArgs a) {
             }
         }
         __syncthreads();
+        if (a.rope && kb + 32 > L) {  // a tile holding tree keys
+            rope_rows(s_k, [&](int kk) {
+                const int n = kb + kk - L;
+                return n >= 0 && n < a.N ? n : -1;
+            });
+            __syncthreads();
+        }
         // Scores of keys sk + 8*jj: 16-byte LDS reads, the query row's
         // (a broadcast within the row's eight lanes) shared by the four keys.
         float dot[4] = {0.f, 0.f, 0.f, 0.f};
@@ -1304,43 +1443,57 @@ static int device_cus() {
     return cus[dev];
 }
 
-template <int D, int RT>
+template <int D, int RT, bool ROPE>
 static int mfma_resident() {
     static int n = 0;
-    if (n == 0) n = resident_per_cu(attn_mfma<D, RT>, 64);
+    if (n == 0) n = resident_per_cu(attn_mfma<D, RT, ROPE>, 64);
     return n;
 }
 
-template <int D>
+template <int D, bool ROPE>
 static int mfma_wg_resident() {
     static int n = 0;
-    if (n == 0) n = resident_per_cu(attn_mfma_wg<D, 2, wg_waves<D>()>, 64 * wg_waves<D>());
+    if (n == 0) n = resident_per_cu(attn_mfma_wg<D, 2, wg_waves<D>(), ROPE>, 64 * wg_waves<D>());
     return n;
 }
 
-template <int D>
+template <int D, bool ROPE>
 static int mfma_resident_rt(int rt, int waves) {
-    if (waves > 1) return mfma_wg_resident<D>();
+    if (waves > 1) return mfma_wg_resident<D, ROPE>();
     switch (rt) {
-        case 1: return mfma_resident<D, 1>();
-        case 2: return mfma_resident<D, 2>();
-        case 3: return mfma_resident<D, 3>();
-        default: return mfma_resident<D, 4>();
+        case 1: return mfma_resident<D, 1, ROPE>();
+        case 2: return mfma_resident<D, 2, ROPE>();
+        case 3: return mfma_resident<D, 3, ROPE>();
+        default: return mfma_resident<D, 4, ROPE>();
+    }
+}
+
+template <int D>
+static int mfma_resident_rt(int rt, int waves, bool rope) {
+    return rope ? mfma_resident_rt<D, true>(rt, waves) : mfma_resident_rt<D, false>(rt, waves);
+}
+
+// The rotating kernels are separate instantiations: the plain ones keep
+// their register allocation (the rotation code in the block loop costs the
+// one-wave kernel a spill).
+template <int D, bool ROPE>
+static void launch_mfma_rt(const AttnPlan& p, const AttnArgs& a, dim3 grid, hipStream_t st) {
+    if (p.waves > 1) {
+        hipLaunchKernelGGL((attn_mfma_wg<D, 2, wg_waves<D>(), ROPE>), grid, dim3(64 * wg_waves<D>()), 0, st, a);
+        return;
+    }
+    switch (p.row_tiles) {
+        case 1: hipLaunchKernelGGL((attn_mfma<D, 1, ROPE>), grid, dim3(64), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((attn_mfma<D, 2, ROPE>), grid, dim3(64), 0, st, a); break;
+        case 3: hipLaunchKernelGGL((attn_mfma<D, 3, ROPE>), grid, dim3(64), 0, st, a); break;
+        default: hipLaunchKernelGGL((attn_mfma<D, 4, ROPE>), grid, dim3(64), 0, st, a); break;
     }
 }
 
 template <int D>
 static void launch_mfma_rt(const AttnPlan& p, const AttnArgs& a, dim3 grid, hipStream_t st) {
-    if (p.waves > 1) {
-        hipLaunchKernelGGL((attn_mfma_wg<D, 2, wg_waves<D>()>), grid, dim3(64 * wg_waves<D>()), 0, st, a);
-        return;
-    }
-    switch (p.row_tiles) {
-        case 1: hipLaunchKernelGGL((attn_mfma<D, 1>), grid, dim3(64), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((attn_mfma<D, 2>), grid, dim3(64), 0, st, a); break;
-        case 3: hipLaunchKernelGGL((attn_mfma<D, 3>), grid, dim3(64), 0, st, a); break;
-        default: hipLaunchKernelGGL((attn_mfma<D, 4>), grid, dim3(64), 0, st, a); break;
-    }
+    if (a.rope) launch_mfma_rt<D, true>(p, a, grid, st);
+    else launch_mfma_rt<D, false>(p, a, grid, st);
 }
 
 int launch_verify_attn(const spec_attn_desc& d, const AttnPlan& p, const void* q, const void* k,
@@ -1366,12 +1519,15 @@ int launch_verify_attn(const spec_attn_desc& d, const AttnPlan& p, const void* q
     a.max_keys = p.max_keys;
     const float scale = d.softmax_scale > 0.f ? d.softmax_scale : 1.0f / sqrtf(static_cast<float>(d.head_dim));
     a.scale_log2 = scale * 1.4426950408889634f;
+    a.rope = d.rope_base > 0.f ? 1 : 0;
+    fill_rope_table(a.rope_tab, d.head_dim, a.rope ? d.rope_base : 1.f);
     const long slabs = static_cast<long>(d.batch) * d.num_kv_heads;
     long units;
     bool combine;
     if (p.balanced) {
-        const int per_cu = d.head_dim == 128 ? mfma_resident_rt<128>(p.row_tiles, p.waves)
-                                             : mfma_resident_rt<64>(p.row_tiles, p.waves);
+        const bool rope = d.rope_base > 0.f;
+        const int per_cu = d.head_dim == 128 ? mfma_resident_rt<128>(p.row_tiles, p.waves, rope)
+                                             : mfma_resident_rt<64>(p.row_tiles, p.waves, rope);
         long P = static_cast<long>(per_cu) * device_cus() / p.row_groups;
         if (P > p.parts_max) P = p.parts_max;
         if (P >= 8) P = P / 8 * 8;

@@ -151,6 +151,61 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
     }
 }
 
+// ---- rotary embedding at depth positions -----------------------------------
+// The pair (x_j, x_{j + D/2}) of a row at position pos turns by
+// pos * base^(-2j/D) radians.  rev[j] = base^(-2j/D) / (2 pi), fp64 from the
+// host: the angle in turns is frac(pos * rev[j]) in fp64, and the sine and
+// cosine come from the hardware's fp32 sine and cosine of a fraction of a
+// turn; the products are fp32.
+constexpr int kRopeMaxPairs = 64;  // D / 2 for D <= 128
+struct RopeTable {
+    double rev[kRopeMaxPairs];
+};
+
+__device__ __forceinline__ void rope_cs(int pos, double rev, float& c, float& s) {
+    double t = static_cast<double>(pos) * rev;
+    t -= floor(t);
+    const float f = static_cast<float>(t);
+    s = __builtin_amdgcn_sinf(f);
+    c = __builtin_amdgcn_cosf(f);
+}
+
+__device__ __forceinline__ void rope_pair(float& x, float& y, float c, float s) {
+    const float xr = x * c - y * s, yr = x * s + y * c;
+    x = xr;
+    y = yr;
+}
+
+// Eight bf16 pairs: lo holds dims j0 .. j0 + 7 of a row, hi the dims D/2
+// further; rev points at the table (LDS).  Rounded back to bf16 (nearest even).
+__device__ __forceinline__ void rope_bf16x8(u32x4& lo, u32x4& hi, int pos, const double* rev, int j0) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        float x0 = __uint_as_float(lo[w] << 16), x1 = __uint_as_float(lo[w] & 0xFFFF0000u);
+        float y0 = __uint_as_float(hi[w] << 16), y1 = __uint_as_float(hi[w] & 0xFFFF0000u);
+        float c, s;
+        rope_cs(pos, rev[j0 + 2 * w], c, s);
+        rope_pair(x0, y0, c, s);
+        rope_cs(pos, rev[j0 + 2 * w + 1], c, s);
+        rope_pair(x1, y1, c, s);
+        lo[w] = pack_bf16x2(x0, x1);
+        hi[w] = pack_bf16x2(y0, y1);
+    }
+}
+
+// Four fp32 pairs (dims j0 .. j0 + 3 and D/2 further).
+__device__ __forceinline__ void rope_f32x4(u32x4& lo, u32x4& hi, int pos, const double* rev, int j0) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        float x = __uint_as_float(lo[w]), y = __uint_as_float(hi[w]);
+        float c, s;
+        rope_cs(pos, rev[j0 + w], c, s);
+        rope_pair(x, y, c, s);
+        lo[w] = __float_as_uint(x);
+        hi[w] = __float_as_uint(y);
+    }
+}
+
 // Wait for this wave's LDS traffic and stop the compiler from moving memory
 // operations across; sufficient for LDS exchange inside one wavefront.
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }

@@ -2,10 +2,12 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 
 #include "../../include/spec_verify.h"
+#include "spec_common.h"
 
 namespace specv {
 
@@ -85,6 +87,13 @@ struct TreeRopeArgs {
 int launch_tree_rope(const TreeRopeArgs& a, int B, bool bf16, hipStream_t stream);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// rev[j] = base^(-2j/D) / (2 pi), j < D/2: turns per position of rotary pair j.
+inline void fill_rope_table(RopeTable& t, int D, float base) {
+    const double two_pi = 6.283185307179586476925286766559;
+    for (int j = 0; j < kRopeMaxPairs; ++j)
+        t.rev[j] = j < D / 2 ? pow(static_cast<double>(base), -2.0 * j / D) / two_pi : 0.0;
+}
 
 // Linear-attention verification / commit (one launch, either or both phases).
 struct LaArgs {

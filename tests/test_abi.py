@@ -34,12 +34,12 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_struct_layout_matches_header():
-    assert ctypes.sizeof(AttnDesc) == 36
+    assert ctypes.sizeof(AttnDesc) == 40
 
 
 def _desc(**kw):
     d = dict(batch=1, num_nodes=6, num_q_heads=32, num_kv_heads=8, head_dim=128, kv_capacity=2054, dtype=1,
-             softmax_scale=0.0, kv_split_keys=0)
+             softmax_scale=0.0, kv_split_keys=0, rope_base=0.0)
     d.update(kw)
     return AttnDesc(**d)
 
@@ -61,6 +61,9 @@ def _attn(desc, mpl=2048, ws_bytes=1 << 30, ws=FAKE):
     (dict(batch=-1), EINVAL),
     (dict(softmax_scale=float("nan")), EINVAL),
     (dict(kv_split_keys=-1), EINVAL),
+    (dict(rope_base=-1.0), EINVAL),
+    (dict(rope_base=float("nan")), EINVAL),
+    (dict(rope_base=float("inf")), EINVAL),
 ])
 def test_attention_argument_errors(kw, want):
     assert _attn(_desc(**kw)) == want

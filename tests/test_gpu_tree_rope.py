@@ -120,3 +120,92 @@ def test_tree_then_rope_then_attention():
     out = sv.spec_verify_attn(qd, kd, vd, pl, par, int(L.max()))
     torch.cuda.synchronize()
     check_attention(host_f64(out), ref, "tree -> rope -> attention")
+
+
+def _fused_case(dtype, D, B, N, Hq, Hkv, L, tree, seed):
+    q, k, Lp, parent, base = _rope_case(dtype, D, B, N, Hq, Hkv, L, tree, seed, base=500000.0)
+    rng = np.random.default_rng(seed + 1)
+    v = rng.standard_normal(k.shape).astype(np.float32)
+    if dtype == "bf16":
+        v = bf16_bits(v)
+    return q, k, v, Lp, parent, base
+
+
+def _rounded(x, dtype):
+    return bf16_bits(x.astype(np.float32)) if dtype == "bf16" else x.astype(np.float32)
+
+
+@pytest.mark.parametrize("dtype,D,B,N,Hq,Hkv,L,tree", [
+    ("bf16", 128, 2, 6, 32, 8, [2048, 31], False),          # Llama-3-8B chain: one-wave kernel, R = 24
+    ("bf16", 128, 3, 46, 32, 32, [0, 700, 4096], True),     # Medusa-shaped tree, MHA: R = 46
+    ("bf16", 128, 2, 64, 64, 8, [3000, 1000], True),        # 64-node tree, R = 512: shared-KV kernel
+    ("bf16", 128, 5, 8, 32, 8, [512, 8000, 77, 1, 4000], False),  # ragged chains
+    ("bf16", 64, 2, 20, 8, 2, [5, 129], True),              # D = 64
+    ("bf16", 64, 2, 40, 16, 4, [300, 90], True),            # D = 64, R = 160: shared-KV kernel
+    ("f32", 128, 2, 9, 4, 4, [77, 0], True),                # fp32 VALU kernel
+    ("f32", 64, 1, 5, 4, 1, [128], False),
+])
+def test_fused_rope_attention_matches_oracle(dtype, D, B, N, Hq, Hkv, L, tree):
+    """spec_verify_attn with rope_base > 0 against the oracle's depth-position
+    rotation (rounded to the dtype) followed by its tree attention; q and the
+    cache are read, not written."""
+    announce(f"fused rope attention {dtype} D={D} B={B} N={N} Hq={Hq} Hkv={Hkv} L={L} tree={tree}")
+    q, k, v, Lp, parent, base = _fused_case(dtype, D, B, N, Hq, Hkv, L, tree, seed=3 * D + N + B)
+    rq, rk = oracle.tree_rope(q, k, Lp, parent, dtype, base)
+    q_rot = _rounded(rq, dtype)
+    k_rot = k.copy()
+    for b in range(B):
+        k_rot[b, :, Lp[b]:Lp[b] + N] = _rounded(rk[b], dtype)
+    ref = oracle.tree_attn(q_rot, k_rot, v, Lp, parent, dtype)
+    qd, kd, vd = dev_kv(q, dtype), dev_kv(k, dtype), dev_kv(v, dtype)
+    q0, k0 = qd.clone(), kd.clone()
+    out = sv.spec_verify_attn(qd, kd, vd, torch.from_numpy(Lp).cuda(),
+                              None if parent is None else torch.from_numpy(parent).cuda(), int(Lp.max()),
+                              rope_base=base)
+    torch.cuda.synchronize()
+    check_attention(host_f64(out), ref, f"fused rope {dtype} D={D}")
+    assert torch.equal(qd, q0) and torch.equal(kd, k0), "the fused call must not write q or the cache"
+
+
+@pytest.mark.parametrize("dtype,D,tree", [("bf16", 128, False), ("bf16", 128, True), ("bf16", 64, True),
+                                          ("f32", 128, True)])
+def test_fused_rope_commit_matches_oracle(dtype, D, tree):
+    """spec_commit_kv with rope_base > 0: the accepted K rows land rotated at
+    their new positions (the oracle: rotate the tree rows at their depth
+    positions, then commit); V rows move unchanged; the prefix is untouched."""
+    B, N, Hkv = 4, 12, 2
+    L = [40, 0, 333, 7]
+    announce(f"fused rope commit {dtype} D={D} tree={tree}")
+    q, k, v, Lp, parent, base = _fused_case(dtype, D, B, N, 4, Hkv, L, tree, seed=D + 17 * tree)
+    par = parent if parent is not None else np.tile(np.arange(-1, N - 1, dtype=np.int32), (B, 1))
+    rng = np.random.default_rng(5)
+    path = np.full((B, N), -1, np.int32)
+    acc = np.zeros(B, np.int32)
+    for b in range(B):  # a random root path of each tree
+        node, p = 0, [0]
+        while True:
+            kids = [i for i in range(N) if par[b, i] == node]
+            if not kids or rng.random() < 0.15:
+                break
+            node = kids[int(rng.integers(len(kids)))]
+            p.append(node)
+        path[b, :len(p)] = p
+        acc[b] = len(p) - 1
+    _, rk = oracle.tree_rope(q, k, Lp, parent, dtype, base)
+    k_ref, v_ref = k.copy(), v.copy()
+    for b in range(B):
+        k_ref[b, :, Lp[b]:Lp[b] + N] = _rounded(rk[b], dtype)
+    pl_ref = oracle.commit(k_ref, v_ref, Lp.copy(), path, acc)
+    kd, vd = dev_kv(k, dtype), dev_kv(v, dtype)
+    pl = torch.from_numpy(Lp.copy()).cuda()
+    sv.spec_commit_kv(kd, vd, pl, torch.from_numpy(path).cuda(), torch.from_numpy(acc).cuda(), rope_base=base)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(pl.cpu().numpy(), pl_ref)
+    gk, gv = host_f64(kd), host_f64(vd)
+    rk_ref, rv_ref = host_f64(dev_kv(k_ref, dtype)), host_f64(dev_kv(v_ref, dtype))
+    rel = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -22
+    for b in range(B):
+        n = int(pl_ref[b])  # the grown prefix
+        err = np.abs(gk[b, :, :n] - rk_ref[b, :, :n])
+        assert (err <= rel * np.abs(rk_ref[b, :, :n]) + 1e-6).all(), f"K b={b}: max err {err.max():.3e}"
+        np.testing.assert_array_equal(gv[b, :, :n], rv_ref[b, :, :n])
