@@ -73,12 +73,12 @@ struct AttnArgs {
     RopeTable rope_tab;
 };
 
-// The rotary table into LDS (threads 0 .. D/2 - 1): each takes its entry by
-// selects over the unrolled constant indices, so the kernel argument is never
-// indexed per lane.
+// The rotary table into LDS (lanes 0 .. D/2 - 1 of every wave, which all
+// write the same values): each takes its entry by selects over the unrolled
+// constant indices, so the kernel argument is never indexed per lane.
 template <int D>
 __device__ __forceinline__ void rope_table_to_lds(const AttnArgs& a, double* s_rev) {
-    const int t = threadIdx.x;
+    const int t = threadIdx.x & 63;
     if (t < D / 2) {
         double v = 0.0;
 #pragma unroll
@@ -496,9 +496,12 @@ __device__ __forceinline__ void block_update(const KRead& kread, const unsigned 
 // registers: lane (n, q) holds row n of each tile (dims 16c + 4q .. +3 of O
 // and the row's running max and sum).  The normalised output when the
 // segment covers its slab, else the partial.
-template <int D, int RT, bool BF16P = true>  // BF16P = false: the caller never stores bf16 partials
+// NCW < D/16: o holds the column tiles c0 .. c0 + NCW - 1 only (a share of
+// a merged result); with_ml: this caller stores the rows' (max, sum).
+template <int D, int RT, bool BF16P = true, int NCW = D / 16>  // BF16P = false: the caller never stores bf16 partials
 __device__ __forceinline__ void write_rows(const AttnArgs& a, const Seg& cur, int row0, const float (&m_run)[RT],
-                                           const float (&l_run)[RT], const f32x4 (&o)[RT][D / 16]) {
+                                           const float (&l_run)[RT], const f32x4 (&o)[RT][NCW], int c0 = 0,
+                                           bool with_ml = true) {
     const int lane = threadIdx.x & 63, n16 = lane & 15, q4 = lane >> 4;
     float l_row[RT];  // the row sums: the four lanes' shares added
 #pragma unroll
@@ -513,63 +516,92 @@ __device__ __forceinline__ void write_rows(const AttnArgs& a, const Seg& cur, in
             uint16_t* orow =
                 static_cast<uint16_t*>(a.out) + ((static_cast<size_t>(cur.b) * a.N + node) * a.Hq + hq) * D;
 #pragma unroll
-            for (int c = 0; c < D / 16; ++c) {
+            for (int c = 0; c < NCW; ++c) {
                 uint2 pk;
                 pk.x = pack_bf16x2(o[t][c][0] * inv, o[t][c][1] * inv);
                 pk.y = pack_bf16x2(o[t][c][2] * inv, o[t][c][3] * inv);
-                *reinterpret_cast<uint2*>(orow + 16 * c + 4 * q4) = pk;
+                *reinterpret_cast<uint2*>(orow + 16 * (c0 + c) + 4 * q4) = pk;
             }
         } else {
             const size_t po = (static_cast<size_t>(cur.part) * a.R + r) * D;
             if (BF16P && a.bf16p) {  // half the bytes: the partials compete with the KV stream for HBM
                 uint16_t* prow = reinterpret_cast<uint16_t*>(a.ws_o) + po;
 #pragma unroll
-                for (int c = 0; c < D / 16; ++c)
-                    *reinterpret_cast<uint2*>(prow + 16 * c + 4 * q4) =
+                for (int c = 0; c < NCW; ++c)
+                    *reinterpret_cast<uint2*>(prow + 16 * (c0 + c) + 4 * q4) =
                         make_uint2(pack_bf16x2(o[t][c][0], o[t][c][1]), pack_bf16x2(o[t][c][2], o[t][c][3]));
             } else {
                 float* prow = a.ws_o + po;
 #pragma unroll
-                for (int c = 0; c < D / 16; ++c) *reinterpret_cast<f32x4*>(prow + 16 * c + 4 * q4) = o[t][c];
+                for (int c = 0; c < NCW; ++c) *reinterpret_cast<f32x4*>(prow + 16 * (c0 + c) + 4 * q4) = o[t][c];
             }
-            if (q4 == 0) a.ws_ml[static_cast<size_t>(cur.part) * a.R + r] = make_float2(m_run[t], l_row[t]);
+            if (with_ml && q4 == 0) a.ws_ml[static_cast<size_t>(cur.part) * a.R + r] = make_float2(m_run[t], l_row[t]);
         }
     }
 }
 
-template <int D, int RT, bool ROPE>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(RT <= 2 ? 2 : 1))) void attn_mfma(AttnArgs a) {
+// Blocks [f0, f1) of segment s taken by wave w of W: contiguous shares
+// (empty when the segment has fewer blocks than W).
+template <int W>
+__device__ __forceinline__ void wave_share(const Seg& s, int w, int& f0, int& f1) {
+    const int n = s.blk1 - s.blk0;
+    f0 = s.blk0 + (w * n) / W;
+    f1 = s.blk0 + ((w + 1) * n) / W;
+}
+
+// W = 1: one wavefront per workgroup streams its range.  W > 1 (small
+// problems, where one-wave ranges would be a couple of blocks each and the
+// partials would rival the KV bytes): W waves split every segment of the
+// range into contiguous shares, then merge their softmax states exactly in
+// LDS -- M = max of the waves' running maxima, O and the sums rescaled by
+// 2^(m_w - M) and added -- so the workgroup writes one partial per segment.
+template <int D, int RT, bool ROPE, int W = 1>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RT <= 2 ? 2 : 1))) void attn_mfma(AttnArgs a) {
     constexpr int NC32 = D / 32;  // k-steps of the QK product
     constexpr int NC16 = D / 16;  // n-tiles of the PV product
     constexpr int CPR = D / 8;    // 16-byte chunks per cache row
     constexpr int KPL = KVBlock<D>::KPL;  // keys per lane in the V load (8 or 4)
     constexpr int KS_BYTES = 2 * NC32 * 64 * 16;  // K fragments of one block, lane-major
     constexpr int VT_BYTES = D * 64;              // V^T of one block
-    __shared__ __attribute__((aligned(16))) unsigned char s_stage[KS_BYTES + VT_BYTES];
+    constexpr int STAGE = KS_BYTES + VT_BYTES;
+    // The merge's O of every wave reuses the stages; each wave stores whole column tiles.
+    static_assert(W == 1 || (W * RT * NC16 * 64 * 16 <= W * STAGE && NC16 % W == 0), "merge layout");
+    __shared__ __attribute__((aligned(16))) unsigned char s_stage[W * STAGE];
     __shared__ int s_cum[kMaxBalancedBatch + 1];
     __shared__ int s_len[kMaxBalancedBatch];
-    __shared__ double s_rev[kRopeMaxPairs];
-    __shared__ int s_depth[kMaxNodes];
+    __shared__ double s_rev[W][kRopeMaxPairs];
+    __shared__ int s_depth[W][kMaxNodes];
+    __shared__ float s_mw[W > 1 ? W * RT * 64 : 1];  // the waves' running maxima (merge)
+    __shared__ float s_lw[W > 1 ? W * RT * 64 : 1];  // their rescaled sums
 
     int unit, rg;
     decode_unit(a, unit, rg);
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63, wave = W > 1 ? uniform(static_cast<int>(threadIdx.x >> 6)) : 0;
     const int n16 = lane & 15, q4 = lane >> 4;
     const int vch = lane % CPR, vkg = lane / CPR;
-    if constexpr (ROPE) rope_table_to_lds<D>(a, s_rev);
-    unsigned char* ks = s_stage;
-    unsigned char* vt = s_stage + KS_BYTES;
+    if constexpr (ROPE) rope_table_to_lds<D>(a, s_rev[wave]);
+    unsigned char* ks = s_stage + wave * STAGE;
+    unsigned char* vt = ks + KS_BYTES;
     const uint16_t* kc = static_cast<const uint16_t*>(a.k);
     const uint16_t* vc = static_cast<const uint16_t*>(a.v);
 
-    SegIter it = begin_segments(a, unit, s_cum, s_len);
+    SegIter it;
+    if constexpr (W > 1) {  // one wave scans the request block counts for all
+        if (a.balanced && wave == 0) scan_request_blocks(a, s_cum, s_len);
+        __syncthreads();
+        it = begin_segments(a, unit, s_cum, s_len, false);
+    } else {
+        it = begin_segments(a, unit, s_cum, s_len);
+    }
     Seg cur;
-    if (!next_segment(a, it, s_cum, s_len, cur)) return;
+    if (!next_segment(a, it, s_cum, s_len, cur)) return;  // uniform over the workgroup
     int L = cur.L;
+    int my0, my1;  // this wave's blocks of the current segment
+    wave_share<W>(cur, wave, my0, my1);
     KVBlock<D> R;
     {
         const size_t head = (static_cast<size_t>(cur.b) * a.Hkv + cur.g) * a.cap * D;
-        load_kv_block<D>(R, kc + head, vc + head, cur.blk0 * 32, L + a.N - 1, n16, q4, vch, vkg);
+        load_kv_block<D>(R, kc + head, vc + head, (my0 < my1 ? my0 : cur.blk0) * 32, L + a.N - 1, n16, q4, vch, vkg);
     }
     auto kread = [&](int h, int c) { return *reinterpret_cast<const u32x4*>(ks + ((h * NC32 + c) * 64 + lane) * 16); };
     for (;;) {
@@ -578,11 +610,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(RT <= 2 ? 2 
         const size_t head = (static_cast<size_t>(b) * a.Hkv + g) * a.cap * D;
         const uint16_t* kbase = kc + head;
         const uint16_t* vbase = vc + head;
-        // The next segment, whose first block is loaded during this one's last.
+        // The next segment, whose first block (of this wave's share) is
+        // loaded during this one's last.
         Seg nxt;
         const bool more = next_segment(a, it, s_cum, s_len, nxt);
         const int Ln = more ? nxt.L : 0;
         const size_t nhead = more ? (static_cast<size_t>(nxt.b) * a.Hkv + nxt.g) * a.cap * D : head;
+        int nmy0 = 0, nmy1 = 0;
+        if (more) wave_share<W>(nxt, wave, nmy0, nmy1);
+        const int nfirst = nmy0 < nmy1 ? nmy0 : nxt.blk0;  // (an empty share loads the segment's first block)
 
         bf16x8 qf[RT][NC32];
         uint64_t anc[RT];
@@ -590,8 +626,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(RT <= 2 ? 2 
             const uint64_t node_anc = anc_mask(a, b);
             load_q<D, RT>(a, b, g, rg * RT * 16, node_anc, qf, anc);
             if constexpr (ROPE) {
-                depths_to_lds(a, node_anc, s_depth);
-                rope_q_frags<D, RT>(qf, anc, L, s_rev);
+                depths_to_lds(a, node_anc, s_depth[wave]);
+                rope_q_frags<D, RT>(qf, anc, L, s_rev[wave]);
             }
         }
         float m_run[RT], l_run[RT];
@@ -604,7 +640,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(RT <= 2 ? 2 
             for (int c = 0; c < NC16; ++c) o[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 
-        for (int xb = cur.blk0; xb < cur.blk1; ++xb) {
+        for (int xb = my0; xb < my1; ++xb) {
             const int kb = xb * 32;
             // Stage the block: K fragments as loaded (each lane reads back its
             // own), V transposed (row d holds the block's 32 keys); keys at
@@ -648,13 +684,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(RT <= 2 ? 2 
                 for (int h = 0; h < 2; ++h) {
                     const int n = kb + 8 * (n16 >> 2) + 4 * h + (n16 & 3) - L;
                     if (n >= 0 && n < a.N) {
-                        const int pos = L + s_depth[n];
+                        const int pos = L + s_depth[wave][n];
 #pragma unroll
                         for (int c = 0; c < NC32 / 2; ++c) {
                             u32x4* lo = reinterpret_cast<u32x4*>(ks + ((h * NC32 + c) * 64 + lane) * 16);
                             u32x4* hi = reinterpret_cast<u32x4*>(ks + ((h * NC32 + c + NC32 / 2) * 64 + lane) * 16);
                             u32x4 x = *lo, y = *hi;
-                            rope_bf16x8(x, y, pos, s_rev, 32 * c + 8 * q4);
+                            rope_bf16x8(x, y, pos, s_rev[wave], 32 * c + 8 * q4);
                             *lo = x;
                             *hi = y;
                         }
@@ -667,10 +703,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(RT <= 2 ? 2 
             // iteration never drains a prefetch early.
             asm volatile("" ::: "memory");
             {
-                const bool here = xb + 1 < cur.blk1;
+                const bool here = xb + 1 < my1;
                 const uint16_t* nk = here || !more ? kbase : kc + nhead;
                 const uint16_t* nv = here || !more ? vbase : vc + nhead;
-                const int nkb = here ? kb + 32 : (more ? nxt.blk0 * 32 : kb);
+                const int nkb = here ? kb + 32 : (more ? nfirst * 32 : kb);
                 const int nmax = here || !more ? Tk - 1 : Ln + a.N - 1;
                 load_kv_block<D>(R, nk, nv, nkb, nmax, n16, q4, vch, vkg);
             }
@@ -678,12 +714,56 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(RT <= 2 ? 2 
             block_update<D, RT, false>(kread, vt, qf, anc, kb, L, Tk, a.scale_log2, m_run, l_run, o);
             wave_lds_sync();
         }
-
-        write_rows<D, RT>(a, cur, rg * RT * 16, m_run, l_run, o);
-        if (cur.table && rg == 0 && lane == 0 && a.seg) a.seg[b * a.Hkv + g] = make_int2(cur.first, cur.count);
+        if constexpr (W > 1) {
+            // A wave with no share here has not loaded the next segment's
+            // first block yet.
+            if (my0 >= my1 && more)
+                load_kv_block<D>(R, kc + nhead, vc + nhead, nfirst * 32, Ln + a.N - 1, n16, q4, vch, vkg);
+            // Merge: the running maxima first (every wave is past its last
+            // stage read once they are all written); then every wave leaves
+            // its rescaled O and sums in the stages, and wave w adds up and
+            // stores column tiles [w*NCW, (w+1)*NCW) of the result.
+#pragma unroll
+            for (int t = 0; t < RT; ++t) s_mw[(wave * RT + t) * 64 + lane] = m_run[t];
+            __syncthreads();
+            f32x4* ob = reinterpret_cast<f32x4*>(s_stage);  // [W][RT][NC16][64 lanes]
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                float M = s_mw[t * 64 + lane];
+#pragma unroll
+                for (int w = 1; w < W; ++w) M = fmaxf(M, s_mw[(w * RT + t) * 64 + lane]);
+                const float f = m_run[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[t] - M);
+                s_lw[(wave * RT + t) * 64 + lane] = l_run[t] * f;
+#pragma unroll
+                for (int c = 0; c < NC16; ++c) ob[((wave * RT + t) * NC16 + c) * 64 + lane] = o[t][c] * f;
+                m_run[t] = M;
+            }
+            __syncthreads();
+            constexpr int NCW = NC16 / W;
+            f32x4 os[RT][NCW];
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                l_run[t] = 0.f;
+#pragma unroll
+                for (int c = 0; c < NCW; ++c) os[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int w = 0; w < W; ++w) {
+                    l_run[t] += s_lw[(w * RT + t) * 64 + lane];
+#pragma unroll
+                    for (int c = 0; c < NCW; ++c) os[t][c] += ob[((w * RT + t) * NC16 + wave * NCW + c) * 64 + lane];
+                }
+            }
+            write_rows<D, RT, true, NCW>(a, cur, rg * RT * 16, m_run, l_run, os, wave * NCW, wave == 0);
+            __syncthreads();  // the stages and the merge arrays are free for the next segment
+        } else {
+            write_rows<D, RT>(a, cur, rg * RT * 16, m_run, l_run, o);
+        }
+        if (cur.table && rg == 0 && threadIdx.x == 0 && a.seg) a.seg[b * a.Hkv + g] = make_int2(cur.first, cur.count);
         if (!more) break;
         cur = nxt;
         L = Ln;
+        my0 = nmy0;
+        my1 = nmy1;
     }
 }
 
@@ -1356,6 +1436,8 @@ __global__ __launch_bounds__(256) void attn_combine4(AttnArgs a, int bf16_out) {
 // Upper bound on resident workgroups of one launch (4 per CU on 256 CUs);
 // sizes the balanced-mode partials independently of the device.
 constexpr int kMaxResident = 2048;
+constexpr int kKeySplitWaves = 4;  // waves splitting one range (small problems, one row tile group)
+constexpr long kKeySplitMinBlocks = 1024;
 
 AttnPlan plan_attn(const spec_attn_desc& d, int max_prefix_len) {
     AttnPlan p{};
@@ -1365,12 +1447,20 @@ AttnPlan plan_attn(const spec_attn_desc& d, int max_prefix_len) {
     const long keys_max = static_cast<long>(max_prefix_len) + d.num_nodes;
     const long blocks_max = (keys_max + 31) / 32;
     long min_blocks = 2;  // balanced mode: least blocks per range
+    p.kwaves = 1;
     if (d.dtype == SPEC_BF16) {
         p.mfma = true;
         if (p.rows <= 64) {  // one wave holds every row
             p.row_tiles = (p.rows + 15) / 16;
             p.row_groups = 1;
             p.waves = 1;
+            // Few blocks in all (under 8 per one-wave range at full
+            // residency): the waves of a workgroup split each range so a
+            // partial covers kKeySplitWaves times the blocks.  Below about
+            // a thousand blocks the step is latency-bound and the merge's
+            // barriers cost more than the partial traffic they save.
+            const long nblk = slabs * blocks_max;
+            if (p.row_tiles <= 2 && nblk >= kKeySplitMinBlocks && nblk < 8L * kMaxResident) p.kwaves = kKeySplitWaves;
         } else {  // wg_waves<D>() waves of 32 rows share each KV block
             p.row_tiles = 2;
             p.waves = d.head_dim == 128 ? wg_waves<128>() : wg_waves<64>();
@@ -1391,7 +1481,8 @@ AttnPlan plan_attn(const spec_attn_desc& d, int max_prefix_len) {
         // P is picked per launch from the device (resident workgroups); the
         // workspace holds the most partials any device can ask for.
         if (d.kv_split_keys > 0) min_blocks = (d.kv_split_keys + 31) / 32;
-        long pcap = kMaxResident / p.row_groups;
+        else if (p.kwaves > 1) min_blocks = p.kwaves;  // one block per wave
+        long pcap = kMaxResident / p.row_groups / p.kwaves;
         if (pcap < 8) pcap = 8;
         const long by_work = (slabs * blocks_max + min_blocks - 1) / min_blocks;
         p.parts_max = static_cast<int>(by_work < pcap ? by_work : pcap);
@@ -1443,10 +1534,10 @@ static int device_cus() {
     return cus[dev];
 }
 
-template <int D, int RT, bool ROPE>
+template <int D, int RT, bool ROPE, int W = 1>
 static int mfma_resident() {
     static int n = 0;
-    if (n == 0) n = resident_per_cu(attn_mfma<D, RT, ROPE>, 64);
+    if (n == 0) n = resident_per_cu(attn_mfma<D, RT, ROPE, W>, 64 * W);
     return n;
 }
 
@@ -1458,8 +1549,9 @@ static int mfma_wg_resident() {
 }
 
 template <int D, bool ROPE>
-static int mfma_resident_rt(int rt, int waves) {
+static int mfma_resident_rt(int rt, int waves, int kwaves) {
     if (waves > 1) return mfma_wg_resident<D, ROPE>();
+    if (kwaves > 1) return rt == 1 ? mfma_resident<D, 1, ROPE, kKeySplitWaves>() : mfma_resident<D, 2, ROPE, kKeySplitWaves>();
     switch (rt) {
         case 1: return mfma_resident<D, 1, ROPE>();
         case 2: return mfma_resident<D, 2, ROPE>();
@@ -1469,8 +1561,8 @@ static int mfma_resident_rt(int rt, int waves) {
 }
 
 template <int D>
-static int mfma_resident_rt(int rt, int waves, bool rope) {
-    return rope ? mfma_resident_rt<D, true>(rt, waves) : mfma_resident_rt<D, false>(rt, waves);
+static int mfma_resident_rt(int rt, int waves, int kwaves, bool rope) {
+    return rope ? mfma_resident_rt<D, true>(rt, waves, kwaves) : mfma_resident_rt<D, false>(rt, waves, kwaves);
 }
 
 // The rotating kernels are separate instantiations: the plain ones keep
@@ -1480,6 +1572,14 @@ template <int D, bool ROPE>
 static void launch_mfma_rt(const AttnPlan& p, const AttnArgs& a, dim3 grid, hipStream_t st) {
     if (p.waves > 1) {
         hipLaunchKernelGGL((attn_mfma_wg<D, 2, wg_waves<D>(), ROPE>), grid, dim3(64 * wg_waves<D>()), 0, st, a);
+        return;
+    }
+    if (p.kwaves > 1) {
+        constexpr int W = kKeySplitWaves;
+        if (p.row_tiles == 1)
+            hipLaunchKernelGGL((attn_mfma<D, 1, ROPE, W>), grid, dim3(64 * W), 0, st, a);
+        else
+            hipLaunchKernelGGL((attn_mfma<D, 2, ROPE, W>), grid, dim3(64 * W), 0, st, a);
         return;
     }
     switch (p.row_tiles) {
@@ -1526,8 +1626,8 @@ int launch_verify_attn(const spec_attn_desc& d, const AttnPlan& p, const void* q
     bool combine;
     if (p.balanced) {
         const bool rope = d.rope_base > 0.f;
-        const int per_cu = d.head_dim == 128 ? mfma_resident_rt<128>(p.row_tiles, p.waves, rope)
-                                             : mfma_resident_rt<64>(p.row_tiles, p.waves, rope);
+        const int per_cu = d.head_dim == 128 ? mfma_resident_rt<128>(p.row_tiles, p.waves, p.kwaves, rope)
+                                             : mfma_resident_rt<64>(p.row_tiles, p.waves, p.kwaves, rope);
         long P = static_cast<long>(per_cu) * device_cus() / p.row_groups;
         if (P > p.parts_max) P = p.parts_max;
         if (P >= 8) P = P / 8 * 8;
@@ -1541,8 +1641,9 @@ int launch_verify_attn(const spec_attn_desc& d, const AttnPlan& p, const void* q
         combine = p.nsplit_max > 1;
     }
     // Partials of the longest slab: its blocks over the blocks per range
-    // (plus one for a range that starts inside it), or its splits.  Up to 16
-    // go to attn_combine4, which takes MFMA partials in bf16.
+    // (plus one for a range that starts inside it), or its splits.  Up to 24
+    // (three rounds of eight) go to attn_combine4, which takes MFMA partials
+    // in bf16.
     long most;
     if (p.balanced) {
         const long per = (slabs * ((static_cast<long>(p.max_keys) + 31) / 32)) / a.nparts;
@@ -1550,7 +1651,7 @@ int launch_verify_attn(const spec_attn_desc& d, const AttnPlan& p, const void* q
     } else {
         most = p.nsplit_max;
     }
-    const bool wide = most > 16;  // one row per wavefront, 32 partials per round (more registers)
+    const bool wide = most > 24;  // one row per wavefront, 32 partials per round (more registers)
     // (the many-row kernel keeps fp32 partials: the bf16 store path cost it
     // registers and time)
     a.bf16p = combine && p.mfma && p.waves == 1 && !wide ? 1 : 0;

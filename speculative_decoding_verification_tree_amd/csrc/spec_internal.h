@@ -19,7 +19,8 @@ struct AttnPlan {
     bool balanced;    // balanced block ranges (else fixed splits per slab)
     int rows;         // R = N * (Hq / Hkv): query rows per (request, kv head)
     int row_tiles;    // MFMA: 16-row tiles per wave
-    int waves;        // wavefronts per workgroup
+    int waves;        // wavefronts per workgroup (row tiles shared between them)
+    int kwaves;       // one-wave MFMA path: waves splitting each range's blocks (merged in LDS)
     int row_groups;   // workgroups sharing one KV range (different query rows)
     int split_blocks; // fixed: 32-key blocks per split; balanced: least blocks per range
     int nsplit_max;   // fixed: splits of the longest request

@@ -73,6 +73,22 @@ def test_attention_edge_cases(over):
     _attn_all_rows(w, f"edge {over}")
 
 
+@pytest.mark.parametrize("cid,over", [
+    (2, dict(batch=4, prefix_len=(0, 2000))),                            # R = 24: two row tiles
+    (2, dict(batch=4, prefix_len=(0, 2000), head_dim=64)),               # D = 64
+    (2, dict(batch=4, prefix_len=(0, 2000), drafts=0)),                  # N = 1: one row tile
+    (2, dict(batch=4, prefix_len=(1500, 2000), num_q_heads=8, num_kv_heads=8)),  # MHA, R = 6
+    (2, dict(batch=1, prefix_len=32768)),                                # one long request
+    (5, dict(batch=4, prefix_len=(2000, 3000), nodes=8, num_q_heads=16, num_kv_heads=4)),  # tree, R = 32
+])
+def test_attention_key_split_waves(cid, over):
+    # One row-tile group and roughly 1k-16k blocks in all: four waves split
+    # each range and merge in LDS (ranges of one block per wave, so short
+    # segments leave some waves without a share).
+    w = generate(scaled(cid, **over), with_accept=False)
+    _attn_all_rows(w, f"key-split cfg{cid} {over}")
+
+
 @pytest.mark.parametrize("over", [
     dict(nodes=64, max_depth=63, prefix_len=37),      # max nodes, deep tree
     dict(nodes=2, prefix_len=5),

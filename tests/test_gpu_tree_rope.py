@@ -142,6 +142,7 @@ def _rounded(x, dtype):
     ("bf16", 128, 5, 8, 32, 8, [512, 8000, 77, 1, 4000], False),  # ragged chains
     ("bf16", 64, 2, 20, 8, 2, [5, 129], True),              # D = 64
     ("bf16", 64, 2, 40, 16, 4, [300, 90], True),            # D = 64, R = 160: shared-KV kernel
+    ("bf16", 64, 4, 6, 16, 4, [3000, 100, 2900, 1], True),  # D = 64, R = 24, 1.5k blocks: key-split waves
     ("f32", 128, 2, 9, 4, 4, [77, 0], True),                # fp32 VALU kernel
     ("f32", 64, 1, 5, 4, 1, [128], False),
 ])
