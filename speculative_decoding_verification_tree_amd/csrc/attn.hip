@@ -22,9 +22,10 @@
 //   fixed    : split s of slab q takes blocks [s*C, (s+1)*C) (large batches,
 //              where slabs far outnumber resident workgroups; VALU path).
 // A slab covered by one segment is written straight to out; otherwise each
-// segment writes its unnormalised partial (O, max, sum) -- O in bf16 when
-// attn_combine4 merges few partials per slab, else fp32 -- and attn_combine4
-// or attn_combine merges a slab's partials with an exact log-sum-exp
+// segment writes its unnormalised partial (O, max, sum) -- O in bf16 from
+// the one-row-group kernels, fp32 from the many-row kernel -- and
+// attn_combine4 (few partials per slab) or attn_combine (many) merges a
+// slab's partials with an exact log-sum-exp
 // rescale, from the (first partial, count) table the segments leave in the
 // workspace.
 //
@@ -68,7 +69,7 @@ struct AttnArgs {
     int split_blocks;  // fixed: 32-key blocks per split
     int max_keys;      // host bound on L_b + N
     float scale_log2;  // softmax scale * log2(e)
-    int bf16p;         // MFMA partials stored as bf16 (slabs of few partials, merged by attn_combine4)
+    int bf16p;         // MFMA partials stored as bf16 (one-row-group kernels)
     int rope;          // fused depth-position rotary embedding of q and the tree's K rows
     RopeTable rope_tab;
 };
@@ -1266,9 +1267,9 @@ __global__ __launch_bounds__(256) void attn_valu(AttnArgs a) {
 // Split combine: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the
 // partials of one slab.  One wavefront per (request, kv head, query row).
 // ----------------------------------------------------------------------------
-template <int D, int SB>  // SB: partials whose loads are in flight together
+template <int D, int SB, bool BP>  // SB: partials whose loads are in flight together; BP: bf16 partials
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int bf16_out) {
-    constexpr int DPL = D / 64;  // output elements per lane
+    constexpr int DPL = D / 64;  // output elements per lane: dims lane + 64 j (fp32), DPL * lane + j (bf16)
     const int lane = threadIdx.x & 63;
     const long id = static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (id >= static_cast<long>(a.B) * a.Hkv * a.R) return;
@@ -1290,16 +1291,42 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int bf16_out) {
     for (int s0 = 0; s0 < count; s0 += SB) {
         float2 ml[SB];
         float ov[SB][DPL];
+        if constexpr (BP) {
+            // DPL consecutive bf16 values per partial (one 4-byte or 2-byte
+            // load) from clamped indexes, selected afterwards: no load under
+            // a branch, so all SB are in flight together.
+            uint32_t raw[SB];
 #pragma unroll
-        for (int k = 0; k < SB; ++k) {
-            const size_t pi = static_cast<size_t>(first + s0 + k);
-            ml[k] = make_float2(-INFINITY, 0.f);
-#pragma unroll
-            for (int j = 0; j < DPL; ++j) ov[k][j] = 0.f;
-            if (s0 + k < count) {
+            for (int k = 0; k < SB; ++k) {
+                const size_t pi = static_cast<size_t>(first + min(s0 + k, count - 1));
                 ml[k] = a.ws_ml[pi * a.R + r];
+                const uint16_t* prow = reinterpret_cast<const uint16_t*>(a.ws_o) + (pi * a.R + r) * D + DPL * lane;
+                if constexpr (DPL == 2) raw[k] = *reinterpret_cast<const uint32_t*>(prow);
+                else raw[k] = *prow;
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int j = 0; j < DPL; ++j) ov[k][j] = a.ws_o[(pi * a.R + r) * D + lane + 64 * j];
+            for (int k = 0; k < SB; ++k) {
+                if (s0 + k >= count) ml[k] = make_float2(-INFINITY, 0.f);
+                if constexpr (DPL == 2) {
+                    ov[k][0] = __uint_as_float(raw[k] << 16);
+                    ov[k][1] = __uint_as_float(raw[k] & 0xFFFF0000u);
+                } else {
+                    ov[k][0] = __uint_as_float(raw[k] << 16);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < SB; ++k) {
+                const size_t pi = static_cast<size_t>(first + s0 + k);
+                ml[k] = make_float2(-INFINITY, 0.f);
+#pragma unroll
+                for (int j = 0; j < DPL; ++j) ov[k][j] = 0.f;
+                if (s0 + k < count) {
+                    ml[k] = a.ws_ml[pi * a.R + r];
+#pragma unroll
+                    for (int j = 0; j < DPL; ++j) ov[k][j] = a.ws_o[(pi * a.R + r) * D + lane + 64 * j];
+                }
             }
         }
         float Mn = M;
@@ -1323,7 +1350,7 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int bf16_out) {
     const int node = r / a.G, hq = g * a.G + r % a.G;
     const size_t ob = ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D;
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) store_out(a.out, bf16_out != 0, ob + lane + 64 * j, acc[j] * inv);
+    for (int j = 0; j < DPL; ++j) store_out(a.out, bf16_out != 0, ob + (BP ? DPL * lane + j : lane + 64 * j), acc[j] * inv);
 }
 
 // Split combine for slabs of few partials: a wavefront merges four rows at
@@ -1654,7 +1681,7 @@ int launch_verify_attn(const spec_attn_desc& d, const AttnPlan& p, const void* q
     const bool wide = most > 24;  // one row per wavefront, 32 partials per round (more registers)
     // (the many-row kernel keeps fp32 partials: the bf16 store path cost it
     // registers and time)
-    a.bf16p = combine && p.mfma && p.waves == 1 && !wide ? 1 : 0;
+    a.bf16p = combine && p.mfma && p.waves == 1 ? 1 : 0;
     if (combine) {
         const long parts = p.balanced ? p.parts_max + slabs : slabs * p.nsplit_max;
         char* ws = static_cast<char*>(workspace);
@@ -1703,10 +1730,15 @@ int launch_verify_attn(const spec_attn_desc& d, const AttnPlan& p, const void* q
             } else {
                 hipLaunchKernelGGL((attn_combine4<64, 8, false>), cgrid4, dim3(256), 0, stream, a, bf16_out);
             }
+        } else if (a.bf16p) {
+            if (d.head_dim == 128)
+                hipLaunchKernelGGL((attn_combine<128, 32, true>), cgrid, dim3(256), 0, stream, a, bf16_out);
+            else
+                hipLaunchKernelGGL((attn_combine<64, 32, true>), cgrid, dim3(256), 0, stream, a, bf16_out);
         } else if (d.head_dim == 128) {
-            hipLaunchKernelGGL((attn_combine<128, 32>), cgrid, dim3(256), 0, stream, a, bf16_out);
+            hipLaunchKernelGGL((attn_combine<128, 32, false>), cgrid, dim3(256), 0, stream, a, bf16_out);
         } else {
-            hipLaunchKernelGGL((attn_combine<64, 32>), cgrid, dim3(256), 0, stream, a, bf16_out);
+            hipLaunchKernelGGL((attn_combine<64, 32, false>), cgrid, dim3(256), 0, stream, a, bf16_out);
         }
         if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     }
