@@ -193,7 +193,14 @@ int spec_accept_reject_filtered(int32_t batch, int32_t num_nodes, int32_t vocab,
  * of spec_accept_reject does not give for nodes with several children.  On
  * a chain both rules agree.  Arguments and outputs as spec_accept_reject;
  * workspace >= spec_accept_multidraft_workspace_bytes(batch, vocab) (two
- * residual rows per request; contents need no initialisation). */
+ * residual rows, 2 KiB of exchange records and a counter per request;
+ * contents need no initialisation: the call clears the counters itself).
+ * Each request's vocabulary is split over up to 64 workgroups that wait on
+ * each other between passes, so the call assumes its grid runs at once (it
+ * is sized from the device's occupancy; nothing else should fill the device
+ * meanwhile); a request whose workgroups were not all running returns
+ * accept_len = -1 after a bounded wait instead of hanging.  Calls that
+ * overlap on one workspace race. */
 size_t spec_accept_multidraft_workspace_bytes(int32_t batch, int32_t vocab);
 int spec_accept_multidraft(int32_t batch, int32_t num_nodes, int32_t vocab, const float* target_logits,
                            const float* draft_probs, const int32_t* tokens, const int32_t* parent,

@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libspecverify.so")
-SOURCES = ["api.hip", "attn.hip", "accept.hip", "commit.hip", "tree.hip", "linattn.hip"]
+SOURCES = ["api.hip", "attn.hip", "accept.hip", "multidraft.hip", "commit.hip", "tree.hip", "linattn.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

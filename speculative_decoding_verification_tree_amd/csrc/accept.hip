@@ -92,7 +92,6 @@ struct AcceptArgs {
     float T, eps, delta;
     int top_k;    // 0: off
     float top_p;  // 1: off
-    float* resid;  // multi-draft rule: two residual rows per request
 };
 
 constexpr int kThreads = 256;
@@ -142,27 +141,6 @@ __device__ __forceinline__ void block_argmax(float& v, int& i, float* s_v, int* 
             v = s_v[k];
             i = s_i[k];
         }
-}
-
-// Minimum of mn and maximum of mx over a wavefront, the two reductions
-// interleaved (DPP within rows, permlane swaps across rows).
-__device__ __forceinline__ void wave_min_max_i(int& mn, int& mx) {
-    mn = min(mn, static_cast<int>(dpp_xor1(static_cast<uint32_t>(mn))));
-    mx = max(mx, static_cast<int>(dpp_xor1(static_cast<uint32_t>(mx))));
-    mn = min(mn, static_cast<int>(dpp_xor2(static_cast<uint32_t>(mn))));
-    mx = max(mx, static_cast<int>(dpp_xor2(static_cast<uint32_t>(mx))));
-    mn = min(mn, static_cast<int>(dpp_mirror8(static_cast<uint32_t>(mn))));
-    mx = max(mx, static_cast<int>(dpp_mirror8(static_cast<uint32_t>(mx))));
-    mn = min(mn, static_cast<int>(dpp_mirror16(static_cast<uint32_t>(mn))));
-    mx = max(mx, static_cast<int>(dpp_mirror16(static_cast<uint32_t>(mx))));
-    auto a = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(mn), static_cast<uint32_t>(mn), false, false);
-    auto c = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(mx), static_cast<uint32_t>(mx), false, false);
-    mn = min(static_cast<int>(a[0]), static_cast<int>(a[1]));
-    mx = max(static_cast<int>(c[0]), static_cast<int>(c[1]));
-    a = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(mn), static_cast<uint32_t>(mn), false, false);
-    c = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(mx), static_cast<uint32_t>(mx), false, false);
-    mn = min(static_cast<int>(a[0]), static_cast<int>(a[1]));
-    mx = max(static_cast<int>(c[0]), static_cast<int>(c[1]));
 }
 
 // The same over the workgroup: one LDS exchange.
@@ -792,27 +770,6 @@ __global__ __launch_bounds__(kThreads) void accept_sample(AcceptArgs a) {
 // ---------------------------------------------------------------------------
 // 64-bit DPP move of a double (both halves with the same control); lanes
 // without a source read 0.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ double dpp_d(double v) {
-    const uint64_t u = __builtin_bit_cast(uint64_t, v);
-    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(u), CTRL, ROW_MASK, 0xF, true);
-    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(u >> 32), CTRL, ROW_MASK, 0xF, true);
-    return __builtin_bit_cast(double, static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32));
-}
-
-// Inclusive prefix sum over the lanes of a wavefront: shifts by 1, 2, 4, 8
-// inside each 16-lane row, then the last lane of row 0 (row 2) is added to
-// row 1 (row 3), and lane 31 to rows 2 and 3.
-__device__ __forceinline__ double wave_incl_scan(double v) {
-    v += dpp_d<0x111, 0xF>(v);  // row_shr:1
-    v += dpp_d<0x112, 0xF>(v);  // row_shr:2
-    v += dpp_d<0x114, 0xF>(v);  // row_shr:4
-    v += dpp_d<0x118, 0xF>(v);  // row_shr:8
-    v += dpp_d<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
-    v += dpp_d<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
-    return v;
-}
-
 // This thread's run of EPT consecutive tokens first .. first + EPT - 1 of a
 // chunk ending at x1, from two rows (16-byte loads when the rows allow):
 // the layout of the token search, which walks each run in token order.
@@ -1357,248 +1314,6 @@ __global__ __launch_bounds__(kFThreads) void accept_filter(AcceptArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Multi-draft tree rejection by recursive residuals, one 1024-thread
-// workgroup per request walking down the tree.  At node v (row statistics in
-// one pass; at T = 0 just the argmax) the children are tested in ascending
-// index, child c with token x against the current residual r:
-// u_accept[c] * q_c(x) < r(x), r = p_v at first.  A rejected child costs one
-// pass writing max(0, r - q_c) into the other residual row (fp32, its total
-// summed in fp64; an all-zero result keeps r).  The first accepted child
-// becomes v.  When every child is rejected the last token is drawn from r,
-// at a leaf from p_v: inverse CDF over contiguous runs of tokens per thread
-// (run sums, one block scan, then each thread walks its run).
-template <class F>
-__device__ __forceinline__ void for_row2(const float* ra, const float* rb, int V, bool vec4, F f) {
-    const int tid = threadIdx.x;
-    if (vec4) {
-        for (int base = 4 * tid; base < V; base += 4 * kFThreads * 4) {
-            float4 va[4], vb[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int x = min(base + 4 * kFThreads * u, V - 4);
-                va[u] = *reinterpret_cast<const float4*>(ra + x);
-                vb[u] = *reinterpret_cast<const float4*>(rb + x);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int x = base + 4 * kFThreads * u;
-                if (x < V) {
-                    f(x, va[u].x, vb[u].x);
-                    f(x + 1, va[u].y, vb[u].y);
-                    f(x + 2, va[u].z, vb[u].z);
-                    f(x + 3, va[u].w, vb[u].w);
-                }
-            }
-        }
-    } else {
-        for (int x = tid; x < V; x += kFThreads) f(x, ra[x], rb[x]);
-    }
-}
-
-__device__ __forceinline__ double block_sum_f(double v, double* s_w) {
-    v = wave_sum(v);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    __syncthreads();
-    if (lane == 0) s_w[wave] = v;
-    __syncthreads();
-    double t = 0.0;
-    for (int k = 0; k < kFWaves; ++k) t += s_w[k];
-    return t;
-}
-
-__global__ __launch_bounds__(kFThreads) void accept_multidraft(AcceptArgs a) {
-    const int b = blockIdx.x, N = a.N, V = a.V;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const bool vec4 = a.vec4 != 0;
-    __shared__ int s_par[kMaxNodes], s_tok[kMaxNodes], s_path[kMaxNodes];
-    __shared__ double s_w[kFWaves];
-    __shared__ float s_m[kFWaves];
-    __shared__ int s_i[kFWaves], s_j[kFWaves];
-    __shared__ int s_flag, s_final;
-    if (tid < N) {
-        s_par[tid] = tree_parent(a.parent, N, b, tid);
-        s_tok[tid] = min(max(a.tokens[static_cast<size_t>(b) * N + tid], 0), V - 1);
-    }
-    if (tid == 0) s_path[0] = 0;
-    float* R[2] = {a.resid + static_cast<size_t>(2 * b) * V, a.resid + static_cast<size_t>(2 * b + 1) * V};
-    const bool greedy = !(a.T > 0.f);
-    const float c2 = greedy ? 0.f : 1.4426950408889634f / a.T;
-    int v = 0, depth = 0, final = 0;
-    __syncthreads();
-    for (;;) {
-        const float* row = a.logits + (static_cast<size_t>(b) * N + v) * V;
-        // Row max (lowest index on ties) and, at T > 0, S = sum 2^((l - M) c2).
-        float best = -INFINITY;
-        int bi = 0x7fffffff;
-        for_row(row, V, vec4, [&](int x, float l) {
-            if (l > best) {
-                best = l;
-                bi = x;
-            }
-        });
-        wave_argmax(best, bi);
-        __syncthreads();
-        if (lane == 0) {
-            s_m[wave] = best;
-            s_i[wave] = bi;
-        }
-        __syncthreads();
-        float M = s_m[0];
-        int arg = s_i[0];
-        for (int k = 1; k < kFWaves; ++k)
-            if (s_m[k] > M || (s_m[k] == M && s_i[k] < arg)) {
-                M = s_m[k];
-                arg = s_i[k];
-            }
-        double S = 1.0;
-        if (!greedy) {
-            double sum = 0.0;
-            for_row(row, V, vec4, [&](int, float l) { sum += __builtin_amdgcn_exp2f((l - M) * c2); });
-            S = block_sum_f(sum, s_w);
-        }
-        // Children in ascending index against the current residual.
-        int cur = -1;  // residual row holding r (unnormalised, total Z); -1: r = p_v
-        double Z = 1.0;
-        int next = -1;
-        for (int c = 1; c < N; ++c) {
-            if (s_par[c] != v) continue;
-            const int x = s_tok[c];
-            const float* qrow = a.draft + (static_cast<size_t>(b) * N + c) * V;
-            if (tid == 0) {
-                const double qx = qrow[x], ua = a.u_acc[static_cast<size_t>(b) * N + c];
-                double rx;
-                if (greedy) rx = x == arg ? 1.0 : 0.0;
-                else if (cur >= 0) rx = static_cast<double>(R[cur][x]) / Z;
-                else rx = static_cast<double>(__builtin_amdgcn_exp2f((row[x] - M) * c2)) / S;
-                s_flag = ua * qx < rx;
-            }
-            __syncthreads();
-            const bool acc = s_flag != 0;
-            __syncthreads();
-            if (acc) {
-                next = c;
-                break;
-            }
-            if (greedy) continue;  // r stays the one-hot argmax
-            // r <- max(0, r - q_c), into the other residual row
-            const int dst = cur == 0 ? 1 : 0;
-            float* out = R[dst];
-            const double invZ = 1.0 / Z, invS = 1.0 / S;
-            double zs = 0.0;
-            auto upd = [&](int y, float src, float qy) {
-                const double ry = cur >= 0 ? static_cast<double>(src) * invZ
-                                           : static_cast<double>(__builtin_amdgcn_exp2f((src - M) * c2)) * invS;
-                const float e = static_cast<float>(fmax(ry - static_cast<double>(qy), 0.0));
-                out[y] = e;
-                zs += e;
-            };
-            for_row2(cur >= 0 ? R[cur] : row, qrow, V, vec4, upd);
-            const double Zn = block_sum_f(zs, s_w);
-            if (Zn > 0.0) {
-                cur = dst;
-                Z = Zn;
-            }
-        }
-        if (next >= 0) {
-            v = next;
-            ++depth;
-            if (tid == 0) s_path[depth] = v;
-            __syncthreads();
-            continue;
-        }
-        // Last token: from r (v had children) or p_v (a leaf).
-        if (greedy) {
-            final = arg;
-            break;
-        }
-        const double u = a.u_smp ? static_cast<double>(a.u_smp[static_cast<size_t>(b) * N + v]) : 0.0;
-        const int run = (V + kFThreads - 1) / kFThreads;
-        const int x0 = min(tid * run, V), x1 = min(x0 + run, V);
-        auto weight = [&](int y) {
-            return cur >= 0 ? static_cast<double>(R[cur][y])
-                            : static_cast<double>(__builtin_amdgcn_exp2f((row[y] - M) * c2));
-        };
-        double mine = 0.0;
-        for (int y = x0; y < x1; ++y) mine += weight(y);
-        const double incl = wave_incl_scan(mine);
-        __syncthreads();
-        if (lane == 63) s_w[wave] = incl;
-        __syncthreads();
-        double before = incl - mine, total = 0.0;
-        for (int k = 0; k < kFWaves; ++k) {
-            if (k < wave) before += s_w[k];
-            total += s_w[k];
-        }
-        const double t = u * total;
-        int hit = 0x7fffffff, lastnz = -1;
-        double cum = before;
-        for (int y = x0; y < x1; ++y) {
-            const double w = weight(y);
-            if (w > 0.0) {
-                lastnz = y;
-                cum += w;
-                if (hit == 0x7fffffff && cum > t) hit = y;
-            }
-        }
-        int ih = hit, il = lastnz;
-        wave_min_max_i(ih, il);
-        __syncthreads();
-        if (lane == 0) {
-            s_i[wave] = ih;
-            s_j[wave] = il;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            int h = 0x7fffffff, l = -1;
-            for (int k = 0; k < kFWaves; ++k) {
-                h = min(h, s_i[k]);
-                l = max(l, s_j[k]);
-            }
-            s_final = h != 0x7fffffff ? h : max(l, 0);
-        }
-        __syncthreads();
-        final = s_final;
-        break;
-    }
-    // Outputs.
-    if (tid < N) {
-        const size_t o = static_cast<size_t>(b) * N + tid;
-        a.path[o] = tid <= depth ? s_path[tid] : -1;
-        a.out_tokens[o] = tid < depth ? s_tok[s_path[tid + 1]] : (tid == depth ? final : -1);
-    }
-    if (tid == 0) a.accept_len[b] = depth;
-}
-
-size_t multidraft_workspace_bytes(int B, int V) { return static_cast<size_t>(B) * 2 * V * sizeof(float); }
-
-int launch_accept_multidraft(int B, int N, int V, const float* logits, const float* draft, const int32_t* tokens,
-                             const int32_t* parent, const float* u_accept, const float* u_sample, float temperature,
-                             int32_t* accept_len, int32_t* path, int32_t* out_tokens, void* workspace,
-                             hipStream_t stream) {
-    AcceptArgs a{};
-    a.logits = logits;
-    a.draft = draft;
-    a.tokens = tokens;
-    a.parent = parent;
-    a.u_acc = u_accept;
-    a.u_smp = u_sample;
-    a.accept_len = accept_len;
-    a.path = path;
-    a.out_tokens = out_tokens;
-    a.resid = static_cast<float*>(workspace);
-    a.B = B;
-    a.N = N;
-    a.V = V;
-    a.rule = 0;
-    a.T = temperature;
-    a.top_p = 1.f;
-    a.vec4 = (V % 4 == 0) && (reinterpret_cast<uintptr_t>(logits) % 16 == 0) &&
-             (draft == nullptr || reinterpret_cast<uintptr_t>(draft) % 16 == 0) &&
-             (reinterpret_cast<uintptr_t>(workspace) % 16 == 0);
-    hipLaunchKernelGGL(accept_multidraft, dim3(B), dim3(kFThreads), 0, stream, a);
-    return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
-}
-
 AcceptPlan plan_accept(int B, int N, int V) {
     AcceptPlan p{};
     p.chunk = accept_ept(B, N, V) * kThreads;

@@ -208,6 +208,48 @@ __device__ __forceinline__ void rope_f32x4(u32x4& lo, u32x4& hi, int pos, const 
 
 // Wait for this wave's LDS traffic and stop the compiler from moving memory
 // operations across; sufficient for LDS exchange inside one wavefront.
+// Minimum of mn and maximum of mx over a wavefront, the two reductions
+// interleaved (DPP within rows, permlane swaps across rows).
+__device__ __forceinline__ void wave_min_max_i(int& mn, int& mx) {
+    mn = min(mn, static_cast<int>(dpp_xor1(static_cast<uint32_t>(mn))));
+    mx = max(mx, static_cast<int>(dpp_xor1(static_cast<uint32_t>(mx))));
+    mn = min(mn, static_cast<int>(dpp_xor2(static_cast<uint32_t>(mn))));
+    mx = max(mx, static_cast<int>(dpp_xor2(static_cast<uint32_t>(mx))));
+    mn = min(mn, static_cast<int>(dpp_mirror8(static_cast<uint32_t>(mn))));
+    mx = max(mx, static_cast<int>(dpp_mirror8(static_cast<uint32_t>(mx))));
+    mn = min(mn, static_cast<int>(dpp_mirror16(static_cast<uint32_t>(mn))));
+    mx = max(mx, static_cast<int>(dpp_mirror16(static_cast<uint32_t>(mx))));
+    auto a = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(mn), static_cast<uint32_t>(mn), false, false);
+    auto c = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(mx), static_cast<uint32_t>(mx), false, false);
+    mn = min(static_cast<int>(a[0]), static_cast<int>(a[1]));
+    mx = max(static_cast<int>(c[0]), static_cast<int>(c[1]));
+    a = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(mn), static_cast<uint32_t>(mn), false, false);
+    c = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(mx), static_cast<uint32_t>(mx), false, false);
+    mn = min(static_cast<int>(a[0]), static_cast<int>(a[1]));
+    mx = max(static_cast<int>(c[0]), static_cast<int>(c[1]));
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_d(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(u), CTRL, ROW_MASK, 0xF, true);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(u >> 32), CTRL, ROW_MASK, 0xF, true);
+    return __builtin_bit_cast(double, static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32));
+}
+
+// Inclusive prefix sum over the lanes of a wavefront: shifts by 1, 2, 4, 8
+// inside each 16-lane row, then the last lane of row 0 (row 2) is added to
+// row 1 (row 3), and lane 31 to rows 2 and 3.
+__device__ __forceinline__ double wave_incl_scan(double v) {
+    v += dpp_d<0x111, 0xF>(v);  // row_shr:1
+    v += dpp_d<0x112, 0xF>(v);  // row_shr:2
+    v += dpp_d<0x114, 0xF>(v);  // row_shr:4
+    v += dpp_d<0x118, 0xF>(v);  // row_shr:8
+    v += dpp_d<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_d<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Parent of node i (-1 for the root); parent == nullptr means a chain.
