@@ -7,7 +7,10 @@
 // none): S_t = alpha_t S_{t-1} + v_t k_t^T, o_t = S_t q_t, per (request,
 // head), S [Dv][Dk] fp32.
 //
-// One 256-thread workgroup per (head, request), two optional phases:
+// One 256-thread workgroup per (head, request, slice of kLaRows state rows):
+// the rows e of S (the output dims) are independent in both phases, so a
+// (head, request) is spread over Dv / kLaRows workgroups, each recomputing
+// the small N x N score matrix.  Two optional phases:
 //   commit: S <- A(-> v] S + sum_{j on the accepted path} A(j -> v] v_j k_j^T,
 //           the path's k, v and decay weights in LDS, every state element
 //           written once (in place; the workgroup owns its slab);
@@ -25,6 +28,7 @@ namespace specv {
 constexpr int kLaThreads = 256;
 constexpr int kLaMaxD = 128;
 constexpr int kLaChunk = 32;
+constexpr int kLaRows = 32;  // state rows (output dims) per workgroup
 
 // Rows [0, rows) of `cols` elements (bf16 or fp32, row t at global element
 // offset row_off(t)) into LDS dst[t * ldst + c], in rounds of kLaBatch
@@ -94,8 +98,8 @@ __device__ __forceinline__ void la_tree(const int32_t* parent, const float* alph
 // of the state), whichever is larger.
 template <int NMAX, bool COMMIT>
 constexpr int la_lds_floats() {
-    constexpr int commit = COMMIT ? kMaxNodes * 2 * kLaMaxD : 0;
-    constexpr int verify = 2 * NMAX * (kLaMaxD + 1) + NMAX * kLaMaxD + NMAX * NMAX + kLaMaxD * (kLaChunk + 1);
+    constexpr int commit = COMMIT ? kMaxNodes * (kLaMaxD + kLaRows) : 0;
+    constexpr int verify = 2 * NMAX * (kLaMaxD + 1) + NMAX * kLaRows + NMAX * NMAX + kLaRows * (kLaChunk + 1);
     return commit > verify ? commit : verify;
 }
 
@@ -105,6 +109,7 @@ template <int NMAX, bool COMMIT>
 __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int Dk = a.Dk, Dv = a.Dv, H = a.H;
+    const int es0 = blockIdx.z * kLaRows, ne = min(kLaRows, Dv - es0);  // this workgroup's state rows
     const bool bf16 = a.bf16 != 0;
     __shared__ float lds[la_lds_floats<NMAX, COMMIT>()];
     __shared__ int s_par[kMaxNodes];
@@ -127,30 +132,31 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
         }
         __syncthreads();
         float* kf = lds;                 // [acc + 1][Dk]
-        float* vf = lds + (acc + 1) * Dk;  // [acc + 1][Dv]
+        float* vf = lds + (acc + 1) * Dk;  // [acc + 1][ne]: this slice's dims of v
         la_rows_to_lds(a.pk, bf16, acc + 1, Dk,
                               [&](int t) { return ((static_cast<size_t>(b) * N + s_j[t]) * H + h) * Dk; }, kf, Dk);
-        la_rows_to_lds(a.pv, bf16, acc + 1, Dv,
-                              [&](int t) { return ((static_cast<size_t>(b) * N + s_j[t]) * H + h) * Dv; }, vf, Dv);
+        la_rows_to_lds(a.pv, bf16, acc + 1, ne,
+                              [&](int t) { return ((static_cast<size_t>(b) * N + s_j[t]) * H + h) * Dv + es0; }, vf,
+                              ne);
         __syncthreads();
-        // This thread's column d, rows e0, e0 + estep, ...: every load issued
-        // before the first update.
+        // This thread's column d, slice rows e0, e0 + estep, ...: every load
+        // issued before the first update.
         const float Av = exp2f(s_L[vstop]);
         const int d = tid % Dk, e0 = tid / Dk, estep = kLaThreads / Dk;
-        constexpr int kRows = kLaMaxD * kLaMaxD / kLaThreads;  // 64 at most
+        constexpr int kRows = kLaRows * kLaMaxD / kLaThreads;  // 16 at most (Dk = 128)
         float sv[kRows];
 #pragma unroll
         for (int r = 0; r < kRows; ++r) {
             const int e = e0 + r * estep;
-            sv[r] = e < Dv ? S[static_cast<size_t>(e) * Dk + d] : 0.f;
+            sv[r] = e < ne ? S[static_cast<size_t>(es0 + e) * Dk + d] : 0.f;
         }
 #pragma unroll
         for (int r = 0; r < kRows; ++r) {
             const int e = e0 + r * estep;
-            if (e < Dv) {
+            if (e < ne) {
                 float s = Av * sv[r];
-                for (int t = 0; t <= acc; ++t) s = fmaf(s_c[t] * vf[t * Dv + e], kf[t * Dk + d], s);
-                S[static_cast<size_t>(e) * Dk + d] = s;
+                for (int t = 0; t <= acc; ++t) s = fmaf(s_c[t] * vf[t * ne + e], kf[t * Dk + d], s);
+                S[static_cast<size_t>(es0 + e) * Dk + d] = s;
             }
         }
         __syncthreads();  // the workgroup's own state writes before its reads below
@@ -162,15 +168,15 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
     const int DkP = Dk + 1;               // padded rows: lanes on different rows hit different banks
     float* Qs = lds;                      // [N][Dk + 1]
     float* Ks = Qs + NMAX * (kLaMaxD + 1);
-    float* Vs = Ks + NMAX * (kLaMaxD + 1);  // [N][Dv]
-    float* W = Vs + NMAX * kLaMaxD;         // [N][N]
-    float* Sc = W + NMAX * NMAX;            // [Dv][kLaChunk + 1]
+    float* Vs = Ks + NMAX * (kLaMaxD + 1);  // [N][ne]: this slice's dims of v
+    float* W = Vs + NMAX * kLaRows;         // [N][N]
+    float* Sc = W + NMAX * NMAX;            // [ne][kLaChunk + 1]
     {
         auto rk = [&](int i) { return ((static_cast<size_t>(b) * N + i) * H + h) * Dk; };
-        auto rv = [&](int i) { return ((static_cast<size_t>(b) * N + i) * H + h) * Dv; };
+        auto rv = [&](int i) { return ((static_cast<size_t>(b) * N + i) * H + h) * Dv + es0; };
         la_rows_to_lds(a.q, bf16, N, Dk, rk, Qs, DkP);
         la_rows_to_lds(a.k, bf16, N, Dk, rk, Ks, DkP);
-        la_rows_to_lds(a.v, bf16, N, Dv, rv, Vs, Dv);
+        la_rows_to_lds(a.v, bf16, N, ne, rv, Vs, ne);
     }
     __syncthreads();
     // W[i][j] = A(j -> i] (q_i . k_j) for j on i's root path, else 0.
@@ -195,22 +201,23 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
         }
         W[x] = w;
     }
-    // Thread (e, group g): nodes g, g + G, ... with G = 256 / Dv groups.
-    const int e = tid % Dv, g = tid / Dv, G = kLaThreads / Dv;
-    constexpr int kPer = NMAX / 2 > 1 ? NMAX / 2 : 1;  // nodes per thread: NMAX / G, G >= 2
+    // Thread (e, group g): slice row e, nodes g, g + G, ... with G = 256 /
+    // kLaRows groups (threads of rows past ne idle).
+    const int e = tid % kLaRows, g = tid / kLaRows, G = kLaThreads / kLaRows;
+    constexpr int kPer = NMAX / (kLaThreads / kLaRows) > 1 ? NMAX / (kLaThreads / kLaRows) : 1;  // nodes per thread
     float acc[kPer];
 #pragma unroll
     for (int n = 0; n < kPer; ++n) acc[n] = 0.f;
-    // The state's 32-column chunks as 16-byte loads (four per thread for Dv =
-    // 128), the next chunk loaded while the current one is used.
-    constexpr int kS4 = kLaMaxD * kLaChunk / 4 / kLaThreads;
-    const int n4 = Dv * (kLaChunk / 4);
+    // The slice's 32-column chunks of the state as 16-byte loads (one per
+    // thread), the next chunk loaded while the current one is used.
+    constexpr int kS4 = (kLaRows * kLaChunk / 4 + kLaThreads - 1) / kLaThreads;
+    const int n4 = ne * (kLaChunk / 4);
     float4 sreg[kS4];
     auto load_chunk = [&](int c0) {
 #pragma unroll
         for (int j = 0; j < kS4; ++j) {
             const int x = min(tid + j * kLaThreads, n4 - 1), r = x / (kLaChunk / 4), c4 = x - r * (kLaChunk / 4);
-            sreg[j] = *reinterpret_cast<const float4*>(S + static_cast<size_t>(r) * Dk + c0 + 4 * c4);
+            sreg[j] = *reinterpret_cast<const float4*>(S + static_cast<size_t>(es0 + r) * Dk + c0 + 4 * c4);
         }
     };
     load_chunk(0);
@@ -230,7 +237,8 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
         }
         if (c0 + kLaChunk < Dk) load_chunk(c0 + kLaChunk);
         __syncthreads();
-        if constexpr (NMAX > 16) {
+        if (e >= ne) {  // a row past the slice (Dv not a multiple of kLaRows): nothing to add
+        } else if constexpr (NMAX > 16) {
             // Large trees, column by column: one state value feeds this
             // thread's kPer nodes as independent chains (a per-node branch
             // kept each node's 32-step chain apart, every step waiting out
@@ -261,12 +269,12 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
 #pragma unroll
     for (int n = 0; n < kPer; ++n) {
         const int i = g + n * G;
-        if (i < N) {
+        if (i < N && e < ne) {
             float o = exp2f(s_L[i]) * acc[n];
             const uint64_t m = s_anc[i];
             for (int j = 0; j <= i; ++j)
-                if ((m >> j) & 1ull) o = fmaf(W[i * N + j], Vs[j * Dv + e], o);
-            const size_t oi = ((static_cast<size_t>(b) * N + i) * H + h) * Dv + e;
+                if ((m >> j) & 1ull) o = fmaf(W[i * N + j], Vs[j * ne + e], o);
+            const size_t oi = ((static_cast<size_t>(b) * N + i) * H + h) * Dv + es0 + e;
             if (bf16)
                 static_cast<uint16_t*>(a.out)[oi] = static_cast<uint16_t>(f32_to_bf16_bits(o));
             else
@@ -276,7 +284,7 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
 }
 
 int launch_la(const LaArgs& a, hipStream_t stream) {
-    const dim3 grid(a.H, a.B);
+    const dim3 grid(a.H, a.B, (a.Dv + kLaRows - 1) / kLaRows);
     const bool small = !a.do_verify || a.N <= 16;
     if (a.do_commit) {
         if (small)
