@@ -149,6 +149,32 @@ def accept_bytes(w, accept_len, path):
     return rows * V * 4 + gathers + outputs
 
 
+def multidraft_bytes(w, accept_len, path):
+    """Algorithmic bytes of one multi-draft call with the given outcome: one
+    read of the target row of every node on the accepted path (its
+    statistics), three row passes per rejected child (the residual or target
+    row and the child's draft row read, the new residual written), and one
+    read of the row the last token is drawn from (T > 0)."""
+    import numpy as np
+
+    B, N, V = w.B, w.N, w.V
+    par = w.parent if w.parent is not None else np.tile(np.arange(-1, N - 1, dtype=np.int32), (B, 1))
+    rows = 0
+    for b in range(B):
+        a = int(accept_len[b])
+        nodes = [int(x) for x in path[b][:a + 1]]
+        for d, v in enumerate(nodes):
+            rows += 1
+            kids = [c for c in range(1, N) if int(par[b][c]) == v]
+            nxt = nodes[d + 1] if d < a else None
+            rej = sum(1 for c in kids if nxt is None or c < nxt)
+            if w.temperature > 0:
+                rows += 3 * rej
+        if w.temperature > 0:
+            rows += 1
+    return rows * V * 4
+
+
 def stored_traffic(kind, name, cid, khash):
     """Per-call HBM bytes from the stored counter file, or None when the file
     is missing or describes other kernel sources."""
@@ -516,7 +542,33 @@ def measure_extras(cfg, w, copies, acc_ws, timer, spg, dev):
         for c in copies:
             accept_multidraft(c)
         ms = timer(capture(accept_multidraft))["median_ms"]
-        out["multidraft_accept"] = {"us": ms * 1e3, "calls": "spec_accept_multidraft"}
+        mb = multidraft_bytes(w, copies[0]["al"].cpu().numpy(), copies[0]["path"].cpu().numpy())
+        out["multidraft_accept"] = {"us": ms * 1e3, "bytes": mb, "achieved_GBs": mb / (ms * 1e-3) / 1e9,
+                                    "frac": mb / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), "calls": "spec_accept_multidraft"}
+
+    if cfg["id"] == HEADLINE:
+        # A short multi-head (Hq = Hkv) chain: 6 query rows per slab, a third
+        # of one 16-row matrix tile; the KV stream bounds it all the same.
+        mB, mH, mD, mL, mN = 16, 32, 128, 4096, 6
+        mq = torch.randn(mB, mN, mH, mD, device=dev).to(torch.bfloat16)
+        mk = torch.randn(mB, mH, mL + mN, mD, device=dev).to(torch.bfloat16)
+        mv = torch.randn(mB, mH, mL + mN, mD, device=dev).to(torch.bfloat16)
+        mpl_t = torch.full((mB,), mL, dtype=torch.int32, device=dev)
+        mo = torch.empty_like(mq)
+        mdesc = sv.attn_desc(mB, mN, mH, mH, mD, mL + mN, torch.bfloat16)
+        mws = torch.empty(max(sv.spec_verify_attn_workspace_bytes(mdesc, mL), 16), dtype=torch.uint8, device=dev)
+
+        def mha(c):
+            sv.spec_verify_attn(mq, mk, mv, mpl_t, None, mL, out=mo, workspace=mws)
+
+        mha(None)
+        ms = timer(capture(mha))["median_ms"]
+        mbytes = (mB * mH * (mL + mN) * mD * 2 * 2) + 2 * mB * mN * mH * mD * 2
+        out["mha_short_chain"] = {
+            "workload": f"B={mB}, Hq=Hkv={mH}, D={mD}, bf16 KV prefix {mL}, K={mN - 1} chain (6 query rows per slab)",
+            "us": ms * 1e3, "bytes": mbytes, "achieved_GBs": mbytes / (ms * 1e-3) / 1e9,
+            "frac": mbytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), "calls": "spec_verify_attn",
+            "note": "one copy of the 1.07 GB KV, larger than the 256 MB Infinity Cache"}
 
     # Linear-attention verification of the same trees (16 heads, Dk = Dv =
     # 128, bf16 q/k/v, fp32 state), its factor commit, and both fused.

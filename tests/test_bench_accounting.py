@@ -90,3 +90,18 @@ def test_attention_flops_follow_root_paths():
     t = SimpleNamespace(dtype="bf16", prefix_len=np.array([7]), N=4, Hkv=1, D=8, B=1, Hq=2, is_chain=False,
                         parent=np.array([[-1, 0, 0, 1]]))
     assert bench.attn_flops(t) == 4 * 8 * 2 * (4 * 7 + 1 + 2 + 2 + 3)
+
+
+def test_multidraft_bytes_count_passes():
+    # chain 0-1-2: the child of 0 passes, the child of 1 is rejected: two
+    # statistics passes, three row passes for the rejection, one draw pass
+    w = SimpleNamespace(B=1, N=3, V=10, parent=None, temperature=1.0)
+    got = bench.multidraft_bytes(w, np.array([1]), np.array([[0, 1, -1]], dtype=np.int32))
+    assert got == (2 + 3 + 1) * 10 * 4
+    # tree 0 <- 1, 0 <- 2, 0 <- 3: children 1 and 2 rejected, 3 passes, 3 a leaf
+    t = SimpleNamespace(B=1, N=4, V=10, parent=np.array([[-1, 0, 0, 0]], dtype=np.int32), temperature=1.0)
+    got = bench.multidraft_bytes(t, np.array([1]), np.array([[0, 3, -1, -1]], dtype=np.int32))
+    assert got == (2 + 3 * 2 + 1) * 10 * 4
+    # greedy: statistics passes only
+    g = SimpleNamespace(B=1, N=4, V=10, parent=np.array([[-1, 0, 0, 0]], dtype=np.int32), temperature=0.0)
+    assert bench.multidraft_bytes(g, np.array([1]), np.array([[0, 3, -1, -1]], dtype=np.int32)) == 2 * 10 * 4
