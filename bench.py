@@ -52,6 +52,9 @@ CSRC = os.path.join(ROOT, "speculative_decoding_verification_tree_amd", "csrc")
 # from these sources.
 ATTN_SOURCES = ("attn.hip", "spec_common.h", "spec_internal.h")
 ACCEPT_SOURCES = ("accept.hip", "spec_common.h", "spec_internal.h")
+# The calls beside the path (truncated and multi-draft acceptance, linear
+# attention): one stored counter file per workload, keyed by these sources.
+EXTRA_SOURCES = ("accept.hip", "multidraft.hip", "linattn.hip", "spec_common.h", "spec_internal.h")
 
 
 def traffic_file(kind, name):
@@ -95,6 +98,23 @@ def kernel_source_hash():
 
 def accept_source_hash():
     return source_hash(ACCEPT_SOURCES)
+
+
+def extra_source_hash():
+    return source_hash(EXTRA_SOURCES)
+
+
+def stored_extra_traffic(name, cid):
+    """Per-call HBM bytes of the calls beside the path ({call: bytes}) from
+    the stored counter file, or {} when it is missing or stale."""
+    path = traffic_file("extras", name)
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        tr = json.load(f)
+    if tr.get("kernel_source_hash") != extra_source_hash() or tr.get("config") != cid:
+        return {}
+    return {k: v["bytes_per_call"] for k, v in tr.get("calls", {}).items()}
 
 
 def attn_bytes(w):
@@ -445,6 +465,14 @@ def measure(cid, args, dev, with_extras):
     }
     if with_extras:
         rec["extras"] = measure_extras(cfg, w, copies, acc_ws, Timer(torch, spg, reps), spg, dev)
+        # counter-measured bytes of each call (when stored for these sources)
+        ex_tr = stored_extra_traffic(cfg["name"], cid)
+        for call, key in (("filtered_accept", "filtered_accept"), ("multidraft_accept", "multidraft_accept"),
+                          ("la_verify", "linear_attention")):
+            ent = rec["extras"].get(key)
+            if ent is None:
+                continue
+            ent["traffic" if call != "la_verify" else "verify_traffic"] = ex_tr.get(call)
     del copies, attn_ws, acc_ws
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

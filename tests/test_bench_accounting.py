@@ -66,7 +66,7 @@ def test_stored_traffic_matches_each_workload():
     from workloads.configs import config
     import json
     found = 0
-    for kind in ("attn", "accept"):
+    for kind in ("attn", "accept", "extras"):
         for cid in (1, 2, 3, 4, 5):
             path = bench.traffic_file(kind, config(cid)["name"])
             if not os.path.exists(path):
@@ -75,7 +75,10 @@ def test_stored_traffic_matches_each_workload():
             with open(path) as f:
                 tr = json.load(f)
             assert tr["config"] == cid
-            assert tr["bytes_per_launch"] > 0
+            if kind == "extras":
+                assert all(v["bytes_per_call"] > 0 for v in tr["calls"].values())
+            else:
+                assert tr["bytes_per_launch"] > 0
             assert len(tr["kernel_source_hash"]) == len(bench.kernel_source_hash())
     assert found >= 1
 
