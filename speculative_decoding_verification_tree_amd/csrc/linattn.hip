@@ -7,10 +7,11 @@
 // none): S_t = alpha_t S_{t-1} + v_t k_t^T, o_t = S_t q_t, per (request,
 // head), S [Dv][Dk] fp32.
 //
-// One 256-thread workgroup per (head, request, slice of kLaRows state rows):
-// the rows e of S (the output dims) are independent in both phases, so a
-// (head, request) is spread over Dv / kLaRows workgroups, each recomputing
-// the small N x N score matrix.  Two optional phases:
+// One 256-thread workgroup per (head, request, slice of state rows): the
+// rows e of S (the output dims) are independent in both phases, so when
+// (head, request) pairs are too few to fill the chip a pair is spread over
+// Dv / 32 workgroups, each recomputing the small N x N score matrix.  Two
+// optional phases:
 //   commit: S <- A(-> v] S + sum_{j on the accepted path} A(j -> v] v_j k_j^T,
 //           the path's k, v and decay weights in LDS, every state element
 //           written once (in place; the workgroup owns its slab);
@@ -28,7 +29,9 @@ namespace specv {
 constexpr int kLaThreads = 256;
 constexpr int kLaMaxD = 128;
 constexpr int kLaChunk = 32;
-constexpr int kLaRows = 32;  // state rows (output dims) per workgroup
+// State rows (output dims) per workgroup: a slice of 32 when (head, request)
+// pairs are few, else the whole state (kLaMaxD).
+constexpr int kLaSliceRows = 32;
 
 // Rows [0, rows) of `cols` elements (bf16 or fp32, row t at global element
 // offset row_off(t)) into LDS dst[t * ldst + c], in rounds of kLaBatch
@@ -96,22 +99,23 @@ __device__ __forceinline__ void la_tree(const int32_t* parent, const float* alph
 // LDS floats for trees of at most NMAX nodes: commit (path factors k, v)
 // or verify (Q and K rows padded by one, V, the scores W, a 32-column chunk
 // of the state), whichever is larger.
-template <int NMAX, bool COMMIT>
+template <int NMAX, bool COMMIT, int ROWS>
 constexpr int la_lds_floats() {
-    constexpr int commit = COMMIT ? kMaxNodes * (kLaMaxD + kLaRows) : 0;
-    constexpr int verify = 2 * NMAX * (kLaMaxD + 1) + NMAX * kLaRows + NMAX * NMAX + kLaRows * (kLaChunk + 1);
+    constexpr int commit = COMMIT ? kMaxNodes * (kLaMaxD + ROWS) : 0;
+    constexpr int verify = 2 * NMAX * (kLaMaxD + 1) + NMAX * ROWS + NMAX * NMAX + ROWS * (kLaChunk + 1);
     return commit > verify ? commit : verify;
 }
 
 // COMMIT: the launch may commit (alone or before verifying); without it the
 // LDS is sized for verification only.
-template <int NMAX, bool COMMIT>
+template <int NMAX, bool COMMIT, int ROWS>
 __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
+    constexpr int kLaRows = ROWS;
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int Dk = a.Dk, Dv = a.Dv, H = a.H;
     const int es0 = blockIdx.z * kLaRows, ne = min(kLaRows, Dv - es0);  // this workgroup's state rows
     const bool bf16 = a.bf16 != 0;
-    __shared__ float lds[la_lds_floats<NMAX, COMMIT>()];
+    __shared__ float lds[la_lds_floats<NMAX, COMMIT, ROWS>()];
     __shared__ int s_par[kMaxNodes];
     __shared__ float s_L[kMaxNodes];
     __shared__ uint64_t s_anc[kMaxNodes];
@@ -283,20 +287,33 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
     }
 }
 
-int launch_la(const LaArgs& a, hipStream_t stream) {
-    const dim3 grid(a.H, a.B, (a.Dv + kLaRows - 1) / kLaRows);
+template <int ROWS>
+static void launch_la_rows(const LaArgs& a, hipStream_t stream) {
+    const dim3 grid(a.H, a.B, (a.Dv + ROWS - 1) / ROWS);
     const bool small = !a.do_verify || a.N <= 16;
     if (a.do_commit) {
         if (small)
-            hipLaunchKernelGGL((la_kernel<16, true>), grid, dim3(kLaThreads), 0, stream, a);
+            hipLaunchKernelGGL((la_kernel<16, true, ROWS>), grid, dim3(kLaThreads), 0, stream, a);
         else
-            hipLaunchKernelGGL((la_kernel<kMaxNodes, true>), grid, dim3(kLaThreads), 0, stream, a);
+            hipLaunchKernelGGL((la_kernel<kMaxNodes, true, ROWS>), grid, dim3(kLaThreads), 0, stream, a);
     } else {
         if (small)
-            hipLaunchKernelGGL((la_kernel<16, false>), grid, dim3(kLaThreads), 0, stream, a);
+            hipLaunchKernelGGL((la_kernel<16, false, ROWS>), grid, dim3(kLaThreads), 0, stream, a);
         else
-            hipLaunchKernelGGL((la_kernel<kMaxNodes, false>), grid, dim3(kLaThreads), 0, stream, a);
+            hipLaunchKernelGGL((la_kernel<kMaxNodes, false, ROWS>), grid, dim3(kLaThreads), 0, stream, a);
     }
+}
+
+int launch_la(const LaArgs& a, hipStream_t stream) {
+    // Slices only when the pairs leave most CUs idle (the slices recompute
+    // the score matrix, which costs more than it spreads once the chip is
+    // full: 64 requests x 16 heads ran slower sliced).
+    if (static_cast<long>(a.B) * a.H < 512)
+        launch_la_rows<kLaSliceRows>(a, stream);
+    else if (a.Dv <= 64)
+        launch_la_rows<64>(a, stream);
+    else
+        launch_la_rows<kLaMaxD>(a, stream);
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
 

@@ -70,6 +70,9 @@ CASES = [
     (2, 20, 2, 128, 64, "bf16", True, True),
     (4, 8, 8, 64, 64, "bf16", False, True),
     (1, 1, 2, 128, 128, "f32", False, True),
+    # 512 (request, head) pairs and more: one workgroup per pair, the whole state
+    (64, 8, 8, 128, 128, "bf16", False, True),
+    (32, 20, 16, 64, 64, "f32", True, True),
 ]
 
 

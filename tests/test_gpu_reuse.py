@@ -83,3 +83,37 @@ def test_graph_replay_matches_eager(cid, over):
         torch.cuda.synchronize()
     ref = oracle.tree_attn(w.q, w.k_cache, w.v_cache, w.prefix_len, None if w.is_chain else w.parent, w.dtype)
     check_attention(host_f64(eager[0]), ref, f"graph cfg{cid}")
+
+
+def test_outputs_written_in_full_and_nothing_past_them():
+    """Debug sentinels: the outputs start as a pattern no call writes (a NaN
+    payload for the attention, 0x7F7F7F7F for the acceptance) inside buffers
+    with a tail past the outputs' end.  Every output element must be written
+    (the path and the emitted tokens padded with -1) and the tails left as
+    they were."""
+    w = generate(scaled(4, batch=5, prefix_len=(50, 1300), vocab=7000), variant=3)
+    announce(f"output sentinels: cfg4 B={w.B} N={w.N}")
+    d = _dev_inputs(w)
+    pad = 4096
+    n_out = d["q"].numel()
+    sent_bf16 = torch.tensor([0x7FC1], dtype=torch.int16).view(torch.bfloat16).item()
+    big = torch.full((n_out + pad,), sent_bf16, dtype=d["q"].dtype, device="cuda")
+    out = big[:n_out].view(d["q"].shape)
+    sent_i = 0x7F7F7F7F
+    al_b = torch.full((w.B + pad,), sent_i, dtype=torch.int32, device="cuda")
+    path_b = torch.full((w.B * w.N + pad,), sent_i, dtype=torch.int32, device="cuda")
+    otok_b = torch.full((w.B * w.N + pad,), sent_i, dtype=torch.int32, device="cuda")
+    al, path, otok = al_b[:w.B], path_b[:w.B * w.N].view(w.B, w.N), otok_b[:w.B * w.N].view(w.B, w.N)
+    sv.spec_verify_attn(d["q"], d["k"], d["v"], d["pl"], d["par"], w.max_prefix_len, out=out)
+    sv.spec_accept_reject(d["lg"], d["dp"], d["tk"], d["par"], d["ua"], d["us"], w.temperature, al, path, otok)
+    torch.cuda.synchronize()
+    tail = big[n_out:].view(torch.int16)
+    assert (tail == 0x7FC1).all(), "attention wrote past its output"
+    assert not torch.isnan(out.float()).any(), "attention left output elements unwritten"
+    for name, buf, n in (("accept_len", al_b, w.B), ("path", path_b, w.B * w.N), ("out_tokens", otok_b, w.B * w.N)):
+        assert (buf[n:] == sent_i).all(), f"{name}: written past its end"
+        assert not (buf[:n] == sent_i).any(), f"{name}: elements left unwritten"
+    ref = oracle.tree_attn(w.q, w.k_cache, w.v_cache, w.prefix_len, None if w.is_chain else w.parent, w.dtype)
+    check_attention(host_f64(out), ref, "sentinels")
+    gpu = dict(accept_len=al.cpu().numpy(), path=path.cpu().numpy(), out_tokens=otok.cpu().numpy())
+    check_accept(w, gpu, oracle_accept(w))
