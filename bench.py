@@ -548,10 +548,12 @@ def measure_extras(cfg, w, copies, acc_ws, timer, spg, dev):
 
     if w.rule == "reject" and w.temperature > 0:
         fk, fp = 50, 0.9
+        filt_ws = torch.empty(max(sv.spec_accept_filtered_workspace_bytes(B, N, V), 16), dtype=torch.uint8,
+                              device=dev)
 
         def accept_filtered(c):
             sv.spec_accept_reject_filtered(c["logits"], c["draft"], c["tokens"], c["parent"], c["ua"], c["us"],
-                                           w.temperature, fk, fp, c["al"], c["path"], c["otok"], workspace=acc_ws)
+                                           w.temperature, fk, fp, c["al"], c["path"], c["otok"], workspace=filt_ws)
 
         for c in copies:
             accept_filtered(c)

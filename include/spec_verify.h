@@ -169,8 +169,21 @@ int spec_accept_reject_noalloc(int32_t batch, int32_t num_nodes, int32_t vocab, 
  * no nucleus; at T == 0 both are no-ops (the argmax is always kept).  The
  * nucleus masses are summed in 2^-44 fixed point over fp32 terms, so a
  * boundary within about 1e-6 of top_p may fall either way.  Arguments and
- * outputs otherwise as spec_accept_reject, same workspace.
+ * outputs otherwise as spec_accept_reject.  workspace: at least
+ * spec_accept_workspace_bytes; with top_k > 0, batch * num_nodes <= 65535
+ * and at least spec_accept_filtered_workspace_bytes, each row's selection is
+ * spread over the workgroups of its vocabulary chunks (each chunk leaves its
+ * top digits' counts and keys in the workspace for the row's finishing
+ * workgroup; nothing needs clearing), else, and for shapes of more than
+ * 65,536 (row, chunk) pairs, one workgroup selects per row; the results are
+ * identical.
  *   top_k >= 0; 0 < top_p <= 1, else SPEC_EINVAL */
+/* Workspace bytes with which spec_accept_reject_filtered splits each row's
+ * top-k selection over its vocabulary chunks: the plain acceptance
+ * workspace, then per (row, chunk) a 16-byte record, 64 digit counts and 256
+ * keys (1,296 bytes).  0 for shapes spec_accept_workspace_bytes rejects. */
+size_t spec_accept_filtered_workspace_bytes(int32_t batch, int32_t num_nodes, int32_t vocab);
+
 int spec_accept_reject_filtered(int32_t batch, int32_t num_nodes, int32_t vocab, const float* target_logits,
                                 const float* draft_probs, const int32_t* tokens, const int32_t* parent,
                                 const float* u_accept, const float* u_sample, float temperature, int32_t top_k,

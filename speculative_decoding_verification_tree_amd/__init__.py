@@ -15,6 +15,7 @@ from .api import (
     spec_accept_reject,
     spec_accept_reject_noalloc,
     spec_accept_reject_filtered,
+    spec_accept_filtered_workspace_bytes,
     spec_accept_typical,
     spec_accept_workspace_bytes,
     spec_commit_kv,
@@ -32,7 +33,7 @@ from ._native import LIB_PATH, SIGNATURES, lib, status_string
 
 __all__ = [
     "SpecError", "attn_desc", "spec_accept_multidraft", "spec_accept_multidraft_workspace_bytes", "spec_accept_reject", "spec_accept_reject_noalloc",
-    "spec_accept_reject_filtered", "spec_accept_typical", "spec_accept_workspace_bytes",
+    "spec_accept_reject_filtered", "spec_accept_filtered_workspace_bytes", "spec_accept_typical", "spec_accept_workspace_bytes",
     "spec_commit_kv", "spec_la_commit", "spec_la_verify", "spec_medusa_tree", "spec_medusa_tree_nodes", "spec_tree_positions", "spec_tree_rope",
     "spec_validate_tree", "spec_verify_attn",
     "spec_verify_attn_workspace_bytes", "LIB_PATH", "SIGNATURES", "lib", "status_string",

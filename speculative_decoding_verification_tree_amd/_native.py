@@ -18,6 +18,7 @@ SIGNATURES = {
     "spec_verify_attn_workspace_bytes": (_Z, [_P, _I]),
     "spec_verify_attn": (ctypes.c_int, [_P, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "spec_accept_workspace_bytes": (_Z, [_I, _I, _I]),
+    "spec_accept_filtered_workspace_bytes": (_Z, [_I, _I, _I]),
     "spec_accept_reject": (ctypes.c_int, [_I, _I, _I, _P, _P, _P, _P, _P, _P, _F, _P, _P, _P, _P, _Z, _P]),
     "spec_accept_reject_noalloc": (ctypes.c_int, [_I, _I, _I, _P, _P, _P, _P, _P, _P, _F, _P, _P, _P, _P]),
     "spec_accept_multidraft_workspace_bytes": (ctypes.c_size_t, [_I, _I]),

@@ -98,6 +98,10 @@ def spec_accept_workspace_bytes(batch, num_nodes, vocab):
     return int(_native.lib().spec_accept_workspace_bytes(int(batch), int(num_nodes), int(vocab)))
 
 
+def spec_accept_filtered_workspace_bytes(batch, num_nodes, vocab):
+    return int(_native.lib().spec_accept_filtered_workspace_bytes(int(batch), int(num_nodes), int(vocab)))
+
+
 def _accept_outputs(B, N, dev, accept_len, path, out_tokens):
     if accept_len is None:
         accept_len = torch.empty(B, dtype=torch.int32, device=dev)
@@ -168,7 +172,7 @@ def spec_accept_reject_filtered(target_logits, draft_probs, tokens, parent, u_ac
     _dev(u_sample, "u_sample", torch.float32)
     accept_len, path, out_tokens = _accept_outputs(B, N, target_logits.device, accept_len, path, out_tokens)
     if workspace is None:
-        workspace = torch.empty(max(spec_accept_workspace_bytes(B, N, V), 1), dtype=torch.uint8,
+        workspace = torch.empty(max(spec_accept_filtered_workspace_bytes(B, N, V), 1), dtype=torch.uint8,
                                 device=target_logits.device)
     rc = _native.lib().spec_accept_reject_filtered(B, N, V, _ptr(target_logits), _ptr(draft_probs), _ptr(tokens),
                                                    _ptr(parent), _ptr(u_accept), _ptr(u_sample), float(temperature),

@@ -92,7 +92,30 @@ struct AcceptArgs {
     float T, eps, delta;
     int top_k;    // 0: off
     float top_p;  // 1: off
+    // Truncation split over the chunks of each row (top_k > 0 and a
+    // workspace of spec_accept_filtered_workspace_bytes), else null.
+    struct ChunkRec* frec;  // [B*N][nchunk] per chunk: max, digit and key counts
+    uint32_t* fbins;        // [B*N][nchunk][kFBinCap] (digit << 20 | count) of the chunk's top digits
+    uint32_t* fkeys;        // [B*N][nchunk][kFKeyCap] the keys of those digits
 };
+
+struct ChunkRec {  // one chunk of a row, split truncation
+    float M;       // chunk max logit
+    int arg;       // its lowest index
+    int nbins;     // non-empty first digits at or above the chunk's top-k digit (> kFBinCap: too many)
+    int nkeys;     // keys of those digits (> kFKeyCap: too many)
+};
+
+// Per chunk: the non-empty first digits at or above the chunk's own top-k
+// digit, and their keys; a row with a chunk over either bound is redone
+// whole by its finishing workgroup.
+constexpr int kFBinCap = 64;  // (one a lane when gathered)
+constexpr int kFKeyCap = 256;
+static_assert(kFBinCap == 64 && kFKeyCap % 64 == 0, "the split finish gathers whole waves of entries");
+// Candidate keys the split finish holds in LDS (more: the row is redone whole).
+constexpr int kFCandRow = 4096;
+// (row, chunk) pairs of a split truncation: a bound on its grid and workspace.
+constexpr long kFMaxSlots = 65536;
 
 constexpr int kThreads = 256;
 
@@ -1026,23 +1049,24 @@ static int accept_ept(int B, int N, int V) {
 // fixed-point masses, so the kept mass comes out of the selection itself.
 constexpr int kFThreads = 1024;
 constexpr int kFWaves = kFThreads / 64;
+constexpr int kFSplitThreads = 256;
 constexpr int kFUnroll = 8;
 constexpr float kFixedOne = 17592186044416.0f;  // 2^44
 
 // f(x, l) for every element of the row, this thread's elements in ascending
 // order; kFUnroll loads are issued before the first f.
-template <class F>
+template <int NT, class F>
 __device__ __forceinline__ void for_row(const float* row, int V, bool vec4, F f) {
     const int tid = threadIdx.x;
     if (vec4) {
-        for (int base = 4 * tid; base < V; base += 4 * kFThreads * kFUnroll) {
+        for (int base = 4 * tid; base < V; base += 4 * NT * kFUnroll) {
             float4 v[kFUnroll];
 #pragma unroll
             for (int u = 0; u < kFUnroll; ++u)
-                v[u] = *reinterpret_cast<const float4*>(row + min(base + 4 * kFThreads * u, V - 4));
+                v[u] = *reinterpret_cast<const float4*>(row + min(base + 4 * NT * u, V - 4));
 #pragma unroll
             for (int u = 0; u < kFUnroll; ++u) {
-                const int x = base + 4 * kFThreads * u;
+                const int x = base + 4 * NT * u;
                 if (x < V) {
                     f(x, v[u].x);
                     f(x + 1, v[u].y);
@@ -1052,17 +1076,18 @@ __device__ __forceinline__ void for_row(const float* row, int V, bool vec4, F f)
             }
         }
     } else {
-        for (int base = tid; base < V; base += kFThreads * kFUnroll) {
+        for (int base = tid; base < V; base += NT * kFUnroll) {
             float v[kFUnroll];
 #pragma unroll
-            for (int u = 0; u < kFUnroll; ++u) v[u] = row[min(base + kFThreads * u, V - 1)];
+            for (int u = 0; u < kFUnroll; ++u) v[u] = row[min(base + NT * u, V - 1)];
 #pragma unroll
             for (int u = 0; u < kFUnroll; ++u)
-                if (base + kFThreads * u < V) f(base + kFThreads * u, v[u]);
+                if (base + NT * u < V) f(base + NT * u, v[u]);
         }
     }
 }
 
+template <int NT>
 __device__ __forceinline__ unsigned long long block_incl_scan_u64(unsigned long long v, unsigned long long* s_w,
                                                                   unsigned long long& total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1075,7 +1100,7 @@ __device__ __forceinline__ unsigned long long block_incl_scan_u64(unsigned long 
     if (lane == 63) s_w[wave] = v;
     __syncthreads();
     total = 0;
-    for (int k = 0; k < kFWaves; ++k) {
+    for (int k = 0; k < NT / 64; ++k) {
         if (k < wave) v += s_w[k];
         total += s_w[k];
     }
@@ -1087,14 +1112,15 @@ __device__ __forceinline__ unsigned long long block_incl_scan_u64(unsigned long 
 // running total first reaches need; *above is the total of the digits above
 // d.  need_frac > 0: need = ceil(need_frac * total of the bins) (nucleus
 // first step).
+template <int NT>
 __device__ __forceinline__ void radix_step(const unsigned long long* h, int nb, unsigned long long& need,
                                            double need_frac, int& d, unsigned long long& above,
                                            unsigned long long* s_w, int* s_d, unsigned long long* s_above) {
-    const int tid = threadIdx.x, per = nb / kFThreads;
+    const int tid = threadIdx.x, per = nb / NT;
     unsigned long long loc = 0;
     for (int j = 0; j < per; ++j) loc += h[nb - 1 - per * tid - j];
     unsigned long long total;
-    const unsigned long long incl = block_incl_scan_u64(loc, s_w, total);
+    const unsigned long long incl = block_incl_scan_u64<NT>(loc, s_w, total);
     if (need_frac > 0.0) {
         const double want = ceil(need_frac * static_cast<double>(total));
         need = want < 1.0 ? 1ull : (want > static_cast<double>(total) ? total : static_cast<unsigned long long>(want));
@@ -1142,36 +1168,142 @@ __device__ __forceinline__ void append_key(bool match, uint32_t key, uint32_t* c
 
 constexpr int kFCand = 16384;  // LDS candidate keys (64 KB)
 
-__global__ __launch_bounds__(kFThreads) void accept_filter(AcceptArgs a) {
-    const int rid = blockIdx.x;  // request * N + node
+// The truncation of row rid = request * N + node by one 1024-thread
+// workgroup.  split: the chunk passes have left the row max, the first digit
+// and the keys at or above it in the workspace; when those keys fit
+// (kFCandRow) the selection starts from them, else from the row.
+template <int NT>
+__device__ __forceinline__ void filter_row(const AcceptArgs& a, int rid, bool split) {
+    // LDS candidate keys: the whole-row workgroup keeps up to kFCand; the
+    // split finish needs at most kFCandRow (more go back to the row).
+    constexpr int CAP = NT == kFThreads ? kFCand : kFCandRow;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float* row = a.logits + static_cast<size_t>(rid) * a.V;
     const bool vec4 = a.vec4 != 0;
     __shared__ unsigned long long s_cnt[2048], s_mass[2048];
-    __shared__ uint32_t s_cand[kFCand];
-    __shared__ unsigned long long s_w[kFWaves];
-    __shared__ float s_m[kFWaves];
-    __shared__ int s_i[kFWaves];
+    __shared__ uint32_t s_cand[CAP];
+    __shared__ unsigned long long s_w[NT / 64];
+    __shared__ float s_m[NT / 64];
+    __shared__ int s_i[NT / 64];
     __shared__ int s_d, s_n;
     __shared__ unsigned long long s_above;
     const bool use_k = a.top_k > 0 && a.top_k < a.V, use_p = a.top_p < 1.f;
     constexpr int kShift[3] = {21, 10, 0};
     constexpr int kBits[3] = {11, 11, 10};
     auto clear = [&](int nb) {
-        for (int i = tid; i < nb; i += kFThreads) {
+        for (int i = tid; i < nb; i += NT) {
             s_cnt[i] = 0ull;
             s_mass[i] = 0ull;
         }
     };
 
+    // Split: the chunk records give the row max, their top digits' counts
+    // give the first digit d0 of the k-th largest key, and their keys of
+    // digit >= d0 are the candidates (every such key: d0 is at or above each
+    // chunk's own top-k digit, since the row's k-th largest key is at least
+    // any chunk's).
+    bool have = false;
+    int d0s = 0, n_split = 0;
+    unsigned long long need_s = 0ull;
+    float Ms = -INFINITY;
+    int args = 0x7fffffff;
+    if (split && use_k) {
+        __shared__ int s_ovf;
+        __shared__ int s_nb[kMaxChunks], s_nk[kMaxChunks];
+        const int nch = a.nchunk;
+        const ChunkRec* rec = a.frec + static_cast<size_t>(rid) * nch;
+        clear(2048);
+        if (tid == 0) {
+            s_ovf = 0;
+            s_n = 0;
+        }
+        for (int c = tid; c < nch; c += NT) {  // ascending chunks: the lowest index of the max
+            const ChunkRec r = rec[c];
+            if (r.M > Ms) {
+                Ms = r.M;
+                args = r.arg;
+            }
+            s_nb[c] = min(r.nbins, kFBinCap);
+            s_nk[c] = min(r.nkeys, kFKeyCap);
+            if (r.nbins > kFBinCap || r.nkeys > kFKeyCap) s_ovf = 1;
+        }
+        wave_argmax(Ms, args);
+        if (lane == 0) {
+            s_m[wave] = Ms;
+            s_i[wave] = args;
+        }
+        __syncthreads();
+        Ms = s_m[0];
+        args = s_i[0];
+        for (int k = 1; k < NT / 64; ++k)
+            if (s_m[k] > Ms || (s_m[k] == Ms && s_i[k] < args)) {
+                Ms = s_m[k];
+                args = s_i[k];
+            }
+        if (!s_ovf) {  // workgroup-uniform
+            // Wave w takes chunks w, w + NT/64, ... in groups of eight, lane
+            // j entry j (then j + 64, ...) of each: eight loads in flight per
+            // lane from clamped slots, the unused ones dropped.
+            constexpr int NW = NT / 64;
+            const uint32_t* bins = a.fbins + static_cast<size_t>(rid) * nch * kFBinCap;
+            for (int g0 = wave; g0 < nch; g0 += 8 * NW) {
+                uint32_t w[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int c = min(g0 + u * NW, nch - 1);
+                    w[u] = bins[c * kFBinCap + lane];  // (kFBinCap == 64: one entry a lane)
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int c = g0 + u * NW;
+                    if (c < nch && lane < s_nb[c])
+                        atomicAdd(&s_cnt[w[u] >> 20], static_cast<unsigned long long>(w[u] & 0xFFFFFu));
+                }
+            }
+            __syncthreads();
+            unsigned long long above;
+            need_s = static_cast<unsigned long long>(a.top_k);
+            radix_step<NT>(s_cnt, 2048, need_s, 0.0, d0s, above, s_w, &s_d, &s_above);
+            need_s -= above;
+            // the candidates: every chunk key of digit >= d0
+            const uint32_t* keys = a.fkeys + static_cast<size_t>(rid) * nch * kFKeyCap;
+            for (int g0 = wave; g0 < nch; g0 += 8 * NW) {
+                int most = 0;  // the group's largest key count (wave-uniform)
+#pragma unroll
+                for (int u = 0; u < 8; ++u) most = max(most, g0 + u * NW < nch ? s_nk[g0 + u * NW] : 0);
+                for (int j0 = 0; j0 < most; j0 += 64) {
+                    uint32_t kv[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int c = min(g0 + u * NW, nch - 1);
+                        kv[u] = keys[c * kFKeyCap + j0 + lane];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int c = g0 + u * NW;
+                        append_key(c < nch && j0 + lane < s_nk[c] && static_cast<int>(kv[u] >> kShift[0]) >= d0s, kv[u],
+                                   s_cand, &s_n, CAP);
+                    }
+                }
+            }
+            __syncthreads();
+            n_split = s_n;
+            have = n_split <= CAP;
+        }
+        __syncthreads();  // (every thread has read s_ovf and s_n before either is reused)
+    }
+    float M, best = -INFINITY;
+    int arg, bi = 0x7fffffff;
+    if (have) {
+        M = Ms;
+        arg = args;
+    } else {
     // Pass 1: the row max with its lowest index and, for top-k, the first
     // digit's count histogram (counts need no max).
     clear(2048);
     if (tid == 0) s_n = 0;
     __syncthreads();
-    float best = -INFINITY;
-    int bi = 0x7fffffff;
-    for_row(row, a.V, vec4, [&](int x, float l) {
+    for_row<NT>(row, a.V, vec4, [&](int x, float l) {
         if (l > best) {
             best = l;
             bi = x;
@@ -1184,24 +1316,25 @@ __global__ __launch_bounds__(kFThreads) void accept_filter(AcceptArgs a) {
         s_i[wave] = bi;
     }
     __syncthreads();
-    float M = s_m[0];
-    int arg = s_i[0];
-    for (int k = 1; k < kFWaves; ++k)
+    M = s_m[0];
+    arg = s_i[0];
+    for (int k = 1; k < NT / 64; ++k)
         if (s_m[k] > M || (s_m[k] == M && s_i[k] < arg)) {
             M = s_m[k];
             arg = s_i[k];
         }
+    }
     const float c2 = 1.4426950408889634f / a.T;
     auto mass_of = [&](float l) { return __float2ull_rn(__builtin_amdgcn_exp2f((l - M) * c2) * kFixedOne); };
 
     // The remaining digits of a selection, from round r0 on, over the keys
     // matching (prefix, pmask) and >= floor_key: from the LDS candidates when
-    // they all fit (n <= kFCand), else from the row.  by_mass selects where the
+    // they all fit (n <= CAP), else from the row.  by_mass selects where the
     // mass from the top reaches need, else where the count does.  Adds to kept
     // the mass of the candidates >= the selected key.
     auto finish = [&](int r0, uint32_t prefix, uint32_t pmask, bool by_mass, uint32_t floor_key,
                       unsigned long long need, int n, unsigned long long& kept, double need_frac) {
-        const bool lds = n <= kFCand;
+        const bool lds = n <= CAP;
         for (int r = r0; r < 3; ++r) {
             const int nb = 1 << kBits[r];
             clear(nb);
@@ -1214,22 +1347,22 @@ __global__ __launch_bounds__(kFThreads) void accept_filter(AcceptArgs a) {
                 }
             };
             if (lds) {
-                for (int i = tid; i < n; i += kFThreads) add(s_cand[i], key_logit(s_cand[i]));
+                for (int i = tid; i < n; i += NT) add(s_cand[i], key_logit(s_cand[i]));
             } else {
-                for_row(row, a.V, vec4, [&](int, float l) { add(logit_key(l), l); });
+                for_row<NT>(row, a.V, vec4, [&](int, float l) { add(logit_key(l), l); });
             }
             __syncthreads();
             int d;
             unsigned long long above;
-            radix_step(by_mass ? s_mass : s_cnt, nb, need, r == 0 ? need_frac : 0.0, d, above, s_w, &s_d, &s_above);
+            radix_step<NT>(by_mass ? s_mass : s_cnt, nb, need, r == 0 ? need_frac : 0.0, d, above, s_w, &s_d, &s_above);
             need -= above;
             if (by_mass) {
                 kept += above;
             } else {
                 unsigned long long mine = 0ull, tot;
-                for (int i = tid; i < nb; i += kFThreads)
+                for (int i = tid; i < nb; i += NT)
                     if (i > d) mine += s_mass[i];
-                (void)block_incl_scan_u64(mine, s_w, tot);
+                (void)block_incl_scan_u64<NT>(mine, s_w, tot);
                 kept += tot;
             }
             if (r == 2) kept += s_mass[d];
@@ -1246,37 +1379,53 @@ __global__ __launch_bounds__(kFThreads) void accept_filter(AcceptArgs a) {
         if (tid == 0) s_n = 0;
         __syncthreads();
         unsigned long long mine = 0ull;
-        for_row(row, a.V, vec4, [&](int, float l) {
+        for_row<NT>(row, a.V, vec4, [&](int, float l) {
             const uint32_t key = logit_key(l);
             const int dig = static_cast<int>(key >> kShift[0]);
             if (dig > d0 && key >= floor_key) mine += mass_of(l);
-            append_key((also_above ? dig >= d0 : dig == d0) && key >= floor_key, key, s_cand, &s_n, kFCand);
+            append_key((also_above ? dig >= d0 : dig == d0) && key >= floor_key, key, s_cand, &s_n, CAP);
         });
         unsigned long long tot;
-        (void)block_incl_scan_u64(mine, s_w, tot);  // (its barriers also publish s_n)
+        (void)block_incl_scan_u64<NT>(mine, s_w, tot);  // (its barriers also publish s_n)
         mass_above = tot;
         return s_n;
     };
 
     uint32_t tau = 0u;
     unsigned long long kept = 0ull;
-    int n_k = kFCand + 1;  // keys >= the top-k threshold held in LDS (when <= kFCand)
+    int n_k = CAP + 1;  // keys >= the top-k threshold held in LDS (when <= CAP)
     if (use_k) {
         // first digit from the pass-1 counts, then the rest from its keys;
         // with a nucleus to follow, the keys above the digit (fewer than k)
         // are collected too, so that the nucleus needs no further pass
         unsigned long long need = static_cast<unsigned long long>(a.top_k);
         int d0;
-        unsigned long long above;
-        radix_step(s_cnt, 2048, need, 0.0, d0, above, s_w, &s_d, &s_above);
-        need -= above;
         unsigned long long mass_above;
-        const int n = collect(d0, 0u, use_p, mass_above);
+        int n;
+        if (have) {
+            // the chunks' candidates (in LDS): every key of digit >= d0
+            d0 = d0s;
+            need = need_s;
+            n = n_split;
+            unsigned long long mine = 0ull;
+            for (int i = tid; i < n; i += NT) {
+                const uint32_t key = s_cand[i];
+                if (static_cast<int>(key >> kShift[0]) > d0) mine += mass_of(key_logit(key));
+            }
+            unsigned long long tot;
+            (void)block_incl_scan_u64<NT>(mine, s_w, tot);
+            mass_above = tot;
+        } else {
+            unsigned long long above;
+            radix_step<NT>(s_cnt, 2048, need, 0.0, d0, above, s_w, &s_d, &s_above);
+            need -= above;
+            n = collect(d0, 0u, use_p, mass_above);
+        }
         kept = mass_above;
         tau = finish(1, static_cast<uint32_t>(d0) << kShift[0], 0x7FFu << kShift[0], false, 0u, need, n, kept, 0.0);
         if (use_p) n_k = n;
     }
-    if (use_p && n_k <= kFCand) {
+    if (use_p && n_k <= CAP) {
         // the nucleus over the top-k-kept keys, all in LDS
         kept = 0ull;
         tau = finish(0, 0u, 0u, true, tau, 0ull, n_k, kept, static_cast<double>(a.top_p));
@@ -1285,7 +1434,7 @@ __global__ __launch_bounds__(kFThreads) void accept_filter(AcceptArgs a) {
         clear(2048);
         __syncthreads();
         const uint32_t floor_key = tau;
-        for_row(row, a.V, vec4, [&](int, float l) {
+        for_row<NT>(row, a.V, vec4, [&](int, float l) {
             const uint32_t key = logit_key(l);
             if (key >= floor_key) atomicAdd(&s_mass[key >> kShift[0]], mass_of(l));
         });
@@ -1293,7 +1442,7 @@ __global__ __launch_bounds__(kFThreads) void accept_filter(AcceptArgs a) {
         unsigned long long need = 0ull;
         int d0;
         unsigned long long above;
-        radix_step(s_mass, 2048, need, static_cast<double>(a.top_p), d0, above, s_w, &s_d, &s_above);
+        radix_step<NT>(s_mass, 2048, need, static_cast<double>(a.top_p), d0, above, s_w, &s_d, &s_above);
         need -= above;
         unsigned long long mass_above;
         const int n = collect(d0, floor_key, false, mass_above);
@@ -1313,6 +1462,117 @@ __global__ __launch_bounds__(kFThreads) void accept_filter(AcceptArgs a) {
     }
 }
 
+__global__ __launch_bounds__(kFThreads) void accept_filter(AcceptArgs a) { filter_row<kFThreads>(a, blockIdx.x, false); }
+
+// Split truncation (top-k, then the nucleus), two launches:
+//   filt_chunk   grid (chunk, row): the chunk's max with its lowest index,
+//                its first-digit counts (LDS), the digit d_c where its own
+//                count from the top reaches top_k, and the non-empty digits
+//                at or above d_c with their counts and keys, into the
+//                chunk's slots of the workspace (no atomics outside LDS);
+//   accept_filter_split  grid row: sums the chunks' digit counts, finds the
+//                row's first digit d0 and gathers the chunks' keys of digit
+//                >= d0, then selects as one workgroup does over a whole row.
+// The counts, the digit, the candidate set and the fixed-point masses are
+// the same integers as in one workgroup's passes, so the records are
+// identical.
+template <int EPT>
+__global__ __launch_bounds__(kThreads) void filt_chunk(AcceptArgs a) {
+    const int c = blockIdx.x, rid = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    __shared__ uint32_t s_h[2048];
+    __shared__ WaveRed s_red;
+    __shared__ uint32_t s_wt[kThreads / 64];
+    __shared__ int s_dc, s_nb, s_nk;
+    const float* row = a.logits + static_cast<size_t>(rid) * a.V;
+    const int x0 = c * a.chunk, x1 = min(x0 + a.chunk, a.V);
+    const bool vec4 = a.vec4 != 0;
+    const Vals<EPT> v = load_chunk<EPT, true>(row, x0, x1, vec4, -INFINITY);
+    for (int i = tid; i < 2048; i += kThreads) s_h[i] = 0u;
+    if (tid == 0) {
+        s_dc = 0;
+        s_nb = 0;
+        s_nk = 0;
+    }
+    float M;
+    int arg;
+    double S, A2;
+    chunk_reduce<EPT, false, true, false>(v, x0, x1, vec4, 0.f, M, arg, S, A2, &s_red);  // (its barrier orders the clear)
+    const int lim = x1 - (x0 + (vec4 ? 4 * tid : tid));
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+        if (elem_off(e, vec4) < lim) atomicAdd(&s_h[logit_key(v.v[e]) >> 21], 1u);
+    __syncthreads();
+    // d_c: thread t sums the eight digits 2047 - 8t - 7 .. 2047 - 8t; a
+    // block scan from the top finds where the chunk's count reaches k (a
+    // chunk of fewer than k keys keeps d_c = 0: all of its digits).
+    constexpr int kPer = 2048 / kThreads;
+    uint32_t mine = 0u;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) mine += s_h[2047 - kPer * tid - j];
+    uint32_t incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) s_wt[wv] = incl;
+    __syncthreads();
+    for (int w = 0; w < wv; ++w) incl += s_wt[w];
+    const uint32_t k = static_cast<uint32_t>(a.top_k), excl = incl - mine;
+    if (excl < k && k <= incl) {  // the crossing lies in this thread's digits
+        uint32_t run = excl;
+        for (int j = 0; j < kPer; ++j) {
+            const int bin = 2047 - kPer * tid - j;
+            run += s_h[bin];
+            if (run >= k) {
+                s_dc = bin;
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    const int dc = s_dc;
+    const size_t slot = static_cast<size_t>(rid) * a.nchunk + c;
+    uint32_t* bins = a.fbins + slot * kFBinCap;
+    for (int i = tid; i < 2048; i += kThreads) {
+        const uint32_t n = s_h[i];
+        if (n && i >= dc) {
+            const int at = atomicAdd(&s_nb, 1);
+            if (at < kFBinCap) bins[at] = (static_cast<uint32_t>(i) << 20) | n;
+        }
+    }
+    // The keys of those digits: every element's ballot first, one LDS
+    // atomic for the wave's total, then each key at its place.
+    uint32_t* keys = a.fkeys + slot * kFKeyCap;
+    uint64_t m[EPT];
+    int total = 0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        m[e] = __ballot(elem_off(e, vec4) < lim && static_cast<int>(logit_key(v.v[e]) >> 21) >= dc);
+        total += __popcll(m[e]);
+    }
+    if (total > 0) {  // wave-uniform
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&s_nk, total);
+        base = __shfl(base, 0);
+        const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int at = base + __popcll(m[e] & below);
+            if (((m[e] >> lane) & 1ull) && at < kFKeyCap) keys[at] = logit_key(v.v[e]);
+            base += __popcll(m[e]);
+        }
+    }
+    __syncthreads();
+    if (tid == 0) a.frec[slot] = ChunkRec{M, arg, min(s_nb, kFBinCap + 1), min(s_nk, kFKeyCap + 1)};
+}
+
+// (from at most kFCandRow candidates: four waves keep the selection's
+// many barriers cheap)
+__global__ __launch_bounds__(kFSplitThreads) void accept_filter_split(AcceptArgs a) {
+    filter_row<kFSplitThreads>(a, blockIdx.x, true);
+}
+
 // ---------------------------------------------------------------------------
 AcceptPlan plan_accept(int B, int N, int V) {
     AcceptPlan p{};
@@ -1326,6 +1586,14 @@ AcceptPlan plan_accept(int B, int N, int V) {
     p.off_cstat = off;
     off = align_up(off + static_cast<size_t>(B) * p.nchunk * sizeof(ChunkStat), 256);
     p.ws_bytes = off;
+    const size_t slots = static_cast<size_t>(B) * N * p.nchunk;
+    p.off_frec = off;
+    off = align_up(off + slots * sizeof(ChunkRec), 256);
+    p.off_fbins = off;
+    off = align_up(off + slots * kFBinCap * sizeof(uint32_t), 256);
+    p.off_fkeys = off;
+    off = align_up(off + slots * kFKeyCap * sizeof(uint32_t), 256);
+    p.ws_filt_bytes = off;
     return p;
 }
 
@@ -1333,7 +1601,11 @@ int max_accept_vocab() { return kMaxChunks * 32 * kThreads; }
 
 template <int EPT, bool FILT>
 static int launch_accept_ept(const AcceptArgs& a, const AcceptPlan& p, hipStream_t stream) {
-    if (FILT) {  // every row's truncation (the stop row may be a leaf)
+    if (FILT && a.frec) {  // every row's truncation, each row over its chunks
+        hipLaunchKernelGGL((filt_chunk<EPT>), dim3(p.nchunk, a.B * a.N), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(accept_filter_split, dim3(a.B * a.N), dim3(kFSplitThreads), 0, stream, a);
+        if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+    } else if (FILT) {  // every row's truncation (the stop row may be a leaf)
         hipLaunchKernelGGL(accept_filter, dim3(a.B * a.N), dim3(kFThreads), 0, stream, a);
         if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     } else if (a.N > 1) {
@@ -1363,7 +1635,7 @@ int launch_accept(int rule, int B, int N, int V, const float* logits, const floa
                   const int32_t* tokens, const int32_t* parent, const float* u_accept,
                   const float* u_sample, float temperature, float epsilon, float delta,
                   int32_t* accept_len, int32_t* path, int32_t* out_tokens, void* workspace,
-                  const AcceptPlan& p, hipStream_t stream, int top_k, float top_p) {
+                  const AcceptPlan& p, hipStream_t stream, int top_k, float top_p, bool split_filter) {
     AcceptArgs a;
     a.logits = logits;
     a.draft = draft;
@@ -1397,6 +1669,11 @@ int launch_accept(int rule, int B, int N, int V, const float* logits, const floa
     // Truncation applies to the rejection rule at T > 0 (at T = 0 the target
     // is the argmax, which every truncation keeps).
     const bool filt = rule == 0 && temperature > 0.f && (a.top_k > 0 || a.top_p < 1.f);
+    // The chunk passes find the top-k digit; a nucleus alone stays whole-row.
+    const bool split = filt && split_filter && a.top_k > 0 && static_cast<long>(B) * N * p.nchunk <= kFMaxSlots;
+    a.frec = split ? reinterpret_cast<ChunkRec*>(ws + p.off_frec) : nullptr;
+    a.fbins = split ? reinterpret_cast<uint32_t*>(ws + p.off_fbins) : nullptr;
+    a.fkeys = split ? reinterpret_cast<uint32_t*>(ws + p.off_fkeys) : nullptr;
     static_assert(sizeof(RowRec) <= sizeof(RowStat), "row records reuse the row-statistics space");
     switch (p.chunk / kThreads) {
         case 8: return filt ? launch_accept_ept<8, true>(a, p, stream) : launch_accept_ept<8, false>(a, p, stream);

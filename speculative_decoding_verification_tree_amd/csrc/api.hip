@@ -92,6 +92,13 @@ size_t spec_accept_workspace_bytes(int32_t batch, int32_t num_nodes, int32_t voc
     return plan_accept(batch, num_nodes, vocab).ws_bytes;
 }
 
+size_t spec_accept_filtered_workspace_bytes(int32_t batch, int32_t num_nodes, int32_t vocab) {
+    if (batch < 1 || batch > 65535 || num_nodes < 1 || num_nodes > kMaxNodes || vocab < 1 ||
+        vocab > max_accept_vocab())
+        return 0;
+    return plan_accept(batch, num_nodes, vocab).ws_filt_bytes;
+}
+
 size_t spec_accept_multidraft_workspace_bytes(int32_t batch, int32_t vocab) {
     if (batch < 1 || batch > 65535 || vocab < 1 || vocab > max_accept_vocab()) return 0;
     return multidraft_workspace_bytes(batch, vocab);
@@ -157,9 +164,12 @@ int spec_accept_reject_filtered(int32_t batch, int32_t num_nodes, int32_t vocab,
     if (static_cast<long long>(batch) * num_nodes > 0x7fffffffLL) return SPEC_EUNSUPPORTED;
     const AcceptPlan plan = plan_accept(batch, num_nodes, vocab);
     if (!workspace || workspace_bytes < plan.ws_bytes) return SPEC_EWORKSPACE;
+    // (the chunk kernels put the rows on the grid's second axis)
+    const bool split = workspace_bytes >= plan.ws_filt_bytes && aligned16(workspace) &&
+                       static_cast<long long>(batch) * num_nodes <= 65535;
     return launch_accept(0, batch, num_nodes, vocab, target_logits, draft_probs, tokens, parent, u_accept,
                          u_sample, temperature, 0.f, 0.f, accept_len, path, out_tokens, workspace, plan,
-                         static_cast<hipStream_t>(stream), top_k, top_p);
+                         static_cast<hipStream_t>(stream), top_k, top_p, split);
 }
 
 int spec_accept_multidraft(int32_t batch, int32_t num_nodes, int32_t vocab, const float* target_logits,

@@ -71,26 +71,39 @@ __device__ __forceinline__ void la_rows_to_lds(const void* src, bool bf16, int r
     }
 }
 
-// Root-path structure of request b's tree of N nodes (thread 0, nodes in
-// index order, parents first): L[i] = log2 of the decay product over the
-// path root .. i, anc[i] = the path's node mask.
+// Root-path structure of request b's tree of N nodes: L[i] = log2 of the
+// decay product over the path root .. i, anc[i] = the path's node mask.
+// One lane per node (wave 0) and pointer doubling: after round r a lane
+// holds the sum and mask over its 2^r nearest path nodes and the node 2^r
+// above it, so six rounds cover 64 levels (a walk from the root would be
+// one dependent LDS round trip per node).
 __device__ __forceinline__ void la_tree(const int32_t* parent, const float* alpha, int b, int N, int H, int h,
-                                        int* s_par, float* s_L, uint64_t* s_anc) {
-    // Every node's parent and log2 decay loaded at once (one thread per
-    // node), then one thread walks the nodes in index order from LDS: the
-    // walk's loads would otherwise be one dependent round trip per node.
+                                        float* s_L, uint64_t* s_anc) {
     const int i = threadIdx.x;
-    if (i < N) {
-        const int p = tree_parent(parent, N, b, i);
-        s_par[i] = p >= 0 && p < i ? p : -1;  // out-of-contract parents read as roots
-        s_L[i] = alpha ? __log2f(alpha[(static_cast<size_t>(b) * N + i) * H + h]) : 0.f;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        for (int n = 0; n < N; ++n) {
-            const int pp = s_par[n];
-            s_L[n] += pp >= 0 ? s_L[pp] : 0.f;
-            s_anc[n] = (pp >= 0 ? s_anc[pp] : 0ull) | (1ull << n);
+    if (i < 64) {
+        int up = -1;
+        float Ls = 0.f;
+        if (i < N) {
+            const int p = tree_parent(parent, N, b, i);
+            up = p >= 0 && p < i ? p : -1;  // out-of-contract parents read as roots
+            Ls = alpha ? __log2f(alpha[(static_cast<size_t>(b) * N + i) * H + h]) : 0.f;
+        }
+        uint64_t anc = 1ull << i;
+#pragma unroll
+        for (int r = 0; r < 6; ++r) {
+            const int u = up >= 0 ? up : i;
+            const float Lu = __shfl(Ls, u);
+            const uint32_t alo = __shfl(static_cast<uint32_t>(anc), u), ahi = __shfl(static_cast<uint32_t>(anc >> 32), u);
+            const int uu = __shfl(up, u);
+            if (up >= 0) {
+                Ls += Lu;
+                anc |= static_cast<uint64_t>(alo) | (static_cast<uint64_t>(ahi) << 32);
+                up = uu;
+            }
+        }
+        if (i < N) {
+            s_L[i] = Ls;
+            s_anc[i] = anc;
         }
     }
     __syncthreads();
@@ -116,16 +129,16 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
     const int es0 = blockIdx.z * kLaRows, ne = min(kLaRows, Dv - es0);  // this workgroup's state rows
     const bool bf16 = a.bf16 != 0;
     __shared__ float lds[la_lds_floats<NMAX, COMMIT, ROWS>()];
-    __shared__ int s_par[kMaxNodes];
     __shared__ float s_L[kMaxNodes];
     __shared__ uint64_t s_anc[kMaxNodes];
     __shared__ float s_c[kMaxNodes];
     __shared__ int s_j[kMaxNodes];
+    __shared__ int s_off[kMaxNodes + 1];
     float* S = a.state + (static_cast<size_t>(b) * H + h) * Dv * Dk;
 
     if (COMMIT && a.do_commit) {
         const int N = a.pN;
-        la_tree(a.pparent, a.palpha, b, N, H, h, s_par, s_L, s_anc);
+        la_tree(a.pparent, a.palpha, b, N, H, h, s_L, s_anc);
         // (device data: out-of-range entries are clamped into the tree)
         const int acc = min(max(a.pacc[b], 0), N - 1);
         const int vstop = min(max(a.ppath[static_cast<size_t>(b) * N + acc], 0), N - 1);
@@ -168,7 +181,7 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
     if (!a.do_verify) return;
 
     const int N = a.N;
-    la_tree(a.parent, a.alpha, b, N, H, h, s_par, s_L, s_anc);
+    la_tree(a.parent, a.alpha, b, N, H, h, s_L, s_anc);
     const int DkP = Dk + 1;               // padded rows: lanes on different rows hit different banks
     float* Qs = lds;                      // [N][Dk + 1]
     float* Ks = Qs + NMAX * (kLaMaxD + 1);
@@ -183,27 +196,46 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
         la_rows_to_lds(a.v, bf16, N, ne, rv, Vs, ne);
     }
     __syncthreads();
-    // W[i][j] = A(j -> i] (q_i . k_j) for j on i's root path, else 0.
-    for (int x = tid; x < N * N; x += kLaThreads) {
-        const int i = x / N, j = x - i * N;
-        float w = 0.f;
-        if ((s_anc[i] >> j) & 1ull) {
-            // four independent partial sums, eight LDS reads per round in
-            // flight (one wave per SIMD here: a single dependent chain
-            // waited out every read's latency)
-            float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
-            const float* qi = Qs + i * DkP;
-            const float* kj = Ks + j * DkP;
-#pragma unroll 4
-            for (int d = 0; d < Dk; d += 4) {
-                d0 = fmaf(qi[d], kj[d], d0);
-                d1 = fmaf(qi[d + 1], kj[d + 1], d1);
-                d2 = fmaf(qi[d + 2], kj[d + 2], d2);
-                d3 = fmaf(qi[d + 3], kj[d + 3], d3);
-            }
-            w = exp2f(s_L[i] - s_L[j]) * ((d0 + d1) + (d2 + d3));
+    // W[i][j] = A(j -> i] (q_i . k_j) for j on i's root path (the other
+    // entries are never read).  The (node, ancestor) pairs are numbered
+    // node by node, s_off[i] the first pair of node i, and dealt out one per
+    // thread: a tree has far fewer pairs than N * N entries.
+    if (tid < 64) {
+        int v = tid < N ? __popcll(s_anc[tid]) : 0;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(v, o);
+            if (tid >= o) v += t;
         }
-        W[x] = w;
+        s_off[tid + 1] = v;
+        if (tid == 0) s_off[0] = 0;
+    }
+    __syncthreads();
+    for (int pr = tid; pr < s_off[N]; pr += kLaThreads) {
+        int lo = 0, hi = N - 1;  // node i: the last with s_off[i] <= pr
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_off[mid] <= pr) lo = mid;
+            else hi = mid - 1;
+        }
+        const int i = lo;
+        uint64_t m = s_anc[i];
+        for (int r = pr - s_off[i]; r > 0; --r) m &= m - 1ull;  // drop the lower ancestors
+        const int j = __ffsll(static_cast<long long>(m)) - 1;
+        // four independent partial sums, eight LDS reads per round in
+        // flight (one wave per SIMD here: a single dependent chain waited
+        // out every read's latency)
+        float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+        const float* qi = Qs + i * DkP;
+        const float* kj = Ks + j * DkP;
+#pragma unroll 4
+        for (int d = 0; d < Dk; d += 4) {
+            d0 = fmaf(qi[d], kj[d], d0);
+            d1 = fmaf(qi[d + 1], kj[d + 1], d1);
+            d2 = fmaf(qi[d + 2], kj[d + 2], d2);
+            d3 = fmaf(qi[d + 3], kj[d + 3], d3);
+        }
+        W[i * N + j] = exp2f(s_L[i] - s_L[j]) * ((d0 + d1) + (d2 + d3));
     }
     // Thread (e, group g): slice row e, nodes g, g + G, ... with G = 256 /
     // kLaRows groups (threads of rows past ne idle).
@@ -275,9 +307,10 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
         const int i = g + n * G;
         if (i < N && e < ne) {
             float o = exp2f(s_L[i]) * acc[n];
-            const uint64_t m = s_anc[i];
-            for (int j = 0; j <= i; ++j)
-                if ((m >> j) & 1ull) o = fmaf(W[i * N + j], Vs[j * ne + e], o);
+            for (uint64_t m = s_anc[i]; m != 0ull; m &= m - 1ull) {  // the ancestors j, ascending
+                const int j = __ffsll(static_cast<long long>(m)) - 1;
+                o = fmaf(W[i * N + j], Vs[j * ne + e], o);
+            }
             const size_t oi = ((static_cast<size_t>(b) * N + i) * H + h) * Dv + es0 + e;
             if (bf16)
                 static_cast<uint16_t*>(a.out)[oi] = static_cast<uint16_t>(f32_to_bf16_bits(o));

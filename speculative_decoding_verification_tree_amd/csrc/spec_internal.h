@@ -39,6 +39,8 @@ struct AcceptPlan {
     int chunk;   // vocabulary entries per chunk
     int nchunk;
     size_t off_rowstat, off_dec, off_cstat, ws_bytes;
+    // the truncation split over chunks, past ws_bytes
+    size_t off_frec, off_fbins, off_fkeys, ws_filt_bytes;
 };
 
 AcceptPlan plan_accept(int B, int N, int V);
@@ -48,7 +50,8 @@ int launch_accept(int rule, int B, int N, int V, const float* logits, const floa
                   const int32_t* tokens, const int32_t* parent, const float* u_accept,
                   const float* u_sample, float temperature, float epsilon, float delta,
                   int32_t* accept_len, int32_t* path, int32_t* out_tokens, void* workspace,
-                  const AcceptPlan& plan, hipStream_t stream, int top_k = 0, float top_p = 1.f);
+                  const AcceptPlan& plan, hipStream_t stream, int top_k = 0, float top_p = 1.f,
+                  bool split_filter = false);
 
 size_t multidraft_workspace_bytes(int B, int V);
 int launch_accept_multidraft(int B, int N, int V, const float* logits, const float* draft, const int32_t* tokens,

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     lib = sv.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -167,6 +167,18 @@ def test_filtered_accept_errors():
     assert _filt(N=65) == EINVAL
     assert _filt(ws_bytes=sv.lib().spec_accept_workspace_bytes(2, 6, 1000) - 1) == EWORKSPACE
     assert _filt(B=0) == OK
+
+
+def test_filtered_workspace_extends_the_plain_one():
+    lib = sv.lib()
+    for B, N, V in ((2, 6, 1000), (1, 6, 128256), (64, 8, 128256), (4, 64, 128256)):
+        plain = lib.spec_accept_workspace_bytes(B, N, V)
+        filt = lib.spec_accept_filtered_workspace_bytes(B, N, V)
+        # per (row, chunk), at least one chunk a row: a 16-byte record, 64 digit counts, 256 keys
+        assert filt >= plain + B * N * (16 + 64 * 4 + 256 * 4), (B, N, V)
+    assert lib.spec_accept_filtered_workspace_bytes(0, 6, 1000) == 0
+    assert lib.spec_accept_filtered_workspace_bytes(2, 65, 1000) == 0
+    assert lib.spec_accept_filtered_workspace_bytes(2, 6, 0) == 0
 
 
 def test_multidraft_errors():

@@ -129,3 +129,44 @@ def test_filtered_accept_dense_bins(kind, k, p):
     excl = check_accept(w, gpu, _ref(w, k, p))
     announce(f"  near-tie requests excluded: {excl} of {w.B}")
     assert excl <= 2, excl
+
+
+def _logits_of(kind, shape, rng):
+    if kind == "near_uniform":
+        return rng.uniform(0.0, 0.01, size=shape).astype(np.float32)
+    if kind == "quantised":
+        return rng.integers(0, 4, size=shape).astype(np.float32)
+    return None
+
+
+@pytest.mark.parametrize("cid,over,kind,k,p", [
+    (2, dict(batch=3), None, 50, 0.9),                        # B = 3 chain, V = 128256: 63 chunks per row
+    (4, dict(batch=16, prefix_len=(10, 40)), None, 20, 0.95),
+    (5, dict(batch=2, prefix_len=(0, 8)), None, 100, 1.0),    # 64-node trees
+    (1, dict(batch=32, vocab=1001), None, 7, 0.7),            # V % 4 != 0: scalar loads
+    (2, dict(batch=6), "near_uniform", 1000, 1.0),            # more candidates than the split keeps: whole-row redo
+    (2, dict(batch=6), "quantised", 100, 0.6),                # ~32k ties with the 100th key: whole-row redo
+])
+def test_split_truncation_equals_whole_row(cid, over, kind, k, p):
+    """The truncation spread over each row's chunks (workspace of
+    spec_accept_filtered_workspace_bytes) and the one-workgroup-per-row
+    selection (workspace of spec_accept_workspace_bytes) give the same bits."""
+    w = generate(scaled(cid, **over), with_attention=False)
+    if kind is not None:
+        w.target_logits[:] = _logits_of(kind, w.target_logits.shape, np.random.default_rng(7))
+    announce(f"split vs whole-row truncation cfg{cid} {over} {kind} top_k={k} top_p={p} B={w.B} N={w.N} V={w.V}")
+    d = _dev(w)
+    small = sv.spec_accept_workspace_bytes(w.B, w.N, w.V)
+    big = sv.spec_accept_filtered_workspace_bytes(w.B, w.N, w.V)
+    assert big > small
+    res = {}
+    for name, nbytes in (("whole", small), ("split", big)):
+        ws = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device="cuda")
+        al, path, out = sv.spec_accept_reject_filtered(d["lg"], d["dp"], d["tk"], d["par"], d["ua"], d["us"],
+                                                       w.temperature, top_k=k, top_p=p, workspace=ws)
+        torch.cuda.synchronize()
+        res[name] = (al.cpu().numpy(), path.cpu().numpy(), out.cpu().numpy())
+    for a, b in zip(res["whole"], res["split"]):
+        np.testing.assert_array_equal(a, b)
+    check_accept(w, dict(accept_len=res["split"][0], path=res["split"][1], out_tokens=res["split"][2]),
+                 _ref(w, k, p))

@@ -96,8 +96,9 @@ def test_outputs_written_in_full_and_nothing_past_them():
     d = _dev_inputs(w)
     pad = 4096
     n_out = d["q"].numel()
-    sent_bf16 = torch.tensor([0x7FC1], dtype=torch.int16).view(torch.bfloat16).item()
-    big = torch.full((n_out + pad,), sent_bf16, dtype=d["q"].dtype, device="cuda")
+    # (filled through an int16 view: a NaN converted from a Python float
+    # would lose the payload)
+    big = torch.full((n_out + pad,), 0x7FC1, dtype=torch.int16, device="cuda").view(d["q"].dtype)
     out = big[:n_out].view(d["q"].shape)
     sent_i = 0x7F7F7F7F
     al_b = torch.full((w.B + pad,), sent_i, dtype=torch.int32, device="cuda")
