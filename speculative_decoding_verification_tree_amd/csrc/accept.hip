@@ -101,7 +101,7 @@ struct AcceptArgs {
 
 struct ChunkRec {  // one chunk of a row, split truncation
     float M;       // chunk max logit
-    int arg;       // its lowest index
+    int arg;       // not computed (0x7fffffff): the truncated rule runs at T > 0, where no argmax is read
     int nbins;     // non-empty first digits at or above the chunk's top-k digit (> kFBinCap: too many)
     int nkeys;     // keys of those digits (> kFKeyCap: too many)
 };
@@ -1217,7 +1217,7 @@ __device__ __forceinline__ void filter_row(const AcceptArgs& a, int rid, bool sp
             s_ovf = 0;
             s_n = 0;
         }
-        for (int c = tid; c < nch; c += NT) {  // ascending chunks: the lowest index of the max
+        for (int c = tid; c < nch; c += NT) {  // the row max (its argmax is not needed at T > 0)
             const ChunkRec r = rec[c];
             if (r.M > Ms) {
                 Ms = r.M;
@@ -1496,11 +1496,20 @@ __global__ __launch_bounds__(kThreads) void filt_chunk(AcceptArgs a) {
     float M;
     int arg;
     double S, A2;
-    chunk_reduce<EPT, false, true, false>(v, x0, x1, vec4, 0.f, M, arg, S, A2, &s_red);  // (its barrier orders the clear)
+    // (no argmax: the truncated rule runs at T > 0, where the row's argmax is unused)
+    chunk_reduce<EPT, false, false, false>(v, x0, x1, vec4, 0.f, M, arg, S, A2, &s_red);  // (its barrier orders the clear)
     const int lim = x1 - (x0 + (vec4 ? 4 * tid : tid));
+    // Keys once, out-of-range elements as 0 (below every digit a chunk of
+    // in-range keys selects: d_c is found over the counted keys only).
+    uint32_t kk[EPT];
+    uint32_t inr = 0u;  // bit e: element e in range
 #pragma unroll
-    for (int e = 0; e < EPT; ++e)
-        if (elem_off(e, vec4) < lim) atomicAdd(&s_h[logit_key(v.v[e]) >> 21], 1u);
+    for (int e = 0; e < EPT; ++e) {
+        const bool in = elem_off(e, vec4) < lim;
+        inr |= static_cast<uint32_t>(in) << e;
+        kk[e] = logit_key(v.v[e]);
+        if (in) atomicAdd(&s_h[kk[e] >> 21], 1u);
+    }
     __syncthreads();
     // d_c: thread t sums the eight digits 2047 - 8t - 7 .. 2047 - 8t; a
     // block scan from the top finds where the chunk's count reaches k (a
@@ -1548,7 +1557,7 @@ __global__ __launch_bounds__(kThreads) void filt_chunk(AcceptArgs a) {
     int total = 0;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-        m[e] = __ballot(elem_off(e, vec4) < lim && static_cast<int>(logit_key(v.v[e]) >> 21) >= dc);
+        m[e] = __ballot(((inr >> e) & 1u) && static_cast<int>(kk[e] >> 21) >= dc);
         total += __popcll(m[e]);
     }
     if (total > 0) {  // wave-uniform
@@ -1558,8 +1567,9 @@ __global__ __launch_bounds__(kThreads) void filt_chunk(AcceptArgs a) {
         const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
+            if (m[e] == 0ull) continue;  // wave-uniform: most elements have no match in the wave
             const int at = base + __popcll(m[e] & below);
-            if (((m[e] >> lane) & 1ull) && at < kFKeyCap) keys[at] = logit_key(v.v[e]);
+            if (((m[e] >> lane) & 1ull) && at < kFKeyCap) keys[at] = kk[e];
             base += __popcll(m[e]);
         }
     }
