@@ -136,6 +136,15 @@ def _logits_of(kind, shape, rng):
         return rng.uniform(0.0, 0.01, size=shape).astype(np.float32)
     if kind == "quantised":
         return rng.integers(0, 4, size=shape).astype(np.float32)
+    if kind == "plateau":
+        # 5000 tokens per row in one first digit ([8, 10)) above N(0, 1) logits:
+        # no chunk over its slots, but more candidates than the finish holds
+        lg = rng.standard_normal(shape).astype(np.float32)
+        for b in range(shape[0]):
+            for i in range(shape[1]):
+                top = rng.choice(shape[2], 5000, replace=False)
+                lg[b, i, top] = rng.uniform(8.0, 9.9, size=5000).astype(np.float32)
+        return lg
     return None
 
 
@@ -146,6 +155,7 @@ def _logits_of(kind, shape, rng):
     (1, dict(batch=32, vocab=1001), None, 7, 0.7),            # V % 4 != 0: scalar loads
     (2, dict(batch=6), "near_uniform", 1000, 1.0),            # more candidates than the split keeps: whole-row redo
     (2, dict(batch=6), "quantised", 100, 0.6),                # ~32k ties with the 100th key: whole-row redo
+    (2, dict(batch=4), "plateau", 100, 0.9),                  # 5000 candidates, every chunk within its slots
 ])
 def test_split_truncation_equals_whole_row(cid, over, kind, k, p):
     """The truncation spread over each row's chunks (workspace of
