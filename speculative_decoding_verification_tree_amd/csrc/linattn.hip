@@ -112,23 +112,23 @@ __device__ __forceinline__ void la_tree(const int32_t* parent, const float* alph
 // LDS floats for trees of at most NMAX nodes: commit (path factors k, v)
 // or verify (Q and K rows padded by one, V, the scores W, a 32-column chunk
 // of the state), whichever is larger.
-template <int NMAX, bool COMMIT, int ROWS>
+template <int NMAX, bool COMMIT, bool VERIFY, int ROWS>
 constexpr int la_lds_floats() {
-    constexpr int commit = COMMIT ? kMaxNodes * (kLaMaxD + ROWS) : 0;
-    constexpr int verify = 2 * NMAX * (kLaMaxD + 1) + NMAX * ROWS + NMAX * NMAX + ROWS * (kLaChunk + 1);
+    constexpr int commit = COMMIT ? NMAX * (kLaMaxD + ROWS) : 0;
+    constexpr int verify = VERIFY ? 2 * NMAX * (kLaMaxD + 1) + NMAX * ROWS + NMAX * NMAX + ROWS * (kLaChunk + 1) : 0;
     return commit > verify ? commit : verify;
 }
 
 // COMMIT: the launch may commit (alone or before verifying); without it the
 // LDS is sized for verification only.
-template <int NMAX, bool COMMIT, int ROWS>
+template <int NMAX, bool COMMIT, bool VERIFY, int ROWS>
 __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
     constexpr int kLaRows = ROWS;
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int Dk = a.Dk, Dv = a.Dv, H = a.H;
     const int es0 = blockIdx.z * kLaRows, ne = min(kLaRows, Dv - es0);  // this workgroup's state rows
     const bool bf16 = a.bf16 != 0;
-    __shared__ float lds[la_lds_floats<NMAX, COMMIT, ROWS>()];
+    __shared__ __attribute__((aligned(16))) float lds[la_lds_floats<NMAX, COMMIT, VERIFY, ROWS>()];
     __shared__ float s_L[kMaxNodes];
     __shared__ uint64_t s_anc[kMaxNodes];
     __shared__ float s_c[kMaxNodes];
@@ -156,29 +156,47 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
                               [&](int t) { return ((static_cast<size_t>(b) * N + s_j[t]) * H + h) * Dv + es0; }, vf,
                               ne);
         __syncthreads();
-        // This thread's column d, slice rows e0, e0 + estep, ...: every load
-        // issued before the first update.
+        // This thread's four columns d4 .. d4 + 3 of slice rows e0, e0 + estep,
+        // ...: 16-byte loads, every one issued before the first update (rows
+        // past the slice read its last row and are not stored).  The path's
+        // terms then go in order t = 0 .. acc, each k row's four values read
+        // once for all of the thread's rows.
         const float Av = exp2f(s_L[vstop]);
-        const int d = tid % Dk, e0 = tid / Dk, estep = kLaThreads / Dk;
-        constexpr int kRows = kLaRows * kLaMaxD / kLaThreads;  // 16 at most (Dk = 128)
-        float sv[kRows];
+        const int tpr = Dk / 4, d4 = 4 * (tid % tpr), e0 = tid / tpr, estep = kLaThreads / tpr;
+        constexpr int kRows4 = kLaRows * kLaMaxD / 4 / kLaThreads;  // row slots a thread may hold
+        float4 sv[kRows4];
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) {
-            const int e = e0 + r * estep;
-            sv[r] = e < ne ? S[static_cast<size_t>(es0 + e) * Dk + d] : 0.f;
+        for (int r = 0; r < kRows4; ++r) {
+            const int e = min(e0 + r * estep, ne - 1);
+            sv[r] = *reinterpret_cast<const float4*>(S + static_cast<size_t>(es0 + e) * Dk + d4);
         }
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) {
-            const int e = e0 + r * estep;
-            if (e < ne) {
-                float s = Av * sv[r];
-                for (int t = 0; t <= acc; ++t) s = fmaf(s_c[t] * vf[t * ne + e], kf[t * Dk + d], s);
-                S[static_cast<size_t>(es0 + e) * Dk + d] = s;
+        for (int r = 0; r < kRows4; ++r) {
+            sv[r].x *= Av;
+            sv[r].y *= Av;
+            sv[r].z *= Av;
+            sv[r].w *= Av;
+        }
+        for (int t = 0; t <= acc; ++t) {
+            const float4 k4 = *reinterpret_cast<const float4*>(kf + t * Dk + d4);
+            const float ct = s_c[t];
+#pragma unroll
+            for (int r = 0; r < kRows4; ++r) {
+                const float w = ct * vf[t * ne + min(e0 + r * estep, ne - 1)];
+                sv[r].x = fmaf(w, k4.x, sv[r].x);
+                sv[r].y = fmaf(w, k4.y, sv[r].y);
+                sv[r].z = fmaf(w, k4.z, sv[r].z);
+                sv[r].w = fmaf(w, k4.w, sv[r].w);
             }
+        }
+#pragma unroll
+        for (int r = 0; r < kRows4; ++r) {
+            const int e = e0 + r * estep;
+            if (e < ne) *reinterpret_cast<float4*>(S + static_cast<size_t>(es0 + e) * Dk + d4) = sv[r];
         }
         __syncthreads();  // the workgroup's own state writes before its reads below
     }
-    if (!a.do_verify) return;
+    if (!VERIFY || !a.do_verify) return;
 
     const int N = a.N;
     la_tree(a.parent, a.alpha, b, N, H, h, s_L, s_anc);
@@ -320,21 +338,26 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
     }
 }
 
+template <int NMAX, int ROWS>
+static void launch_la_n(const LaArgs& a, const dim3& grid, hipStream_t stream) {
+    if (a.do_commit && a.do_verify)
+        hipLaunchKernelGGL((la_kernel<NMAX, true, true, ROWS>), grid, dim3(kLaThreads), 0, stream, a);
+    else if (a.do_commit)
+        hipLaunchKernelGGL((la_kernel<NMAX, true, false, ROWS>), grid, dim3(kLaThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((la_kernel<NMAX, false, true, ROWS>), grid, dim3(kLaThreads), 0, stream, a);
+}
+
 template <int ROWS>
 static void launch_la_rows(const LaArgs& a, hipStream_t stream) {
     const dim3 grid(a.H, a.B, (a.Dv + ROWS - 1) / ROWS);
-    const bool small = !a.do_verify || a.N <= 16;
-    if (a.do_commit) {
-        if (small)
-            hipLaunchKernelGGL((la_kernel<16, true, ROWS>), grid, dim3(kLaThreads), 0, stream, a);
-        else
-            hipLaunchKernelGGL((la_kernel<kMaxNodes, true, ROWS>), grid, dim3(kLaThreads), 0, stream, a);
-    } else {
-        if (small)
-            hipLaunchKernelGGL((la_kernel<16, false, ROWS>), grid, dim3(kLaThreads), 0, stream, a);
-        else
-            hipLaunchKernelGGL((la_kernel<kMaxNodes, false, ROWS>), grid, dim3(kLaThreads), 0, stream, a);
-    }
+    // NMAX bounds both trees: the one verified and the one whose path is
+    // committed (LDS is sized for the phases the launch runs).
+    const bool small = (!a.do_verify || a.N <= 16) && (!a.do_commit || a.pN <= 16);
+    if (small)
+        launch_la_n<16, ROWS>(a, grid, stream);
+    else
+        launch_la_n<kMaxNodes, ROWS>(a, grid, stream);
 }
 
 int launch_la(const LaArgs& a, hipStream_t stream) {

@@ -96,12 +96,20 @@ def test_la_verify_and_commit_match_oracle(B, N, H, Dk, Dv, dtype, tree, decay):
     assert (err <= 1e-5 * np.abs(want) + 1e-5 * rms).all(), err.max()
 
 
-def test_la_deferred_commit_equals_commit_then_verify():
-    announce("linear attention: deferred commit folded into the next verification")
-    B, N, H, Dk, Dv = 3, 24, 4, 128, 128
-    S, q, k, v, al, par = _case(5, B, N, H, Dk, Dv, "f32", True, True)
-    _, q2, k2, v2, al2, par2 = _case(6, B, N, H, Dk, Dv, "f32", True, True)
-    path, acc = _random_paths(np.random.default_rng(1), par, B, N)
+@pytest.mark.parametrize("B,H,Np,Nv", [
+    (3, 4, 24, 24),
+    (3, 4, 64, 8),   # a large committed tree before a small verified one
+    (3, 4, 8, 8),    # both within the small-tree launch
+    (2, 4, 16, 40),
+    (64, 8, 8, 8),   # one workgroup per (head, request), the whole state
+])
+def test_la_deferred_commit_equals_commit_then_verify(B, H, Np, Nv):
+    announce(f"linear attention: deferred commit folded into the next verification B={B} H={H} "
+             f"committed tree {Np} verified tree {Nv}")
+    Dk, Dv = 128, 128
+    S, q, k, v, al, par = _case(5, B, Np, H, Dk, Dv, "f32", True, True)
+    _, q2, k2, v2, al2, par2 = _case(6, B, Nv, H, Dk, Dv, "f32", True, True)
+    path, acc = _random_paths(np.random.default_rng(1), par, B, Np)
     f = (_dev(k), _dev(v), _dev(al), _dev(par), _dev(path), _dev(acc))
     # two launches
     s1 = _dev(S)
