@@ -206,8 +206,8 @@ int spec_accept_reject_filtered(int32_t batch, int32_t num_nodes, int32_t vocab,
  * of spec_accept_reject does not give for nodes with several children.  On
  * a chain both rules agree.  Arguments and outputs as spec_accept_reject;
  * workspace >= spec_accept_multidraft_workspace_bytes(batch, vocab) (two
- * residual rows, 2 KiB of exchange records and a counter per request;
- * contents need no initialisation: the call clears the counters itself).
+ * residual rows and 2 KiB of tagged exchange records per request; contents
+ * need no initialisation: the call clears the records' tags itself).
  * Each request's vocabulary is split over up to 64 workgroups that wait on
  * each other between passes, so the call assumes its grid runs at once (it
  * is sized from the device's occupancy; nothing else should fill the device

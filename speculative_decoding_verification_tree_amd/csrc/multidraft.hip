@@ -49,8 +49,7 @@ struct MdArgs {
     int32_t* path;
     int32_t* out_tokens;
     float* resid;    // [B][2][V]: the part's slices of the two residual rows
-    MdRec* recs;     // [B][2][kMdMaxParts]: the records of the last two rounds
-    uint32_t* cnt;   // [B]: records published so far (zeroed before the launch)
+    MdRec* recs;     // [B][2][kMdMaxParts]: the records of the last two rounds (tags cleared before the launch)
     int B, N, V;
     int P, cw;       // parts per request, tokens per part (a multiple of 4)
     float T;
@@ -129,9 +128,20 @@ __device__ __forceinline__ void md_for2(const float* ra, const float* rb, int x0
     }
 }
 
-__global__ void md_clear(uint32_t* cnt, int B) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < B) cnt[i] = 0u;
+// A record in memory: word 0 the sum, word 1 the max's bits, then its index
+// (24 bits, 0xFFFFFF: none) and the round's tag (8 bits) in the high half.
+// The tag tells a reader that the record is the round's: the writer stores
+// word 0, waits for it, then stores word 1.  Rounds stay below 255 (at most
+// two per node and one for the draw); cleared records carry tag 0xFF.
+constexpr uint32_t kMdNoArg = 0xFFFFFFu;
+__device__ __forceinline__ uint64_t md_word1(float m, int arg, uint32_t round) {
+    const uint32_t a24 = arg < 0 || arg >= static_cast<int>(kMdNoArg) ? kMdNoArg : static_cast<uint32_t>(arg);
+    return static_cast<uint64_t>(__float_as_uint(m)) | (static_cast<uint64_t>(a24 | ((round & 0xFFu) << 24)) << 32);
+}
+
+__global__ void md_clear(uint64_t* recs, size_t nwords) {
+    const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < nwords) recs[i] = ~0ull;  // (word 1 of every record: tag 0xFF)
 }
 
 __global__ __launch_bounds__(kMdThreads) void accept_md(MdArgs a) {
@@ -171,28 +181,33 @@ __global__ __launch_bounds__(kMdThreads) void accept_md(MdArgs a) {
             MdRec* slots = a.recs + (static_cast<size_t>(b) * 2 + (round & 1u)) * kMdMaxParts;
             if (tid == 0) {
                 md_st64(&slots[p].s, __builtin_bit_cast(uint64_t, mine.s));
-                md_st64(&slots[p].m, static_cast<uint64_t>(__float_as_uint(mine.m)) |
-                                         (static_cast<uint64_t>(static_cast<uint32_t>(mine.arg)) << 32));
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the record is stored before it is counted
-                __hip_atomic_fetch_add(a.cnt + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const uint32_t target = (round + 1u) * static_cast<uint32_t>(P);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the sum is stored before the tagged word
+                md_st64(&slots[p].m, md_word1(mine.m, mine.arg, round));
+            }
+            if (wave == 0) {
+                // Lane k waits for part k's tagged word (a bounded poll), then
+                // reads the sum, which was stored before it.
+                const int k = min(lane, P - 1);
+                uint64_t w = 0ull;
                 uint32_t polls = 0;
-                while (__hip_atomic_load(a.cnt + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+                for (;;) {
+                    w = md_ld64(&slots[k].m);
+                    const bool here = ((w >> 56) & 0xFFu) == (round & 0xFFu);
+                    if (__ballot(!here) == 0ull) break;  // (wave-uniform exit)
                     __builtin_amdgcn_s_sleep(2);
                     if (++polls > kMdSpinLimit) {
-                        s_fail = 1;
+                        if (lane == 0) s_fail = 1;
                         break;
                     }
                 }
-            }
-            __syncthreads();
-            if (tid < P) {
-                MdRec r;
-                r.s = __builtin_bit_cast(double, md_ld64(&slots[tid].s));
-                const uint64_t w = md_ld64(&slots[tid].m);
-                r.m = __uint_as_float(static_cast<uint32_t>(w));
-                r.arg = static_cast<int>(static_cast<uint32_t>(w >> 32));
-                s_rec[tid] = r;
+                if (lane < P) {
+                    MdRec r;
+                    r.s = __builtin_bit_cast(double, md_ld64(&slots[k].s));
+                    r.m = __uint_as_float(static_cast<uint32_t>(w));
+                    const uint32_t a24 = static_cast<uint32_t>(w >> 32) & kMdNoArg;
+                    r.arg = a24 == kMdNoArg ? 0x7fffffff : static_cast<int>(a24);
+                    s_rec[lane] = r;
+                }
             }
         } else if (tid == 0) {
             s_rec[0] = mine;
@@ -409,7 +424,7 @@ static size_t md_resid_bytes(int B, int V) { return align_up(static_cast<size_t>
 static size_t md_rec_bytes(int B) { return align_up(static_cast<size_t>(B) * 2 * kMdMaxParts * sizeof(MdRec), 256); }
 
 size_t multidraft_workspace_bytes(int B, int V) {
-    return md_resid_bytes(B, V) + md_rec_bytes(B) + align_up(static_cast<size_t>(B) * sizeof(uint32_t), 256);
+    return md_resid_bytes(B, V) + md_rec_bytes(B);
 }
 
 // Parts per request: as many as the device holds at once for the batch
@@ -450,7 +465,6 @@ int launch_accept_multidraft(int B, int N, int V, const float* logits, const flo
     char* ws = static_cast<char*>(workspace);
     a.resid = reinterpret_cast<float*>(ws);
     a.recs = reinterpret_cast<MdRec*>(ws + md_resid_bytes(B, V));
-    a.cnt = reinterpret_cast<uint32_t*>(ws + md_resid_bytes(B, V) + md_rec_bytes(B));
     a.B = B;
     a.N = N;
     a.V = V;
@@ -461,7 +475,9 @@ int launch_accept_multidraft(int B, int N, int V, const float* logits, const flo
     const int P0 = md_parts(B, V);
     a.cw = ((V + P0 - 1) / P0 + 3) / 4 * 4;
     a.P = (V + a.cw - 1) / a.cw;  // no empty part
-    hipLaunchKernelGGL(md_clear, dim3((B + 255) / 256), dim3(256), 0, stream, a.cnt, B);
+    const size_t nwords = static_cast<size_t>(B) * 2 * kMdMaxParts * sizeof(MdRec) / sizeof(uint64_t);
+    hipLaunchKernelGGL(md_clear, dim3(static_cast<unsigned>((nwords + 255) / 256)), dim3(256), 0, stream,
+                       reinterpret_cast<uint64_t*>(a.recs), nwords);
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     hipLaunchKernelGGL(accept_md, dim3(a.P, B), dim3(kMdThreads), 0, stream, a);
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;

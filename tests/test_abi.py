@@ -186,8 +186,8 @@ def test_multidraft_errors():
     need = lib.spec_accept_multidraft_workspace_bytes(2, 1000)
     up = lambda n: (n + 255) // 256 * 256  # noqa: E731
     # two residual rows per request, two rounds of 64 16-byte records per
-    # request, one counter per request, each region 256-byte aligned
-    assert need == up(2 * 2 * 1000 * 4) + up(2 * 2 * 64 * 16) + up(2 * 4)
+    # request, each region 256-byte aligned
+    assert need == up(2 * 2 * 1000 * 4) + up(2 * 2 * 64 * 16)
     assert lib.spec_accept_multidraft_workspace_bytes(0, 1000) == 0
     assert lib.spec_accept_multidraft_workspace_bytes(2, 0) == 0
 
