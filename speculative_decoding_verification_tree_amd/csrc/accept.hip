@@ -1026,13 +1026,14 @@ __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
 
 // ---------------------------------------------------------------------------
 // Entries per thread and chunk: 8, raised to 16 or 32 for large batches so
-// the statistics kernel launches at most ~4k workgroups of useful size
-// (an ~8k bound left cfg 3's 5.9k short-lived workgroups running in about
-// three rounds: its acceptance 22.1 -> 20.8 us with the lower bound).
+// the statistics kernel launches at most ~2k workgroups of useful size (on
+// 8 requests of 46-node trees over 32000 tokens, ~5.9k short-lived
+// workgroups ran in about three rounds: the acceptance took 22.1 us against
+// 20.8 at a ~4k bound and 19.0 at ~2k).
 static int accept_ept(int B, int N, int V) {
     int ept = 8;
     auto nchunk = [&](int e) { return (V + e * kThreads - 1) / (e * kThreads); };
-    while (ept < 32 && (static_cast<long>(B) * N * nchunk(ept) > 4096 || nchunk(ept) > kMaxChunks)) ept *= 2;
+    while (ept < 32 && (static_cast<long>(B) * N * nchunk(ept) > 2048 || nchunk(ept) > kMaxChunks)) ept *= 2;
     return ept;
 }
 
