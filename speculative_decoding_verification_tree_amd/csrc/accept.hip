@@ -1480,7 +1480,7 @@ __global__ __launch_bounds__(kFThreads) void accept_filter(AcceptArgs a) { filte
 // The counts, the digit, the candidate set and the fixed-point masses are
 // the same integers as in one workgroup's passes, so the records are
 // identical.
-template <int EPT>
+template <int EPT, bool NT>
 __global__ __launch_bounds__(kThreads) void filt_chunk(AcceptArgs a) {
     const int c = blockIdx.x, rid = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     __shared__ uint32_t s_h[2048];
@@ -1490,7 +1490,7 @@ __global__ __launch_bounds__(kThreads) void filt_chunk(AcceptArgs a) {
     const float* row = a.logits + static_cast<size_t>(rid) * a.V;
     const int x0 = c * a.chunk, x1 = min(x0 + a.chunk, a.V);
     const bool vec4 = a.vec4 != 0;
-    const Vals<EPT> v = load_chunk<EPT, true>(row, x0, x1, vec4, -INFINITY);
+    const Vals<EPT> v = load_chunk<EPT, NT>(row, x0, x1, vec4, -INFINITY);
     for (int i = tid; i < 2048; i += kThreads) s_h[i] = 0u;
     if (tid == 0) {
         s_dc = 0;
@@ -1616,7 +1616,11 @@ int max_accept_vocab() { return kMaxChunks * 32 * kThreads; }
 template <int EPT, bool FILT>
 static int launch_accept_ept(const AcceptArgs& a, const AcceptPlan& p, hipStream_t stream) {
     if (FILT && a.frec) {  // every row's truncation, each row over its chunks
-        hipLaunchKernelGGL((filt_chunk<EPT>), dim3(p.nchunk, a.B * a.N), dim3(kThreads), 0, stream, a);
+        // (non-temporal row loads above 16 MB of rows, as for the statistics)
+        if (static_cast<size_t>(a.B) * a.N * a.V * sizeof(float) > (16u << 20))
+            hipLaunchKernelGGL((filt_chunk<EPT, true>), dim3(p.nchunk, a.B * a.N), dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((filt_chunk<EPT, false>), dim3(p.nchunk, a.B * a.N), dim3(kThreads), 0, stream, a);
         hipLaunchKernelGGL(accept_filter_split, dim3(a.B * a.N), dim3(kFSplitThreads), 0, stream, a);
         if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     } else if (FILT) {  // every row's truncation (the stop row may be a leaf)
