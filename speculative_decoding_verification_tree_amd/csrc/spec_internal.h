@@ -118,6 +118,7 @@ struct LaArgs {
     const int32_t* ppath;
     const int32_t* pacc;
     int do_commit, do_verify;
+    int vec;  // every q, k, v row source 16-byte aligned (set by launch_la)
 };
 int launch_la(const LaArgs& a, hipStream_t stream);
 

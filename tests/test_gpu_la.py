@@ -73,6 +73,10 @@ CASES = [
     # 512 (request, head) pairs and more: one workgroup per pair, the whole state
     (64, 8, 8, 128, 128, "bf16", False, True),
     (32, 20, 16, 64, 64, "f32", True, True),
+    # about a hundred pairs of a large tree: on a 256-CU device, slices of 64
+    # state rows (32-row slices would not all run at once)
+    (8, 46, 12, 128, 128, "bf16", True, True),
+    (8, 46, 12, 128, 128, "f32", True, False),
 ]
 
 
@@ -134,3 +138,33 @@ def test_la_chain_parent_array_equals_null():
     b = sv.spec_la_verify(_dev(S), _dev(q), _dev(k), _dev(v), _dev(al), _dev(chain))
     torch.cuda.synchronize()
     np.testing.assert_array_equal(a.cpu().numpy(), b.cpu().numpy())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_la_rows_not_16_byte_aligned(dtype):
+    """q, k and v starting off a 16-byte boundary take the element-wise loads; the
+    values reaching the arithmetic are the same, so the results are bit-identical."""
+    B, N, H, Dk, Dv = 3, 20, 4, 128, 128
+    announce(f"linear attention: rows off a 16-byte boundary ({dtype})")
+    S, q, k, v, al, par = _case(11, B, N, H, Dk, Dv, dtype, True, True)
+
+    def shifted(x):
+        t = _dev(x, dtype)
+        flat = t.reshape(-1)
+        buf = torch.empty(flat.numel() + 1, dtype=t.dtype, device=t.device)
+        buf[1:] = flat
+        out = buf[1:].view(t.shape)
+        assert out.data_ptr() % 16 != 0
+        return out
+
+    path, acc = _random_paths(np.random.default_rng(3), par, B, N)
+    outs, states = [], []
+    for make in (lambda x: _dev(x, dtype), shifted):
+        st = _dev(S)
+        f = (make(k), make(v), _dev(al), _dev(par), _dev(path), _dev(acc))
+        o = sv.spec_la_verify(st, make(q), make(k), make(v), _dev(al), _dev(par), pending=f)
+        torch.cuda.synchronize()
+        outs.append(o.float().cpu().numpy())
+        states.append(st.cpu().numpy())
+    np.testing.assert_array_equal(outs[1], outs[0])
+    np.testing.assert_array_equal(states[1], states[0])
