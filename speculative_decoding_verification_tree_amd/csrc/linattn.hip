@@ -17,7 +17,8 @@
 //           written once (in place; the workgroup owns its slab);
 //   verify: o_i = A(-> i] S q_i + sum_{j in anc(i)} A(j -> i] (q_i . k_j) v_j
 //           with Q, K, V in LDS, the N x N decayed, masked scores in LDS and
-//           the state streamed through LDS in 32-column chunks.
+//           S q_i on the matrix cores (fp32), the state's tiles loaded
+//           straight into operand registers.
 // Both phases in one launch are the deferred update: the previous step's
 // commit folded into this step's verification (one state read and write).
 // Decay products are exp2 of differences of log2 prefix sums along root paths.
@@ -30,7 +31,6 @@ namespace specv {
 
 constexpr int kLaThreads = 256;
 constexpr int kLaMaxD = 128;
-constexpr int kLaChunk = 32;
 // State rows (output dims) per workgroup: a slice of 32 when (head, request)
 // pairs are few, else the whole state (kLaMaxD).
 constexpr int kLaSliceRows = 32;
@@ -153,13 +153,12 @@ __device__ __forceinline__ void la_tree(const int32_t* parent, const float* alph
 }
 
 // LDS floats for trees of at most NMAX nodes: commit (path factors k, v)
-// or verify (Q and K rows padded by one, V, the scores W, a 32-column chunk
-// of the state), whichever is larger.
+// or verify (Q and K rows padded by four, V, the scores W), whichever is
+// larger.
 template <int NMAX, bool COMMIT, bool VERIFY, int ROWS>
 constexpr int la_lds_floats() {
     constexpr int commit = COMMIT ? NMAX * (kLaMaxD + ROWS) : 0;
-    constexpr int ks_sc = NMAX * (kLaMaxD + 4) > ROWS * (kLaChunk + 4) ? NMAX * (kLaMaxD + 4) : ROWS * (kLaChunk + 4);
-    constexpr int verify = VERIFY ? NMAX * (kLaMaxD + 4) + ks_sc + NMAX * ROWS + NMAX * NMAX : 0;
+    constexpr int verify = VERIFY ? 2 * NMAX * (kLaMaxD + 4) + NMAX * ROWS + NMAX * NMAX : 0;
     return commit > verify ? commit : verify;
 }
 
@@ -180,19 +179,60 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
     __shared__ int s_off[kMaxNodes + 1];
     float* S = a.state + (static_cast<size_t>(b) * H + h) * Dv * Dk;
 
-    if (COMMIT && a.do_commit) {
-        const int N = a.pN;
-        // This thread's four columns d4 .. d4 + 3 of slice rows e0, e0 + estep,
-        // ...: 16-byte loads, issued first (no address depends on the path;
-        // rows past the slice read its last row and are not stored).
-        const int tpr = Dk / 4, d4 = 4 * (tid % tpr), e0 = tid / tpr, estep = kLaThreads / tpr;
-        constexpr int kRows4 = kLaRows * kLaMaxD / 4 / kLaThreads;  // row slots a thread may hold
-        float4 sv[kRows4];
+    // The slice of the state lives in registers, in the matrix-core operand
+    // layout of the verification's S q_i (v_mfma_f32_16x16x4_f32, C[e][i] =
+    // sum_d S[e][d] Q[i][d] per 16-row tile and 16-node tile): lane (r, g) =
+    // (lane % 16, lane / 16) holds S[e0 + r][16j + 4g .. 16j + 4g + 3] for
+    // every 16-column group j (16-byte loads, issued first: no address
+    // depends on the tree or the path).  Component c of group j is the A
+    // operand of one product, whose contraction index g stands for column
+    // 16j + 4g + c; the B operand (Q[node][that column]) comes from LDS the
+    // same way, and the result lands as C[e0 + 4g + c][node tile + r].  The
+    // commit updates these registers in place, so a launch that commits and
+    // verifies reads the state once.
+    // Waves: with four or more row tiles each wave takes every fourth tile
+    // and all node tiles; with two, two waves per row tile split the node
+    // tiles (both update the tile; the first stores it).
+    constexpr int kRT = kLaRows / 16;
+    constexpr int kRowW = kRT >= 4 ? 4 : kRT;
+    constexpr int kNodeW = 4 / kRowW;
+    constexpr int kTPW = kRT / kRowW;       // row tiles per wave
+    constexpr int kJ = kLaMaxD / 16;        // 16-column groups (Dk = 64: the spare ones re-read the last)
+    static_assert(kRT * 16 == kLaRows && kRowW * kNodeW == 4 && kTPW * kRowW == kRT, "row tiles over four waves");
+    // A launch that only commits 32-row slices keeps the row-major layout
+    // below instead (two waves per tile would duplicate the update).
+    constexpr bool kTiled = VERIFY || kNodeW == 1;
+    const int wave = tid >> 6, lr = tid & 15, lg = (tid >> 4) & 3;
+    const int rsel = wave % kRowW, nsel = wave / kRowW;
+    float4 sreg[kTiled ? kTPW * kJ : 1];
+    if constexpr (kTiled) {
+#pragma unroll
+        for (int t = 0; t < kTPW; ++t) {
+            const int row = min((rsel + kRowW * t) * 16 + lr, ne - 1);
+#pragma unroll
+            for (int j = 0; j < kJ; ++j) {
+                const int jj = min(j, Dk / 16 - 1);
+                sreg[t * kJ + j] =
+                    *reinterpret_cast<const float4*>(S + static_cast<size_t>(es0 + row) * Dk + 16 * jj + 4 * lg);
+            }
+        }
+    }
+    // Row-major: this thread's four columns d4 .. d4 + 3 of slice rows e0,
+    // e0 + estep, ... (rows past the slice read its last row and are not
+    // stored).
+    const int tpr = Dk / 4, d4 = 4 * (tid % tpr), e0 = tid / tpr, estep = kLaThreads / tpr;
+    constexpr int kRows4 = kTiled ? 1 : kLaRows * kLaMaxD / 4 / kLaThreads;
+    float4 sv[kRows4];
+    if constexpr (!kTiled) {
 #pragma unroll
         for (int r = 0; r < kRows4; ++r) {
             const int e = min(e0 + r * estep, ne - 1);
             sv[r] = *reinterpret_cast<const float4*>(S + static_cast<size_t>(es0 + e) * Dk + d4);
         }
+    }
+
+    if (COMMIT && a.do_commit) {
+        const int N = a.pN;
         la_tree(a.pparent, a.palpha, b, N, H, h, s_L, s_anc);
         // (device data: out-of-range entries are clamped into the tree)
         const int acc = min(max(a.pacc[b], 0), N - 1);
@@ -226,34 +266,70 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
             path_rows(std::false_type{});
         }
         __syncthreads();
-        // The path's terms in order t = 0 .. acc, each k row's four values
-        // read once for all of the thread's rows.
+        // S <- A(-> v] S + sum_t c_t v_t[e] k_t^T, the path's terms in order
+        // t = 0 .. acc.
         const float Av = exp2f(s_L[vstop]);
-#pragma unroll
-        for (int r = 0; r < kRows4; ++r) {
-            sv[r].x *= Av;
-            sv[r].y *= Av;
-            sv[r].z *= Av;
-            sv[r].w *= Av;
-        }
-        for (int t = 0; t <= acc; ++t) {
-            const float4 k4 = *reinterpret_cast<const float4*>(kf + t * Dk + d4);
-            const float ct = s_c[t];
+        if constexpr (!kTiled) {
 #pragma unroll
             for (int r = 0; r < kRows4; ++r) {
-                const float w = ct * vf[t * ne + min(e0 + r * estep, ne - 1)];
-                sv[r].x = fmaf(w, k4.x, sv[r].x);
-                sv[r].y = fmaf(w, k4.y, sv[r].y);
-                sv[r].z = fmaf(w, k4.z, sv[r].z);
-                sv[r].w = fmaf(w, k4.w, sv[r].w);
+                sv[r].x *= Av;
+                sv[r].y *= Av;
+                sv[r].z *= Av;
+                sv[r].w *= Av;
+            }
+            for (int t = 0; t <= acc; ++t) {  // each k row's four values read once for all rows
+                const float4 k4 = *reinterpret_cast<const float4*>(kf + t * Dk + d4);
+                const float ct = s_c[t];
+#pragma unroll
+                for (int r = 0; r < kRows4; ++r) {
+                    const float w = ct * vf[t * ne + min(e0 + r * estep, ne - 1)];
+                    sv[r].x = fmaf(w, k4.x, sv[r].x);
+                    sv[r].y = fmaf(w, k4.y, sv[r].y);
+                    sv[r].z = fmaf(w, k4.z, sv[r].z);
+                    sv[r].w = fmaf(w, k4.w, sv[r].w);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < kRows4; ++r) {
+                const int e = e0 + r * estep;
+                if (e < ne) *reinterpret_cast<float4*>(S + static_cast<size_t>(es0 + e) * Dk + d4) = sv[r];
             }
         }
 #pragma unroll
-        for (int r = 0; r < kRows4; ++r) {
-            const int e = e0 + r * estep;
-            if (e < ne) *reinterpret_cast<float4*>(S + static_cast<size_t>(es0 + e) * Dk + d4) = sv[r];
+        for (int t = 0; t < (kTiled ? kTPW : 0); ++t) {
+            const int r0 = (rsel + kRowW * t) * 16;
+            if (r0 >= ne) continue;  // wave-uniform
+            const int row = r0 + lr;
+#pragma unroll
+            for (int j = 0; j < kJ; ++j) {
+                float4& x = sreg[t * kJ + j];
+                x.x *= Av;
+                x.y *= Av;
+                x.z *= Av;
+                x.w *= Av;
+            }
+            for (int tt = 0; tt <= acc; ++tt) {
+                const float w = s_c[tt] * vf[tt * ne + row];
+                const float* kr = kf + tt * Dk + 4 * lg;
+#pragma unroll
+                for (int j = 0; j < kJ; ++j) {
+                    const float4 k4 = *reinterpret_cast<const float4*>(kr + 16 * min(j, Dk / 16 - 1));
+                    float4& x = sreg[t * kJ + j];
+                    x.x = fmaf(w, k4.x, x.x);
+                    x.y = fmaf(w, k4.y, x.y);
+                    x.z = fmaf(w, k4.z, x.z);
+                    x.w = fmaf(w, k4.w, x.w);
+                }
+            }
+            if (nsel == 0) {  // wave-uniform: one writer per tile
+#pragma unroll
+                for (int j = 0; j < kJ; ++j)
+                    if (16 * j < Dk)
+                        *reinterpret_cast<float4*>(S + static_cast<size_t>(es0 + row) * Dk + 16 * j + 4 * lg) =
+                            sreg[t * kJ + j];
+            }
         }
-        __syncthreads();  // the workgroup's own state writes before its reads below
+        __syncthreads();  // the path rows in LDS are read before the verification's stores
     }
     if (!VERIFY || !a.do_verify) return;
 
@@ -261,31 +337,12 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
     // Rows padded by four floats: 16-byte aligned for vector reads, and the
     // 16-byte reads of eight lanes on consecutive rows fall on distinct banks.
     const int DkP = Dk + 4;
-    constexpr int kScP = kLaChunk + 4;
-    // K is read only for the scores W, so the state's chunks reuse its space.
-    constexpr int kKsSc = NMAX * (kLaMaxD + 4) > kLaRows * kScP ? NMAX * (kLaMaxD + 4) : kLaRows * kScP;
     float* Qs = lds;                      // [N][Dk + 4]
     float* Ks = Qs + NMAX * (kLaMaxD + 4);
-    float* Sc = Ks;                       // [ne][kLaChunk + 4], after W is complete
-    float* Vs = Ks + kKsSc;               // [N][ne]: this slice's dims of v
-    float* W = Vs + NMAX * kLaRows;       // [N][N]
-    // Every load of the phase goes first: the slice's state, all of its
-    // 32-column chunks as 16-byte loads (one per thread and chunk), then
-    // the rows of Q, K and the slice's V; the tree's parents and decays
-    // follow, and the LDS stores wait for all of them together.
-    constexpr int kNC = kLaMaxD / kLaChunk;
-    constexpr int kS4 = (kLaRows * kLaChunk / 4 + kLaThreads - 1) / kLaThreads;
-    const int n4 = ne * (kLaChunk / 4);
-    float4 sreg[kNC * kS4];
-#pragma unroll
-    for (int c = 0; c < kNC; ++c) {
-        const int c0 = min(c * kLaChunk, Dk - kLaChunk);  // Dk = 64: the spare chunks re-read the last
-#pragma unroll
-        for (int j = 0; j < kS4; ++j) {
-            const int x = min(tid + j * kLaThreads, n4 - 1), r = x / (kLaChunk / 4), c4 = x - r * (kLaChunk / 4);
-            sreg[c * kS4 + j] = *reinterpret_cast<const float4*>(S + static_cast<size_t>(es0 + r) * Dk + c0 + 4 * c4);
-        }
-    }
+    float* Vs = Ks + NMAX * (kLaMaxD + 4);  // [N][ne]: this slice's dims of v
+    float* W = Vs + NMAX * kLaRows;         // [N][N]
+    // The rows of Q, K and the slice's V are loaded next; the tree's parents
+    // and decays follow, and the LDS stores wait for all of them together.
     auto rk = [&](int i) { return ((static_cast<size_t>(b) * N + i) * H + h) * Dk; };
     auto rv = [&](int i) { return ((static_cast<size_t>(b) * N + i) * H + h) * Dv + es0; };
     auto qkv_rows = [&](auto bfc) {
@@ -352,95 +409,54 @@ __global__ __launch_bounds__(kLaThreads) void la_kernel(LaArgs a) {
         }
         W[i * N + j] = exp2f(s_L[i] - s_L[j]) * ((d0 + d1) + (d2 + d3));
     }
-    // Thread (e, group g): slice row e, nodes g, g + G, ... with G = 256 /
-    // kLaRows groups (threads of rows past ne idle).
-    const int e = tid % kLaRows, g = tid / kLaRows, G = kLaThreads / kLaRows;
-    constexpr int kPer = NMAX / (kLaThreads / kLaRows) > 1 ? NMAX / (kLaThreads / kLaRows) : 1;  // nodes per thread
-    float acc[kPer];
+    __syncthreads();  // W is complete
+    const int ntiles = (N + 15) / 16;
 #pragma unroll
-    for (int n = 0; n < kPer; ++n) acc[n] = 0.f;
-    // Chunk C: columns 32C .. 32C + 31 (a compile-time index, so the
-    // state's registers are never addressed dynamically).
-    auto chunk = [&](auto cidx) {
-        constexpr int C = decltype(cidx)::value;
-        const int c0 = C * kLaChunk;
-        __syncthreads();  // the previous chunk is consumed (and W is complete)
+    for (int t = 0; t < kTPW; ++t) {
+        const int r0 = (rsel + kRowW * t) * 16;
+        if (r0 >= ne) continue;  // wave-uniform
+        for (int nt = nsel; nt < ntiles; nt += kNodeW) {
+            const int node = nt * 16 + lr;
+            const float* qrow = Qs + min(node, N - 1) * DkP;
+            // two independent accumulator chains, added at the end
+            f32x4 ca = {0.f, 0.f, 0.f, 0.f}, cb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < kS4; ++j) {
-            const int x = tid + j * kLaThreads;
-            if (x < n4) {
-                const int r = x / (kLaChunk / 4), c4 = x - r * (kLaChunk / 4);
-                // (four scalar stores: a 16-byte store of the register
-                // array's element made the compiler keep the array in
-                // scratch memory)
-                float* dst = Sc + r * kScP + 4 * c4;
-                dst[0] = sreg[C * kS4 + j].x;
-                dst[1] = sreg[C * kS4 + j].y;
-                dst[2] = sreg[C * kS4 + j].z;
-                dst[3] = sreg[C * kS4 + j].w;
-            }
-        }
-        __syncthreads();
-        const float4* srow = reinterpret_cast<const float4*>(Sc + min(e, ne - 1) * kScP);
-        if (e >= ne) {  // a row past the slice (Dv not a multiple of kLaRows): nothing to add
-        } else if constexpr (NMAX > 16) {
-            // Large trees, four columns at a time: one 16-byte state read
-            // feeds this thread's kPer nodes as independent chains.  Rows
-            // past N hold stale LDS; their sums are never used.
-#pragma unroll 2
-            for (int c4 = 0; c4 < kLaChunk / 4; ++c4) {
-                const float4 s4 = srow[c4];
-#pragma unroll
-                for (int n = 0; n < kPer; ++n) {
-                    const int i = min(g + n * G, NMAX - 1);
-                    const float4 q4 = *reinterpret_cast<const float4*>(Qs + i * DkP + c0 + 4 * c4);
-                    float t = fmaf(s4.x, q4.x, acc[n]);
-                    t = fmaf(s4.y, q4.y, t);
-                    t = fmaf(s4.z, q4.z, t);
-                    acc[n] = fmaf(s4.w, q4.w, t);
+            for (int j = 0; j < kJ; ++j) {
+                if (16 * j < Dk) {  // workgroup-uniform
+                    const float4 q4 = *reinterpret_cast<const float4*>(qrow + 16 * j + 4 * lg);
+                    const float4 s4 = sreg[t * kJ + j];
+                    ca = __builtin_amdgcn_mfma_f32_16x16x4f32(s4.x, q4.x, ca, 0, 0, 0);
+                    cb = __builtin_amdgcn_mfma_f32_16x16x4f32(s4.y, q4.y, cb, 0, 0, 0);
+                    ca = __builtin_amdgcn_mfma_f32_16x16x4f32(s4.z, q4.z, ca, 0, 0, 0);
+                    cb = __builtin_amdgcn_mfma_f32_16x16x4f32(s4.w, q4.w, cb, 0, 0, 0);
                 }
             }
-        } else {  // small trees: only the nodes that exist
+            if (node < N) {
+                // rows e = r0 + 4g + c of node `node`: the decayed state term,
+                // then the tree's own terms over the ancestors j, ascending
+                const int e0 = r0 + 4 * lg;
+                const float base = exp2f(s_L[node]);
+                float o[4];
 #pragma unroll
-            for (int n = 0; n < kPer; ++n) {
-                const int i = g + n * G;
-                if (i < N) {
-                    const float4* qrow = reinterpret_cast<const float4*>(Qs + i * DkP + c0);
-                    float t = acc[n];
+                for (int c = 0; c < 4; ++c) o[c] = base * (ca[c] + cb[c]);
+                for (uint64_t m = s_anc[node]; m != 0ull; m &= m - 1ull) {
+                    const int j = __ffsll(static_cast<long long>(m)) - 1;
+                    const float w = W[node * N + j];
+                    const float4 v4 = *reinterpret_cast<const float4*>(Vs + j * ne + e0);
+                    o[0] = fmaf(w, v4.x, o[0]);
+                    o[1] = fmaf(w, v4.y, o[1]);
+                    o[2] = fmaf(w, v4.z, o[2]);
+                    o[3] = fmaf(w, v4.w, o[3]);
+                }
+                const size_t oi = ((static_cast<size_t>(b) * N + node) * H + h) * Dv + es0 + e0;
 #pragma unroll
-                    for (int c4 = 0; c4 < kLaChunk / 4; ++c4) {
-                        const float4 s4 = srow[c4], q4 = qrow[c4];
-                        t = fmaf(s4.x, q4.x, t);
-                        t = fmaf(s4.y, q4.y, t);
-                        t = fmaf(s4.z, q4.z, t);
-                        t = fmaf(s4.w, q4.w, t);
-                    }
-                    acc[n] = t;
+                for (int c = 0; c < 4; ++c) {
+                    if (bf16)
+                        static_cast<uint16_t*>(a.out)[oi + c] = static_cast<uint16_t>(f32_to_bf16_bits(o[c]));
+                    else
+                        static_cast<float*>(a.out)[oi + c] = o[c];
                 }
             }
-        }
-    };
-    static_assert(kNC == 4, "Dk is 64 or 128: two or four chunks");
-    chunk(std::integral_constant<int, 0>{});
-    chunk(std::integral_constant<int, 1>{});
-    if (Dk > 2 * kLaChunk) {  // workgroup-uniform
-        chunk(std::integral_constant<int, 2>{});
-        chunk(std::integral_constant<int, 3>{});
-    }
-#pragma unroll
-    for (int n = 0; n < kPer; ++n) {
-        const int i = g + n * G;
-        if (i < N && e < ne) {
-            float o = exp2f(s_L[i]) * acc[n];
-            for (uint64_t m = s_anc[i]; m != 0ull; m &= m - 1ull) {  // the ancestors j, ascending
-                const int j = __ffsll(static_cast<long long>(m)) - 1;
-                o = fmaf(W[i * N + j], Vs[j * ne + e], o);
-            }
-            const size_t oi = ((static_cast<size_t>(b) * N + i) * H + h) * Dv + es0 + e;
-            if (bf16)
-                static_cast<uint16_t*>(a.out)[oi] = static_cast<uint16_t>(f32_to_bf16_bits(o));
-            else
-                static_cast<float*>(a.out)[oi] = o;
         }
     }
 }
