@@ -48,6 +48,8 @@
 // fp32 (and any dtype) VALU path: 32 rows x 32 keys tiles through LDS.
 #include <stdlib.h>
 
+#include <atomic>
+
 #include "spec_common.h"
 #include "spec_internal.h"
 
@@ -1549,29 +1551,39 @@ static int resident_per_cu(K kernel, int threads) {
     return n;
 }
 
+// Queried once and cached (atomics: host threads may launch concurrently;
+// every thread computes the same value).
 static int device_cus() {
-    static int cus[64] = {0};
+    static std::atomic<int> cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int n = 0;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
-        cus[dev] = n;
+        cus[dev].store(n, std::memory_order_relaxed);
     }
-    return cus[dev];
+    return n;
 }
 
 template <int D, int RT, bool ROPE, int W = 1>
 static int mfma_resident() {
-    static int n = 0;
-    if (n == 0) n = resident_per_cu(attn_mfma<D, RT, ROPE, W>, 64 * W);
+    static std::atomic<int> cached{0};
+    int n = cached.load(std::memory_order_relaxed);
+    if (n == 0) {
+        n = resident_per_cu(attn_mfma<D, RT, ROPE, W>, 64 * W);
+        cached.store(n, std::memory_order_relaxed);
+    }
     return n;
 }
 
 template <int D, bool ROPE>
 static int mfma_wg_resident() {
-    static int n = 0;
-    if (n == 0) n = resident_per_cu(attn_mfma_wg<D, 2, wg_waves<D>(), ROPE>, 64 * wg_waves<D>());
+    static std::atomic<int> cached{0};
+    int n = cached.load(std::memory_order_relaxed);
+    if (n == 0) {
+        n = resident_per_cu(attn_mfma_wg<D, 2, wg_waves<D>(), ROPE>, 64 * wg_waves<D>());
+        cached.store(n, std::memory_order_relaxed);
+    }
     return n;
 }
 

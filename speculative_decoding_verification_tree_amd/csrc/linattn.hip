@@ -22,6 +22,7 @@
 // Both phases in one launch are the deferred update: the previous step's
 // commit folded into this step's verification (one state read and write).
 // Decay products are exp2 of differences of log2 prefix sums along root paths.
+#include <atomic>
 #include <type_traits>
 
 #include "spec_common.h"
@@ -475,11 +476,14 @@ static void launch_la_n(const LaArgs& a, const dim3& grid, hipStream_t stream) {
 // (queried once per device and phase combination).
 template <int NMAX, int ROWS>
 static long la_resident(const LaArgs& a) {
-    static long cache[64][3];
+    static std::atomic<long> cache[64][3];  // host threads may race to fill it (same value)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = -1;
     const int kind = a.do_commit && a.do_verify ? 0 : a.do_commit ? 1 : 2;
-    if (dev >= 0 && cache[dev][kind] > 0) return cache[dev][kind];
+    if (dev >= 0) {
+        const long c = cache[dev][kind].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
     int n = 0;
     hipError_t e;
     if (a.do_commit && a.do_verify)
@@ -493,7 +497,7 @@ static long la_resident(const LaArgs& a) {
     if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
         cus = 256;
     const long r = static_cast<long>(n) * cus;
-    if (dev >= 0) cache[dev][kind] = r;
+    if (dev >= 0) cache[dev][kind].store(r, std::memory_order_relaxed);
     return r;
 }
 

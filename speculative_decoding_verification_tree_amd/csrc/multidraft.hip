@@ -22,6 +22,8 @@
 // very arithmetic of the passes.  The grid is sized to be co-resident (the
 // waits need every part running); the waits are bounded, so a grid that is
 // not co-resident ends with accept_len = -1 instead of hanging.
+#include <atomic>
+
 #include "spec_common.h"
 #include "spec_internal.h"
 
@@ -431,18 +433,20 @@ size_t multidraft_workspace_bytes(int B, int V) {
 // (every part of a request must run concurrently), at most kMdMaxParts and
 // about a thousand tokens each at least.
 static int md_parts(int B, int V) {
-    static int resident[64] = {0};
+    static std::atomic<int> resident[64];  // per device, cached (host threads may race to fill it)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
-    if (resident[dev] == 0) {
+    int res = resident[dev].load(std::memory_order_relaxed);
+    if (res == 0) {
         int per_cu = 0, cus = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, accept_md, kMdThreads, 0) != hipSuccess ||
             per_cu < 1)
             per_cu = 1;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
-        resident[dev] = per_cu * cus;
+        res = per_cu * cus;
+        resident[dev].store(res, std::memory_order_relaxed);
     }
-    long P = resident[dev] / std::max(B, 1);
+    long P = res / std::max(B, 1);
     P = std::min<long>(P, kMdMaxParts);
     P = std::min<long>(P, (V + 1023) / 1024);
     return static_cast<int>(std::max<long>(P, 1));
