@@ -1102,6 +1102,24 @@ __global__ __launch_bounds__(256) void attn_valu(AttnArgs a) {
         }
     };
     const T* qp = static_cast<const T*>(a.q);
+    const size_t head = (static_cast<size_t>(b) * a.Hkv + g) * a.cap;
+    const T* kp = static_cast<const T*>(a.k) + head * D;
+    const T* vp = static_cast<const T*>(a.v) + head * D;
+    // fp32: the K and V rows of one 32-key tile as 16-byte loads, all in
+    // flight at once; the first tile's go out with the queries', and each
+    // next tile's while the current one is computed.
+    float4 kr[sizeof(T) == 4 ? NV4 : 1], vr[sizeof(T) == 4 ? NV4 : 1];
+    auto load_tile = [&](int kb) {
+        if constexpr (sizeof(T) == 4) {
+#pragma unroll
+            for (int i = 0; i < NV4; ++i) {
+                const int e4 = tid + 256 * i, kk = e4 / (D / 4), d4 = e4 % (D / 4);
+                const size_t off = static_cast<size_t>(min(kb + kk, Tk - 1)) * D + 4 * d4;
+                kr[i] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(kp) + off);
+                vr[i] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(vp) + off);
+            }
+        }
+    };
     if constexpr (sizeof(T) == 4) {
         // fp32: 16-byte loads, all of a thread's issued before its LDS stores
         float4 qr[NV4];
@@ -1113,6 +1131,7 @@ __global__ __launch_bounds__(256) void attn_valu(AttnArgs a) {
             qr[i] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(qp) +
                                                      ((static_cast<size_t>(b) * a.N + node) * a.Hq + hq) * D + 4 * d4);
         }
+        load_tile(k0);
 #pragma unroll
         for (int i = 0; i < NV4; ++i) {
             const int e4 = tid + 256 * i, lr = e4 / (D / 4), d4 = e4 % (D / 4);
@@ -1147,28 +1166,26 @@ __global__ __launch_bounds__(256) void attn_valu(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < DPL; ++j) o[j] = 0.f;
 
-    const size_t head = (static_cast<size_t>(b) * a.Hkv + g) * a.cap;
-    const T* kp = static_cast<const T*>(a.k) + head * D;
-    const T* vp = static_cast<const T*>(a.v) + head * D;
-
     for (int kb = k0; kb < k1; kb += 32) {
         __syncthreads();
         if constexpr (sizeof(T) == 4) {
-            // every 16-byte load of the tile in flight before the first LDS store
-            float4 kr[NV4], vr[NV4];
 #pragma unroll
             for (int i = 0; i < NV4; ++i) {
                 const int e4 = tid + 256 * i, kk = e4 / (D / 4), d4 = e4 % (D / 4);
-                const size_t off = static_cast<size_t>(min(kb + kk, Tk - 1)) * D + 4 * d4;
-                kr[i] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(kp) + off);
-                vr[i] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(vp) + off);
+                // (component stores: a 16-byte store of the register array's
+                // element made the compiler keep the array in scratch)
+                float* kd = &s_k[kk][4 * d4];
+                float* vd = &s_v[kk][4 * d4];
+                kd[0] = kr[i].x;
+                kd[1] = kr[i].y;
+                kd[2] = kr[i].z;
+                kd[3] = kr[i].w;
+                vd[0] = vr[i].x;
+                vd[1] = vr[i].y;
+                vd[2] = vr[i].z;
+                vd[3] = vr[i].w;
             }
-#pragma unroll
-            for (int i = 0; i < NV4; ++i) {
-                const int e4 = tid + 256 * i, kk = e4 / (D / 4), d4 = e4 % (D / 4);
-                *reinterpret_cast<float4*>(&s_k[kk][4 * d4]) = kr[i];
-                *reinterpret_cast<float4*>(&s_v[kk][4 * d4]) = vr[i];
-            }
+            if (kb + 32 < k1) load_tile(kb + 32);  // workgroup-uniform
         } else {
             for (int e = tid; e < 32 * D; e += 256) {
                 const int kk = e / D, d = e % D;
