@@ -77,6 +77,8 @@ CASES = [
     # state rows (32-row slices would not all run at once)
     (8, 46, 12, 128, 128, "bf16", True, True),
     (8, 46, 12, 128, 128, "f32", True, False),
+    # 512 pairs of 24-node trees: the whole state per workgroup, the large-tree instance
+    (32, 24, 16, 128, 128, "bf16", True, True),
 ]
 
 
@@ -106,6 +108,7 @@ def test_la_verify_and_commit_match_oracle(B, N, H, Dk, Dv, dtype, tree, decay):
     (3, 4, 8, 8),    # both within the small-tree launch
     (2, 4, 16, 40),
     (64, 8, 8, 8),   # one workgroup per (head, request), the whole state
+    (64, 8, 24, 20),  # the same with the large-tree instance
 ])
 def test_la_deferred_commit_equals_commit_then_verify(B, H, Np, Nv):
     announce(f"linear attention: deferred commit folded into the next verification B={B} H={H} "
