@@ -1480,8 +1480,10 @@ __global__ __launch_bounds__(kFThreads) void accept_filter(AcceptArgs a) { filte
 // The counts, the digit, the candidate set and the fixed-point masses are
 // the same integers as in one workgroup's passes, so the records are
 // identical.
-template <int EPT, bool NT>
-__global__ __launch_bounds__(kThreads) void filt_chunk(AcceptArgs a) {
+// FULL: a whole chunk of a 16-byte-aligned row, so no element needs a
+// range test (every chunk of a row but its last).
+template <int EPT, bool NT, bool FULL>
+__device__ __forceinline__ void filt_chunk_body(const AcceptArgs& a) {
     const int c = blockIdx.x, rid = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     __shared__ uint32_t s_h[2048];
     __shared__ WaveRed s_red;
@@ -1489,8 +1491,21 @@ __global__ __launch_bounds__(kThreads) void filt_chunk(AcceptArgs a) {
     __shared__ int s_dc, s_nb, s_nk;
     const float* row = a.logits + static_cast<size_t>(rid) * a.V;
     const int x0 = c * a.chunk, x1 = min(x0 + a.chunk, a.V);
-    const bool vec4 = a.vec4 != 0;
-    const Vals<EPT> v = load_chunk<EPT, NT>(row, x0, x1, vec4, -INFINITY);
+    const bool vec4 = FULL || a.vec4 != 0;
+    Vals<EPT> v;
+    if constexpr (FULL) {
+#pragma unroll
+        for (int j = 0; j < EPT / 4; ++j) {
+            const float* src = row + x0 + 4 * (tid + kThreads * j);
+            const float4 f = NT ? ld_stream_f4(src) : *reinterpret_cast<const float4*>(src);
+            v.v[4 * j] = f.x;
+            v.v[4 * j + 1] = f.y;
+            v.v[4 * j + 2] = f.z;
+            v.v[4 * j + 3] = f.w;
+        }
+    } else {
+        v = load_chunk<EPT, NT>(row, x0, x1, vec4, -INFINITY);
+    }
     for (int i = tid; i < 2048; i += kThreads) s_h[i] = 0u;
     if (tid == 0) {
         s_dc = 0;
@@ -1509,8 +1524,8 @@ __global__ __launch_bounds__(kThreads) void filt_chunk(AcceptArgs a) {
     uint32_t inr = 0u;  // bit e: element e in range
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-        const bool in = elem_off(e, vec4) < lim;
-        inr |= static_cast<uint32_t>(in) << e;
+        const bool in = FULL || elem_off(e, vec4) < lim;
+        if constexpr (!FULL) inr |= static_cast<uint32_t>(in) << e;
         kk[e] = logit_key(v.v[e]);
         if (in) atomicAdd(&s_h[kk[e] >> 21], 1u);
     }
@@ -1561,7 +1576,7 @@ __global__ __launch_bounds__(kThreads) void filt_chunk(AcceptArgs a) {
     int total = 0;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-        m[e] = __ballot(((inr >> e) & 1u) && static_cast<int>(kk[e] >> 21) >= dc);
+        m[e] = __ballot((FULL || ((inr >> e) & 1u)) && static_cast<int>(kk[e] >> 21) >= dc);
         total += __popcll(m[e]);
     }
     if (total > 0) {  // wave-uniform
@@ -1579,6 +1594,14 @@ __global__ __launch_bounds__(kThreads) void filt_chunk(AcceptArgs a) {
     }
     __syncthreads();
     if (tid == 0) a.frec[slot] = ChunkRec{M, arg, min(s_nb, kFBinCap + 1), min(s_nk, kFKeyCap + 1)};
+}
+
+template <int EPT, bool NT>
+__global__ __launch_bounds__(kThreads) void filt_chunk(AcceptArgs a) {
+    if (a.vec4 != 0 && (static_cast<int>(blockIdx.x) + 1) * a.chunk <= a.V)  // workgroup-uniform
+        filt_chunk_body<EPT, NT, true>(a);
+    else
+        filt_chunk_body<EPT, NT, false>(a);
 }
 
 // (from at most kFCandRow candidates: four waves keep the selection's
