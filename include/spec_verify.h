@@ -337,7 +337,10 @@ typedef struct {
  *   state  [B][H][Dv][Dk] fp32, device: the committed state (read); with
  *          pending != NULL it is first advanced in place by that step's
  *          accepted factors (the deferred commit), then read
- *   q, k   [B][N][H][Dk], v and out [B][N][H][Dv] (dtype), device
+ *   q, k   [B][N][H][Dk], v and out [B][N][H][Dv] (dtype), device; any
+ *          alignment of the element type (16-byte aligned q, k, v and
+ *          factor rows are read as 16-byte vectors, others element by
+ *          element, with the same results)
  *   alpha  [B][N][H] fp32 decays in (0, 1] or NULL; parent [B][N] or NULL
  * Errors: SPEC_EINVAL (null pointers, sizes, a state pointer not 16-byte
  * aligned), SPEC_EUNSUPPORTED (Dk, Dv). */
