@@ -86,6 +86,9 @@ struct AcceptArgs {
     RowRec* rowrec;  // truncated rows (aliases rowstat's space)
     Decision* dec;
     ChunkStat* cstat;
+    // [B][nchunk][2][kSubMax]: per 1024-token slice of each stop-row chunk,
+    // the residual (or bonus) mass, then the plain mass
+    double* cslice;
     int B, N, V, chunk, nchunk, rule;  // rule 0 = rejection, 1 = typical
     int lg_seg;                        // log2 of the lanes per row in the decision: 2^lg_seg >= min(nchunk, 64)
     int vec4;                          // rows are 16-byte aligned: 16-byte loads
@@ -118,6 +121,10 @@ constexpr int kFCandRow = 4096;
 constexpr long kFMaxSlots = 65536;
 
 constexpr int kThreads = 256;
+// Slices of a chunk for the token search: four entries of every thread
+// (1024 tokens, contiguous in both load layouts); at most 8 per chunk.
+constexpr int kSubTokens = 4 * kThreads;
+constexpr int kSubMax = 8;
 
 // Helpers that take LDS arrays by pointer are force-inlined: called out of
 // line they receive generic pointers, whose LDS-aperture test this compiler
@@ -134,18 +141,29 @@ __device__ __forceinline__ double block_sum_d(double v, double* s_red) {
     return s_red[0] + s_red[1] + s_red[2] + s_red[3];
 }
 
-__device__ __forceinline__ void block_sum2_d(double& a, double& b, double* s_red) {
-    a = wave_sum(a);
-    b = wave_sum(b);
+// Block sums of NS pairs of per-slice values (s_sl: 8 * NS doubles); every
+// thread gets the totals, the waves added in a fixed order.
+template <int NS>
+__device__ __forceinline__ void block_sum_slices(double (&x)[NS], double (&y)[NS], double* s_sl) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        x[j] = wave_sum(x[j]);
+        y[j] = wave_sum(y[j]);
+    }
     if (lane == 0) {
-        s_red[wv] = a;
-        s_red[4 + wv] = b;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            s_sl[wv * 2 * NS + j] = x[j];
+            s_sl[wv * 2 * NS + NS + j] = y[j];
+        }
     }
     __syncthreads();
-    a = s_red[0] + s_red[1] + s_red[2] + s_red[3];
-    b = s_red[4] + s_red[5] + s_red[6] + s_red[7];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        x[j] = ((s_sl[j] + s_sl[2 * NS + j]) + s_sl[4 * NS + j]) + s_sl[6 * NS + j];
+        y[j] = ((s_sl[NS + j] + s_sl[3 * NS + j]) + s_sl[5 * NS + j]) + s_sl[7 * NS + j];
+    }
 }
 
 __device__ __forceinline__ void block_argmax(float& v, int& i, float* s_v, int* s_i) {
@@ -740,7 +758,9 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
 // sum 2^((l - max) * log2(e) / T) (MODE_BONUS), or only the max (MODE_ARGMAX).
 template <int EPT, bool FILT = false>
 __device__ __forceinline__ ChunkStat chunk_work(const AcceptArgs& a, int b, const Decision& d, int c, WaveRed* s_red,
-                                                double* s_r2) {
+                                                double* s_sl) {
+    constexpr int NS = EPT / 4;  // 1024-token slices of the chunk
+    static_assert(NS >= 1 && NS <= kSubMax, "slices per chunk");
     const float* row = a.logits + (static_cast<size_t>(b) * a.N + d.v) * a.V;
     const int x0 = c * a.chunk, x1 = min(x0 + a.chunk, a.V);
     ChunkStat cs;
@@ -748,14 +768,16 @@ __device__ __forceinline__ ChunkStat chunk_work(const AcceptArgs& a, int b, cons
     cs.M = 0.f;
     cs.arg = 0;
     const bool vec4 = a.vec4 != 0;
+    const int lim = x1 - (x0 + (vec4 ? 4 * static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x)));
+    // Per slice (entries 4j .. 4j + 3 of every thread): fp32 pairwise per
+    // thread, fp64 across threads; the chunk's masses are the slices' sums.
+    double sa[NS], sb[NS];
     if (d.mode == MODE_RESID) {
         const float* qrow = a.draft + (static_cast<size_t>(b) * a.N + d.c) * a.V;
         const float invS = static_cast<float>(1.0 / d.S);
         const float c2 = 1.4426950408889634f / a.T;
         Vals<EPT> lvals, qvals;
         load_chunk2<EPT>(row, qrow, x0, x1, vec4, lvals, qvals);
-        const int lim = x1 - (x0 + (vec4 ? 4 * static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x)));
-        // Non-negative terms: pairwise in fp32 per thread, fp64 across threads.
         float rv[EPT], pvv[EPT];
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
@@ -764,20 +786,61 @@ __device__ __forceinline__ ChunkStat chunk_work(const AcceptArgs& a, int b, cons
             pvv[e] = pv;
             rv[e] = in ? fmaxf(pv - qvals.v[e], 0.f) : 0.f;
         }
-        pairwise_sum<EPT>(rv);
-        pairwise_sum<EPT>(pvv);
-        double r = rv[0], p = pvv[0];
-        block_sum2_d(r, p, s_r2);
-        cs.m1 = r;
-        cs.m2 = p;
-    } else {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            sa[j] = (rv[4 * j] + rv[4 * j + 1]) + (rv[4 * j + 2] + rv[4 * j + 3]);
+            sb[j] = (pvv[4 * j] + pvv[4 * j + 1]) + (pvv[4 * j + 2] + pvv[4 * j + 3]);
+        }
+        block_sum_slices<NS>(sa, sb, s_sl);
+    } else if (d.mode == MODE_BONUS) {
+        // 2^((l - M) * log2(e) / T) relative to the chunk max M (the truncated
+        // rule keeps only tokens at or above tau; the max stays the chunk's)
+        const Vals<EPT> v = load_chunk<EPT>(row, x0, x1, vec4, -INFINITY);
+        float bm = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) bm = fmaxf(bm, v.v[e]);
+        bm = wave_max(bm);
+        if ((threadIdx.x & 63) == 0) s_red->m[threadIdx.x >> 6] = bm;
+        __syncthreads();
+        const float M = fmaxf(fmaxf(s_red->m[0], s_red->m[1]), fmaxf(s_red->m[2], s_red->m[3]));
+        const float c2 = 1.4426950408889634f / a.T;
+        float ex[EPT];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const bool in = elem_off(e, vec4) < lim && (!FILT || logit_key(v.v[e]) >= d.tau);
+            ex[e] = in ? __builtin_amdgcn_exp2f((v.v[e] - M) * c2) : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            sa[j] = (ex[4 * j] + ex[4 * j + 1]) + (ex[4 * j + 2] + ex[4 * j + 3]);
+            sb[j] = 0.0;
+        }
+        block_sum_slices<NS>(sa, sb, s_sl);
+        cs.M = M;
+    } else {  // MODE_ARGMAX
         float M;
         int arg;
         double S, A2;
-        chunk_stats<EPT, FILT>(row, x0, x1, vec4, d.mode == MODE_BONUS ? a.T : 0.f, M, arg, S, A2, s_red, d.tau);
+        chunk_stats<EPT, FILT>(row, x0, x1, vec4, 0.f, M, arg, S, A2, s_red, d.tau);
         cs.M = M;
         cs.arg = arg;
-        cs.m1 = S;
+        return cs;
+    }
+    double m1 = 0.0, m2 = 0.0;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        m1 += sa[j];
+        m2 += sb[j];
+    }
+    cs.m1 = m1;
+    cs.m2 = m2;
+    if (NS >= 4 && threadIdx.x < 2 * NS) {  // the slices, for the token search of chunks of four or more
+        const int j = threadIdx.x % NS, which = threadIdx.x / NS;
+        double val = 0.0;
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+            if (i == j) val = which ? sb[i] : sa[i];
+        a.cslice[(static_cast<size_t>(b) * a.nchunk + c) * (2 * kSubMax) + which * kSubMax + j] = val;
     }
     return cs;
 }
@@ -786,10 +849,10 @@ template <int EPT, int RPW, bool FILT = false>
 __global__ __launch_bounds__(kThreads) void accept_sample(AcceptArgs a) {
     const int c = blockIdx.x, b = blockIdx.y;
     __shared__ WaveRed s_red;
-    __shared__ double s_r2[8];
+    __shared__ double s_sl[8 * (EPT / 4)];
     const Decision d = decide_request<RPW, FILT>(a, b, c == 0);
     if (d.mode == MODE_DONE) return;
-    const ChunkStat cs = chunk_work<EPT, FILT>(a, b, d, c, &s_red, s_r2);
+    const ChunkStat cs = chunk_work<EPT, FILT>(a, b, d, c, &s_red, s_sl);
     if (threadIdx.x == 0) a.cstat[static_cast<size_t>(b) * a.nchunk + c] = cs;
 }
 
@@ -948,9 +1011,9 @@ __device__ __forceinline__ void select_token(const AcceptArgs& a, int b, const D
     if (ih != 0x7fffffff && hit == ih) s_base = hit_base;
     __syncthreads();
 
-    // Token inside the chosen chunk, from its coalesced layout: row j of the
-    // layout is W*kThreads consecutive tokens, W per thread (W = 4 with
-    // 16-byte loads, else 1).
+    // The chunk's slice that holds t, from the slice masses the sampling
+    // pass stored (the same fp32 terms, in the units of the chunk scan),
+    // then the token inside that slice.
     const int pc = s_pick;
     const double base = s_base;
     const int x0 = pc * a.chunk, x1 = min(x0 + a.chunk, a.V);
@@ -964,46 +1027,75 @@ __device__ __forceinline__ void select_token(const AcceptArgs& a, int b, const D
 #pragma unroll
     for (int k = 0; k < CPT; ++k)
         if (tid * CPT + k == pc) s_v[0] = cs[k].M;
+    __shared__ int s_js;
+    __shared__ double s_sbase;
+    // Chunks of two slices (8 entries a thread) are searched whole: there
+    // the slice masses' extra round trip costs more than the reload saves.
+    constexpr int NS = EPT / 4;
+    constexpr bool kSlices = NS >= 4;
+    // (every wave loads, from clamped slots: no load under a branch)
+    const size_t so = (static_cast<size_t>(b) * a.nchunk + pc) * (2 * kSubMax) + (usep ? kSubMax : 0);
+    const double raw = kSlices ? a.cslice[so + min(lane, NS - 1)] : 0.0;
+    __syncthreads();  // s_v[0]
+    if (kSlices && wave == 0) {
+        const double scl = d.mode == MODE_BONUS ? exp2((static_cast<double>(s_v[0]) - Mg) * c2d) : 1.0;
+        const double w = lane < NS ? raw * scl : 0.0;
+        const double incl = wave_incl_scan(w);
+        const uint64_t hm = __ballot(w > 0.0 && base + incl > t), nz = __ballot(w > 0.0);
+        const int jh = hm ? __ffsll(static_cast<long long>(hm)) - 1 : -1;
+        const int jl = nz ? 63 - __clzll(static_cast<long long>(nz)) : 0;
+        const double bef = __shfl(incl - w, jh >= 0 ? jh : 0);
+        if (lane == 0) {
+            // the first slice whose mass reaches past t, else the last slice
+            // with mass and its last token with weight
+            s_js = jh >= 0 ? jh : jl;
+            s_sbase = jh >= 0 ? base + bef : -INFINITY;
+        }
+    }
     __syncthreads();
     const float Mc = s_v[0];
     const double scale = d.mode == MODE_BONUS ? exp2((static_cast<double>(Mc) - Mg) * c2d) : 1.0;
-    // Thread tid owns tokens first .. first + EPT - 1 of the chunk; weights
-    // of tokens past the chunk end are 0.
-    const int first = x0 + tid * EPT;
-    Vals<EPT> lvals, qvals;
-    load_run2<EPT>(row, qrow, first, x1, vec4, lvals, qvals);
-    double wv[EPT];
+    const int js = kSlices ? s_js : 0;
+    const double sbase = kSlices ? s_sbase : base;
+    // Thread tid owns tokens first .. first + RL - 1 of the slice (or of the
+    // chunk); weights of tokens past its end are 0.
+    constexpr int RL = kSlices ? 4 : EPT;
+    const int xs1 = kSlices ? min(x0 + (js + 1) * kSubTokens, x1) : x1;
+    const int first = x0 + js * kSubTokens + tid * RL;
+    Vals<RL> lvals, qvals;
+    load_run2<RL>(row, qrow, first, xs1, vec4, lvals, qvals);
+    double wv[RL];
     if (d.mode == MODE_RESID) {
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
+        for (int e = 0; e < RL; ++e) {
             const float pv = target_prob(lvals.v[e], d.M, c2, invS);
             const float wgt = usep ? pv : fmaxf(pv - qvals.v[e], 0.f);
-            const bool in = first + e < x1 && (!FILT || logit_key(lvals.v[e]) >= d.tau);
+            const bool in = first + e < xs1 && (!FILT || logit_key(lvals.v[e]) >= d.tau);
             wv[e] = in ? static_cast<double>(wgt) : 0.0;
         }
     } else {
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
+        for (int e = 0; e < RL; ++e) {
             const float wgt = __builtin_amdgcn_exp2f((lvals.v[e] - Mc) * c2);
-            const bool in = first + e < x1 && (!FILT || logit_key(lvals.v[e]) >= d.tau);
+            const bool in = first + e < xs1 && (!FILT || logit_key(lvals.v[e]) >= d.tau);
             wv[e] = in ? static_cast<double>(wgt) * scale : 0.0;
         }
     }
     // Mass before this thread's run: block exclusive scan of the run totals.
     double mine = 0.0;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) mine += wv[e];
+    for (int e = 0; e < RL; ++e) mine += wv[e];
     const double incl_r = wave_incl_scan(mine);
     if (lane == 63) s_wtot[4 + wave] = incl_r;  // slots 4..7: the chunk scan's 0..3 may still be read
     __syncthreads();
-    double c = base + (incl_r - mine);
+    double c = sbase + (incl_r - mine);
     for (int k = 0; k < wave; ++k) c += s_wtot[4 + k];
     // Walk the run in token order: the first token whose cumulative mass
     // exceeds t, and the last token with weight (the fallback when rounding
-    // leaves the chunk's recomputed mass short of t).
+    // leaves the slice's recomputed mass short of t).
     int xhit = 0x7fffffff, lastnz = -1;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
+    for (int e = 0; e < RL; ++e) {
         const bool nz = wv[e] > 0.0;
         c += wv[e];
         lastnz = nz ? first + e : lastnz;
@@ -1622,6 +1714,8 @@ AcceptPlan plan_accept(int B, int N, int V) {
     off = align_up(off + static_cast<size_t>(B) * sizeof(Decision), 256);
     p.off_cstat = off;
     off = align_up(off + static_cast<size_t>(B) * p.nchunk * sizeof(ChunkStat), 256);
+    p.off_cslice = off;
+    off = align_up(off + static_cast<size_t>(B) * p.nchunk * 2 * kSubMax * sizeof(double), 256);
     p.ws_bytes = off;
     const size_t slots = static_cast<size_t>(B) * N * p.nchunk;
     p.off_frec = off;
@@ -1697,6 +1791,7 @@ int launch_accept(int rule, int B, int N, int V, const float* logits, const floa
     a.rowrec = reinterpret_cast<RowRec*>(ws + p.off_rowstat);  // B*N records fit in B*N*nchunk RowStats
     a.dec = reinterpret_cast<Decision*>(ws + p.off_dec);
     a.cstat = reinterpret_cast<ChunkStat*>(ws + p.off_cstat);
+    a.cslice = reinterpret_cast<double*>(ws + p.off_cslice);
     a.B = B;
     a.N = N;
     a.V = V;

@@ -38,7 +38,7 @@ int launch_verify_attn(const spec_attn_desc& d, const AttnPlan& plan, const void
 struct AcceptPlan {
     int chunk;   // vocabulary entries per chunk
     int nchunk;
-    size_t off_rowstat, off_dec, off_cstat, ws_bytes;
+    size_t off_rowstat, off_dec, off_cstat, off_cslice, ws_bytes;
     // the truncation split over chunks, past ws_bytes
     size_t off_frec, off_fbins, off_fkeys, ws_filt_bytes;
 };
