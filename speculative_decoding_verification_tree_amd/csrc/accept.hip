@@ -141,29 +141,25 @@ __device__ __forceinline__ double block_sum_d(double v, double* s_red) {
     return s_red[0] + s_red[1] + s_red[2] + s_red[3];
 }
 
-// Block sums of NS pairs of per-slice values (s_sl: 8 * NS doubles); every
-// thread gets the totals, the waves added in a fixed order.
-template <int NS>
-__device__ __forceinline__ void block_sum_slices(double (&x)[NS], double (&y)[NS], double* s_sl) {
+// Block sums of NS per-slice values and, with TWO, one more value (s_sl:
+// 4 * (NS + 1) doubles); every thread gets the totals, the waves added in a
+// fixed order.
+template <int NS, bool TWO>
+__device__ __forceinline__ void block_sum_slices(double (&x)[NS], double& y, double* s_sl) {
+    constexpr int W = NS + 1;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-        x[j] = wave_sum(x[j]);
-        y[j] = wave_sum(y[j]);
-    }
+    for (int j = 0; j < NS; ++j) x[j] = wave_sum(x[j]);
+    if constexpr (TWO) y = wave_sum(y);
     if (lane == 0) {
 #pragma unroll
-        for (int j = 0; j < NS; ++j) {
-            s_sl[wv * 2 * NS + j] = x[j];
-            s_sl[wv * 2 * NS + NS + j] = y[j];
-        }
+        for (int j = 0; j < NS; ++j) s_sl[wv * W + j] = x[j];
+        if constexpr (TWO) s_sl[wv * W + NS] = y;
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-        x[j] = ((s_sl[j] + s_sl[2 * NS + j]) + s_sl[4 * NS + j]) + s_sl[6 * NS + j];
-        y[j] = ((s_sl[NS + j] + s_sl[3 * NS + j]) + s_sl[5 * NS + j]) + s_sl[7 * NS + j];
-    }
+    for (int j = 0; j < NS; ++j) x[j] = ((s_sl[j] + s_sl[W + j]) + s_sl[2 * W + j]) + s_sl[3 * W + j];
+    if constexpr (TWO) y = ((s_sl[NS] + s_sl[W + NS]) + s_sl[2 * W + NS]) + s_sl[3 * W + NS];
 }
 
 __device__ __forceinline__ void block_argmax(float& v, int& i, float* s_v, int* s_i) {
@@ -770,8 +766,9 @@ __device__ __forceinline__ ChunkStat chunk_work(const AcceptArgs& a, int b, cons
     const bool vec4 = a.vec4 != 0;
     const int lim = x1 - (x0 + (vec4 ? 4 * static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x)));
     // Per slice (entries 4j .. 4j + 3 of every thread): fp32 pairwise per
-    // thread, fp64 across threads; the chunk's masses are the slices' sums.
-    double sa[NS], sb[NS];
+    // thread, fp64 across threads; the chunk's mass is the slices' sum.  The
+    // plain target mass (the residual's rare fallback) is kept per chunk only.
+    double sa[NS], sb = 0.0;
     if (d.mode == MODE_RESID) {
         const float* qrow = a.draft + (static_cast<size_t>(b) * a.N + d.c) * a.V;
         const float invS = static_cast<float>(1.0 / d.S);
@@ -787,11 +784,10 @@ __device__ __forceinline__ ChunkStat chunk_work(const AcceptArgs& a, int b, cons
             rv[e] = in ? fmaxf(pv - qvals.v[e], 0.f) : 0.f;
         }
 #pragma unroll
-        for (int j = 0; j < NS; ++j) {
-            sa[j] = (rv[4 * j] + rv[4 * j + 1]) + (rv[4 * j + 2] + rv[4 * j + 3]);
-            sb[j] = (pvv[4 * j] + pvv[4 * j + 1]) + (pvv[4 * j + 2] + pvv[4 * j + 3]);
-        }
-        block_sum_slices<NS>(sa, sb, s_sl);
+        for (int j = 0; j < NS; ++j) sa[j] = (rv[4 * j] + rv[4 * j + 1]) + (rv[4 * j + 2] + rv[4 * j + 3]);
+        pairwise_sum<EPT>(pvv);
+        sb = pvv[0];
+        block_sum_slices<NS, true>(sa, sb, s_sl);
     } else if (d.mode == MODE_BONUS) {
         // 2^((l - M) * log2(e) / T) relative to the chunk max M (the truncated
         // rule keeps only tokens at or above tau; the max stays the chunk's)
@@ -811,11 +807,8 @@ __device__ __forceinline__ ChunkStat chunk_work(const AcceptArgs& a, int b, cons
             ex[e] = in ? __builtin_amdgcn_exp2f((v.v[e] - M) * c2) : 0.f;
         }
 #pragma unroll
-        for (int j = 0; j < NS; ++j) {
-            sa[j] = (ex[4 * j] + ex[4 * j + 1]) + (ex[4 * j + 2] + ex[4 * j + 3]);
-            sb[j] = 0.0;
-        }
-        block_sum_slices<NS>(sa, sb, s_sl);
+        for (int j = 0; j < NS; ++j) sa[j] = (ex[4 * j] + ex[4 * j + 1]) + (ex[4 * j + 2] + ex[4 * j + 3]);
+        block_sum_slices<NS, false>(sa, sb, s_sl);
         cs.M = M;
     } else {  // MODE_ARGMAX
         float M;
@@ -826,21 +819,18 @@ __device__ __forceinline__ ChunkStat chunk_work(const AcceptArgs& a, int b, cons
         cs.arg = arg;
         return cs;
     }
-    double m1 = 0.0, m2 = 0.0;
+    double m1 = 0.0;
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-        m1 += sa[j];
-        m2 += sb[j];
-    }
+    for (int j = 0; j < NS; ++j) m1 += sa[j];
     cs.m1 = m1;
-    cs.m2 = m2;
-    if (NS >= 4 && threadIdx.x < 2 * NS) {  // the slices, for the token search of chunks of four or more
-        const int j = threadIdx.x % NS, which = threadIdx.x / NS;
+    cs.m2 = sb;
+    if (NS >= 4 && threadIdx.x < NS) {  // the slices, for the token search of chunks of four or more
+        const int j = threadIdx.x;
         double val = 0.0;
 #pragma unroll
         for (int i = 0; i < NS; ++i)
-            if (i == j) val = which ? sb[i] : sa[i];
-        a.cslice[(static_cast<size_t>(b) * a.nchunk + c) * (2 * kSubMax) + which * kSubMax + j] = val;
+            if (i == j) val = sa[i];
+        a.cslice[(static_cast<size_t>(b) * a.nchunk + c) * kSubMax + j] = val;
     }
     return cs;
 }
@@ -849,7 +839,7 @@ template <int EPT, int RPW, bool FILT = false>
 __global__ __launch_bounds__(kThreads) void accept_sample(AcceptArgs a) {
     const int c = blockIdx.x, b = blockIdx.y;
     __shared__ WaveRed s_red;
-    __shared__ double s_sl[8 * (EPT / 4)];
+    __shared__ double s_sl[4 * (EPT / 4 + 1)];
     const Decision d = decide_request<RPW, FILT>(a, b, c == 0);
     if (d.mode == MODE_DONE) return;
     const ChunkStat cs = chunk_work<EPT, FILT>(a, b, d, c, &s_red, s_sl);
@@ -900,6 +890,64 @@ __device__ __forceinline__ void load_run2(const float* row, const float* qrow, i
             l.v[e] = in ? lv[e] : -INFINITY;
             q.v[e] = in ? qv[e] : 0.f;
         }
+    }
+}
+
+// The token search over [xs0, xs1): thread tid owns tokens xs0 + RL*tid ..
+// + RL - 1 (weights past xs1 are 0); base is the mass before xs0 (-inf:
+// take the last token with weight).
+template <int RL, bool FILT>
+__device__ __forceinline__ void search_run(const AcceptArgs& a, const Decision& d, const float* row,
+                                           const float* qrow, int xs0, int xs1, bool vec4, double base, bool usep,
+                                           float Mc, double scale, float invS, float c2, double t, int x0, int32_t* out,
+                                           double* s_wtot, int* s_mn, int* s_mx) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int first = xs0 + tid * RL;
+    Vals<RL> lvals, qvals;
+    load_run2<RL>(row, qrow, first, xs1, vec4, lvals, qvals);
+    double wv[RL];
+    if (d.mode == MODE_RESID) {
+#pragma unroll
+        for (int e = 0; e < RL; ++e) {
+            const float pv = target_prob(lvals.v[e], d.M, c2, invS);
+            const float wgt = usep ? pv : fmaxf(pv - qvals.v[e], 0.f);
+            const bool in = first + e < xs1 && (!FILT || logit_key(lvals.v[e]) >= d.tau);
+            wv[e] = in ? static_cast<double>(wgt) : 0.0;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < RL; ++e) {
+            const float wgt = __builtin_amdgcn_exp2f((lvals.v[e] - Mc) * c2);
+            const bool in = first + e < xs1 && (!FILT || logit_key(lvals.v[e]) >= d.tau);
+            wv[e] = in ? static_cast<double>(wgt) * scale : 0.0;
+        }
+    }
+    // Mass before this thread's run: block exclusive scan of the run totals.
+    double mine = 0.0;
+#pragma unroll
+    for (int e = 0; e < RL; ++e) mine += wv[e];
+    const double incl_r = wave_incl_scan(mine);
+    if (lane == 63) s_wtot[4 + wave] = incl_r;  // slots 4..7: the chunk scan's 0..3 may still be read
+    __syncthreads();
+    double c = base + (incl_r - mine);
+    for (int k = 0; k < wave; ++k) c += s_wtot[4 + k];
+    // Walk the run in token order: the first token whose cumulative mass
+    // exceeds t, and the last token with weight (the fallback when rounding
+    // leaves the slice's recomputed mass short of t).
+    int xhit = 0x7fffffff, lastnz = -1;
+#pragma unroll
+    for (int e = 0; e < RL; ++e) {
+        const bool nz = wv[e] > 0.0;
+        c += wv[e];
+        lastnz = nz ? first + e : lastnz;
+        xhit = nz && xhit == 0x7fffffff && c > t ? first + e : xhit;
+    }
+    int ix = xhit, iz = lastnz;
+    block_min_max_i(ix, iz, s_mn, s_mx);
+    if (tid == 0) {
+        int final = ix != 0x7fffffff ? ix : iz;
+        if (final < 0) final = x0;
+        *out = final;
     }
 }
 
@@ -1031,13 +1079,16 @@ __device__ __forceinline__ void select_token(const AcceptArgs& a, int b, const D
     __shared__ double s_sbase;
     // Chunks of two slices (8 entries a thread) are searched whole: there
     // the slice masses' extra round trip costs more than the reload saves.
+    // The residual's rare fallback to the plain mass searches the chunk whole
+    // too (only the residual or bonus mass is kept per slice).
     constexpr int NS = EPT / 4;
-    constexpr bool kSlices = NS >= 4;
+    constexpr bool kSliced = NS >= 4;
+    const bool sliced = kSliced && !usep;
     // (every wave loads, from clamped slots: no load under a branch)
-    const size_t so = (static_cast<size_t>(b) * a.nchunk + pc) * (2 * kSubMax) + (usep ? kSubMax : 0);
-    const double raw = kSlices ? a.cslice[so + min(lane, NS - 1)] : 0.0;
+    const size_t so = (static_cast<size_t>(b) * a.nchunk + pc) * kSubMax;
+    const double raw = kSliced ? a.cslice[so + min(lane, NS - 1)] : 0.0;
     __syncthreads();  // s_v[0]
-    if (kSlices && wave == 0) {
+    if (sliced && wave == 0) {  // (workgroup-uniform)
         const double scl = d.mode == MODE_BONUS ? exp2((static_cast<double>(s_v[0]) - Mg) * c2d) : 1.0;
         const double w = lane < NS ? raw * scl : 0.0;
         const double incl = wave_incl_scan(w);
@@ -1055,59 +1106,14 @@ __device__ __forceinline__ void select_token(const AcceptArgs& a, int b, const D
     __syncthreads();
     const float Mc = s_v[0];
     const double scale = d.mode == MODE_BONUS ? exp2((static_cast<double>(Mc) - Mg) * c2d) : 1.0;
-    const int js = kSlices ? s_js : 0;
-    const double sbase = kSlices ? s_sbase : base;
     // Thread tid owns tokens first .. first + RL - 1 of the slice (or of the
     // chunk); weights of tokens past its end are 0.
-    constexpr int RL = kSlices ? 4 : EPT;
-    const int xs1 = kSlices ? min(x0 + (js + 1) * kSubTokens, x1) : x1;
-    const int first = x0 + js * kSubTokens + tid * RL;
-    Vals<RL> lvals, qvals;
-    load_run2<RL>(row, qrow, first, xs1, vec4, lvals, qvals);
-    double wv[RL];
-    if (d.mode == MODE_RESID) {
-#pragma unroll
-        for (int e = 0; e < RL; ++e) {
-            const float pv = target_prob(lvals.v[e], d.M, c2, invS);
-            const float wgt = usep ? pv : fmaxf(pv - qvals.v[e], 0.f);
-            const bool in = first + e < xs1 && (!FILT || logit_key(lvals.v[e]) >= d.tau);
-            wv[e] = in ? static_cast<double>(wgt) : 0.0;
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < RL; ++e) {
-            const float wgt = __builtin_amdgcn_exp2f((lvals.v[e] - Mc) * c2);
-            const bool in = first + e < xs1 && (!FILT || logit_key(lvals.v[e]) >= d.tau);
-            wv[e] = in ? static_cast<double>(wgt) * scale : 0.0;
-        }
-    }
-    // Mass before this thread's run: block exclusive scan of the run totals.
-    double mine = 0.0;
-#pragma unroll
-    for (int e = 0; e < RL; ++e) mine += wv[e];
-    const double incl_r = wave_incl_scan(mine);
-    if (lane == 63) s_wtot[4 + wave] = incl_r;  // slots 4..7: the chunk scan's 0..3 may still be read
-    __syncthreads();
-    double c = sbase + (incl_r - mine);
-    for (int k = 0; k < wave; ++k) c += s_wtot[4 + k];
-    // Walk the run in token order: the first token whose cumulative mass
-    // exceeds t, and the last token with weight (the fallback when rounding
-    // leaves the slice's recomputed mass short of t).
-    int xhit = 0x7fffffff, lastnz = -1;
-#pragma unroll
-    for (int e = 0; e < RL; ++e) {
-        const bool nz = wv[e] > 0.0;
-        c += wv[e];
-        lastnz = nz ? first + e : lastnz;
-        xhit = nz && xhit == 0x7fffffff && c > t ? first + e : xhit;
-    }
-    int ix = xhit, iz = lastnz;
-    block_min_max_i(ix, iz, s_mn, s_mx);
-    if (tid == 0) {
-        int final = ix != 0x7fffffff ? ix : iz;
-        if (final < 0) final = x0;
-        *out = final;
-    }
+    if (sliced)
+        search_run<4, FILT>(a, d, row, qrow, x0 + s_js * kSubTokens, min(x0 + (s_js + 1) * kSubTokens, x1), vec4,
+                            s_sbase, usep, Mc, scale, invS, c2, t, x0, out, s_wtot, s_mn, s_mx);
+    else
+        search_run<EPT, FILT>(a, d, row, qrow, x0, x1, vec4, base, usep, Mc, scale, invS, c2, t, x0, out, s_wtot,
+                              s_mn, s_mx);
 }
 
 template <int EPT, bool FILT = false>
