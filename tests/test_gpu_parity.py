@@ -218,6 +218,8 @@ def test_accept_full_size(cid):
     (5, dict(batch=5, vocab=4000, nodes=40, max_depth=8)),        # 2 chunks: 32 rows per decision pass
     (5, dict(batch=7, vocab=15000, nodes=64, max_depth=5)),       # 8 chunks: 8 rows per decision pass
     (3, dict(batch=3, vocab=7000, epsilon=0.02, delta=0.05)),     # 4 chunks, typical rule
+    (4, dict(batch=64, vocab=20001)),                             # slice search, V % 4 != 0 (no 16-byte loads)
+    (4, dict(batch=64, vocab=9000)),                              # slice search, a last chunk of one slice
 ])
 def test_accept_edge_cases(cid, over):
     w = generate(scaled(cid, **over), with_attention=False)
