@@ -58,15 +58,6 @@ struct MdArgs {
     int vec4;
 };
 
-// Device-scope (agent) relaxed stores and loads: they bypass the caches that
-// are not coherent across the XCDs.
-__device__ __forceinline__ void md_st64(void* p, uint64_t v) {
-    __hip_atomic_store(static_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t md_ld64(const void* p) {
-    return __hip_atomic_load(static_cast<uint64_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // One residual element: max(0, r * inv - q) rounded to fp32, r the previous
 // residual (or the unnormalised target weight) and inv the reciprocal of its
@@ -182,9 +173,9 @@ __global__ __launch_bounds__(kMdThreads) void accept_md(MdArgs a) {
         if (P > 1) {
             MdRec* slots = a.recs + (static_cast<size_t>(b) * 2 + (round & 1u)) * kMdMaxParts;
             if (tid == 0) {
-                md_st64(&slots[p].s, __builtin_bit_cast(uint64_t, mine.s));
+                agent_st64(&slots[p].s, __builtin_bit_cast(uint64_t, mine.s));
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the sum is stored before the tagged word
-                md_st64(&slots[p].m, md_word1(mine.m, mine.arg, round));
+                agent_st64(&slots[p].m, md_word1(mine.m, mine.arg, round));
             }
             if (wave == 0) {
                 // Lane k waits for part k's tagged word (a bounded poll), then
@@ -193,7 +184,7 @@ __global__ __launch_bounds__(kMdThreads) void accept_md(MdArgs a) {
                 uint64_t w = 0ull;
                 uint32_t polls = 0;
                 for (;;) {
-                    w = md_ld64(&slots[k].m);
+                    w = agent_ld64(&slots[k].m);
                     const bool here = ((w >> 56) & 0xFFu) == (round & 0xFFu);
                     if (__ballot(!here) == 0ull) break;  // (wave-uniform exit)
                     __builtin_amdgcn_s_sleep(2);
@@ -204,7 +195,7 @@ __global__ __launch_bounds__(kMdThreads) void accept_md(MdArgs a) {
                 }
                 if (lane < P) {
                     MdRec r;
-                    r.s = __builtin_bit_cast(double, md_ld64(&slots[k].s));
+                    r.s = __builtin_bit_cast(double, agent_ld64(&slots[k].s));
                     r.m = __uint_as_float(static_cast<uint32_t>(w));
                     const uint32_t a24 = static_cast<uint32_t>(w >> 32) & kMdNoArg;
                     r.arg = a24 == kMdNoArg ? 0x7fffffff : static_cast<int>(a24);

@@ -254,6 +254,18 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcn
 
 // Parent of node i (-1 for the root); parent == nullptr means a chain.
 // Out-of-contract entries (p < 0 or p >= i for i > 0) are reported as -2.
+// Device-scope (agent) relaxed 64-bit stores and loads: they bypass the
+// caches that are not coherent across the XCDs, so workgroups on different
+// XCDs can exchange records inside one launch (a store is complete, and
+// visible to such loads, once the storing thread's vmcnt has drained).
+__device__ __forceinline__ void agent_st64(void* p, uint64_t v) {
+    __hip_atomic_store(static_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t agent_ld64(const void* p) {
+    return __hip_atomic_load(static_cast<uint64_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ int tree_parent(const int32_t* parent, int N, int b, int i) {
     if (i <= 0) return -1;
     if (!parent) return i - 1;
