@@ -602,7 +602,7 @@ __device__ __forceinline__ void write_decision(const AcceptArgs& a, int b, const
     if (tid == 0) a.accept_len[b] = d.a;
 }
 
-template <int RPW, bool FILT = false>  // node rows per wave (N <= 4 * RPW)
+template <int RPW, bool FILT = false>  // combining passes per wave (rows <= 4 * RPW * 64 / L)
 __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, bool writer) {
     const int N = a.N, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __shared__ DecLds L;
@@ -1765,12 +1765,21 @@ static int launch_accept_ept(const AcceptArgs& a, const AcceptPlan& p, hipStream
         }
         if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     }
-    // Few rows need fewer registers for the decision: more workgroups per CU.
-    if (a.N <= 16)
-        hipLaunchKernelGGL((accept_sample<EPT, 4, FILT>), dim3(p.nchunk, a.B), dim3(kThreads), 0, stream, a);
+    // The decision loads one chunk record per lane and combining pass; a wave
+    // owns a quarter of the rows and combines 64 / L of them per pass (L the
+    // lanes of a row's chunk segment).  Fewer passes need fewer registers and
+    // loads: more workgroups per CU.  The truncated rule reads row records.
+    const int nrows = a.N - 1 + (a.parent != nullptr);
+    const int passes = FILT ? 1 : (((nrows + 3) / 4) + (64 >> a.lg_seg) - 1) / (64 >> a.lg_seg);
+    const dim3 sgrid(p.nchunk, a.B);
+    if (passes <= 1)
+        hipLaunchKernelGGL((accept_sample<EPT, 1, FILT>), sgrid, dim3(kThreads), 0, stream, a);
+    else if (passes <= 2)
+        hipLaunchKernelGGL((accept_sample<EPT, 2, FILT>), sgrid, dim3(kThreads), 0, stream, a);
+    else if (passes <= 4)
+        hipLaunchKernelGGL((accept_sample<EPT, 4, FILT>), sgrid, dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL((accept_sample<EPT, kRowsPerWave, FILT>), dim3(p.nchunk, a.B), dim3(kThreads), 0, stream,
-                           a);
+        hipLaunchKernelGGL((accept_sample<EPT, kRowsPerWave, FILT>), sgrid, dim3(kThreads), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
     hipLaunchKernelGGL((accept_select<EPT, FILT>), dim3(a.B), dim3(kThreads), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
