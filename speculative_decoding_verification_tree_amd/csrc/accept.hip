@@ -691,9 +691,11 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
             rr[t] = a.rowstat[(static_cast<size_t>(b) * N + min(wave + 4 * (t * R + sr), N - 1)) * a.nchunk + cl];
     }
     gather();
+    // Below 16 passes every pass runs (passes past the last row combine
+    // nothing and store nothing), so the compiler can interleave them.
 #pragma unroll
     for (int t = 0; t < RPW; ++t) {
-        if (t < passes) {  // wave-uniform
+        if (RPW < kRowsPerWave || t < passes) {  // wave-uniform
             const int u = wave + 4 * (t * R + sr);
             const bool row_in = u < nrows, in = row_in && cc < a.nchunk;
             float m = in ? rr[t].M : -INFINITY;
@@ -727,11 +729,13 @@ __device__ __forceinline__ Decision decide_request(const AcceptArgs& a, int b, b
                 S = seg_sum(S, lg);
                 A2 = seg_sum(A2, lg);
             }
+            // the entropy only for the typical rule
+            const double H = T > 0.0 && a.rule == 1 ? log(S) - 0.6931471805599453 * A2 / S : 0.0;
             if (cc == 0 && row_in) {
                 s_M[u] = m;
                 s_arg[u] = ar;
                 s_S[u] = S;
-                s_H[u] = T > 0.0 ? log(S) - 0.6931471805599453 * A2 / S : 0.0;
+                s_H[u] = H;
             }
         }
     }
