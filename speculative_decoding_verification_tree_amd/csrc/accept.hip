@@ -86,8 +86,8 @@ struct AcceptArgs {
     RowRec* rowrec;  // truncated rows (aliases rowstat's space)
     Decision* dec;
     ChunkStat* cstat;
-    // [B][nchunk][2][kSubMax]: per 1024-token slice of each stop-row chunk,
-    // the residual (or bonus) mass, then the plain mass
+    // [B][nchunk][kSubMax]: per 1024-token slice of each stop-row chunk of
+    // four or more slices, the residual (or bonus) mass
     double* cslice;
     int B, N, V, chunk, nchunk, rule;  // rule 0 = rejection, 1 = typical
     int lg_seg;                        // log2 of the lanes per row in the decision: 2^lg_seg >= min(nchunk, 64)
@@ -1725,7 +1725,7 @@ AcceptPlan plan_accept(int B, int N, int V) {
     p.off_cstat = off;
     off = align_up(off + static_cast<size_t>(B) * p.nchunk * sizeof(ChunkStat), 256);
     p.off_cslice = off;
-    off = align_up(off + static_cast<size_t>(B) * p.nchunk * 2 * kSubMax * sizeof(double), 256);
+    off = align_up(off + static_cast<size_t>(B) * p.nchunk * kSubMax * sizeof(double), 256);
     p.ws_bytes = off;
     const size_t slots = static_cast<size_t>(B) * N * p.nchunk;
     p.off_frec = off;
