@@ -1134,11 +1134,13 @@ __global__ __launch_bounds__(kThreads) void accept_select(AcceptArgs a) {
 // the statistics kernel launches at most ~2k workgroups of useful size (on
 // 8 requests of 46-node trees over 32000 tokens, ~5.9k short-lived
 // workgroups ran in about three rounds: the acceptance took 22.1 us against
-// 20.8 at a ~4k bound and 19.0 at ~2k).
+// 20.8 at a ~4k bound and 19.0 at ~2k), and for rows of more than 32 chunks
+// (the decision then combines two or more rows per wave pass, and the
+// truncation's finish gathers fewer chunk records).
 static int accept_ept(int B, int N, int V) {
     int ept = 8;
     auto nchunk = [&](int e) { return (V + e * kThreads - 1) / (e * kThreads); };
-    while (ept < 32 && (static_cast<long>(B) * N * nchunk(ept) > 2048 || nchunk(ept) > kMaxChunks)) ept *= 2;
+    while (ept < 32 && (static_cast<long>(B) * N * nchunk(ept) > 2048 || nchunk(ept) > 32)) ept *= 2;
     return ept;
 }
 
