@@ -149,7 +149,7 @@ def _logits_of(kind, shape, rng):
 
 
 @pytest.mark.parametrize("cid,over,kind,k,p", [
-    (2, dict(batch=3), None, 50, 0.9),                        # B = 3 chain, V = 128256: 63 chunks per row
+    (2, dict(batch=3), None, 50, 0.9),                        # B = 3 chain, V = 128256: 32 chunks per row
     (4, dict(batch=16, prefix_len=(10, 40)), None, 20, 0.95),
     (5, dict(batch=2, prefix_len=(0, 8)), None, 100, 1.0),    # 64-node trees
     (1, dict(batch=32, vocab=1001), None, 7, 0.7),            # V % 4 != 0: scalar loads

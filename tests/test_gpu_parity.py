@@ -213,10 +213,11 @@ def test_accept_full_size(cid):
     (1, dict(batch=32, drafts=0)),                                # N = 1: bonus only
     (5, dict(batch=6, vocab=5000, nodes=64, max_depth=63)),       # deep tree, max N
     (4, dict(batch=32, vocab=20000, draft_noise=[0.0])),          # q == p: all accepted
-    (2, dict(batch=3, vocab=300000)),                             # > 64 vocabulary chunks
-    (3, dict(batch=2, vocab=300001, temperature=0.0)),            # > 64 chunks, argmax path
+    (2, dict(batch=3, vocab=300000)),                             # 37 chunks: one row per decision pass
+    (2, dict(batch=1, vocab=600000)),                             # 74 chunks: > 64 vocabulary chunks
+    (3, dict(batch=1, vocab=600001, temperature=0.0)),            # > 64 chunks, argmax path
     (5, dict(batch=5, vocab=4000, nodes=40, max_depth=8)),        # 2 chunks: 32 rows per decision pass
-    (5, dict(batch=7, vocab=15000, nodes=64, max_depth=5)),       # 8 chunks: 8 rows per decision pass
+    (5, dict(batch=7, vocab=15000, nodes=64, max_depth=5)),       # 4 chunks: 16 rows per decision pass
     (3, dict(batch=3, vocab=7000, epsilon=0.02, delta=0.05)),     # 4 chunks, typical rule
     (4, dict(batch=64, vocab=20001)),                             # slice search, V % 4 != 0 (no 16-byte loads)
     (4, dict(batch=64, vocab=9000)),                              # slice search, a last chunk of one slice
